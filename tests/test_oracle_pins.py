@@ -1,0 +1,403 @@
+"""Pins of the fp64 oracle against what the pages and mathematics fix.
+
+Citation key: [D] damodev.csdn.net TTT deep-dive; [Y] lryc.cn TTT article;
+[X] xiaohu.ai TTT summary.
+
+Each pin is chosen so that a plausible mistake in the oracle (a dropped LN
+term, a wrong sign, a transposed W, a wrong eta index, applying before
+updating, an off-by-one chunk boundary) fails at least one of them:
+  * autograd references (torch, fp64) for b = 1 and mini-batch b > 1;
+  * complex-step and finite-difference gradients of the per-token loss;
+  * brute force with every gradient taken by central differences;
+  * closed forms (eta = 0 static layer, fixed point), invariants of the LN
+    backward, and structural identities (dual = primal, resume, permutation).
+"""
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from test_sequence_layer_ttt_amd import gen
+from tests import torch_ref
+
+pytestmark = pytest.mark.filterwarnings("ignore::DeprecationWarning")
+
+
+def _rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.abs(a - b).max() / max(np.abs(b).max(), 1e-300))
+
+
+def _small_linear(seed, B=2, H=3, L=37, d=8, ln_random=True, b_random=True, w_std=0.3):
+    return gen.make_linear(seed, B, H, L, d, io="f32", ln_random=ln_random,
+                           b_random=b_random, w_std=w_std)
+
+
+# ---------------------------------------------------------------------------
+# Generator
+# ---------------------------------------------------------------------------
+def test_generator_deterministic():
+    a = gen.make_workload(2, L=64, B=1, H=2)
+    b = gen.make_workload(2, L=64, B=1, H=2)
+    for k in ("XQ", "XK", "XV", "eta", "W0"):
+        assert getattr(a, k).tobytes() == getattr(b, k).tobytes()
+
+
+def test_generator_blockwise_equals_single_draw():
+    r1 = np.random.default_rng(7)
+    r2 = np.random.default_rng(7)
+    x = gen._normal_f32(r1, (3, 1000), block=37)
+    y = r2.standard_normal(3000).astype(np.float32).reshape(3, 1000)
+    assert x.tobytes() == y.tobytes()
+
+
+def test_bf16_rounding_matches_torch_rne():
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal(100000) * 10 ** rng.uniform(-3, 3, 100000)).astype(np.float32)
+    # add exact ties
+    x[:100] = gen.bf16_to_f32(np.arange(100, dtype=np.uint16) + 16256) + np.float32(2 ** -8)
+    ours = gen.round_bf16(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert ours.tobytes() == ref.tobytes()
+
+
+def test_rms_normalised_inputs():
+    x = gen.make_workload(2, L=32, B=1, H=2)
+    r = np.sqrt(np.mean(x.XQ.astype(np.float64) ** 2, axis=-1))
+    assert np.allclose(r, 1.0, atol=1e-2)
+
+
+def test_eta_gate_range():
+    for num in (1, 2, 3):
+        x = gen.make_workload(num, L=32, B=1, H=1)
+        assert np.all(x.eta > 0) and np.all(x.eta < 1.0 / x.d)
+
+
+# ---------------------------------------------------------------------------
+# LN + L2 backward ([D] §4.2, fused LN-L2 gradient)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("d", [4, 16, 64])
+def test_ln_l2_bwd_complex_step(d):
+    rng = np.random.default_rng(d)
+    Z = rng.standard_normal((20, d)) * rng.uniform(0.05, 3, (20, 1)) + rng.standard_normal((20, 1))
+    T = rng.standard_normal((20, d))
+    g = 1 + 0.3 * rng.standard_normal(d)
+    b = 0.3 * rng.standard_normal(d)
+    G = oracle.ln_l2_bwd(Z, T, g, b, 1e-6)
+    Gc = torch_ref.complex_step_grad(Z, T, g, b, 1e-6)
+    assert _rel(G, Gc) < 1e-12
+
+
+def test_ln_l2_bwd_matches_autograd():
+    rng = np.random.default_rng(11)
+    d = 64
+    Z = rng.standard_normal((50, d))
+    T = rng.standard_normal((50, d))
+    g = 1 + 0.1 * rng.standard_normal(d)
+    b = 0.1 * rng.standard_normal(d)
+    z = torch.tensor(Z, requires_grad=True)
+    y = F.layer_norm(z, (d,), torch.tensor(g), torch.tensor(b), 1e-6)
+    (0.5 * ((y - torch.tensor(T)) ** 2).sum()).backward()
+    assert _rel(oracle.ln_l2_bwd(Z, T, g, b, 1e-6), z.grad.numpy()) < 1e-12
+
+
+def test_ln_l2_bwd_central_differences():
+    rng = np.random.default_rng(5)
+    d = 8
+    z = rng.standard_normal((1, d))
+    t = rng.standard_normal((1, d))
+    g = 1 + 0.2 * rng.standard_normal(d)
+    b = 0.2 * rng.standard_normal(d)
+    G = oracle.ln_l2_bwd(z, t, g, b, 1e-6)
+    h = 1e-6
+    fd = np.zeros(d)
+    for j in range(d):
+        zp = z.copy(); zp[0, j] += h
+        zm = z.copy(); zm[0, j] -= h
+        fd[j] = (torch_ref.token_loss_np(zp, t, g, b, 1e-6)[0]
+                 - torch_ref.token_loss_np(zm, t, g, b, 1e-6)[0]) / (2 * h)
+    assert _rel(G[0], fd) < 1e-7
+
+
+def test_ln_l2_bwd_invariants():
+    """sum_j G_j = 0 exactly (sum of xhat is 0); sum_j G_j xhat_j equals
+    (eps/(v+eps)) * mean-free correction, i.e. ~0; G(alpha z) = G(z)/alpha
+    when eps -> 0 and gamma = 1, beta = 0 rescale-free target."""
+    rng = np.random.default_rng(9)
+    d = 64
+    Z = rng.standard_normal((30, d)) * 2 + 0.5
+    T = rng.standard_normal((30, d))
+    g = np.ones(d)
+    b = np.zeros(d)
+    eps = 1e-6
+    G = oracle.ln_l2_bwd(Z, T, g, b, eps)
+    assert np.abs(G.sum(-1)).max() < 1e-12 * np.abs(G).max() * d
+    mu = Z.mean(-1, keepdims=True)
+    v = ((Z - mu) ** 2).mean(-1, keepdims=True)
+    xh = (Z - mu) / np.sqrt(v + eps)
+    # exact identity: sum_j G_j xh_j = (eps/(v+eps)) * sum_j gh_j xh_j / sigma
+    gh = g * (g * xh + b - T)
+    lhs = (G * xh).sum(-1)
+    rhs = (eps / (v[:, 0] + eps)) * (gh * xh).sum(-1) / np.sqrt(v[:, 0] + eps)
+    assert np.abs(lhs - rhs).max() < 1e-11
+    G0 = oracle.ln_l2_bwd(Z, T, g, b, 1e-300)
+    G3 = oracle.ln_l2_bwd(3.0 * Z, T, g, b, 1e-300)
+    assert _rel(G3 * 3.0, G0) < 1e-12
+
+
+def test_ln_fwd_matches_torch():
+    rng = np.random.default_rng(2)
+    Z = rng.standard_normal((10, 64)) * 3 + 1
+    g = 1 + 0.1 * rng.standard_normal(64)
+    b = 0.1 * rng.standard_normal(64)
+    ref = F.layer_norm(torch.tensor(Z), (64,), torch.tensor(g), torch.tensor(b), 1e-6).numpy()
+    assert _rel(oracle.ln_fwd(Z, g, b, 1e-6), ref) < 1e-13
+
+
+# ---------------------------------------------------------------------------
+# TTT-Linear recurrence
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("mb,L", [(1, 24), (16, 64), (4, 21), (16, 37)])
+def test_linear_matches_autograd(mb, L):
+    """P1 (mb = 1: the literal per-token recurrence of [D] §3.1) and the
+    mini-batch form of [D] §4.1 (mb > 1, including a partial last chunk),
+    each against torch autograd in fp64."""
+    x = _small_linear(10 + mb, B=1, H=2, L=L, d=16)
+    O, W, b = oracle.linear_forward(x.XQ, x.XK, x.XV, x.eta, x.W0, x.b0, x.gamma, x.beta,
+                                    x.eps, mb=mb)
+    for h in range(2):
+        Or, Wr, br = torch_ref.linear_autograd(x.XQ[0, h], x.XK[0, h], x.XV[0, h], x.eta[0, h],
+                                               x.W0[h], x.b0[h], x.gamma[h], x.beta[h],
+                                               x.eps, mb)
+        assert _rel(O[0, h], Or) < 1e-12
+        assert _rel(W[0, h], Wr) < 1e-12
+        assert _rel(b[0, h], br) < 1e-12
+
+
+def test_linear_bruteforce_finite_differences():
+    """P5: every gradient by central differences, no analytic LN backward."""
+    x = _small_linear(21, B=1, H=1, L=12, d=4, w_std=0.5)
+    O, W, b = oracle.linear_forward(x.XQ, x.XK, x.XV, x.eta, x.W0, x.b0, x.gamma, x.beta,
+                                    x.eps, mb=4)
+    Or, Wr, br = torch_ref.linear_bruteforce_fd(x.XQ[0, 0], x.XK[0, 0], x.XV[0, 0],
+                                                x.eta[0, 0], x.W0[0], x.b0[0], x.gamma[0],
+                                                x.beta[0], x.eps, 4)
+    assert _rel(O[0, 0], Or) < 1e-6
+    assert _rel(W[0, 0], Wr) < 1e-6
+    assert _rel(b[0, 0], br) < 1e-6
+
+
+def test_weight_gradient_is_outer_product():
+    """P4: grad_W l = xk^T G and grad_b l = G (row-vector convention Z = XK W,
+    [D] §4.2) against complex-step differentiation with respect to W."""
+    rng = np.random.default_rng(4)
+    d = 8
+    xk = rng.standard_normal(d)
+    tau = rng.standard_normal(d)
+    W = rng.standard_normal((d, d)) * 0.3
+    bb = rng.standard_normal(d) * 0.1
+    g = 1 + 0.2 * rng.standard_normal(d)
+    be = 0.2 * rng.standard_normal(d)
+    G = oracle.ln_l2_bwd((xk @ W + bb)[None], tau[None], g, be, 1e-6)[0]
+    gw = np.zeros((d, d))
+    hh = 1e-30
+    for i in range(d):
+        for j in range(d):
+            Wc = W.astype(np.complex128)
+            Wc[i, j] += 1j * hh
+            gw[i, j] = torch_ref.token_loss_np(xk @ Wc + bb, tau, g, be, 1e-6).imag / hh
+    assert _rel(np.outer(xk, G), gw) < 1e-12
+
+
+def test_eta_zero_is_static_layer():
+    """P2: eta = 0 leaves the state unchanged and O = XQ + LN(XQ W0 + b0)."""
+    x = _small_linear(31, B=2, H=2, L=40, d=16)
+    eta = np.zeros_like(x.eta)
+    O, W, b = oracle.linear_forward(x.XQ, x.XK, x.XV, eta, x.W0, x.b0, x.gamma, x.beta,
+                                    x.eps, mb=16)
+    for n in range(2):
+        for h in range(2):
+            z = torch.tensor(x.XQ[n, h], dtype=torch.float64) @ torch.tensor(x.W0[h], dtype=torch.float64) \
+                + torch.tensor(x.b0[h], dtype=torch.float64)
+            ref = x.XQ[n, h] + F.layer_norm(z, (16,), torch.tensor(x.gamma[h], dtype=torch.float64),
+                                            torch.tensor(x.beta[h], dtype=torch.float64), x.eps).numpy()
+            assert _rel(O[n, h], ref) < 1e-13
+            assert np.array_equal(W[n, h], x.W0[h].astype(np.float64))
+            assert np.array_equal(b[n, h], x.b0[h].astype(np.float64))
+
+
+def test_fixed_point_chunk_zero():
+    """P7: if XV = XK + LN(XK W0 + b0) on chunk 0 the gradient vanishes, so the
+    state is unchanged after chunk 0 and chunk 0's outputs are the static layer."""
+    x = _small_linear(41, B=1, H=1, L=32, d=16)
+    XV = x.XV.astype(np.float64).copy()
+    z0 = x.XK[0, 0, :16].astype(np.float64) @ x.W0[0] + x.b0[0]
+    XV[0, 0, :16] = x.XK[0, 0, :16] + oracle.ln_fwd(z0, x.gamma[0], x.beta[0], x.eps)
+    O, W, b = oracle.linear_forward(x.XQ[:, :, :16], x.XK[:, :, :16], XV[:, :, :16],
+                                    x.eta[:, :, :16], x.W0, x.b0, x.gamma, x.beta, x.eps, mb=16)
+    assert _rel(W[0, 0], x.W0[0]) < 1e-13
+    assert np.abs(b[0, 0] - x.b0[0]).max() < 1e-13
+    zq = x.XQ[0, 0, :16].astype(np.float64) @ x.W0[0] + x.b0[0]
+    assert _rel(O[0, 0], x.XQ[0, 0, :16] + oracle.ln_fwd(zq, x.gamma[0], x.beta[0], x.eps)) < 1e-12
+
+
+@pytest.mark.parametrize("mb", [16, 5])
+def test_dual_equals_primal_linear(mb):
+    """P3: the dual form of [D] §4.2 / [X] gives the primal result."""
+    x = _small_linear(51, B=2, H=3, L=53, d=16)
+    a = oracle.linear_forward(x.XQ, x.XK, x.XV, x.eta, x.W0, x.b0, x.gamma, x.beta, x.eps, mb=mb)
+    b = oracle.linear_forward(x.XQ, x.XK, x.XV, x.eta, x.W0, x.b0, x.gamma, x.beta, x.eps, mb=mb,
+                              dual=True)
+    for u, v in zip(a, b):
+        assert _rel(u, v) < 1e-12
+
+
+def test_resume_is_exact():
+    """P8: forward(L1) then forward(L2 from the returned state) equals
+    forward(L1 + L2) when L1 is a multiple of mb (state = the cache, [D] §5.2)."""
+    x = _small_linear(61, B=2, H=2, L=80, d=16)
+    full = oracle.linear_forward(x.XQ, x.XK, x.XV, x.eta, x.W0, x.b0, x.gamma, x.beta, x.eps)
+    s = slice(0, 48)
+    r = slice(48, 80)
+    O1, W1, b1 = oracle.linear_forward(x.XQ[:, :, s], x.XK[:, :, s], x.XV[:, :, s],
+                                       x.eta[:, :, s], x.W0, x.b0, x.gamma, x.beta, x.eps)
+    O2, W2, b2 = oracle.linear_forward(x.XQ[:, :, r], x.XK[:, :, r], x.XV[:, :, r],
+                                       x.eta[:, :, r], W1, b1, x.gamma, x.beta, x.eps,
+                                       w0_batched=True)
+    assert np.array_equal(np.concatenate([O1, O2], axis=2), full[0])
+    assert np.array_equal(W2, full[1]) and np.array_equal(b2, full[2])
+
+
+def test_prefill_then_decode_equals_mixed_schedule():
+    """P9: prefill (mb = 16) followed by single-token decode steps equals one
+    run with chunk schedule [16]*k + [1]*n ([D] §5.2: prefill vs decode)."""
+    x = _small_linear(71, B=1, H=2, L=40, d=16)
+    Lp = 32
+    ref = oracle.linear_forward(x.XQ, x.XK, x.XV, x.eta, x.W0, x.b0, x.gamma, x.beta, x.eps,
+                                schedule=[16, 16] + [1] * 8)
+    _, W, b = oracle.linear_forward(x.XQ[:, :, :Lp], x.XK[:, :, :Lp], x.XV[:, :, :Lp],
+                                    x.eta[:, :, :Lp], x.W0, x.b0, x.gamma, x.beta, x.eps)
+    for t in range(Lp, 40):
+        o, W, b = oracle.decode_step(x.XQ[:, :, t], x.XK[:, :, t], x.XV[:, :, t],
+                                     x.eta[:, :, t], W, b, x.gamma, x.beta, x.eps)
+        assert np.array_equal(o, ref[0][:, :, t])
+    assert np.array_equal(W, ref[1]) and np.array_equal(b, ref[2])
+
+
+def test_permutation_of_sequences():
+    """P10: permuting (n, h) permutes the outputs (per-sequence W0 given)."""
+    x = _small_linear(81, B=2, H=3, L=20, d=8)
+    W0b = np.broadcast_to(x.W0, (2, 3, 8, 8)).copy() + np.arange(6).reshape(2, 3, 1, 1) * 0.01
+    b0b = np.broadcast_to(x.b0, (2, 3, 8)).copy()
+    gam = np.broadcast_to(x.gamma[0], (3, 8)).copy()
+    bet = np.broadcast_to(x.beta[0], (3, 8)).copy()
+    O, W, b = oracle.linear_forward(x.XQ, x.XK, x.XV, x.eta, W0b, b0b, gam, bet, x.eps,
+                                    w0_batched=True)
+    p = np.random.default_rng(0).permutation(6)
+
+    def perm(a):
+        s = a.shape
+        return a.reshape((6,) + s[2:])[p].reshape(s)
+
+    Op, Wp, bp = oracle.linear_forward(perm(x.XQ), perm(x.XK), perm(x.XV), perm(x.eta),
+                                       perm(W0b), perm(b0b), gam, bet, x.eps, w0_batched=True)
+    assert np.array_equal(Op, perm(O)) and np.array_equal(Wp, perm(W)) and np.array_equal(bp, perm(b))
+
+
+def test_threads_do_not_change_result():
+    x = _small_linear(91, B=3, H=3, L=33, d=8)
+    a = oracle.linear_forward(x.XQ, x.XK, x.XV, x.eta, x.W0, x.b0, x.gamma, x.beta, x.eps, nthreads=1)
+    b = oracle.linear_forward(x.XQ, x.XK, x.XV, x.eta, x.W0, x.b0, x.gamma, x.beta, x.eps, nthreads=5)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def test_bad_schedule_rejected():
+    x = _small_linear(1, B=1, H=1, L=8, d=4)
+    with pytest.raises(RuntimeError):
+        oracle.linear_forward(x.XQ, x.XK, x.XV, x.eta, x.W0, x.b0, x.gamma, x.beta, x.eps,
+                              schedule=[4, 3])
+
+
+def test_empty_sequence_passes_state_through():
+    x = _small_linear(2, B=2, H=2, L=0, d=8)
+    O, W, b = oracle.linear_forward(x.XQ, x.XK, x.XV, x.eta, x.W0, x.b0, x.gamma, x.beta, x.eps)
+    assert O.shape == (2, 2, 0, 8)
+    assert np.array_equal(W, np.broadcast_to(x.W0, W.shape))
+
+
+# ---------------------------------------------------------------------------
+# TTT-MLP ([Y] §2.1: d -> 4d GELU -> d inside the LN residual)
+# ---------------------------------------------------------------------------
+def _small_mlp(seed, B=1, H=2, L=24, d=8, w_std=0.3):
+    return gen.make_mlp(seed, B, H, L, d, io="f32", ln_random=True, w_std=w_std, b_random=True)
+
+
+@pytest.mark.parametrize("mb,L", [(1, 12), (8, 24), (16, 21)])
+def test_mlp_matches_autograd(mb, L):
+    x = _small_mlp(100 + mb, L=L)
+    O, W1, b1, W2, b2 = oracle.mlp_forward(x.XQ, x.XK, x.XV, x.eta, x.W1, x.b1, x.W2, x.b2,
+                                           x.gamma, x.beta, x.eps, mb=mb)
+    for h in range(2):
+        r = torch_ref.mlp_autograd(x.XQ[0, h], x.XK[0, h], x.XV[0, h], x.eta[0, h], x.W1[h],
+                                   x.b1[h], x.W2[h], x.b2[h], x.gamma[h], x.beta[h], x.eps, mb)
+        for got, ref in zip((O[0, h], W1[0, h], b1[0, h], W2[0, h], b2[0, h]), r):
+            assert _rel(got, ref) < 1e-11
+
+
+def test_mlp_eta_zero_is_static_layer():
+    x = _small_mlp(111, L=20)
+    O, W1, b1, W2, b2 = oracle.mlp_forward(x.XQ, x.XK, x.XV, np.zeros_like(x.eta), x.W1, x.b1,
+                                           x.W2, x.b2, x.gamma, x.beta, x.eps)
+    for h in range(2):
+        q = torch.tensor(x.XQ[0, h], dtype=torch.float64)
+        hid = F.gelu(q @ torch.tensor(x.W1[h], dtype=torch.float64)
+                     + torch.tensor(x.b1[h], dtype=torch.float64))
+        z = hid @ torch.tensor(x.W2[h], dtype=torch.float64) + torch.tensor(x.b2[h], dtype=torch.float64)
+        ref = q.numpy() + F.layer_norm(z, (8,), torch.tensor(x.gamma[h], dtype=torch.float64),
+                                       torch.tensor(x.beta[h], dtype=torch.float64), x.eps).numpy()
+        assert _rel(O[0, h], ref) < 1e-13
+        assert np.array_equal(W1[0, h], x.W1[h].astype(np.float64))
+        assert np.array_equal(W2[0, h], x.W2[h].astype(np.float64))
+
+
+@pytest.mark.parametrize("mb", [16, 6])
+def test_dual_equals_primal_mlp(mb):
+    x = _small_mlp(121, B=2, H=2, L=35, d=8)
+    a = oracle.mlp_forward(x.XQ, x.XK, x.XV, x.eta, x.W1, x.b1, x.W2, x.b2, x.gamma, x.beta,
+                           x.eps, mb=mb)
+    b = oracle.mlp_forward(x.XQ, x.XK, x.XV, x.eta, x.W1, x.b1, x.W2, x.b2, x.gamma, x.beta,
+                           x.eps, mb=mb, dual=True)
+    for u, v in zip(a, b):
+        assert _rel(u, v) < 1e-12
+
+
+def test_mlp_gradients_central_differences():
+    """P4 for the MLP: one chunk of one token; the state change divided by
+    -eta is the gradient; compare with central differences of the loss."""
+    x = _small_mlp(131, B=1, H=1, L=1, d=4, w_std=0.5)
+    eta = np.full_like(x.eta, 1e-3)
+    _, W1, b1, W2, b2 = oracle.mlp_forward(x.XQ, x.XK, x.XV, eta, x.W1, x.b1, x.W2, x.b2,
+                                           x.gamma, x.beta, x.eps, mb=1)
+    xk = x.XK[0, 0, 0].astype(np.float64)
+    tau = x.XV[0, 0, 0] - xk
+    P0 = [x.W1[0].astype(np.float64), x.b1[0].astype(np.float64),
+          x.W2[0].astype(np.float64), x.b2[0].astype(np.float64)]
+
+    def loss(P):
+        from math import erf, sqrt
+        z1 = xk @ P[0] + P[1]
+        a = np.array([0.5 * v * (1 + erf(v / sqrt(2))) for v in z1])
+        return torch_ref.token_loss_np(a @ P[2] + P[3], tau, x.gamma[0], x.beta[0], x.eps)
+
+    h = 1e-6
+    for idx, got in enumerate((W1[0, 0], b1[0, 0], W2[0, 0], b2[0, 0])):
+        g_an = (P0[idx] - got) / 1e-3
+        fd = np.zeros_like(P0[idx])
+        for k in np.ndindex(P0[idx].shape):
+            Pp = [p.copy() for p in P0]; Pp[idx][k] += h
+            Pm = [p.copy() for p in P0]; Pm[idx][k] -= h
+            fd[k] = (loss(Pp) - loss(Pm)) / (2 * h)
+        assert _rel(g_an, fd) < 1e-6
