@@ -1,0 +1,173 @@
+"""Benchmark: TTT-Linear dual-form prefill at L = 8192 (B=2, H=32, d=64, b=16,
+bf16 inputs, fp32 state) through the C ABI on one MI355X.
+
+A step is one ttt_linear_forward call over the whole workload with inputs
+already resident in HBM. Prints ONE JSON line (metric, tokens/s, roofline of
+the prefill kernel measured with HIP events on the launch stream, and the
+fp64 CPU oracle timed on the host cores on the same workload).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, datasheet
+WORKLOAD = 3
+METRIC = "TTT layer tokens/s (dual-form prefill, L=8192) + % of roofline"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_linear_prefill_workload3.json")
+
+
+def alg_bytes_linear(B, H, L, d, s_in=2, s_out=2):
+    """Algorithmic HBM bytes of one prefill launch: XQ, XK, XV and eta read,
+    O written once per token-head, plus the fp32 state (W, b) read and
+    written once per sequence."""
+    per_token_head = 3 * d * s_in + 4 + d * s_out
+    state = 2 * (d * d + d) * 4
+    return B * H * L * per_token_head + B * H * state
+
+
+def kernel_sources_hash():
+    from test_sequence_layer_ttt_amd import build as hb
+    h = hashlib.sha256()
+    for p in hb.sources() + [os.path.join(hb.CSRC, "common.hpp")]:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(alg_bytes):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    counters, if they were taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("sources_hash") != kernel_sources_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the TTT inner "
+              "loop shards over independent (batch, head) sequences with no exchange, so "
+              "N GPUs run N independent copies of this measurement.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from test_sequence_layer_ttt_amd import gen, ttt
+
+    w = gen.WORKLOADS[WORKLOAD]
+    x = gen.make_workload(WORKLOAD)
+    B, H, L, d = x.B, x.H, x.L, x.d
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bf = torch.bfloat16
+    T = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev).to(dt)
+    XQ, XK, XV = T(x.XQ, bf), T(x.XK, bf), T(x.XV, bf)
+    eta, W0, b0, gam, bet = T(x.eta), T(x.W0), T(x.b0), T(x.gamma), T(x.beta)
+    O = torch.empty_like(XQ)
+    Wo = torch.empty((B, H, d, d), device=dev)
+    bo = torch.empty((B, H, d), device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ttt.ttt_linear_forward(XQ, XK, XV, eta, W0, b0, gam, bet, O=O, W_out=Wo, b_out=bo,
+                               mb=16, ln_eps=x.eps, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[2 * i].record(stream)
+        step()
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(K)]
+    kern_avg_s = float(np.mean(kern_ms)) / 1e3
+    ms_per_step = wall * 1e3 / K
+    tokens = B * L
+    value = tokens / (wall / K)
+
+    ab = alg_bytes_linear(B, H, L, d)
+    achieved = ab / kern_avg_s / 1e9
+    traffic = measured_traffic(ab)
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "L": L, "d": d, "mini_batch": 16,
+                   "io": "bf16", "state": "fp32", "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "linear_prefill", "kernel_avg_us": kern_avg_s * 1e6,
+                     "alg_bytes_per_launch": ab},
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        nt = cpu_threads()
+        xs = {k: np.ascontiguousarray(getattr(x, k), np.float64)
+              for k in ("XQ", "XK", "XV", "eta", "W0", "b0", "gamma", "beta")}
+        t1 = time.perf_counter()
+        ro, rW, rb = oracle.linear_forward(xs["XQ"], xs["XK"], xs["XV"], xs["eta"], xs["W0"],
+                                           xs["b0"], xs["gamma"], xs["beta"], x.eps, mb=16,
+                                           nthreads=nt)
+        tc = time.perf_counter() - t1
+        out["cpu_baseline"] = {"value": tokens / tc, "unit": "tokens/s", "cores": nt,
+                               "kind": "oracle",
+                               "sample": f"full workload (B={B}, H={H}, L={L}), fp64 primal "
+                                         f"form, {nt} threads over (n,h), {tc:.2f} s"}
+        # parity of the timed launch's outputs against the oracle (S18 metric)
+        def rel(g, r):
+            g = g.detach().float().cpu().numpy().reshape(B * H, -1).astype(np.float64)
+            r = r.reshape(B * H, -1)
+            return float((np.abs(g - r).max(1) / np.abs(r).max(1)).max())
+        out["parity_vs_oracle"] = {"O": rel(O, ro), "W_out": rel(Wo, rW), "b_out": rel(bo, rb),
+                                   "tol": 2e-2}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

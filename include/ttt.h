@@ -1,0 +1,141 @@
+/*
+ * ttt.h -- C ABI of libttt.so: the TTT layer inner loop on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Source pages (citation key):
+ *   [D] damodev.csdn.net TTT deep-dive: §3.1 update/apply equation, §4.1
+ *       mini-batch TTT, §4.2 inner-loop excerpt (reconstruction target
+ *       XV - XK, forward XK W + b, fused LN + L2 backward, dual-form state
+ *       update), §4.3 fast-weight shapes [heads, d, d] and [heads, 1, d],
+ *       §5.2 the fast-weight cache used for decode.
+ *   [Y] lryc.cn "测试时学习（TTT）" article: §2.1 LN-residual output
+ *       f(x) = x + LN(f_res(x)) and the d -> 4d GELU -> d MLP, §2.2 the
+ *       per-token learning-rate gate, §2.4 mini-batch b = 16 and the dual form.
+ *   [X] xiaohu.ai TTT summary: mini-batch TTT and the dual form.
+ *
+ * Computation (per independent sequence (n,h), tokens t = 0..L-1, chunks of
+ * `mb` tokens aligned at t = 0, the last chunk possibly shorter):
+ *   for each chunk, at the chunk-start state (W, b):
+ *     G_s = d/dz [ 1/2 || LN_{gamma,beta}(z) - (xv_s - xk_s) ||^2 ] at
+ *           z = xk_s W + b                                   ([D] §4.2)
+ *   then for each token t of the chunk, in order:
+ *     W <- W - eta_t xk_t^T G_t ;  b <- b - eta_t G_t        ([D] §3.1, §4.2)
+ *     o_t = xq_t + LN_{gamma,beta}(xq_t W + b)               ([Y] §2.1)
+ *   W_out, b_out = the state after the last token.
+ * LN uses the biased variance over the d features with ln_eps inside the
+ * square root; the same gamma/beta serve the loss and the output. Row-vector
+ * convention: W[i][j] maps input feature i to output feature j.
+ * The MLP variant replaces x W + b by GELU(x W1 + b1) W2 + b2 (exact GELU,
+ * hidden width 4d) and updates W1, b1, W2, b2 with their gradients.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers to row-major contiguous arrays owned
+ *     by the caller. The library never allocates, frees or synchronises; each
+ *     call enqueues its kernel(s) on `stream` and returns.
+ *   - Validation runs on the host before any HIP call. A pointer may be NULL
+ *     only when the array it addresses has zero elements (or is documented as
+ *     optional). Every pointer must be aligned to its element size; the
+ *     prefill entry points also need 16-byte alignment of XQ, XK, XV, O and
+ *     the state arrays (their kernels use 16-byte vector accesses).
+ *   - Return value: TTT_OK (0) or a negative TTT_E_* code; ttt_last_error()
+ *     then returns a message (thread-local, valid until the next call on the
+ *     same thread). Faults inside a kernel surface at the caller's next
+ *     synchronisation of `stream`.
+ *   - Calls on one stream are ordered; calls that write the same buffers on
+ *     different streams race.
+ */
+#ifndef TTT_H
+#define TTT_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TTT_OK 0
+#define TTT_E_NULL (-1)  /* a required pointer is NULL                          */
+#define TTT_E_SHAPE (-2) /* negative size, or unsupported d / mb               */
+#define TTT_E_DTYPE (-3) /* io is not TTT_F32 / TTT_BF16                       */
+#define TTT_E_ALIGN (-4) /* a pointer is not aligned as required               */
+#define TTT_E_ALIAS (-5) /* an output overlaps an input or another output      */
+#define TTT_E_HIP (-6)   /* the kernel launch failed                           */
+
+/* Storage type of XQ/XK/XV and O. State, eta and LN parameters are fp32. */
+typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
+
+/*
+ * TTT-Linear prefill over [B,H,L,d] inputs, mini-batch form, computed in the
+ * dual form ([D] §4.2 dual branch; [X]; [Y] §2.4).
+ *   B, H >= 0, L >= 0; d in {16, 64}; 1 <= mb <= 16. L need not be a multiple
+ *   of mb: the last chunk is then shorter.
+ *   io       : storage type of XQ, XK, XV, O.
+ *   XQ,XK,XV : [B,H,L,d] io.         eta : [B,H,L] fp32 per-token rate
+ *              (already gated, e.g. eta_base * sigmoid(theta_lr . x), [Y] §2.2).
+ *   W0, b0   : fp32, [H,d,d] and [H,d] shared by every n when w0_batched == 0
+ *              (the per-head parameter of [D] §4.3), else [B,H,d,d], [B,H,d].
+ *   ln_gamma, ln_beta : [H,d] fp32.
+ *   O        : [B,H,L,d] io, written.  Must not overlap any other argument.
+ *   W_out, b_out : [B,H,d,d], [B,H,d] fp32, the final state; optional (NULL
+ *              skips the store). With w0_batched == 1 they may be exactly
+ *              W0 / b0 (in-place resume); any other overlap is TTT_E_ALIAS.
+ * Numerics: state and accumulation in fp32; products with the state use
+ * split-bf16 MFMA operands on the bf16 path.
+ */
+int ttt_linear_forward(int B, int H, int L, int d, int mb, int io, float ln_eps,
+                       const void *XQ, const void *XK, const void *XV, const float *eta,
+                       const float *W0, const float *b0, int w0_batched,
+                       const float *ln_gamma, const float *ln_beta, void *O,
+                       float *W_out, float *b_out, hipStream_t stream);
+
+/*
+ * TTT-MLP prefill ([Y] §2.1: f_res(x) = GELU(x W1 + b1) W2 + b2, hidden m = 4d,
+ * exact GELU x * Phi(x)), mini-batch form as above.
+ *   d = 64 (m = 256); 1 <= mb <= 16.
+ *   W1_0 [.,H,d,m], b1_0 [.,H,m], W2_0 [.,H,m,d], b2_0 [.,H,d] fp32, where
+ *   "." is absent (shared over B) when w0_batched == 0, else B.
+ *   Outputs W1_out [B,H,d,m], b1_out [B,H,m], W2_out [B,H,m,d], b2_out [B,H,d]
+ *   are optional as a group (all NULL or all non-NULL) and may equal the
+ *   corresponding inputs when w0_batched == 1.
+ */
+int ttt_mlp_forward(int B, int H, int L, int d, int mb, int io, float ln_eps,
+                    const void *XQ, const void *XK, const void *XV, const float *eta,
+                    const float *W1_0, const float *b1_0, const float *W2_0,
+                    const float *b2_0, int w0_batched, const float *ln_gamma,
+                    const float *ln_beta, void *O, float *W1_out, float *b1_out,
+                    float *W2_out, float *b2_out, hipStream_t stream);
+
+/*
+ * One single-token TTT-Linear step (b = 1, primal form) for B x H independent
+ * states held in place -- the fast-weight cache of [D] §5.2:
+ *   G = lnbwd(xk W + b, xv - xk);  W <- W - eta xk^T G;  b <- b - eta G;
+ *   o = xq + LN(xq W + b)   (with the updated W, b).
+ *   d in {16, 64}.  xq, xk, xv : [B,H,d] io;  eta : [B,H] fp32;
+ *   W [B,H,d,d], b [B,H,d] fp32, read and overwritten;  o [B,H,d] io.
+ */
+int ttt_decode_step(int B, int H, int d, int io, float ln_eps, const void *xq,
+                    const void *xk, const void *xv, const float *eta, float *W, float *b,
+                    const float *ln_gamma, const float *ln_beta, void *o,
+                    hipStream_t stream);
+
+/*
+ * The fused layer-norm + L2 backward step on its own ([D] §4.2), row-wise:
+ *   G[r] = d/dz [ 1/2 || LN_{gamma,beta}(z) - target[r] ||^2 ] at z = Z[r].
+ *   rows >= 0; d in {16, 32, 64}. Z, target, G : [rows,d] fp32;
+ *   gamma, beta : [d] fp32. G must not overlap Z or target.
+ */
+int ttt_ln_l2_bwd(int rows, int d, const float *Z, const float *target,
+                  const float *ln_gamma, const float *ln_beta, float ln_eps, float *G,
+                  hipStream_t stream);
+
+/* Message for the last non-zero return on this thread ("" if none). */
+const char *ttt_last_error(void);
+
+/* ABI version (incremented on incompatible changes). */
+int ttt_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTT_H */

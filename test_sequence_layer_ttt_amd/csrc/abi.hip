@@ -1,0 +1,232 @@
+// extern "C" entry points of libttt.so (declared and documented in ttt.h).
+// Every argument is validated on the host before any HIP call; the kernels
+// are then enqueued on the caller's stream. Nothing here allocates or
+// synchronises.
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <climits>
+
+#include "launch.hpp"
+#include "ttt.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return TTT_OK;
+}
+
+struct Buf {
+    const void *p;
+    size_t bytes;
+    const char *name;
+    bool optional;
+    unsigned align;  // required alignment in bytes
+};
+
+bool mul_ok(size_t a, size_t b, size_t *out) { return !__builtin_mul_overflow(a, b, out); }
+
+// product of non-negative ints as bytes; false on overflow
+bool nbytes(size_t *out, std::initializer_list<size_t> dims) {
+    size_t r = 1;
+    for (size_t v : dims)
+        if (!mul_ok(r, v, &r)) return false;
+    *out = r;
+    return true;
+}
+
+int check_bufs(const Buf *b, int n) {
+    for (int i = 0; i < n; ++i) {
+        if (!b[i].p) {
+            if (b[i].bytes && !b[i].optional)
+                return fail(TTT_E_NULL, "%s is NULL (%zu bytes expected)", b[i].name, b[i].bytes);
+            continue;
+        }
+        if (reinterpret_cast<uintptr_t>(b[i].p) & (b[i].align - 1))
+            return fail(TTT_E_ALIGN, "%s (%p) is not %u-byte aligned", b[i].name, b[i].p, b[i].align);
+    }
+    return TTT_OK;
+}
+
+bool overlaps(const Buf &a, const Buf &b) {
+    if (!a.p || !b.p || !a.bytes || !b.bytes) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Outputs must not overlap any other buffer, except that an output may be
+// exactly the same buffer as its paired input (`same_ok[out] == in`).
+int check_alias(const Buf *outs, int nout, const Buf *ins, int nin, const int *pair) {
+    for (int o = 0; o < nout; ++o) {
+        for (int i = 0; i < nin; ++i) {
+            if (!overlaps(outs[o], ins[i])) continue;
+            if (pair && pair[o] == i && outs[o].p == ins[i].p && outs[o].bytes == ins[i].bytes) continue;
+            return fail(TTT_E_ALIAS, "%s overlaps %s", outs[o].name, ins[i].name);
+        }
+        for (int o2 = o + 1; o2 < nout; ++o2)
+            if (overlaps(outs[o], outs[o2]))
+                return fail(TTT_E_ALIAS, "%s overlaps %s", outs[o].name, outs[o2].name);
+    }
+    return TTT_OK;
+}
+
+int check_common(int B, int H, int L, int mb, int io) {
+    if (B < 0 || H < 0 || L < 0) return fail(TTT_E_SHAPE, "negative size (B=%d H=%d L=%d)", B, H, L);
+    if (io != TTT_F32 && io != TTT_BF16) return fail(TTT_E_DTYPE, "io dtype %d is not TTT_F32/TTT_BF16", io);
+    if (mb < 1 || mb > 16) return fail(TTT_E_SHAPE, "mini-batch size %d not in [1, 16]", mb);
+    if (static_cast<long long>(B) * H > INT_MAX) return fail(TTT_E_SHAPE, "B*H = %lld too large", static_cast<long long>(B) * H);
+    return TTT_OK;
+}
+
+int launched(hipError_t e) {
+    if (e != hipSuccess) return fail(TTT_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int ttt_version(void) { return 1; }
+
+const char *ttt_last_error(void) { return g_err; }
+
+int ttt_ln_l2_bwd(int rows, int d, const float *Z, const float *target, const float *ln_gamma,
+                  const float *ln_beta, float ln_eps, float *G, hipStream_t stream) {
+    if (rows < 0) return fail(TTT_E_SHAPE, "rows = %d < 0", rows);
+    if (d != 16 && d != 32 && d != 64) return fail(TTT_E_SHAPE, "d = %d not in {16, 32, 64}", d);
+    size_t rb;
+    if (!nbytes(&rb, {static_cast<size_t>(rows), static_cast<size_t>(d), sizeof(float)}))
+        return fail(TTT_E_SHAPE, "rows*d overflows");
+    const Buf in[] = {{Z, rb, "Z", false, 4}, {target, rb, "target", false, 4},
+                      {ln_gamma, d * sizeof(float), "ln_gamma", false, 4},
+                      {ln_beta, d * sizeof(float), "ln_beta", false, 4}};
+    const Buf out[] = {{G, rb, "G", false, 4}};
+    int st;
+    if ((st = check_bufs(in, 4)) || (st = check_bufs(out, 1))) return st;
+    if ((st = check_alias(out, 1, in, 4, nullptr))) return st;
+    return launched(ttt::launch_ln_l2_bwd(rows, d, Z, target, ln_gamma, ln_beta, ln_eps, G, stream));
+}
+
+int ttt_linear_forward(int B, int H, int L, int d, int mb, int io, float ln_eps,
+                       const void *XQ, const void *XK, const void *XV, const float *eta,
+                       const float *W0, const float *b0, int w0_batched,
+                       const float *ln_gamma, const float *ln_beta, void *O,
+                       float *W_out, float *b_out, hipStream_t stream) {
+    int st;
+    if ((st = check_common(B, H, L, mb, io))) return st;
+    if (d != 16 && d != 64) return fail(TTT_E_SHAPE, "d = %d not in {16, 64}", d);
+    const size_t es = io == TTT_BF16 ? 2 : 4;
+    const size_t nb = w0_batched ? static_cast<size_t>(B) : 1;
+    size_t xb, eb, wb, bb, ob_w, ob_b;
+    if (!nbytes(&xb, {size_t(B), size_t(H), size_t(L), size_t(d), es}) ||
+        !nbytes(&eb, {size_t(B), size_t(H), size_t(L), sizeof(float)}) ||
+        !nbytes(&wb, {nb, size_t(H), size_t(d), size_t(d), sizeof(float)}) ||
+        !nbytes(&bb, {nb, size_t(H), size_t(d), sizeof(float)}) ||
+        !nbytes(&ob_w, {size_t(B), size_t(H), size_t(d), size_t(d), sizeof(float)}) ||
+        !nbytes(&ob_b, {size_t(B), size_t(H), size_t(d), sizeof(float)}))
+        return fail(TTT_E_SHAPE, "sizes overflow");
+    const size_t pb = static_cast<size_t>(H) * d * sizeof(float);
+    const Buf in[] = {{XQ, xb, "XQ", false, 16}, {XK, xb, "XK", false, 16},
+                      {XV, xb, "XV", false, 16}, {eta, eb, "eta", false, 4},
+                      {W0, wb, "W0", false, 16}, {b0, bb, "b0", false, 16},
+                      {ln_gamma, pb, "ln_gamma", false, 4}, {ln_beta, pb, "ln_beta", false, 4}};
+    const Buf out[] = {{O, xb, "O", false, 16}, {W_out, ob_w, "W_out", true, 16},
+                       {b_out, ob_b, "b_out", true, 16}};
+    if ((st = check_bufs(in, 8)) || (st = check_bufs(out, 3))) return st;
+    // W_out may be exactly W0 (and b_out exactly b0) when the state is per batch.
+    const int pair[] = {-1, w0_batched ? 4 : -1, w0_batched ? 5 : -1};
+    if ((st = check_alias(out, 3, in, 8, pair))) return st;
+    if (B * H == 0) return ok();
+
+    ttt::LinearArgs a{B, H, L, d, mb, io, ln_eps, XQ, XK, XV, eta, W0, b0, w0_batched ? 1 : 0,
+                      ln_gamma, ln_beta, O, W_out, b_out};
+    if (ttt::linear_mfma_supported(a)) return launched(ttt::launch_linear_mfma(a, stream));
+    return launched(ttt::launch_linear_valu(a, stream));
+}
+
+int ttt_mlp_forward(int B, int H, int L, int d, int mb, int io, float ln_eps,
+                    const void *XQ, const void *XK, const void *XV, const float *eta,
+                    const float *W1_0, const float *b1_0, const float *W2_0,
+                    const float *b2_0, int w0_batched, const float *ln_gamma,
+                    const float *ln_beta, void *O, float *W1_out, float *b1_out,
+                    float *W2_out, float *b2_out, hipStream_t stream) {
+    int st;
+    if ((st = check_common(B, H, L, mb, io))) return st;
+    if (d != 64) return fail(TTT_E_SHAPE, "d = %d: the MLP supports d = 64 only", d);
+    const int nout = (W1_out != nullptr) + (b1_out != nullptr) + (W2_out != nullptr) + (b2_out != nullptr);
+    if (nout != 0 && nout != 4) return fail(TTT_E_NULL, "state outputs must be all NULL or all non-NULL");
+    const size_t es = io == TTT_BF16 ? 2 : 4, m = 4 * static_cast<size_t>(d);
+    const size_t nb = w0_batched ? static_cast<size_t>(B) : 1;
+    size_t xb, eb, w1b, b1b, w2b, b2b, o1, o2, o3, o4;
+    if (!nbytes(&xb, {size_t(B), size_t(H), size_t(L), size_t(d), es}) ||
+        !nbytes(&eb, {size_t(B), size_t(H), size_t(L), sizeof(float)}) ||
+        !nbytes(&w1b, {nb, size_t(H), size_t(d), m, sizeof(float)}) ||
+        !nbytes(&b1b, {nb, size_t(H), m, sizeof(float)}) ||
+        !nbytes(&w2b, {nb, size_t(H), m, size_t(d), sizeof(float)}) ||
+        !nbytes(&b2b, {nb, size_t(H), size_t(d), sizeof(float)}) ||
+        !nbytes(&o1, {size_t(B), size_t(H), size_t(d), m, sizeof(float)}) ||
+        !nbytes(&o2, {size_t(B), size_t(H), m, sizeof(float)}) ||
+        !nbytes(&o3, {size_t(B), size_t(H), m, size_t(d), sizeof(float)}) ||
+        !nbytes(&o4, {size_t(B), size_t(H), size_t(d), sizeof(float)}))
+        return fail(TTT_E_SHAPE, "sizes overflow");
+    const size_t pb = static_cast<size_t>(H) * d * sizeof(float);
+    const Buf in[] = {{XQ, xb, "XQ", false, 16}, {XK, xb, "XK", false, 16},
+                      {XV, xb, "XV", false, 16}, {eta, eb, "eta", false, 4},
+                      {W1_0, w1b, "W1_0", false, 16}, {b1_0, b1b, "b1_0", false, 16},
+                      {W2_0, w2b, "W2_0", false, 16}, {b2_0, b2b, "b2_0", false, 16},
+                      {ln_gamma, pb, "ln_gamma", false, 4}, {ln_beta, pb, "ln_beta", false, 4}};
+    const Buf out[] = {{O, xb, "O", false, 16}, {W1_out, o1, "W1_out", true, 16},
+                       {b1_out, o2, "b1_out", true, 16}, {W2_out, o3, "W2_out", true, 16},
+                       {b2_out, o4, "b2_out", true, 16}};
+    if ((st = check_bufs(in, 10)) || (st = check_bufs(out, 5))) return st;
+    const int pair[] = {-1, w0_batched ? 4 : -1, w0_batched ? 5 : -1, w0_batched ? 6 : -1,
+                        w0_batched ? 7 : -1};
+    if ((st = check_alias(out, 5, in, 10, pair))) return st;
+    if (B * H == 0) return ok();
+    ttt::MLPArgs a{B, H, L, d, mb, io, ln_eps, XQ, XK, XV, eta, W1_0, b1_0, W2_0, b2_0,
+                   w0_batched ? 1 : 0, ln_gamma, ln_beta, O, W1_out, b1_out, W2_out, b2_out};
+    return launched(ttt::launch_mlp(a, stream));
+}
+
+int ttt_decode_step(int B, int H, int d, int io, float ln_eps, const void *xq,
+                    const void *xk, const void *xv, const float *eta, float *W, float *b,
+                    const float *ln_gamma, const float *ln_beta, void *o,
+                    hipStream_t stream) {
+    int st;
+    if ((st = check_common(B, H, 1, 1, io))) return st;
+    if (d != 16 && d != 64) return fail(TTT_E_SHAPE, "d = %d not in {16, 64}", d);
+    const size_t es = io == TTT_BF16 ? 2 : 4;
+    size_t xb, eb, wb, bb;
+    if (!nbytes(&xb, {size_t(B), size_t(H), size_t(d), es}) ||
+        !nbytes(&eb, {size_t(B), size_t(H), sizeof(float)}) ||
+        !nbytes(&wb, {size_t(B), size_t(H), size_t(d), size_t(d), sizeof(float)}) ||
+        !nbytes(&bb, {size_t(B), size_t(H), size_t(d), sizeof(float)}))
+        return fail(TTT_E_SHAPE, "sizes overflow");
+    const size_t pb = static_cast<size_t>(H) * d * sizeof(float);
+    const unsigned ea = static_cast<unsigned>(es);
+    const Buf in[] = {{xq, xb, "xq", false, ea}, {xk, xb, "xk", false, ea},
+                      {xv, xb, "xv", false, ea}, {eta, eb, "eta", false, 4},
+                      {ln_gamma, pb, "ln_gamma", false, 4}, {ln_beta, pb, "ln_beta", false, 4}};
+    const Buf out[] = {{W, wb, "W", false, 4}, {b, bb, "b", false, 4}, {o, xb, "o", false, ea}};
+    if ((st = check_bufs(in, 6)) || (st = check_bufs(out, 3))) return st;
+    if ((st = check_alias(out, 3, in, 6, nullptr))) return st;
+    if (B * H == 0) return ok();
+    ttt::DecodeArgs a{B, H, d, io, ln_eps, xq, xk, xv, eta, W, b, ln_gamma, ln_beta, o};
+    return launched(ttt::launch_decode(a, stream));
+}
+
+}  // extern "C"

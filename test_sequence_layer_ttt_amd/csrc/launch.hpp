@@ -1,0 +1,50 @@
+// Internal launchers (host side) of libttt.so. Arguments are validated by the
+// C ABI before these are called; each enqueues on `stream` and returns the
+// launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace ttt {
+
+struct LinearArgs {
+    int B, H, L, d, mb, io;
+    float eps;
+    const void *XQ, *XK, *XV;
+    const float *eta, *W0, *b0;
+    int w0_batched;
+    const float *gamma, *beta;
+    void *O;
+    float *W_out, *b_out;
+};
+
+struct MLPArgs {
+    int B, H, L, d, mb, io;
+    float eps;
+    const void *XQ, *XK, *XV;
+    const float *eta, *W1, *b1, *W2, *b2;
+    int w0_batched;
+    const float *gamma, *beta;
+    void *O;
+    float *W1_out, *b1_out, *W2_out, *b2_out;
+};
+
+struct DecodeArgs {
+    int B, H, d, io;
+    float eps;
+    const void *xq, *xk, *xv;
+    const float *eta;
+    float *W, *b;
+    const float *gamma, *beta;
+    void *o;
+};
+
+hipError_t launch_ln_l2_bwd(int rows, int d, const float *Z, const float *T, const float *gamma,
+                            const float *beta, float eps, float *G, hipStream_t stream);
+hipError_t launch_linear_valu(const LinearArgs &a, hipStream_t stream);
+bool linear_mfma_supported(const LinearArgs &a);
+hipError_t launch_linear_mfma(const LinearArgs &a, hipStream_t stream);
+hipError_t launch_mlp(const MLPArgs &a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
+}  // namespace ttt

@@ -1,0 +1,163 @@
+"""Python binding of libttt.so with the C ABI's names.
+
+Argument marshalling only: checks device / dtype / shape / contiguity of
+torch tensors, then passes raw device pointers and the current HIP stream.
+Every step of the computation runs in the library's kernels.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import TTT_BF16, TTT_F32, TTTError  # noqa: F401
+
+_IO = {torch.float32: TTT_F32, torch.bfloat16: TTT_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    return t.data_ptr() or None
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def ttt_linear_forward(XQ, XK, XV, eta, W0, b0, ln_gamma, ln_beta, O=None, W_out=None,
+                       b_out=None, mb: int = 16, ln_eps: float = 1e-6, stream=None):
+    """TTT-Linear prefill. XQ/XK/XV/O [B,H,L,d] (fp32 or bf16); eta [B,H,L];
+    W0 [H,d,d] (shared over B) or [B,H,d,d]; b0 [H,d] or [B,H,d]; gamma/beta [H,d].
+    Returns (O, W_out, b_out); outputs are allocated when not given."""
+    B, H, L, d = XQ.shape
+    io = _IO.get(XQ.dtype)
+    if io is None:
+        raise TypeError(f"XQ dtype {XQ.dtype} not supported")
+    batched = W0.dim() == 4
+    for t, n in ((XQ, "XQ"), (XK, "XK"), (XV, "XV")):
+        _need(t, n, (B, H, L, d), XQ.dtype)
+    _need(eta, "eta", (B, H, L), torch.float32)
+    _need(W0, "W0", ((B,) if batched else ()) + (H, d, d), torch.float32)
+    _need(b0, "b0", ((B,) if batched else ()) + (H, d), torch.float32)
+    _need(ln_gamma, "ln_gamma", (H, d), torch.float32)
+    _need(ln_beta, "ln_beta", (H, d), torch.float32)
+    if O is None:
+        O = torch.empty_like(XQ)
+    if W_out is None:
+        W_out = torch.empty((B, H, d, d), device=XQ.device, dtype=torch.float32)
+    if b_out is None:
+        b_out = torch.empty((B, H, d), device=XQ.device, dtype=torch.float32)
+    _need(O, "O", (B, H, L, d), XQ.dtype)
+    _need(W_out, "W_out", (B, H, d, d), torch.float32)
+    _need(b_out, "b_out", (B, H, d), torch.float32)
+    lib = _lib.load()
+    _lib.check(lib.ttt_linear_forward(B, H, L, d, mb, io, ln_eps, _ptr(XQ), _ptr(XK), _ptr(XV),
+                                      _ptr(eta), _ptr(W0), _ptr(b0), int(batched),
+                                      _ptr(ln_gamma), _ptr(ln_beta), _ptr(O), _ptr(W_out),
+                                      _ptr(b_out), _stream(stream)))
+    return O, W_out, b_out
+
+
+def ttt_mlp_forward(XQ, XK, XV, eta, W1, b1, W2, b2, ln_gamma, ln_beta, O=None, outs=None,
+                    mb: int = 16, ln_eps: float = 1e-6, stream=None):
+    """TTT-MLP prefill (d = 64, hidden 4d). W1 [.,H,d,4d], b1 [.,H,4d],
+    W2 [.,H,4d,d], b2 [.,H,d] with "." = B when per batch. Returns
+    (O, W1_out, b1_out, W2_out, b2_out)."""
+    B, H, L, d = XQ.shape
+    m = 4 * d
+    io = _IO.get(XQ.dtype)
+    if io is None:
+        raise TypeError(f"XQ dtype {XQ.dtype} not supported")
+    batched = W1.dim() == 4
+    pre = (B,) if batched else ()
+    for t, n in ((XQ, "XQ"), (XK, "XK"), (XV, "XV")):
+        _need(t, n, (B, H, L, d), XQ.dtype)
+    _need(eta, "eta", (B, H, L), torch.float32)
+    _need(W1, "W1", pre + (H, d, m), torch.float32)
+    _need(b1, "b1", pre + (H, m), torch.float32)
+    _need(W2, "W2", pre + (H, m, d), torch.float32)
+    _need(b2, "b2", pre + (H, d), torch.float32)
+    _need(ln_gamma, "ln_gamma", (H, d), torch.float32)
+    _need(ln_beta, "ln_beta", (H, d), torch.float32)
+    if O is None:
+        O = torch.empty_like(XQ)
+    if outs is None:
+        kw = dict(device=XQ.device, dtype=torch.float32)
+        outs = (torch.empty((B, H, d, m), **kw), torch.empty((B, H, m), **kw),
+                torch.empty((B, H, m, d), **kw), torch.empty((B, H, d), **kw))
+    _need(O, "O", (B, H, L, d), XQ.dtype)
+    for t, n, s in zip(outs, ("W1_out", "b1_out", "W2_out", "b2_out"),
+                       ((B, H, d, m), (B, H, m), (B, H, m, d), (B, H, d))):
+        _need(t, n, s, torch.float32)
+    lib = _lib.load()
+    _lib.check(lib.ttt_mlp_forward(B, H, L, d, mb, io, ln_eps, _ptr(XQ), _ptr(XK), _ptr(XV),
+                                   _ptr(eta), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
+                                   int(batched), _ptr(ln_gamma), _ptr(ln_beta), _ptr(O),
+                                   *(_ptr(t) for t in outs), _stream(stream)))
+    return (O,) + tuple(outs)
+
+
+def ttt_decode_step(xq, xk, xv, eta, W, b, ln_gamma, ln_beta, o=None, ln_eps: float = 1e-6,
+                    stream=None):
+    """One b = 1 step on B x H states, updating W [B,H,d,d] and b [B,H,d] in
+    place. xq/xk/xv/o [B,H,d]; eta [B,H]. Returns o."""
+    B, H, d = xq.shape
+    io = _IO.get(xq.dtype)
+    if io is None:
+        raise TypeError(f"xq dtype {xq.dtype} not supported")
+    for t, n in ((xq, "xq"), (xk, "xk"), (xv, "xv")):
+        _need(t, n, (B, H, d), xq.dtype)
+    _need(eta, "eta", (B, H), torch.float32)
+    _need(W, "W", (B, H, d, d), torch.float32)
+    _need(b, "b", (B, H, d), torch.float32)
+    _need(ln_gamma, "ln_gamma", (H, d), torch.float32)
+    _need(ln_beta, "ln_beta", (H, d), torch.float32)
+    if o is None:
+        o = torch.empty_like(xq)
+    _need(o, "o", (B, H, d), xq.dtype)
+    lib = _lib.load()
+    _lib.check(lib.ttt_decode_step(B, H, d, io, ln_eps, _ptr(xq), _ptr(xk), _ptr(xv),
+                                   _ptr(eta), _ptr(W), _ptr(b), _ptr(ln_gamma), _ptr(ln_beta),
+                                   _ptr(o), _stream(stream)))
+    return o
+
+
+def ttt_ln_l2_bwd(Z, target, ln_gamma, ln_beta, G=None, ln_eps: float = 1e-6, stream=None):
+    """Row-wise fused LN + L2 backward. Z, target, G [rows,d] fp32; gamma/beta [d]."""
+    rows, d = Z.shape
+    _need(Z, "Z", (rows, d), torch.float32)
+    _need(target, "target", (rows, d), torch.float32)
+    _need(ln_gamma, "ln_gamma", (d,), torch.float32)
+    _need(ln_beta, "ln_beta", (d,), torch.float32)
+    if G is None:
+        G = torch.empty_like(Z)
+    _need(G, "G", (rows, d), torch.float32)
+    lib = _lib.load()
+    _lib.check(lib.ttt_ln_l2_bwd(rows, d, _ptr(Z), _ptr(target), _ptr(ln_gamma), _ptr(ln_beta),
+                                 ln_eps, _ptr(G), _stream(stream)))
+    return G
+
+
+def ttt_version() -> int:
+    return _lib.load().ttt_version()
+
+
+def ttt_last_error() -> str:
+    return _lib.load().ttt_last_error().decode()

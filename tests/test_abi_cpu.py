@@ -1,0 +1,130 @@
+"""libttt.so loads, exports every function include/ttt.h declares, and its host
+validation rejects bad arguments before any HIP call (no GPU needed: the
+pointers below are never dereferenced)."""
+import ctypes
+
+import pytest
+
+from test_sequence_layer_ttt_amd import _lib
+
+FAKE = 0x10000          # 16-byte aligned, never dereferenced by the host checks
+FAKE2 = 0x20000000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _lib.header_functions()
+    assert set(names) >= {"ttt_linear_forward", "ttt_mlp_forward", "ttt_decode_step",
+                          "ttt_ln_l2_bwd", "ttt_last_error", "ttt_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_version(lib):
+    assert lib.ttt_version() == 1
+
+
+def _lin(lib, B=1, H=1, L=16, d=64, mb=16, io=1, ptrs=None, batched=0, W_out=None, b_out=None,
+         O=None):
+    # distinct non-overlapping fake buffers, 1 MiB apart
+    p = ptrs or [FAKE + i * (1 << 20) for i in range(8)]
+    Wo = W_out if W_out is not None else FAKE + 9 * (1 << 20)
+    bo = b_out if b_out is not None else FAKE + 10 * (1 << 20)
+    Oo = O if O is not None else FAKE + 11 * (1 << 20)
+    return lib.ttt_linear_forward(B, H, L, d, mb, io, 1e-6, p[0], p[1], p[2], p[3], p[4], p[5],
+                                  batched, p[6], p[7], Oo, Wo, bo, None)
+
+
+def test_linear_rejects_negative_sizes(lib):
+    assert _lin(lib, B=-1) == _lib.TTT_E_SHAPE
+    assert _lin(lib, L=-3) == _lib.TTT_E_SHAPE
+    assert "negative" in lib.ttt_last_error().decode()
+
+
+def test_linear_rejects_unsupported_d_and_mb(lib):
+    assert _lin(lib, d=48) == _lib.TTT_E_SHAPE
+    assert _lin(lib, mb=0) == _lib.TTT_E_SHAPE
+    assert _lin(lib, mb=17) == _lib.TTT_E_SHAPE
+
+
+def test_linear_rejects_bad_dtype(lib):
+    assert _lin(lib, io=7) == _lib.TTT_E_DTYPE
+
+
+def test_linear_rejects_null(lib):
+    p = [FAKE + i * (1 << 20) for i in range(8)]
+    p[2] = 0
+    assert _lin(lib, ptrs=p) == _lib.TTT_E_NULL
+    assert "XV" in lib.ttt_last_error().decode()
+
+
+def test_linear_rejects_misaligned(lib):
+    p = [FAKE + i * (1 << 20) for i in range(8)]
+    p[0] += 4
+    assert _lin(lib, ptrs=p) == _lib.TTT_E_ALIGN
+
+
+def test_linear_rejects_aliasing(lib):
+    p = [FAKE + i * (1 << 20) for i in range(8)]
+    assert _lin(lib, ptrs=p, O=p[1] + 64) == _lib.TTT_E_ALIAS
+    # W_out == W0 is only allowed with per-batch state
+    assert _lin(lib, ptrs=p, W_out=p[4]) == _lib.TTT_E_ALIAS
+    # partial overlap of W_out with W0 is never allowed
+    assert _lin(lib, ptrs=p, batched=1, W_out=p[4] + 16) == _lib.TTT_E_ALIAS
+    # W_out overlapping b_out
+    assert _lin(lib, ptrs=p, W_out=FAKE2, b_out=FAKE2 + 256) == _lib.TTT_E_ALIAS
+
+
+def test_linear_empty_batch_is_a_noop(lib):
+    # B*H == 0: every buffer is empty, NULL pointers are fine, nothing launched
+    # (per-head parameters W0, b0, gamma, beta are still [H, ...] and non-empty)
+    assert lib.ttt_linear_forward(0, 4, 16, 64, 16, 1, 1e-6, None, None, None, None, FAKE,
+                                  FAKE2, 0, FAKE2 + 4096, FAKE2 + 8192, None, None, None,
+                                  None) == _lib.TTT_OK
+
+
+def test_mlp_validation(lib):
+    p = [FAKE + i * (1 << 20) for i in range(16)]
+
+    def call(d=64, mb=16, outs=(p[11], p[12], p[13], p[14]), io=1):
+        return lib.ttt_mlp_forward(1, 1, 16, d, mb, io, 1e-6, p[0], p[1], p[2], p[3], p[4], p[5],
+                                   p[6], p[7], 0, p[8], p[9], p[10], *outs, None)
+
+    assert call(d=16) == _lib.TTT_E_SHAPE
+    assert call(mb=0) == _lib.TTT_E_SHAPE
+    assert call(io=2) == _lib.TTT_E_DTYPE
+    assert call(outs=(p[11], None, p[13], p[14])) == _lib.TTT_E_NULL
+    assert call(outs=(p[4], p[12], p[13], p[14])) == _lib.TTT_E_ALIAS
+
+
+def test_decode_validation(lib):
+    p = [FAKE + i * (1 << 20) for i in range(10)]
+    assert lib.ttt_decode_step(1, 1, 32, 1, 1e-6, *p[:9], None) == _lib.TTT_E_SHAPE
+    assert lib.ttt_decode_step(1, 1, 64, 1, 1e-6, p[0], p[1], p[2], p[3], p[0], p[5], p[6],
+                               p[7], p[8], None) == _lib.TTT_E_ALIAS
+    assert lib.ttt_decode_step(1, 1, 64, 1, 1e-6, p[0], 0, p[2], p[3], p[4], p[5], p[6], p[7],
+                               p[8], None) == _lib.TTT_E_NULL
+
+
+def test_ln_bwd_validation(lib):
+    assert lib.ttt_ln_l2_bwd(4, 48, FAKE, FAKE2, FAKE + 4096, FAKE + 8192, 1e-6,
+                             FAKE2 + (1 << 20), None) == _lib.TTT_E_SHAPE
+    assert lib.ttt_ln_l2_bwd(-1, 64, FAKE, FAKE2, FAKE + 4096, FAKE + 8192, 1e-6,
+                             FAKE2 + (1 << 20), None) == _lib.TTT_E_SHAPE
+    assert lib.ttt_ln_l2_bwd(4, 64, FAKE, FAKE2, FAKE + 4096, FAKE + 8192, 1e-6, FAKE,
+                             None) == _lib.TTT_E_ALIAS
+    assert lib.ttt_ln_l2_bwd(0, 64, None, None, FAKE, FAKE + 4096, 1e-6, None, None) == _lib.TTT_OK
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    from test_sequence_layer_ttt_amd import ttt
+    x = torch.zeros(1, 1, 16, 64)
+    with pytest.raises(ValueError):
+        ttt.ttt_linear_forward(x, x, x, torch.zeros(1, 1, 16), torch.zeros(1, 64, 64),
+                               torch.zeros(1, 64), torch.ones(1, 64), torch.zeros(1, 64))

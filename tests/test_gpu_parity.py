@@ -1,0 +1,221 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs. Sizes range from oracle-quick cases that span several
+chunks and a ragged tail up to the five full workloads."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from test_sequence_layer_ttt_amd import gen, ttt
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+LIN_NAMES = ("O", "W_out", "b_out")
+MLP_NAMES = ("O", "W1", "b1", "W2", "b2")
+
+
+def _report(tag, err):
+    print(f"[parity] {tag}: " + " ".join(f"{k}={v:.3e}" for k, v in err.items()), flush=True)
+
+
+def _check_linear(x, tag, mb=None, tol=None):
+    got = P.linear_gpu(x, mb=mb)
+    ref = P.linear_oracle(x, mb=mb)
+    err = P.errors(got, ref, x.B * x.H, LIN_NAMES)
+    _report(tag, err)
+    tol = tol or P.TOL[x.io]
+    assert max(err.values()) <= tol, err
+    return got
+
+
+# ---------------------------------------------------------------------------
+# LN + L2 backward on its own
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("d", [16, 32, 64])
+@pytest.mark.parametrize("rows", [1, 17, 1000])
+def test_ln_l2_bwd(d, rows):
+    rng = np.random.default_rng(rows * 100 + d)
+    Z = (rng.standard_normal((rows, d)) * rng.uniform(0.1, 3, (rows, 1))
+         + rng.standard_normal((rows, 1))).astype(np.float32)
+    T = rng.standard_normal((rows, d)).astype(np.float32)
+    g = (1 + 0.2 * rng.standard_normal(d)).astype(np.float32)
+    b = (0.2 * rng.standard_normal(d)).astype(np.float32)
+    G = ttt.ttt_ln_l2_bwd(P.dev(Z), P.dev(T), P.dev(g), P.dev(b), ln_eps=1e-6)
+    torch.cuda.synchronize()
+    ref = oracle.ln_l2_bwd(Z, T, g, b, 1e-6)
+    err = np.abs(P.to_np(G) - ref).max(1) / np.abs(ref).max(1)
+    assert err.max() < 1e-5, err.max()
+
+
+# ---------------------------------------------------------------------------
+# TTT-Linear prefill
+# ---------------------------------------------------------------------------
+def test_linear_workload1_fp32():
+    _check_linear(gen.make_workload(1), "workload1 fp32 d16")
+
+
+@pytest.mark.parametrize("mb", [16, 5, 1])
+@pytest.mark.parametrize("d", [16, 64])
+def test_linear_fp32_ragged(d, mb):
+    x = gen.make_linear(200 + d + mb, 2, 3, 53, d, io="f32", ln_random=True, b_random=True)
+    _check_linear(x, f"fp32 d{d} mb{mb} L53")
+
+
+@pytest.mark.parametrize("num", [2, 3])
+def test_linear_bf16_small(num):
+    x = gen.make_workload(num, L=16 * 12 + 7, B=2, H=3)
+    _check_linear(x, f"workload{num} small L199")
+
+
+def test_linear_bf16_random_ln():
+    x = gen.make_linear(301, 2, 4, 16 * 20, 64, io="bf16", ln_random=True, b_random=True)
+    _check_linear(x, "bf16 random gamma/beta/b0")
+
+
+@pytest.mark.parametrize("L", [1, 15, 16, 17])
+def test_linear_bf16_short(L):
+    x = gen.make_linear(400 + L, 1, 2, L, 64, io="bf16")
+    _check_linear(x, f"bf16 L{L}")
+
+
+@pytest.mark.parametrize("num", [2, 3])
+def test_linear_full_workload(num):
+    x = gen.make_workload(num)
+    _check_linear(x, f"workload{num} full")
+
+
+def test_linear_full_workload5_prefill():
+    pre, _ = gen.make_workload(5, decode_steps=0)
+    _check_linear(pre, "workload5 prefill L32768")
+
+
+def test_linear_empty_sequence_passes_state():
+    x = gen.make_linear(500, 2, 3, 0, 64, io="bf16", b_random=True)
+    O, W, b = P.linear_gpu(x)
+    assert O.shape == (2, 3, 0, 64)
+    assert np.array_equal(W, np.broadcast_to(x.W0, W.shape))
+    assert np.array_equal(b, np.broadcast_to(x.b0, b.shape))
+
+
+def test_linear_in_place_resume():
+    """forward(L1) with the state updated in place, then forward(L2) from it,
+    matches the oracle's forward(L1 + L2)."""
+    x = gen.make_linear(510, 2, 3, 160, 64, io="bf16")
+    dt = torch.bfloat16
+    W = P.dev(np.broadcast_to(x.W0, (2, 3, 64, 64)))
+    b = P.dev(np.broadcast_to(x.b0, (2, 3, 64)))
+    outs = []
+    for s in (slice(0, 96), slice(96, 160)):
+        O, _, _ = ttt.ttt_linear_forward(P.dev(x.XQ[:, :, s], dt), P.dev(x.XK[:, :, s], dt),
+                                         P.dev(x.XV[:, :, s], dt), P.dev(x.eta[:, :, s]), W, b,
+                                         P.dev(x.gamma), P.dev(x.beta), W_out=W, b_out=b)
+        outs.append(P.to_np(O))
+    torch.cuda.synchronize()
+    ref = P.linear_oracle(x)
+    err = P.errors((np.concatenate(outs, 2), P.to_np(W), P.to_np(b)), ref, 6, LIN_NAMES)
+    _report("in-place resume", err)
+    assert max(err.values()) <= P.TOL["bf16"]
+
+
+def test_linear_bitwise_repeatable():
+    x = gen.make_workload(3, L=16 * 40, B=2, H=4)
+    a = P.linear_gpu(x)
+    b = P.linear_gpu(x)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+# ---------------------------------------------------------------------------
+# TTT-MLP prefill
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("io,mb", [("f32", 16), ("f32", 3), ("bf16", 16)])
+def test_mlp_small(io, mb):
+    x = gen.make_mlp(600 + mb, 2, 2, 16 * 5 + 9, 64, io=io, ln_random=True, b_random=True)
+    got = P.mlp_gpu(x, mb=mb)
+    ref = P.mlp_oracle(x, mb=mb)
+    err = P.errors(got, ref, 4, MLP_NAMES)
+    _report(f"mlp {io} mb{mb}", err)
+    assert max(err.values()) <= P.TOL[io], err
+
+
+def test_mlp_full_workload4():
+    x = gen.make_workload(4)
+    got = P.mlp_gpu(x)
+    ref = P.mlp_oracle(x)
+    err = P.errors(got, ref, x.B * x.H, MLP_NAMES)
+    _report("workload4 full", err)
+    assert max(err.values()) <= P.TOL["bf16"], err
+
+
+# ---------------------------------------------------------------------------
+# Decode (b = 1 primal step, state in place)
+# ---------------------------------------------------------------------------
+def _decode_run(W0, b0, dec, gamma, beta, eps):
+    dt = P.io_dtype(dec.io)
+    W = P.dev(W0)
+    b = P.dev(b0)
+    g, be = P.dev(gamma), P.dev(beta)
+    xq, xk, xv, et = (P.dev(dec.XQ, dt), P.dev(dec.XK, dt), P.dev(dec.XV, dt), P.dev(dec.eta))
+    outs = []
+    for s in range(dec.steps):
+        outs.append(ttt.ttt_decode_step(xq[s], xk[s], xv[s], et[s], W, b, g, be, ln_eps=eps))
+    torch.cuda.synchronize()
+    O = np.stack([P.to_np(o) for o in outs], 2)  # [B,H,steps,d]
+    return O, P.to_np(W), P.to_np(b)
+
+
+def _decode_oracle(W0, b0, dec, gamma, beta, eps):
+    tr = lambda a: np.ascontiguousarray(np.moveaxis(a, 0, 2))  # step-major -> [B,H,steps,...]
+    return oracle.linear_forward(tr(dec.XQ), tr(dec.XK), tr(dec.XV), tr(dec.eta), W0, b0,
+                                 gamma, beta, eps, mb=1, w0_batched=True)
+
+
+@pytest.mark.parametrize("io,d", [("f32", 16), ("f32", 64), ("bf16", 64)])
+def test_decode_small(io, d):
+    rng = np.random.default_rng(700 + d)
+    dec = gen.make_decode(rng, 20, 3, 2, d, io)
+    W0 = (0.3 * rng.standard_normal((3, 2, d, d))).astype(np.float32)
+    b0 = (0.1 * rng.standard_normal((3, 2, d))).astype(np.float32)
+    gamma = (1 + 0.1 * rng.standard_normal((2, d))).astype(np.float32)
+    beta = (0.1 * rng.standard_normal((2, d))).astype(np.float32)
+    got = _decode_run(W0, b0, dec, gamma, beta, 1e-6)
+    ref = _decode_oracle(W0, b0, dec, gamma, beta, 1e-6)
+    err = P.errors(got, ref, 6, LIN_NAMES)
+    _report(f"decode {io} d{d}", err)
+    assert max(err.values()) <= P.TOL[io], err
+
+
+def test_prefill_then_decode_matches_mixed_schedule():
+    """Prefill (mb = 16) then decode steps equals the oracle's single run with
+    chunk schedule [16]*k + [1]*n."""
+    x = gen.make_linear(720, 1, 4, 64 + 24, 64, io="bf16")
+    Lp = 64
+    sl = slice(0, Lp)
+    pre = gen.LinearInputs(1, 4, Lp, 64, "bf16", x.XQ[:, :, sl], x.XK[:, :, sl], x.XV[:, :, sl],
+                           x.eta[:, :, sl], x.W0, x.b0, x.gamma, x.beta)
+    _, W, b = P.linear_gpu(pre)
+    mv = lambda a: np.ascontiguousarray(np.moveaxis(a[:, :, Lp:], 2, 0))
+    dec = gen.DecodeInputs(24, 1, 4, 64, "bf16", mv(x.XQ), mv(x.XK), mv(x.XV), mv(x.eta))
+    O, Wd, bd = _decode_run(W.astype(np.float32), b.astype(np.float32), dec, x.gamma, x.beta, x.eps)
+    ref = P.linear_oracle(x, schedule=[16] * 4 + [1] * 24)
+    err = P.errors((O, Wd, bd), (ref[0][:, :, Lp:], ref[1], ref[2]), 4, LIN_NAMES)
+    _report("prefill+decode", err)
+    assert max(err.values()) <= P.TOL["bf16"], err
+
+
+def test_decode_full_workload5():
+    """Workload 5: prefill B=1, H=32, L=32768, then 1024 single-token steps for
+    64 independent sequences, each starting from a copy of the prefill state."""
+    pre, dec = gen.make_workload(5)
+    _, Wp, bp = P.linear_gpu(pre)
+    rW, rb = P.linear_oracle(pre)[1:]
+    W0 = np.broadcast_to(Wp[0], (64,) + Wp.shape[1:]).astype(np.float32)
+    b0 = np.broadcast_to(bp[0], (64,) + bp.shape[1:]).astype(np.float32)
+    got = _decode_run(W0, b0, dec, pre.gamma, pre.beta, pre.eps)
+    # the oracle continues from its own prefill state
+    ref = _decode_oracle(np.broadcast_to(rW[0], W0.shape), np.broadcast_to(rb[0], b0.shape),
+                         dec, pre.gamma, pre.beta, pre.eps)
+    err = P.errors(got, ref, 64 * 32, LIN_NAMES)
+    _report("workload5 decode 64x1024", err)
+    assert max(err.values()) <= P.TOL["bf16"], err
