@@ -71,6 +71,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 256 MiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the TTT inner "
@@ -82,6 +84,18 @@ def main():
     import torch
 
     from test_sequence_layer_ttt_amd import gen, ttt
+
+    if args.copy_calibration:
+        # Reference for the HBM byte counters: each launch reads and writes
+        # exactly 256 MiB.
+        n = 256 << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": n, "launches": max(1, args.steps)}))
+        return
 
     w = gen.WORKLOADS[WORKLOAD]
     x = gen.make_workload(WORKLOAD)

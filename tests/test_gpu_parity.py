@@ -219,3 +219,10 @@ def test_decode_full_workload5():
     err = P.errors(got, ref, 64 * 32, LIN_NAMES)
     _report("workload5 decode 64x1024", err)
     assert max(err.values()) <= P.TOL["bf16"], err
+
+
+@pytest.mark.parametrize("mb", [8, 13])
+def test_linear_bf16_other_minibatch(mb):
+    """Mini-batch sizes other than 16 (VALU path) with bf16 storage."""
+    x = gen.make_linear(800 + mb, 2, 3, 16 * 6 + 3, 64, io="bf16", ln_random=True)
+    _check_linear(x, f"bf16 mb{mb}", mb=mb)
