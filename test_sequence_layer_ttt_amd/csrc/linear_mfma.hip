@@ -1,31 +1,42 @@
 // TTT-Linear prefill, MFMA path: bf16 storage, d = 64, mini-batch b = 16.
 //
-// What is computed (per sequence, chunk of 16 tokens, state W, b at chunk
-// start) -- the dual form of the damodev.csdn.net TTT deep-dive §4.2 with the
-// LN-residual output of the lryc.cn TTT article §2.1:
-//   Z    = XK W + b ;  G = lnbwd(Z, XV - XK) ;  E = -eta * G      (per row)
-//   T    = tril(XQ XK^T + 1)                      (token s <= t)
-//   Zbar = XQ W + b + T E ;  O = XQ + LN(Zbar)
-//   W   += XK^T E ;  b += 1^T E
+// What is computed (per sequence; chunk c of 16 tokens; W_c, b_c = state at
+// the start of chunk c) -- the dual form of the damodev.csdn.net TTT
+// deep-dive §4.2 with the LN-residual output of the lryc.cn TTT article §2.1:
+//   Z_c    = XK_c W_c + b_c ;   E_c = -eta * lnbwd(Z_c, XV_c - XK_c)   (per row)
+//   Zbar_c = XQ_c W_c + b_c + T_c E_c,   T_c = tril(XQ_c XK_c^T + 1)
+//   O_c    = XQ_c + LN(Zbar_c)
+//   W_{c+1} = W_c + XK_c^T E_c ;  b_{c+1} = b_c + 1^T E_c
 //
-// Design (gfx950, one 256-thread workgroup = 4 waves per (n,h) sequence):
-//   * The fp32 state never leaves registers. Wave w owns columns
-//     16w..16w+15 of W; lane (g = lane/16, c = lane%16) holds
-//     W[16 rb + 4 g + i][16 w + c] for rb, i in 0..3 -- exactly the output
-//     layout of the 16x16x16 MFMA that applies the update, and (with the
-//     contraction index permuted consistently on both operands) the B-operand
-//     layout of the 16x16x32 MFMAs that form XK W and XQ W.
-//   * The bias is kept the same way (b[16 w + c] on every lane) and updated by
-//     an MFMA with an all-ones A operand, which sums E over tokens.
-//   * MFMA operands are bf16 (state and gradients rounded once per chunk),
-//     accumulation and state are fp32.
-//   * The row-wise layer-norm work runs in a "row layout": 16 lanes share a
-//     token, 4 consecutive features each, reduced with DPP row operations;
-//     tiles move between the MFMA layout and the row layout through LDS.
-//   * Q/K/V chunks stream from HBM with 8-byte loads issued three chunks
-//     ahead into a ring of register sets; each thread's loads are exactly the
-//     values its row-layout work needs (XV never goes to LDS), and XQ/XK are
-//     staged into LDS (XK also transposed, for the update's A operand).
+// The serial chain runs through Z -> E -> state. Two exact rewrites shorten it:
+//  * look-ahead: Z_{c+1} = P_{c+1} + K_c E_c with P_{c+1} = XK_{c+1} W_c + b_c
+//    and K_c = XK_{c+1} XK_c^T + 1 (both known one chunk early), so between
+//    two layer-norm backwards sits a single 16x16x16 MFMA;
+//  * with gamma = 1, beta = 0 the gradient has the closed form
+//      G = a (z - mu) - rstd (tau - mean tau),
+//      a = rstd^2 (eps rstd^2 + rstd (mean(tau z) - mean(tau) mu)),
+//    which needs one round of row sums (z, z^2, tau z) instead of two.
+//
+// Layout (gfx950, one 512-thread workgroup per (n,h) sequence):
+//  * waves 0-3 compute. Wave w owns columns 16w..16w+15 of the fp32 state:
+//    lane (g = lane/16, c = lane%16) holds W[16 rb + 4 g + i][16 w + c] --
+//    the output layout of the 16x16x16 MFMA that applies the update and, with
+//    the contraction index permuted identically on both operands, the
+//    B-operand layout of the 16x16x32 MFMAs that form XK W and XQ W. The bias
+//    lives alongside and is updated by an MFMA with an all-ones A operand.
+//    MFMA operands are bf16; state and accumulation are fp32.
+//  * row-wise layer-norm work uses a row layout: 16 lanes per token, four
+//    consecutive features each, DPP row reductions; tiles cross between the
+//    MFMA layout and the row layout through LDS.
+//  * waves 4-7 prepare inputs: 8-byte loads issued four chunks ahead into a
+//    register ring (these waves never store, so their load waits stay
+//    precise), then bf16 rows, the transposed XK, fp32 XQ, the target
+//    XV - XK with its row mean, and eta are staged in a 5-chunk LDS ring.
+//  * per chunk two barriers: phase X (MFMA layout: Z_c, Zbar_{c-1}; row
+//    layout: O_{c-2}) and phase Y (row layout: E_c; MFMA layout: state update
+//    with E_{c-1}, P_{c+1}, XQ_c W_c, Gram, K_c).
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -37,61 +48,319 @@ typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int D = 64, MB = 16;
-constexpr int NCW = 4;              // compute waves
-constexpr int NT = 64 * (NCW + 1);  // + one loader wave
-constexpr int QK_STRIDE = 72;       // bf16 per staged XQ / XK / XV row (64 + pad)
-constexpr int KT_STRIDE = 20;       // bf16 per transposed-XK row (16 tokens + pad)
-constexpr int Z_STRIDE = 68;        // fp32 per Z / Zbar row (64 + pad)
-constexpr int ET_STRIDE = 20;       // bf16 per transposed-E row
-constexpr int NSET = 4;             // register sets in the loader's ring
+constexpr int NCW = 4, NPW = 4, NT = 64 * (NCW + NPW);
+constexpr int RS = 68;       // row stride (elements) of every [16][64] tile in LDS
+constexpr int KS = 20;       // row stride (bf16) of the transposed XK tile [64][16]
+constexpr int NSLOT = 5;     // LDS ring: chunks c-2 .. c+2
+constexpr int NSET = 4;      // prep register ring depth (chunks)
 
-// One chunk as held by the loader wave: lane l covers token 8p + l/8,
-// features 8 (l%8) .. +7 of XQ, XK, XV (p = 0, 1), and eta of token l (l < 16).
-struct ChunkRegs {
-    uint4 q[2], k[2], v[2];
+struct alignas(16) Slot {
+    alignas(16) uint16_t xq[MB * RS];   // bf16 rows
+    alignas(16) uint16_t xk[MB * RS];   // bf16 rows
+    alignas(16) uint16_t xkt[D * KS];   // bf16, [feature][token]
+    alignas(16) float xqf[MB * RS];     // fp32 rows
+    alignas(16) float tau[MB * RS];     // XV - XK, fp32 rows
+    alignas(16) float eta[MB];
+    alignas(16) float mutau[MB];        // mean over features of tau
+};
+
+struct alignas(16) Smem {
+    Slot slot[NSLOT];
+    alignas(16) float z[MB * RS];          // Z_c
+    alignas(16) float zbar[2][MB * RS];    // Zbar, two chunks in flight
+    alignas(16) uint16_t e[MB * RS];       // E_c, bf16 rows
+};
+
+struct PrepRegs {
+    uint2 q, k, v;  // 4 bf16 features of one token
     float eta;
 };
 
 __device__ __forceinline__ float lo_bf(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float hi_bf(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
-__device__ __forceinline__ void unpack4(uint2 p, float (&f)[4]) {
-    f[0] = lo_bf(p.x);
-    f[1] = hi_bf(p.x);
-    f[2] = lo_bf(p.y);
-    f[3] = hi_bf(p.y);
+__device__ __forceinline__ f32x4 unpack4(uint2 p) {
+    return f32x4{lo_bf(p.x), hi_bf(p.x), lo_bf(p.y), hi_bf(p.y)};
 }
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+// Two floats -> packed bf16 pair (round to nearest even), one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
-    const __bf16 x = static_cast<__bf16>(a), y = static_cast<__bf16>(b);
-    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, x)) |
-           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, y)) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
-// Sum over the 16 lanes of a DPP row; every lane receives the total.
+// Sum over the 16 lanes of a DPP row; every lane receives the total. Each
+// step is one v_add_f32_dpp (identity 0 for lanes outside the pattern).
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
 __device__ __forceinline__ float row16_sum(float v) {
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));  // quad [1,0,3,2]
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));  // quad [2,3,0,1]
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)); // half-row mirror
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)); // row mirror
+    v = dpp_add<0xB1>(v);   // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]
+    v = dpp_add<0x141>(v);  // row_half_mirror
+    v = dpp_add<0x140>(v);  // row_mirror
     return v;
 }
 
-struct alignas(16) Smem {
-    alignas(16) uint16_t xq[2][MB * QK_STRIDE];
-    alignas(16) uint16_t xk[2][MB * QK_STRIDE];
-    alignas(16) uint16_t xv[2][MB * QK_STRIDE];
-    alignas(16) uint16_t xkt[2][D * KT_STRIDE];
-    alignas(16) float eta[2][MB];
-    alignas(16) float z[MB * Z_STRIDE];
-    alignas(16) uint16_t et[D * ET_STRIDE];
-};
-
 // Barrier for LDS hand-offs only: waits for this wave's LDS operations, not
-// for its outstanding global loads / stores.
+// for its outstanding global loads or stores.
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// A-operand fragment of a bf16 [16][64] row tile for 16x16x32 MFMAs over
+// k-block kb. Lane (g, c) takes row c, features 32kb + 4g .. +3 and
+// 32kb + 16 + 4g .. +3: the same contraction order the state fragment uses.
+__device__ __forceinline__ bf16x8 row_frag(const uint16_t *tile, int c, int g, int kb) {
+    const uint2 a = *reinterpret_cast<const uint2 *>(&tile[c * RS + 32 * kb + 4 * g]);
+    const uint2 b = *reinterpret_cast<const uint2 *>(&tile[c * RS + 32 * kb + 16 + 4 * g]);
+    return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+
+// Layer-norm + L2 backward of one row (row layout), returning E = -eta * G.
+template <bool IDENT>
+__device__ __forceinline__ f32x4 ln_bwd_row(f32x4 z, f32x4 tau, float mutau, float eta_r,
+                                            const float (&gam)[4], const float (&bet)[4],
+                                            float eps) {
+    constexpr float inv_d = 1.0f / D;
+    f32x4 ev;
+    if constexpr (IDENT) {
+        const float s1 = row16_sum((z[0] + z[1]) + (z[2] + z[3]));
+        const float s2 = row16_sum(z[0] * z[0] + z[1] * z[1] + z[2] * z[2] + z[3] * z[3]);
+        const float s3 = row16_sum(tau[0] * z[0] + tau[1] * z[1] + tau[2] * z[2] + tau[3] * z[3]);
+        const float mu = s1 * inv_d;
+        const float var = fmaxf(s2 * inv_d - mu * mu, 0.f);
+        const float rstd = rsqrtf(var + eps);
+        const float mtz = s3 * inv_d - mutau * mu;
+        const float a = rstd * rstd * (eps * rstd * rstd + rstd * mtz);
+        // E = -eta (a (z - mu) - rstd (tau - mutau)) = cz z + ct tau + c0
+        const float cz = -eta_r * a, ct = eta_r * rstd;
+        const float c0 = eta_r * (a * mu - rstd * mutau);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ev[e] = fmaf(cz, z[e], fmaf(ct, tau[e], c0));
+    } else {
+        const float mu = row16_sum((z[0] + z[1]) + (z[2] + z[3])) * inv_d;
+        float cz[4], s2 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            cz[e] = z[e] - mu;
+            s2 += cz[e] * cz[e];
+        }
+        const float rstd = rsqrtf(row16_sum(s2) * inv_d + eps);
+        float xh[4], gh[4], a1 = 0.f, a2 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            xh[e] = cz[e] * rstd;
+            gh[e] = gam[e] * (gam[e] * xh[e] + bet[e] - tau[e]);
+            a1 += gh[e];
+            a2 += gh[e] * xh[e];
+        }
+        const float m1 = row16_sum(a1) * inv_d, m2 = row16_sum(a2) * inv_d;
+        const float ne = -eta_r * rstd;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ev[e] = ne * (gh[e] - m1 - xh[e] * m2);
+    }
+    return ev;
+}
+
+// O row = XQ row + LN(Zbar row) (row layout).
+template <bool IDENT>
+__device__ __forceinline__ f32x4 ln_fwd_row(f32x4 z, f32x4 xq, const float (&gam)[4],
+                                            const float (&bet)[4], float eps) {
+    constexpr float inv_d = 1.0f / D;
+    const float mu = row16_sum((z[0] + z[1]) + (z[2] + z[3])) * inv_d;
+    float cz[4], s2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        cz[e] = z[e] - mu;
+        s2 += cz[e] * cz[e];
+    }
+    const float rstd = rsqrtf(row16_sum(s2) * inv_d + eps);
+    f32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if constexpr (IDENT)
+            o[e] = fmaf(cz[e], rstd, xq[e]);
+        else
+            o[e] = xq[e] + fmaf(gam[e], cz[e] * rstd, bet[e]);
+    }
+    return o;
+}
+
+struct Ctx {
+    int L, nch, iters;
+    float eps;
+    bf16_t *Oseq;  // output rows of this sequence
+};
+
+// Compute waves: the chain and the output, two barriers per iteration.
+// The state is kept as MFMA accumulators: Wv[rb] holds rows 16 rb + 4 g .. +3
+// of column 16 w + c, bv holds b[16 w + c] in all four slots.
+template <bool IDENT>
+__device__ __forceinline__ void compute_loop(Smem &sm, const Ctx &cx, int w, int g, int c,
+                                             f32x4 (&Wv)[4], f32x4 &bv, const float (&gam)[4],
+                                             const float (&bet)[4]) {
+    const int col = 16 * w + c;           // MFMA layout column
+    const int r = 4 * w + g, f0 = 4 * c;  // row layout token / first feature
+    const int nch = cx.nch;
+    const s16x4 ones = {0x3F80, 0x3F80, 0x3F80, 0x3F80};  // bf16 1.0
+    const s16x4 zero4 = {0, 0, 0, 0};
+    const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
+    // causal mask of T[t = c][s = 4g + i] as 0/1 factors: T = (Gram + 1) * m
+    f32x4 tmask;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tmask[i] = (4 * g + i <= c) ? 1.f : 0.f;
+
+    auto cvt_state = [&](bf16x8 (&wb)[2]) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            wb[kb] = __builtin_bit_cast(
+                bf16x8, make_uint4(pack2(Wv[2 * kb][0], Wv[2 * kb][1]), pack2(Wv[2 * kb][2], Wv[2 * kb][3]),
+                                   pack2(Wv[2 * kb + 1][0], Wv[2 * kb + 1][1]),
+                                   pack2(Wv[2 * kb + 1][2], Wv[2 * kb + 1][3])));
+    };
+
+    // P_0 = XK_0 W_0 + b_0
+    f32x4 P = bv, Zq = fzero;
+    s16x4 Ka = zero4, Ta = zero4;
+    if (nch > 0) {
+        bf16x8 wb[2];
+        cvt_state(wb);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) P = mfma32(row_frag(sm.slot[0].xk, c, g, kb), wb[kb], P);
+    }
+
+    const uint16_t *Ecol = sm.e + (4 * g) * RS + col;  // E[4g + i][col] at Ecol[i * RS]
+    float *Zw = sm.z + (4 * g) * RS + col;             // MFMA-layout writes
+    const float *Zr = sm.z + r * RS + f0;              // row-layout reads
+    int sc = 0, sp = NSLOT - 1, sp2 = NSLOT - 2, sn = 1;  // slots of chunks it, it-1, it-2, it+1
+
+    // One iteration. chain: Z_it and E_it; upd: apply E_{it-1}; out: O_{it-2}.
+    // In the steady state all three hold and the body is one straight block,
+    // so the scheduler can interleave its independent LDS, MFMA and VALU work.
+    auto iteration = [&](int it, auto chain_t, auto upd_t, auto out_t, bool chain_r, bool upd_r,
+                         bool out_r) {
+        constexpr bool CT = decltype(chain_t)::value, UT = decltype(upd_t)::value,
+                       OT = decltype(out_t)::value;
+        const bool chain = CT || chain_r, upd = UT || upd_r, out = OT || out_r;
+
+        // ===== phase X ========================================================
+        // Every LDS read of the phase is issued before any LDS write (the
+        // compiler cannot reorder them past writes it cannot disambiguate).
+        s16x4 eb = zero4;  // E_{it-1} as the B operand: E[4g + i][col]
+        if (upd) {
+            const uint32_t e01 = static_cast<uint32_t>(Ecol[0]) | (static_cast<uint32_t>(Ecol[RS]) << 16);
+            const uint32_t e23 = static_cast<uint32_t>(Ecol[2 * RS]) | (static_cast<uint32_t>(Ecol[3 * RS]) << 16);
+            eb = __builtin_bit_cast(s16x4, make_uint2(e01, e23));
+        }
+        f32x4 zbr = fzero, xqr = fzero;
+        if (out) {
+            zbr = *reinterpret_cast<const f32x4 *>(&sm.zbar[it & 1][r * RS + f0]);  // Zbar_{it-2}
+            xqr = *reinterpret_cast<const f32x4 *>(&sm.slot[sp2].xqf[r * RS + f0]);
+        }
+        f32x4 z = P, zb = fzero;
+        if (chain && (UT || it > 0)) z = mfma16(Ka, eb, P);
+        if (upd) zb = mfma16(Ta, eb, Zq);
+        f32x4 o = fzero;
+        if (out) o = ln_fwd_row<IDENT>(zbr, xqr, gam, bet, cx.eps);
+        if (chain) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Zw[i * RS] = z[i];
+        }
+        if (upd) {
+            float *Zb = sm.zbar[(it - 1) & 1] + (4 * g) * RS + col;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Zb[i * RS] = zb[i];
+        }
+        if (out) {
+            const int oc = it - 2;
+            if (oc * MB + r < cx.L)
+                *reinterpret_cast<uint2 *>(cx.Oseq + static_cast<uint32_t>((oc * MB + r) * D + f0)) =
+                    make_uint2(pack2(o[0], o[1]), pack2(o[2], o[3]));
+        }
+        lds_barrier();
+
+        // ===== phase Y ========================================================
+        const Slot &S = sm.slot[sc], &N = sm.slot[sn];
+        f32x4 zz = fzero, tau = fzero;
+        float mutau = 0.f, eta_r = 0.f;
+        bf16x8 akc[2], aqc[2], akn[2];
+        s16x4 ka[4];
+        if (chain) {
+            zz = *reinterpret_cast<const f32x4 *>(Zr);
+            tau = *reinterpret_cast<const f32x4 *>(&S.tau[r * RS + f0]);
+            mutau = S.mutau[r];
+            eta_r = S.eta[r];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                akc[kb] = row_frag(S.xk, c, g, kb);
+                aqc[kb] = row_frag(S.xq, c, g, kb);
+                akn[kb] = row_frag(N.xk, c, g, kb);
+            }
+        }
+        if (upd) {
+            const uint16_t *XKT = sm.slot[sp].xkt + c * KS + 4 * g;
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+                ka[rb] = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(XKT + 16 * rb * KS));
+        }
+        // state update with E_{it-1}
+        if (upd) {
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) Wv[rb] = mfma16(ka[rb], eb, Wv[rb]);
+            bv = mfma16(ones, eb, bv);
+        }
+        // chain: E_it (the critical path of the loop) goes out first
+        if (chain) {
+            const f32x4 ev = ln_bwd_row<IDENT>(zz, tau, mutau, eta_r, gam, bet, cx.eps);
+            *reinterpret_cast<uint2 *>(&sm.e[r * RS + f0]) = make_uint2(pack2(ev[0], ev[1]), pack2(ev[2], ev[3]));
+        }
+        if (chain) {
+            bf16x8 wb[2];
+            cvt_state(wb);
+            f32x4 p = bv, zq = bv, gt = fzero, kt = fzero;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                p = mfma32(akn[kb], wb[kb], p);
+                zq = mfma32(aqc[kb], wb[kb], zq);
+                gt = mfma32(akc[kb], aqc[kb], gt);  // [s = 4g+i][t = c] = XQ_t . XK_s
+                kt = mfma32(akc[kb], akn[kb], kt);  // [s = 4g+i][t = c] = XK_{it+1, t} . XK_{it, s}
+            }
+            P = p;
+            Zq = zq;
+            // A operands (row t = c, contraction s = 4g + i)
+            Ta = __builtin_bit_cast(s16x4, make_uint2(pack2(fmaf(gt[0], tmask[0], tmask[0]), fmaf(gt[1], tmask[1], tmask[1])),
+                                                      pack2(fmaf(gt[2], tmask[2], tmask[2]), fmaf(gt[3], tmask[3], tmask[3]))));
+            Ka = __builtin_bit_cast(s16x4, make_uint2(pack2(kt[0] + 1.f, kt[1] + 1.f), pack2(kt[2] + 1.f, kt[3] + 1.f)));
+        }
+        lds_barrier();
+        // rotate the ring
+        sp2 = sp;
+        sp = sc;
+        sc = sn;
+        sn = (sn + 1 == NSLOT) ? 0 : sn + 1;
+    };
+
+    using F = std::false_type;
+    using T = std::true_type;
+    const int steady_end = max(nch, 2);
+    int it = 0;
+    for (; it < min(2, cx.iters); ++it)  // warm-up: no update / no output yet
+        iteration(it, F{}, F{}, F{}, it < nch, it >= 1 && it <= nch, false);
+    for (; it < steady_end; ++it)        // steady state: branch-free body
+        iteration(it, T{}, T{}, T{}, true, true, true);
+    for (; it < cx.iters; ++it)          // drain (and padding to the prep ring)
+        iteration(it, F{}, F{}, F{}, it < nch, it >= 1 && it <= nch, it >= 2 && it <= nch + 1);
 }
 
 }  // namespace
@@ -109,66 +378,79 @@ __global__ __launch_bounds__(NT) void linear_prefill_mfma(
     const long seq = blockIdx.x;
     const int h = static_cast<int>(seq % H);
     const long n = seq / H;
+    Ctx cx;
+    cx.L = L;
+    cx.nch = (L + MB - 1) / MB;
+    cx.iters = (cx.nch + 2 + NSET - 1) / NSET * NSET;  // whole turns of the prep ring
+    cx.eps = eps;
     const size_t xbase = static_cast<size_t>(seq) * L * D;
-    const size_t ebase = static_cast<size_t>(seq) * L;
-    const int nch = (L + MB - 1) / MB;
+    cx.Oseq = O + xbase;
 
-    const int nch_pad = (nch + NSET - 1) / NSET * NSET;  // loader ring runs in whole turns
-
-    if (w == NCW) {
-        // ================= loader wave: HBM -> registers -> LDS =============
-        // Loads run NSET chunks ahead of their staging and are issued
-        // unconditionally (addresses clamped into the sequence, values past
-        // its end zeroed when staged); this wave issues no stores, so its
-        // waits on the load counter stay precise.
-        if (nch == 0) return;
-        auto load = [&](ChunkRegs &R, int ch) {
-#pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                const int tok = min(ch * MB + 8 * p + (lane >> 3), L - 1);
-                const size_t off = xbase + static_cast<size_t>(tok) * D + 8 * (lane & 7);
-                R.q[p] = *reinterpret_cast<const uint4 *>(XQ + off);
-                R.k[p] = *reinterpret_cast<const uint4 *>(XK + off);
-                R.v[p] = *reinterpret_cast<const uint4 *>(XV + off);
-            }
-            R.eta = eta[ebase + min(ch * MB + (lane & 15), L - 1)];
+    if (w >= NCW) {
+        // ======== prep waves: HBM -> registers -> LDS ring ==================
+        const int r = 4 * (w - NCW) + g, f0 = 4 * c;  // token, first feature
+        // per-sequence bases; per-lane offsets stay 32-bit
+        const bf16_t *xq = XQ + xbase, *xk = XK + xbase, *xv = XV + xbase;
+        const float *et = eta + static_cast<size_t>(seq) * L;
+        auto load = [&](PrepRegs &R, int ch) {
+            const uint32_t tok = static_cast<uint32_t>(min(ch * MB + r, L - 1));  // clamped: in bounds
+            const uint32_t off = tok * D + f0;
+            R.q = *reinterpret_cast<const uint2 *>(xq + off);
+            R.k = *reinterpret_cast<const uint2 *>(xk + off);
+            R.v = *reinterpret_cast<const uint2 *>(xv + off);
+            R.eta = et[tok];
         };
-        auto stage = [&](const ChunkRegs &R, int ch) {
-            const int s = ch & 1;
-            const uint4 zero = make_uint4(0, 0, 0, 0);
-#pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                const int tok = 8 * p + (lane >> 3), f = 8 * (lane & 7);
-                const bool ok = ch * MB + tok < L;
-                const uint4 q = ok ? R.q[p] : zero, k = ok ? R.k[p] : zero, v = ok ? R.v[p] : zero;
-                *reinterpret_cast<uint4 *>(&sm.xq[s][tok * QK_STRIDE + f]) = q;
-                *reinterpret_cast<uint4 *>(&sm.xk[s][tok * QK_STRIDE + f]) = k;
-                *reinterpret_cast<uint4 *>(&sm.xv[s][tok * QK_STRIDE + f]) = v;
-                const uint32_t kw[4] = {k.x, k.y, k.z, k.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    sm.xkt[s][(f + 2 * e) * KT_STRIDE + tok] = static_cast<uint16_t>(kw[e] & 0xffffu);
-                    sm.xkt[s][(f + 2 * e + 1) * KT_STRIDE + tok] = static_cast<uint16_t>(kw[e] >> 16);
-                }
+        auto stage_rows = [&](Slot &S, uint2 q, uint2 k, uint2 v, float e) {
+            *reinterpret_cast<uint2 *>(&S.xq[r * RS + f0]) = q;
+            *reinterpret_cast<uint2 *>(&S.xk[r * RS + f0]) = k;
+            S.xkt[(f0 + 0) * KS + r] = static_cast<uint16_t>(k.x & 0xffffu);
+            S.xkt[(f0 + 1) * KS + r] = static_cast<uint16_t>(k.x >> 16);
+            S.xkt[(f0 + 2) * KS + r] = static_cast<uint16_t>(k.y & 0xffffu);
+            S.xkt[(f0 + 3) * KS + r] = static_cast<uint16_t>(k.y >> 16);
+            *reinterpret_cast<f32x4 *>(&S.xqf[r * RS + f0]) = unpack4(q);
+            const f32x4 tau = unpack4(v) - unpack4(k);
+            *reinterpret_cast<f32x4 *>(&S.tau[r * RS + f0]) = tau;
+            const float mt = row16_sum((tau[0] + tau[1]) + (tau[2] + tau[3])) * (1.0f / D);
+            if (c == 0) {
+                S.mutau[r] = mt;
+                S.eta[r] = e;
             }
-            if (lane < MB) sm.eta[s][lane] = (ch * MB + lane < L) ? R.eta : 0.f;
         };
-
-        ChunkRegs R[NSET];
+        auto stage = [&](const PrepRegs &R, int ch, int slot) {
+            Slot &S = sm.slot[slot];
+            if (ch * MB + MB <= L) {  // whole chunk inside the sequence (uniform)
+                stage_rows(S, R.q, R.k, R.v, R.eta);
+            } else {
+                const bool ok = ch * MB + r < L;
+                const uint2 z2 = make_uint2(0u, 0u);
+                stage_rows(S, ok ? R.q : z2, ok ? R.k : z2, ok ? R.v : z2, ok ? R.eta : 0.f);
+            }
+        };
+        if (cx.nch == 0) {  // same barrier count as the compute waves
+            lds_barrier();
+            for (int it = 0; it < cx.iters; ++it) {
+                lds_barrier();
+                lds_barrier();
+            }
+            return;
+        }
+        PrepRegs R[NSET];
 #pragma unroll
         for (int k = 0; k < NSET; ++k) load(R[k], k);
-        stage(R[0], 0);
+        stage(R[0], 0, 0);
         load(R[0], NSET);
+        stage(R[1], 1, 1);
+        load(R[1], NSET + 1);
         lds_barrier();
-        for (int ch = 0; ch < nch_pad; ch += NSET) {
+        int slot = 2;  // slot of chunk it + 2
+        for (int it = 0; it < cx.iters; it += NSET) {
 #pragma unroll
             for (int k = 0; k < NSET; ++k) {
-                // during chunk ch + k: stage chunk ch + k + 1, refill its set
-                const int kn = (k + 1) % NSET;
-                stage(R[kn], ch + k + 1);
-                load(R[kn], ch + k + 1 + NSET);
-                lds_barrier();
-                lds_barrier();
+                // during iteration it + k: stage chunk it + k + 2, refill its set
+                const int ks = (k + 2) % NSET;
+                stage(R[ks], it + k + 2, slot);
+                load(R[ks], it + k + 2 + NSET);
+                slot = (slot + 1 == NSLOT) ? 0 : slot + 1;
                 lds_barrier();
                 lds_barrier();
             }
@@ -176,163 +458,43 @@ __global__ __launch_bounds__(NT) void linear_prefill_mfma(
         return;
     }
 
-    // ===================== compute waves ====================================
+    // =========== compute waves ==============================================
     const size_t wofs = (w0_batched ? static_cast<size_t>(n) * H * D * D : 0) + static_cast<size_t>(h) * D * D;
     const size_t bofs = (w0_batched ? static_cast<size_t>(n) * H * D : 0) + static_cast<size_t>(h) * D;
-
-    // state in the MFMA layout
     const int col = 16 * w + c;
-    float Wr[4][4];
+    f32x4 Wv[4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Wr[rb][i] = W0[wofs + static_cast<size_t>(16 * rb + 4 * g + i) * D + col];
-    float bv = b0[bofs + col];
-
-    // row layout: token r = tid / 16, features f0 .. f0 + 3
-    const int r = tid >> 4, f0 = 4 * c;
+        for (int i = 0; i < 4; ++i) Wv[rb][i] = W0[wofs + static_cast<size_t>(16 * rb + 4 * g + i) * D + col];
+    const float b_init = b0[bofs + col];
+    f32x4 bv = {b_init, b_init, b_init, b_init};
     float gam[4], bet[4];
+    bool ident = true;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        gam[e] = gamma[static_cast<size_t>(h) * D + f0 + e];
-        bet[e] = beta[static_cast<size_t>(h) * D + f0 + e];
+        gam[e] = gamma[static_cast<size_t>(h) * D + 4 * c + e];
+        bet[e] = beta[static_cast<size_t>(h) * D + 4 * c + e];
+        ident = ident && gam[e] == 1.0f && bet[e] == 0.0f;
     }
-    const float inv_d = 1.0f / D;
-    const s16x4 ones = {0x3F80, 0x3F80, 0x3F80, 0x3F80};  // bf16 1.0
+    // every compute wave covers all 64 features in its row layout, so the
+    // wave-wide vote is the same in all four waves
+    ident = __all(ident);
 
     lds_barrier();
-    for (int ch = 0; ch < nch; ++ch) {
-        const int s = ch & 1;
-        const int len = min(MB, L - ch * MB);
-
-        // ---- phase A: Z = XK W + b, Zq = XQ W + b, Gram^T = XK XQ^T ------
-        bf16x8 wb[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                wb[kb][j] = static_cast<__bf16>(Wr[2 * kb][j]);
-                wb[kb][4 + j] = static_cast<__bf16>(Wr[2 * kb + 1][j]);
-            }
-        bf16x8 ak[2], aq[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const uint2 k0 = *reinterpret_cast<const uint2 *>(&sm.xk[s][c * QK_STRIDE + 32 * kb + 4 * g]);
-            const uint2 k1 = *reinterpret_cast<const uint2 *>(&sm.xk[s][c * QK_STRIDE + 32 * kb + 16 + 4 * g]);
-            const uint2 q0 = *reinterpret_cast<const uint2 *>(&sm.xq[s][c * QK_STRIDE + 32 * kb + 4 * g]);
-            const uint2 q1 = *reinterpret_cast<const uint2 *>(&sm.xq[s][c * QK_STRIDE + 32 * kb + 16 + 4 * g]);
-            ak[kb] = __builtin_bit_cast(bf16x8, make_uint4(k0.x, k0.y, k1.x, k1.y));
-            aq[kb] = __builtin_bit_cast(bf16x8, make_uint4(q0.x, q0.y, q1.x, q1.y));
-        }
-        f32x4 z = {bv, bv, bv, bv}, zq = {bv, bv, bv, bv}, gt = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[kb], wb[kb], z, 0, 0, 0);
-            zq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[kb], wb[kb], zq, 0, 0, 0);
-            gt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[kb], aq[kb], gt, 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sm.z[(4 * g + i) * Z_STRIDE + col] = z[i];
-        lds_barrier();
-
-        // ---- phase B (row layout): E = -eta * lnbwd(Z, XV - XK) ----------
-        {
-            const f32x4 zz = *reinterpret_cast<const f32x4 *>(&sm.z[r * Z_STRIDE + f0]);
-            float xv[4], xk[4];
-            unpack4(*reinterpret_cast<const uint2 *>(&sm.xv[s][r * QK_STRIDE + f0]), xv);
-            unpack4(*reinterpret_cast<const uint2 *>(&sm.xk[s][r * QK_STRIDE + f0]), xk);
-            const float et_r = sm.eta[s][r];
-            const float mu = row16_sum((zz[0] + zz[1]) + (zz[2] + zz[3])) * inv_d;
-            float cz[4], s2 = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                cz[e] = zz[e] - mu;
-                s2 += cz[e] * cz[e];
-            }
-            const float rstd = rsqrtf(row16_sum(s2) * inv_d + eps);
-            float xh[4], gh[4], a1 = 0.f, a2 = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                xh[e] = cz[e] * rstd;
-                gh[e] = gam[e] * (gam[e] * xh[e] + bet[e] - (xv[e] - xk[e]));
-                a1 += gh[e];
-                a2 += gh[e] * xh[e];
-            }
-            const float m1 = row16_sum(a1) * inv_d, m2 = row16_sum(a2) * inv_d;
-            const float ne = -et_r * rstd;
-            float ev[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ev[e] = ne * (gh[e] - m1 - xh[e] * m2);
-            const uint32_t p01 = pack2(ev[0], ev[1]), p23 = pack2(ev[2], ev[3]);
-            sm.et[(f0 + 0) * ET_STRIDE + r] = static_cast<uint16_t>(p01 & 0xffffu);
-            sm.et[(f0 + 1) * ET_STRIDE + r] = static_cast<uint16_t>(p01 >> 16);
-            sm.et[(f0 + 2) * ET_STRIDE + r] = static_cast<uint16_t>(p23 & 0xffffu);
-            sm.et[(f0 + 3) * ET_STRIDE + r] = static_cast<uint16_t>(p23 >> 16);
-        }
-        lds_barrier();
-
-        // ---- phase C: state update, bias update, Zbar = Zq + T E ---------
-        {
-            const s16x4 eb = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(&sm.et[col * ET_STRIDE + 4 * g]));
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                const s16x4 ka = __builtin_bit_cast(
-                    s16x4, *reinterpret_cast<const uint2 *>(&sm.xkt[s][(16 * rb + c) * KT_STRIDE + 4 * g]));
-                f32x4 acc = {Wr[rb][0], Wr[rb][1], Wr[rb][2], Wr[rb][3]};
-                acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka, eb, acc, 0, 0, 0);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Wr[rb][i] = acc[i];
-            }
-            f32x4 bacc = {bv, bv, bv, bv};
-            bacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, eb, bacc, 0, 0, 0);
-            bv = bacc[0];
-            // T[t = c][s = 4g + i] = Gram + 1 on and below the diagonal
-            const uint32_t t01 = pack2((4 * g + 0 <= c) ? gt[0] + 1.f : 0.f, (4 * g + 1 <= c) ? gt[1] + 1.f : 0.f);
-            const uint32_t t23 = pack2((4 * g + 2 <= c) ? gt[2] + 1.f : 0.f, (4 * g + 3 <= c) ? gt[3] + 1.f : 0.f);
-            const s16x4 ta = __builtin_bit_cast(s16x4, make_uint2(t01, t23));
-            zq = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ta, eb, zq, 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sm.z[(4 * g + i) * Z_STRIDE + col] = zq[i];
-        }
-        lds_barrier();
-
-        // ---- phase D (row layout): O = XQ + LN(Zbar) -----------------------
-        {
-            const f32x4 zz = *reinterpret_cast<const f32x4 *>(&sm.z[r * Z_STRIDE + f0]);
-            float xq[4], o[4];
-            unpack4(*reinterpret_cast<const uint2 *>(&sm.xq[s][r * QK_STRIDE + f0]), xq);
-            const float mu = row16_sum((zz[0] + zz[1]) + (zz[2] + zz[3])) * inv_d;
-            float cz[4], s2 = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                cz[e] = zz[e] - mu;
-                s2 += cz[e] * cz[e];
-            }
-            const float rstd = rsqrtf(row16_sum(s2) * inv_d + eps);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = xq[e] + gam[e] * (cz[e] * rstd) + bet[e];
-            if (r < len) {
-                const size_t t = static_cast<size_t>(ch) * MB + r;
-                *reinterpret_cast<uint2 *>(O + xbase + t * D + f0) = make_uint2(pack2(o[0], o[1]), pack2(o[2], o[3]));
-            }
-        }
-        lds_barrier();
-    }
-    for (int ch = nch; ch < nch_pad; ++ch) {  // keep step with the loader's ring
-        lds_barrier();
-        lds_barrier();
-        lds_barrier();
-        lds_barrier();
-    }
+    if (ident)
+        compute_loop<true>(sm, cx, w, g, c, Wv, bv, gam, bet);
+    else
+        compute_loop<false>(sm, cx, w, g, c, Wv, bv, gam, bet);
 
     if (W_out) {
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                W_out[static_cast<size_t>(seq) * D * D + static_cast<size_t>(16 * rb + 4 * g + i) * D + col] = Wr[rb][i];
+                W_out[static_cast<size_t>(seq) * D * D + static_cast<size_t>(16 * rb + 4 * g + i) * D + col] = Wv[rb][i];
     }
-    if (b_out && g == 0) b_out[static_cast<size_t>(seq) * D + col] = bv;
+    if (b_out && g == 0) b_out[static_cast<size_t>(seq) * D + col] = bv[0];
 }
 
 bool linear_mfma_supported(const LinearArgs &a) { return a.io == 1 && a.d == 64 && a.mb == 16; }
