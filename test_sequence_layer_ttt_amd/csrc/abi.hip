@@ -199,6 +199,7 @@ int ttt_mlp_forward(int B, int H, int L, int d, int mb, int io, float ln_eps,
     if (B * H == 0) return ok();
     ttt::MLPArgs a{B, H, L, d, mb, io, ln_eps, XQ, XK, XV, eta, W1_0, b1_0, W2_0, b2_0,
                    w0_batched ? 1 : 0, ln_gamma, ln_beta, O, W1_out, b1_out, W2_out, b2_out};
+    if (ttt::mlp_mfma_supported(a)) return launched(ttt::launch_mlp_mfma(a, stream));
     return launched(ttt::launch_mlp(a, stream));
 }
 

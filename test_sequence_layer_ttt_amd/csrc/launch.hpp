@@ -45,6 +45,8 @@ hipError_t launch_linear_valu(const LinearArgs &a, hipStream_t stream);
 bool linear_mfma_supported(const LinearArgs &a);
 hipError_t launch_linear_mfma(const LinearArgs &a, hipStream_t stream);
 hipError_t launch_mlp(const MLPArgs &a, hipStream_t stream);
+bool mlp_mfma_supported(const MLPArgs &a);
+hipError_t launch_mlp_mfma(const MLPArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 
 }  // namespace ttt

@@ -1,0 +1,391 @@
+// TTT-MLP prefill, MFMA path: bf16 storage, d = 64, hidden m = 4d = 256,
+// mini-batch b = 16. The hidden model d -> 4d GELU -> d inside the LN
+// residual is the one of the lryc.cn TTT article §2.1; the inner loop is the
+// dual form of the damodev.csdn.net TTT deep-dive §4.2 applied to both layers.
+//
+// Per chunk (state W1, b1, W2, b2 at chunk start; E = -eta * G row-scaled):
+//   Z1 = XK W1 + b1, A = gelu(Z1), Z2 = A W2 + b2, E2 = -eta lnbwd(Z2, XV - XK)
+//   E1 = (E2 W2^T) * gelu'(Z1)
+//   Zb1 = XQ W1 + b1 + T1 E1,   T1 = tril(XQ XK^T + 1),   Ab = gelu(Zb1)
+//   Zb2 = Ab W2 + b2 + T2 E2,   T2 = tril(Ab A^T + 1),    O = XQ + LN(Zb2)
+//   W1 += XK^T E1, b1 += 1^T E1, W2 += A^T E2, b2 += 1^T E2
+//
+// Layout (gfx950, one 512-thread workgroup = 8 waves per (n,h) sequence, two
+// per SIMD):
+//  * wave w owns hidden units 32w .. 32w+31 (two hidden tiles t of 16). Its
+//    share of the fp32 state lives in registers as MFMA accumulators, each in
+//    the output layout of its own update (lane (g, c) holds rows 4g .. 4g+3 of
+//    column c):
+//      W1v[t][rb] = W1[in 16rb + 4g + i][hid 32w + 16t + c]    (XK^T E1)
+//      b1v[t]     = b1[hid 32w + 16t + 4g + i]                 (E1^T 1)
+//      W2v[u][rb] = W2[hid 32w + 16rb + 4g + i][out 16u + c]   (A^T E2)
+//      b2w        = b2[out 16w + c]   (waves 0-3)               (1^T E2)
+//    With the contraction index permuted identically on both operands these
+//    are also the operand layouts of the forward products, so no product
+//    reads the state through LDS. W2 is contracted over hidden units (A W2)
+//    and over outputs (E2 W2^T); for the latter its bf16 tiles are transposed
+//    each chunk by MFMAs with the identity.
+//  * Z1 and Zb1 are computed transposed (hidden as the output row), so their
+//    GELU outputs are directly the A operands of A W2 and Ab W2; A and E1 are
+//    transposed by identity MFMAs for the token-contracting updates.
+//  * contractions over all 256 hidden units (Z2, Zb2, the Gram Ab A^T) are
+//    summed across the eight waves through LDS. Waves 0-3 also run the
+//    row-layout work (16 lanes per token, DPP reductions) and load the input
+//    rows of their four tokens one chunk ahead; a chunk is staged into LDS a
+//    full iteration after its loads were issued.
+//  * GELU: x Phi(x) with erf from Abramowitz & Stegun 7.1.26 (|error| <=
+//    1.5e-7, far below the bf16 resolution of the MFMA operands); GELU and its
+//    derivative share one exponential.
+#include "launch.hpp"
+#include "tile.hpp"
+
+namespace ttt {
+namespace {
+
+using namespace tile;
+
+constexpr int M = 4 * D;     // hidden units
+constexpr int NW = 8, NT = 64 * NW;
+constexpr int NRW = 4;       // waves running the row-layout work (16 tokens x 16 lanes)
+constexpr int GS = 20;       // row stride (fp32) of the Gram partial tiles
+
+struct alignas(16) MlpSmem {
+    Slot slot[2];
+    alignas(16) float part[NW + 1][MB * RS];  // per-wave partial sums of Z2 / Zb2 (+ T2 E2 + b2)
+    alignas(16) float gram[NW][MB * GS];      // per-wave partial Gram Ab A^T, [t][s]
+    alignas(16) uint16_t e2[MB * RS];         // E2, bf16 rows [token][out]
+    alignas(16) uint16_t e2t[D * KS];         // E2 transposed, bf16 [out][token]
+};
+
+// Phi(x) and phi(x) (standard normal cdf / pdf) with erf from Abramowitz &
+// Stegun 7.1.26: erf(y) = 1 - (a1 t + ... + a5 t^5) exp(-y^2), t = 1/(1 + p y).
+__device__ __forceinline__ void normal_cdf_pdf(float x, float &Phi, float &phi) {
+    const float y = fabsf(x) * 0.70710678118654752f;  // |x| / sqrt(2)
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, y, 1.0f));
+    const float p = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 1.061405429f, -1.453152027f), 1.421413741f),
+                                     -0.284496736f), 0.254829592f);
+    const float e = __expf(-y * y);                   // exp(-x^2 / 2)
+    const float half_erfc = 0.5f * p * e;             // erfc(|x| / sqrt(2)) / 2
+    Phi = x >= 0.f ? 1.0f - half_erfc : half_erfc;
+    phi = 0.39894228040143268f * e;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(NT) void mlp_prefill_mfma(
+    int H, int L, float eps, const bf16_t *__restrict__ XQ, const bf16_t *__restrict__ XK,
+    const bf16_t *__restrict__ XV, const float *__restrict__ eta,
+    const float *__restrict__ W1_0, const float *__restrict__ b1_0,
+    const float *__restrict__ W2_0, const float *__restrict__ b2_0, int w0_batched,
+    const float *__restrict__ gamma, const float *__restrict__ beta, bf16_t *__restrict__ O,
+    float *W1_out, float *b1_out, float *W2_out, float *b2_out) {
+    __shared__ MlpSmem sm;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6, g = lane >> 4, c = lane & 15;
+    const long seq = blockIdx.x;
+    const int h = static_cast<int>(seq % H);
+    const long n = seq / H;
+    const size_t st = w0_batched ? static_cast<size_t>(n) * H + h : static_cast<size_t>(h);
+    const size_t xbase = static_cast<size_t>(seq) * L * D;
+    const int nch = (L + MB - 1) / MB;
+    const int hw = 32 * w;        // first hidden unit of this wave
+    const bool roww = w < NRW;    // runs the row-layout work
+
+    // ---- state (this wave's share) -------------------------------------------
+    f32x4 W1v[2][4], W2v[4][2], b1v[2], b2w;
+    {
+        const float *W1s = W1_0 + st * D * M, *W2s = W2_0 + st * M * D;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) W1v[t][rb][i] = W1s[(16 * rb + 4 * g + i) * M + hw + 16 * t + c];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) W2v[u][rb][i] = W2s[(hw + 16 * rb + 4 * g + i) * D + 16 * u + c];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) b1v[t][i] = b1_0[st * M + hw + 16 * t + 4 * g + i];
+        // b2 tile w (columns 16w .. 16w+15), held by waves 0-3 only
+        const float bb = b2_0[st * D + 16 * (w & 3) + c];
+        b2w = f32x4{bb, bb, bb, bb};
+    }
+    // row layout (waves 0-3): token r, features f0 .. f0+3
+    const int r = 4 * (w & 3) + g, f0 = 4 * c;
+    float gam[4], bet[4];
+    bool ident = true;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        gam[e] = gamma[static_cast<size_t>(h) * D + f0 + e];
+        bet[e] = beta[static_cast<size_t>(h) * D + f0 + e];
+        ident = ident && gam[e] == 1.0f && bet[e] == 0.0f;
+    }
+    ident = __all(ident);  // every wave covers all 64 features: same vote everywhere
+
+    const s16x4 ones = {0x3F80, 0x3F80, 0x3F80, 0x3F80};  // bf16 1.0
+    s16x4 eye;  // identity as a B operand: B[k = 4g + i][n = c]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) eye[i] = (4 * g + i == c) ? 0x3F80 : 0;
+    const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 tmask;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tmask[i] = (4 * g + i <= c) ? 1.f : 0.f;
+
+    // ---- input rows of this lane's token, one chunk ahead (waves 0-3) --------
+    const bf16_t *xq = XQ + xbase, *xk = XK + xbase, *xv = XV + xbase;
+    const float *et = eta + static_cast<size_t>(seq) * L;
+    PrepRegs R;
+    auto load = [&](int ch) {
+        const uint32_t tok = static_cast<uint32_t>(min(ch * MB + r, L - 1));
+        const uint32_t off = tok * D + f0;
+        R.q = *reinterpret_cast<const uint2 *>(xq + off);
+        R.k = *reinterpret_cast<const uint2 *>(xk + off);
+        R.v = *reinterpret_cast<const uint2 *>(xv + off);
+        R.eta = et[tok];
+    };
+    auto stage = [&](int ch) {
+        Slot &S = sm.slot[ch & 1];
+        const bool ok = ch * MB + r < L;
+        const uint2 z2 = make_uint2(0u, 0u);
+        const uint2 q = ok ? R.q : z2, k = ok ? R.k : z2, v = ok ? R.v : z2;
+        *reinterpret_cast<uint2 *>(&S.xq[r * RS + f0]) = q;
+        *reinterpret_cast<uint2 *>(&S.xk[r * RS + f0]) = k;
+        S.xkt[(f0 + 0) * KS + r] = static_cast<uint16_t>(k.x & 0xffffu);
+        S.xkt[(f0 + 1) * KS + r] = static_cast<uint16_t>(k.x >> 16);
+        S.xkt[(f0 + 2) * KS + r] = static_cast<uint16_t>(k.y & 0xffffu);
+        S.xkt[(f0 + 3) * KS + r] = static_cast<uint16_t>(k.y >> 16);
+        *reinterpret_cast<f32x4 *>(&S.xqf[r * RS + f0]) = unpack4(q);
+        const f32x4 tau = unpack4(v) - unpack4(k);
+        *reinterpret_cast<f32x4 *>(&S.tau[r * RS + f0]) = tau;
+        const float mt = row16_sum((tau[0] + tau[1]) + (tau[2] + tau[3])) * (1.0f / D);
+        if (c == 0) {
+            S.mutau[r] = mt;
+            S.eta[r] = ok ? R.eta : 0.f;
+        }
+    };
+    if (roww && nch > 0) {
+        load(0);
+        stage(0);
+        load(1);
+    }
+    lds_barrier();
+
+    auto w1frag = [&](int t, int kb) { return pack8(W1v[t][2 * kb], W1v[t][2 * kb + 1]); };
+
+    for (int ch = 0; ch < nch; ++ch) {
+        const Slot &S = sm.slot[ch & 1];
+        float *P = sm.part[w] + (4 * g) * RS + c;
+
+        // ===== A: Z1^T, A = gelu(Z1), Z2 partials, T1, A transposed ============
+        bf16x8 xkf[2], xqf[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            xkf[kb] = row_frag(S.xk, c, g, kb);
+            xqf[kb] = row_frag(S.xq, c, g, kb);
+        }
+        f32x4 Aact[2], Ap[2], zq[2];  // [hid 16t + 4g + i][token c]
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const bf16x8 wa = w1frag(t, 0), wb = w1frag(t, 1);
+            f32x4 z = mfma32(wa, xkf[0], b1v[t]);
+            z = mfma32(wb, xkf[1], z);
+            zq[t] = mfma32(wb, xqf[1], mfma32(wa, xqf[0], b1v[t]));  // (XQ W1 + b1)^T
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float Phi, phi;
+                normal_cdf_pdf(z[i], Phi, phi);
+                Aact[t][i] = z[i] * Phi;
+                Ap[t][i] = fmaf(z[i], phi, Phi);
+            }
+        }
+        const bf16x8 Af = pack8(Aact[0], Aact[1]);  // A operand [m = token c][k = this wave's hidden]
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            // chunk-start W2 as B operand [k = hidden][n = out]; b2 tile u added by wave u
+            const f32x4 acc = mfma32(Af, pack8(W2v[u][0], W2v[u][1]), w == u ? b2w : fzero);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) P[i * RS + 16 * u] = acc[i];
+        }
+        f32x4 gt = fzero;  // [s = 4g+i][t = c] = XQ_t . XK_s
+        gt = mfma32(xkf[0], xqf[0], gt);
+        gt = mfma32(xkf[1], xqf[1], gt);
+        f32x4 tv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tv[i] = fmaf(gt[i], tmask[i], tmask[i]);
+        const s16x4 T1b = pack4(tv);  // T1^T as a B operand: [k = s][n = t]
+        s16x4 Atr[2];                 // A[token 4g+i][hid 16t + c]
+#pragma unroll
+        for (int t = 0; t < 2; ++t) Atr[t] = pack4(mfma16(pack4(Aact[t]), eye, fzero));
+        lds_barrier();
+
+        // ===== B (row layout): Z2 -> E2 =====================================
+        if (roww) {
+            f32x4 z2 = *reinterpret_cast<const f32x4 *>(&sm.part[0][r * RS + f0]);
+#pragma unroll
+            for (int q = 1; q < NW; ++q) z2 += *reinterpret_cast<const f32x4 *>(&sm.part[q][r * RS + f0]);
+            const f32x4 tau = *reinterpret_cast<const f32x4 *>(&S.tau[r * RS + f0]);
+            const f32x4 ev = ident ? ln_bwd_row<true>(z2, tau, S.mutau[r], S.eta[r], gam, bet, eps)
+                                   : ln_bwd_row<false>(z2, tau, S.mutau[r], S.eta[r], gam, bet, eps);
+            const uint32_t p01 = pack2(ev[0], ev[1]), p23 = pack2(ev[2], ev[3]);
+            *reinterpret_cast<uint2 *>(&sm.e2[r * RS + f0]) = make_uint2(p01, p23);
+            sm.e2t[(f0 + 0) * KS + r] = static_cast<uint16_t>(p01 & 0xffffu);
+            sm.e2t[(f0 + 1) * KS + r] = static_cast<uint16_t>(p01 >> 16);
+            sm.e2t[(f0 + 2) * KS + r] = static_cast<uint16_t>(p23 & 0xffffu);
+            sm.e2t[(f0 + 3) * KS + r] = static_cast<uint16_t>(p23 >> 16);
+        }
+        lds_barrier();
+
+        // ===== C: E1, Zb1^T, Ab, Gram partials, Zb2 partials, state update ===
+        // Repack W2 here rather than keep the packed copy of phase A alive
+        // across the row-layout phase (the empty asm hides the equality).
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) asm volatile("" : "+v"(W2v[u][rb]));
+        bf16x8 W2f[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) W2f[u] = pack8(W2v[u][0], W2v[u][1]);
+        bf16x8 e2f[2];  // E2 rows: B operand [k = out][n = token c]
+        s16x4 e2b[4];   // E2 as B operand [k = token 4g+i][n = out 16u + c]
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) e2f[kb] = row_frag(sm.e2, c, g, kb);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            e2b[u] = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(&sm.e2t[(16 * u + c) * KS + 4 * g]));
+        s16x4 E1tr[2];  // E1[token 4g+i][hid 16t + c]
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            // W2 rows of hidden tile t, transposed: [out 16u + 4g + i][hid 16t + c]
+            f32x4 w2t[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint4 pk = __builtin_bit_cast(uint4, W2f[u]);
+                const s16x4 half = __builtin_bit_cast(s16x4, t ? make_uint2(pk.z, pk.w) : make_uint2(pk.x, pk.y));
+                w2t[u] = mfma16(half, eye, fzero);
+            }
+            f32x4 g1 = fzero;  // (E2 W2^T)^T: [hid 16t + 4g + i][token c]
+            g1 = mfma32(pack8(w2t[0], w2t[1]), e2f[0], g1);
+            g1 = mfma32(pack8(w2t[2], w2t[3]), e2f[1], g1);
+            E1tr[t] = pack4(mfma16(pack4(g1 * Ap[t]), eye, fzero));
+        }
+        f32x4 Ab[2];  // gelu(Zb1)^T: [hid 16t + 4g + i][token c]
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const f32x4 zb = mfma16(E1tr[t], T1b, zq[t]);  // + (T1 E1)^T
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float Phi, phi;
+                normal_cdf_pdf(zb[i], Phi, phi);
+                Ab[t][i] = zb[i] * Phi;
+            }
+        }
+        const bf16x8 Abf = pack8(Ab[0], Ab[1]);
+        // [s = 4g+i][t = c] = sum over this wave's hidden units of A_s . Ab_t
+        *reinterpret_cast<f32x4 *>(&sm.gram[w][c * GS + 4 * g]) = mfma32(Af, Abf, fzero);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const f32x4 acc = mfma32(Abf, W2f[u], fzero);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) P[i * RS + 16 * u] = acc[i];
+        }
+        // state update (the forward products above used the chunk-start state)
+        {
+            s16x4 xkt[4];  // XK^T as A operand [m = in 16rb + c][k = token 4g+i]
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+                xkt[rb] = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(&S.xkt[(16 * rb + c) * KS + 4 * g]));
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) W1v[t][rb] = mfma16(xkt[rb], E1tr[t], W1v[t][rb]);
+                b1v[t] = mfma16(E1tr[t], ones, b1v[t]);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) W2v[u][rb] = mfma16(Atr[rb], e2b[u], W2v[u][rb]);
+        }
+        lds_barrier();
+
+        // ===== D: T2 E2 + b2 for output tile w (waves 0-3) ===================
+        if (roww) {
+            f32x4 g2 = *reinterpret_cast<const f32x4 *>(&sm.gram[0][c * GS + 4 * g]);
+#pragma unroll
+            for (int q = 1; q < NW; ++q) g2 += *reinterpret_cast<const f32x4 *>(&sm.gram[q][c * GS + 4 * g]);
+            f32x4 t2;  // T2 as the A operand: [m = t = c][k = s = 4g+i]
+#pragma unroll
+            for (int i = 0; i < 4; ++i) t2[i] = fmaf(g2[i], tmask[i], tmask[i]);
+            const s16x4 e2w = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(&sm.e2t[(16 * w + c) * KS + 4 * g]));
+            const f32x4 corr = mfma16(pack4(t2), e2w, b2w);
+            float *Q = sm.part[NW] + (4 * g) * RS + 16 * w + c;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Q[i * RS] = corr[i];
+            b2w = mfma16(ones, e2w, b2w);
+        }
+        lds_barrier();
+
+        // ===== E (row layout): stage the next chunk, O = XQ + LN(Zb2) ========
+        if (roww) {
+            f32x4 zb2 = *reinterpret_cast<const f32x4 *>(&sm.part[0][r * RS + f0]);
+#pragma unroll
+            for (int q = 1; q <= NW; ++q) zb2 += *reinterpret_cast<const f32x4 *>(&sm.part[q][r * RS + f0]);
+            const f32x4 xqv = *reinterpret_cast<const f32x4 *>(&S.xqf[r * RS + f0]);
+            if (ch + 1 < nch) {
+                stage(ch + 1);
+                load(ch + 2);
+            }
+            const f32x4 o = ident ? ln_fwd_row<true>(zb2, xqv, gam, bet, eps)
+                                  : ln_fwd_row<false>(zb2, xqv, gam, bet, eps);
+            if (ch * MB + r < L)
+                *reinterpret_cast<uint2 *>(O + xbase + static_cast<uint32_t>((ch * MB + r) * D + f0)) =
+                    make_uint2(pack2(o[0], o[1]), pack2(o[2], o[3]));
+        }
+        lds_barrier();
+    }
+
+    if (W1_out) {
+        // Recompute the lane coordinates here (opaque copy) instead of keeping
+        // the store addresses alive through the chunk loop.
+        int lane2 = lane;
+        asm volatile("" : "+v"(lane2));
+        const int g = lane2 >> 4, c = lane2 & 15;
+        float *W1d = W1_out + static_cast<size_t>(seq) * D * M, *W2d = W2_out + static_cast<size_t>(seq) * M * D;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) W1d[(16 * rb + 4 * g + i) * M + hw + 16 * t + c] = W1v[t][rb][i];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) W2d[(hw + 16 * rb + 4 * g + i) * D + 16 * u + c] = W2v[u][rb][i];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) b1_out[static_cast<size_t>(seq) * M + hw + 16 * t + 4 * g + i] = b1v[t][i];
+        if (roww && g == 0) b2_out[static_cast<size_t>(seq) * D + 16 * w + c] = b2w[0];
+    }
+}
+
+bool mlp_mfma_supported(const MLPArgs &a) { return a.io == 1 && a.d == 64 && a.mb == 16; }
+
+hipError_t launch_mlp_mfma(const MLPArgs &a, hipStream_t stream) {
+    if (a.B * a.H == 0) return hipSuccess;
+    hipLaunchKernelGGL(mlp_prefill_mfma, dim3(a.B * a.H), dim3(NT), 0, stream, a.H, a.L, a.eps,
+                       static_cast<const bf16_t *>(a.XQ), static_cast<const bf16_t *>(a.XK),
+                       static_cast<const bf16_t *>(a.XV), a.eta, a.W1, a.b1, a.W2, a.b2,
+                       a.w0_batched, a.gamma, a.beta, static_cast<bf16_t *>(a.O), a.W1_out,
+                       a.b1_out, a.W2_out, a.b2_out);
+    return hipGetLastError();
+}
+
+}  // namespace ttt
