@@ -8,35 +8,47 @@
 //   O_c    = XQ_c + LN(Zbar_c)
 //   W_{c+1} = W_c + XK_c^T E_c ;  b_{c+1} = b_c + 1^T E_c
 //
-// The serial chain runs through Z -> E -> state. Two exact rewrites shorten it:
-//  * look-ahead: Z_{c+1} = P_{c+1} + K_c E_c with P_{c+1} = XK_{c+1} W_c + b_c
-//    and K_c = XK_{c+1} XK_c^T + 1 (both known one chunk early), so between
-//    two layer-norm backwards sits a single 16x16x16 MFMA;
-//  * with gamma = 1, beta = 0 the gradient has the closed form
+// The serial chain runs Z_c -> E_c -> Z_{c+1}. Exact rewrites keep it short:
+//  * two-step look-ahead: with K(j, i) = XK_j XK_i^T + 1 (the +1 is the bias
+//    path),
+//      Z_{c+1} = [XK_{c+1} W_{c-1} + b_{c-1} + K(c+1, c-1) E_{c-1}] + K(c+1, c) E_c,
+//    so only the last product waits for E_c and the state update never sits
+//    on the chain;
+//  * the layer-norm backward needs one round of per-token row sums: with
+//    gamma = 1, beta = 0 three (z, z^2, tau z) and
 //      G = a (z - mu) - rstd (tau - mean tau),
-//      a = rstd^2 (eps rstd^2 + rstd (mean(tau z) - mean(tau) mu)),
-//    which needs one round of row sums (z, z^2, tau z) instead of two.
+//      a = rstd^2 (eps rstd^2 + rstd (mean(tau z) - mean(tau) mu));
+//    otherwise seven (z, z^2, g^2 z, g^2 z^2, g b z, g tau z, g tau), from
+//    which mean(ghat) and mean(ghat xhat) follow in closed form.
 //
-// Layout (gfx950, one 512-thread workgroup per (n,h) sequence):
-//  * waves 0-3 compute. Wave w owns columns 16w..16w+15 of the fp32 state:
-//    lane (g = lane/16, c = lane%16) holds W[16 rb + 4 g + i][16 w + c] --
-//    the output layout of the 16x16x16 MFMA that applies the update and, with
-//    the contraction index permuted identically on both operands, the
-//    B-operand layout of the 16x16x32 MFMAs that form XK W and XQ W. The bias
-//    lives alongside and is updated by an MFMA with an all-ones A operand.
-//    MFMA operands are bf16; state and accumulation are fp32.
-//  * row-wise layer-norm work uses a row layout: 16 lanes per token, four
-//    consecutive features each, DPP row reductions; tiles cross between the
-//    MFMA layout and the row layout through LDS.
-//  * waves 4-7 prepare inputs: 8-byte loads issued four chunks ahead into a
-//    register ring (these waves never store, so their load waits stay
-//    precise), then bf16 rows, the transposed XK, fp32 XQ, the target
-//    XV - XK with its row mean, and eta are staged in a 5-chunk LDS ring.
-//  * per chunk two barriers: phase X (MFMA layout: Z_c, Zbar_{c-1}; row
-//    layout: O_{c-2}) and phase Y (row layout: E_c; MFMA layout: state update
-//    with E_{c-1}, P_{c+1}, XQ_c W_c, Gram, K_c).
-#include <type_traits>
-
+// Layout (gfx950, one 768-thread workgroup = 12 waves per (n,h) sequence):
+//  * feature-major tiles: the products are formed transposed, [feature][token],
+//    so lane (g = lane/16, c = lane%16) of a wave with feature tile u holds
+//    features 16u + 4g .. +3 of token c. A token's row sum is four in-lane
+//    values, a sum over the four lane rows (two lane swaps) and a sum over
+//    the four waves of a role (a few floats per token through LDS).
+//  * chain waves 0-3 (tile u = wave): Z^T = E^T K^T + bracket, the row sums,
+//    E, and E transposed into the operand layout [feature][token] by an MFMA
+//    with the identity (exact: the bf16 values pass through unchanged).
+//  * state waves 4-7 (tile u = wave - 4) hold W[:, 16u .. 16u+15] and b as
+//    fp32 MFMA accumulators for the whole sequence: lane (g, c) holds
+//    W[16 rb + 4 g + i][16 u + c], the output layout of the XK^T E update
+//    and, with the contraction index permuted identically on both operands,
+//    the A-operand layout of W^T XK^T. They apply the updates, form the
+//    brackets, K, XQ W + b and T, and emit O = XQ + LN(Zbar).
+//  * prep waves 8-11 stream chunks three ahead into a 5-slot LDS ring and
+//    form the token x token operands K(j, j-1), K(j, j-2) and T_j once per
+//    chunk (they depend on the inputs only).
+//  * LDS traffic is the scarce resource: operand fragments are 16 contiguous
+//    bytes (the contraction order of the 16x16x32 products puts input
+//    features 32 kb + 8 g .. +7 in lane row g; W's accumulator rows follow
+//    that order), bf16 rows are padded to 72 elements and the row-sum
+//    exchange to 36 floats per token so 16-byte accesses of eight
+//    consecutive lanes hit distinct banks.
+//  * two barriers per chunk. Phase 1: chain Z_c and its partial row sums;
+//    state waves apply E_{c-1} and start O_{c-1}. Phase 2: chain E_c; state
+//    waves finish O_{c-1} and prepare the operands of chunks c .. c+2.
+//  MFMA operands are bf16; state, accumulation and row statistics are fp32.
 #include "launch.hpp"
 #include "tile.hpp"
 
@@ -45,180 +57,410 @@ namespace {
 
 using namespace tile;
 
-constexpr int NCW = 4, NPW = 4, NT = 64 * (NCW + NPW);
-constexpr int NSLOT = 5;  // LDS ring: chunks c-2 .. c+2
+constexpr int NCW = 4, NSW = 4, NPW = 4, NW = NCW + NSW + NPW, NT = 64 * NW;
+constexpr int NSLOT = 5, AHEAD = 3;
+constexpr int RB = 72;  // row stride (bf16) of the staged XQ / XK rows
+constexpr int SB = 36;  // per-token stride (floats) of the row-sum exchange
+
+// One staged chunk.
+struct alignas(16) LSlot {
+    alignas(16) uint16_t xq[MB * RB];  // bf16 rows
+    alignas(16) uint16_t xk[MB * RB];  // bf16 rows
+    alignas(16) uint16_t xkt[D * KS];  // bf16, [permuted feature][token]
+    alignas(16) float tau[MB * RS];    // XV - XK, fp32 rows
+    alignas(16) float eta[MB];
+};
 
 struct alignas(16) Smem {
-    Slot slot[NSLOT];
-    alignas(16) float z[MB * RS];          // Z_c
-    alignas(16) float zbar[2][MB * RS];    // Zbar, two chunks in flight
-    alignas(16) uint16_t e[MB * RS];       // E_c, bf16 rows
+    LSlot slot[NSLOT];
+    alignas(16) float stb[MB * SB];  // LN-backward partial row sums [token][value][chain wave]
+    alignas(16) float stf[MB * SB];  // LN-forward partial row sums [token][value][state wave]
+    alignas(16) uint2 ea[NCW][64];   // E of the newest chunk, bf16 operand layout, per tile
+    alignas(16) f32x4 q[2][NCW][64];    // bracket of Z_j^T per tile, by chunk parity
+    // token x token operands (B layout [k = s][n = t], bf16), by chunk parity:
+    alignas(16) uint2 ka[2][64];        // K(j, j-1)
+    alignas(16) uint2 k2[2][64];        // K(j, j-2)
+    alignas(16) uint2 tb[2][64];        // T_j^T
 };
 
 struct Ctx {
     int L, nch, iters;
     float eps;
-    bf16_t *Oseq;  // output rows of this sequence
 };
 
-// Compute waves: the chain and the output, two barriers per iteration.
-// The state is kept as MFMA accumulators: Wv[rb] holds rows 16 rb + 4 g .. +3
-// of column 16 w + c, bv holds b[16 w + c] in all four slots.
-template <bool IDENT>
-__device__ __forceinline__ void compute_loop(Smem &sm, const Ctx &cx, int w, int g, int c,
-                                             f32x4 (&Wv)[4], f32x4 &bv, const float (&gam)[4],
-                                             const float (&bet)[4]) {
-    const int col = 16 * w + c;           // MFMA layout column
-    const int r = 4 * w + g, f0 = 4 * c;  // row layout token / first feature
-    const int nch = cx.nch;
-    const s16x4 ones = {0x3F80, 0x3F80, 0x3F80, 0x3F80};  // bf16 1.0
-    const s16x4 zero4 = {0, 0, 0, 0};
-    const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
-    // causal mask of T[t = c][s = 4g + i] as 0/1 factors: T = (Gram + 1) * m
-    f32x4 tmask;
+__device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+__device__ __forceinline__ s16x4 ld_s4(const void *p) {
+    return __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(p));
+}
+__device__ __forceinline__ void st_s4(void *p, s16x4 v) {
+    *reinterpret_cast<uint2 *>(p) = __builtin_bit_cast(uint2, v);
+}
+__device__ __forceinline__ float sum4(f32x4 v) { return (v[0] + v[1]) + (v[2] + v[3]); }
+
+// Input feature held in row m = 4 g + i of the state accumulator Wv[rb]:
+// pack8(Wv[2 kb], Wv[2 kb + 1]) then covers features 32 kb + 8 g .. +7.
+__device__ __forceinline__ int win(int rb, int m) {
+    return 32 * (rb >> 1) + 8 * (m >> 2) + 4 * (rb & 1) + (m & 3);
+}
+// Row of the transposed XK tile that holds feature f (so that row 16 rb + m
+// holds feature win(rb, m), the order the update's A operand needs).
+__device__ __forceinline__ int xkt_row(int f) {
+    return 16 * (2 * (f >> 5) + ((f >> 2) & 1)) + 4 * ((f >> 3) & 3) + (f & 3);
+}
+// 16x16x32 operand fragment of a bf16 row tile: row c, features 32 kb + 8 g .. +7.
+__device__ __forceinline__ bf16x8 frag(const uint16_t *rows, int c, int g, int kb) {
+    return *reinterpret_cast<const bf16x8 *>(&rows[c * RB + 32 * kb + 8 * g]);
+}
+
+// ---------------------------------------------------------------------------
+// Prep waves: HBM -> registers -> LDS ring. Chunk j lives in slot j % NSLOT;
+// chunk it + AHEAD is staged at the start of iteration it (chunks 0 ..
+// AHEAD-1 before the two prologue barriers). Loads run NSET chunks ahead of
+// their staging and are unconditional (addresses clamped into the sequence,
+// values past its end zeroed when staged); these waves never store to
+// global memory, so their waits on the load counter stay precise.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void prep_waves(Smem &sm, int pw, int g, int c, int lane, const bf16_t *xq,
+                                           const bf16_t *xk, const bf16_t *xv, const float *et,
+                                           int L, int iters) {
+    constexpr int PRE = 2, BPI = 2;
+    LSlot *slots = sm.slot;
+    const int r = 4 * pw + g, f0 = 4 * c;  // token, first feature
+    const int kr = xkt_row(f0);            // features f0 .. f0+3 -> rows kr .. kr+3
+    if (L == 0) {  // same barrier count as the other waves
+        for (int it = 0; it < PRE + iters * BPI; ++it) lds_barrier();
+        return;
+    }
+    const char *bq = reinterpret_cast<const char *>(xq), *bk = reinterpret_cast<const char *>(xk),
+               *bv = reinterpret_cast<const char *>(xv);
+    auto load = [&](PrepRegs &R, int ch) {
+        const uint32_t tok = static_cast<uint32_t>(min(ch * MB + r, L - 1));
+        const uint32_t off = (tok * D + f0) * 2u;  // bytes, 32-bit
+        R.q = *reinterpret_cast<const uint2 *>(bq + off);
+        R.k = *reinterpret_cast<const uint2 *>(bk + off);
+        R.v = *reinterpret_cast<const uint2 *>(bv + off);
+        R.eta = et[tok];
+    };
+    auto stage_rows = [&](LSlot &S, uint2 q, uint2 k, uint2 v, float e) {
+        *reinterpret_cast<uint2 *>(&S.xq[r * RB + f0]) = q;
+        *reinterpret_cast<uint2 *>(&S.xk[r * RB + f0]) = k;
+        S.xkt[(kr + 0) * KS + r] = static_cast<uint16_t>(k.x & 0xffffu);
+        S.xkt[(kr + 1) * KS + r] = static_cast<uint16_t>(k.x >> 16);
+        S.xkt[(kr + 2) * KS + r] = static_cast<uint16_t>(k.y & 0xffffu);
+        S.xkt[(kr + 3) * KS + r] = static_cast<uint16_t>(k.y >> 16);
+        *reinterpret_cast<f32x4 *>(&S.tau[r * RS + f0]) = unpack4(v) - unpack4(k);
+        if (c == 0) S.eta[r] = e;
+    };
+    auto stage = [&](const PrepRegs &R, int ch, int slot) {
+        LSlot &S = slots[slot];
+        if (ch * MB + MB <= L) {  // whole chunk inside the sequence (uniform)
+            stage_rows(S, R.q, R.k, R.v, R.eta);
+        } else {
+            const bool ok = ch * MB + r < L;
+            const uint2 z2 = make_uint2(0u, 0u);
+            stage_rows(S, ok ? R.q : z2, ok ? R.k : z2, ok ? R.v : z2, ok ? R.eta : 0.f);
+        }
+    };
+    const f32x4 fzero = {0.f, 0.f, 0.f, 0.f}, fone = {1.f, 1.f, 1.f, 1.f};
+    f32x4 tmask;  // causal mask of T^T[s = 4g + i][t = c]
 #pragma unroll
     for (int i = 0; i < 4; ++i) tmask[i] = (4 * g + i <= c) ? 1.f : 0.f;
-
-    auto cvt_state = [&](bf16x8 (&wb)[2]) {
+    // [s = 4g + i][t = c] = A_s . B_t + init for bf16 row tiles A, B, packed
+    auto gram = [&](const uint16_t *A, const uint16_t *B, f32x4 init) {
+        return mfma32(frag(A, c, g, 1), frag(B, c, g, 1), mfma32(frag(A, c, g, 0), frag(B, c, g, 0), init));
+    };
+    auto tmat = [&](const LSlot &S) {  // T^T of a chunk as a B operand
+        const f32x4 gt = gram(S.xk, S.xq, fzero);
+        f32x4 tv;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-            wb[kb] = __builtin_bit_cast(
-                bf16x8, make_uint4(pack2(Wv[2 * kb][0], Wv[2 * kb][1]), pack2(Wv[2 * kb][2], Wv[2 * kb][3]),
-                                   pack2(Wv[2 * kb + 1][0], Wv[2 * kb + 1][1]),
-                                   pack2(Wv[2 * kb + 1][2], Wv[2 * kb + 1][3])));
+        for (int i = 0; i < 4; ++i) tv[i] = fmaf(gt[i], tmask[i], tmask[i]);
+        return pack4(tv);
     };
 
-    // P_0 = XK_0 W_0 + b_0
-    f32x4 P = bv, Zq = fzero;
-    s16x4 Ka = zero4, Ta = zero4;
-    if (nch > 0) {
-        bf16x8 wb[2];
-        cvt_state(wb);
+    PrepRegs R[NSET];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) P = mfma32(row_frag(sm.slot[0].xk, c, g, kb), wb[kb], P);
+    for (int k = 0; k < NSET; ++k) load(R[k], k);
+#pragma unroll
+    for (int a = 0; a < AHEAD; ++a) {
+        stage(R[a], a, a % NSLOT);
+        load(R[a], a + NSET);
+    }
+    lds_barrier();
+    // prologue operands: K(1, 0) and T_0
+    if (pw == 1) st_s4(&sm.ka[1][lane], pack4(gram(slots[0].xk, slots[1].xk, fone)));
+    if (pw == 2) st_s4(&sm.tb[0][lane], tmat(slots[0]));
+    lds_barrier();
+    int slot = AHEAD % NSLOT;  // slot of chunk it + AHEAD
+    for (int it = 0; it < iters; it += NSET) {
+#pragma unroll
+        for (int k = 0; k < NSET; ++k) {
+            const int ks = (k + AHEAD) % NSET;
+            stage(R[ks], it + k + AHEAD, slot);
+            load(R[ks], it + k + AHEAD + NSET);
+            lds_barrier();
+            // phase 2: K(j+2, j), K(j+2, j+1) and T_{j+1} for j = it + k
+            const int s2 = slot == 0 ? NSLOT - 1 : slot - 1;  // chunk j+2
+            const int s1 = s2 == 0 ? NSLOT - 1 : s2 - 1;      // chunk j+1
+            const int s0 = s1 == 0 ? NSLOT - 1 : s1 - 1;      // chunk j
+            const int par = (it + k) & 1;                     // parity of j (= of j+2)
+            if (pw == 0) st_s4(&sm.k2[par][lane], pack4(gram(slots[s0].xk, slots[s2].xk, fone)));
+            if (pw == 1) st_s4(&sm.ka[par][lane], pack4(gram(slots[s1].xk, slots[s2].xk, fone)));
+            if (pw == 2) st_s4(&sm.tb[par ^ 1][lane], tmat(slots[s1]));
+            slot = (slot + 1 == NSLOT) ? 0 : slot + 1;
+            lds_barrier();
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Chain waves: Z_c^T (feature tile u) -> row sums -> E_c -> operand layout.
+// ---------------------------------------------------------------------------
+template <bool IDENT>
+__device__ __forceinline__ void chain_waves(Smem &sm, const Ctx &cx, int u, int g, int c, int lane,
+                                            const float *gam_h, const float *bet_h) {
+    constexpr float inv_d = 1.0f / D;
+    const int f0 = 16 * u + 4 * g;  // first feature of this lane
+    s16x4 eye;                      // identity as a B operand: B[k = 4g + i][n = c]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) eye[i] = (4 * g + i == c) ? 0x3F80 : 0;
+    const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
+
+    // general layer norm: this lane's gamma and beta, and per-head sums
+    f32x4 gm = {1.f, 1.f, 1.f, 1.f}, bt = fzero;
+    float Sg2 = static_cast<float>(D), Sgb = 0.f;
+    if constexpr (!IDENT) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            gm[i] = gam_h[f0 + i];
+            bt[i] = bet_h[f0 + i];
+        }
+        const float ga = gam_h[lane], ba = bet_h[lane];  // one feature per lane
+        Sg2 = rows4_sum(row16_sum(ga * ga));
+        Sgb = rows4_sum(row16_sum(ga * ba));
+    }
+    const f32x4 g2 = gm * gm, gb = gm * bt;
+
+    lds_barrier();  // prologue chunks staged
+    lds_barrier();  // first bracket and K written
+    if (cx.nch == 0) {
+        for (int it = 0; it < 2 * cx.iters; ++it) lds_barrier();
+        return;
+    }
+    f32x4 Q = sm.q[0][u][lane];  // bracket of Z_0: XK_0 W_0 + b_0
+    s16x4 EA = {0, 0, 0, 0};     // E_{c-1}, A operand [m = feature 16u + c][k = token 4g + i]
+    s16x4 KB = {0, 0, 0, 0};     // K(c, c-1) as the B operand [k = s][n = t]
+    int sc = 0;                  // slot of chunk it
+
+    float *stw = &sm.stb[c * SB + u];  // this wave's column of token c
+
+    for (int it = 0; it < cx.nch; ++it) {
+        const LSlot &S = sm.slot[sc];
+        // ===== phase 1: Z^T and partial row sums ==============================
+        const f32x4 z = mfma16(EA, KB, Q);  // [feature f0 + i][token c]
+        const f32x4 tau = ld4(&S.tau[c * RS + f0]);
+        // lane row g receives this tile's partial sum number g of token c
+        if constexpr (IDENT) {
+            stw[4 * g] = rows4_reduce4(sum4(z), sum4(z * z), sum4(tau * z), sum4(tau));
+        } else {
+            const f32x4 g2z = g2 * z, gt = gm * tau;
+            stw[4 * g] = rows4_reduce4(sum4(z), sum4(z * z), sum4(g2z), sum4(g2z * z));
+            stw[16 + 4 * g] = rows4_reduce4(sum4(gb * z), sum4(gt * z), sum4(gt), 0.f);
+        }
+        lds_barrier();
+
+        // ===== phase 2: E_c, transposed into the operand layout =============
+        const f32x4 Qn = sm.q[(it + 1) & 1][u][lane];        // bracket of Z_{it+1}
+        const s16x4 Kn = ld_s4(&sm.ka[(it + 1) & 1][lane]);  // K(it+1, it)
+        const float et = S.eta[c];
+        f32x4 ev;
+        // lane row g adds value g over the four waves; the gather hands every
+        // lane all four totals
+        const f32x4 s = rows4_gather(sum4(ld4(&sm.stb[c * SB + 4 * g])));
+        if constexpr (IDENT) {  // s = sums of z, z^2, tau z, tau
+            const float mut = s[3] * inv_d;
+            const float mu = s[0] * inv_d;
+            const float var = fmaxf(fmaf(s[1], inv_d, -mu * mu), 0.f);
+            const float r = rsq(var + cx.eps);
+            const float mtz = fmaf(s[2], inv_d, -mut * mu);
+            const float r2 = r * r;
+            const float a = r2 * fmaf(r, mtz, cx.eps * r2);
+            // E = -eta (a (z - mu) - r (tau - mean tau)) = cz z + ct tau + c0
+            const float cz = -et * a, ct = et * r;
+            const float c0 = et * fmaf(a, mu, -r * mut);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ev[i] = fmaf(cz, z[i], fmaf(ct, tau[i], c0));
+        } else {
+            const f32x4 s2 = rows4_gather(sum4(ld4(&sm.stb[c * SB + 16 + 4 * g])));
+            const float mu = s[0] * inv_d;
+            const float var = fmaxf(fmaf(s[1], inv_d, -mu * mu), 0.f);
+            const float r = rsq(var + cx.eps);
+            // mean(ghat) and mean(ghat xhat), ghat = gamma (gamma xhat + beta - tau)
+            const float m1 = (fmaf(r, fmaf(-mu, Sg2, s[2]), Sgb) - s2[2]) * inv_d;
+            const float q2 = fmaf(mu, fmaf(mu, Sg2, -2.f * s[2]), s[3]);       // sum g^2 (z - mu)^2
+            const float q1 = fmaf(-mu, Sgb, s2[0]) - fmaf(-mu, s2[2], s2[1]);  // sum g (b - tau)(z - mu)
+            const float m2 = fmaf(r * r, q2, r * q1) * inv_d;
+            // E = -eta r [r (g^2 - m2)(z - mu) + g (b - tau) - m1]
+            const float k1 = -et * r * r, k2 = -et * r, k3 = et * r * m1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                ev[i] = fmaf(k1 * (g2[i] - m2), z[i] - mu, fmaf(k2 * gm[i], bt[i] - tau[i], k3));
+        }
+        // [token c][feature f0 + i] as the A operand times the identity gives
+        // [token 4g + i][feature 16u + c]: E^T in the operand layout.
+        EA = pack4(mfma16(pack4(ev), eye, fzero));
+        st_s4(&sm.ea[u][lane], EA);
+        Q = Qn;
+        KB = Kn;
+        sc = (sc + 1 == NSLOT) ? 0 : sc + 1;
+        lds_barrier();
+    }
+    for (int it = cx.nch; it < cx.iters; ++it) {
+        lds_barrier();
+        lds_barrier();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// State waves: W, b of feature tile u; brackets and K; outputs.
+// ---------------------------------------------------------------------------
+template <bool IDENT>
+__device__ __forceinline__ void state_waves(Smem &sm, const Ctx &cx, int u, int g, int c, int lane,
+                                            const float *W0s, const float *b0s, const float *gam_h,
+                                            const float *bet_h, bf16_t *Oseq, float *W_out,
+                                            float *b_out) {
+    constexpr float inv_d = 1.0f / D;
+    const int f0 = 16 * u + 4 * g;
+    const s16x4 ones = {0x3F80, 0x3F80, 0x3F80, 0x3F80};  // bf16 1.0
+    const f32x4 fzero = {0.f, 0.f, 0.f, 0.f}, fone = {1.f, 1.f, 1.f, 1.f};
+
+    f32x4 Wv[4];  // W[16 rb + 4g + i][16u + c]
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Wv[rb][i] = W0s[win(rb, 4 * g + i) * D + 16 * u + c];
+    f32x4 bv = ld4(b0s + f0);  // b[f0 + i]
+    f32x4 gm = fone, bt = fzero;
+    if constexpr (!IDENT) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            gm[i] = gam_h[f0 + i];
+            bt[i] = bet_h[f0 + i];
+        }
+    }
+    auto wfrag = [&](int kb) { return pack8(Wv[2 * kb], Wv[2 * kb + 1]); };  // A: [m = out][k = in]
+    auto xfrag = [&](const uint16_t *rows, int kb) { return frag(rows, c, g, kb); };
+    // [feature f0 + i][token c] = (X W + b)^T for a bf16 row tile X
+    auto xw = [&](const bf16x8 (&wf)[2], const uint16_t *rows) {
+        return mfma32(wf[1], xfrag(rows, 1), mfma32(wf[0], xfrag(rows, 0), bv));
+    };
+
+    lds_barrier();  // prologue chunks 0 .. 2 staged
+    f32x4 Pp = fzero;  // XK_{j+2} W_j + b_j, waiting for E_j
+    if (cx.nch > 0) {
+        const bf16x8 wf[2] = {wfrag(0), wfrag(1)};
+        sm.q[0][u][lane] = xw(wf, sm.slot[0].xk);  // bracket of Z_0 = XK_0 W_0 + b_0
+        Pp = xw(wf, sm.slot[1].xk);                // XK_1 W_0 + b_0 (E_{-1} = 0)
+    }
+    lds_barrier();
+
+    f32x4 Zq = fzero;  // (XQ_j W_j + b_j)^T of the chunk awaiting its E
+    int sm1 = NSLOT - 1, s0 = 0, s1 = 1, s2 = 2;  // slots of chunks it-1 .. it+2
+
+    // One iteration: apply E_{it-1} and emit O_{it-1} (upd); write the bracket
+    // of Z_{it+1} and prepare the operands of chunks it .. it+2 (fwd). Each
+    // phase issues all of its LDS reads first, so one round trip covers them.
+    auto iteration = [&](int it, bool upd, bool fwd) {
+        // ===== phase 1 ==========================================================
+        s16x4 EAp = {0, 0, 0, 0}, xkt[4], K2 = {0, 0, 0, 0}, TB;
+        if (upd) {
+            const LSlot &P = sm.slot[sm1];
+            EAp = ld_s4(&sm.ea[u][lane]);  // E_{it-1}, A operand [feature][token]
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) xkt[rb] = ld_s4(&P.xkt[(16 * rb + c) * KS + 4 * g]);
+            K2 = ld_s4(&sm.k2[(it + 1) & 1][lane]);  // K(it+1, it-1)
+            TB = ld_s4(&sm.tb[(it - 1) & 1][lane]);  // T_{it-1}^T
+        }
+        __builtin_amdgcn_sched_barrier(0);  // all reads of the phase in flight together
+        if (fwd) sm.q[(it + 1) & 1][u][lane] = upd ? mfma16(EAp, K2, Pp) : Pp;
+        f32x4 zb = fzero;
+        if (upd) {
+            zb = mfma16(EAp, TB, Zq);  // Zbar_{it-1}^T
+            // rows 0, 1 receive the tile's sum of zb, rows 2, 3 that of zb^2
+            sm.stf[c * SB + 4 * g + u] = rows4_reduce2(sum4(zb), sum4(zb * zb));
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) Wv[rb] = mfma16(xkt[rb], EAp, Wv[rb]);
+            bv = mfma16(EAp, ones, bv);
+        }
+        lds_barrier();
+
+        // ===== phase 2 ==========================================================
+        f32x4 st;
+        uint2 xqb;
+        bf16x8 q0[2], k2[2];
+        if (upd) {
+            st = ld4(&sm.stf[c * SB + 4 * (g & 2)]);  // rows 0, 1: sums of zb; rows 2, 3: of zb^2
+            xqb = *reinterpret_cast<const uint2 *>(&sm.slot[sm1].xq[c * RB + f0]);
+        }
+        if (fwd) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                k2[kb] = xfrag(sm.slot[s2].xk, kb);
+                q0[kb] = xfrag(sm.slot[s0].xq, kb);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (fwd) {
+            const bf16x8 wf[2] = {wfrag(0), wfrag(1)};
+            Pp = mfma32(wf[1], k2[1], mfma32(wf[0], k2[0], bv));  // XK_{it+2} W_it + b_it
+            Zq = mfma32(wf[1], q0[1], mfma32(wf[0], q0[0], bv));  // XQ_it W_it + b_it
+        }
+        if (upd) {
+            const uint32_t sb = __float_as_uint(sum4(st));
+            const auto tt = __builtin_amdgcn_permlane32_swap(sb, sb, false, false);
+            const float t1 = __uint_as_float(tt[0]), t2 = __uint_as_float(tt[1]);
+            const float mu = t1 * inv_d;
+            const f32x4 xq = unpack4(xqb);
+            const float r = rsq(fmaxf(fmaf(t2, inv_d, -mu * mu), 0.f) + cx.eps);
+            f32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if constexpr (IDENT)
+                    o[i] = fmaf(zb[i] - mu, r, xq[i]);
+                else
+                    o[i] = xq[i] + fmaf(gm[i], (zb[i] - mu) * r, bt[i]);
+            }
+            uint2 ov = make_uint2(pack2(o[0], o[1]), pack2(o[2], o[3]));
+            asm volatile("" : "+v"(ov));  // keep the math out of the store's branch
+            const int tok = (it - 1) * MB + c;
+            if (tok < cx.L) *reinterpret_cast<uint2 *>(Oseq + static_cast<uint32_t>(tok * D + f0)) = ov;
+        }
+        sm1 = s0;
+        s0 = s1;
+        s1 = s2;
+        s2 = (s2 + 1 == NSLOT) ? 0 : s2 + 1;
+        lds_barrier();
+    };
+
+    const int nch = cx.nch;
+    int it = 0;
+    if (nch > 0) {
+        iteration(0, false, true);
+        for (it = 1; it < nch; ++it) iteration(it, true, true);
+        iteration(nch, true, false);
+        it = nch + 1;
+    }
+    for (; it < cx.iters; ++it) {
+        lds_barrier();
+        lds_barrier();
     }
 
-    const uint16_t *Ecol = sm.e + (4 * g) * RS + col;  // E[4g + i][col] at Ecol[i * RS]
-    float *Zw = sm.z + (4 * g) * RS + col;             // MFMA-layout writes
-    const float *Zr = sm.z + r * RS + f0;              // row-layout reads
-    int sc = 0, sp = NSLOT - 1, sp2 = NSLOT - 2, sn = 1;  // slots of chunks it, it-1, it-2, it+1
-
-    // One iteration. chain: Z_it and E_it; upd: apply E_{it-1}; out: O_{it-2}.
-    // In the steady state all three hold and the body is one straight block,
-    // so the scheduler can interleave its independent LDS, MFMA and VALU work.
-    auto iteration = [&](int it, auto chain_t, auto upd_t, auto out_t, bool chain_r, bool upd_r,
-                         bool out_r) {
-        constexpr bool CT = decltype(chain_t)::value, UT = decltype(upd_t)::value,
-                       OT = decltype(out_t)::value;
-        const bool chain = CT || chain_r, upd = UT || upd_r, out = OT || out_r;
-
-        // ===== phase X ========================================================
-        // Every LDS read of the phase is issued before any LDS write (the
-        // compiler cannot reorder them past writes it cannot disambiguate).
-        s16x4 eb = zero4;  // E_{it-1} as the B operand: E[4g + i][col]
-        if (upd) {
-            const uint32_t e01 = static_cast<uint32_t>(Ecol[0]) | (static_cast<uint32_t>(Ecol[RS]) << 16);
-            const uint32_t e23 = static_cast<uint32_t>(Ecol[2 * RS]) | (static_cast<uint32_t>(Ecol[3 * RS]) << 16);
-            eb = __builtin_bit_cast(s16x4, make_uint2(e01, e23));
-        }
-        f32x4 zbr = fzero, xqr = fzero;
-        if (out) {
-            zbr = *reinterpret_cast<const f32x4 *>(&sm.zbar[it & 1][r * RS + f0]);  // Zbar_{it-2}
-            xqr = *reinterpret_cast<const f32x4 *>(&sm.slot[sp2].xqf[r * RS + f0]);
-        }
-        f32x4 z = P, zb = fzero;
-        if (chain && (UT || it > 0)) z = mfma16(Ka, eb, P);
-        if (upd) zb = mfma16(Ta, eb, Zq);
-        f32x4 o = fzero;
-        if (out) o = ln_fwd_row<IDENT>(zbr, xqr, gam, bet, cx.eps);
-        if (chain) {
+    if (W_out) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Zw[i * RS] = z[i];
-        }
-        if (upd) {
-            float *Zb = sm.zbar[(it - 1) & 1] + (4 * g) * RS + col;
+        for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Zb[i * RS] = zb[i];
-        }
-        if (out) {
-            const int oc = it - 2;
-            if (oc * MB + r < cx.L)
-                *reinterpret_cast<uint2 *>(cx.Oseq + static_cast<uint32_t>((oc * MB + r) * D + f0)) =
-                    make_uint2(pack2(o[0], o[1]), pack2(o[2], o[3]));
-        }
-        lds_barrier();
-
-        // ===== phase Y ========================================================
-        const Slot &S = sm.slot[sc], &N = sm.slot[sn];
-        f32x4 zz = fzero, tau = fzero;
-        float mutau = 0.f, eta_r = 0.f;
-        bf16x8 akc[2], aqc[2], akn[2];
-        s16x4 ka[4];
-        if (chain) {
-            zz = *reinterpret_cast<const f32x4 *>(Zr);
-            tau = *reinterpret_cast<const f32x4 *>(&S.tau[r * RS + f0]);
-            mutau = S.mutau[r];
-            eta_r = S.eta[r];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                akc[kb] = row_frag(S.xk, c, g, kb);
-                aqc[kb] = row_frag(S.xq, c, g, kb);
-                akn[kb] = row_frag(N.xk, c, g, kb);
-            }
-        }
-        if (upd) {
-            const uint16_t *XKT = sm.slot[sp].xkt + c * KS + 4 * g;
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
-                ka[rb] = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(XKT + 16 * rb * KS));
-        }
-        // state update with E_{it-1}
-        if (upd) {
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) Wv[rb] = mfma16(ka[rb], eb, Wv[rb]);
-            bv = mfma16(ones, eb, bv);
-        }
-        // chain: E_it (the critical path of the loop) goes out first
-        if (chain) {
-            const f32x4 ev = ln_bwd_row<IDENT>(zz, tau, mutau, eta_r, gam, bet, cx.eps);
-            *reinterpret_cast<uint2 *>(&sm.e[r * RS + f0]) = make_uint2(pack2(ev[0], ev[1]), pack2(ev[2], ev[3]));
-        }
-        if (chain) {
-            bf16x8 wb[2];
-            cvt_state(wb);
-            f32x4 p = bv, zq = bv, gt = fzero, kt = fzero;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                p = mfma32(akn[kb], wb[kb], p);
-                zq = mfma32(aqc[kb], wb[kb], zq);
-                gt = mfma32(akc[kb], aqc[kb], gt);  // [s = 4g+i][t = c] = XQ_t . XK_s
-                kt = mfma32(akc[kb], akn[kb], kt);  // [s = 4g+i][t = c] = XK_{it+1, t} . XK_{it, s}
-            }
-            P = p;
-            Zq = zq;
-            // A operands (row t = c, contraction s = 4g + i)
-            Ta = __builtin_bit_cast(s16x4, make_uint2(pack2(fmaf(gt[0], tmask[0], tmask[0]), fmaf(gt[1], tmask[1], tmask[1])),
-                                                      pack2(fmaf(gt[2], tmask[2], tmask[2]), fmaf(gt[3], tmask[3], tmask[3]))));
-            Ka = __builtin_bit_cast(s16x4, make_uint2(pack2(kt[0] + 1.f, kt[1] + 1.f), pack2(kt[2] + 1.f, kt[3] + 1.f)));
-        }
-        lds_barrier();
-        // rotate the ring
-        sp2 = sp;
-        sp = sc;
-        sc = sn;
-        sn = (sn + 1 == NSLOT) ? 0 : sn + 1;
-    };
-
-    using F = std::false_type;
-    using T = std::true_type;
-    const int steady_end = max(nch, 2);
-    int it = 0;
-    for (; it < min(2, cx.iters); ++it)  // warm-up: no update / no output yet
-        iteration(it, F{}, F{}, F{}, it < nch, it >= 1 && it <= nch, false);
-    for (; it < steady_end; ++it)        // steady state: branch-free body
-        iteration(it, T{}, T{}, T{}, true, true, true);
-    for (; it < cx.iters; ++it)          // drain (and padding to the prep ring)
-        iteration(it, F{}, F{}, F{}, it < nch, it >= 1 && it <= nch, it >= 2 && it <= nch + 1);
+            for (int i = 0; i < 4; ++i) W_out[win(rb, 4 * g + i) * D + 16 * u + c] = Wv[rb][i];
+    }
+    if (b_out && c == 0) *reinterpret_cast<f32x4 *>(b_out + f0) = bv;
 }
 
 }  // namespace
@@ -239,56 +481,35 @@ __global__ __launch_bounds__(NT) void linear_prefill_mfma(
     Ctx cx;
     cx.L = L;
     cx.nch = (L + MB - 1) / MB;
-    cx.iters = (cx.nch + 2 + NSET - 1) / NSET * NSET;  // whole turns of the prep ring
+    cx.iters = (cx.nch + 1 + NSET - 1) / NSET * NSET;  // whole turns of the prep ring
     cx.eps = eps;
     const size_t xbase = static_cast<size_t>(seq) * L * D;
-    cx.Oseq = O + xbase;
+    const float *gam_h = gamma + static_cast<size_t>(h) * D, *bet_h = beta + static_cast<size_t>(h) * D;
 
-    if (w >= NCW) {
-        // prep waves: chunk it + 2 is staged during iteration it; two barriers
-        // per iteration
-        prep_waves<NSLOT, 2, 2>(sm.slot, w - NCW, g, c, XQ + xbase, XK + xbase, XV + xbase,
-                                eta + static_cast<size_t>(seq) * L, L, cx.iters);
+    if (w >= NCW + NSW) {
+        prep_waves(sm, w - NCW - NSW, g, c, lane, XQ + xbase, XK + xbase, XV + xbase,
+                   eta + static_cast<size_t>(seq) * L, L, cx.iters);
         return;
     }
+    // gamma = 1 and beta = 0 over the head (one feature per lane; same vote in every wave)
+    const bool ident = __all(gam_h[lane] == 1.0f && bet_h[lane] == 0.0f);
 
-    // =========== compute waves ==============================================
-    const size_t wofs = (w0_batched ? static_cast<size_t>(n) * H * D * D : 0) + static_cast<size_t>(h) * D * D;
-    const size_t bofs = (w0_batched ? static_cast<size_t>(n) * H * D : 0) + static_cast<size_t>(h) * D;
-    const int col = 16 * w + c;
-    f32x4 Wv[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Wv[rb][i] = W0[wofs + static_cast<size_t>(16 * rb + 4 * g + i) * D + col];
-    const float b_init = b0[bofs + col];
-    f32x4 bv = {b_init, b_init, b_init, b_init};
-    float gam[4], bet[4];
-    bool ident = true;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        gam[e] = gamma[static_cast<size_t>(h) * D + 4 * c + e];
-        bet[e] = beta[static_cast<size_t>(h) * D + 4 * c + e];
-        ident = ident && gam[e] == 1.0f && bet[e] == 0.0f;
+    if (w < NCW) {
+        if (ident)
+            chain_waves<true>(sm, cx, w, g, c, lane, gam_h, bet_h);
+        else
+            chain_waves<false>(sm, cx, w, g, c, lane, gam_h, bet_h);
+        return;
     }
-    // every compute wave covers all 64 features in its row layout, so the
-    // wave-wide vote is the same in all four waves
-    ident = __all(ident);
-
-    lds_barrier();
+    const size_t st = (w0_batched ? static_cast<size_t>(n) * H : 0) + static_cast<size_t>(h);
+    float *Wd = W_out ? W_out + static_cast<size_t>(seq) * D * D : nullptr;
+    float *bd = b_out ? b_out + static_cast<size_t>(seq) * D : nullptr;
     if (ident)
-        compute_loop<true>(sm, cx, w, g, c, Wv, bv, gam, bet);
+        state_waves<true>(sm, cx, w - NCW, g, c, lane, W0 + st * D * D, b0 + st * D, gam_h, bet_h,
+                          O + xbase, Wd, bd);
     else
-        compute_loop<false>(sm, cx, w, g, c, Wv, bv, gam, bet);
-
-    if (W_out) {
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                W_out[static_cast<size_t>(seq) * D * D + static_cast<size_t>(16 * rb + 4 * g + i) * D + col] = Wv[rb][i];
-    }
-    if (b_out && g == 0) b_out[static_cast<size_t>(seq) * D + col] = bv[0];
+        state_waves<false>(sm, cx, w - NCW, g, c, lane, W0 + st * D * D, b0 + st * D, gam_h, bet_h,
+                           O + xbase, Wd, bd);
 }
 
 bool linear_mfma_supported(const LinearArgs &a) { return a.io == 1 && a.d == 64 && a.mb == 16; }

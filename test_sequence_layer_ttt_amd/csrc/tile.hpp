@@ -1,6 +1,6 @@
 // Shared pieces of the MFMA prefill kernels (gfx950): operand types, bf16
-// packing, DPP row reductions, LDS-only barriers, row-layout layer norms, and
-// the prep waves that stream Q/K/V chunks from HBM into an LDS ring.
+// packing, DPP and lane-swap row reductions, LDS-only barriers, row-layout
+// layer norms and the staged-chunk layout.
 //
 // Layout conventions (d = 64, chunks of MB = 16 tokens):
 //  * MFMA layout: lane (g = lane/16, c = lane%16) of a 16x16 tile holds rows
@@ -56,6 +56,54 @@ __device__ __forceinline__ float row16_sum(float v) {
     v = dpp_add<0x140>(v);  // row_mirror
     return v;
 }
+
+// Sum over the four DPP rows (lanes c, c+16, c+32, c+48); every lane receives
+// the total, bitwise identical across the four rows. Each step swaps halves
+// (v_permlane32_swap), then odd and even rows (v_permlane16_swap), and adds.
+__device__ __forceinline__ float rows4_sum(float v) {
+    const uint32_t b = __float_as_uint(v);
+    const auto h = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    v = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+    const uint32_t b2 = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane16_swap(b2, b2, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Four row sums at once (butterfly over the four DPP rows): the lane in row
+// k (= lane / 16) receives the sum of v_k over lanes c, c+16, c+32, c+48.
+// The half swap pairs (v0, v2) and (v1, v3), the row swap pairs the results.
+__device__ __forceinline__ float rows4_reduce4(float v0, float v1, float v2, float v3) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v0), __float_as_uint(v2), false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v1), __float_as_uint(v3), false, false);
+    const float A = __uint_as_float(a[0]) + __uint_as_float(a[1]);  // rows 0,1: v0; rows 2,3: v2
+    const float B = __uint_as_float(b[0]) + __uint_as_float(b[1]);  // rows 0,1: v1; rows 2,3: v3
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(A), __float_as_uint(B), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Two row sums at once: rows 0 and 1 receive the sum of v0, rows 2 and 3 that of v1.
+__device__ __forceinline__ float rows4_reduce2(float v0, float v1) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v0), __float_as_uint(v1), false, false);
+    const float A = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const uint32_t b = __float_as_uint(A);
+    const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Inverse of the row reductions: the lane in row k holds S_k; every lane
+// receives (S_0, S_1, S_2, S_3). Element 0 of a swap result is the first
+// operand's new value, element 1 the second's.
+__device__ __forceinline__ f32x4 rows4_gather(float x) {
+    const uint32_t b = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane32_swap(b, b, false, false);  // rows (S0,S1,S0,S1), (S2,S3,S2,S3)
+    const auto lo = __builtin_amdgcn_permlane16_swap(a[0], a[0], false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap(a[1], a[1], false, false);
+    return f32x4{__uint_as_float(lo[0]), __uint_as_float(lo[1]), __uint_as_float(hi[0]),
+                 __uint_as_float(hi[1])};
+}
+
+// 1/sqrt(x) for a normal (non-denormal) x: one v_rsq_f32, no rescaling.
+__device__ __forceinline__ float rsq(float x) { return __builtin_amdgcn_rsqf(x); }
 
 // Barrier for LDS hand-offs only: waits for this wave's LDS operations, not
 // for its outstanding global loads or stores.
@@ -174,80 +222,6 @@ struct PrepRegs {
     uint2 q, k, v;  // 4 bf16 features of one token
     float eta;
 };
-
-// Prep waves: stream chunks HBM -> registers -> LDS ring. Chunk j lives in
-// slots[j % NSLOT]; chunk it + AHEAD is staged during compute iteration it
-// (chunks 0 .. AHEAD-1 before the first barrier), each iteration ends with
-// BPI barriers, and `iters` is a multiple of NSET. Loads are issued NSET
-// chunks before their staging and unconditionally (addresses clamped into
-// the sequence, values past its end zeroed when staged); these waves never
-// store to global memory, so their waits on the load counter stay precise.
-template <int NSLOT, int AHEAD, int BPI>
-__device__ __forceinline__ void prep_waves(Slot *slots, int pw, int g, int c, const bf16_t *xq,
-                                           const bf16_t *xk, const bf16_t *xv, const float *et,
-                                           int L, int iters) {
-    const int r = 4 * pw + g, f0 = 4 * c;  // token, first feature
-    if (L == 0) {  // same barrier count as the compute waves
-        lds_barrier();
-        for (int it = 0; it < iters * BPI; ++it) lds_barrier();
-        return;
-    }
-    auto load = [&](PrepRegs &R, int ch) {
-        const uint32_t tok = static_cast<uint32_t>(min(ch * MB + r, L - 1));
-        const uint32_t off = tok * D + f0;
-        R.q = *reinterpret_cast<const uint2 *>(xq + off);
-        R.k = *reinterpret_cast<const uint2 *>(xk + off);
-        R.v = *reinterpret_cast<const uint2 *>(xv + off);
-        R.eta = et[tok];
-    };
-    auto stage_rows = [&](Slot &S, uint2 q, uint2 k, uint2 v, float e) {
-        *reinterpret_cast<uint2 *>(&S.xq[r * RS + f0]) = q;
-        *reinterpret_cast<uint2 *>(&S.xk[r * RS + f0]) = k;
-        S.xkt[(f0 + 0) * KS + r] = static_cast<uint16_t>(k.x & 0xffffu);
-        S.xkt[(f0 + 1) * KS + r] = static_cast<uint16_t>(k.x >> 16);
-        S.xkt[(f0 + 2) * KS + r] = static_cast<uint16_t>(k.y & 0xffffu);
-        S.xkt[(f0 + 3) * KS + r] = static_cast<uint16_t>(k.y >> 16);
-        *reinterpret_cast<f32x4 *>(&S.xqf[r * RS + f0]) = unpack4(q);
-        const f32x4 tau = unpack4(v) - unpack4(k);
-        *reinterpret_cast<f32x4 *>(&S.tau[r * RS + f0]) = tau;
-        const float mt = row16_sum((tau[0] + tau[1]) + (tau[2] + tau[3])) * (1.0f / D);
-        if (c == 0) {
-            S.mutau[r] = mt;
-            S.eta[r] = e;
-        }
-    };
-    auto stage = [&](const PrepRegs &R, int ch, int slot) {
-        Slot &S = slots[slot];
-        if (ch * MB + MB <= L) {  // whole chunk inside the sequence (uniform)
-            stage_rows(S, R.q, R.k, R.v, R.eta);
-        } else {
-            const bool ok = ch * MB + r < L;
-            const uint2 z2 = make_uint2(0u, 0u);
-            stage_rows(S, ok ? R.q : z2, ok ? R.k : z2, ok ? R.v : z2, ok ? R.eta : 0.f);
-        }
-    };
-    PrepRegs R[NSET];
-#pragma unroll
-    for (int k = 0; k < NSET; ++k) load(R[k], k);
-#pragma unroll
-    for (int a = 0; a < AHEAD; ++a) {
-        stage(R[a], a, a % NSLOT);
-        load(R[a], a + NSET);
-    }
-    lds_barrier();
-    int slot = AHEAD % NSLOT;  // slot of chunk it + AHEAD
-    for (int it = 0; it < iters; it += NSET) {
-#pragma unroll
-        for (int k = 0; k < NSET; ++k) {
-            const int ks = (k + AHEAD) % NSET;
-            stage(R[ks], it + k + AHEAD, slot);
-            load(R[ks], it + k + AHEAD + NSET);
-            slot = (slot + 1 == NSLOT) ? 0 : slot + 1;
-#pragma unroll
-            for (int b = 0; b < BPI; ++b) lds_barrier();
-        }
-    }
-}
 
 }  // namespace tile
 }  // namespace ttt
