@@ -66,7 +66,7 @@ constexpr int SB = 36;  // per-token stride (floats) of the row-sum exchange
 struct alignas(16) LSlot {
     alignas(16) uint16_t xq[MB * RB];  // bf16 rows
     alignas(16) uint16_t xk[MB * RB];  // bf16 rows
-    alignas(16) uint16_t xkt[D * KS];  // bf16, [permuted feature][token]
+    alignas(16) uint16_t xkt[D * KS + 16];  // bf16, [permuted feature][token], see xkt_at
     alignas(16) float tau[MB * RS];    // XV - XK, fp32 rows
     alignas(16) float eta[MB];
 };
@@ -107,6 +107,11 @@ __device__ __forceinline__ int win(int rb, int m) {
 __device__ __forceinline__ int xkt_row(int f) {
     return 16 * (2 * (f >> 5) + ((f >> 2) & 1)) + 4 * ((f >> 3) & 3) + (f & 3);
 }
+// Element offset of (row, token) in the transposed XK tile. Each group of 16
+// rows is shifted by two dwords so that the prep waves' stores (rows 16 apart
+// in one instruction) fall into distinct banks; a reader's 16 rows share a
+// group.
+__device__ __forceinline__ int xkt_at(int row, int tok) { return row * KS + 4 * (row >> 4) + tok; }
 // 16x16x32 operand fragment of a bf16 row tile: row c, features 32 kb + 8 g .. +7.
 __device__ __forceinline__ bf16x8 frag(const uint16_t *rows, int c, int g, int kb) {
     return *reinterpret_cast<const bf16x8 *>(&rows[c * RB + 32 * kb + 8 * g]);
@@ -114,11 +119,14 @@ __device__ __forceinline__ bf16x8 frag(const uint16_t *rows, int c, int g, int k
 
 // ---------------------------------------------------------------------------
 // Prep waves: HBM -> registers -> LDS ring. Chunk j lives in slot j % NSLOT;
-// chunk it + AHEAD is staged at the start of iteration it (chunks 0 ..
-// AHEAD-1 before the two prologue barriers). Loads run NSET chunks ahead of
-// their staging and are unconditional (addresses clamped into the sequence,
-// values past its end zeroed when staged); these waves never store to
-// global memory, so their waits on the load counter stay precise.
+// chunk it + AHEAD is staged in phase 1 of iteration it (chunks 0 .. AHEAD-1
+// before the prologue barriers). Loads run NSET chunks ahead of their
+// staging and are unconditional (addresses clamped into the sequence, values
+// past its end zeroed when staged); these waves never store to global
+// memory, so their waits on the load counter stay precise. In phase 2 of
+// iteration j they form K(j+2, j), K(j+2, j+1) and T_{j+1}; each is read in
+// the next iteration (T_{j+1} in the one after) and rewritten two
+// iterations later.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void prep_waves(Smem &sm, int pw, int g, int c, int lane, const bf16_t *xq,
                                            const bf16_t *xk, const bf16_t *xv, const float *et,
@@ -144,10 +152,10 @@ __device__ __forceinline__ void prep_waves(Smem &sm, int pw, int g, int c, int l
     auto stage_rows = [&](LSlot &S, uint2 q, uint2 k, uint2 v, float e) {
         *reinterpret_cast<uint2 *>(&S.xq[r * RB + f0]) = q;
         *reinterpret_cast<uint2 *>(&S.xk[r * RB + f0]) = k;
-        S.xkt[(kr + 0) * KS + r] = static_cast<uint16_t>(k.x & 0xffffu);
-        S.xkt[(kr + 1) * KS + r] = static_cast<uint16_t>(k.x >> 16);
-        S.xkt[(kr + 2) * KS + r] = static_cast<uint16_t>(k.y & 0xffffu);
-        S.xkt[(kr + 3) * KS + r] = static_cast<uint16_t>(k.y >> 16);
+        S.xkt[xkt_at(kr + 0, r)] = static_cast<uint16_t>(k.x & 0xffffu);
+        S.xkt[xkt_at(kr + 1, r)] = static_cast<uint16_t>(k.x >> 16);
+        S.xkt[xkt_at(kr + 2, r)] = static_cast<uint16_t>(k.y & 0xffffu);
+        S.xkt[xkt_at(kr + 3, r)] = static_cast<uint16_t>(k.y >> 16);
         *reinterpret_cast<f32x4 *>(&S.tau[r * RS + f0]) = unpack4(v) - unpack4(k);
         if (c == 0) S.eta[r] = e;
     };
@@ -186,7 +194,7 @@ __device__ __forceinline__ void prep_waves(Smem &sm, int pw, int g, int c, int l
         load(R[a], a + NSET);
     }
     lds_barrier();
-    // prologue operands: K(1, 0) and T_0
+    // prologue operands K(1, 0) and T_0
     if (pw == 1) st_s4(&sm.ka[1][lane], pack4(gram(slots[0].xk, slots[1].xk, fone)));
     if (pw == 2) st_s4(&sm.tb[0][lane], tmat(slots[0]));
     lds_barrier();
@@ -195,14 +203,15 @@ __device__ __forceinline__ void prep_waves(Smem &sm, int pw, int g, int c, int l
 #pragma unroll
         for (int k = 0; k < NSET; ++k) {
             const int ks = (k + AHEAD) % NSET;
-            stage(R[ks], it + k + AHEAD, slot);
-            load(R[ks], it + k + AHEAD + NSET);
-            lds_barrier();
-            // phase 2: K(j+2, j), K(j+2, j+1) and T_{j+1} for j = it + k
+            // phase 1: stage chunk j+3 (j = it + k), load chunk j+3+NSET
             const int s2 = slot == 0 ? NSLOT - 1 : slot - 1;  // chunk j+2
             const int s1 = s2 == 0 ? NSLOT - 1 : s2 - 1;      // chunk j+1
             const int s0 = s1 == 0 ? NSLOT - 1 : s1 - 1;      // chunk j
-            const int par = (it + k) & 1;                     // parity of j (= of j+2)
+            stage(R[ks], it + k + AHEAD, slot);
+            load(R[ks], it + k + AHEAD + NSET);
+            lds_barrier();
+            // phase 2: K(j+2, j), K(j+2, j+1) and T_{j+1}
+            const int par = (it + k) & 1;  // parity of j (= of j+2)
             if (pw == 0) st_s4(&sm.k2[par][lane], pack4(gram(slots[s0].xk, slots[s2].xk, fone)));
             if (pw == 1) st_s4(&sm.ka[par][lane], pack4(gram(slots[s1].xk, slots[s2].xk, fone)));
             if (pw == 2) st_s4(&sm.tb[par ^ 1][lane], tmat(slots[s1]));
@@ -376,7 +385,7 @@ __device__ __forceinline__ void state_waves(Smem &sm, const Ctx &cx, int u, int 
             const LSlot &P = sm.slot[sm1];
             EAp = ld_s4(&sm.ea[u][lane]);  // E_{it-1}, A operand [feature][token]
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) xkt[rb] = ld_s4(&P.xkt[(16 * rb + c) * KS + 4 * g]);
+            for (int rb = 0; rb < 4; ++rb) xkt[rb] = ld_s4(&P.xkt[xkt_at(16 * rb + c, 4 * g)]);
             K2 = ld_s4(&sm.k2[(it + 1) & 1][lane]);  // K(it+1, it-1)
             TB = ld_s4(&sm.tb[(it - 1) & 1][lane]);  // T_{it-1}^T
         }
