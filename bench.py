@@ -6,7 +6,14 @@ already resident in HBM. Prints ONE JSON line (metric, tokens/s, roofline of
 the prefill kernel measured with HIP events on the launch stream, and the
 fp64 CPU oracle timed on the host cores on the same workload).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Other workloads of the same hot path (--workload):
+  2   TTT-Linear prefill, B=4, H=12, L=2048 (RMS-normalised inputs)
+  5p  TTT-Linear prefill, B=1, H=32, L=32768
+  4   TTT-MLP prefill, B=2, H=12, L=8192 (roofline: bf16 MFMA)
+  5d  TTT-Linear decode: one b=1 step on 64 x 32 states (roofline: state bytes)
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+                       [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -21,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, datasheet
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, datasheet
 WORKLOAD = 3
 METRIC = "TTT layer tokens/s (dual-form prefill, L=8192) + % of roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_linear_prefill_workload3.json")
@@ -33,6 +41,18 @@ def alg_bytes_linear(B, H, L, d, s_in=2, s_out=2):
     per_token_head = 3 * d * s_in + 4 + d * s_out
     state = 2 * (d * d + d) * 4
     return B * H * L * per_token_head + B * H * state
+
+
+def alg_flops_mlp(B, H, L, d, b=16):
+    """Algorithmic flops of one TTT-MLP prefill launch (dual form, hidden 4d):
+    56 d^2 + 20 b d per token-head."""
+    return B * H * L * (56 * d * d + 20 * b * d)
+
+
+def alg_bytes_decode(B, H, d, s_in=2, s_out=2):
+    """Algorithmic HBM bytes of one decode step: each fp32 state (W, b) read and
+    written once, xq/xk/xv and eta read, o written."""
+    return B * H * (2 * (d * d + d) * 4 + 3 * d * s_in + 4 + d * s_out)
 
 
 def kernel_sources_hash():
@@ -73,6 +93,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="3", choices=["3", "2", "5p", "4", "5d"])
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -99,8 +120,15 @@ def main():
         print(json.dumps({"copy_bytes_each_way": n, "launches": max(1, args.steps)}))
         return
 
-    w = gen.WORKLOADS[WORKLOAD]
-    x = gen.make_workload(WORKLOAD)
+    if args.workload == "4":
+        return bench_mlp(args)
+    if args.workload == "5d":
+        return bench_decode(args)
+    wl = {"3": 3, "2": 2, "5p": 5}[args.workload]
+    w = gen.WORKLOADS[wl]
+    x = gen.make_workload(wl, decode_steps=0) if wl == 5 else gen.make_workload(wl)
+    if wl == 5:
+        x = x[0]
     B, H, L, d = x.B, x.H, x.L, x.d
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -139,9 +167,9 @@ def main():
 
     ab = alg_bytes_linear(B, H, L, d)
     achieved = ab / kern_avg_s / 1e9
-    traffic = measured_traffic(ab)
+    traffic = measured_traffic(ab) if wl == WORKLOAD else None
     out = {
-        "metric": METRIC,
+        "metric": METRIC if wl == WORKLOAD else f"TTT-Linear prefill tokens/s (L={L})",
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -183,6 +211,132 @@ def main():
         out["parity_vs_oracle"] = {"O": rel(O, ro), "W_out": rel(Wo, rW), "b_out": rel(bo, rb),
                                    "tol": 2e-2}
     print(json.dumps(out), flush=True)
+
+
+def _timed(step, stream, warmup, K):
+    """Warm up, then time K steps: wall clock around all of them and HIP
+    events around each launch on the launch stream."""
+    import numpy as np
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[2 * i].record(stream)
+        step()
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = float(np.mean([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(K)])) / 1e3
+    return wall / K, kern
+
+
+def _line(metric, value, args, wall_step, dtype, config, roofline, extra=None):
+    out = {"metric": metric, "value": value, "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall_step * 1e3,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+           "data": "synthetic", "config": config, "roofline": roofline}
+    out.update(extra or {})
+    print(json.dumps(out), flush=True)
+
+
+def bench_mlp(args):
+    """TTT-MLP prefill, workload 4 (B=2, H=12, L=8192, d=64, hidden 256)."""
+    import numpy as np
+    import torch
+    from test_sequence_layer_ttt_amd import gen, ttt
+    x = gen.make_workload(4)
+    B, H, L, d = x.B, x.H, x.L, x.d
+    dev = torch.device("cuda:0")
+    T = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev).to(dt)
+    bf = torch.bfloat16
+    ins = [T(x.XQ, bf), T(x.XK, bf), T(x.XV, bf), T(x.eta), T(x.W1), T(x.b1), T(x.W2), T(x.b2),
+           T(x.gamma), T(x.beta)]
+    O = torch.empty_like(ins[0])
+    kw = dict(device=dev, dtype=torch.float32)
+    outs = (torch.empty((B, H, d, 4 * d), **kw), torch.empty((B, H, 4 * d), **kw),
+            torch.empty((B, H, 4 * d, d), **kw), torch.empty((B, H, d), **kw))
+    stream = torch.cuda.current_stream()
+    step = lambda: ttt.ttt_mlp_forward(*ins, O=O, outs=outs, ln_eps=x.eps, stream=stream)
+    wall, kern = _timed(step, stream, args.warmup, args.steps)
+    fl = alg_flops_mlp(B, H, L, d)
+    roof = {"bound": "mfma", "achieved": fl / kern / 1e12, "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": fl / kern / 1e12 / BF16_PEAK_TFLOPS, "traffic": None,
+            "kernel": "mlp_prefill", "kernel_avg_us": kern * 1e6, "alg_flops_per_launch": fl}
+    extra = {}
+    if not args.no_cpu_baseline:
+        import oracle
+        nt = cpu_threads()
+        Ls = 512  # bounded sample: the first 512 tokens of every sequence
+        sl = slice(0, Ls)
+        t1 = time.perf_counter()
+        oracle.mlp_forward(x.XQ[:, :, sl], x.XK[:, :, sl], x.XV[:, :, sl], x.eta[:, :, sl],
+                           x.W1, x.b1, x.W2, x.b2, x.gamma, x.beta, x.eps, mb=16, nthreads=nt)
+        tc = time.perf_counter() - t1
+        extra["cpu_baseline"] = {"value": B * Ls / tc, "unit": "tokens/s", "cores": nt,
+                                 "kind": "oracle",
+                                 "sample": f"first {Ls} tokens of each of the {B}x{H} sequences, "
+                                           f"fp64 primal form, {nt} threads, {tc:.2f} s"}
+    _line(f"TTT-MLP prefill tokens/s (L={L})", B * L / wall, args, wall, "bf16",
+          {"workload": gen.WORKLOADS[4].name, "B": B, "H": H, "L": L, "d": d, "hidden": 4 * d,
+           "mini_batch": 16, "io": "bf16", "state": "fp32", "parallelism": "none (1 GPU)"},
+          roof, extra)
+
+
+def bench_decode(args):
+    """One b=1 decode step on the 64 x 32 states of workload 5, each started
+    from the B=1, L=32768 prefill's final state."""
+    import numpy as np
+    import torch
+    from test_sequence_layer_ttt_amd import gen, ttt
+    nsteps = args.warmup + args.steps
+    pre, dec = gen.make_workload(5, decode_steps=nsteps)
+    dev = torch.device("cuda:0")
+    T = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev).to(dt)
+    bf = torch.bfloat16
+    _, Wp, bp = ttt.ttt_linear_forward(T(pre.XQ, bf), T(pre.XK, bf), T(pre.XV, bf), T(pre.eta),
+                                       T(pre.W0), T(pre.b0), T(pre.gamma), T(pre.beta),
+                                       ln_eps=pre.eps)
+    B, H, d = dec.B, dec.H, dec.d
+    W = Wp[0].expand(B, H, d, d).contiguous()
+    b = bp[0].expand(B, H, d).contiguous()
+    xq, xk, xv, et = T(dec.XQ, bf), T(dec.XK, bf), T(dec.XV, bf), T(dec.eta)
+    g, be = T(pre.gamma), T(pre.beta)
+    o = torch.empty((B, H, d), device=dev, dtype=bf)
+    stream = torch.cuda.current_stream()
+    it = [0]
+
+    def step():
+        i = it[0]
+        it[0] += 1
+        ttt.ttt_decode_step(xq[i], xk[i], xv[i], et[i], W, b, g, be, o=o, ln_eps=pre.eps,
+                            stream=stream)
+    wall, kern = _timed(step, stream, args.warmup, args.steps)
+    ab = alg_bytes_decode(B, H, d)
+    roof = {"bound": "hbm", "achieved": ab / kern / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": ab / kern / 1e9 / HBM_PEAK_GBS, "traffic": None, "kernel": "decode_step",
+            "kernel_avg_us": kern * 1e6, "alg_bytes_per_launch": ab}
+    extra = {}
+    if not args.no_cpu_baseline:
+        import oracle
+        nt = cpu_threads()
+        Wn = np.broadcast_to(Wp[0].cpu().numpy(), (B, H, d, d)).astype(np.float64)
+        bn = np.broadcast_to(bp[0].cpu().numpy(), (B, H, d)).astype(np.float64)
+        ns = 4  # bounded sample: four steps
+        t1 = time.perf_counter()
+        for s_ in range(ns):
+            oracle.decode_step(dec.XQ[s_], dec.XK[s_], dec.XV[s_], dec.eta[s_], Wn, bn,
+                               pre.gamma, pre.beta, pre.eps, nthreads=nt)
+        tc = time.perf_counter() - t1
+        extra["cpu_baseline"] = {"value": B * ns / tc, "unit": "tokens/s", "cores": nt,
+                                 "kind": "oracle",
+                                 "sample": f"{ns} steps on all {B}x{H} states, fp64, {nt} threads, "
+                                           f"{tc:.2f} s"}
+    _line("TTT-Linear decode tokens/s (64 sequences x 32 heads, b=1)", B / wall, args, wall,
+          "bf16", {"workload": "ttt_linear_decode_bf16_B64_H32_d64", "B": B, "H": H, "d": d,
+                   "io": "bf16", "state": "fp32", "parallelism": "none (1 GPU)"}, roof, extra)
 
 
 if __name__ == "__main__":

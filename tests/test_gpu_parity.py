@@ -148,6 +148,84 @@ def test_mlp_full_workload4():
     assert max(err.values()) <= P.TOL["bf16"], err
 
 
+@pytest.mark.parametrize("L", [0, 1, 16, 17])
+def test_mlp_bf16_short(L):
+    """MFMA path (bf16, mb = 16) at the lengths around one chunk, random LN and biases."""
+    x = gen.make_mlp(640 + L, 2, 3, L, 64, io="bf16", ln_random=True, b_random=True)
+    got = P.mlp_gpu(x)
+    ref = P.mlp_oracle(x)
+    assert got[0].shape == (2, 3, L, 64)
+    err = P.errors(got, ref, 6, MLP_NAMES)
+    _report(f"mlp bf16 L{L}", err)
+    if L == 0:  # the state passes through unchanged
+        for g_, r_ in zip(got[1:], (x.W1, x.b1, x.W2, x.b2)):
+            assert np.array_equal(g_, np.broadcast_to(r_, g_.shape))
+    assert max(err.values()) <= P.TOL["bf16"], err
+
+
+def test_mlp_in_place_resume():
+    """forward(L1) with the per-batch state updated in place, then forward(L2)
+    from it, matches the oracle's forward(L1 + L2)."""
+    x = gen.make_mlp(660, 2, 2, 112, 64, io="bf16", b_random=True)
+    dt = torch.bfloat16
+    st = [P.dev(np.broadcast_to(a, (2,) + a.shape)) for a in (x.W1, x.b1, x.W2, x.b2)]
+    outs = []
+    for s_ in (slice(0, 64), slice(64, 112)):
+        res = ttt.ttt_mlp_forward(P.dev(x.XQ[:, :, s_], dt), P.dev(x.XK[:, :, s_], dt),
+                                  P.dev(x.XV[:, :, s_], dt), P.dev(x.eta[:, :, s_]), *st,
+                                  P.dev(x.gamma), P.dev(x.beta), outs=tuple(st))
+        outs.append(P.to_np(res[0]))
+    torch.cuda.synchronize()
+    ref = P.mlp_oracle(x)
+    got = (np.concatenate(outs, 2),) + tuple(P.to_np(t) for t in st)
+    err = P.errors(got, ref, 4, MLP_NAMES)
+    _report("mlp in-place resume", err)
+    assert max(err.values()) <= P.TOL["bf16"], err
+
+
+def test_mlp_bitwise_repeatable():
+    x = gen.make_workload(4, L=16 * 20, B=1, H=3)
+    a = P.mlp_gpu(x)
+    b = P.mlp_gpu(x)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+# ---------------------------------------------------------------------------
+# Chunk-local parity: the oracle's state at the start of a sampled chunk is
+# handed to the kernel, which runs that one chunk; its outputs are compared
+# with the oracle's run of the same chunk from the same state. This checks
+# the kernel at depth without the chain's accumulated rounding.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("num,chunks", [(3, (0, 1, 255, 511)), (5, (1024, 2047))])
+def test_linear_chunk_local_teacher_forced(num, chunks):
+    x = gen.make_workload(num, decode_steps=0) if num == 5 else gen.make_workload(num)
+    if num == 5:
+        x = x[0]
+    B, H = x.B, x.H
+    worst = 0.0
+    for c in chunks:
+        t0 = 16 * c
+        pre = slice(0, t0)
+        cur = slice(t0, t0 + 16)
+        if t0 > 0:
+            _, Wc, bc = oracle.linear_forward(x.XQ[:, :, pre], x.XK[:, :, pre], x.XV[:, :, pre],
+                                              x.eta[:, :, pre], x.W0, x.b0, x.gamma, x.beta, x.eps)
+        else:
+            Wc = np.broadcast_to(x.W0, (B, H, 64, 64))
+            bc = np.broadcast_to(x.b0, (B, H, 64))
+        Wc = np.ascontiguousarray(Wc, np.float32)  # both sides start from the same fp32 state
+        bc = np.ascontiguousarray(bc, np.float32)
+        one = gen.LinearInputs(B, H, 16, 64, x.io, x.XQ[:, :, cur], x.XK[:, :, cur], x.XV[:, :, cur],
+                               x.eta[:, :, cur], Wc, bc, x.gamma, x.beta)
+        got = P.linear_gpu(one)
+        ref = P.linear_oracle(one)
+        err = P.errors(got, ref, B * H, LIN_NAMES)
+        _report(f"workload{num} chunk {c} teacher-forced", err)
+        worst = max(worst, max(err.values()))
+    assert worst <= P.TOL["bf16"], worst
+
+
 # ---------------------------------------------------------------------------
 # Decode (b = 1 primal step, state in place)
 # ---------------------------------------------------------------------------
