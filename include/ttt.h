@@ -55,7 +55,7 @@ extern "C" {
 
 #define TTT_OK 0
 #define TTT_E_NULL (-1)  /* a required pointer is NULL                          */
-#define TTT_E_SHAPE (-2) /* negative size, or unsupported d / mb               */
+#define TTT_E_SHAPE (-2) /* negative size, unsupported d / mb, or bad ln_eps  */
 #define TTT_E_DTYPE (-3) /* io is not TTT_F32 / TTT_BF16                       */
 #define TTT_E_ALIGN (-4) /* a pointer is not aligned as required               */
 #define TTT_E_ALIAS (-5) /* an output overlaps an input or another output      */
@@ -79,8 +79,14 @@ typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
  *   W_out, b_out : [B,H,d,d], [B,H,d] fp32, the final state; optional (NULL
  *              skips the store). With w0_batched == 1 they may be exactly
  *              W0 / b0 (in-place resume); any other overlap is TTT_E_ALIAS.
- * Numerics: state and accumulation in fp32; products with the state use
- * split-bf16 MFMA operands on the bf16 path.
+ *   ln_eps   : a positive normal float (>= FLT_MIN, finite), else TTT_E_SHAPE
+ *              (the same for every entry point below).
+ * Numerics: state, accumulation and layer-norm statistics in fp32. On the
+ * bf16 path with d = 64 and mb = 16 the products XK W and XQ W take W and
+ * the XQ / XK rows as fp16 MFMA operands (the bf16 inputs convert exactly;
+ * |XQ|, |XK| and |W| must stay below 65504, the fp16 range); the products
+ * with E and with the token x token matrices XK XK^T + 1 and XQ XK^T + 1
+ * take bf16 operands.
  */
 int ttt_linear_forward(int B, int H, int L, int d, int mb, int io, float ln_eps,
                        const void *XQ, const void *XK, const void *XV, const float *eta,
@@ -97,6 +103,8 @@ int ttt_linear_forward(int B, int H, int L, int d, int mb, int io, float ln_eps,
  *   Outputs W1_out [B,H,d,m], b1_out [B,H,m], W2_out [B,H,m,d], b2_out [B,H,d]
  *   are optional as a group (all NULL or all non-NULL) and may equal the
  *   corresponding inputs when w0_batched == 1.
+ * Numerics: state, accumulation and layer-norm statistics in fp32; on the
+ *   bf16 path (mb = 16) the products take bf16 MFMA operands.
  */
 int ttt_mlp_forward(int B, int H, int L, int d, int mb, int io, float ln_eps,
                     const void *XQ, const void *XK, const void *XV, const float *eta,

@@ -7,7 +7,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <cfloat>
 #include <climits>
+#include <cmath>
 
 #include "launch.hpp"
 #include "ttt.h"
@@ -91,6 +93,14 @@ int check_common(int B, int H, int L, int mb, int io) {
     return TTT_OK;
 }
 
+// The layer norms evaluate 1/sqrt(var + eps) with var >= 0, which needs a
+// positive normal eps.
+int check_eps(float eps) {
+    if (!(eps >= FLT_MIN) || !std::isfinite(eps))
+        return fail(TTT_E_SHAPE, "ln_eps = %g is not a positive normal float", static_cast<double>(eps));
+    return TTT_OK;
+}
+
 int launched(hipError_t e) {
     if (e != hipSuccess) return fail(TTT_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -107,6 +117,7 @@ const char *ttt_last_error(void) { return g_err; }
 int ttt_ln_l2_bwd(int rows, int d, const float *Z, const float *target, const float *ln_gamma,
                   const float *ln_beta, float ln_eps, float *G, hipStream_t stream) {
     if (rows < 0) return fail(TTT_E_SHAPE, "rows = %d < 0", rows);
+    if (check_eps(ln_eps)) return TTT_E_SHAPE;
     if (d != 16 && d != 32 && d != 64) return fail(TTT_E_SHAPE, "d = %d not in {16, 32, 64}", d);
     size_t rb;
     if (!nbytes(&rb, {static_cast<size_t>(rows), static_cast<size_t>(d), sizeof(float)}))
@@ -127,7 +138,7 @@ int ttt_linear_forward(int B, int H, int L, int d, int mb, int io, float ln_eps,
                        const float *ln_gamma, const float *ln_beta, void *O,
                        float *W_out, float *b_out, hipStream_t stream) {
     int st;
-    if ((st = check_common(B, H, L, mb, io))) return st;
+    if ((st = check_common(B, H, L, mb, io)) || (st = check_eps(ln_eps))) return st;
     if (d != 16 && d != 64) return fail(TTT_E_SHAPE, "d = %d not in {16, 64}", d);
     const size_t es = io == TTT_BF16 ? 2 : 4;
     const size_t nb = w0_batched ? static_cast<size_t>(B) : 1;
@@ -165,7 +176,7 @@ int ttt_mlp_forward(int B, int H, int L, int d, int mb, int io, float ln_eps,
                     const float *ln_beta, void *O, float *W1_out, float *b1_out,
                     float *W2_out, float *b2_out, hipStream_t stream) {
     int st;
-    if ((st = check_common(B, H, L, mb, io))) return st;
+    if ((st = check_common(B, H, L, mb, io)) || (st = check_eps(ln_eps))) return st;
     if (d != 64) return fail(TTT_E_SHAPE, "d = %d: the MLP supports d = 64 only", d);
     const int nout = (W1_out != nullptr) + (b1_out != nullptr) + (W2_out != nullptr) + (b2_out != nullptr);
     if (nout != 0 && nout != 4) return fail(TTT_E_NULL, "state outputs must be all NULL or all non-NULL");
@@ -208,7 +219,7 @@ int ttt_decode_step(int B, int H, int d, int io, float ln_eps, const void *xq,
                     const float *ln_gamma, const float *ln_beta, void *o,
                     hipStream_t stream) {
     int st;
-    if ((st = check_common(B, H, 1, 1, io))) return st;
+    if ((st = check_common(B, H, 1, 1, io)) || (st = check_eps(ln_eps))) return st;
     if (d != 16 && d != 64) return fail(TTT_E_SHAPE, "d = %d not in {16, 64}", d);
     const size_t es = io == TTT_BF16 ? 2 : 4;
     size_t xb, eb, wb, bb;

@@ -48,7 +48,13 @@
 //  * two barriers per chunk. Phase 1: chain Z_c and its partial row sums;
 //    state waves apply E_{c-1} and start O_{c-1}. Phase 2: chain E_c; state
 //    waves finish O_{c-1} and prepare the operands of chunks c .. c+2.
-//  MFMA operands are bf16; state, accumulation and row statistics are fp32.
+//  Precision: W grows along the sequence and its bf16 rounding would dominate
+//  the error of XK W and XQ W, so those products take W and the XQ / XK rows
+//  in fp16 (the bf16 inputs convert exactly for |x| >= 2^-14, within 3e-8
+//  below; W and the inputs lie far inside the fp16 range). The token x token
+//  operands K and T, E and the transposed XK stay bf16, whose range cannot
+//  overflow for any bf16 input. State, accumulation and row statistics are
+//  fp32.
 #include "launch.hpp"
 #include "tile.hpp"
 
@@ -64,8 +70,8 @@ constexpr int SB = 36;  // per-token stride (floats) of the row-sum exchange
 
 // One staged chunk.
 struct alignas(16) LSlot {
-    alignas(16) uint16_t xq[MB * RB];  // bf16 rows
-    alignas(16) uint16_t xk[MB * RB];  // bf16 rows
+    alignas(16) uint16_t xq[MB * RB];       // fp16 rows
+    alignas(16) uint16_t xk[MB * RB];       // fp16 rows
     alignas(16) uint16_t xkt[D * KS + 16];  // bf16, [permuted feature][token], see xkt_at
     alignas(16) float tau[MB * RS];    // XV - XK, fp32 rows
     alignas(16) float eta[MB];
@@ -98,7 +104,7 @@ __device__ __forceinline__ void st_s4(void *p, s16x4 v) {
 __device__ __forceinline__ float sum4(f32x4 v) { return (v[0] + v[1]) + (v[2] + v[3]); }
 
 // Input feature held in row m = 4 g + i of the state accumulator Wv[rb]:
-// pack8(Wv[2 kb], Wv[2 kb + 1]) then covers features 32 kb + 8 g .. +7.
+// pack8h(Wv[2 kb], Wv[2 kb + 1]) then covers features 32 kb + 8 g .. +7.
 __device__ __forceinline__ int win(int rb, int m) {
     return 32 * (rb >> 1) + 8 * (m >> 2) + 4 * (rb & 1) + (m & 3);
 }
@@ -112,9 +118,9 @@ __device__ __forceinline__ int xkt_row(int f) {
 // in one instruction) fall into distinct banks; a reader's 16 rows share a
 // group.
 __device__ __forceinline__ int xkt_at(int row, int tok) { return row * KS + 4 * (row >> 4) + tok; }
-// 16x16x32 operand fragment of a bf16 row tile: row c, features 32 kb + 8 g .. +7.
-__device__ __forceinline__ bf16x8 frag(const uint16_t *rows, int c, int g, int kb) {
-    return *reinterpret_cast<const bf16x8 *>(&rows[c * RB + 32 * kb + 8 * g]);
+// 16x16x32 operand fragment of an fp16 row tile: row c, features 32 kb + 8 g .. +7.
+__device__ __forceinline__ f16x8 fragh(const uint16_t *rows, int c, int g, int kb) {
+    return *reinterpret_cast<const f16x8 *>(&rows[c * RB + 32 * kb + 8 * g]);
 }
 
 // ---------------------------------------------------------------------------
@@ -150,13 +156,16 @@ __device__ __forceinline__ void prep_waves(Smem &sm, int pw, int g, int c, int l
         R.eta = et[tok];
     };
     auto stage_rows = [&](LSlot &S, uint2 q, uint2 k, uint2 v, float e) {
-        *reinterpret_cast<uint2 *>(&S.xq[r * RB + f0]) = q;
-        *reinterpret_cast<uint2 *>(&S.xk[r * RB + f0]) = k;
+        const f32x4 qf = unpack4(q), kf = unpack4(k);
+        const uint2 qh = make_uint2(pack2h(qf[0], qf[1]), pack2h(qf[2], qf[3]));
+        const uint2 kh = make_uint2(pack2h(kf[0], kf[1]), pack2h(kf[2], kf[3]));
+        *reinterpret_cast<uint2 *>(&S.xq[r * RB + f0]) = qh;
+        *reinterpret_cast<uint2 *>(&S.xk[r * RB + f0]) = kh;
         S.xkt[xkt_at(kr + 0, r)] = static_cast<uint16_t>(k.x & 0xffffu);
         S.xkt[xkt_at(kr + 1, r)] = static_cast<uint16_t>(k.x >> 16);
         S.xkt[xkt_at(kr + 2, r)] = static_cast<uint16_t>(k.y & 0xffffu);
         S.xkt[xkt_at(kr + 3, r)] = static_cast<uint16_t>(k.y >> 16);
-        *reinterpret_cast<f32x4 *>(&S.tau[r * RS + f0]) = unpack4(v) - unpack4(k);
+        *reinterpret_cast<f32x4 *>(&S.tau[r * RS + f0]) = unpack4(v) - kf;
         if (c == 0) S.eta[r] = e;
     };
     auto stage = [&](const PrepRegs &R, int ch, int slot) {
@@ -175,7 +184,7 @@ __device__ __forceinline__ void prep_waves(Smem &sm, int pw, int g, int c, int l
     for (int i = 0; i < 4; ++i) tmask[i] = (4 * g + i <= c) ? 1.f : 0.f;
     // [s = 4g + i][t = c] = A_s . B_t + init for bf16 row tiles A, B, packed
     auto gram = [&](const uint16_t *A, const uint16_t *B, f32x4 init) {
-        return mfma32(frag(A, c, g, 1), frag(B, c, g, 1), mfma32(frag(A, c, g, 0), frag(B, c, g, 0), init));
+        return mfma32h(fragh(A, c, g, 1), fragh(B, c, g, 1), mfma32h(fragh(A, c, g, 0), fragh(B, c, g, 0), init));
     };
     auto tmat = [&](const LSlot &S) {  // T^T of a chunk as a B operand
         const f32x4 gt = gram(S.xk, S.xq, fzero);
@@ -229,7 +238,7 @@ __device__ __forceinline__ void chain_waves(Smem &sm, const Ctx &cx, int u, int 
                                             const float *gam_h, const float *bet_h) {
     constexpr float inv_d = 1.0f / D;
     const int f0 = 16 * u + 4 * g;  // first feature of this lane
-    s16x4 eye;                      // identity as a B operand: B[k = 4g + i][n = c]
+    s16x4 eye;                      // identity as a B operand: B[k = 4g + i][n = c] (bf16)
 #pragma unroll
     for (int i = 0; i < 4; ++i) eye[i] = (4 * g + i == c) ? 0x3F80 : 0;
     const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
@@ -356,17 +365,18 @@ __device__ __forceinline__ void state_waves(Smem &sm, const Ctx &cx, int u, int 
             bt[i] = bet_h[f0 + i];
         }
     }
-    auto wfrag = [&](int kb) { return pack8(Wv[2 * kb], Wv[2 * kb + 1]); };  // A: [m = out][k = in]
-    auto xfrag = [&](const uint16_t *rows, int kb) { return frag(rows, c, g, kb); };
-    // [feature f0 + i][token c] = (X W + b)^T for a bf16 row tile X
-    auto xw = [&](const bf16x8 (&wf)[2], const uint16_t *rows) {
-        return mfma32(wf[1], xfrag(rows, 1), mfma32(wf[0], xfrag(rows, 0), bv));
+    // W as the A operand [m = out][k = in] (fp16)
+    auto wfrag = [&](int kb) { return pack8h(Wv[2 * kb], Wv[2 * kb + 1]); };
+    auto xfrag = [&](const uint16_t *rows, int kb) { return fragh(rows, c, g, kb); };
+    // [feature f0 + i][token c] = (X W + b)^T for an fp16 row tile X
+    auto xw = [&](const f16x8 (&wf)[2], const uint16_t *rows) {
+        return mfma32h(wf[1], xfrag(rows, 1), mfma32h(wf[0], xfrag(rows, 0), bv));
     };
 
     lds_barrier();  // prologue chunks 0 .. 2 staged
     f32x4 Pp = fzero;  // XK_{j+2} W_j + b_j, waiting for E_j
     if (cx.nch > 0) {
-        const bf16x8 wf[2] = {wfrag(0), wfrag(1)};
+        const f16x8 wf[2] = {wfrag(0), wfrag(1)};
         sm.q[0][u][lane] = xw(wf, sm.slot[0].xk);  // bracket of Z_0 = XK_0 W_0 + b_0
         Pp = xw(wf, sm.slot[1].xk);                // XK_1 W_0 + b_0 (E_{-1} = 0)
     }
@@ -405,7 +415,7 @@ __device__ __forceinline__ void state_waves(Smem &sm, const Ctx &cx, int u, int 
         // ===== phase 2 ==========================================================
         f32x4 st;
         uint2 xqb;
-        bf16x8 q0[2], k2[2];
+        f16x8 q0[2], k2[2];
         if (upd) {
             st = ld4(&sm.stf[c * SB + 4 * (g & 2)]);  // rows 0, 1: sums of zb; rows 2, 3: of zb^2
             xqb = *reinterpret_cast<const uint2 *>(&sm.slot[sm1].xq[c * RB + f0]);
@@ -419,16 +429,16 @@ __device__ __forceinline__ void state_waves(Smem &sm, const Ctx &cx, int u, int 
         }
         __builtin_amdgcn_sched_barrier(0);
         if (fwd) {
-            const bf16x8 wf[2] = {wfrag(0), wfrag(1)};
-            Pp = mfma32(wf[1], k2[1], mfma32(wf[0], k2[0], bv));  // XK_{it+2} W_it + b_it
-            Zq = mfma32(wf[1], q0[1], mfma32(wf[0], q0[0], bv));  // XQ_it W_it + b_it
+            const f16x8 wf[2] = {wfrag(0), wfrag(1)};
+            Pp = mfma32h(wf[1], k2[1], mfma32h(wf[0], k2[0], bv));  // XK_{it+2} W_it + b_it
+            Zq = mfma32h(wf[1], q0[1], mfma32h(wf[0], q0[0], bv));  // XQ_it W_it + b_it
         }
         if (upd) {
             const uint32_t sb = __float_as_uint(sum4(st));
             const auto tt = __builtin_amdgcn_permlane32_swap(sb, sb, false, false);
             const float t1 = __uint_as_float(tt[0]), t2 = __uint_as_float(tt[1]);
             const float mu = t1 * inv_d;
-            const f32x4 xq = unpack4(xqb);
+            const f32x4 xq = unpack4h(xqb);
             const float r = rsq(fmaxf(fmaf(t2, inv_d, -mu * mu), 0.f) + cx.eps);
             f32x4 o;
 #pragma unroll

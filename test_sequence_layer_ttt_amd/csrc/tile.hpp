@@ -18,6 +18,8 @@ typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 
 constexpr int D = 64, MB = 16;
 constexpr int RS = 68;   // row stride (elements) of a [16][64] tile in LDS
@@ -114,6 +116,30 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Two floats -> packed fp16 pair (round to nearest even).
+__device__ __forceinline__ uint32_t pack2h(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
+__device__ __forceinline__ f16x8 pack8h(f32x4 lo, f32x4 hi) {
+    return __builtin_bit_cast(f16x8, make_uint4(pack2h(lo[0], lo[1]), pack2h(lo[2], lo[3]),
+                                                pack2h(hi[0], hi[1]), pack2h(hi[2], hi[3])));
+}
+__device__ __forceinline__ s16x4 pack4h(f32x4 v) {
+    return __builtin_bit_cast(s16x4, make_uint2(pack2h(v[0], v[1]), pack2h(v[2], v[3])));
+}
+__device__ __forceinline__ f32x4 unpack4h(uint2 p) {
+    typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+    return __builtin_convertvector(__builtin_bit_cast(f16x4, p), f32x4);
+}
+__device__ __forceinline__ f32x4 mfma32h(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+// 16x16x16 fp16 product on operands held as 4 x 16-bit containers.
+__device__ __forceinline__ f32x4 mfma16h(s16x4 a, s16x4 b, f32x4 c) {
+    typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c,
+                                                 0, 0, 0);
+}
 __device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }

@@ -30,13 +30,13 @@ def test_version(lib):
 
 
 def _lin(lib, B=1, H=1, L=16, d=64, mb=16, io=1, ptrs=None, batched=0, W_out=None, b_out=None,
-         O=None):
+         O=None, eps=1e-6):
     # distinct non-overlapping fake buffers, 1 MiB apart
     p = ptrs or [FAKE + i * (1 << 20) for i in range(8)]
     Wo = W_out if W_out is not None else FAKE + 9 * (1 << 20)
     bo = b_out if b_out is not None else FAKE + 10 * (1 << 20)
     Oo = O if O is not None else FAKE + 11 * (1 << 20)
-    return lib.ttt_linear_forward(B, H, L, d, mb, io, 1e-6, p[0], p[1], p[2], p[3], p[4], p[5],
+    return lib.ttt_linear_forward(B, H, L, d, mb, io, eps, p[0], p[1], p[2], p[3], p[4], p[5],
                                   batched, p[6], p[7], Oo, Wo, bo, None)
 
 
@@ -50,6 +50,19 @@ def test_linear_rejects_unsupported_d_and_mb(lib):
     assert _lin(lib, d=48) == _lib.TTT_E_SHAPE
     assert _lin(lib, mb=0) == _lib.TTT_E_SHAPE
     assert _lin(lib, mb=17) == _lib.TTT_E_SHAPE
+
+
+@pytest.mark.parametrize("eps", [0.0, -1e-6, 1e-40, float("inf"), float("nan")])
+def test_every_entry_point_rejects_bad_eps(lib, eps):
+    """The layer norms need var + eps to be a positive normal float."""
+    assert _lin(lib, eps=eps) == _lib.TTT_E_SHAPE
+    assert "ln_eps" in lib.ttt_last_error().decode()
+    p = [FAKE + i * (1 << 20) for i in range(16)]
+    assert lib.ttt_mlp_forward(1, 1, 16, 64, 16, 1, eps, *p[:8], 0, p[8], p[9], p[10], p[11],
+                               p[12], p[13], p[14], None) == _lib.TTT_E_SHAPE
+    assert lib.ttt_decode_step(1, 1, 64, 1, eps, *p[:9], None) == _lib.TTT_E_SHAPE
+    assert lib.ttt_ln_l2_bwd(4, 64, FAKE, FAKE2, FAKE + 4096, FAKE + 8192, eps,
+                             FAKE2 + (1 << 20), None) == _lib.TTT_E_SHAPE
 
 
 def test_linear_rejects_bad_dtype(lib):
