@@ -11,6 +11,8 @@ Other workloads of the same hot path (--workload):
   5p  TTT-Linear prefill, B=1, H=32, L=32768
   4   TTT-MLP prefill, B=2, H=12, L=8192 (roofline: bf16 MFMA)
   5d  TTT-Linear decode: one b=1 step on 64 x 32 states (roofline: state bytes)
+  5r  TTT-Linear decode: 1024 b=1 steps on 64 x 32 states in one call, states
+      resident in registers (roofline: fp32 vector ALU)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
                        [--no-cpu-baseline]
@@ -29,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, datasheet
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, datasheet
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (packed FMA), datasheet
 WORKLOAD = 3
 METRIC = "TTT layer tokens/s (dual-form prefill, L=8192) + % of roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_linear_prefill_workload3.json")
@@ -55,11 +58,17 @@ def alg_bytes_decode(B, H, d, s_in=2, s_out=2):
     return B * H * (2 * (d * d + d) * 4 + 3 * d * s_in + 4 + d * s_out)
 
 
+def alg_flops_decode_step(B, H, d):
+    """Algorithmic flops of one b=1 step on B x H states: xk W, xq W and the
+    rank-one update, 2 d^2 each (the O(d) layer-norm work is left out)."""
+    return B * H * 6 * d * d
+
+
 def kernel_sources_hash():
     from test_sequence_layer_ttt_amd import build as hb
     h = hashlib.sha256()
-    # the sources the timed prefill kernel is built from
-    for name in ("linear_mfma.hip", "tile.hpp", "common.hpp", "launch.hpp"):
+    # the sources that define the timed prefill kernel's code
+    for name in ("linear_mfma.hip", "tile.hpp", "common.hpp"):
         p = os.path.join(hb.CSRC, name)
         with open(p, "rb") as f:
             h.update(f.read())
@@ -93,7 +102,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="3", choices=["3", "2", "5p", "4", "5d"])
+    ap.add_argument("--workload", default="3", choices=["3", "2", "5p", "4", "5d", "5r"])
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -124,6 +133,8 @@ def main():
         return bench_mlp(args)
     if args.workload == "5d":
         return bench_decode(args)
+    if args.workload == "5r":
+        return bench_decode_steps(args)
     wl = {"3": 3, "2": 2, "5p": 5}[args.workload]
     w = gen.WORKLOADS[wl]
     x = gen.make_workload(wl, decode_steps=0) if wl == 5 else gen.make_workload(wl)
@@ -337,6 +348,60 @@ def bench_decode(args):
     _line("TTT-Linear decode tokens/s (64 sequences x 32 heads, b=1)", B / wall, args, wall,
           "bf16", {"workload": "ttt_linear_decode_bf16_B64_H32_d64", "B": B, "H": H, "d": d,
                    "io": "bf16", "state": "fp32", "parallelism": "none (1 GPU)"}, roof, extra)
+
+
+def bench_decode_steps(args):
+    """Workload 5's 1024 b=1 decode steps on 64 x 32 states in one
+    ttt_decode_steps call (states resident in registers), each state started
+    from the B=1, L=32768 prefill's final state. A bench step is one call;
+    successive calls continue from the state the previous one left."""
+    import numpy as np
+    import torch
+    from test_sequence_layer_ttt_amd import gen, ttt
+    pre, dec = gen.make_workload(5)
+    dev = torch.device("cuda:0")
+    T = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev).to(dt)
+    bf = torch.bfloat16
+    _, Wp, bp = ttt.ttt_linear_forward(T(pre.XQ, bf), T(pre.XK, bf), T(pre.XV, bf), T(pre.eta),
+                                       T(pre.W0), T(pre.b0), T(pre.gamma), T(pre.beta),
+                                       ln_eps=pre.eps)
+    S, B, H, d = dec.steps, dec.B, dec.H, dec.d
+    W = Wp[0].expand(B, H, d, d).contiguous()
+    b = bp[0].expand(B, H, d).contiguous()
+    xq, xk, xv, et = T(dec.XQ, bf), T(dec.XK, bf), T(dec.XV, bf), T(dec.eta)
+    g, be = T(pre.gamma), T(pre.beta)
+    o = torch.empty((S, B, H, d), device=dev, dtype=bf)
+    stream = torch.cuda.current_stream()
+    step = lambda: ttt.ttt_decode_steps(xq, xk, xv, et, W, b, g, be, o=o, ln_eps=pre.eps,
+                                        stream=stream)
+    wall, kern = _timed(step, stream, args.warmup, args.steps)
+    fl = S * alg_flops_decode_step(B, H, d)
+    roof = {"bound": "alu", "achieved": fl / kern / 1e12, "peak": FP32_VECTOR_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": fl / kern / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
+            "traffic": None, "kernel": "decode_steps_kernel", "kernel_avg_us": kern * 1e6,
+            "alg_flops_per_launch": fl, "hbm_bytes_per_launch": S * B * H * (3 * d * 2 + 4 + d * 2)
+            + 2 * B * H * (d * d + d) * 4}
+    extra = {}
+    if not args.no_cpu_baseline:
+        import oracle
+        nt = cpu_threads()
+        Wn = np.broadcast_to(Wp[0].cpu().numpy(), (B, H, d, d)).astype(np.float64)
+        bn = np.broadcast_to(bp[0].cpu().numpy(), (B, H, d)).astype(np.float64)
+        ns = 4  # bounded sample: four steps
+        t1 = time.perf_counter()
+        for s_ in range(ns):
+            oracle.decode_step(dec.XQ[s_], dec.XK[s_], dec.XV[s_], dec.eta[s_], Wn, bn,
+                               pre.gamma, pre.beta, pre.eps, nthreads=nt)
+        tc = time.perf_counter() - t1
+        extra["cpu_baseline"] = {"value": B * ns / tc, "unit": "tokens/s", "cores": nt,
+                                 "kind": "oracle",
+                                 "sample": f"{ns} steps on all {B}x{H} states, fp64, {nt} threads, "
+                                           f"{tc:.2f} s"}
+    _line("TTT-Linear decode tokens/s (64 sequences x 32 heads, b=1, 1024 steps per call)",
+          B * S / wall, args, wall, "bf16",
+          {"workload": "ttt_linear_decode_steps_bf16_T1024_B64_H32_d64", "T": S, "B": B, "H": H,
+           "d": d, "io": "bf16", "state": "fp32, resident in registers",
+           "parallelism": "none (1 GPU)"}, roof, extra)
 
 
 if __name__ == "__main__":

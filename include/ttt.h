@@ -127,6 +127,26 @@ int ttt_decode_step(int B, int H, int d, int io, float ln_eps, const void *xq,
                     hipStream_t stream);
 
 /*
+ * T consecutive single-token steps, each exactly as ttt_decode_step, on the
+ * same B x H states: step t reads xq[t], xk[t], xv[t], eta[t] and writes
+ * o[t]; W and b hold the state after the last step. This is the cache of
+ * [D] §5.2 carried through a run of decode steps whose inputs are known in
+ * advance (teacher-forced decoding, b = 1 prefill).
+ *   T >= 0 (T = 0 leaves W and b unchanged); d in {16, 64}.
+ *   xq, xk, xv, o : [T,B,H,d] io, step-major;  eta : [T,B,H] fp32;
+ *   W [B,H,d,d], b [B,H,d] fp32, read and overwritten.
+ * For d = 64 one launch keeps every state in registers for all T steps, so
+ * only the per-step inputs and outputs cross HBM; for d = 16 it issues one
+ * single-step launch per step. Numerics: fp32 throughout (as
+ * ttt_decode_step; the two differ only in summation order).
+ * Errors as ttt_decode_step, plus TTT_E_SHAPE for T < 0.
+ */
+int ttt_decode_steps(int T, int B, int H, int d, int io, float ln_eps, const void *xq,
+                     const void *xk, const void *xv, const float *eta, float *W, float *b,
+                     const float *ln_gamma, const float *ln_beta, void *o,
+                     hipStream_t stream);
+
+/*
  * The fused layer-norm + L2 backward step on its own ([D] §4.2), row-wise:
  *   G[r] = d/dz [ 1/2 || LN_{gamma,beta}(z) - target[r] ||^2 ] at z = Z[r].
  *   rows >= 0; d in {16, 32, 64}. Z, target, G : [rows,d] fp32;

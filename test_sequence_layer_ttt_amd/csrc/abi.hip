@@ -241,4 +241,45 @@ int ttt_decode_step(int B, int H, int d, int io, float ln_eps, const void *xq,
     return launched(ttt::launch_decode(a, stream));
 }
 
+int ttt_decode_steps(int T, int B, int H, int d, int io, float ln_eps, const void *xq,
+                     const void *xk, const void *xv, const float *eta, float *W, float *b,
+                     const float *ln_gamma, const float *ln_beta, void *o,
+                     hipStream_t stream) {
+    int st;
+    if (T < 0) return fail(TTT_E_SHAPE, "T = %d is negative", T);
+    if ((st = check_common(B, H, 1, 1, io)) || (st = check_eps(ln_eps))) return st;
+    if (d != 16 && d != 64) return fail(TTT_E_SHAPE, "d = %d not in {16, 64}", d);
+    const size_t es = io == TTT_BF16 ? 2 : 4;
+    size_t xb, eb, wb, bb;
+    if (!nbytes(&xb, {size_t(T), size_t(B), size_t(H), size_t(d), es}) ||
+        !nbytes(&eb, {size_t(T), size_t(B), size_t(H), sizeof(float)}) ||
+        !nbytes(&wb, {size_t(B), size_t(H), size_t(d), size_t(d), sizeof(float)}) ||
+        !nbytes(&bb, {size_t(B), size_t(H), size_t(d), sizeof(float)}))
+        return fail(TTT_E_SHAPE, "sizes overflow");
+    const size_t pb = static_cast<size_t>(H) * d * sizeof(float);
+    const unsigned ea = static_cast<unsigned>(es);
+    const Buf in[] = {{xq, xb, "xq", false, ea}, {xk, xb, "xk", false, ea},
+                      {xv, xb, "xv", false, ea}, {eta, eb, "eta", false, 4},
+                      {ln_gamma, pb, "ln_gamma", false, 4}, {ln_beta, pb, "ln_beta", false, 4}};
+    const Buf out[] = {{W, wb, "W", false, 4}, {b, bb, "b", false, 4}, {o, xb, "o", false, ea}};
+    if ((st = check_bufs(in, 6)) || (st = check_bufs(out, 3))) return st;
+    if ((st = check_alias(out, 3, in, 6, nullptr))) return st;
+    if (B * H == 0 || T == 0) return ok();
+    if (ttt::decode_steps_resident(d)) {
+        ttt::DecodeArgs a{B, H, d, io, ln_eps, xq, xk, xv, eta, W, b, ln_gamma, ln_beta, o};
+        return launched(ttt::launch_decode_steps(a, T, stream));
+    }
+    // other d: one launch of the single-step kernel per step
+    const size_t step = static_cast<size_t>(B) * H * d * es;
+    const size_t estep = static_cast<size_t>(B) * H;
+    for (int t = 0; t < T; ++t) {
+        ttt::DecodeArgs a{B, H, d, io, ln_eps,
+                          static_cast<const char *>(xq) + t * step, static_cast<const char *>(xk) + t * step,
+                          static_cast<const char *>(xv) + t * step, eta + t * estep, W, b, ln_gamma,
+                          ln_beta, static_cast<char *>(o) + t * step};
+        if ((st = launched(ttt::launch_decode(a, stream)))) return st;
+    }
+    return ok();
+}
+
 }  // extern "C"

@@ -48,5 +48,7 @@ hipError_t launch_mlp(const MLPArgs &a, hipStream_t stream);
 bool mlp_mfma_supported(const MLPArgs &a);
 hipError_t launch_mlp_mfma(const MLPArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+bool decode_steps_resident(int d);
+hipError_t launch_decode_steps(const DecodeArgs &a, int T, hipStream_t stream);
 
 }  // namespace ttt

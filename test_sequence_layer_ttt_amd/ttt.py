@@ -139,6 +139,32 @@ def ttt_decode_step(xq, xk, xv, eta, W, b, ln_gamma, ln_beta, o=None, ln_eps: fl
     return o
 
 
+def ttt_decode_steps(xq, xk, xv, eta, W, b, ln_gamma, ln_beta, o=None, ln_eps: float = 1e-6,
+                     stream=None):
+    """T consecutive b = 1 steps on B x H states, updating W [B,H,d,d] and
+    b [B,H,d] in place. xq/xk/xv/o [T,B,H,d] step-major; eta [T,B,H].
+    Returns o."""
+    T, B, H, d = xq.shape
+    io = _IO.get(xq.dtype)
+    if io is None:
+        raise TypeError(f"xq dtype {xq.dtype} not supported")
+    for t, n in ((xq, "xq"), (xk, "xk"), (xv, "xv")):
+        _need(t, n, (T, B, H, d), xq.dtype)
+    _need(eta, "eta", (T, B, H), torch.float32)
+    _need(W, "W", (B, H, d, d), torch.float32)
+    _need(b, "b", (B, H, d), torch.float32)
+    _need(ln_gamma, "ln_gamma", (H, d), torch.float32)
+    _need(ln_beta, "ln_beta", (H, d), torch.float32)
+    if o is None:
+        o = torch.empty_like(xq)
+    _need(o, "o", (T, B, H, d), xq.dtype)
+    lib = _lib.load()
+    _lib.check(lib.ttt_decode_steps(T, B, H, d, io, ln_eps, _ptr(xq), _ptr(xk), _ptr(xv),
+                                    _ptr(eta), _ptr(W), _ptr(b), _ptr(ln_gamma), _ptr(ln_beta),
+                                    _ptr(o), _stream(stream)))
+    return o
+
+
 def ttt_ln_l2_bwd(Z, target, ln_gamma, ln_beta, G=None, ln_eps: float = 1e-6, stream=None):
     """Row-wise fused LN + L2 backward. Z, target, G [rows,d] fp32; gamma/beta [d]."""
     rows, d = Z.shape

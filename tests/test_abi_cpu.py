@@ -19,7 +19,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _lib.header_functions()
     assert set(names) >= {"ttt_linear_forward", "ttt_mlp_forward", "ttt_decode_step",
-                          "ttt_ln_l2_bwd", "ttt_last_error", "ttt_version"}
+                          "ttt_decode_steps", "ttt_ln_l2_bwd", "ttt_last_error", "ttt_version"}
     for n in names:
         assert hasattr(lib, n), n
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
@@ -61,6 +61,7 @@ def test_every_entry_point_rejects_bad_eps(lib, eps):
     assert lib.ttt_mlp_forward(1, 1, 16, 64, 16, 1, eps, *p[:8], 0, p[8], p[9], p[10], p[11],
                                p[12], p[13], p[14], None) == _lib.TTT_E_SHAPE
     assert lib.ttt_decode_step(1, 1, 64, 1, eps, *p[:9], None) == _lib.TTT_E_SHAPE
+    assert lib.ttt_decode_steps(4, 1, 1, 64, 1, eps, *p[:9], None) == _lib.TTT_E_SHAPE
     assert lib.ttt_ln_l2_bwd(4, 64, FAKE, FAKE2, FAKE + 4096, FAKE + 8192, eps,
                              FAKE2 + (1 << 20), None) == _lib.TTT_E_SHAPE
 
@@ -122,6 +123,25 @@ def test_decode_validation(lib):
                                p[7], p[8], None) == _lib.TTT_E_ALIAS
     assert lib.ttt_decode_step(1, 1, 64, 1, 1e-6, p[0], 0, p[2], p[3], p[4], p[5], p[6], p[7],
                                p[8], None) == _lib.TTT_E_NULL
+
+
+def test_decode_steps_validation(lib):
+    p = [FAKE + i * (1 << 20) for i in range(10)]
+    assert lib.ttt_decode_steps(-1, 1, 1, 64, 1, 1e-6, *p[:9], None) == _lib.TTT_E_SHAPE
+    assert "T = -1" in lib.ttt_last_error().decode()
+    assert lib.ttt_decode_steps(3, 1, 1, 32, 1, 1e-6, *p[:9], None) == _lib.TTT_E_SHAPE
+    assert lib.ttt_decode_steps(3, 1, 1, 64, 5, 1e-6, *p[:9], None) == _lib.TTT_E_DTYPE
+    # W overlapping xq
+    assert lib.ttt_decode_steps(3, 1, 1, 64, 1, 1e-6, p[0], p[1], p[2], p[3], p[0], p[5], p[6],
+                                p[7], p[8], None) == _lib.TTT_E_ALIAS
+    assert lib.ttt_decode_steps(3, 1, 1, 64, 1, 1e-6, p[0], 0, p[2], p[3], p[4], p[5], p[6], p[7],
+                                p[8], None) == _lib.TTT_E_NULL
+    # misaligned xk (bf16 needs 2-byte alignment)
+    assert lib.ttt_decode_steps(3, 1, 1, 64, 1, 1e-6, p[0], p[1] + 1, p[2], p[3], p[4], p[5], p[6],
+                                p[7], p[8], None) == _lib.TTT_E_ALIGN
+    # no steps, or no states: nothing to do, no HIP call
+    assert lib.ttt_decode_steps(0, 2, 3, 64, 1, 1e-6, *p[:9], None) == _lib.TTT_OK
+    assert lib.ttt_decode_steps(5, 0, 3, 64, 1, 1e-6, *p[:9], None) == _lib.TTT_OK
 
 
 def test_ln_bwd_validation(lib):

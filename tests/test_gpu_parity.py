@@ -299,6 +299,95 @@ def test_decode_full_workload5():
     assert max(err.values()) <= P.TOL["bf16"], err
 
 
+def _steps_run(W0, b0, dec, gamma, beta, eps):
+    """ttt_decode_steps over all steps of `dec` in one call."""
+    dt = P.io_dtype(dec.io)
+    W = P.dev(W0)
+    b = P.dev(b0)
+    o = ttt.ttt_decode_steps(P.dev(dec.XQ, dt), P.dev(dec.XK, dt), P.dev(dec.XV, dt),
+                             P.dev(dec.eta), W, b, P.dev(gamma), P.dev(beta), ln_eps=eps)
+    torch.cuda.synchronize()
+    return np.ascontiguousarray(np.moveaxis(P.to_np(o), 0, 2)), P.to_np(W), P.to_np(b)
+
+
+def _decode_case(seed, steps, B, H, d, io, ln):
+    rng = np.random.default_rng(seed)
+    dec = gen.make_decode(rng, steps, B, H, d, io)
+    W0 = (0.3 * rng.standard_normal((B, H, d, d))).astype(np.float32)
+    b0 = (0.1 * rng.standard_normal((B, H, d))).astype(np.float32)
+    if ln == "ident":
+        gamma, beta = np.ones((H, d), np.float32), np.zeros((H, d), np.float32)
+    else:
+        gamma = (1 + 0.1 * rng.standard_normal((H, d))).astype(np.float32)
+        beta = (0.1 * rng.standard_normal((H, d))).astype(np.float32)
+    return dec, W0, b0, gamma, beta
+
+
+@pytest.mark.parametrize("io,d,ln", [("f32", 16, "random"), ("f32", 64, "random"),
+                                     ("f32", 64, "ident"), ("bf16", 64, "random"),
+                                     ("bf16", 64, "ident")])
+def test_decode_steps_small(io, d, ln):
+    """T steps in one call (state resident for d = 64) against the oracle's
+    b = 1 schedule, and against T calls of the single-step entry point."""
+    dec, W0, b0, gamma, beta = _decode_case(760 + d, 37, 3, 2, d, io, ln)
+    got = _steps_run(W0, b0, dec, gamma, beta, 1e-6)
+    ref = _decode_oracle(W0, b0, dec, gamma, beta, 1e-6)
+    err = P.errors(got, ref, 6, LIN_NAMES)
+    _report(f"decode_steps {io} d{d} {ln}", err)
+    assert max(err.values()) <= P.TOL[io], err
+    one = _decode_run(W0, b0, dec, gamma, beta, 1e-6)
+    err1 = P.errors(got, one, 6, LIN_NAMES)
+    _report(f"decode_steps vs single steps {io} d{d} {ln}", err1)
+    assert max(err1.values()) <= P.TOL[io], err1
+
+
+@pytest.mark.parametrize("steps", [0, 1, 2])
+def test_decode_steps_edge(steps):
+    """T = 0 leaves the state untouched; T = 1 and 2 equal the single-step path."""
+    dec, W0, b0, gamma, beta = _decode_case(790 + steps, steps, 2, 3, 64, "bf16", "random")
+    got = _steps_run(W0, b0, dec, gamma, beta, 1e-6)
+    if steps == 0:
+        assert np.array_equal(got[1], W0) and np.array_equal(got[2], b0)
+        assert got[0].shape == (2, 3, 0, 64)
+        return
+    ref = _decode_oracle(W0, b0, dec, gamma, beta, 1e-6)
+    err = P.errors(got, ref, 6, LIN_NAMES)
+    _report(f"decode_steps T{steps}", err)
+    assert max(err.values()) <= P.TOL["bf16"], err
+
+
+def test_decode_steps_resume_and_repeatable():
+    """Two calls of T1 and T2 steps equal one call of T1 + T2 steps bit for
+    bit (the state is exactly what the kernel holds), and a repeat of the
+    same call is bitwise identical."""
+    dec, W0, b0, gamma, beta = _decode_case(795, 24, 2, 4, 64, "bf16", "ident")
+    full = _steps_run(W0, b0, dec, gamma, beta, 1e-6)
+    again = _steps_run(W0, b0, dec, gamma, beta, 1e-6)
+    for a, b in zip(full, again):
+        assert np.array_equal(a, b)
+    cut = lambda lo, hi: gen.DecodeInputs(hi - lo, dec.B, dec.H, dec.d, dec.io, dec.XQ[lo:hi],
+                                          dec.XK[lo:hi], dec.XV[lo:hi], dec.eta[lo:hi])
+    O1, W1, b1 = _steps_run(W0, b0, cut(0, 10), gamma, beta, 1e-6)
+    O2, W2, b2 = _steps_run(W1, b1, cut(10, 24), gamma, beta, 1e-6)
+    assert np.array_equal(np.concatenate([O1, O2], 2), full[0])
+    assert np.array_equal(W2, full[1]) and np.array_equal(b2, full[2])
+
+
+def test_decode_steps_full_workload5():
+    """Workload 5's 1024 decode steps for 64 x 32 states in one call."""
+    pre, dec = gen.make_workload(5)
+    _, Wp, bp = P.linear_gpu(pre)
+    rW, rb = P.linear_oracle(pre)[1:]
+    W0 = np.broadcast_to(Wp[0], (64,) + Wp.shape[1:]).astype(np.float32)
+    b0 = np.broadcast_to(bp[0], (64,) + bp.shape[1:]).astype(np.float32)
+    got = _steps_run(W0, b0, dec, pre.gamma, pre.beta, pre.eps)
+    ref = _decode_oracle(np.broadcast_to(rW[0], W0.shape), np.broadcast_to(rb[0], b0.shape),
+                         dec, pre.gamma, pre.beta, pre.eps)
+    err = P.errors(got, ref, 64 * 32, LIN_NAMES)
+    _report("workload5 decode_steps 64x1024", err)
+    assert max(err.values()) <= P.TOL["bf16"], err
+
+
 @pytest.mark.parametrize("mb", [8, 13])
 def test_linear_bf16_other_minibatch(mb):
     """Mini-batch sizes other than 16 (VALU path) with bf16 storage."""
