@@ -104,7 +104,10 @@ int ttt_linear_forward(int B, int H, int L, int d, int mb, int io, float ln_eps,
  *   are optional as a group (all NULL or all non-NULL) and may equal the
  *   corresponding inputs when w0_batched == 1.
  * Numerics: state, accumulation and layer-norm statistics in fp32; on the
- *   bf16 path (mb = 16) the products take bf16 MFMA operands.
+ *   bf16 path (mb = 16) every product takes fp16 MFMA operands (inputs,
+ *   state, activations, E1, E2 and the Grams rounded to fp16, accumulated in
+ *   fp32), so |W1|, |W2|, the activations and the Gram entries must stay
+ *   below 65504.
  */
 int ttt_mlp_forward(int B, int H, int L, int d, int mb, int io, float ln_eps,
                     const void *XQ, const void *XK, const void *XV, const float *eta,

@@ -23,7 +23,7 @@
 //    With the contraction index permuted identically on both operands these
 //    are also the operand layouts of the forward products, so no product
 //    reads the state through LDS. W2 is contracted over hidden units (A W2)
-//    and over outputs (E2 W2^T); for the latter its bf16 tiles are transposed
+//    and over outputs (E2 W2^T); for the latter its fp16 tiles are transposed
 //    each chunk by MFMAs with the identity.
 //  * Z1 and Zb1 are computed transposed (hidden as the output row), so their
 //    GELU outputs are directly the A operands of A W2 and Ab W2; A and E1 are
@@ -34,8 +34,15 @@
 //    rows of their four tokens one chunk ahead; a chunk is staged into LDS a
 //    full iteration after its loads were issued.
 //  * GELU: x Phi(x) with erf from Abramowitz & Stegun 7.1.26 (|error| <=
-//    1.5e-7, far below the bf16 resolution of the MFMA operands); GELU and its
+//    1.5e-7, far below the resolution of the MFMA operands); GELU and its
 //    derivative share one exponential.
+//  * precision: every MFMA takes fp16 operands (10-bit mantissa) and
+//    accumulates in fp32. W1 and W2 grow along the sequence while a 16-bit
+//    operand's rounding stays relative, so bf16 operands (7-bit mantissa)
+//    would dominate the error. The bf16 inputs convert exactly above 2^-14;
+//    the state, activations, E1, E2 and the Grams T1, T2 stay far below the
+//    fp16 limit of 65504, and E values below 2^-14 keep an absolute
+//    resolution of 2^-24. The transposes (identity MFMAs) add no rounding.
 #include "launch.hpp"
 #include "tile.hpp"
 
@@ -53,8 +60,8 @@ struct alignas(16) MlpSmem {
     Slot slot[2];
     alignas(16) float part[NW + 1][MB * RS];  // per-wave partial sums of Z2 / Zb2 (+ T2 E2 + b2)
     alignas(16) float gram[NW][MB * GS];      // per-wave partial Gram Ab A^T, [t][s]
-    alignas(16) uint16_t e2[MB * RS];         // E2, bf16 rows [token][out]
-    alignas(16) uint16_t e2t[D * KS];         // E2 transposed, bf16 [out][token]
+    alignas(16) uint16_t e2[MB * RS];         // E2, fp16 rows [token][out]
+    alignas(16) uint16_t e2t[D * KS];         // E2 transposed, fp16 [out][token]
 };
 
 // Phi(x) and phi(x) (standard normal cdf / pdf) with erf from Abramowitz &
@@ -128,10 +135,12 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
     }
     ident = __all(ident);  // every wave covers all 64 features: same vote everywhere
 
-    const s16x4 ones = {0x3F80, 0x3F80, 0x3F80, 0x3F80};  // bf16 1.0
-    s16x4 eye;  // identity as a B operand: B[k = 4g + i][n = c]
+    const s16x4 ones = {0x3C00, 0x3C00, 0x3C00, 0x3C00};  // fp16 1.0
+    s16x4 eye;  // identity as a B operand: B[k = 4g + i][n = c] (fp16)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) eye[i] = (4 * g + i == c) ? 0x3F80 : 0;
+    for (int i = 0; i < 4; ++i) {
+        eye[i] = (4 * g + i == c) ? 0x3C00 : 0;
+    }
     const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
     f32x4 tmask;
 #pragma unroll
@@ -154,14 +163,16 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
         const bool ok = ch * MB + r < L;
         const uint2 z2 = make_uint2(0u, 0u);
         const uint2 q = ok ? R.q : z2, k = ok ? R.k : z2, v = ok ? R.v : z2;
-        *reinterpret_cast<uint2 *>(&S.xq[r * RS + f0]) = q;
-        *reinterpret_cast<uint2 *>(&S.xk[r * RS + f0]) = k;
-        S.xkt[(f0 + 0) * KS + r] = static_cast<uint16_t>(k.x & 0xffffu);
-        S.xkt[(f0 + 1) * KS + r] = static_cast<uint16_t>(k.x >> 16);
-        S.xkt[(f0 + 2) * KS + r] = static_cast<uint16_t>(k.y & 0xffffu);
-        S.xkt[(f0 + 3) * KS + r] = static_cast<uint16_t>(k.y >> 16);
-        *reinterpret_cast<f32x4 *>(&S.xqf[r * RS + f0]) = unpack4(q);
-        const f32x4 tau = unpack4(v) - unpack4(k);
+        const f32x4 qf = unpack4(q), kf = unpack4(k);
+        const uint2 kh = make_uint2(pack2h(kf[0], kf[1]), pack2h(kf[2], kf[3]));
+        *reinterpret_cast<uint2 *>(&S.xq[r * RS + f0]) = make_uint2(pack2h(qf[0], qf[1]), pack2h(qf[2], qf[3]));
+        *reinterpret_cast<uint2 *>(&S.xk[r * RS + f0]) = kh;
+        S.xkt[(f0 + 0) * KS + r] = static_cast<uint16_t>(kh.x & 0xffffu);
+        S.xkt[(f0 + 1) * KS + r] = static_cast<uint16_t>(kh.x >> 16);
+        S.xkt[(f0 + 2) * KS + r] = static_cast<uint16_t>(kh.y & 0xffffu);
+        S.xkt[(f0 + 3) * KS + r] = static_cast<uint16_t>(kh.y >> 16);
+        *reinterpret_cast<f32x4 *>(&S.xqf[r * RS + f0]) = qf;
+        const f32x4 tau = unpack4(v) - kf;
         *reinterpret_cast<f32x4 *>(&S.tau[r * RS + f0]) = tau;
         const float mt = row16_sum((tau[0] + tau[1]) + (tau[2] + tau[3])) * (1.0f / D);
         if (c == 0) {
@@ -176,26 +187,27 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
     }
     lds_barrier();
 
-    auto w1frag = [&](int t, int kb) { return pack8(W1v[t][2 * kb], W1v[t][2 * kb + 1]); };
+    auto w1frag = [&](int t, int kb) { return pack8h(W1v[t][2 * kb], W1v[t][2 * kb + 1]); };
+    auto rowh = [&](const uint16_t *tile, int kb) { return __builtin_bit_cast(f16x8, row_frag(tile, c, g, kb)); };
 
     for (int ch = 0; ch < nch; ++ch) {
         const Slot &S = sm.slot[ch & 1];
         float *P = sm.part[w] + (4 * g) * RS + c;
 
         // ===== A: Z1^T, A = gelu(Z1), Z2 partials, T1, A transposed ============
-        bf16x8 xkf[2], xqf[2];
+        f16x8 xkf[2], xqf[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            xkf[kb] = row_frag(S.xk, c, g, kb);
-            xqf[kb] = row_frag(S.xq, c, g, kb);
+            xkf[kb] = rowh(S.xk, kb);
+            xqf[kb] = rowh(S.xq, kb);
         }
         f32x4 Aact[2], Ap[2], zq[2];  // [hid 16t + 4g + i][token c]
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const bf16x8 wa = w1frag(t, 0), wb = w1frag(t, 1);
-            f32x4 z = mfma32(wa, xkf[0], b1v[t]);
-            z = mfma32(wb, xkf[1], z);
-            zq[t] = mfma32(wb, xqf[1], mfma32(wa, xqf[0], b1v[t]));  // (XQ W1 + b1)^T
+            const f16x8 wa = w1frag(t, 0), wb = w1frag(t, 1);
+            f32x4 z = mfma32h(wa, xkf[0], b1v[t]);
+            z = mfma32h(wb, xkf[1], z);
+            zq[t] = mfma32h(wb, xqf[1], mfma32h(wa, xqf[0], b1v[t]));  // (XQ W1 + b1)^T
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float Phi, phi;
@@ -204,24 +216,24 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
                 Ap[t][i] = fmaf(z[i], phi, Phi);
             }
         }
-        const bf16x8 Af = pack8(Aact[0], Aact[1]);  // A operand [m = token c][k = this wave's hidden]
+        const f16x8 Af = pack8h(Aact[0], Aact[1]);  // A operand [m = token c][k = this wave's hidden]
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             // chunk-start W2 as B operand [k = hidden][n = out]; b2 tile u added by wave u
-            const f32x4 acc = mfma32(Af, pack8(W2v[u][0], W2v[u][1]), w == u ? b2w : fzero);
+            const f32x4 acc = mfma32h(Af, pack8h(W2v[u][0], W2v[u][1]), w == u ? b2w : fzero);
 #pragma unroll
             for (int i = 0; i < 4; ++i) P[i * RS + 16 * u] = acc[i];
         }
         f32x4 gt = fzero;  // [s = 4g+i][t = c] = XQ_t . XK_s
-        gt = mfma32(xkf[0], xqf[0], gt);
-        gt = mfma32(xkf[1], xqf[1], gt);
+        gt = mfma32h(xkf[0], xqf[0], gt);
+        gt = mfma32h(xkf[1], xqf[1], gt);
         f32x4 tv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) tv[i] = fmaf(gt[i], tmask[i], tmask[i]);
-        const s16x4 T1b = pack4(tv);  // T1^T as a B operand: [k = s][n = t]
+        const s16x4 T1b = pack4h(tv);  // T1^T as a B operand: [k = s][n = t]
         s16x4 Atr[2];                 // A[token 4g+i][hid 16t + c]
 #pragma unroll
-        for (int t = 0; t < 2; ++t) Atr[t] = pack4(mfma16(pack4(Aact[t]), eye, fzero));
+        for (int t = 0; t < 2; ++t) Atr[t] = pack4h(mfma16h(pack4h(Aact[t]), eye, fzero));
         lds_barrier();
 
         // ===== B (row layout): Z2 -> E2 =====================================
@@ -232,7 +244,7 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
             const f32x4 tau = *reinterpret_cast<const f32x4 *>(&S.tau[r * RS + f0]);
             const f32x4 ev = ident ? ln_bwd_row<true>(z2, tau, S.mutau[r], S.eta[r], gam, bet, eps)
                                    : ln_bwd_row<false>(z2, tau, S.mutau[r], S.eta[r], gam, bet, eps);
-            const uint32_t p01 = pack2(ev[0], ev[1]), p23 = pack2(ev[2], ev[3]);
+            const uint32_t p01 = pack2h(ev[0], ev[1]), p23 = pack2h(ev[2], ev[3]);
             *reinterpret_cast<uint2 *>(&sm.e2[r * RS + f0]) = make_uint2(p01, p23);
             sm.e2t[(f0 + 0) * KS + r] = static_cast<uint16_t>(p01 & 0xffffu);
             sm.e2t[(f0 + 1) * KS + r] = static_cast<uint16_t>(p01 >> 16);
@@ -248,13 +260,13 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
         for (int u = 0; u < 4; ++u)
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) asm volatile("" : "+v"(W2v[u][rb]));
-        bf16x8 W2f[4];
+        f16x8 W2f[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) W2f[u] = pack8(W2v[u][0], W2v[u][1]);
-        bf16x8 e2f[2];  // E2 rows: B operand [k = out][n = token c]
+        for (int u = 0; u < 4; ++u) W2f[u] = pack8h(W2v[u][0], W2v[u][1]);
+        f16x8 e2f[2];  // E2 rows: B operand [k = out][n = token c]
         s16x4 e2b[4];   // E2 as B operand [k = token 4g+i][n = out 16u + c]
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) e2f[kb] = row_frag(sm.e2, c, g, kb);
+        for (int kb = 0; kb < 2; ++kb) e2f[kb] = rowh(sm.e2, kb);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
             e2b[u] = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(&sm.e2t[(16 * u + c) * KS + 4 * g]));
@@ -267,17 +279,17 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
             for (int u = 0; u < 4; ++u) {
                 const uint4 pk = __builtin_bit_cast(uint4, W2f[u]);
                 const s16x4 half = __builtin_bit_cast(s16x4, t ? make_uint2(pk.z, pk.w) : make_uint2(pk.x, pk.y));
-                w2t[u] = mfma16(half, eye, fzero);
+                w2t[u] = mfma16h(half, eye, fzero);
             }
             f32x4 g1 = fzero;  // (E2 W2^T)^T: [hid 16t + 4g + i][token c]
-            g1 = mfma32(pack8(w2t[0], w2t[1]), e2f[0], g1);
-            g1 = mfma32(pack8(w2t[2], w2t[3]), e2f[1], g1);
-            E1tr[t] = pack4(mfma16(pack4(g1 * Ap[t]), eye, fzero));
+            g1 = mfma32h(pack8h(w2t[0], w2t[1]), e2f[0], g1);
+            g1 = mfma32h(pack8h(w2t[2], w2t[3]), e2f[1], g1);
+            E1tr[t] = pack4h(mfma16h(pack4h(g1 * Ap[t]), eye, fzero));
         }
         f32x4 Ab[2];  // gelu(Zb1)^T: [hid 16t + 4g + i][token c]
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const f32x4 zb = mfma16(E1tr[t], T1b, zq[t]);  // + (T1 E1)^T
+            const f32x4 zb = mfma16h(E1tr[t], T1b, zq[t]);  // + (T1 E1)^T
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float Phi, phi;
@@ -285,12 +297,12 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
                 Ab[t][i] = zb[i] * Phi;
             }
         }
-        const bf16x8 Abf = pack8(Ab[0], Ab[1]);
+        const f16x8 Abf = pack8h(Ab[0], Ab[1]);
         // [s = 4g+i][t = c] = sum over this wave's hidden units of A_s . Ab_t
-        *reinterpret_cast<f32x4 *>(&sm.gram[w][c * GS + 4 * g]) = mfma32(Af, Abf, fzero);
+        *reinterpret_cast<f32x4 *>(&sm.gram[w][c * GS + 4 * g]) = mfma32h(Af, Abf, fzero);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const f32x4 acc = mfma32(Abf, W2f[u], fzero);
+            const f32x4 acc = mfma32h(Abf, W2f[u], fzero);
 #pragma unroll
             for (int i = 0; i < 4; ++i) P[i * RS + 16 * u] = acc[i];
         }
@@ -303,13 +315,13 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
 #pragma unroll
-                for (int rb = 0; rb < 4; ++rb) W1v[t][rb] = mfma16(xkt[rb], E1tr[t], W1v[t][rb]);
-                b1v[t] = mfma16(E1tr[t], ones, b1v[t]);
+                for (int rb = 0; rb < 4; ++rb) W1v[t][rb] = mfma16h(xkt[rb], E1tr[t], W1v[t][rb]);
+                b1v[t] = mfma16h(E1tr[t], ones, b1v[t]);
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u)
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb) W2v[u][rb] = mfma16(Atr[rb], e2b[u], W2v[u][rb]);
+                for (int rb = 0; rb < 2; ++rb) W2v[u][rb] = mfma16h(Atr[rb], e2b[u], W2v[u][rb]);
         }
         lds_barrier();
 
@@ -322,11 +334,11 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
 #pragma unroll
             for (int i = 0; i < 4; ++i) t2[i] = fmaf(g2[i], tmask[i], tmask[i]);
             const s16x4 e2w = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(&sm.e2t[(16 * w + c) * KS + 4 * g]));
-            const f32x4 corr = mfma16(pack4(t2), e2w, b2w);
+            const f32x4 corr = mfma16h(pack4h(t2), e2w, b2w);
             float *Q = sm.part[NW] + (4 * g) * RS + 16 * w + c;
 #pragma unroll
             for (int i = 0; i < 4; ++i) Q[i * RS] = corr[i];
-            b2w = mfma16(ones, e2w, b2w);
+            b2w = mfma16h(ones, e2w, b2w);
         }
         lds_barrier();
 

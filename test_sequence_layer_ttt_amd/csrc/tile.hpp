@@ -235,9 +235,9 @@ __device__ __forceinline__ f32x4 ln_fwd_row(f32x4 z, f32x4 xq, const float (&gam
 
 // One staged chunk in LDS.
 struct alignas(16) Slot {
-    alignas(16) uint16_t xq[MB * RS];   // bf16 rows
-    alignas(16) uint16_t xk[MB * RS];   // bf16 rows
-    alignas(16) uint16_t xkt[D * KS];   // bf16, [feature][token]
+    alignas(16) uint16_t xq[MB * RS];   // 16-bit rows (fp16 in the MLP kernel)
+    alignas(16) uint16_t xk[MB * RS];   // 16-bit rows (fp16 in the MLP kernel)
+    alignas(16) uint16_t xkt[D * KS];   // 16-bit, [feature][token] (fp16 in the MLP kernel)
     alignas(16) float xqf[MB * RS];     // fp32 rows
     alignas(16) float tau[MB * RS];     // XV - XK, fp32 rows
     alignas(16) float eta[MB];
