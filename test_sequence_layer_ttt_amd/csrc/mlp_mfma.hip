@@ -28,8 +28,10 @@
 //  * Z1 and Zb1 are computed transposed (hidden as the output row), so their
 //    GELU outputs are directly the A operands of A W2 and Ab W2; A and E1 are
 //    transposed by identity MFMAs for the token-contracting updates.
-//  * contractions over all 256 hidden units (Z2, Zb2, the Gram Ab A^T) are
-//    summed across the eight waves through LDS. Waves 0-3 also run the
+//  * contractions over all 256 hidden units (Z2 and Zb2) are summed across
+//    the eight waves through LDS. T2 E2 needs no sum of its own: masking is
+//    linear, so each wave adds tril(Ab_w A_w^T) E2 over its own hidden units
+//    to its Zb2 partial (and wave 0 the tril(1) E2 term). Waves 0-3 also run the
 //    row-layout work (16 lanes per token, DPP reductions) and load the input
 //    rows of their four tokens one chunk ahead; a chunk is staged into LDS a
 //    full iteration after its loads were issued.
@@ -54,12 +56,10 @@ using namespace tile;
 constexpr int M = 4 * D;     // hidden units
 constexpr int NW = 8, NT = 64 * NW;
 constexpr int NRW = 4;       // waves running the row-layout work (16 tokens x 16 lanes)
-constexpr int GS = 20;       // row stride (fp32) of the Gram partial tiles
 
 struct alignas(16) MlpSmem {
     Slot slot[2];
-    alignas(16) float part[NW + 1][MB * RS];  // per-wave partial sums of Z2 / Zb2 (+ T2 E2 + b2)
-    alignas(16) float gram[NW][MB * GS];      // per-wave partial Gram Ab A^T, [t][s]
+    alignas(16) float part[NW][MB * RS];  // per-wave partial sums of Z2 / Zb2
     alignas(16) uint16_t e2[MB * RS];         // E2, fp16 rows [token][out]
     alignas(16) uint16_t e2t[D * KS];         // E2 transposed, fp16 [out][token]
 };
@@ -298,11 +298,21 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
             }
         }
         const f16x8 Abf = pack8h(Ab[0], Ab[1]);
-        // [s = 4g+i][t = c] = sum over this wave's hidden units of A_s . Ab_t
-        *reinterpret_cast<f32x4 *>(&sm.gram[w][c * GS + 4 * g]) = mfma32h(Af, Abf, fzero);
+        // This wave's share of T2 E2: the causal mask is linear, so
+        // tril(Ab A^T + 1) E2 = sum over waves of tril(Ab_w A_w^T) E2, plus
+        // tril(1) E2 added once (wave 0). The partial Gram
+        // [s = 4g+i][t = c] = A_s . Ab_t over this wave's hidden units is in the
+        // A-operand layout [m = t][k = s] as it stands.
+        const f32x4 gw = mfma32h(Af, Abf, fzero);
+        f32x4 t2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t2[i] = (w == 0 ? gw[i] + 1.f : gw[i]) * tmask[i];
+        const s16x4 t2h = pack4h(t2);
+        // Zb2 partials: Ab_w W2_w + tril(Ab_w A_w^T (+1)) E2, plus the
+        // chunk-start b2 tile u from wave u
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const f32x4 acc = mfma32h(Abf, W2f[u], fzero);
+            const f32x4 acc = mfma16h(t2h, e2b[u], mfma32h(Abf, W2f[u], w == u ? b2w : fzero));
 #pragma unroll
             for (int i = 0; i < 4; ++i) P[i * RS + 16 * u] = acc[i];
         }
@@ -322,23 +332,10 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
             for (int u = 0; u < 4; ++u)
 #pragma unroll
                 for (int rb = 0; rb < 2; ++rb) W2v[u][rb] = mfma16h(Atr[rb], e2b[u], W2v[u][rb]);
-        }
-        lds_barrier();
-
-        // ===== D: T2 E2 + b2 for output tile w (waves 0-3) ===================
-        if (roww) {
-            f32x4 g2 = *reinterpret_cast<const f32x4 *>(&sm.gram[0][c * GS + 4 * g]);
-#pragma unroll
-            for (int q = 1; q < NW; ++q) g2 += *reinterpret_cast<const f32x4 *>(&sm.gram[q][c * GS + 4 * g]);
-            f32x4 t2;  // T2 as the A operand: [m = t = c][k = s = 4g+i]
-#pragma unroll
-            for (int i = 0; i < 4; ++i) t2[i] = fmaf(g2[i], tmask[i], tmask[i]);
-            const s16x4 e2w = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(&sm.e2t[(16 * w + c) * KS + 4 * g]));
-            const f32x4 corr = mfma16h(pack4h(t2), e2w, b2w);
-            float *Q = sm.part[NW] + (4 * g) * RS + 16 * w + c;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Q[i * RS] = corr[i];
-            b2w = mfma16h(ones, e2w, b2w);
+            if (roww) {  // b2 tile w += 1^T E2
+                const s16x4 e2w = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(&sm.e2t[(16 * w + c) * KS + 4 * g]));
+                b2w = mfma16h(ones, e2w, b2w);
+            }
         }
         lds_barrier();
 
@@ -346,7 +343,7 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
         if (roww) {
             f32x4 zb2 = *reinterpret_cast<const f32x4 *>(&sm.part[0][r * RS + f0]);
 #pragma unroll
-            for (int q = 1; q <= NW; ++q) zb2 += *reinterpret_cast<const f32x4 *>(&sm.part[q][r * RS + f0]);
+            for (int q = 1; q < NW; ++q) zb2 += *reinterpret_cast<const f32x4 *>(&sm.part[q][r * RS + f0]);
             const f32x4 xqv = *reinterpret_cast<const f32x4 *>(&S.xqf[r * RS + f0]);
             if (ch + 1 < nch) {
                 stage(ch + 1);
