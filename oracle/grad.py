@@ -1,0 +1,103 @@
+"""fp64 gradients of the TTT-Linear inner loop -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests and the benchmark's CPU baseline may import this module; the
+GPU path never does, and it shares nothing with the GPU path.
+
+The forward below is the primal mini-batch recurrence (the definition: the
+per-token update-then-apply rule of the damodev.csdn.net TTT deep-dive §3.1
+with every token of a chunk taking its gradient at the chunk-start state,
+§4.1-4.2, and the LN-residual output of the lryc.cn TTT article §2.1), written
+with PyTorch CPU float64 tensor operations. Reverse-mode automatic
+differentiation of
+
+    loss = <dO, O> + <dW_out, W_L> + <db_out, b_L>
+
+then gives, to rounding, the gradients a training step needs from this layer
+(the deep-dive's §6 / §7.1 train the outer-loop parameters through the inner
+loop): with respect to XQ, XK, XV, eta, W0, b0, gamma and beta.
+
+The layer-norm L2 gradient G is written out (the same closed form as the C
+oracle's ln_l2_bwd) so that autograd differentiates through it; the tests pin
+that formula against autograd of the loss it is the gradient of, and the whole
+forward against the C oracle.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+_F64 = torch.float64
+
+
+def _t(a, grad: bool = False) -> torch.Tensor:
+    return torch.tensor(np.asarray(a, dtype=np.float64), dtype=_F64, requires_grad=grad)
+
+
+def ln(z: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor, eps: float) -> torch.Tensor:
+    """LN_{gamma,beta}(z) over the last axis, biased variance, eps inside the root."""
+    mu = z.mean(-1, keepdim=True)
+    var = ((z - mu) ** 2).mean(-1, keepdim=True)
+    return gamma * (z - mu) / torch.sqrt(var + eps) + beta
+
+
+def ln_l2_grad(z: torch.Tensor, tau: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor,
+               eps: float) -> torch.Tensor:
+    """G = d/dz 1/2 || LN_{gamma,beta}(z) - tau ||^2, row-wise (the deep-dive §4.2 step)."""
+    mu = z.mean(-1, keepdim=True)
+    sigma = torch.sqrt(((z - mu) ** 2).mean(-1, keepdim=True) + eps)
+    xhat = (z - mu) / sigma
+    ghat = gamma * (gamma * xhat + beta - tau)
+    return (ghat - ghat.mean(-1, keepdim=True) - xhat * (ghat * xhat).mean(-1, keepdim=True)) / sigma
+
+
+def linear_primal(XQ, XK, XV, eta, W0, b0, gamma, beta, eps: float, mb: int):
+    """Primal forward on torch tensors. XQ, XK, XV [B,H,L,d]; eta [B,H,L];
+    W0 [B,H,d,d]; b0 [B,H,d]; gamma, beta [H,d]. Returns O, W_L, b_L."""
+    B, H, L, d = XQ.shape
+    g = gamma[None, :, :]
+    bt = beta[None, :, :]
+    W, b = W0, b0
+    outs = []
+    for c0 in range(0, L, mb):
+        sl = slice(c0, min(L, c0 + mb))
+        xq, xk, xv, et = XQ[:, :, sl], XK[:, :, sl], XV[:, :, sl], eta[:, :, sl]
+        # every token of the chunk takes its gradient at the chunk-start state
+        Z = xk @ W + b[:, :, None, :]
+        G = ln_l2_grad(Z, xv - xk, g[:, :, None, :], bt[:, :, None, :], eps)
+        for t in range(xq.shape[2]):
+            # update with token t, then apply to token t
+            W = W - et[:, :, t, None, None] * xk[:, :, t, :, None] * G[:, :, t, None, :]
+            b = b - et[:, :, t, None] * G[:, :, t, :]
+            zb = (xq[:, :, t, None, :] @ W)[:, :, 0, :] + b
+            outs.append(xq[:, :, t, :] + ln(zb, g, bt, eps))
+    O = torch.stack(outs, 2) if outs else XQ * 0.0
+    return O, W, b
+
+
+def linear_backward(XQ, XK, XV, eta, W0, b0, gamma, beta, eps: float, mb: int, dO,
+                    dW_out: Optional[np.ndarray] = None, db_out: Optional[np.ndarray] = None) -> dict:
+    """Gradients of <dO, O> + <dW_out, W_L> + <db_out, b_L> (float64 NumPy).
+
+    W0 and b0 are per sequence ([B,H,d,d], [B,H,d]); gamma and beta are per
+    head ([H,d]), so their gradients are summed over the batch."""
+    B, H, L, d = np.shape(XQ)
+    W0 = np.broadcast_to(W0, (B, H, d, d))
+    b0 = np.broadcast_to(b0, (B, H, d))
+    names = ("XQ", "XK", "XV", "eta", "W0", "b0", "gamma", "beta")
+    ts = [_t(a, True) for a in (XQ, XK, XV, eta, W0, b0, gamma, beta)]
+    O, W, b = linear_primal(*ts, eps, mb)
+    loss = (O * _t(dO)).sum()
+    if dW_out is not None:
+        loss = loss + (W * _t(dW_out)).sum()
+    if db_out is not None:
+        loss = loss + (b * _t(db_out)).sum()
+    grads = torch.autograd.grad(loss, ts, allow_unused=True)
+    out = {}
+    for n, t, gr in zip(names, ts, grads):
+        out["d" + n] = np.zeros(t.shape) if gr is None else gr.detach().numpy()
+    out["O"] = O.detach().numpy()
+    out["W"] = W.detach().numpy()
+    out["b"] = b.detach().numpy()
+    return out
