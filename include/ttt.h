@@ -117,6 +117,38 @@ int ttt_mlp_forward(int B, int H, int L, int d, int mb, int io, float ln_eps,
                     float *W2_out, float *b2_out, hipStream_t stream);
 
 /*
+ * Backward of ttt_linear_forward: the gradients of
+ *   loss = <dO, O> + <dW_out, W_L> + <db_out, b_L>
+ * with respect to XQ, XK, XV, eta, W0, b0, gamma and beta, the gradients a
+ * training step takes through the inner loop ([D] §6, §7.1). Arguments as
+ * ttt_linear_forward for the forward inputs (same B, H, L, d, mb, io,
+ * ln_eps, w0_batched), plus:
+ *   dO [B,H,L,d] fp32; dW_out [B,H,d,d], db_out [B,H,d] fp32 or NULL (zero).
+ *   Outputs, fp32 and per sequence: dXQ, dXK, dXV [B,H,L,d]; deta [B,H,L];
+ *   dW0 [B,H,d,d]; db0, dgamma, dbeta [B,H,d]. Parameters shared over the
+ *   batch (W0 and b0 when w0_batched == 0, gamma, beta) need the caller's
+ *   sum over B.
+ *   workspace: device memory of at least the size ttt_linear_backward_workspace
+ *   reports (the state at every chunk start), caller-owned, overwritten.
+ * No output may overlap an input, another output or the workspace.
+ * Numerics: fp32 throughout (bf16 inputs widened); the forward is recomputed
+ * chunk by chunk from the stored states in the dual form ([D] §4.2).
+ * Errors as ttt_linear_forward; TTT_E_SHAPE also for a short workspace.
+ */
+int ttt_linear_backward(int B, int H, int L, int d, int mb, int io, float ln_eps,
+                        const void *XQ, const void *XK, const void *XV, const float *eta,
+                        const float *W0, const float *b0, int w0_batched,
+                        const float *ln_gamma, const float *ln_beta, const float *dO,
+                        const float *dW_out, const float *db_out, float *dXQ, float *dXK,
+                        float *dXV, float *deta, float *dW0, float *db0, float *dgamma,
+                        float *dbeta, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/* Workspace bytes ttt_linear_backward needs: B*H*ceil(L/mb)*(d*d+d)*4.
+ * Validates B, H, L, d, mb as ttt_linear_backward does. */
+int ttt_linear_backward_workspace(int B, int H, int L, int d, int mb, size_t *bytes);
+
+/*
  * One single-token TTT-Linear step (b = 1, primal form) for B x H independent
  * states held in place -- the fast-weight cache of [D] §5.2:
  *   G = lnbwd(xk W + b, xv - xk);  W <- W - eta xk^T G;  b <- b - eta G;

@@ -169,6 +169,64 @@ int ttt_linear_forward(int B, int H, int L, int d, int mb, int io, float ln_eps,
     return launched(ttt::launch_linear_valu(a, stream));
 }
 
+int ttt_linear_backward_workspace(int B, int H, int L, int d, int mb, size_t *bytes) {
+    int st;
+    if ((st = check_common(B, H, L, mb, TTT_F32))) return st;
+    if (d != 16 && d != 64) return fail(TTT_E_SHAPE, "d = %d not in {16, 64}", d);
+    if (!bytes) return fail(TTT_E_NULL, "bytes is NULL");
+    const size_t nch = L > 0 ? static_cast<size_t>((L + mb - 1) / mb) : 0;
+    if (!nbytes(bytes, {size_t(B), size_t(H), nch, size_t(d) * d + d, sizeof(float)}))
+        return fail(TTT_E_SHAPE, "sizes overflow");
+    return ok();
+}
+
+int ttt_linear_backward(int B, int H, int L, int d, int mb, int io, float ln_eps,
+                        const void *XQ, const void *XK, const void *XV, const float *eta,
+                        const float *W0, const float *b0, int w0_batched,
+                        const float *ln_gamma, const float *ln_beta, const float *dO,
+                        const float *dW_out, const float *db_out, float *dXQ, float *dXK,
+                        float *dXV, float *deta, float *dW0, float *db0, float *dgamma,
+                        float *dbeta, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+    int st;
+    if ((st = check_common(B, H, L, mb, io)) || (st = check_eps(ln_eps))) return st;
+    if (d != 16 && d != 64) return fail(TTT_E_SHAPE, "d = %d not in {16, 64}", d);
+    const size_t es = io == TTT_BF16 ? 2 : 4;
+    const size_t nb = w0_batched ? static_cast<size_t>(B) : 1;
+    size_t xb, fb, eb, wb, bb, ob_w, ob_b, pb, need;
+    if (!nbytes(&xb, {size_t(B), size_t(H), size_t(L), size_t(d), es}) ||
+        !nbytes(&fb, {size_t(B), size_t(H), size_t(L), size_t(d), sizeof(float)}) ||
+        !nbytes(&eb, {size_t(B), size_t(H), size_t(L), sizeof(float)}) ||
+        !nbytes(&wb, {nb, size_t(H), size_t(d), size_t(d), sizeof(float)}) ||
+        !nbytes(&bb, {nb, size_t(H), size_t(d), sizeof(float)}) ||
+        !nbytes(&ob_w, {size_t(B), size_t(H), size_t(d), size_t(d), sizeof(float)}) ||
+        !nbytes(&ob_b, {size_t(B), size_t(H), size_t(d), sizeof(float)}) ||
+        !nbytes(&pb, {size_t(H), size_t(d), sizeof(float)}))
+        return fail(TTT_E_SHAPE, "sizes overflow");
+    if ((st = ttt_linear_backward_workspace(B, H, L, d, mb, &need))) return st;
+    const Buf in[] = {{XQ, xb, "XQ", false, 16},        {XK, xb, "XK", false, 16},
+                      {XV, xb, "XV", false, 16},        {eta, eb, "eta", false, 4},
+                      {W0, wb, "W0", false, 16},        {b0, bb, "b0", false, 16},
+                      {ln_gamma, pb, "ln_gamma", false, 4}, {ln_beta, pb, "ln_beta", false, 4},
+                      {dO, fb, "dO", false, 4},         {dW_out, ob_w, "dW_out", true, 4},
+                      {db_out, ob_b, "db_out", true, 4}};
+    const Buf out[] = {{dXQ, fb, "dXQ", false, 4},   {dXK, fb, "dXK", false, 4},
+                       {dXV, fb, "dXV", false, 4},   {deta, eb, "deta", false, 4},
+                       {dW0, ob_w, "dW0", false, 4}, {db0, ob_b, "db0", false, 4},
+                       {dgamma, ob_b, "dgamma", false, 4}, {dbeta, ob_b, "dbeta", false, 4},
+                       {workspace, need, "workspace", false, 4}};
+    if ((st = check_bufs(in, 11)) || (st = check_bufs(out, 9))) return st;
+    if (workspace_bytes < need)
+        return fail(TTT_E_SHAPE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    if ((st = check_alias(out, 9, in, 11, nullptr))) return st;
+    if (B * H == 0) return ok();
+    ttt::LinearBwdArgs a{{B, H, L, d, mb, io, ln_eps, XQ, XK, XV, eta, W0, b0, w0_batched ? 1 : 0,
+                          ln_gamma, ln_beta, nullptr, nullptr, nullptr},
+                         dO, dW_out, db_out, dXQ, dXK, dXV, deta, dW0, db0, dgamma, dbeta,
+                         static_cast<float *>(workspace)};
+    return launched(ttt::launch_linear_backward(a, stream));
+}
+
 int ttt_mlp_forward(int B, int H, int L, int d, int mb, int io, float ln_eps,
                     const void *XQ, const void *XK, const void *XV, const float *eta,
                     const float *W1_0, const float *b1_0, const float *W2_0,

@@ -18,6 +18,13 @@ struct LinearArgs {
     float *W_out, *b_out;
 };
 
+struct LinearBwdArgs {
+    LinearArgs f;  // forward arguments (O, W_out, b_out unused)
+    const float *dO, *dW_out, *db_out;
+    float *dXQ, *dXK, *dXV, *deta, *dW0, *db0, *dgamma, *dbeta;
+    float *ws;  // chunk-start states, linear_backward_workspace_floats floats
+};
+
 struct MLPArgs {
     int B, H, L, d, mb, io;
     float eps;
@@ -44,6 +51,8 @@ hipError_t launch_ln_l2_bwd(int rows, int d, const float *Z, const float *T, con
 hipError_t launch_linear_valu(const LinearArgs &a, hipStream_t stream);
 bool linear_mfma_supported(const LinearArgs &a);
 hipError_t launch_linear_mfma(const LinearArgs &a, hipStream_t stream);
+size_t linear_backward_workspace_floats(int B, int H, int L, int d, int mb);
+hipError_t launch_linear_backward(const LinearBwdArgs &a, hipStream_t stream);
 hipError_t launch_mlp(const MLPArgs &a, hipStream_t stream);
 bool mlp_mfma_supported(const MLPArgs &a);
 hipError_t launch_mlp_mfma(const MLPArgs &a, hipStream_t stream);

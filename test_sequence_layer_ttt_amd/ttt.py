@@ -6,6 +6,7 @@ Every step of the computation runs in the library's kernels.
 """
 from __future__ import annotations
 
+import ctypes
 from typing import Optional
 
 import torch
@@ -73,6 +74,59 @@ def ttt_linear_forward(XQ, XK, XV, eta, W0, b0, ln_gamma, ln_beta, O=None, W_out
                                       _ptr(ln_gamma), _ptr(ln_beta), _ptr(O), _ptr(W_out),
                                       _ptr(b_out), _stream(stream)))
     return O, W_out, b_out
+
+
+def ttt_linear_backward_workspace(B: int, H: int, L: int, d: int, mb: int = 16) -> int:
+    """Bytes of device workspace ttt_linear_backward needs."""
+    n = ctypes.c_size_t(0)
+    lib = _lib.load()
+    _lib.check(lib.ttt_linear_backward_workspace(B, H, L, d, mb, ctypes.byref(n)))
+    return n.value
+
+
+def ttt_linear_backward(XQ, XK, XV, eta, W0, b0, ln_gamma, ln_beta, dO, dW_out=None, db_out=None,
+                        mb: int = 16, ln_eps: float = 1e-6, workspace=None, stream=None) -> dict:
+    """Gradients of <dO,O> + <dW_out,W_L> + <db_out,b_L> through ttt_linear_forward.
+    Inputs as ttt_linear_forward plus dO [B,H,L,d] fp32 and optional dW_out
+    [B,H,d,d], db_out [B,H,d]. Returns per-sequence fp32 gradients dXQ, dXK,
+    dXV [B,H,L,d], deta [B,H,L], dW0 [B,H,d,d], db0, dgamma, dbeta [B,H,d]."""
+    B, H, L, d = XQ.shape
+    io = _IO.get(XQ.dtype)
+    if io is None:
+        raise TypeError(f"XQ dtype {XQ.dtype} not supported")
+    batched = W0.dim() == 4
+    for t, n in ((XQ, "XQ"), (XK, "XK"), (XV, "XV")):
+        _need(t, n, (B, H, L, d), XQ.dtype)
+    _need(eta, "eta", (B, H, L), torch.float32)
+    _need(W0, "W0", ((B,) if batched else ()) + (H, d, d), torch.float32)
+    _need(b0, "b0", ((B,) if batched else ()) + (H, d), torch.float32)
+    _need(ln_gamma, "ln_gamma", (H, d), torch.float32)
+    _need(ln_beta, "ln_beta", (H, d), torch.float32)
+    _need(dO, "dO", (B, H, L, d), torch.float32)
+    if dW_out is not None:
+        _need(dW_out, "dW_out", (B, H, d, d), torch.float32)
+    if db_out is not None:
+        _need(db_out, "db_out", (B, H, d), torch.float32)
+    kw = dict(device=XQ.device, dtype=torch.float32)
+    g = {"dXQ": torch.empty((B, H, L, d), **kw), "dXK": torch.empty((B, H, L, d), **kw),
+         "dXV": torch.empty((B, H, L, d), **kw), "deta": torch.empty((B, H, L), **kw),
+         "dW0": torch.empty((B, H, d, d), **kw), "db0": torch.empty((B, H, d), **kw),
+         "dgamma": torch.empty((B, H, d), **kw), "dbeta": torch.empty((B, H, d), **kw)}
+    need = ttt_linear_backward_workspace(B, H, L, d, mb)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), device=XQ.device, dtype=torch.uint8)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    lib = _lib.load()
+    _lib.check(lib.ttt_linear_backward(B, H, L, d, mb, io, ln_eps, _ptr(XQ), _ptr(XK), _ptr(XV),
+                                       _ptr(eta), _ptr(W0), _ptr(b0), int(batched),
+                                       _ptr(ln_gamma), _ptr(ln_beta), _ptr(dO), _ptr(dW_out),
+                                       _ptr(db_out), _ptr(g["dXQ"]), _ptr(g["dXK"]),
+                                       _ptr(g["dXV"]), _ptr(g["deta"]), _ptr(g["dW0"]),
+                                       _ptr(g["db0"]), _ptr(g["dgamma"]), _ptr(g["dbeta"]),
+                                       _ptr(workspace), nbytes, _stream(stream)))
+    return g
 
 
 def ttt_mlp_forward(XQ, XK, XV, eta, W1, b1, W2, b2, ln_gamma, ln_beta, O=None, outs=None,

@@ -19,7 +19,9 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _lib.header_functions()
     assert set(names) >= {"ttt_linear_forward", "ttt_mlp_forward", "ttt_decode_step",
-                          "ttt_decode_steps", "ttt_ln_l2_bwd", "ttt_last_error", "ttt_version"}
+                          "ttt_decode_steps", "ttt_linear_backward",
+                          "ttt_linear_backward_workspace", "ttt_ln_l2_bwd", "ttt_last_error",
+                          "ttt_version"}
     for n in names:
         assert hasattr(lib, n), n
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
@@ -142,6 +144,44 @@ def test_decode_steps_validation(lib):
     # no steps, or no states: nothing to do, no HIP call
     assert lib.ttt_decode_steps(0, 2, 3, 64, 1, 1e-6, *p[:9], None) == _lib.TTT_OK
     assert lib.ttt_decode_steps(5, 0, 3, 64, 1, 1e-6, *p[:9], None) == _lib.TTT_OK
+
+
+def _bwd(lib, B=2, H=3, L=40, d=64, mb=16, io=1, eps=1e-6, ws_bytes=None, ptrs=None, ws=None):
+    p = ptrs or [FAKE + i * (1 << 24) for i in range(20)]
+    need = ctypes.c_size_t(0)
+    lib.ttt_linear_backward_workspace(max(B, 0), max(H, 0), max(L, 0), 64, 16, ctypes.byref(need))
+    nb = need.value if ws_bytes is None else ws_bytes
+    return lib.ttt_linear_backward(B, H, L, d, mb, io, eps, p[0], p[1], p[2], p[3], p[4], p[5], 0,
+                                   p[6], p[7], p[8], None, None, p[9], p[10], p[11], p[12], p[13],
+                                   p[14], p[15], p[16], ws if ws is not None else p[17], nb, None)
+
+
+def test_linear_backward_workspace_size(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.ttt_linear_backward_workspace(2, 3, 40, 64, 16, ctypes.byref(n)) == _lib.TTT_OK
+    assert n.value == 2 * 3 * 3 * (64 * 64 + 64) * 4  # ceil(40 / 16) = 3 chunk-start states
+    assert lib.ttt_linear_backward_workspace(2, 3, 0, 16, 4, ctypes.byref(n)) == _lib.TTT_OK
+    assert n.value == 0
+    assert lib.ttt_linear_backward_workspace(2, 3, 40, 48, 16, ctypes.byref(n)) == _lib.TTT_E_SHAPE
+    assert lib.ttt_linear_backward_workspace(2, 3, 40, 64, 16, None) == _lib.TTT_E_NULL
+
+
+def test_linear_backward_validation(lib):
+    assert _bwd(lib, ws_bytes=1024) == _lib.TTT_E_SHAPE
+    assert "workspace" in lib.ttt_last_error().decode()
+    assert _bwd(lib, d=32) == _lib.TTT_E_SHAPE
+    assert _bwd(lib, mb=0) == _lib.TTT_E_SHAPE
+    assert _bwd(lib, io=3) == _lib.TTT_E_DTYPE
+    assert _bwd(lib, eps=0.0) == _lib.TTT_E_SHAPE
+    p = [FAKE + i * (1 << 24) for i in range(20)]
+    q = list(p); q[9] = p[0]  # dXQ on XQ
+    assert _bwd(lib, ptrs=q) == _lib.TTT_E_ALIAS
+    q = list(p); q[12] = p[13]  # deta on dW0
+    assert _bwd(lib, ptrs=q) == _lib.TTT_E_ALIAS
+    assert _bwd(lib, ws=p[11]) == _lib.TTT_E_ALIAS  # workspace on dXV
+    q = list(p); q[8] = 0  # dO
+    assert _bwd(lib, ptrs=q) == _lib.TTT_E_NULL
+    assert _bwd(lib, B=0) == _lib.TTT_OK  # nothing to do, no HIP call
 
 
 def test_ln_bwd_validation(lib):
