@@ -13,6 +13,8 @@ Other workloads of the same hot path (--workload):
   5d  TTT-Linear decode: one b=1 step on 64 x 32 states (roofline: state bytes)
   5r  TTT-Linear decode: 1024 b=1 steps on 64 x 32 states in one call, states
       resident in registers (roofline: fp32 vector ALU)
+  3b  TTT-Linear backward (ttt_linear_backward) on workload 3's shapes
+      (roofline: fp32 vector ALU)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
                        [--no-cpu-baseline]
@@ -64,6 +66,15 @@ def alg_flops_decode_step(B, H, d):
     return B * H * 6 * d * d
 
 
+def alg_flops_linear_backward(B, H, L, d, b=16):
+    """Algorithmic flops of one ttt_linear_backward launch per token-head:
+    the forward pass that stores the chunk-start states (XK W and the state
+    update, 4 d^2), the recomputed chunk (XK W, XQ W, T E: 4 d^2 + 2 b d),
+    and the reverse products (dZb W^T, XK dW', E dW'^T, dZ W^T, XQ^T dZb,
+    XK^T dZ: 12 d^2; dA, T^T dZb, dA XK, dA^T XQ: 8 b d; T: 2 b d)."""
+    return B * H * L * (20 * d * d + 12 * b * d)
+
+
 def kernel_sources_hash():
     from test_sequence_layer_ttt_amd import build as hb
     h = hashlib.sha256()
@@ -102,7 +113,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="3", choices=["3", "2", "5p", "4", "5d", "5r"])
+    ap.add_argument("--workload", default="3", choices=["3", "2", "5p", "4", "5d", "5r", "3b"])
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -135,6 +146,8 @@ def main():
         return bench_decode(args)
     if args.workload == "5r":
         return bench_decode_steps(args)
+    if args.workload == "3b":
+        return bench_backward(args)
     wl = {"3": 3, "2": 2, "5p": 5}[args.workload]
     w = gen.WORKLOADS[wl]
     x = gen.make_workload(wl, decode_steps=0) if wl == 5 else gen.make_workload(wl)
@@ -402,6 +415,51 @@ def bench_decode_steps(args):
           {"workload": "ttt_linear_decode_steps_bf16_T1024_B64_H32_d64", "T": S, "B": B, "H": H,
            "d": d, "io": "bf16", "state": "fp32, resident in registers",
            "parallelism": "none (1 GPU)"}, roof, extra)
+
+
+def bench_backward(args):
+    """ttt_linear_backward on workload 3's shapes (B=2, H=32, L=8192, d=64,
+    b=16, bf16 inputs), with a seeded dO and dW_out = db_out = 0."""
+    import numpy as np
+    import torch
+    from test_sequence_layer_ttt_amd import gen, ttt
+    x = gen.make_workload(3)
+    B, H, L, d = x.B, x.H, x.L, x.d
+    dev = torch.device("cuda:0")
+    T = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev).to(dt)
+    bf = torch.bfloat16
+    ins = [T(x.XQ, bf), T(x.XK, bf), T(x.XV, bf), T(x.eta), T(x.W0), T(x.b0), T(x.gamma), T(x.beta)]
+    dO = torch.randn((B, H, L, d), generator=torch.Generator(device="cpu").manual_seed(3),
+                     dtype=torch.float32).to(dev)
+    ws = torch.empty(ttt.ttt_linear_backward_workspace(B, H, L, d, 16), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+    step = lambda: ttt.ttt_linear_backward(*ins, dO, mb=16, ln_eps=x.eps, workspace=ws,
+                                           stream=stream)
+    wall, kern = _timed(step, stream, args.warmup, args.steps)
+    fl = alg_flops_linear_backward(B, H, L, d)
+    roof = {"bound": "alu", "achieved": fl / kern / 1e12, "peak": FP32_VECTOR_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": fl / kern / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
+            "traffic": None, "kernel": "linear_backward_kernel", "kernel_avg_us": kern * 1e6,
+            "alg_flops_per_launch": fl}
+    extra = {}
+    if not args.no_cpu_baseline:
+        from oracle import grad as OG
+        # bounded sample: one sequence, the first 1024 tokens
+        ns = 1024
+        sl = lambda a: np.ascontiguousarray(a[:1, :1, :ns])
+        t1 = time.perf_counter()
+        OG.linear_backward(sl(x.XQ), sl(x.XK), sl(x.XV), sl(x.eta), x.W0[:1], x.b0[:1],
+                           x.gamma[:1], x.beta[:1], x.eps, 16, dO[:1, :1, :ns].cpu().numpy())
+        tc = time.perf_counter() - t1
+        extra["cpu_baseline"] = {"value": ns / tc, "unit": "token-heads/s (one head)",
+                                 "cores": torch.get_num_threads(), "kind": "oracle",
+                                 "sample": f"autograd of the fp64 primal recurrence, one head, "
+                                           f"{ns} tokens, {tc:.2f} s"}
+    _line("TTT-Linear backward tokens/s (L=8192)", B * L / wall, args, wall, "bf16 in, fp32",
+          {"workload": "ttt_linear_backward_bf16_B2_H32_L8192_d64", "B": B, "H": H, "L": L,
+           "d": d, "mini_batch": 16, "io": "bf16", "grads": "fp32", "parallelism": "none (1 GPU)"},
+          roof, extra)
 
 
 if __name__ == "__main__":

@@ -29,27 +29,46 @@
 // One 256-thread workgroup per (n, h) sequence. A forward pass stores the
 // state at every chunk start in the caller's workspace; the reverse pass
 // reloads it, recomputes the chunk and applies the rules above, keeping the
-// adjoint dW, db in LDS. Row work runs 16 threads per token row (thread
-// (r, q) holds features q + 16u); products are fp32 FMAs over LDS tiles
-// whose rows are padded to d + 1 floats so that the 16 row groups reading
-// the same column hit different banks.
+// adjoint dW, db in LDS. Row work (layer norms, their reverses) runs 16
+// threads per token row, one DPP row (thread (r, q) holds features q + 16u;
+// row sums are four v_add_f32_dpp steps). Every product
+// runs on fp32 matrix cores (16x16x4 f32 MFMA: full fp32 products, fp32
+// accumulation): wave u computes the 16-column tile u of each [16 x d]
+// result, and tiles (rb, u) of each [d x d] state update, reading its
+// operands from LDS tiles whose rows are padded to d + 1 floats.
 #include "common.hpp"
 #include "launch.hpp"
+#include "tile.hpp"
 
 namespace ttt {
 namespace {
 
 constexpr int NT = 256, RW = 16;  // threads; lanes per token row
 
+using tile::f32x4;
+
 template <int D>
 struct BwdSmem {
-    static constexpr int DP = D + 1;
+    static constexpr int DP = D + 1, TP = RW + 1;
     float W[D * DP], dW[D * DP];
     float b[D], db[D];
-    float XQ[RW * DP], XK[RW * DP], E[RW * DP], dZb[RW * DP], dZ[RW * DP];
-    float T[RW * (RW + 1)], dA[RW * (RW + 1)];
-    float red[RW * D];  // final dgamma / dbeta reduction over rows
+    // [16 x d] row tiles (token rows, feature columns)
+    float XQ[RW * DP], XK[RW * DP], Z[RW * DP], Zb[RW * DP], E[RW * DP], dZb[RW * DP];
+    float dE[RW * DP], dZ[RW * DP], dT[RW * DP], dO[RW * DP];
+    float T[RW * TP], dA[RW * TP];  // [t][s]
+    float red[RW * D];              // final dgamma / dbeta reduction over rows
 };
+
+// One 16x16 output tile of C + A B over K (a multiple of 4) on fp32 MFMAs.
+// Lane (g, c) supplies A[c][k] and B[k][c] for k = 4 kb + g and receives
+// rows 4g .. 4g+3 of column c. A(m, k) and B(k, n) are accessors into LDS.
+template <int K, typename FA, typename FB>
+__device__ __forceinline__ f32x4 mma(FA A, FB B, int g, int c, f32x4 acc) {
+#pragma unroll
+    for (int kb = 0; kb < K / 4; ++kb)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A(c, 4 * kb + g), B(4 * kb + g, c), acc, 0, 0, 0);
+    return acc;
+}
 
 template <int D, typename TIO>
 __global__ __launch_bounds__(NT) void linear_backward_kernel(
@@ -61,12 +80,14 @@ __global__ __launch_bounds__(NT) void linear_backward_kernel(
     float *__restrict__ dXV, float *__restrict__ deta, float *__restrict__ dW0,
     float *__restrict__ db0, float *__restrict__ dgamma, float *__restrict__ dbeta,
     float *__restrict__ ws) {
-    constexpr int NF = D / RW, DP = D + 1, TP = RW + 1;
+    constexpr int NF = D / RW, DP = D + 1, TP = RW + 1, NTL = D / 16;
     constexpr float inv_d = 1.0f / D;
     using io = io_traits<TIO>;
     __shared__ BwdSmem<D> sm;
 
     const int tid = threadIdx.x, r = tid / RW, q = tid % RW;
+    const int w = tid / 64, lane = tid % 64, g = lane / 16, c = lane % 16;  // MFMA coordinates
+    const bool mw = w < NTL;  // this wave owns column tile w
     const long seq = blockIdx.x;
     const int h = static_cast<int>(seq % H);
     const long n = seq / H;
@@ -74,6 +95,40 @@ __global__ __launch_bounds__(NT) void linear_backward_kernel(
     const size_t xbase = static_cast<size_t>(seq) * L * D;
     const size_t st = (w0_batched ? static_cast<size_t>(n) * H : 0) + static_cast<size_t>(h);
     float *wsq = ws + static_cast<size_t>(seq) * nch * (D * D + D);
+    const f32x4 fz = {0.f, 0.f, 0.f, 0.f};
+
+    // LDS accessors: row-major tiles and their transposes
+    auto rowm = [](const float *M, int ld) { return [M, ld](int i, int j) { return M[i * ld + j]; }; };
+    auto colm = [](const float *M, int ld) { return [M, ld](int i, int j) { return M[j * ld + i]; }; };
+    // store a [16 x d] tile result (rows 4g+i, column 16 w + c)
+    auto put = [&](float *M, f32x4 v) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) M[(4 * g + i) * DP + 16 * w + c] = v[i];
+    };
+    auto get = [&](const float *M) {
+        f32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = M[(4 * g + i) * DP + 16 * w + c];
+        return v;
+    };
+    auto brow = [&](const float *bb) {  // b broadcast over the tile's rows
+        const float x = bb[16 * w + c];
+        return f32x4{x, x, x, x};
+    };
+    // M[d x d] += P^T Q over the m token rows, on tiles (rb, w); P, Q [16 x d]
+    auto state_update = [&](float *M, const float *P, const float *Q, const float *P2, const float *Q2) {
+        if (!mw) return;
+#pragma unroll
+        for (int rb = 0; rb < NTL; ++rb) {
+            f32x4 acc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = M[(16 * rb + 4 * g + i) * DP + 16 * w + c];
+            acc = mma<RW>(colm(P + 16 * rb, DP), rowm(Q + 16 * w, DP), g, c, acc);
+            if (P2) acc = mma<RW>(colm(P2 + 16 * rb, DP), rowm(Q2 + 16 * w, DP), g, c, acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) M[(16 * rb + 4 * g + i) * DP + 16 * w + c] = acc[i];
+        }
+    };
 
     float gm[NF], bt[NF];
 #pragma unroll
@@ -83,18 +138,9 @@ __global__ __launch_bounds__(NT) void linear_backward_kernel(
     }
     for (int i = tid; i < D * D; i += NT) sm.W[(i / D) * DP + i % D] = W0[st * D * D + i];
     if (tid < D) sm.b[tid] = b0[st * D + tid];
+    for (int i = tid; i < RW * DP; i += NT) sm.E[i] = 0.f;
     __syncthreads();
 
-    // Z = XK W + b for this thread's row and features (XK row in LDS)
-    auto xw = [&](const float *X, float (&out)[NF]) {
-#pragma unroll
-        for (int u = 0; u < NF; ++u) out[u] = sm.b[q + RW * u];
-        for (int k = 0; k < D; ++k) {
-            const float x = X[r * DP + k];
-#pragma unroll
-            for (int u = 0; u < NF; ++u) out[u] = fmaf(x, sm.W[k * DP + q + RW * u], out[u]);
-        }
-    };
     // layer-norm L2 gradient of one row (16 lanes) and what its reverse needs
     struct Lnl2 {
         float xh[NF], gh[NF], G[NF];
@@ -104,10 +150,10 @@ __global__ __launch_bounds__(NT) void linear_backward_kernel(
         float s1 = 0.f, s2 = 0.f;
 #pragma unroll
         for (int u = 0; u < NF; ++u) s1 += z[u];
-        const float mu = group_sum<RW>(s1) * inv_d;
+        const float mu = tile::row16_sum(s1) * inv_d;
 #pragma unroll
         for (int u = 0; u < NF; ++u) s2 += (z[u] - mu) * (z[u] - mu);
-        s.sigma = sqrtf(group_sum<RW>(s2) * inv_d + eps);
+        s.sigma = sqrtf(tile::row16_sum(s2) * inv_d + eps);
         const float rs = 1.0f / s.sigma;
         float sa = 0.f, sc = 0.f;
 #pragma unroll
@@ -117,47 +163,82 @@ __global__ __launch_bounds__(NT) void linear_backward_kernel(
             sa += s.gh[u];
             sc += s.gh[u] * s.xh[u];
         }
-        const float a = group_sum<RW>(sa) * inv_d;
-        s.c = group_sum<RW>(sc) * inv_d;
+        const float a = tile::row16_sum(sa) * inv_d;
+        s.c = tile::row16_sum(sc) * inv_d;
 #pragma unroll
         for (int u = 0; u < NF; ++u) s.G[u] = (s.gh[u] - a - s.xh[u] * s.c) * rs;
     };
-    auto load_rows = [&](int c, int m, float (&xk)[NF], float (&tau)[NF], float &et) {
-        const bool ok = r < m;
-        const size_t row = xbase + static_cast<size_t>(c * mb + (ok ? r : 0)) * D;
+    // Inputs of one chunk for this thread's row (zero past the end of the
+    // sequence), and one chunk-start state: fetched into registers a chunk
+    // ahead of their use so that the global-memory latency hides behind the
+    // current chunk.
+    constexpr int NWP = D * D / NT;
+    struct Rows {
+        float xq[NF], xk[NF], xv[NF], go[NF], et;
+    };
+    struct State {
+        float w[NWP], b;
+    };
+    auto fetch_rows = [&](int ch, bool rev, Rows &R) {
+        const bool ok = r < min(mb, L - ch * mb);
+        const size_t row = xbase + static_cast<size_t>(ch * mb + (ok ? r : 0)) * D;
 #pragma unroll
         for (int u = 0; u < NF; ++u) {
             const int f = q + RW * u;
-            xk[u] = ok ? io::load(XK, row + f) : 0.f;
-            tau[u] = ok ? io::load(XV, row + f) - xk[u] : 0.f;
-            sm.XK[r * DP + f] = xk[u];
+            R.xk[u] = ok ? io::load(XK, row + f) : 0.f;
+            R.xv[u] = ok ? io::load(XV, row + f) : 0.f;
+            R.xq[u] = ok && rev ? io::load(XQ, row + f) : 0.f;
+            R.go[u] = ok && rev ? dO[row + f] : 0.f;
         }
-        et = ok ? eta[static_cast<size_t>(seq) * L + c * mb + r] : 0.f;
+        R.et = ok ? eta[static_cast<size_t>(seq) * L + ch * mb + r] : 0.f;
+    };
+    auto fetch_state = [&](int ch, State &S) {
+        const float *wc = wsq + static_cast<size_t>(ch) * (D * D + D);
+#pragma unroll
+        for (int k = 0; k < NWP; ++k) S.w[k] = wc[tid + NT * k];
+        S.b = tid < D ? wc[D * D + tid] : 0.f;
+    };
+    // stage a chunk's rows: XK (and XQ, dO) into LDS; tau and eta into registers
+    auto stage_rows = [&](const Rows &R, bool rev, float (&tau)[NF], float &et) {
+#pragma unroll
+        for (int u = 0; u < NF; ++u) {
+            const int f = q + RW * u;
+            sm.XK[r * DP + f] = R.xk[u];
+            tau[u] = R.xv[u] - R.xk[u];
+            if (rev) {
+                sm.XQ[r * DP + f] = R.xq[u];
+                sm.dO[r * DP + f] = R.go[u];
+            }
+        }
+        et = R.et;
+    };
+    auto rowz = [&](const float *M, float (&z)[NF]) {
+#pragma unroll
+        for (int u = 0; u < NF; ++u) z[u] = M[r * DP + q + RW * u];
     };
 
     // ===== forward: chunk-start states to the workspace ========================
-    for (int c = 0; c < nch; ++c) {
-        const int m = min(mb, L - c * mb);
-        float *wc = wsq + static_cast<size_t>(c) * (D * D + D);
+    Rows R;
+    if (nch > 0) fetch_rows(0, false, R);
+    for (int ch = 0; ch < nch; ++ch) {
+        const int m = min(mb, L - ch * mb);
+        float *wc = wsq + static_cast<size_t>(ch) * (D * D + D);
         for (int i = tid; i < D * D; i += NT) wc[i] = sm.W[(i / D) * DP + i % D];
         if (tid < D) wc[D * D + tid] = sm.b[tid];
-        float xk[NF], tau[NF], et;
-        load_rows(c, m, xk, tau, et);
+        float tau[NF], et;
+        stage_rows(R, false, tau, et);
+        if (ch + 1 < nch) fetch_rows(ch + 1, false, R);
+        __syncthreads();
+        if (mw) put(sm.Z, mma<D>(rowm(sm.XK, DP), rowm(sm.W + 16 * w, DP), g, c, brow(sm.b)));
         __syncthreads();
         float z[NF];
-        xw(sm.XK, z);
+        rowz(sm.Z, z);
         Lnl2 s;
         lnl2(z, tau, s);
 #pragma unroll
         for (int u = 0; u < NF; ++u) sm.E[r * DP + q + RW * u] = -et * s.G[u];
         __syncthreads();
-        // W += XK^T E, b += 1^T E
-        for (int i = tid; i < D * D; i += NT) {
-            const int a = i / D, bcol = i % D;
-            float acc = sm.W[a * DP + bcol];
-            for (int s2 = 0; s2 < m; ++s2) acc = fmaf(sm.XK[s2 * DP + a], sm.E[s2 * DP + bcol], acc);
-            sm.W[a * DP + bcol] = acc;
-        }
+        state_update(sm.W, sm.XK, sm.E, nullptr, nullptr);  // W += XK^T E
         if (tid < D) {
             float acc = sm.b[tid];
             for (int s2 = 0; s2 < m; ++s2) acc += sm.E[s2 * DP + tid];
@@ -175,58 +256,68 @@ __global__ __launch_bounds__(NT) void linear_backward_kernel(
 #pragma unroll
     for (int u = 0; u < NF; ++u) dg_acc[u] = db_acc[u] = 0.f;
 
-    for (int c = nch - 1; c >= 0; --c) {
-        const int m = min(mb, L - c * mb);
+    State S;
+    if (nch > 0) {
+        fetch_rows(nch - 1, true, R);
+        fetch_state(nch - 1, S);
+    }
+    for (int ch = nch - 1; ch >= 0; --ch) {
+        const int m = min(mb, L - ch * mb);
         const bool ok = r < m;
-        const float *wc = wsq + static_cast<size_t>(c) * (D * D + D);
         __syncthreads();  // the previous chunk is done with every tile
-        for (int i = tid; i < D * D; i += NT) sm.W[(i / D) * DP + i % D] = wc[i];
-        if (tid < D) sm.b[tid] = wc[D * D + tid];
-        float xk[NF], tau[NF], et, xq[NF], go[NF];
-        load_rows(c, m, xk, tau, et);
-        const size_t row = xbase + static_cast<size_t>(c * mb + (ok ? r : 0)) * D;
 #pragma unroll
-        for (int u = 0; u < NF; ++u) {
-            const int f = q + RW * u;
-            xq[u] = ok ? io::load(XQ, row + f) : 0.f;
-            go[u] = ok ? dO[row + f] : 0.f;
-            sm.XQ[r * DP + f] = xq[u];
+        for (int k = 0; k < NWP; ++k) {
+            const int i = tid + NT * k;
+            sm.W[(i / D) * DP + i % D] = S.w[k];
+        }
+        if (tid < D) sm.b[tid] = S.b;
+        float tau[NF], et, go[NF];
+        stage_rows(R, true, tau, et);
+#pragma unroll
+        for (int u = 0; u < NF; ++u) go[u] = R.go[u];
+        if (ch > 0) {
+            fetch_rows(ch - 1, true, R);
+            fetch_state(ch - 1, S);
         }
         __syncthreads();
 
-        // recompute: Z, G, E; XQ W + b
-        float z[NF], zq[NF];
-        xw(sm.XK, z);
-        xw(sm.XQ, zq);
+        // Z = XK W + b, Zq = XQ W + b (tile w); T = XQ XK^T + 1 on the causal triangle
+        if (mw) {
+            put(sm.Z, mma<D>(rowm(sm.XK, DP), rowm(sm.W + 16 * w, DP), g, c, brow(sm.b)));
+            put(sm.Zb, mma<D>(rowm(sm.XQ, DP), rowm(sm.W + 16 * w, DP), g, c, brow(sm.b)));
+        }
+        if (w == NT / 64 - 1) {
+            const f32x4 t4 = mma<D>(rowm(sm.XQ, DP), colm(sm.XK, DP), g, c, fz);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 4 * g + i;
+                sm.T[t * TP + c] = (c <= t && t < m) ? t4[i] + 1.f : 0.f;
+            }
+        }
+        __syncthreads();
+        float z[NF];
+        rowz(sm.Z, z);
         Lnl2 s;
         lnl2(z, tau, s);
 #pragma unroll
         for (int u = 0; u < NF; ++u) sm.E[r * DP + q + RW * u] = -et * s.G[u];
-        {  // T[t][s] = XQ_t . XK_s + 1 on the causal triangle of the chunk
-            const int t = tid / RW, s2 = tid % RW;
-            float acc = 0.f;
-            for (int k = 0; k < D; ++k) acc = fmaf(sm.XQ[t * DP + k], sm.XK[s2 * DP + k], acc);
-            sm.T[t * TP + s2] = (s2 <= t && t < m) ? acc + 1.f : 0.f;
-        }
         __syncthreads();
 
-        // Zb = XQ W + b + T E, its layer norm, and the reverse of O = XQ + LN(Zb)
-        float zb[NF];
-#pragma unroll
-        for (int u = 0; u < NF; ++u) zb[u] = zq[u];
-        for (int s2 = 0; s2 < RW; ++s2) {
-            const float tv = sm.T[r * TP + s2];
-#pragma unroll
-            for (int u = 0; u < NF; ++u) zb[u] = fmaf(tv, sm.E[s2 * DP + q + RW * u], zb[u]);
-        }
+        // Zb = XQ W + b + T E
+        if (mw) put(sm.Zb, mma<RW>(rowm(sm.T, TP), rowm(sm.E + 16 * w, DP), g, c, get(sm.Zb)));
+        __syncthreads();
+
+        // the reverse of O = XQ + LN(Zb)
         {
+            float zb[NF];
+            rowz(sm.Zb, zb);
             float s1 = 0.f, s2 = 0.f;
 #pragma unroll
             for (int u = 0; u < NF; ++u) s1 += zb[u];
-            const float mu = group_sum<RW>(s1) * inv_d;
+            const float mu = tile::row16_sum(s1) * inv_d;
 #pragma unroll
             for (int u = 0; u < NF; ++u) s2 += (zb[u] - mu) * (zb[u] - mu);
-            const float rs = 1.0f / sqrtf(group_sum<RW>(s2) * inv_d + eps);
+            const float rs = 1.0f / sqrtf(tile::row16_sum(s2) * inv_d + eps);
             float xb[NF], dx[NF], m1 = 0.f, m2 = 0.f;
 #pragma unroll
             for (int u = 0; u < NF; ++u) {
@@ -237,59 +328,45 @@ __global__ __launch_bounds__(NT) void linear_backward_kernel(
                 m1 += dx[u];
                 m2 += dx[u] * xb[u];
             }
-            m1 = group_sum<RW>(m1) * inv_d;
-            m2 = group_sum<RW>(m2) * inv_d;
+            m1 = tile::row16_sum(m1) * inv_d;
+            m2 = tile::row16_sum(m2) * inv_d;
 #pragma unroll
             for (int u = 0; u < NF; ++u) sm.dZb[r * DP + q + RW * u] = (dx[u] - m1 - xb[u] * m2) * rs;
         }
         __syncthreads();
 
-        // dXQ = dO + dZb W^T;  dE = T^T dZb + XK dW' + db';  dXK = E dW'^T;
-        // dA = (dZb E^T) on the causal triangle (dW', db' not yet updated)
-        float gq[NF], gk[NF], de[NF];
-#pragma unroll
-        for (int u = 0; u < NF; ++u) {
-            gq[u] = go[u];
-            gk[u] = 0.f;
-            de[u] = sm.db[q + RW * u];
+        // dE = T^T dZb + XK dW' + db';  dXQ tile = dZb W^T;  dXK tile = E dW'^T;
+        // dA = (dZb E^T) on the causal triangle  (dW', db' not yet updated)
+        f32x4 gq = fz, gk = fz;
+        if (mw) {
+            f32x4 de = mma<D>(rowm(sm.XK, DP), rowm(sm.dW + 16 * w, DP), g, c, brow(sm.db));
+            de = mma<RW>(colm(sm.T, TP), rowm(sm.dZb + 16 * w, DP), g, c, de);
+            put(sm.dE, de);
+            gq = mma<D>(rowm(sm.dZb, DP), colm(sm.W + 16 * w * DP, DP), g, c, fz);
+            gk = mma<D>(rowm(sm.E, DP), colm(sm.dW + 16 * w * DP, DP), g, c, fz);
         }
-        for (int j = 0; j < D; ++j) {
-            const float dzb = sm.dZb[r * DP + j], e = sm.E[r * DP + j], x = sm.XK[r * DP + j];
+        if (w == NT / 64 - 1) {
+            const f32x4 a4 = mma<D>(rowm(sm.dZb, DP), colm(sm.E, DP), g, c, fz);
 #pragma unroll
-            for (int u = 0; u < NF; ++u) {
-                const int f = q + RW * u;
-                gq[u] = fmaf(dzb, sm.W[f * DP + j], gq[u]);
-                gk[u] = fmaf(e, sm.dW[f * DP + j], gk[u]);
-                de[u] = fmaf(x, sm.dW[j * DP + f], de[u]);
+            for (int i = 0; i < 4; ++i) {
+                const int t = 4 * g + i;
+                sm.dA[t * TP + c] = (c <= t && t < m) ? a4[i] : 0.f;
             }
-        }
-        for (int t = 0; t < RW; ++t) {
-            const float tv = sm.T[t * TP + r];
-#pragma unroll
-            for (int u = 0; u < NF; ++u) de[u] = fmaf(tv, sm.dZb[t * DP + q + RW * u], de[u]);
-        }
-        {
-            const int t = tid / RW, s2 = tid % RW;
-            float acc = 0.f;
-            for (int k = 0; k < D; ++k) acc = fmaf(sm.dZb[t * DP + k], sm.E[s2 * DP + k], acc);
-            sm.dA[t * TP + s2] = (s2 <= t && t < m) ? acc : 0.f;
         }
         __syncthreads();
 
-        // dXQ += dA XK;  dXK += dA^T XQ
-        for (int s2 = 0; s2 < RW; ++s2) {
-            const float a1 = sm.dA[r * TP + s2], a2 = sm.dA[s2 * TP + r];
-#pragma unroll
-            for (int u = 0; u < NF; ++u) {
-                gq[u] = fmaf(a1, sm.XK[s2 * DP + q + RW * u], gq[u]);
-                gk[u] = fmaf(a2, sm.XQ[s2 * DP + q + RW * u], gk[u]);
-            }
+        // dXQ tile += dA XK;  dXK tile += dA^T XQ
+        if (mw) {
+            gq = mma<RW>(rowm(sm.dA, TP), rowm(sm.XK + 16 * w, DP), g, c, gq);
+            gk = mma<RW>(colm(sm.dA, TP), rowm(sm.XQ + 16 * w, DP), g, c, gk);
         }
-        // E = -eta G:  deta = -G . dE,  dG = -eta dE;  then the reverse of lnl2
+        // row work: deta = -G . dE, dG = -eta dE, then the reverse of lnl2
+        float de[NF];
+        rowz(sm.dE, de);
         float pe = 0.f;
 #pragma unroll
         for (int u = 0; u < NF; ++u) pe = fmaf(s.G[u], de[u], pe);
-        const float d_eta = -group_sum<RW>(pe);
+        const float d_eta = -tile::row16_sum(pe);
         float dG[NF], mdg = 0.f, mdgx = 0.f, sgG = 0.f;
 #pragma unroll
         for (int u = 0; u < NF; ++u) {
@@ -298,56 +375,51 @@ __global__ __launch_bounds__(NT) void linear_backward_kernel(
             mdgx += dG[u] * s.xh[u];
             sgG += dG[u] * s.G[u];
         }
-        mdg = group_sum<RW>(mdg) * inv_d;
-        mdgx = group_sum<RW>(mdgx) * inv_d;
+        mdg = tile::row16_sum(mdg) * inv_d;
+        mdgx = tile::row16_sum(mdgx) * inv_d;
         const float rs = 1.0f / s.sigma;
-        const float dsig = -group_sum<RW>(sgG) * rs;
-        float dxh[NF], mdx = 0.f, mdxx = 0.f, dtau[NF];
+        const float dsig = -tile::row16_sum(sgG) * rs;
+        float dxh[NF], mdx = 0.f, mdxx = 0.f;
 #pragma unroll
         for (int u = 0; u < NF; ++u) {
             const float dgh = (dG[u] - mdg - s.xh[u] * mdgx) * rs;
             dxh[u] = gm[u] * gm[u] * dgh - (s.c * dG[u] + s.gh[u] * mdgx) * rs;
-            dtau[u] = -gm[u] * dgh;
+            const float dtau = -gm[u] * dgh;
+            sm.dT[r * DP + q + RW * u] = ok ? dtau : 0.f;
             dg_acc[u] = fmaf(dgh, fmaf(2.f * gm[u], s.xh[u], bt[u] - tau[u]), dg_acc[u]);
             db_acc[u] = fmaf(gm[u], dgh, db_acc[u]);
             mdx += dxh[u];
             mdxx += dxh[u] * s.xh[u];
         }
-        mdx = group_sum<RW>(mdx) * inv_d;
-        mdxx = group_sum<RW>(mdxx) * inv_d;
+        mdx = tile::row16_sum(mdx) * inv_d;
+        mdxx = tile::row16_sum(mdxx) * inv_d;
 #pragma unroll
         for (int u = 0; u < NF; ++u) {
             const float dz = fmaf(dsig * inv_d, s.xh[u], (dxh[u] - mdx - s.xh[u] * mdxx) * rs);
             sm.dZ[r * DP + q + RW * u] = ok ? dz : 0.f;
-            gk[u] -= dtau[u];
+        }
+        if (ok) {
+            if (q == 0) deta[static_cast<size_t>(seq) * L + ch * mb + r] = d_eta;
         }
         __syncthreads();
 
-        // dXK += dZ W^T; write the chunk's input gradients
-        for (int j = 0; j < D; ++j) {
-            const float dz = sm.dZ[r * DP + j];
+        // dXK tile += dZ W^T - dtau;  dXQ tile += dO;  write the tiles
+        if (mw) {
+            gk = mma<D>(rowm(sm.dZ, DP), colm(sm.W + 16 * w * DP, DP), g, c, gk);
+            const f32x4 dt4 = get(sm.dT), do4 = get(sm.dO);
 #pragma unroll
-            for (int u = 0; u < NF; ++u) gk[u] = fmaf(dz, sm.W[(q + RW * u) * DP + j], gk[u]);
-        }
-        if (ok) {
-#pragma unroll
-            for (int u = 0; u < NF; ++u) {
-                const int f = q + RW * u;
-                dXQ[row + f] = gq[u];
-                dXK[row + f] = gk[u];
-                dXV[row + f] = dtau[u];
+            for (int i = 0; i < 4; ++i) {
+                const int t = 4 * g + i;
+                if (t < m) {
+                    const size_t at = xbase + static_cast<size_t>(ch * mb + t) * D + 16 * w + c;
+                    dXQ[at] = gq[i] + do4[i];
+                    dXK[at] = gk[i] - dt4[i];
+                    dXV[at] = dt4[i];
+                }
             }
-            if (q == 0) deta[static_cast<size_t>(seq) * L + c * mb + r] = d_eta;
         }
         // dW += XQ^T dZb + XK^T dZ;  db += 1^T (dZb + dZ)
-        for (int i = tid; i < D * D; i += NT) {
-            const int a = i / D, bcol = i % D;
-            float acc = sm.dW[a * DP + bcol];
-            for (int s2 = 0; s2 < m; ++s2)
-                acc = fmaf(sm.XQ[s2 * DP + a], sm.dZb[s2 * DP + bcol],
-                           fmaf(sm.XK[s2 * DP + a], sm.dZ[s2 * DP + bcol], acc));
-            sm.dW[a * DP + bcol] = acc;
-        }
+        state_update(sm.dW, sm.XQ, sm.dZb, sm.XK, sm.dZ);
         if (tid < D) {
             float acc = sm.db[tid];
             for (int s2 = 0; s2 < m; ++s2) acc += sm.dZb[s2 * DP + tid] + sm.dZ[s2 * DP + tid];
