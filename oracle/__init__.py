@@ -172,3 +172,27 @@ def decode_step(xq, xk, xv, eta, W, b, gamma, beta, eps: float, nthreads: Option
                                W, b, gamma, beta, eps, mb=1, w0_batched=True,
                                nthreads=nthreads)
     return O.reshape(B, H, d), Wn, bn
+
+
+def eta_gate(XK, theta_lr, eta_base: float) -> np.ndarray:
+    """Per-token learning rate of the lryc.cn article §2.2: eta = eta_base
+    times the logistic sigmoid of theta_lr . x, per token and per head.
+
+    The article leaves the gate input x open; this oracle takes x := that
+    head's key XK_t. XK [B,H,L,d]; theta_lr [H,d]. Returns eta [B,H,L] in
+    float64 (exp overflow for a very negative theta . x gives eta = 0)."""
+    XK, th = _f64(XK), _f64(theta_lr)
+    B, H, L, d = XK.shape
+    eta = np.empty((B, H, L))
+    with np.errstate(over="ignore"):
+        for h in range(H):
+            s = XK[:, h] @ th[h]                       # theta_lr . x per token
+            eta[:, h] = float(eta_base) / (1.0 + np.exp(-s))
+    return eta
+
+
+def linear_forward_gated(XQ, XK, XV, theta_lr, eta_base: float, W0, b0, gamma, beta,
+                         eps: float, mb: int = 16, **kw):
+    """TTT-Linear with eta from the gate (eta_gate), then linear_forward."""
+    return linear_forward(XQ, XK, XV, eta_gate(XK, theta_lr, eta_base), W0, b0, gamma,
+                          beta, eps, mb=mb, **kw)

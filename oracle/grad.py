@@ -101,3 +101,54 @@ def linear_backward(XQ, XK, XV, eta, W0, b0, gamma, beta, eps: float, mb: int, d
     out["W"] = W.detach().numpy()
     out["b"] = b.detach().numpy()
     return out
+
+
+def eta_gate_t(XK: torch.Tensor, theta: torch.Tensor, eta_base: float) -> torch.Tensor:
+    """eta = eta_base * logistic(theta . x) per token with x := the head's key
+    (the lryc.cn article §2.2 gate). XK [B,H,L,d]; theta [B,H,d] or [H,d]."""
+    th = theta if theta.dim() == 3 else theta[None]
+    s = (XK * th[:, :, None, :]).sum(-1)
+    return eta_base / (1.0 + torch.exp(-s))
+
+
+def eta_gate_backward(XK, theta_lr, eta_base: float, deta) -> dict:
+    """Gradients of <deta, eta_gate(XK, theta_lr)>: dXK [B,H,L,d] (the gate's
+    share only) and dtheta per sequence [B,H,d] (sum over B for the per-head
+    parameter)."""
+    B, H, L, d = np.shape(XK)
+    xk = _t(XK, True)
+    th = _t(np.broadcast_to(theta_lr, (B, H, d)), True)
+    loss = (eta_gate_t(xk, th, eta_base) * _t(deta)).sum()
+    gx, gt = torch.autograd.grad(loss, (xk, th), allow_unused=True)
+    zero = lambda t: np.zeros(t.shape)
+    return {"dXK": zero(xk) if gx is None else gx.detach().numpy(),
+            "dtheta": zero(th) if gt is None else gt.detach().numpy()}
+
+
+def linear_backward_gated(XQ, XK, XV, theta_lr, eta_base: float, W0, b0, gamma, beta,
+                          eps: float, mb: int, dO, dW_out: Optional[np.ndarray] = None,
+                          db_out: Optional[np.ndarray] = None) -> dict:
+    """Gradients of <dO, O> + <dW_out, W_L> + <db_out, b_L> when eta comes from
+    the gate: dXK includes the path through eta, and dtheta ([H,d], summed
+    over the batch) replaces deta. Also returns O, W, b and the gated eta."""
+    B, H, L, d = np.shape(XQ)
+    W0 = np.broadcast_to(W0, (B, H, d, d))
+    b0 = np.broadcast_to(b0, (B, H, d))
+    names = ("XQ", "XK", "XV", "theta", "W0", "b0", "gamma", "beta")
+    ts = [_t(a, True) for a in (XQ, XK, XV, theta_lr, W0, b0, gamma, beta)]
+    eta = eta_gate_t(ts[1], ts[3], eta_base)
+    O, W, b = linear_primal(ts[0], ts[1], ts[2], eta, *ts[4:], eps, mb)
+    loss = (O * _t(dO)).sum()
+    if dW_out is not None:
+        loss = loss + (W * _t(dW_out)).sum()
+    if db_out is not None:
+        loss = loss + (b * _t(db_out)).sum()
+    grads = torch.autograd.grad(loss, ts, allow_unused=True)
+    out = {}
+    for n, t, gr in zip(names, ts, grads):
+        out["d" + n] = np.zeros(t.shape) if gr is None else gr.detach().numpy()
+    out["O"] = O.detach().numpy()
+    out["W"] = W.detach().numpy()
+    out["b"] = b.detach().numpy()
+    out["eta"] = eta.detach().numpy()
+    return out

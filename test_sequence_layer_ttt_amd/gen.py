@@ -8,7 +8,11 @@ Sources for the shapes and distributions:
   * fast-weight init W ~ N(0, 0.02^2), b = 0, per head  -- damodev.csdn.net,
     "TTT-LM" deep-dive, section 4.3 (TTTLinear initialisation excerpt).
   * per-token learning rate eta(x) = eta_base * sigmoid(theta_lr . x)  --
-    lryc.cn article, section 2.2 (dynamic learning-rate formula).
+    lryc.cn article, section 2.2 (dynamic learning-rate formula). Where a
+    workload gates eta, only theta_lr and eta_base are drawn here; the
+    oracle and the kernels evaluate the gate. Elsewhere eta itself is drawn
+    from the distribution the gate gives for a standard-normal
+    pre-activation: (1/d) times a logit-normal variate.
   * mini-batch size b = 16  -- lryc.cn article, section 2.4.
   * TTT-MLP hidden width 4d with GELU  -- lryc.cn article, section 2.1.
 
@@ -72,8 +76,9 @@ def _normal_f32(rng: np.random.Generator, shape, scale: float = 1.0,
     return out.reshape(shape)
 
 
-def _sigmoid64(x: np.ndarray) -> np.ndarray:
-    return 1.0 / (1.0 + np.exp(-x))
+def _logit_normal64(z: np.ndarray) -> np.ndarray:
+    """Map standard-normal draws z to logit-normal variates in (0, 1)."""
+    return 1.0 / (1.0 + np.exp(-z))
 
 
 # ----------------------------------------------------------------------------
@@ -89,13 +94,15 @@ class LinearInputs:
     XQ: np.ndarray               # [B,H,L,d] float32 (exact device values)
     XK: np.ndarray
     XV: np.ndarray
-    eta: np.ndarray              # [B,H,L] float32
+    eta: Optional[np.ndarray]    # [B,H,L] float32; None when the gate below gives it
     W0: np.ndarray               # [H,d,d] float32 (broadcast over B)
     b0: np.ndarray               # [H,d]   float32
     gamma: np.ndarray            # [H,d]   float32
     beta: np.ndarray             # [H,d]   float32
     eps: float = LN_EPS
     mb: int = MINI_BATCH
+    theta_lr: Optional[np.ndarray] = None  # [H,d] float32 gate weights (gated inputs)
+    eta_base: float = 0.0                  # gate scale (gated inputs)
 
 
 @dataclass
@@ -149,7 +156,7 @@ def _rms_normalise(x32: np.ndarray) -> np.ndarray:
 
 def _eta_from_logits(rng, shape, d) -> np.ndarray:
     logits = rng.standard_normal(int(np.prod(shape))).reshape(shape)
-    return ((1.0 / d) * _sigmoid64(logits)).astype(np.float32)
+    return ((1.0 / d) * _logit_normal64(logits)).astype(np.float32)
 
 
 def make_linear(seed: int, B: int, H: int, L: int, d: int, io: str = "bf16",
@@ -158,9 +165,9 @@ def make_linear(seed: int, B: int, H: int, L: int, d: int, io: str = "bf16",
                 b_random: bool = False) -> LinearInputs:
     """TTT-Linear inputs.
 
-    gate="logits": eta = (1/d) * sigmoid(z), z ~ N(0,1) per token.
-    gate="theta":  eta = (1/d) * sigmoid(theta_lr[h] . XK[n,h,t]), theta_lr
-                   ~ N(0, 0.02^2) of shape [H,d] (gate input x := XK).
+    gate="logits": eta = (1/d) * logit-normal draw per token.
+    gate="theta":  eta is left to the gate: theta_lr ~ N(0, 0.02^2) of shape
+                   [H,d] and eta_base = 1/d are drawn/set here, eta = None.
     ln_random:     gamma ~ 1 + N(0,0.1^2), beta ~ N(0,0.1^2) (drawn last).
     b_random:      b0 ~ N(0, 0.02^2) instead of zeros (drawn last).
     """
@@ -175,9 +182,8 @@ def make_linear(seed: int, B: int, H: int, L: int, d: int, io: str = "bf16",
     if gate == "logits":
         eta = _eta_from_logits(rng, (B, H, L), d)
     elif gate == "theta":
-        theta = rng.standard_normal(H * d).reshape(H, d) * 0.02
-        s = np.einsum("bhld,hd->bhl", XK.astype(np.float64), theta)
-        eta = ((1.0 / d) * _sigmoid64(s)).astype(np.float32)
+        theta = (rng.standard_normal(H * d).reshape(H, d) * 0.02).astype(np.float32)
+        eta = None
     else:
         raise ValueError(gate)
     W0 = (rng.standard_normal(H * d * d) * w_std).reshape(H, d, d).astype(np.float32)
@@ -189,7 +195,10 @@ def make_linear(seed: int, B: int, H: int, L: int, d: int, io: str = "bf16",
         beta = (0.1 * rng.standard_normal(H * d)).reshape(H, d).astype(np.float32)
     if b_random:
         b0 = (w_std * rng.standard_normal(H * d)).reshape(H, d).astype(np.float32)
-    return LinearInputs(B, H, L, d, io, XQ, XK, XV, eta, W0, b0, gamma, beta)
+    x = LinearInputs(B, H, L, d, io, XQ, XK, XV, eta, W0, b0, gamma, beta)
+    if gate == "theta":
+        x.theta_lr, x.eta_base = theta, 1.0 / d
+    return x
 
 
 def make_mlp(seed: int, B: int, H: int, L: int, d: int, io: str = "bf16",

@@ -69,8 +69,8 @@ def test_rms_normalised_inputs():
     assert np.allclose(r, 1.0, atol=1e-2)
 
 
-def test_eta_gate_range():
-    for num in (1, 2, 3):
+def test_eta_range():
+    for num in (2, 3):
         x = gen.make_workload(num, L=32, B=1, H=1)
         assert np.all(x.eta > 0) and np.all(x.eta < 1.0 / x.d)
 
