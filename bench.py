@@ -15,6 +15,10 @@ Other workloads of the same hot path (--workload):
       resident in registers (roofline: fp32 vector ALU)
   3b  TTT-Linear backward (ttt_linear_backward) on workload 3's shapes
       (roofline: fp32 vector ALU)
+  3g  workload 3 through ttt_linear_forward_gated: eta from the learning-rate
+      gate evaluated in the kernel (theta_lr ~ N(0, 0.02^2), eta_base = 1/d)
+  3gb ttt_eta_gate_backward on workload 3's keys (dXK += the path through
+      eta, dtheta per sequence; roofline: HBM)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
                        [--no-cpu-baseline]
@@ -113,7 +117,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="3", choices=["3", "2", "5p", "4", "5d", "5r", "3b"])
+    ap.add_argument("--workload", default="3", choices=["3", "2", "5p", "4", "5d", "5r", "3b", "3g", "3gb"])
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -148,7 +152,10 @@ def main():
         return bench_decode_steps(args)
     if args.workload == "3b":
         return bench_backward(args)
-    wl = {"3": 3, "2": 2, "5p": 5}[args.workload]
+    if args.workload == "3gb":
+        return bench_gate_backward(args)
+    wl = {"3": 3, "3g": 3, "2": 2, "5p": 5}[args.workload]
+    gated = args.workload == "3g"
     w = gen.WORKLOADS[wl]
     x = gen.make_workload(wl, decode_steps=0) if wl == 5 else gen.make_workload(wl)
     if wl == 5:
@@ -164,10 +171,17 @@ def main():
     Wo = torch.empty((B, H, d, d), device=dev)
     bo = torch.empty((B, H, d), device=dev)
     stream = torch.cuda.current_stream()
+    if gated:  # gate weights drawn on a stream of their own (seed 3 + 1000)
+        theta_np = (0.02 * np.random.default_rng(1003).standard_normal((H, d))).astype(np.float32)
+        theta, eta_base = T(theta_np), 1.0 / d
 
     def step():
-        ttt.ttt_linear_forward(XQ, XK, XV, eta, W0, b0, gam, bet, O=O, W_out=Wo, b_out=bo,
-                               mb=16, ln_eps=x.eps, stream=stream)
+        if gated:
+            ttt.ttt_linear_forward_gated(XQ, XK, XV, theta, eta_base, W0, b0, gam, bet, O=O,
+                                         W_out=Wo, b_out=bo, mb=16, ln_eps=x.eps, stream=stream)
+        else:
+            ttt.ttt_linear_forward(XQ, XK, XV, eta, W0, b0, gam, bet, O=O, W_out=Wo, b_out=bo,
+                                   mb=16, ln_eps=x.eps, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -190,10 +204,13 @@ def main():
     value = tokens / (wall / K)
 
     ab = alg_bytes_linear(B, H, L, d)
+    if gated:  # no eta array read; theta_lr [H,d] read once per sequence
+        ab += B * H * (d * 4 - L * 4)
     achieved = ab / kern_avg_s / 1e9
-    traffic = measured_traffic(ab) if wl == WORKLOAD else None
+    traffic = measured_traffic(ab) if (wl == WORKLOAD and not gated) else None
     out = {
-        "metric": METRIC if wl == WORKLOAD else f"TTT-Linear prefill tokens/s (L={L})",
+        "metric": (METRIC if wl == WORKLOAD and not gated else
+                   f"TTT-Linear prefill tokens/s (L={L}{', gated eta' if gated else ''})"),
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -205,7 +222,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "B": B, "H": H, "L": L, "d": d, "mini_batch": 16,
+        "config": {"workload": w.name + ("+eta_gate" if gated else ""), "B": B, "H": H, "L": L, "d": d, "mini_batch": 16,
                    "io": "bf16", "state": "fp32", "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
@@ -219,6 +236,8 @@ def main():
         xs = {k: np.ascontiguousarray(getattr(x, k), np.float64)
               for k in ("XQ", "XK", "XV", "eta", "W0", "b0", "gamma", "beta")}
         t1 = time.perf_counter()
+        if gated:
+            xs["eta"] = oracle.eta_gate(xs["XK"], theta_np, eta_base)
         ro, rW, rb = oracle.linear_forward(xs["XQ"], xs["XK"], xs["XV"], xs["eta"], xs["W0"],
                                            xs["b0"], xs["gamma"], xs["beta"], x.eps, mb=16,
                                            nthreads=nt)
@@ -460,6 +479,52 @@ def bench_backward(args):
           {"workload": "ttt_linear_backward_bf16_B2_H32_L8192_d64", "B": B, "H": H, "L": L,
            "d": d, "mini_batch": 16, "io": "bf16", "grads": "fp32", "parallelism": "none (1 GPU)"},
           roof, extra)
+
+
+
+def bench_gate_backward(args):
+    """ttt_eta_gate_backward on workload 3's keys (B=2, H=32, L=8192, d=64,
+    bf16): a seeded deta, theta_lr ~ N(0, 0.02^2), eta_base = 1/d. Algorithmic
+    bytes per call: XK and deta read once, dXK read and written, per token-head."""
+    import numpy as np
+    import torch
+    from test_sequence_layer_ttt_amd import gen, ttt
+    x = gen.make_workload(3)
+    B, H, L, d = x.B, x.H, x.L, x.d
+    dev = torch.device("cuda:0")
+    XK = torch.from_numpy(x.XK).to(dev).to(torch.bfloat16)
+    rng = np.random.default_rng(1003)
+    theta_np = (0.02 * rng.standard_normal((H, d))).astype(np.float32)
+    deta_np = rng.standard_normal((B, H, L)).astype(np.float32)
+    th, deta = torch.from_numpy(theta_np).to(dev), torch.from_numpy(deta_np).to(dev)
+    dXK = torch.zeros((B, H, L, d), device=dev)
+    dth = torch.empty((B, H, d), device=dev)
+    stream = torch.cuda.current_stream()
+    eta = torch.empty((B, H, L), device=dev)
+    fwd = lambda: ttt.ttt_eta_gate(XK, th, 1.0 / d, eta=eta, stream=stream)
+    _, kern_f = _timed(fwd, stream, args.warmup, args.steps)  # the forward gate, for reference
+    fb = B * H * L * (d * 2 + 4) + H * d * 4
+    step = lambda: ttt.ttt_eta_gate_backward(XK, th, 1.0 / d, deta, dXK, dtheta=dth, stream=stream)
+    wall, kern = _timed(step, stream, args.warmup, args.steps)
+    ab = B * H * L * (d * 2 + 4 + 2 * d * 4) + H * d * 4 + B * H * d * 4
+    roof = {"bound": "hbm", "achieved": ab / kern / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": ab / kern / 1e9 / HBM_PEAK_GBS, "traffic": None,
+            "kernel": "eta_gate_bwd_dx + eta_gate_bwd_dtheta (one call)",
+            "kernel_avg_us": kern * 1e6, "alg_bytes_per_launch": ab}
+    extra = {"eta_gate_fwd": {"kernel_avg_us": kern_f * 1e6, "alg_bytes_per_launch": fb,
+                              "achieved_GBps": fb / kern_f / 1e9}}
+    if not args.no_cpu_baseline:
+        from oracle import grad as OG
+        t1 = time.perf_counter()
+        OG.eta_gate_backward(x.XK, theta_np, 1.0 / d, deta_np)
+        tc = time.perf_counter() - t1
+        extra["cpu_baseline"] = {"value": B * L / tc, "unit": "tokens/s",
+                                 "cores": torch.get_num_threads(), "kind": "oracle",
+                                 "sample": f"autograd of the fp64 gate over the whole workload, "
+                                           f"{tc:.2f} s"}
+    _line("learning-rate gate backward tokens/s (L=8192)", B * L / wall, args, wall, "bf16 in, fp32",
+          {"workload": "ttt_eta_gate_backward_bf16_B2_H32_L8192_d64", "B": B, "H": H, "L": L,
+           "d": d, "io": "bf16", "grads": "fp32", "parallelism": "none (1 GPU)"}, roof, extra)
 
 
 if __name__ == "__main__":

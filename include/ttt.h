@@ -95,6 +95,48 @@ int ttt_linear_forward(int B, int H, int L, int d, int mb, int io, float ln_eps,
                        float *W_out, float *b_out, hipStream_t stream);
 
 /*
+ * ttt_linear_forward with each token's rate taken from the learning-rate gate
+ * of [Y] §2.2 inside the kernel (no eta array is read):
+ *   eta_t = eta_base * logistic(theta_lr[h] . XK_t),  logistic(s) = 1/(1+e^-s).
+ * The gate input x is read as the head's key XK_t ([Y] leaves x open).
+ *   theta_lr : [H,d] fp32, 16-byte aligned.  eta_base : finite, else TTT_E_SHAPE.
+ * Every other argument, and the numerics, as ttt_linear_forward; the gate
+ * itself is evaluated in fp32 (dot product, exp, divide).
+ */
+int ttt_linear_forward_gated(int B, int H, int L, int d, int mb, int io, float ln_eps,
+                             const void *XQ, const void *XK, const void *XV,
+                             const float *theta_lr, float eta_base, const float *W0,
+                             const float *b0, int w0_batched, const float *ln_gamma,
+                             const float *ln_beta, void *O, float *W_out, float *b_out,
+                             hipStream_t stream);
+
+/*
+ * The learning-rate gate of [Y] §2.2 on its own, for the paths that take eta
+ * as an array (MLP prefill, decode, the backward):
+ *   eta[n,h,t] = eta_base * logistic(theta_lr[h] . XK[n,h,t]).
+ *   B, H, L >= 0; d in {16, 32, 64}; io as above.
+ *   XK [B,H,L,d] io, 16-byte aligned; theta_lr [H,d] fp32; eta [B,H,L] fp32,
+ *   written, must not overlap XK or theta_lr. eta_base finite. fp32 throughout.
+ */
+int ttt_eta_gate(int B, int H, int L, int d, int io, const void *XK, const float *theta_lr,
+                 float eta_base, float *eta, hipStream_t stream);
+
+/*
+ * Backward of ttt_eta_gate: with deta = dLoss/deta (e.g. ttt_linear_backward's
+ * deta) and logistic'(s) = logistic(s) (1 - logistic(s)), s = theta_lr[h] . XK_t:
+ *   dXK[n,h,t,:] += deta * eta_base * logistic'(s) * theta_lr[h]   (in place)
+ *   dtheta[n,h,:] = sum_t deta * eta_base * logistic'(s) * XK[n,h,t,:]
+ * dXK [B,H,L,d] fp32 (16-byte aligned) is read and updated, so passing the
+ * inner-loop backward's dXK yields the key's total gradient. dtheta
+ * [B,H,d] fp32 is written per sequence (the parameter's gradient is its sum
+ * over n); its sum over t runs in a fixed order, so repeated calls give the
+ * same bits. Other arguments as ttt_eta_gate; no output may overlap an input.
+ */
+int ttt_eta_gate_backward(int B, int H, int L, int d, int io, const void *XK,
+                          const float *theta_lr, float eta_base, const float *deta, float *dXK,
+                          float *dtheta, hipStream_t stream);
+
+/*
  * TTT-MLP prefill ([Y] §2.1: f_res(x) = GELU(x W1 + b1) W2 + b2, hidden m = 4d,
  * exact GELU x * Phi(x)), mini-batch form as above.
  *   d = 64 (m = 256); 1 <= mb <= 16.

@@ -44,6 +44,10 @@ def load():
                           "python test_sequence_layer_ttt_amd/build.py")
     lib = ctypes.CDLL(LIB_PATH)
     lib.ttt_linear_forward.argtypes = [_i] * 6 + [_f] + [_P] * 6 + [_i] + [_P] * 5 + [_P]
+    lib.ttt_linear_forward_gated.argtypes = ([_i] * 6 + [_f] + [_P] * 4 + [_f] + [_P] * 2 + [_i]
+                                            + [_P] * 5 + [_P])
+    lib.ttt_eta_gate.argtypes = [_i] * 5 + [_P, _P, _f, _P, _P]
+    lib.ttt_eta_gate_backward.argtypes = [_i] * 5 + [_P, _P, _f, _P, _P, _P, _P]
     lib.ttt_mlp_forward.argtypes = [_i] * 6 + [_f] + [_P] * 8 + [_i] + [_P] * 7 + [_P]
     lib.ttt_decode_step.argtypes = [_i] * 4 + [_f] + [_P] * 9 + [_P]
     lib.ttt_decode_steps.argtypes = [_i] * 5 + [_f] + [_P] * 9 + [_P]
@@ -53,6 +57,7 @@ def load():
     lib.ttt_ln_l2_bwd.argtypes = [_i, _i, _P, _P, _P, _P, _f, _P, _P]
     for name in ("ttt_linear_forward", "ttt_mlp_forward", "ttt_decode_step", "ttt_decode_steps",
                  "ttt_linear_backward", "ttt_linear_backward_workspace", "ttt_ln_l2_bwd",
+                 "ttt_linear_forward_gated", "ttt_eta_gate", "ttt_eta_gate_backward",
                  "ttt_version"):
         getattr(lib, name).restype = _i
     lib.ttt_last_error.restype = ctypes.c_char_p

@@ -132,14 +132,21 @@ int ttt_ln_l2_bwd(int rows, int d, const float *Z, const float *target, const fl
     return launched(ttt::launch_ln_l2_bwd(rows, d, Z, target, ln_gamma, ln_beta, ln_eps, G, stream));
 }
 
-int ttt_linear_forward(int B, int H, int L, int d, int mb, int io, float ln_eps,
-                       const void *XQ, const void *XK, const void *XV, const float *eta,
-                       const float *W0, const float *b0, int w0_batched,
-                       const float *ln_gamma, const float *ln_beta, void *O,
-                       float *W_out, float *b_out, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// TTT-Linear prefill with eta given (theta == nullptr) or from the gate.
+int linear_forward(int B, int H, int L, int d, int mb, int io, float ln_eps, const void *XQ,
+                   const void *XK, const void *XV, const float *eta, const float *theta,
+                   float eta_base, const float *W0, const float *b0, int w0_batched,
+                   const float *ln_gamma, const float *ln_beta, void *O, float *W_out,
+                   float *b_out, hipStream_t stream, bool gated) {
     int st;
     if ((st = check_common(B, H, L, mb, io)) || (st = check_eps(ln_eps))) return st;
     if (d != 16 && d != 64) return fail(TTT_E_SHAPE, "d = %d not in {16, 64}", d);
+    if (gated && !std::isfinite(eta_base))
+        return fail(TTT_E_SHAPE, "eta_base = %g is not finite", static_cast<double>(eta_base));
     const size_t es = io == TTT_BF16 ? 2 : 4;
     const size_t nb = w0_batched ? static_cast<size_t>(B) : 1;
     size_t xb, eb, wb, bb, ob_w, ob_b;
@@ -152,7 +159,8 @@ int ttt_linear_forward(int B, int H, int L, int d, int mb, int io, float ln_eps,
         return fail(TTT_E_SHAPE, "sizes overflow");
     const size_t pb = static_cast<size_t>(H) * d * sizeof(float);
     const Buf in[] = {{XQ, xb, "XQ", false, 16}, {XK, xb, "XK", false, 16},
-                      {XV, xb, "XV", false, 16}, {eta, eb, "eta", false, 4},
+                      {XV, xb, "XV", false, 16},
+                      gated ? Buf{theta, pb, "theta_lr", false, 16} : Buf{eta, eb, "eta", false, 4},
                       {W0, wb, "W0", false, 16}, {b0, bb, "b0", false, 16},
                       {ln_gamma, pb, "ln_gamma", false, 4}, {ln_beta, pb, "ln_beta", false, 4}};
     const Buf out[] = {{O, xb, "O", false, 16}, {W_out, ob_w, "W_out", true, 16},
@@ -163,10 +171,83 @@ int ttt_linear_forward(int B, int H, int L, int d, int mb, int io, float ln_eps,
     if ((st = check_alias(out, 3, in, 8, pair))) return st;
     if (B * H == 0) return ok();
 
-    ttt::LinearArgs a{B, H, L, d, mb, io, ln_eps, XQ, XK, XV, eta, W0, b0, w0_batched ? 1 : 0,
-                      ln_gamma, ln_beta, O, W_out, b_out};
+    ttt::LinearArgs a{B, H, L, d, mb, io, ln_eps, XQ, XK, XV, gated ? nullptr : eta, W0, b0,
+                      w0_batched ? 1 : 0, ln_gamma, ln_beta, O, W_out, b_out};
+    if (gated) {
+        a.theta = theta;
+        a.eta_base = eta_base;
+    }
     if (ttt::linear_mfma_supported(a)) return launched(ttt::launch_linear_mfma(a, stream));
     return launched(ttt::launch_linear_valu(a, stream));
+}
+
+// XK, theta and eta/deta checks shared by the two gate entry points.
+int gate_common(int B, int H, int L, int d, int io, float eta_base, size_t *xb, size_t *eb,
+                size_t *pb) {
+    int st;
+    if ((st = check_common(B, H, L, 1, io))) return st;
+    if (d != 16 && d != 32 && d != 64) return fail(TTT_E_SHAPE, "d = %d not in {16, 32, 64}", d);
+    if (!std::isfinite(eta_base))
+        return fail(TTT_E_SHAPE, "eta_base = %g is not finite", static_cast<double>(eta_base));
+    const size_t es = io == TTT_BF16 ? 2 : 4;
+    if (!nbytes(xb, {size_t(B), size_t(H), size_t(L), size_t(d), es}) ||
+        !nbytes(eb, {size_t(B), size_t(H), size_t(L), sizeof(float)}))
+        return fail(TTT_E_SHAPE, "sizes overflow");
+    *pb = static_cast<size_t>(H) * d * sizeof(float);
+    return TTT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ttt_linear_forward(int B, int H, int L, int d, int mb, int io, float ln_eps,
+                       const void *XQ, const void *XK, const void *XV, const float *eta,
+                       const float *W0, const float *b0, int w0_batched,
+                       const float *ln_gamma, const float *ln_beta, void *O,
+                       float *W_out, float *b_out, hipStream_t stream) {
+    return linear_forward(B, H, L, d, mb, io, ln_eps, XQ, XK, XV, eta, nullptr, 0.f, W0, b0,
+                          w0_batched, ln_gamma, ln_beta, O, W_out, b_out, stream, false);
+}
+
+int ttt_linear_forward_gated(int B, int H, int L, int d, int mb, int io, float ln_eps,
+                             const void *XQ, const void *XK, const void *XV,
+                             const float *theta_lr, float eta_base, const float *W0,
+                             const float *b0, int w0_batched, const float *ln_gamma,
+                             const float *ln_beta, void *O, float *W_out, float *b_out,
+                             hipStream_t stream) {
+    return linear_forward(B, H, L, d, mb, io, ln_eps, XQ, XK, XV, nullptr, theta_lr, eta_base,
+                          W0, b0, w0_batched, ln_gamma, ln_beta, O, W_out, b_out, stream, true);
+}
+
+int ttt_eta_gate(int B, int H, int L, int d, int io, const void *XK, const float *theta_lr,
+                 float eta_base, float *eta, hipStream_t stream) {
+    size_t xb, eb, pb;
+    int st;
+    if ((st = gate_common(B, H, L, d, io, eta_base, &xb, &eb, &pb))) return st;
+    const Buf in[] = {{XK, xb, "XK", false, 16}, {theta_lr, pb, "theta_lr", false, 4}};
+    const Buf out[] = {{eta, eb, "eta", false, 4}};
+    if ((st = check_bufs(in, 2)) || (st = check_bufs(out, 1))) return st;
+    if ((st = check_alias(out, 1, in, 2, nullptr))) return st;
+    return launched(ttt::launch_eta_gate(B, H, L, d, io, XK, theta_lr, eta_base, eta, stream));
+}
+
+int ttt_eta_gate_backward(int B, int H, int L, int d, int io, const void *XK,
+                          const float *theta_lr, float eta_base, const float *deta, float *dXK,
+                          float *dtheta, hipStream_t stream) {
+    size_t xb, eb, pb, gb, tb;
+    int st;
+    if ((st = gate_common(B, H, L, d, io, eta_base, &xb, &eb, &pb))) return st;
+    if (!nbytes(&gb, {size_t(B), size_t(H), size_t(L), size_t(d), sizeof(float)}) ||
+        !nbytes(&tb, {size_t(B), size_t(H), size_t(d), sizeof(float)}))
+        return fail(TTT_E_SHAPE, "sizes overflow");
+    const Buf in[] = {{XK, xb, "XK", false, 16}, {theta_lr, pb, "theta_lr", false, 4},
+                      {deta, eb, "deta", false, 4}};
+    const Buf out[] = {{dXK, gb, "dXK", false, 16}, {dtheta, tb, "dtheta", false, 4}};
+    if ((st = check_bufs(in, 3)) || (st = check_bufs(out, 2))) return st;
+    if ((st = check_alias(out, 2, in, 3, nullptr))) return st;
+    return launched(ttt::launch_eta_gate_backward(B, H, L, d, io, XK, theta_lr, eta_base, deta,
+                                                  dXK, dtheta, stream));
 }
 
 int ttt_linear_backward_workspace(int B, int H, int L, int d, int mb, size_t *bytes) {

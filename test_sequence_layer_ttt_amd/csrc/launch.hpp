@@ -16,6 +16,10 @@ struct LinearArgs {
     const float *gamma, *beta;
     void *O;
     float *W_out, *b_out;
+    // learning-rate gate: when theta is set, eta is ignored and each token's
+    // rate is eta_base * logistic(theta[h] . XK_t), evaluated in the kernel
+    const float *theta = nullptr;
+    float eta_base = 0.f;
 };
 
 struct LinearBwdArgs {
@@ -51,6 +55,12 @@ hipError_t launch_ln_l2_bwd(int rows, int d, const float *Z, const float *T, con
 hipError_t launch_linear_valu(const LinearArgs &a, hipStream_t stream);
 bool linear_mfma_supported(const LinearArgs &a);
 hipError_t launch_linear_mfma(const LinearArgs &a, hipStream_t stream);
+hipError_t launch_eta_gate(int B, int H, int L, int d, int io, const void *XK, const float *theta,
+                           float eta_base, float *eta, hipStream_t stream);
+hipError_t launch_eta_gate_backward(int B, int H, int L, int d, int io, const void *XK,
+                                    const float *theta, float eta_base, const float *deta,
+                                    float *dXK, float *dtheta, hipStream_t stream);
+
 size_t linear_backward_workspace_floats(int B, int H, int L, int d, int mb);
 hipError_t launch_linear_backward(const LinearBwdArgs &a, hipStream_t stream);
 hipError_t launch_mlp(const MLPArgs &a, hipStream_t stream);

@@ -134,9 +134,10 @@ __device__ __forceinline__ f16x8 fragh(const uint16_t *rows, int c, int g, int k
 // the next iteration (T_{j+1} in the one after) and rewritten two
 // iterations later.
 // ---------------------------------------------------------------------------
+template <bool GATED>
 __device__ __forceinline__ void prep_waves(Smem &sm, int pw, int g, int c, int lane, const bf16_t *xq,
                                            const bf16_t *xk, const bf16_t *xv, const float *et,
-                                           int L, int iters) {
+                                           const float *th, float eta_base, int L, int iters) {
     constexpr int PRE = 2, BPI = 2;
     LSlot *slots = sm.slot;
     const int r = 4 * pw + g, f0 = 4 * c;  // token, first feature
@@ -153,7 +154,17 @@ __device__ __forceinline__ void prep_waves(Smem &sm, int pw, int g, int c, int l
         R.q = *reinterpret_cast<const uint2 *>(bq + off);
         R.k = *reinterpret_cast<const uint2 *>(bk + off);
         R.v = *reinterpret_cast<const uint2 *>(bv + off);
-        R.eta = et[tok];
+        if constexpr (!GATED) R.eta = et[tok];
+    };
+    // learning-rate gate (GATED): eta = eta_base * logistic(theta . XK_t), the
+    // dot product split over the 16 lanes of the token's DPP row; exp2 and
+    // reciprocal are the hardware approximations (about 1 ulp each)
+    f32x4 thv = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (GATED) thv = *reinterpret_cast<const f32x4 *>(th + f0) * -1.4426950408889634f;
+    auto gate = [&](uint2 k) {  // thv holds -theta * log2(e)
+        const f32x4 kf = unpack4(k);
+        const float ns = row16_sum(fmaf(thv[0], kf[0], thv[1] * kf[1]) + fmaf(thv[2], kf[2], thv[3] * kf[3]));
+        return eta_base * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(ns));
     };
     auto stage_rows = [&](LSlot &S, uint2 q, uint2 k, uint2 v, float e) {
         const f32x4 qf = unpack4(q), kf = unpack4(k);
@@ -170,12 +181,17 @@ __device__ __forceinline__ void prep_waves(Smem &sm, int pw, int g, int c, int l
     };
     auto stage = [&](const PrepRegs &R, int ch, int slot) {
         LSlot &S = slots[slot];
+        float e;
+        if constexpr (GATED)
+            e = gate(R.k);  // all lanes (DPP sum)
+        else
+            e = R.eta;
         if (ch * MB + MB <= L) {  // whole chunk inside the sequence (uniform)
-            stage_rows(S, R.q, R.k, R.v, R.eta);
+            stage_rows(S, R.q, R.k, R.v, e);
         } else {
             const bool ok = ch * MB + r < L;
             const uint2 z2 = make_uint2(0u, 0u);
-            stage_rows(S, ok ? R.q : z2, ok ? R.k : z2, ok ? R.v : z2, ok ? R.eta : 0.f);
+            stage_rows(S, ok ? R.q : z2, ok ? R.k : z2, ok ? R.v : z2, ok ? e : 0.f);
         }
     };
     const f32x4 fzero = {0.f, 0.f, 0.f, 0.f}, fone = {1.f, 1.f, 1.f, 1.f};
@@ -486,8 +502,8 @@ __device__ __forceinline__ void state_waves(Smem &sm, const Ctx &cx, int u, int 
 
 __global__ __launch_bounds__(NT) void linear_prefill_mfma(
     int H, int L, float eps, const bf16_t *__restrict__ XQ, const bf16_t *__restrict__ XK,
-    const bf16_t *__restrict__ XV, const float *__restrict__ eta,
-    const float *__restrict__ W0, const float *__restrict__ b0, int w0_batched,
+    const bf16_t *__restrict__ XV, const float *__restrict__ eta, const float *__restrict__ theta,
+    float eta_base, const float *__restrict__ W0, const float *__restrict__ b0, int w0_batched,
     const float *__restrict__ gamma, const float *__restrict__ beta, bf16_t *__restrict__ O,
     float *W_out, float *b_out) {
     __shared__ Smem sm;
@@ -506,8 +522,12 @@ __global__ __launch_bounds__(NT) void linear_prefill_mfma(
     const float *gam_h = gamma + static_cast<size_t>(h) * D, *bet_h = beta + static_cast<size_t>(h) * D;
 
     if (w >= NCW + NSW) {
-        prep_waves(sm, w - NCW - NSW, g, c, lane, XQ + xbase, XK + xbase, XV + xbase,
-                   eta + static_cast<size_t>(seq) * L, L, cx.iters);
+        if (theta)
+            prep_waves<true>(sm, w - NCW - NSW, g, c, lane, XQ + xbase, XK + xbase, XV + xbase,
+                             nullptr, theta + static_cast<size_t>(h) * D, eta_base, L, cx.iters);
+        else
+            prep_waves<false>(sm, w - NCW - NSW, g, c, lane, XQ + xbase, XK + xbase, XV + xbase,
+                              eta + static_cast<size_t>(seq) * L, nullptr, 0.f, L, cx.iters);
         return;
     }
     // gamma = 1 and beta = 0 over the head (one feature per lane; same vote in every wave)
@@ -537,7 +557,8 @@ hipError_t launch_linear_mfma(const LinearArgs &a, hipStream_t stream) {
     if (a.B * a.H == 0) return hipSuccess;
     hipLaunchKernelGGL(linear_prefill_mfma, dim3(a.B * a.H), dim3(NT), 0, stream, a.H, a.L, a.eps,
                        static_cast<const bf16_t *>(a.XQ), static_cast<const bf16_t *>(a.XK),
-                       static_cast<const bf16_t *>(a.XV), a.eta, a.W0, a.b0, a.w0_batched, a.gamma,
+                       static_cast<const bf16_t *>(a.XV), a.eta, a.theta, a.eta_base, a.W0, a.b0,
+                       a.w0_batched, a.gamma,
                        a.beta, static_cast<bf16_t *>(a.O), a.W_out, a.b_out);
     return hipGetLastError();
 }

@@ -10,6 +10,8 @@
 //   Zbar = XQ W + b - M G        ;  O = XQ + LN(Zbar)
 //   W   -= (eta * XK)^T G        ;  b -= eta^T G
 // Tokens past the end of a short last chunk carry eta = 0 and G = 0.
+// With the learning-rate gate (theta set) eta_t = eta_base * logistic(theta_h .
+// XK_t) is formed from the staged keys (the lryc.cn article §2.2 gate).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -18,8 +20,9 @@ namespace ttt {
 template <int D, typename TIO>
 __global__ __launch_bounds__(256) void linear_prefill_valu(
     int H, int L, int mb, float eps, const TIO *__restrict__ XQ, const TIO *__restrict__ XK,
-    const TIO *__restrict__ XV, const float *__restrict__ eta, const float *__restrict__ W0,
-    const float *__restrict__ b0, int w0_batched, const float *__restrict__ gamma,
+    const TIO *__restrict__ XV, const float *__restrict__ eta, const float *__restrict__ theta,
+    float eta_base, const float *__restrict__ W0, const float *__restrict__ b0, int w0_batched,
+    const float *__restrict__ gamma,
     const float *__restrict__ beta, TIO *__restrict__ O, float *W_out, float *b_out) {
     constexpr int NT = 256, MB = 16, DP = D + 1;
     constexpr int R = MB * D / NT;  // outputs per thread in the row-by-column products
@@ -32,6 +35,7 @@ __global__ __launch_bounds__(256) void linear_prefill_valu(
     __shared__ float sQ[MB * DP], sK[MB * DP];
     __shared__ float sT[MB * D], sZ[MB * D], sG[MB * D];
     __shared__ float sEta[MB], sM[MB * MB];
+    __shared__ float sTh[D];
 
     const int tid = threadIdx.x;
     const long seq = blockIdx.x;
@@ -44,6 +48,7 @@ __global__ __launch_bounds__(256) void linear_prefill_valu(
 
     for (int e = tid; e < D * D; e += NT) sW[e] = W0[wofs + e];
     if (tid < D) sb[tid] = b0[bofs + tid];
+    if (theta && tid < D) sTh[tid] = theta[static_cast<size_t>(h) * D + tid];
 
     const int rrow = tid / 16, rl = tid % 16;  // 16-lane row groups
     float gam[E], bet[E];
@@ -71,10 +76,15 @@ __global__ __launch_bounds__(256) void linear_prefill_valu(
             sK[s * DP + j] = k;
             sT[s * D + j] = v - k;
         }
-        if (tid < MB) sEta[tid] = tid < len ? eta[ebase + t0 + tid] : 0.f;
+        if (!theta && tid < MB) sEta[tid] = tid < len ? eta[ebase + t0 + tid] : 0.f;
         __syncthreads();
 
-        // 2. Z = XK W + b
+        // 2. Z = XK W + b (and the gated eta, read after the next barrier)
+        if (theta && tid < MB) {
+            float s = 0.f;
+            for (int i = 0; i < D; ++i) s = fmaf(sK[tid * DP + i], sTh[i], s);
+            sEta[tid] = tid < len ? eta_base / (1.0f + __expf(-s)) : 0.f;
+        }
         {
             float acc[R];
 #pragma unroll
@@ -169,7 +179,7 @@ static hipError_t launch_valu_t(const LinearArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((linear_prefill_valu<D, TIO>), dim3(a.B * a.H), dim3(256), 0, stream, a.H,
                        a.L, a.mb, a.eps, static_cast<const TIO *>(a.XQ),
                        static_cast<const TIO *>(a.XK), static_cast<const TIO *>(a.XV), a.eta,
-                       a.W0, a.b0, a.w0_batched, a.gamma, a.beta, static_cast<TIO *>(a.O),
+                       a.theta, a.eta_base, a.W0, a.b0, a.w0_batched, a.gamma, a.beta, static_cast<TIO *>(a.O),
                        a.W_out, a.b_out);
     return hipGetLastError();
 }

@@ -76,6 +76,73 @@ def ttt_linear_forward(XQ, XK, XV, eta, W0, b0, ln_gamma, ln_beta, O=None, W_out
     return O, W_out, b_out
 
 
+def ttt_linear_forward_gated(XQ, XK, XV, theta_lr, eta_base: float, W0, b0, ln_gamma, ln_beta,
+                             O=None, W_out=None, b_out=None, mb: int = 16, ln_eps: float = 1e-6,
+                             stream=None):
+    """TTT-Linear prefill with eta_t = eta_base * logistic(theta_lr[h] . XK_t)
+    evaluated in the kernel. theta_lr [H,d] fp32; the rest as ttt_linear_forward."""
+    B, H, L, d = XQ.shape
+    io = _IO.get(XQ.dtype)
+    if io is None:
+        raise TypeError(f"XQ dtype {XQ.dtype} not supported")
+    batched = W0.dim() == 4
+    for t, n in ((XQ, "XQ"), (XK, "XK"), (XV, "XV")):
+        _need(t, n, (B, H, L, d), XQ.dtype)
+    _need(theta_lr, "theta_lr", (H, d), torch.float32)
+    _need(W0, "W0", ((B,) if batched else ()) + (H, d, d), torch.float32)
+    _need(b0, "b0", ((B,) if batched else ()) + (H, d), torch.float32)
+    _need(ln_gamma, "ln_gamma", (H, d), torch.float32)
+    _need(ln_beta, "ln_beta", (H, d), torch.float32)
+    O = torch.empty_like(XQ) if O is None else O
+    if W_out is None:
+        W_out = torch.empty((B, H, d, d), device=XQ.device, dtype=torch.float32)
+    if b_out is None:
+        b_out = torch.empty((B, H, d), device=XQ.device, dtype=torch.float32)
+    _need(O, "O", (B, H, L, d), XQ.dtype)
+    _need(W_out, "W_out", (B, H, d, d), torch.float32)
+    _need(b_out, "b_out", (B, H, d), torch.float32)
+    lib = _lib.load()
+    _lib.check(lib.ttt_linear_forward_gated(B, H, L, d, mb, io, ln_eps, _ptr(XQ), _ptr(XK),
+                                            _ptr(XV), _ptr(theta_lr), float(eta_base), _ptr(W0),
+                                            _ptr(b0), int(batched), _ptr(ln_gamma),
+                                            _ptr(ln_beta), _ptr(O), _ptr(W_out), _ptr(b_out),
+                                            _stream(stream)))
+    return O, W_out, b_out
+
+
+def ttt_eta_gate(XK, theta_lr, eta_base: float, eta=None, stream=None):
+    """eta [B,H,L] = eta_base * logistic(theta_lr[h] . XK[n,h,t])."""
+    B, H, L, d = XK.shape
+    io = _IO.get(XK.dtype)
+    if io is None:
+        raise TypeError(f"XK dtype {XK.dtype} not supported")
+    _need(theta_lr, "theta_lr", (H, d), torch.float32)
+    eta = torch.empty((B, H, L), device=XK.device, dtype=torch.float32) if eta is None else eta
+    _need(eta, "eta", (B, H, L), torch.float32)
+    lib = _lib.load()
+    _lib.check(lib.ttt_eta_gate(B, H, L, d, io, _ptr(XK), _ptr(theta_lr), float(eta_base),
+                                _ptr(eta), _stream(stream)))
+    return eta
+
+
+def ttt_eta_gate_backward(XK, theta_lr, eta_base: float, deta, dXK, dtheta=None, stream=None):
+    """Adds the gate's share to dXK [B,H,L,d] fp32 in place; returns dtheta
+    [B,H,d] per sequence (sum over B for the parameter's gradient)."""
+    B, H, L, d = XK.shape
+    io = _IO.get(XK.dtype)
+    if io is None:
+        raise TypeError(f"XK dtype {XK.dtype} not supported")
+    _need(theta_lr, "theta_lr", (H, d), torch.float32)
+    _need(deta, "deta", (B, H, L), torch.float32)
+    _need(dXK, "dXK", (B, H, L, d), torch.float32)
+    dtheta = torch.empty((B, H, d), device=XK.device, dtype=torch.float32) if dtheta is None else dtheta
+    _need(dtheta, "dtheta", (B, H, d), torch.float32)
+    lib = _lib.load()
+    _lib.check(lib.ttt_eta_gate_backward(B, H, L, d, io, _ptr(XK), _ptr(theta_lr), float(eta_base),
+                                         _ptr(deta), _ptr(dXK), _ptr(dtheta), _stream(stream)))
+    return dtheta
+
+
 def ttt_linear_backward_workspace(B: int, H: int, L: int, d: int, mb: int = 16) -> int:
     """Bytes of device workspace ttt_linear_backward needs."""
     n = ctypes.c_size_t(0)

@@ -46,9 +46,16 @@ def linear_gpu(x, mb=None, W0=None, b0=None, stream=None):
     dt = io_dtype(x.io)
     W0 = x.W0 if W0 is None else W0
     b0 = x.b0 if b0 is None else b0
-    O, Wo, bo = ttt.ttt_linear_forward(dev(x.XQ, dt), dev(x.XK, dt), dev(x.XV, dt), dev(x.eta),
-                                       dev(W0), dev(b0), dev(x.gamma), dev(x.beta),
-                                       mb=mb or x.mb, ln_eps=x.eps, stream=stream)
+    if x.eta is None:  # gated inputs: the kernel evaluates the gate
+        O, Wo, bo = ttt.ttt_linear_forward_gated(dev(x.XQ, dt), dev(x.XK, dt), dev(x.XV, dt),
+                                                 dev(x.theta_lr), x.eta_base, dev(W0), dev(b0),
+                                                 dev(x.gamma), dev(x.beta), mb=mb or x.mb,
+                                                 ln_eps=x.eps, stream=stream)
+    else:
+        O, Wo, bo = ttt.ttt_linear_forward(dev(x.XQ, dt), dev(x.XK, dt), dev(x.XV, dt),
+                                           dev(x.eta), dev(W0), dev(b0), dev(x.gamma),
+                                           dev(x.beta), mb=mb or x.mb, ln_eps=x.eps,
+                                           stream=stream)
     torch.cuda.synchronize()
     return to_np(O), to_np(Wo), to_np(bo)
 
@@ -56,7 +63,8 @@ def linear_gpu(x, mb=None, W0=None, b0=None, stream=None):
 def linear_oracle(x, mb=None, W0=None, b0=None, schedule=None):
     W0 = x.W0 if W0 is None else W0
     b0 = x.b0 if b0 is None else b0
-    return oracle.linear_forward(x.XQ, x.XK, x.XV, x.eta, W0, b0, x.gamma, x.beta, x.eps,
+    eta = x.eta if x.eta is not None else oracle.eta_gate(x.XK, x.theta_lr, x.eta_base)
+    return oracle.linear_forward(x.XQ, x.XK, x.XV, eta, W0, b0, x.gamma, x.beta, x.eps,
                                  mb=mb or x.mb, w0_batched=np.ndim(W0) == 4, schedule=schedule)
 
 

@@ -21,7 +21,8 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) >= {"ttt_linear_forward", "ttt_mlp_forward", "ttt_decode_step",
                           "ttt_decode_steps", "ttt_linear_backward",
                           "ttt_linear_backward_workspace", "ttt_ln_l2_bwd", "ttt_last_error",
-                          "ttt_version"}
+                          "ttt_version", "ttt_linear_forward_gated", "ttt_eta_gate",
+                          "ttt_eta_gate_backward"}
     for n in names:
         assert hasattr(lib, n), n
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
@@ -182,6 +183,60 @@ def test_linear_backward_validation(lib):
     q = list(p); q[8] = 0  # dO
     assert _bwd(lib, ptrs=q) == _lib.TTT_E_NULL
     assert _bwd(lib, B=0) == _lib.TTT_OK  # nothing to do, no HIP call
+
+
+def _gated(lib, B=1, H=1, L=16, d=64, mb=16, io=1, theta=None, eta_base=1 / 64, eps=1e-6,
+           O=None):
+    p = [FAKE + i * (1 << 20) for i in range(8)]
+    th = theta if theta is not None else p[3]
+    Oo = O if O is not None else FAKE + 11 * (1 << 20)
+    return lib.ttt_linear_forward_gated(B, H, L, d, mb, io, eps, p[0], p[1], p[2], th, eta_base,
+                                        p[4], p[5], 0, p[6], p[7], Oo, FAKE + 9 * (1 << 20),
+                                        FAKE + 10 * (1 << 20), None)
+
+
+def test_linear_forward_gated_validation(lib):
+    assert _gated(lib, B=-1) == _lib.TTT_E_SHAPE
+    assert _gated(lib, d=32) == _lib.TTT_E_SHAPE
+    assert _gated(lib, eps=0.0) == _lib.TTT_E_SHAPE
+    for bad in (float("inf"), float("nan")):
+        assert _gated(lib, eta_base=bad) == _lib.TTT_E_SHAPE
+        assert "eta_base" in lib.ttt_last_error().decode()
+    assert _gated(lib, theta=0) == _lib.TTT_E_NULL
+    assert "theta_lr" in lib.ttt_last_error().decode()
+    assert _gated(lib, theta=FAKE + 3 * (1 << 20) + 4) == _lib.TTT_E_ALIGN
+    assert _gated(lib, O=FAKE + 3 * (1 << 20)) == _lib.TTT_E_ALIAS  # O over theta_lr
+    assert _gated(lib, B=0) == _lib.TTT_OK
+
+
+def _gate(lib, B=2, H=3, L=40, d=64, io=1, xk=FAKE, th=FAKE + (1 << 20), eta_base=0.5,
+          eta=FAKE + 2 * (1 << 20)):
+    return lib.ttt_eta_gate(B, H, L, d, io, xk, th, eta_base, eta, None)
+
+
+def _gate_bwd(lib, B=2, H=3, L=40, d=64, io=1, deta=FAKE + 2 * (1 << 20),
+              dxk=FAKE + 3 * (1 << 20), dth=FAKE + 4 * (1 << 20), eta_base=0.5):
+    return lib.ttt_eta_gate_backward(B, H, L, d, io, FAKE, FAKE + (1 << 20), eta_base, deta, dxk,
+                                     dth, None)
+
+
+def test_eta_gate_validation(lib):
+    assert _gate(lib, L=-1) == _lib.TTT_E_SHAPE
+    assert _gate(lib, d=48) == _lib.TTT_E_SHAPE
+    assert _gate(lib, io=2) == _lib.TTT_E_DTYPE
+    assert _gate(lib, eta_base=float("nan")) == _lib.TTT_E_SHAPE
+    assert _gate(lib, xk=0) == _lib.TTT_E_NULL
+    assert _gate(lib, eta=0) == _lib.TTT_E_NULL
+    assert _gate(lib, xk=FAKE + 8) == _lib.TTT_E_ALIGN
+    assert _gate(lib, eta=FAKE + 64) == _lib.TTT_E_ALIAS
+    assert _gate(lib, B=0) == _lib.TTT_OK and _gate(lib, L=0) == _lib.TTT_OK
+    assert _gate_bwd(lib, d=8) == _lib.TTT_E_SHAPE
+    assert _gate_bwd(lib, deta=0) == _lib.TTT_E_NULL
+    assert _gate_bwd(lib, dth=0) == _lib.TTT_E_NULL
+    assert _gate_bwd(lib, dxk=FAKE + 3 * (1 << 20) + 4) == _lib.TTT_E_ALIGN
+    assert _gate_bwd(lib, dxk=FAKE) == _lib.TTT_E_ALIAS          # dXK over XK
+    assert _gate_bwd(lib, dth=FAKE + 3 * (1 << 20) + 256) == _lib.TTT_E_ALIAS
+    assert _gate_bwd(lib, B=0) == _lib.TTT_OK
 
 
 def test_ln_bwd_validation(lib):
