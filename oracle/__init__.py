@@ -50,6 +50,10 @@ def _load():
         f = getattr(lib, name)
         f.argtypes = mlp_args
         f.restype = ctypes.c_int
+    lib.oracle_linear_forward_opts.argtypes = [ctypes.c_int] * 5 + [_I, ctypes.c_double] \
+        + [_D] * 6 + [ctypes.c_int] + [_D] * 2 + [ctypes.c_int, ctypes.c_double] + [_D] * 3 \
+        + [ctypes.c_int]
+    lib.oracle_linear_forward_opts.restype = ctypes.c_int
     lib.oracle_ln_l2_bwd.argtypes = [ctypes.c_int, ctypes.c_int, _D, _D, _D, _D,
                                      ctypes.c_double, _D]
     lib.oracle_ln_l2_bwd.restype = None
@@ -132,6 +136,33 @@ def linear_forward(XQ, XK, XV, eta, W0, b0, gamma, beta, eps: float, mb: int = 1
            _p(Wo), _p(bo), nthreads or default_threads())
     if st != 0:
         raise RuntimeError(f"oracle linear returned {st}")
+    return O, Wo, bo
+
+
+def linear_forward_opts(XQ, XK, XV, eta, W0, b0, gamma, beta, eps: float, mb: int = 16,
+                        loss: str = "mse", weight_decay: float = 0.0,
+                        schedule: Optional[Sequence[int]] = None, w0_batched: bool = False,
+                        nthreads: Optional[int] = None):
+    """TTT-Linear with the Modular-TTT options (primal form): loss "mse" (the
+    squared reconstruction error of linear_forward) or "inner_product"
+    (-< XK + LN(XK W + b), XV > per token), and weight decay lambda/2 ||W||^2
+    added to every token's loss (W only). Returns (O, W_out, b_out)."""
+    lib = _load()
+    XQ, XK, XV, eta = _f64(XQ), _f64(XK), _f64(XV), _f64(eta)
+    B, H, L, d = XQ.shape
+    W0, b0, gamma, beta = _f64(W0), _f64(b0), _f64(gamma), _f64(beta)
+    sched, nch = _sched(L, mb, schedule)
+    O = np.zeros((B, H, L, d))
+    Wo = np.zeros((B, H, d, d))
+    bo = np.zeros((B, H, d))
+    code = {"mse": 0, "inner_product": 1}[loss]
+    st = lib.oracle_linear_forward_opts(B, H, L, d, nch, sched.ctypes.data_as(_I), float(eps),
+                                        _p(XQ), _p(XK), _p(XV), _p(eta), _p(W0), _p(b0),
+                                        int(bool(w0_batched)), _p(gamma), _p(beta), code,
+                                        float(weight_decay), _p(O), _p(Wo), _p(bo),
+                                        nthreads or default_threads())
+    if st != 0:
+        raise RuntimeError(f"oracle linear (options) returned {st}")
     return O, Wo, bo
 
 

@@ -28,7 +28,11 @@
  *   the same gamma/beta serve the loss and the output; row-vector convention
  *   Z = X W with W[i][j] mapping input i to output j ([D] §4.2 forward line);
  *   chunks are aligned at t = 0 and the last chunk may be partial;
- *   GELU is the exact x * Phi(x).
+ *   GELU is the exact x * Phi(x);
+ *   Modular-TTT options (TTT-Linear only): the inner-product loss scores the
+ *   prediction f(xk) = xk + LN(xk W + b) against xv as -<f(xk), xv>; weight
+ *   decay adds lambda/2 ||W||^2 to each token's loss (W only, not b), its
+ *   gradient taken at the chunk-start state like the rest.
  *
  * Layouts (row-major, contiguous):
  *   XQ, XK, XV, O : [B,H,L,d]         eta : [B,H,L]
@@ -102,6 +106,39 @@ static void ln_l2_grad_row(int d, const double *z, const double *tau,
     }
 }
 
+/*
+ * Gradient of the inner-product loss l(z) = -< x + LN_{gamma,beta}(z), v >
+ * (the prediction f(x) = x + LN(z) scored against the target v by an inner
+ * product instead of a squared distance, the loss alternative named on the
+ * Modular-TTT page) with respect to z: the upstream gradient dl/dy is -v, so
+ *   gh = -gamma*v,  dl/dz = (gh - mean(gh) - xh * mean(gh*xh)) / sigma.
+ * (x does not depend on z; beta drops out.)
+ */
+static void ln_ip_grad_row(int d, const double *z, const double *v,
+                           const double *gamma, double eps, double *G)
+{
+    double mu = 0.0, var = 0.0;
+    for (int j = 0; j < d; ++j) mu += z[j];
+    mu /= d;
+    for (int j = 0; j < d; ++j) var += (z[j] - mu) * (z[j] - mu);
+    var /= d;
+    double sigma = sqrt(var + eps);
+    double m1 = 0.0, m2 = 0.0;
+    for (int j = 0; j < d; ++j) {
+        double xh = (z[j] - mu) / sigma;
+        double gh = -gamma[j] * v[j];
+        m1 += gh;
+        m2 += gh * xh;
+    }
+    m1 /= d;
+    m2 /= d;
+    for (int j = 0; j < d; ++j) {
+        double xh = (z[j] - mu) / sigma;
+        double gh = -gamma[j] * v[j];
+        G[j] = (gh - m1 - xh * m2) / sigma;
+    }
+}
+
 void oracle_ln_fwd(int rows, int d, const double *Z, const double *gamma,
                    const double *beta, double eps, double *Y)
 {
@@ -143,6 +180,8 @@ typedef struct {
     int w0_batched;
     const double *gamma, *beta;
     double *O, *W_out, *b_out, *W2_out, *b2_out;
+    int loss;      /* Linear: 0 = squared error (the default), 1 = inner product */
+    double wd;     /* Linear: weight decay lambda on W (0 = none)               */
     int nthreads;
     int tid;
     int status;
@@ -236,6 +275,7 @@ static void linear_primal_seq(job_t *j, int n, int h, double *scratch)
     double *z = G + (size_t)j->max_chunk * d; /* d                        */
     double *tau = z + d;                    /* d                          */
     double *y = tau + d;                    /* d                          */
+    double *Wc = y + d;                     /* d*d: chunk-start W (decay)  */
 
     const size_t w_off = (j->w0_batched ? (size_t)n * H * d * d : 0) + (size_t)h * d * d;
     const size_t b_off = (j->w0_batched ? (size_t)n * H * d : 0) + (size_t)h * d;
@@ -254,8 +294,14 @@ static void linear_primal_seq(job_t *j, int n, int h, double *scratch)
                 z[jj] = acc;
                 tau[jj] = v[jj] - k[jj];     /* reconstruction target XV - XK */
             }
-            ln_l2_grad_row(d, z, tau, gamma, beta, j->eps, G + (size_t)s * d);
+            if (j->loss == 1)
+                ln_ip_grad_row(d, z, v, gamma, j->eps, G + (size_t)s * d);
+            else
+                ln_l2_grad_row(d, z, tau, gamma, beta, j->eps, G + (size_t)s * d);
         }
+        /* weight decay: each token's gradient also carries lambda * W at the
+           chunk-start state (the gradient of lambda/2 ||W||^2 there) */
+        if (j->wd != 0.0) memcpy(Wc, W, sizeof(double) * d * d);
         /* token order: update with the token's own gradient, then apply */
         for (int s = 0; s < len; ++s) {
             const int t = t0 + s;
@@ -263,7 +309,11 @@ static void linear_primal_seq(job_t *j, int n, int h, double *scratch)
             const double *g = G + (size_t)s * d;
             const double e = eta[t];
             for (int i = 0; i < d; ++i)
-                for (int jj = 0; jj < d; ++jj) W[(size_t)i * d + jj] -= e * k[i] * g[jj];
+                for (int jj = 0; jj < d; ++jj) {
+                    double gw = k[i] * g[jj];
+                    if (j->wd != 0.0) gw += j->wd * Wc[(size_t)i * d + jj];
+                    W[(size_t)i * d + jj] -= e * gw;
+                }
             for (int jj = 0; jj < d; ++jj) b[jj] -= e * g[jj];
             for (int jj = 0; jj < d; ++jj) {
                 double acc = b[jj];
@@ -294,7 +344,36 @@ int oracle_linear_forward(int B, int H, int L, int d, int nchunks, const int *ch
     j.eps = eps; j.XQ = XQ; j.XK = XK; j.XV = XV; j.eta = eta; j.W0 = W0; j.b0 = b0;
     j.w0_batched = w0_batched; j.gamma = gamma; j.beta = beta; j.O = O;
     j.W_out = W_out; j.b_out = b_out; j.nthreads = nthreads;
-    size_t scratch = (size_t)d * d + (size_t)d * (4 + j.max_chunk);
+    size_t scratch = 2 * (size_t)d * d + (size_t)d * (4 + j.max_chunk);
+    return run_pool(&j, linear_primal_seq, scratch);
+}
+
+/*
+ * TTT-Linear with the Modular-TTT design choices as options: loss = 0 is the
+ * squared reconstruction error above, loss = 1 the inner-product loss
+ * -< x + LN(x W + b), v > (ln_ip_grad_row); weight_decay = lambda adds
+ * lambda/2 ||W||^2 to every token's loss (W only, the bias is not decayed).
+ * Mini-batch rule as before: every gradient, decay term included, is taken at
+ * the chunk-start state.
+ */
+int oracle_linear_forward_opts(int B, int H, int L, int d, int nchunks, const int *chunk_len,
+                               double eps, const double *XQ, const double *XK,
+                               const double *XV, const double *eta, const double *W0,
+                               const double *b0, int w0_batched, const double *gamma,
+                               const double *beta, int loss, double weight_decay, double *O,
+                               double *W_out, double *b_out, int nthreads)
+{
+    if (B < 0 || H < 0 || L < 0 || d <= 0 || (loss != 0 && loss != 1)) return ORACLE_E_ARG;
+    job_t j;
+    memset(&j, 0, sizeof j);
+    int st = check_schedule(L, nchunks, chunk_len, &j.max_chunk);
+    if (st) return st;
+    j.B = B; j.H = H; j.L = L; j.d = d; j.nchunks = nchunks; j.chunk_len = chunk_len;
+    j.eps = eps; j.XQ = XQ; j.XK = XK; j.XV = XV; j.eta = eta; j.W0 = W0; j.b0 = b0;
+    j.w0_batched = w0_batched; j.gamma = gamma; j.beta = beta; j.O = O;
+    j.W_out = W_out; j.b_out = b_out; j.nthreads = nthreads;
+    j.loss = loss; j.wd = weight_decay;
+    size_t scratch = 2 * (size_t)d * d + (size_t)d * (4 + j.max_chunk);
     return run_pool(&j, linear_primal_seq, scratch);
 }
 

@@ -56,6 +56,37 @@ def linear_autograd(XQ, XK, XV, eta, W0, b0, gamma, beta, eps, mb):
     return O.numpy(), W.detach().numpy(), b.detach().numpy()
 
 
+def linear_autograd_opts(XQ, XK, XV, eta, W0, b0, gamma, beta, eps, mb, loss="mse", wd=0.0):
+    """linear_autograd with the Modular-TTT options: per-token loss "mse"
+    (1/2 ||LN(z) - (xv - xk)||^2) or "inner_product" (-< xk + LN(z), xv >),
+    plus wd/2 ||W||^2; every gradient by autograd at the chunk-start state."""
+    xq, xk, xv, et = _t(XQ), _t(XK), _t(XV), _t(eta)
+    W = _t(W0).clone()
+    b = _t(b0).clone()
+    g_, be_ = _t(gamma), _t(beta)
+    L, d = xq.shape
+    O = torch.zeros(L, d, dtype=torch.float64)
+    t0 = 0
+    for n in chunk_schedule(L, mb):
+        Wc = W.clone().requires_grad_(True)
+        bc = b.clone().requires_grad_(True)
+        grads = []
+        for s in range(t0, t0 + n):
+            y = F.layer_norm(xk[s] @ Wc + bc, (d,), g_, be_, eps)
+            if loss == "mse":
+                ls = 0.5 * ((y - (xv[s] - xk[s])) ** 2).sum()
+            else:
+                ls = -((xk[s] + y) * xv[s]).sum()
+            ls = ls + 0.5 * wd * (Wc ** 2).sum()
+            grads.append(torch.autograd.grad(ls, (Wc, bc)))
+        for i, s in enumerate(range(t0, t0 + n)):
+            W = W - et[s] * grads[i][0]
+            b = b - et[s] * grads[i][1]
+            O[s] = xq[s] + F.layer_norm(xq[s] @ W + b, (d,), g_, be_, eps)
+        t0 += n
+    return O.numpy(), W.detach().numpy(), b.detach().numpy()
+
+
 def mlp_autograd(XQ, XK, XV, eta, W1, b1, W2, b2, gamma, beta, eps, mb):
     """Mini-batch TTT-MLP (d -> 4d exact GELU -> d) via autograd. Inputs [L,d]."""
     xq, xk, xv, et = _t(XQ), _t(XK), _t(XV), _t(eta)
