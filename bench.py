@@ -19,6 +19,8 @@ Other workloads of the same hot path (--workload):
       gate evaluated in the kernel (theta_lr ~ N(0, 0.02^2), eta_base = 1/d)
   3gb ttt_eta_gate_backward on workload 3's keys (dXK += the path through
       eta, dtheta per sequence; roofline: HBM)
+  3o  workload 3 through ttt_linear_forward_opts with the inner-product loss
+      and weight decay 0.5 (the MFMA prefill's option instantiation; roofline: HBM)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
                        [--no-cpu-baseline]
@@ -117,7 +119,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="3", choices=["3", "2", "5p", "4", "5d", "5r", "3b", "3g", "3gb"])
+    ap.add_argument("--workload", default="3", choices=["3", "2", "5p", "4", "5d", "5r", "3b", "3g", "3gb", "3o"])
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -154,8 +156,9 @@ def main():
         return bench_backward(args)
     if args.workload == "3gb":
         return bench_gate_backward(args)
-    wl = {"3": 3, "3g": 3, "2": 2, "5p": 5}[args.workload]
+    wl = {"3": 3, "3g": 3, "3o": 3, "2": 2, "5p": 5}[args.workload]
     gated = args.workload == "3g"
+    opts = args.workload == "3o"  # inner-product loss, weight decay 0.5
     w = gen.WORKLOADS[wl]
     x = gen.make_workload(wl, decode_steps=0) if wl == 5 else gen.make_workload(wl)
     if wl == 5:
@@ -179,6 +182,10 @@ def main():
         if gated:
             ttt.ttt_linear_forward_gated(XQ, XK, XV, theta, eta_base, W0, b0, gam, bet, O=O,
                                          W_out=Wo, b_out=bo, mb=16, ln_eps=x.eps, stream=stream)
+        elif opts:
+            ttt.ttt_linear_forward_opts(XQ, XK, XV, eta, W0, b0, gam, bet, "inner_product", 0.5,
+                                        O=O, W_out=Wo, b_out=bo, mb=16, ln_eps=x.eps,
+                                        stream=stream)
         else:
             ttt.ttt_linear_forward(XQ, XK, XV, eta, W0, b0, gam, bet, O=O, W_out=Wo, b_out=bo,
                                    mb=16, ln_eps=x.eps, stream=stream)
@@ -207,10 +214,11 @@ def main():
     if gated:  # no eta array read; theta_lr [H,d] read once per sequence
         ab += B * H * (d * 4 - L * 4)
     achieved = ab / kern_avg_s / 1e9
-    traffic = measured_traffic(ab) if (wl == WORKLOAD and not gated) else None
+    plain = not (gated or opts)
+    traffic = measured_traffic(ab) if (wl == WORKLOAD and plain) else None
+    tag = ", gated eta" if gated else (", inner-product loss, weight decay 0.5" if opts else "")
     out = {
-        "metric": (METRIC if wl == WORKLOAD and not gated else
-                   f"TTT-Linear prefill tokens/s (L={L}{', gated eta' if gated else ''})"),
+        "metric": METRIC if wl == WORKLOAD and plain else f"TTT-Linear prefill tokens/s (L={L}{tag})",
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -222,11 +230,12 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name + ("+eta_gate" if gated else ""), "B": B, "H": H, "L": L, "d": d, "mini_batch": 16,
+        "config": {"workload": w.name + ("+eta_gate" if gated else "") + ("+ip_loss+wd" if opts else ""), "B": B, "H": H, "L": L, "d": d, "mini_batch": 16,
                    "io": "bf16", "state": "fp32", "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "linear_prefill", "kernel_avg_us": kern_avg_s * 1e6,
+                     "kernel": "linear_prefill_mfma",
+                     "kernel_avg_us": kern_avg_s * 1e6,
                      "alg_bytes_per_launch": ab},
     }
 
@@ -238,7 +247,10 @@ def main():
         t1 = time.perf_counter()
         if gated:
             xs["eta"] = oracle.eta_gate(xs["XK"], theta_np, eta_base)
-        ro, rW, rb = oracle.linear_forward(xs["XQ"], xs["XK"], xs["XV"], xs["eta"], xs["W0"],
+        run = (lambda *a, **k: oracle.linear_forward_opts(*a, loss="inner_product",
+                                                          weight_decay=0.5, **k)) if opts \
+            else oracle.linear_forward
+        ro, rW, rb = run(xs["XQ"], xs["XK"], xs["XV"], xs["eta"], xs["W0"],
                                            xs["b0"], xs["gamma"], xs["beta"], x.eps, mb=16,
                                            nthreads=nt)
         tc = time.perf_counter() - t1

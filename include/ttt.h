@@ -12,6 +12,8 @@
  *       f(x) = x + LN(f_res(x)) and the d -> 4d GELU -> d MLP, §2.2 the
  *       per-token learning-rate gate, §2.4 mini-batch b = 16 and the dual form.
  *   [X] xiaohu.ai TTT summary: mini-batch TTT and the dual form.
+ *   [M] ai-feeds.com "Modular TTT" summary: inner loss (MSE or inner
+ *       product) and weight decay as design axes of the fast-weight learner.
  *
  * Computation (per independent sequence (n,h), tokens t = 0..L-1, chunks of
  * `mb` tokens aligned at t = 0, the last chunk possibly shorter):
@@ -55,11 +57,16 @@ extern "C" {
 
 #define TTT_OK 0
 #define TTT_E_NULL (-1)  /* a required pointer is NULL                          */
-#define TTT_E_SHAPE (-2) /* negative size, unsupported d / mb, or bad ln_eps  */
+#define TTT_E_SHAPE (-2) /* negative size, unsupported d / mb, bad ln_eps or  */
+                         /* another scalar argument out of its range         */
 #define TTT_E_DTYPE (-3) /* io is not TTT_F32 / TTT_BF16                       */
 #define TTT_E_ALIGN (-4) /* a pointer is not aligned as required               */
 #define TTT_E_ALIAS (-5) /* an output overlaps an input or another output      */
 #define TTT_E_HIP (-6)   /* the kernel launch failed                           */
+
+/* Inner loss of ttt_linear_forward_opts. */
+#define TTT_LOSS_MSE 0           /* 1/2 ||LN(XK W + b) - (XV - XK)||^2 per token  */
+#define TTT_LOSS_INNER_PRODUCT 1 /* -< XK + LN(XK W + b), XV > per token          */
 
 /* Storage type of XQ/XK/XV and O. State, eta and LN parameters are fp32. */
 typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
@@ -109,6 +116,28 @@ int ttt_linear_forward_gated(int B, int H, int L, int d, int mb, int io, float l
                              const float *b0, int w0_batched, const float *ln_gamma,
                              const float *ln_beta, void *O, float *W_out, float *b_out,
                              hipStream_t stream);
+
+/*
+ * ttt_linear_forward with two design choices of the Modular-TTT page ([M]:
+ * inner loss and weight decay on the fast weights), which names them without
+ * an update rule; the readings taken:
+ *   inner_loss   : TTT_LOSS_MSE (the layer above) or TTT_LOSS_INNER_PRODUCT,
+ *                  each token's loss -< XK_t + LN(XK_t W + b), XV_t >; any other
+ *                  value is TTT_E_SHAPE.
+ *   weight_decay : lambda >= 0 (finite, else TTT_E_SHAPE); every token's loss
+ *                  gains lambda/2 ||W||^2 (W only, not b), its gradient taken at
+ *                  the chunk-start state W_c like the rest, so a chunk maps
+ *                  W_c -> (1 - lambda * sum_t eta_t) W_c - (eta * XK)^T G.
+ * Every other argument as ttt_linear_forward. The defaults (TTT_LOSS_MSE,
+ * 0) run ttt_linear_forward's kernels; other values run the fp32 VALU prefill
+ * kernel for every shape.
+ */
+int ttt_linear_forward_opts(int B, int H, int L, int d, int mb, int io, float ln_eps,
+                            const void *XQ, const void *XK, const void *XV, const float *eta,
+                            const float *W0, const float *b0, int w0_batched,
+                            const float *ln_gamma, const float *ln_beta, int inner_loss,
+                            float weight_decay, void *O, float *W_out, float *b_out,
+                            hipStream_t stream);
 
 /*
  * The learning-rate gate of [Y] §2.2 on its own, for the paths that take eta

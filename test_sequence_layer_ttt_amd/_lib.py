@@ -12,6 +12,8 @@ LIB_PATH = os.path.join(PKG, "libttt.so")
 HEADER = os.path.join(ROOT, "include", "ttt.h")
 
 TTT_OK = 0
+TTT_LOSS_MSE = 0
+TTT_LOSS_INNER_PRODUCT = 1
 TTT_E_NULL = -1
 TTT_E_SHAPE = -2
 TTT_E_DTYPE = -3
@@ -46,6 +48,8 @@ def load():
     lib.ttt_linear_forward.argtypes = [_i] * 6 + [_f] + [_P] * 6 + [_i] + [_P] * 5 + [_P]
     lib.ttt_linear_forward_gated.argtypes = ([_i] * 6 + [_f] + [_P] * 4 + [_f] + [_P] * 2 + [_i]
                                             + [_P] * 5 + [_P])
+    lib.ttt_linear_forward_opts.argtypes = ([_i] * 6 + [_f] + [_P] * 6 + [_i] + [_P] * 2
+                                            + [_i, _f] + [_P] * 3 + [_P])
     lib.ttt_eta_gate.argtypes = [_i] * 5 + [_P, _P, _f, _P, _P]
     lib.ttt_eta_gate_backward.argtypes = [_i] * 5 + [_P, _P, _f, _P, _P, _P, _P]
     lib.ttt_mlp_forward.argtypes = [_i] * 6 + [_f] + [_P] * 8 + [_i] + [_P] * 7 + [_P]
@@ -58,6 +62,7 @@ def load():
     for name in ("ttt_linear_forward", "ttt_mlp_forward", "ttt_decode_step", "ttt_decode_steps",
                  "ttt_linear_backward", "ttt_linear_backward_workspace", "ttt_ln_l2_bwd",
                  "ttt_linear_forward_gated", "ttt_eta_gate", "ttt_eta_gate_backward",
+                 "ttt_linear_forward_opts",
                  "ttt_version"):
         getattr(lib, name).restype = _i
     lib.ttt_last_error.restype = ctypes.c_char_p

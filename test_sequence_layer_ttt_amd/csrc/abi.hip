@@ -141,10 +141,16 @@ int linear_forward(int B, int H, int L, int d, int mb, int io, float ln_eps, con
                    const void *XK, const void *XV, const float *eta, const float *theta,
                    float eta_base, const float *W0, const float *b0, int w0_batched,
                    const float *ln_gamma, const float *ln_beta, void *O, float *W_out,
-                   float *b_out, hipStream_t stream, bool gated) {
+                   float *b_out, hipStream_t stream, bool gated, int loss = TTT_LOSS_MSE,
+                   float weight_decay = 0.f) {
     int st;
     if ((st = check_common(B, H, L, mb, io)) || (st = check_eps(ln_eps))) return st;
     if (d != 16 && d != 64) return fail(TTT_E_SHAPE, "d = %d not in {16, 64}", d);
+    if (loss != TTT_LOSS_MSE && loss != TTT_LOSS_INNER_PRODUCT)
+        return fail(TTT_E_SHAPE, "inner_loss = %d is not TTT_LOSS_MSE / TTT_LOSS_INNER_PRODUCT", loss);
+    if (!(weight_decay >= 0.f) || !std::isfinite(weight_decay))
+        return fail(TTT_E_SHAPE, "weight_decay = %g is not a finite value >= 0",
+                    static_cast<double>(weight_decay));
     if (gated && !std::isfinite(eta_base))
         return fail(TTT_E_SHAPE, "eta_base = %g is not finite", static_cast<double>(eta_base));
     const size_t es = io == TTT_BF16 ? 2 : 4;
@@ -177,6 +183,8 @@ int linear_forward(int B, int H, int L, int d, int mb, int io, float ln_eps, con
         a.theta = theta;
         a.eta_base = eta_base;
     }
+    a.loss = loss;
+    a.wd = weight_decay;
     if (ttt::linear_mfma_supported(a)) return launched(ttt::launch_linear_mfma(a, stream));
     return launched(ttt::launch_linear_valu(a, stream));
 }
@@ -218,6 +226,17 @@ int ttt_linear_forward_gated(int B, int H, int L, int d, int mb, int io, float l
                              hipStream_t stream) {
     return linear_forward(B, H, L, d, mb, io, ln_eps, XQ, XK, XV, nullptr, theta_lr, eta_base,
                           W0, b0, w0_batched, ln_gamma, ln_beta, O, W_out, b_out, stream, true);
+}
+
+int ttt_linear_forward_opts(int B, int H, int L, int d, int mb, int io, float ln_eps,
+                            const void *XQ, const void *XK, const void *XV, const float *eta,
+                            const float *W0, const float *b0, int w0_batched,
+                            const float *ln_gamma, const float *ln_beta, int inner_loss,
+                            float weight_decay, void *O, float *W_out, float *b_out,
+                            hipStream_t stream) {
+    return linear_forward(B, H, L, d, mb, io, ln_eps, XQ, XK, XV, eta, nullptr, 0.f, W0, b0,
+                          w0_batched, ln_gamma, ln_beta, O, W_out, b_out, stream, false,
+                          inner_loss, weight_decay);
 }
 
 int ttt_eta_gate(int B, int H, int L, int d, int io, const void *XK, const float *theta_lr,

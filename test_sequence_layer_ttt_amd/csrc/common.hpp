@@ -101,6 +101,29 @@ __device__ __forceinline__ void ln_l2_grad(const float (&z)[E], const float (&ta
     for (int e = 0; e < E; ++e) G[e] = rstd * (gh[e] - s1 - xh[e] * s2);
 }
 
+// Gradient of the inner-product loss -< x + LN(z), v > with respect to z:
+// the upstream gradient is -v, so gh = -gamma * v (beta drops out).
+template <int GL, int E>
+__device__ __forceinline__ void ln_ip_grad(const float (&z)[E], const float (&v)[E],
+                                           const float (&gamma)[E], float inv_d, float eps,
+                                           float (&G)[E]) {
+    float mu, rstd;
+    row_stats<GL, E>(z, inv_d, eps, mu, rstd);
+    float xh[E], gh[E];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        xh[e] = (z[e] - mu) * rstd;
+        gh[e] = -gamma[e] * v[e];
+        s1 += gh[e];
+        s2 += gh[e] * xh[e];
+    }
+    s1 = group_sum<GL>(s1) * inv_d;
+    s2 = group_sum<GL>(s2) * inv_d;
+#pragma unroll
+    for (int e = 0; e < E; ++e) G[e] = rstd * (gh[e] - s1 - xh[e] * s2);
+}
+
 template <int GL, int E>
 __device__ __forceinline__ void ln_fwd(const float (&z)[E], const float (&gamma)[E],
                                        const float (&beta)[E], float inv_d, float eps,

@@ -20,6 +20,10 @@ struct LinearArgs {
     // rate is eta_base * logistic(theta[h] . XK_t), evaluated in the kernel
     const float *theta = nullptr;
     float eta_base = 0.f;
+    // inner loss (0: squared reconstruction error, 1: inner product) and
+    // weight decay lambda on W; the MFMA kernel takes only the defaults
+    int loss = 0;
+    float wd = 0.f;
 };
 
 struct LinearBwdArgs {

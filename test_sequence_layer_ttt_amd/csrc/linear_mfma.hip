@@ -73,7 +73,7 @@ struct alignas(16) LSlot {
     alignas(16) uint16_t xq[MB * RB];       // fp16 rows
     alignas(16) uint16_t xk[MB * RB];       // fp16 rows
     alignas(16) uint16_t xkt[D * KS + 16];  // bf16, [permuted feature][token], see xkt_at
-    alignas(16) float tau[MB * RS];    // XV - XK, fp32 rows
+    alignas(16) float tau[MB * RS];    // the loss's target (XV - XK, or XV), fp32 rows
     alignas(16) float eta[MB];
 };
 
@@ -87,6 +87,10 @@ struct alignas(16) Smem {
     alignas(16) uint2 ka[2][64];        // K(j, j-1)
     alignas(16) uint2 k2[2][64];        // K(j, j-2)
     alignas(16) uint2 tb[2][64];        // T_j^T
+    // weight decay, per slot: 1 - lambda * (sum of eta up to token t), and
+    // alpha = 1 - lambda * (sum of the chunk's eta)
+    alignas(16) float dec[NSLOT][MB];
+    float alpha[NSLOT];
 };
 
 struct Ctx {
@@ -134,10 +138,11 @@ __device__ __forceinline__ f16x8 fragh(const uint16_t *rows, int c, int g, int k
 // the next iteration (T_{j+1} in the one after) and rewritten two
 // iterations later.
 // ---------------------------------------------------------------------------
-template <bool GATED>
+template <bool GATED, int LOSS, bool DECAY>
 __device__ __forceinline__ void prep_waves(Smem &sm, int pw, int g, int c, int lane, const bf16_t *xq,
                                            const bf16_t *xk, const bf16_t *xv, const float *et,
-                                           const float *th, float eta_base, int L, int iters) {
+                                           const float *th, float eta_base, float wd, int L,
+                                           int iters) {
     constexpr int PRE = 2, BPI = 2;
     LSlot *slots = sm.slot;
     const int r = 4 * pw + g, f0 = 4 * c;  // token, first feature
@@ -176,7 +181,11 @@ __device__ __forceinline__ void prep_waves(Smem &sm, int pw, int g, int c, int l
         S.xkt[xkt_at(kr + 1, r)] = static_cast<uint16_t>(k.x >> 16);
         S.xkt[xkt_at(kr + 2, r)] = static_cast<uint16_t>(k.y & 0xffffu);
         S.xkt[xkt_at(kr + 3, r)] = static_cast<uint16_t>(k.y >> 16);
-        *reinterpret_cast<f32x4 *>(&S.tau[r * RS + f0]) = unpack4(v) - kf;
+        // target: XV - XK (squared error) or XV (inner-product loss)
+        if constexpr (LOSS == 1)
+            *reinterpret_cast<f32x4 *>(&S.tau[r * RS + f0]) = unpack4(v);
+        else
+            *reinterpret_cast<f32x4 *>(&S.tau[r * RS + f0]) = unpack4(v) - kf;
         if (c == 0) S.eta[r] = e;
     };
     auto stage = [&](const PrepRegs &R, int ch, int slot) {
@@ -202,6 +211,27 @@ __device__ __forceinline__ void prep_waves(Smem &sm, int pw, int g, int c, int l
     auto gram = [&](const uint16_t *A, const uint16_t *B, f32x4 init) {
         return mfma32h(fragh(A, c, g, 1), fragh(B, c, g, 1), mfma32h(fragh(A, c, g, 0), fragh(B, c, g, 0), init));
     };
+    // weight decay factors of a staged chunk (one wave, lanes 0..15 = tokens)
+    // (lane c of each DPP row holds token c: inclusive scan by row shifts)
+    auto decay = [&](int si) {
+        const float e = slots[si].eta[c];
+        float cum = e;
+        cum += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(cum), 0x111, 0xF, 0xF, true));
+        cum += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(cum), 0x112, 0xF, 0xF, true));
+        cum += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(cum), 0x114, 0xF, 0xF, true));
+        cum += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(cum), 0x118, 0xF, 0xF, true));
+        const float all = row16_sum(e);
+        if (g == 0) sm.dec[si][c] = 1.0f - wd * cum;
+        if (lane == 0) sm.alpha[si] = 1.0f - wd * all;
+    };
+    // K(j+2, j) with decay: alpha_{j+1} XK_{j+2} XK_j^T + 1 (the bias path is not decayed)
+    auto gram_dec = [&](const uint16_t *A, const uint16_t *B, float alpha) {
+        const f32x4 gt = gram(A, B, fzero);
+        f32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = fmaf(alpha, gt[i], 1.f);
+        return v;
+    };
     auto tmat = [&](const LSlot &S) {  // T^T of a chunk as a B operand
         const f32x4 gt = gram(S.xk, S.xq, fzero);
         f32x4 tv;
@@ -222,6 +252,11 @@ __device__ __forceinline__ void prep_waves(Smem &sm, int pw, int g, int c, int l
     // prologue operands K(1, 0) and T_0
     if (pw == 1) st_s4(&sm.ka[1][lane], pack4(gram(slots[0].xk, slots[1].xk, fone)));
     if (pw == 2) st_s4(&sm.tb[0][lane], tmat(slots[0]));
+    if constexpr (DECAY) {
+        if (pw == 3)
+#pragma unroll
+            for (int a = 0; a < AHEAD; ++a) decay(a);
+    }
     lds_barrier();
     int slot = AHEAD % NSLOT;  // slot of chunk it + AHEAD
     for (int it = 0; it < iters; it += NSET) {
@@ -237,7 +272,13 @@ __device__ __forceinline__ void prep_waves(Smem &sm, int pw, int g, int c, int l
             lds_barrier();
             // phase 2: K(j+2, j), K(j+2, j+1) and T_{j+1}
             const int par = (it + k) & 1;  // parity of j (= of j+2)
-            if (pw == 0) st_s4(&sm.k2[par][lane], pack4(gram(slots[s0].xk, slots[s2].xk, fone)));
+            if constexpr (DECAY) {
+                if (pw == 0)
+                    st_s4(&sm.k2[par][lane], pack4(gram_dec(slots[s0].xk, slots[s2].xk, sm.alpha[s1])));
+                if (pw == 3) decay(slot);  // chunk j+3, staged in phase 1
+            } else {
+                if (pw == 0) st_s4(&sm.k2[par][lane], pack4(gram(slots[s0].xk, slots[s2].xk, fone)));
+            }
             if (pw == 1) st_s4(&sm.ka[par][lane], pack4(gram(slots[s1].xk, slots[s2].xk, fone)));
             if (pw == 2) st_s4(&sm.tb[par ^ 1][lane], tmat(slots[s1]));
             slot = (slot + 1 == NSLOT) ? 0 : slot + 1;
@@ -249,7 +290,7 @@ __device__ __forceinline__ void prep_waves(Smem &sm, int pw, int g, int c, int l
 // ---------------------------------------------------------------------------
 // Chain waves: Z_c^T (feature tile u) -> row sums -> E_c -> operand layout.
 // ---------------------------------------------------------------------------
-template <bool IDENT>
+template <bool IDENT, int LOSS>
 __device__ __forceinline__ void chain_waves(Smem &sm, const Ctx &cx, int u, int g, int c, int lane,
                                             const float *gam_h, const float *bet_h) {
     constexpr float inv_d = 1.0f / D;
@@ -317,7 +358,9 @@ __device__ __forceinline__ void chain_waves(Smem &sm, const Ctx &cx, int u, int 
             const float r = rsq(var + cx.eps);
             const float mtz = fmaf(s[2], inv_d, -mut * mu);
             const float r2 = r * r;
-            const float a = r2 * fmaf(r, mtz, cx.eps * r2);
+            // squared error: a = eps r^4 + r^3 mean((tau - mean tau)(z - mu));
+            // inner product (ghat = -tau): the eps r^4 term from LN(z) drops out
+            const float a = LOSS == 1 ? r2 * (r * mtz) : r2 * fmaf(r, mtz, cx.eps * r2);
             // E = -eta (a (z - mu) - r (tau - mean tau)) = cz z + ct tau + c0
             const float cz = -et * a, ct = et * r;
             const float c0 = et * fmaf(a, mu, -r * mut);
@@ -328,6 +371,16 @@ __device__ __forceinline__ void chain_waves(Smem &sm, const Ctx &cx, int u, int 
             const float mu = s[0] * inv_d;
             const float var = fmaxf(fmaf(s[1], inv_d, -mu * mu), 0.f);
             const float r = rsq(var + cx.eps);
+            if constexpr (LOSS == 1) {
+                // ghat = -gamma tau: mean(ghat) = -sum(g tau)/d,
+                // mean(ghat xhat) = -r (sum(g tau z) - mu sum(g tau))/d;
+                // E = -eta r (ghat - m1 - xhat m2)
+                const float m1 = -s2[2] * inv_d;
+                const float m2 = -r * fmaf(-mu, s2[2], s2[1]) * inv_d;
+                const float k1 = et * r, k2 = et * r * r * m2, k3 = et * r * m1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ev[i] = fmaf(k1 * gm[i], tau[i], fmaf(k2, z[i] - mu, k3));
+            } else {
             // mean(ghat) and mean(ghat xhat), ghat = gamma (gamma xhat + beta - tau)
             const float m1 = (fmaf(r, fmaf(-mu, Sg2, s[2]), Sgb) - s2[2]) * inv_d;
             const float q2 = fmaf(mu, fmaf(mu, Sg2, -2.f * s[2]), s[3]);       // sum g^2 (z - mu)^2
@@ -338,6 +391,7 @@ __device__ __forceinline__ void chain_waves(Smem &sm, const Ctx &cx, int u, int 
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 ev[i] = fmaf(k1 * (g2[i] - m2), z[i] - mu, fmaf(k2 * gm[i], bt[i] - tau[i], k3));
+            }
         }
         // [token c][feature f0 + i] as the A operand times the identity gives
         // [token 4g + i][feature 16u + c]: E^T in the operand layout.
@@ -357,11 +411,11 @@ __device__ __forceinline__ void chain_waves(Smem &sm, const Ctx &cx, int u, int 
 // ---------------------------------------------------------------------------
 // State waves: W, b of feature tile u; brackets and K; outputs.
 // ---------------------------------------------------------------------------
-template <bool IDENT>
+template <bool IDENT, bool DECAY>
 __device__ __forceinline__ void state_waves(Smem &sm, const Ctx &cx, int u, int g, int c, int lane,
                                             const float *W0s, const float *b0s, const float *gam_h,
                                             const float *bet_h, bf16_t *Oseq, float *W_out,
-                                            float *b_out) {
+                                            float *b_out, float wd) {
     constexpr float inv_d = 1.0f / D;
     const int f0 = 16 * u + 4 * g;
     const s16x4 ones = {0x3F80, 0x3F80, 0x3F80, 0x3F80};  // bf16 1.0
@@ -390,11 +444,21 @@ __device__ __forceinline__ void state_waves(Smem &sm, const Ctx &cx, int u, int 
     };
 
     lds_barrier();  // prologue chunks 0 .. 2 staged
-    f32x4 Pp = fzero;  // XK_{j+2} W_j + b_j, waiting for E_j
+    f32x4 Pp = fzero;  // XK_{j+2} W_j + b_j, waiting for E_j (with decay: XK_{j+2} W_j alone)
+    float pk = 1.f, zk = 1.f;  // weight decay: the factors Pp and Zq still need (then + b)
     if (cx.nch > 0) {
         const f16x8 wf[2] = {wfrag(0), wfrag(1)};
         sm.q[0][u][lane] = xw(wf, sm.slot[0].xk);  // bracket of Z_0 = XK_0 W_0 + b_0
-        Pp = xw(wf, sm.slot[1].xk);                // XK_1 W_0 + b_0 (E_{-1} = 0)
+        if constexpr (DECAY) {  // alpha_0 XK_1 W_0 + b_0, alpha_0 from chunk 0's eta
+            const float *e = sm.slot[0].eta;
+            float all = 0.f;
+#pragma unroll
+            for (int s = 0; s < MB; ++s) all += e[s];
+            Pp = mfma32h(wf[1], xfrag(sm.slot[1].xk, 1), mfma32h(wf[0], xfrag(sm.slot[1].xk, 0), fzero));
+            pk = 1.0f - wd * all;
+        } else {
+            Pp = xw(wf, sm.slot[1].xk);  // XK_1 W_0 + b_0 (E_{-1} = 0)
+        }
     }
     lds_barrier();
 
@@ -416,6 +480,13 @@ __device__ __forceinline__ void state_waves(Smem &sm, const Ctx &cx, int u, int 
             TB = ld_s4(&sm.tb[(it - 1) & 1][lane]);  // T_{it-1}^T
         }
         __builtin_amdgcn_sched_barrier(0);  // all reads of the phase in flight together
+        if constexpr (DECAY) {  // the deferred factors; bv is still b of the chunk they were formed at
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                Pp[i] = fmaf(pk, Pp[i], bv[i]);
+                Zq[i] = fmaf(zk, Zq[i], bv[i]);
+            }
+        }
         if (fwd) sm.q[(it + 1) & 1][u][lane] = upd ? mfma16(EAp, K2, Pp) : Pp;
         f32x4 zb = fzero;
         if (upd) {
@@ -423,7 +494,7 @@ __device__ __forceinline__ void state_waves(Smem &sm, const Ctx &cx, int u, int 
             // rows 0, 1 receive the tile's sum of zb, rows 2, 3 that of zb^2
             sm.stf[c * SB + 4 * g + u] = rows4_reduce2(sum4(zb), sum4(zb * zb));
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) Wv[rb] = mfma16(xkt[rb], EAp, Wv[rb]);
+            for (int rb = 0; rb < 4; ++rb) Wv[rb] = mfma16(xkt[rb], EAp, Wv[rb]);  // (W already decayed)
             bv = mfma16(EAp, ones, bv);
         }
         lds_barrier();
@@ -432,6 +503,12 @@ __device__ __forceinline__ void state_waves(Smem &sm, const Ctx &cx, int u, int 
         f32x4 st;
         uint2 xqb;
         f16x8 q0[2], k2[2];
+        if constexpr (DECAY) {  // token c's XQ factor; alpha_it alpha_{it+1} (applied next phase)
+            if (fwd) {
+                zk = sm.dec[s0][c];
+                pk = sm.alpha[s0] * sm.alpha[s1];
+            }
+        }
         if (upd) {
             st = ld4(&sm.stf[c * SB + 4 * (g & 2)]);  // rows 0, 1: sums of zb; rows 2, 3: of zb^2
             xqb = *reinterpret_cast<const uint2 *>(&sm.slot[sm1].xq[c * RB + f0]);
@@ -446,8 +523,20 @@ __device__ __forceinline__ void state_waves(Smem &sm, const Ctx &cx, int u, int 
         __builtin_amdgcn_sched_barrier(0);
         if (fwd) {
             const f16x8 wf[2] = {wfrag(0), wfrag(1)};
-            Pp = mfma32h(wf[1], k2[1], mfma32h(wf[0], k2[0], bv));  // XK_{it+2} W_it + b_it
-            Zq = mfma32h(wf[1], q0[1], mfma32h(wf[0], q0[0], bv));  // XQ_it W_it + b_it
+            if constexpr (DECAY) {
+                // XK_{it+2} W_it and XQ_it W_it; their factors and b_it follow
+                // in the next phase, off this phase's MFMA latency
+                Pp = mfma32h(wf[1], k2[1], mfma32h(wf[0], k2[0], fzero));
+                Zq = mfma32h(wf[1], q0[1], mfma32h(wf[0], q0[0], fzero));
+                // W_{it+1} = alpha_it W_it + XK_it^T E_it: the decay now (the
+                // products above took W_it as fp16 copies), the update next phase
+                const float a_it = sm.alpha[s0];
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) Wv[rb] = Wv[rb] * a_it;
+            } else {
+                Pp = mfma32h(wf[1], k2[1], mfma32h(wf[0], k2[0], bv));  // XK_{it+2} W_it + b_it
+                Zq = mfma32h(wf[1], q0[1], mfma32h(wf[0], q0[0], bv));  // XQ_it W_it + b_it
+            }
         }
         if (upd) {
             const uint32_t sb = __float_as_uint(sum4(st));
@@ -500,12 +589,14 @@ __device__ __forceinline__ void state_waves(Smem &sm, const Ctx &cx, int u, int 
 
 }  // namespace
 
+// LOSS: 0 squared error, 1 inner product; DECAY: weight decay wd on W.
+template <int LOSS, bool DECAY>
 __global__ __launch_bounds__(NT) void linear_prefill_mfma(
     int H, int L, float eps, const bf16_t *__restrict__ XQ, const bf16_t *__restrict__ XK,
     const bf16_t *__restrict__ XV, const float *__restrict__ eta, const float *__restrict__ theta,
     float eta_base, const float *__restrict__ W0, const float *__restrict__ b0, int w0_batched,
     const float *__restrict__ gamma, const float *__restrict__ beta, bf16_t *__restrict__ O,
-    float *W_out, float *b_out) {
+    float *W_out, float *b_out, float wd) {
     __shared__ Smem sm;
 
     const int tid = threadIdx.x;
@@ -523,11 +614,13 @@ __global__ __launch_bounds__(NT) void linear_prefill_mfma(
 
     if (w >= NCW + NSW) {
         if (theta)
-            prep_waves<true>(sm, w - NCW - NSW, g, c, lane, XQ + xbase, XK + xbase, XV + xbase,
-                             nullptr, theta + static_cast<size_t>(h) * D, eta_base, L, cx.iters);
+            prep_waves<true, LOSS, DECAY>(sm, w - NCW - NSW, g, c, lane, XQ + xbase, XK + xbase,
+                                          XV + xbase, nullptr, theta + static_cast<size_t>(h) * D,
+                                          eta_base, wd, L, cx.iters);
         else
-            prep_waves<false>(sm, w - NCW - NSW, g, c, lane, XQ + xbase, XK + xbase, XV + xbase,
-                              eta + static_cast<size_t>(seq) * L, nullptr, 0.f, L, cx.iters);
+            prep_waves<false, LOSS, DECAY>(sm, w - NCW - NSW, g, c, lane, XQ + xbase, XK + xbase,
+                                           XV + xbase, eta + static_cast<size_t>(seq) * L, nullptr,
+                                           0.f, wd, L, cx.iters);
         return;
     }
     // gamma = 1 and beta = 0 over the head (one feature per lane; same vote in every wave)
@@ -535,32 +628,39 @@ __global__ __launch_bounds__(NT) void linear_prefill_mfma(
 
     if (w < NCW) {
         if (ident)
-            chain_waves<true>(sm, cx, w, g, c, lane, gam_h, bet_h);
+            chain_waves<true, LOSS>(sm, cx, w, g, c, lane, gam_h, bet_h);
         else
-            chain_waves<false>(sm, cx, w, g, c, lane, gam_h, bet_h);
+            chain_waves<false, LOSS>(sm, cx, w, g, c, lane, gam_h, bet_h);
         return;
     }
     const size_t st = (w0_batched ? static_cast<size_t>(n) * H : 0) + static_cast<size_t>(h);
     float *Wd = W_out ? W_out + static_cast<size_t>(seq) * D * D : nullptr;
     float *bd = b_out ? b_out + static_cast<size_t>(seq) * D : nullptr;
     if (ident)
-        state_waves<true>(sm, cx, w - NCW, g, c, lane, W0 + st * D * D, b0 + st * D, gam_h, bet_h,
-                          O + xbase, Wd, bd);
+        state_waves<true, DECAY>(sm, cx, w - NCW, g, c, lane, W0 + st * D * D, b0 + st * D, gam_h,
+                                 bet_h, O + xbase, Wd, bd, wd);
     else
-        state_waves<false>(sm, cx, w - NCW, g, c, lane, W0 + st * D * D, b0 + st * D, gam_h, bet_h,
-                           O + xbase, Wd, bd);
+        state_waves<false, DECAY>(sm, cx, w - NCW, g, c, lane, W0 + st * D * D, b0 + st * D, gam_h,
+                                  bet_h, O + xbase, Wd, bd, wd);
 }
 
 bool linear_mfma_supported(const LinearArgs &a) { return a.io == 1 && a.d == 64 && a.mb == 16; }
 
+template <int LOSS, bool DECAY>
+static hipError_t launch_mfma_t(const LinearArgs &a, hipStream_t stream) {
+    hipLaunchKernelGGL((linear_prefill_mfma<LOSS, DECAY>), dim3(a.B * a.H), dim3(NT), 0, stream, a.H,
+                       a.L, a.eps, static_cast<const bf16_t *>(a.XQ),
+                       static_cast<const bf16_t *>(a.XK), static_cast<const bf16_t *>(a.XV), a.eta,
+                       a.theta, a.eta_base, a.W0, a.b0, a.w0_batched, a.gamma, a.beta,
+                       static_cast<bf16_t *>(a.O), a.W_out, a.b_out, a.wd);
+    return hipGetLastError();
+}
+
 hipError_t launch_linear_mfma(const LinearArgs &a, hipStream_t stream) {
     if (a.B * a.H == 0) return hipSuccess;
-    hipLaunchKernelGGL(linear_prefill_mfma, dim3(a.B * a.H), dim3(NT), 0, stream, a.H, a.L, a.eps,
-                       static_cast<const bf16_t *>(a.XQ), static_cast<const bf16_t *>(a.XK),
-                       static_cast<const bf16_t *>(a.XV), a.eta, a.theta, a.eta_base, a.W0, a.b0,
-                       a.w0_batched, a.gamma,
-                       a.beta, static_cast<bf16_t *>(a.O), a.W_out, a.b_out);
-    return hipGetLastError();
+    const bool decay = a.wd != 0.f;
+    if (a.loss == 1) return decay ? launch_mfma_t<1, true>(a, stream) : launch_mfma_t<1, false>(a, stream);
+    return decay ? launch_mfma_t<0, true>(a, stream) : launch_mfma_t<0, false>(a, stream);
 }
 
 }  // namespace ttt

@@ -12,6 +12,11 @@
 // Tokens past the end of a short last chunk carry eta = 0 and G = 0.
 // With the learning-rate gate (theta set) eta_t = eta_base * logistic(theta_h .
 // XK_t) is formed from the staged keys (the lryc.cn article §2.2 gate).
+// Modular-TTT options: loss = 1 takes G from the inner-product loss
+// -< XK + LN(Z), XV > (target XV, gh = -gamma * XV); weight decay lambda adds
+// lambda * W_c to every token's W gradient (W_c = chunk-start state), so
+//   Zbar_t = (1 - lambda * cum_t) XQ_t W_c + b - (M G)_t,  cum_t = sum_{s<=t} eta_s
+//   W     <- (1 - lambda * cum_last) W_c - (eta * XK)^T G.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -23,7 +28,8 @@ __global__ __launch_bounds__(256) void linear_prefill_valu(
     const TIO *__restrict__ XV, const float *__restrict__ eta, const float *__restrict__ theta,
     float eta_base, const float *__restrict__ W0, const float *__restrict__ b0, int w0_batched,
     const float *__restrict__ gamma,
-    const float *__restrict__ beta, TIO *__restrict__ O, float *W_out, float *b_out) {
+    const float *__restrict__ beta, TIO *__restrict__ O, float *W_out, float *b_out, int loss,
+    float wd) {
     constexpr int NT = 256, MB = 16, DP = D + 1;
     constexpr int R = MB * D / NT;  // outputs per thread in the row-by-column products
     constexpr int SS = NT / D;      // token stride between them
@@ -36,6 +42,7 @@ __global__ __launch_bounds__(256) void linear_prefill_valu(
     __shared__ float sT[MB * D], sZ[MB * D], sG[MB * D];
     __shared__ float sEta[MB], sM[MB * MB];
     __shared__ float sTh[D];
+    __shared__ float sDec[MB];  // 1 - lambda * cum_t (weight decay)
 
     const int tid = threadIdx.x;
     const long seq = blockIdx.x;
@@ -74,7 +81,7 @@ __global__ __launch_bounds__(256) void linear_prefill_valu(
             }
             sQ[s * DP + j] = q;
             sK[s * DP + j] = k;
-            sT[s * D + j] = v - k;
+            sT[s * D + j] = loss ? v : v - k;  // the loss's target
         }
         if (!theta && tid < MB) sEta[tid] = tid < len ? eta[ebase + t0 + tid] : 0.f;
         __syncthreads();
@@ -107,7 +114,15 @@ __global__ __launch_bounds__(256) void linear_prefill_valu(
                 z[e] = sZ[rrow * D + rl + 16 * e];
                 tau[e] = sT[rrow * D + rl + 16 * e];
             }
-            ln_l2_grad<16, E>(z, tau, gam, bet, 1.0f / D, eps, g);
+            if (loss)
+                ln_ip_grad<16, E>(z, tau, gam, 1.0f / D, eps, g);
+            else
+                ln_l2_grad<16, E>(z, tau, gam, bet, 1.0f / D, eps, g);
+            if (tid < MB) {  // decay factor of token tid's W_c term
+                float cum = 0.f;
+                for (int s = 0; s <= tid; ++s) cum += sEta[s];
+                sDec[tid] = 1.0f - wd * cum;
+            }
 #pragma unroll
             for (int e = 0; e < E; ++e) sG[rrow * D + rl + 16 * e] = rrow < len ? g[e] : 0.f;
 
@@ -118,16 +133,19 @@ __global__ __launch_bounds__(256) void linear_prefill_valu(
         }
         __syncthreads();
 
-        // 4. Zbar = XQ W + b - M G
+        // 4. Zbar = (1 - lambda cum) XQ W + b - M G
         {
             float acc[R];
 #pragma unroll
-            for (int r = 0; r < R; ++r) acc[r] = sb[cj];
+            for (int r = 0; r < R; ++r) acc[r] = 0.f;
             for (int i = 0; i < D; ++i) {
                 const float w = sW[i * D + cj];
 #pragma unroll
                 for (int r = 0; r < R; ++r) acc[r] += sQ[(cs0 + r * SS) * DP + i] * w;
             }
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                acc[r] = (wd != 0.f ? acc[r] * sDec[cs0 + r * SS] : acc[r]) + sb[cj];
             for (int s = 0; s < MB; ++s) {
                 const float gs = sG[s * D + cj];
 #pragma unroll
@@ -151,12 +169,13 @@ __global__ __launch_bounds__(256) void linear_prefill_valu(
                     io::store(O, xbase + static_cast<size_t>(t0 + rrow) * D + j, sQ[rrow * DP + j] + y[e]);
                 }
             }
+            const float dec = sDec[MB - 1];  // eta past the chunk's end is 0
             for (int e = tid; e < D * D; e += NT) {
                 const int i = e / D, j = e % D;
                 float acc = 0.f;
 #pragma unroll
                 for (int s = 0; s < MB; ++s) acc += sEta[s] * sK[s * DP + i] * sG[s * D + j];
-                sW[e] -= acc;
+                sW[e] = (wd != 0.f ? sW[e] * dec : sW[e]) - acc;
             }
             if (tid < D) {
                 float acc = 0.f;
@@ -180,7 +199,7 @@ static hipError_t launch_valu_t(const LinearArgs &a, hipStream_t stream) {
                        a.L, a.mb, a.eps, static_cast<const TIO *>(a.XQ),
                        static_cast<const TIO *>(a.XK), static_cast<const TIO *>(a.XV), a.eta,
                        a.theta, a.eta_base, a.W0, a.b0, a.w0_batched, a.gamma, a.beta, static_cast<TIO *>(a.O),
-                       a.W_out, a.b_out);
+                       a.W_out, a.b_out, a.loss, a.wd);
     return hipGetLastError();
 }
 

@@ -110,6 +110,43 @@ def ttt_linear_forward_gated(XQ, XK, XV, theta_lr, eta_base: float, W0, b0, ln_g
     return O, W_out, b_out
 
 
+def ttt_linear_forward_opts(XQ, XK, XV, eta, W0, b0, ln_gamma, ln_beta, inner_loss: str = "mse",
+                            weight_decay: float = 0.0, O=None, W_out=None, b_out=None,
+                            mb: int = 16, ln_eps: float = 1e-6, stream=None):
+    """TTT-Linear prefill with the inner loss ("mse" or "inner_product") and
+    weight decay on W as options; the rest as ttt_linear_forward."""
+    B, H, L, d = XQ.shape
+    io = _IO.get(XQ.dtype)
+    if io is None:
+        raise TypeError(f"XQ dtype {XQ.dtype} not supported")
+    loss = {"mse": _lib.TTT_LOSS_MSE, "inner_product": _lib.TTT_LOSS_INNER_PRODUCT}.get(inner_loss)
+    if loss is None:
+        raise ValueError(f"inner_loss {inner_loss!r} is not 'mse' or 'inner_product'")
+    batched = W0.dim() == 4
+    for t, n in ((XQ, "XQ"), (XK, "XK"), (XV, "XV")):
+        _need(t, n, (B, H, L, d), XQ.dtype)
+    _need(eta, "eta", (B, H, L), torch.float32)
+    _need(W0, "W0", ((B,) if batched else ()) + (H, d, d), torch.float32)
+    _need(b0, "b0", ((B,) if batched else ()) + (H, d), torch.float32)
+    _need(ln_gamma, "ln_gamma", (H, d), torch.float32)
+    _need(ln_beta, "ln_beta", (H, d), torch.float32)
+    O = torch.empty_like(XQ) if O is None else O
+    if W_out is None:
+        W_out = torch.empty((B, H, d, d), device=XQ.device, dtype=torch.float32)
+    if b_out is None:
+        b_out = torch.empty((B, H, d), device=XQ.device, dtype=torch.float32)
+    _need(O, "O", (B, H, L, d), XQ.dtype)
+    _need(W_out, "W_out", (B, H, d, d), torch.float32)
+    _need(b_out, "b_out", (B, H, d), torch.float32)
+    lib = _lib.load()
+    _lib.check(lib.ttt_linear_forward_opts(B, H, L, d, mb, io, ln_eps, _ptr(XQ), _ptr(XK), _ptr(XV),
+                                           _ptr(eta), _ptr(W0), _ptr(b0), int(batched),
+                                           _ptr(ln_gamma), _ptr(ln_beta), loss,
+                                           float(weight_decay), _ptr(O), _ptr(W_out),
+                                           _ptr(b_out), _stream(stream)))
+    return O, W_out, b_out
+
+
 def ttt_eta_gate(XK, theta_lr, eta_base: float, eta=None, stream=None):
     """eta [B,H,L] = eta_base * logistic(theta_lr[h] . XK[n,h,t])."""
     B, H, L, d = XK.shape

@@ -209,6 +209,24 @@ def test_linear_forward_gated_validation(lib):
     assert _gated(lib, B=0) == _lib.TTT_OK
 
 
+def _opts(lib, loss=0, wd=0.0, B=1, d=64):
+    p = [FAKE + i * (1 << 20) for i in range(8)]
+    return lib.ttt_linear_forward_opts(B, 1, 16, d, 16, 1, 1e-6, p[0], p[1], p[2], p[3], p[4],
+                                       p[5], 0, p[6], p[7], loss, wd, FAKE + 11 * (1 << 20),
+                                       FAKE + 9 * (1 << 20), FAKE + 10 * (1 << 20), None)
+
+
+def test_linear_forward_opts_validation(lib):
+    assert _opts(lib, loss=2) == _lib.TTT_E_SHAPE
+    assert "inner_loss" in lib.ttt_last_error().decode()
+    assert _opts(lib, loss=-1) == _lib.TTT_E_SHAPE
+    for bad in (-0.1, float("inf"), float("nan")):
+        assert _opts(lib, wd=bad) == _lib.TTT_E_SHAPE
+        assert "weight_decay" in lib.ttt_last_error().decode()
+    assert _opts(lib, d=32) == _lib.TTT_E_SHAPE
+    assert _opts(lib, loss=1, wd=0.5, B=0) == _lib.TTT_OK
+
+
 def _gate(lib, B=2, H=3, L=40, d=64, io=1, xk=FAKE, th=FAKE + (1 << 20), eta_base=0.5,
           eta=FAKE + 2 * (1 << 20)):
     return lib.ttt_eta_gate(B, H, L, d, io, xk, th, eta_base, eta, None)

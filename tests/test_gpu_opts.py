@@ -1,0 +1,86 @@
+"""GPU parity of ttt_linear_forward_opts (the Modular-TTT options: inner
+loss and weight decay on W) through the C ABI against the fp64 oracle's
+linear_forward_opts on the same inputs. bf16 storage with d = 64 and b = 16
+runs the MFMA prefill (both layer-norm paths: general gamma/beta and
+gamma = 1, beta = 0); the other shapes run the fp32 VALU prefill."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from test_sequence_layer_ttt_amd import gen, ttt
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("O", "W_out", "b_out")
+
+
+def _run(x, loss, wd, mb):
+    dt = P.io_dtype(x.io)
+    O, W, b = ttt.ttt_linear_forward_opts(P.dev(x.XQ, dt), P.dev(x.XK, dt), P.dev(x.XV, dt),
+                                          P.dev(x.eta), P.dev(x.W0), P.dev(x.b0), P.dev(x.gamma),
+                                          P.dev(x.beta), inner_loss=loss, weight_decay=wd, mb=mb,
+                                          ln_eps=x.eps)
+    torch.cuda.synchronize()
+    return P.to_np(O), P.to_np(W), P.to_np(b)
+
+
+def _ref(x, loss, wd, mb):
+    return oracle.linear_forward_opts(x.XQ, x.XK, x.XV, x.eta, x.W0, x.b0, x.gamma, x.beta, x.eps,
+                                      mb=mb, loss=loss, weight_decay=wd)
+
+
+@pytest.mark.parametrize("loss", ["mse", "inner_product"])
+@pytest.mark.parametrize("wd", [0.0, 0.5])
+@pytest.mark.parametrize("io,d,mb,L", [("f32", 16, 16, 64), ("f32", 64, 16, 16 * 5 + 3),
+                                       ("bf16", 64, 16, 16 * 6 + 5), ("bf16", 64, 5, 23),
+                                       ("f32", 16, 1, 9)])
+def test_options(loss, wd, io, d, mb, L):
+    x = gen.make_linear(600 + d + L + mb, 2, 3, L, d, io=io, ln_random=True, b_random=True,
+                        w_std=0.3)
+    got, ref = _run(x, loss, wd, mb), _ref(x, loss, wd, mb)
+    err = P.errors(got, ref, x.B * x.H, NAMES)
+    print(f"[parity] opts {loss} wd={wd} {io} d{d} mb{mb} L{L}: "
+          + " ".join(f"{k}={v:.2e}" for k, v in err.items()), flush=True)
+    assert max(err.values()) <= P.TOL[io], err
+
+
+@pytest.mark.parametrize("loss", ["mse", "inner_product"])
+@pytest.mark.parametrize("wd", [0.0, 0.5])
+def test_options_mfma_identity_layer_norm(loss, wd):
+    """gamma = 1, beta = 0 takes the MFMA kernel's three-sum layer-norm path."""
+    x = gen.make_linear(650, 2, 3, 16 * 9 + 7, 64, io="bf16", b_random=True, w_std=0.3)
+    got, ref = _run(x, loss, wd, 16), _ref(x, loss, wd, 16)
+    err = P.errors(got, ref, x.B * x.H, NAMES)
+    print(f"[parity] opts mfma ident {loss} wd={wd}: "
+          + " ".join(f"{k}={v:.2e}" for k, v in err.items()), flush=True)
+    assert max(err.values()) <= P.TOL["bf16"], err
+
+
+def test_defaults_run_the_plain_kernels():
+    """TTT_LOSS_MSE with no decay is ttt_linear_forward (same kernel, same bits)."""
+    x = gen.make_workload(3, L=16 * 9 + 3, B=2, H=3)
+    a = _run(x, "mse", 0.0, 16)
+    b = P.linear_gpu(x)
+    for p, q in zip(a, b):
+        assert np.array_equal(p, q)
+
+
+def test_workload3_shape_sampled_heads():
+    """Workload 3's shape (B=2, H=32, L=8192, bf16) with the inner-product loss
+    and weight decay 0.5; the oracle checks batch 1, heads 5 and 30."""
+    full = gen.make_workload(3)
+    got = _run(full, "inner_product", 0.5, 16)
+    hs = [5, 30]
+    sl = lambda a: np.ascontiguousarray(a[1:2, hs])
+    ref = oracle.linear_forward_opts(sl(full.XQ), sl(full.XK), sl(full.XV), sl(full.eta),
+                                     np.ascontiguousarray(full.W0[hs]),
+                                     np.ascontiguousarray(full.b0[hs]),
+                                     np.ascontiguousarray(full.gamma[hs]),
+                                     np.ascontiguousarray(full.beta[hs]), full.eps, mb=16,
+                                     loss="inner_product", weight_decay=0.5)
+    err = P.errors(tuple(sl(g) for g in got), ref, 2, NAMES)
+    print("[parity] opts workload3 shape: " + " ".join(f"{k}={v:.2e}" for k, v in err.items()),
+          flush=True)
+    assert max(err.values()) <= P.TOL["bf16"], err
