@@ -13,6 +13,8 @@ Other workloads of the same hot path (--workload):
   5d  TTT-Linear decode: one b=1 step on 64 x 32 states (roofline: state bytes)
   5r  TTT-Linear decode: 1024 b=1 steps on 64 x 32 states in one call, states
       resident in registers (roofline: fp32 vector ALU)
+  5m  the same 1024 tokens under the mini-batch rule (b = 16) through
+      ttt_decode_steps_mb: both states resident (roofline: fp32 vector ALU)
   3b  TTT-Linear backward (ttt_linear_backward) on workload 3's shapes
       (roofline: fp32 vector ALU)
   3g  workload 3 through ttt_linear_forward_gated: eta from the learning-rate
@@ -119,7 +121,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="3", choices=["3", "2", "5p", "4", "5d", "5r", "3b", "3g", "3gb", "3o"])
+    ap.add_argument("--workload", default="3", choices=["3", "2", "5p", "4", "5d", "5r", "5m", "3b", "3g", "3gb", "3o"])
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -152,6 +154,8 @@ def main():
         return bench_decode(args)
     if args.workload == "5r":
         return bench_decode_steps(args)
+    if args.workload == "5m":
+        return bench_decode_steps(args, mb=16)
     if args.workload == "3b":
         return bench_backward(args)
     if args.workload == "3gb":
@@ -394,11 +398,13 @@ def bench_decode(args):
                    "io": "bf16", "state": "fp32", "parallelism": "none (1 GPU)"}, roof, extra)
 
 
-def bench_decode_steps(args):
+def bench_decode_steps(args, mb: int = 1):
     """Workload 5's 1024 b=1 decode steps on 64 x 32 states in one
     ttt_decode_steps call (states resident in registers), each state started
     from the B=1, L=32768 prefill's final state. A bench step is one call;
-    successive calls continue from the state the previous one left."""
+    successive calls continue from the state the previous one left. With
+    mb > 1 the same tokens go through ttt_decode_steps_mb (mini-batch rule,
+    chunk-start state as a second resident copy)."""
     import numpy as np
     import torch
     from test_sequence_layer_ttt_amd import gen, ttt
@@ -416,8 +422,13 @@ def bench_decode_steps(args):
     g, be = T(pre.gamma), T(pre.beta)
     o = torch.empty((S, B, H, d), device=dev, dtype=bf)
     stream = torch.cuda.current_stream()
-    step = lambda: ttt.ttt_decode_steps(xq, xk, xv, et, W, b, g, be, o=o, ln_eps=pre.eps,
-                                        stream=stream)
+    if mb == 1:
+        step = lambda: ttt.ttt_decode_steps(xq, xk, xv, et, W, b, g, be, o=o, ln_eps=pre.eps,
+                                            stream=stream)
+    else:  # 1024 steps are 64 whole chunks, so every call starts a chunk (pos = 0)
+        Wc, bc = torch.empty_like(W), torch.empty_like(b)
+        step = lambda: ttt.ttt_decode_steps_mb(xq, xk, xv, et, Wc, bc, W, b, g, be, mb=mb, pos=0,
+                                               o=o, ln_eps=pre.eps, stream=stream)
     wall, kern = _timed(step, stream, args.warmup, args.steps)
     fl = S * alg_flops_decode_step(B, H, d)
     roof = {"bound": "alu", "achieved": fl / kern / 1e12, "peak": FP32_VECTOR_PEAK_TFLOPS,
@@ -426,7 +437,7 @@ def bench_decode_steps(args):
             "alg_flops_per_launch": fl, "hbm_bytes_per_launch": S * B * H * (3 * d * 2 + 4 + d * 2)
             + 2 * B * H * (d * d + d) * 4}
     extra = {}
-    if not args.no_cpu_baseline:
+    if mb == 1 and not args.no_cpu_baseline:
         import oracle
         nt = cpu_threads()
         Wn = np.broadcast_to(Wp[0].cpu().numpy(), (B, H, d, d)).astype(np.float64)
@@ -441,11 +452,26 @@ def bench_decode_steps(args):
                                  "kind": "oracle",
                                  "sample": f"{ns} steps on all {B}x{H} states, fp64, {nt} threads, "
                                            f"{tc:.2f} s"}
-    _line("TTT-Linear decode tokens/s (64 sequences x 32 heads, b=1, 1024 steps per call)",
+    if mb > 1 and not args.no_cpu_baseline:
+        # the oracle's mini-batch rule over one chunk of mb tokens on all states
+        import oracle
+        nt = cpu_threads()
+        Wn = np.broadcast_to(Wp[0].cpu().numpy(), (B, H, d, d)).astype(np.float64)
+        bn = np.broadcast_to(bp[0].cpu().numpy(), (B, H, d)).astype(np.float64)
+        tok = lambda a: np.ascontiguousarray(np.moveaxis(a[:mb], 0, 2))  # [T,B,H,..] -> [B,H,T,..]
+        t1 = time.perf_counter()
+        oracle.linear_forward(tok(dec.XQ), tok(dec.XK), tok(dec.XV), tok(dec.eta), Wn, bn,
+                              pre.gamma, pre.beta, pre.eps, mb=mb, w0_batched=True, nthreads=nt)
+        tc = time.perf_counter() - t1
+        extra["cpu_baseline"] = {"value": B * mb / tc, "unit": "tokens/s", "cores": nt,
+                                 "kind": "oracle",
+                                 "sample": f"one chunk of {mb} tokens on all {B}x{H} states "
+                                           f"(mini-batch rule), fp64, {nt} threads, {tc:.2f} s"}
+    _line(f"TTT-Linear decode tokens/s (64 sequences x 32 heads, b={mb}, 1024 steps per call)",
           B * S / wall, args, wall, "bf16",
-          {"workload": "ttt_linear_decode_steps_bf16_T1024_B64_H32_d64", "T": S, "B": B, "H": H,
-           "d": d, "io": "bf16", "state": "fp32, resident in registers",
-           "parallelism": "none (1 GPU)"}, roof, extra)
+          {"workload": "ttt_linear_decode_steps_bf16_T1024_B64_H32_d64" + (f"_mb{mb}" if mb > 1 else ""),
+           "T": S, "B": B, "H": H, "d": d, "mini_batch": mb, "io": "bf16",
+           "state": "fp32, resident in registers", "parallelism": "none (1 GPU)"}, roof, extra)
 
 
 def bench_backward(args):

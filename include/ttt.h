@@ -253,6 +253,34 @@ int ttt_decode_steps(int T, int B, int H, int d, int io, float ln_eps, const voi
                      hipStream_t stream);
 
 /*
+ * Mini-batch decode: T consecutive tokens under the mini-batch rule of [D]
+ * §4.1 with b = mb, so that a prefill followed by any sequence of these calls
+ * gives the same outputs and state as one prefill over the whole sequence
+ * (chunks aligned at its first token). The cache of [D] §5.2 then holds two
+ * states: the current one (W, b) and the start state of the current chunk
+ * (W_chunk, b_chunk), at which every token of the chunk takes its gradient:
+ *   at a chunk's first token   W_chunk, b_chunk <- W, b
+ *   z = xk W_chunk + b_chunk;  G = lnbwd(z, xv - xk)
+ *   W <- W - eta xk^T G;  b <- b - eta G;  o = xq + LN(xq W + b)
+ *   mb  : 1 <= mb <= 16 (mb = 1 is ttt_decode_steps).
+ *   pos : 0 <= pos < mb, the position of the first step within its chunk
+ *         (the number of the chunk's tokens already processed); the next
+ *         call continues at (pos + T) mod mb.
+ *   W_chunk, b_chunk : [B,H,d,d], [B,H,d] fp32, read when pos > 0, written
+ *         with the start state of the chunk of the last step (so a call
+ *         ending inside a chunk can be continued). Required when mb > 1,
+ *         ignored when mb = 1; must not overlap any other argument.
+ * Every other argument, the layouts and the errors as ttt_decode_steps, plus
+ * TTT_E_SHAPE for mb or pos out of range. d = 64 keeps both states in
+ * registers for all T steps; d = 16 runs one launch per step.
+ */
+int ttt_decode_steps_mb(int T, int B, int H, int d, int io, float ln_eps, int mb, int pos,
+                        const void *xq, const void *xk, const void *xv, const float *eta,
+                        float *W_chunk, float *b_chunk, float *W, float *b,
+                        const float *ln_gamma, const float *ln_beta, void *o,
+                        hipStream_t stream);
+
+/*
  * The fused layer-norm + L2 backward step on its own ([D] §4.2), row-wise:
  *   G[r] = d/dz [ 1/2 || LN_{gamma,beta}(z) - target[r] ||^2 ] at z = Z[r].
  *   rows >= 0; d in {16, 32, 64}. Z, target, G : [rows,d] fp32;

@@ -55,6 +55,7 @@ def load():
     lib.ttt_mlp_forward.argtypes = [_i] * 6 + [_f] + [_P] * 8 + [_i] + [_P] * 7 + [_P]
     lib.ttt_decode_step.argtypes = [_i] * 4 + [_f] + [_P] * 9 + [_P]
     lib.ttt_decode_steps.argtypes = [_i] * 5 + [_f] + [_P] * 9 + [_P]
+    lib.ttt_decode_steps_mb.argtypes = [_i] * 5 + [_f] + [_i] * 2 + [_P] * 11 + [_P]
     lib.ttt_linear_backward.argtypes = ([_i] * 6 + [_f] + [_P] * 6 + [_i] + [_P] * 14
                                         + [ctypes.c_size_t, _P])
     lib.ttt_linear_backward_workspace.argtypes = [_i] * 5 + [ctypes.POINTER(ctypes.c_size_t)]
@@ -62,7 +63,7 @@ def load():
     for name in ("ttt_linear_forward", "ttt_mlp_forward", "ttt_decode_step", "ttt_decode_steps",
                  "ttt_linear_backward", "ttt_linear_backward_workspace", "ttt_ln_l2_bwd",
                  "ttt_linear_forward_gated", "ttt_eta_gate", "ttt_eta_gate_backward",
-                 "ttt_linear_forward_opts",
+                 "ttt_linear_forward_opts", "ttt_decode_steps_mb",
                  "ttt_version"):
         getattr(lib, name).restype = _i
     lib.ttt_last_error.restype = ctypes.c_char_p

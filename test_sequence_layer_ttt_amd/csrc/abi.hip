@@ -399,14 +399,23 @@ int ttt_decode_step(int B, int H, int d, int io, float ln_eps, const void *xq,
     return launched(ttt::launch_decode(a, stream));
 }
 
-int ttt_decode_steps(int T, int B, int H, int d, int io, float ln_eps, const void *xq,
-                     const void *xk, const void *xv, const float *eta, float *W, float *b,
-                     const float *ln_gamma, const float *ln_beta, void *o,
-                     hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// T decode steps; mb = 1 is b = 1 TTT (Wc, bc unused), mb > 1 the mini-batch
+// rule with the chunk-start state in (Wc, bc) and the first step at position
+// pos of its chunk.
+int decode_steps(int T, int B, int H, int d, int io, float ln_eps, int mb, int pos,
+                 const void *xq, const void *xk, const void *xv, const float *eta, float *Wc,
+                 float *bc, float *W, float *b, const float *ln_gamma, const float *ln_beta,
+                 void *o, hipStream_t stream) {
     int st;
     if (T < 0) return fail(TTT_E_SHAPE, "T = %d is negative", T);
-    if ((st = check_common(B, H, 1, 1, io)) || (st = check_eps(ln_eps))) return st;
+    if ((st = check_common(B, H, 1, mb, io)) || (st = check_eps(ln_eps))) return st;
+    if (pos < 0 || pos >= mb) return fail(TTT_E_SHAPE, "pos = %d not in [0, mb = %d)", pos, mb);
     if (d != 16 && d != 64) return fail(TTT_E_SHAPE, "d = %d not in {16, 64}", d);
+    const bool ch = mb > 1;
     const size_t es = io == TTT_BF16 ? 2 : 4;
     size_t xb, eb, wb, bb;
     if (!nbytes(&xb, {size_t(T), size_t(B), size_t(H), size_t(d), es}) ||
@@ -419,12 +428,21 @@ int ttt_decode_steps(int T, int B, int H, int d, int io, float ln_eps, const voi
     const Buf in[] = {{xq, xb, "xq", false, ea}, {xk, xb, "xk", false, ea},
                       {xv, xb, "xv", false, ea}, {eta, eb, "eta", false, 4},
                       {ln_gamma, pb, "ln_gamma", false, 4}, {ln_beta, pb, "ln_beta", false, 4}};
-    const Buf out[] = {{W, wb, "W", false, 4}, {b, bb, "b", false, 4}, {o, xb, "o", false, ea}};
-    if ((st = check_bufs(in, 6)) || (st = check_bufs(out, 3))) return st;
-    if ((st = check_alias(out, 3, in, 6, nullptr))) return st;
+    const Buf out[] = {{W, wb, "W", false, 4}, {b, bb, "b", false, 4}, {o, xb, "o", false, ea},
+                       {ch ? Wc : nullptr, ch ? wb : 0, "W_chunk", false, 4},
+                       {ch ? bc : nullptr, ch ? bb : 0, "b_chunk", false, 4}};
+    const int nout = ch ? 5 : 3;
+    if ((st = check_bufs(in, 6)) || (st = check_bufs(out, nout))) return st;
+    if ((st = check_alias(out, nout, in, 6, nullptr))) return st;
     if (B * H == 0 || T == 0) return ok();
     if (ttt::decode_steps_resident(d)) {
         ttt::DecodeArgs a{B, H, d, io, ln_eps, xq, xk, xv, eta, W, b, ln_gamma, ln_beta, o};
+        if (ch) {
+            a.Wc = Wc;
+            a.bc = bc;
+            a.mb = mb;
+            a.pos = pos;
+        }
         return launched(ttt::launch_decode_steps(a, T, stream));
     }
     // other d: one launch of the single-step kernel per step
@@ -435,9 +453,35 @@ int ttt_decode_steps(int T, int B, int H, int d, int io, float ln_eps, const voi
                           static_cast<const char *>(xq) + t * step, static_cast<const char *>(xk) + t * step,
                           static_cast<const char *>(xv) + t * step, eta + t * estep, W, b, ln_gamma,
                           ln_beta, static_cast<char *>(o) + t * step};
+        if (ch) {
+            a.Wc = Wc;
+            a.bc = bc;
+            a.mode = (pos + t) % mb == 0 ? 1 : 2;
+        }
         if ((st = launched(ttt::launch_decode(a, stream)))) return st;
     }
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int ttt_decode_steps(int T, int B, int H, int d, int io, float ln_eps, const void *xq,
+                     const void *xk, const void *xv, const float *eta, float *W, float *b,
+                     const float *ln_gamma, const float *ln_beta, void *o,
+                     hipStream_t stream) {
+    return decode_steps(T, B, H, d, io, ln_eps, 1, 0, xq, xk, xv, eta, nullptr, nullptr, W, b,
+                        ln_gamma, ln_beta, o, stream);
+}
+
+int ttt_decode_steps_mb(int T, int B, int H, int d, int io, float ln_eps, int mb, int pos,
+                        const void *xq, const void *xk, const void *xv, const float *eta,
+                        float *W_chunk, float *b_chunk, float *W, float *b,
+                        const float *ln_gamma, const float *ln_beta, void *o,
+                        hipStream_t stream) {
+    return decode_steps(T, B, H, d, io, ln_eps, mb, pos, xq, xk, xv, eta, W_chunk, b_chunk, W, b,
+                        ln_gamma, ln_beta, o, stream);
 }
 
 }  // extern "C"

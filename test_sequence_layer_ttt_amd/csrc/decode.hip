@@ -12,6 +12,12 @@
 // One 256-thread workgroup per state. Thread (p, j) owns column j, rows
 // p*RPT .. p*RPT+RPT-1 of W; for fixed rows a wave reads a contiguous row
 // segment (coalesced). Column partials meet in LDS.
+//
+// Mini-batch decode (b > 1, mode != 0): the gradient is taken at the
+// chunk-start state (Wc, bc) instead of (W, b); mode 1 starts a chunk (the
+// current state is copied to Wc, bc first, and z uses it), mode 2 reads Wc,
+// bc. The output identity still uses the current W: xq W' + b' =
+// (xq W + b) - eta (xq . xk + 1) G.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -22,7 +28,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     int H, float eps, const TIO *__restrict__ xq, const TIO *__restrict__ xk,
     const TIO *__restrict__ xv, const float *__restrict__ eta, float *__restrict__ W,
     float *__restrict__ b, const float *__restrict__ gamma, const float *__restrict__ beta,
-    TIO *__restrict__ o) {
+    TIO *__restrict__ o, float *__restrict__ Wc, float *__restrict__ bc, int mode) {
     constexpr int NT = 256, P = NT / D, RPT = D / P, E = D / 16;
     using io = io_traits<TIO>;
     __shared__ float sq[D], sk[D], sG[D];
@@ -39,15 +45,23 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         sq[tid] = io::load(xq, static_cast<size_t>(seq) * D + tid);
         sk[tid] = io::load(xk, static_cast<size_t>(seq) * D + tid);
     }
-    float w[RPT];
+    float w[RPT], wz[RPT];  // current state; state the gradient is taken at
+    float *Wcs = Wc ? Wc + static_cast<size_t>(seq) * D * D : nullptr;
 #pragma unroll
     for (int r = 0; r < RPT; ++r) w[r] = Ws[static_cast<size_t>(p * RPT + r) * D + j];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r)
+        wz[r] = mode == 2 ? Wcs[static_cast<size_t>(p * RPT + r) * D + j] : w[r];
+    if (mode == 1) {  // a chunk starts here: its start state is the current one
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) Wcs[static_cast<size_t>(p * RPT + r) * D + j] = w[r];
+    }
     __syncthreads();
 
     float pz = 0.f, pq = 0.f;
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
-        pz += sk[p * RPT + r] * w[r];
+        pz += sk[p * RPT + r] * wz[r];
         pq += sq[p * RPT + r] * w[r];
     }
     sPz[p * D + j] = pz;
@@ -68,7 +82,9 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
                 qs += sPq[pp * D + jj];
             }
             bb[e] = b[static_cast<size_t>(seq) * D + jj];
-            z[e] = zs + bb[e];
+            const size_t bi = static_cast<size_t>(seq) * D + jj;
+            z[e] = zs + (mode == 2 ? bc[bi] : bb[e]);
+            if (mode == 1) bc[bi] = bb[e];
             q[e] = qs;
             tau[e] = io::load(xv, static_cast<size_t>(seq) * D + jj) - sk[jj];
             gm[e] = gamma[static_cast<size_t>(h) * D + jj];
@@ -103,7 +119,7 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((decode_step_kernel<D, TIO>), dim3(a.B * a.H), dim3(256), 0, stream, a.H,
                        a.eps, static_cast<const TIO *>(a.xq), static_cast<const TIO *>(a.xk),
                        static_cast<const TIO *>(a.xv), a.eta, a.W, a.b, a.gamma, a.beta,
-                       static_cast<TIO *>(a.o));
+                       static_cast<TIO *>(a.o), a.Wc, a.bc, a.mode);
     return hipGetLastError();
 }
 

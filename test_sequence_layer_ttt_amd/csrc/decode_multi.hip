@@ -15,6 +15,12 @@
 // layer-norm sums over the 64 features are wave reductions (DPP row sums,
 // then row swaps). HBM carries only the per-step inputs and outputs; W and b
 // are read once at the start and written once at the end.
+//
+// Mini-batch decode (CH, b = mb > 1): the tokens of a chunk take their
+// gradient at the chunk-start state, held as a second register copy (wc, bc)
+// that is refreshed from (W, b) when a chunk starts; z uses the copy, the
+// output and the update use the current state, so the identity above still
+// holds with W the current state.
 #include "common.hpp"
 #include "launch.hpp"
 #include "tile.hpp"
@@ -113,18 +119,29 @@ __device__ __forceinline__ void axpy_bcast(const float (&x)[4], float e, float (
 }
 using Rows16 = std::make_integer_sequence<int, 16>;
 
-template <typename TIO, bool IDENT>
+template <typename TIO, bool IDENT, bool CH>
 __device__ __forceinline__ void run_steps(int T, int BH, float eps, int seq, int j,
                                           const TIO *__restrict__ xq, const TIO *__restrict__ xk,
                                           const TIO *__restrict__ xv, const float *__restrict__ eta,
                                           float *__restrict__ Ws, float *__restrict__ bs, float gm,
-                                          float bt, TIO *__restrict__ o) {
+                                          float bt, TIO *__restrict__ o, int mb, int pos,
+                                          float *__restrict__ Wcs, float *__restrict__ bcs) {
     using io = io_traits<TIO>;
     constexpr float inv_d = 1.0f / DM;
     float w[DM];  // W[i][j], i = 0 .. 63
 #pragma unroll
     for (int i = 0; i < DM; ++i) w[i] = Ws[i * DM + j];
     float bj = bs[j];
+    float wc[DM];  // CH: chunk-start W[i][j] (read when the first step continues a chunk)
+    float bcj = 0.f;
+    if constexpr (CH) {
+        if (pos > 0) {
+#pragma unroll
+            for (int i = 0; i < DM; ++i) wc[i] = Wcs[i * DM + j];
+            bcj = bcs[j];
+        }
+    }
+    int k = pos;  // CH: position of step t within its chunk
     // per-head constants of the general layer-norm backward
     float Sg2 = static_cast<float>(DM), Sgb = 0.f;
     if constexpr (!IDENT) {
@@ -158,10 +175,22 @@ __device__ __forceinline__ void run_steps(int T, int BH, float eps, int seq, int
         const float tau = xvj - xkj;
         const float qk = wave_sum(xqj * xkj);
 
-        // (xq W)_j and z_j = (xk W + b)_j
-        float p0 = 0.f, p1 = 0.f, z0 = bj, z1 = 0.f;
+        // (xq W)_j and z_j = (xk W + b)_j, W, b at the chunk start for z
+        float p0 = 0.f, p1 = 0.f, z0, z1 = 0.f;
         dot_bcast(qb, w, p0, p1, Rows16{});
-        dot_bcast(kb, w, z0, z1, Rows16{});
+        if constexpr (CH) {
+            if (k == 0) {  // a chunk starts: its start state is the current one
+#pragma unroll
+                for (int i = 0; i < DM; ++i) wc[i] = w[i];
+                bcj = bj;
+            }
+            z0 = bcj;
+            dot_bcast(kb, wc, z0, z1, Rows16{});
+            k = (k + 1 == mb) ? 0 : k + 1;
+        } else {
+            z0 = bj;
+            dot_bcast(kb, w, z0, z1, Rows16{});
+        }
         const float z = z0 + z1, p = p0 + p1;
 
         // E_j = -eta * d/dz_j [ 1/2 || LN(z) - tau ||^2 ]
@@ -204,24 +233,42 @@ __device__ __forceinline__ void run_steps(int T, int BH, float eps, int seq, int
 #pragma unroll
     for (int i = 0; i < DM; ++i) Ws[i * DM + j] = w[i];
     bs[j] = bj;
+    if constexpr (CH) {  // the start state of the chunk the last step belongs to
+#pragma unroll
+        for (int i = 0; i < DM; ++i) Wcs[i * DM + j] = wc[i];
+        bcs[j] = bcj;
+    }
 }
 
-template <typename TIO>
+template <typename TIO, bool CH>
 __global__ __launch_bounds__(64) void decode_steps_kernel(
     int T, int BH, int H, float eps, const TIO *__restrict__ xq, const TIO *__restrict__ xk,
     const TIO *__restrict__ xv, const float *__restrict__ eta, float *__restrict__ W,
     float *__restrict__ b, const float *__restrict__ gamma, const float *__restrict__ beta,
-    TIO *__restrict__ o) {
+    TIO *__restrict__ o, int mb, int pos, float *__restrict__ Wc, float *__restrict__ bc) {
     const int j = threadIdx.x;
     const int seq = blockIdx.x;
     const int h = seq % H;
     float *Ws = W + static_cast<size_t>(seq) * DM * DM;
     float *bs = b + static_cast<size_t>(seq) * DM;
+    float *Wcs = CH ? Wc + static_cast<size_t>(seq) * DM * DM : nullptr;
+    float *bcs = CH ? bc + static_cast<size_t>(seq) * DM : nullptr;
     const float gm = gamma[h * DM + j], bt = beta[h * DM + j];
     if (__all(gm == 1.0f && bt == 0.0f))
-        run_steps<TIO, true>(T, BH, eps, seq, j, xq, xk, xv, eta, Ws, bs, gm, bt, o);
+        run_steps<TIO, true, CH>(T, BH, eps, seq, j, xq, xk, xv, eta, Ws, bs, gm, bt, o, mb, pos,
+                                 Wcs, bcs);
     else
-        run_steps<TIO, false>(T, BH, eps, seq, j, xq, xk, xv, eta, Ws, bs, gm, bt, o);
+        run_steps<TIO, false, CH>(T, BH, eps, seq, j, xq, xk, xv, eta, Ws, bs, gm, bt, o, mb, pos,
+                                  Wcs, bcs);
+}
+
+template <typename TIO, bool CH>
+hipError_t launch_steps_t(const DecodeArgs &a, int T, hipStream_t stream) {
+    hipLaunchKernelGGL((decode_steps_kernel<TIO, CH>), dim3(a.B * a.H), dim3(64), 0, stream, T,
+                       a.B * a.H, a.H, a.eps, static_cast<const TIO *>(a.xq),
+                       static_cast<const TIO *>(a.xk), static_cast<const TIO *>(a.xv), a.eta, a.W,
+                       a.b, a.gamma, a.beta, static_cast<TIO *>(a.o), a.mb, a.pos, a.Wc, a.bc);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -230,18 +277,9 @@ bool decode_steps_resident(int d) { return d == DM; }
 
 hipError_t launch_decode_steps(const DecodeArgs &a, int T, hipStream_t stream) {
     if (a.B * a.H == 0 || T == 0) return hipSuccess;
-    const int BH = a.B * a.H;
-    if (a.io)
-        hipLaunchKernelGGL(decode_steps_kernel<bf16_t>, dim3(BH), dim3(64), 0, stream, T, BH, a.H,
-                           a.eps, static_cast<const bf16_t *>(a.xq), static_cast<const bf16_t *>(a.xk),
-                           static_cast<const bf16_t *>(a.xv), a.eta, a.W, a.b, a.gamma, a.beta,
-                           static_cast<bf16_t *>(a.o));
-    else
-        hipLaunchKernelGGL(decode_steps_kernel<float>, dim3(BH), dim3(64), 0, stream, T, BH, a.H,
-                           a.eps, static_cast<const float *>(a.xq), static_cast<const float *>(a.xk),
-                           static_cast<const float *>(a.xv), a.eta, a.W, a.b, a.gamma, a.beta,
-                           static_cast<float *>(a.o));
-    return hipGetLastError();
+    const bool ch = a.Wc != nullptr;  // mini-batch decode
+    if (a.io) return ch ? launch_steps_t<bf16_t, true>(a, T, stream) : launch_steps_t<bf16_t, false>(a, T, stream);
+    return ch ? launch_steps_t<float, true>(a, T, stream) : launch_steps_t<float, false>(a, T, stream);
 }
 
 }  // namespace ttt

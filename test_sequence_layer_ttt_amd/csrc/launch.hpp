@@ -52,6 +52,12 @@ struct DecodeArgs {
     float *W, *b;
     const float *gamma, *beta;
     void *o;
+    // mini-batch decode (b = mb > 1): every token of a chunk takes its
+    // gradient at the chunk-start state (Wc, bc). Single-step kernel: mode
+    // 1 starts a chunk (Wc, bc <- W, b first), mode 2 continues one; multi-
+    // step kernel: pos = position of the first step within its chunk.
+    float *Wc = nullptr, *bc = nullptr;
+    int mode = 0, mb = 1, pos = 0;
 };
 
 hipError_t launch_ln_l2_bwd(int rows, int d, const float *Z, const float *T, const float *gamma,

@@ -323,6 +323,37 @@ def ttt_decode_steps(xq, xk, xv, eta, W, b, ln_gamma, ln_beta, o=None, ln_eps: f
     return o
 
 
+def ttt_decode_steps_mb(xq, xk, xv, eta, W_chunk, b_chunk, W, b, ln_gamma, ln_beta, mb: int,
+                        pos: int = 0, o=None, ln_eps: float = 1e-6, stream=None):
+    """T consecutive tokens under the mini-batch rule with b = mb: every token
+    of a chunk takes its gradient at the chunk-start state (W_chunk, b_chunk),
+    and the current state (W, b) is updated token by token; pos is the first
+    step's position within its chunk. All four state tensors are updated in
+    place. Shapes as ttt_decode_steps. Returns o."""
+    T, B, H, d = xq.shape
+    io = _IO.get(xq.dtype)
+    if io is None:
+        raise TypeError(f"xq dtype {xq.dtype} not supported")
+    for t, n in ((xq, "xq"), (xk, "xk"), (xv, "xv")):
+        _need(t, n, (T, B, H, d), xq.dtype)
+    _need(eta, "eta", (T, B, H), torch.float32)
+    for t, n in ((W_chunk, "W_chunk"), (W, "W")):
+        _need(t, n, (B, H, d, d), torch.float32)
+    for t, n in ((b_chunk, "b_chunk"), (b, "b")):
+        _need(t, n, (B, H, d), torch.float32)
+    _need(ln_gamma, "ln_gamma", (H, d), torch.float32)
+    _need(ln_beta, "ln_beta", (H, d), torch.float32)
+    if o is None:
+        o = torch.empty_like(xq)
+    _need(o, "o", (T, B, H, d), xq.dtype)
+    lib = _lib.load()
+    _lib.check(lib.ttt_decode_steps_mb(T, B, H, d, io, ln_eps, mb, pos, _ptr(xq), _ptr(xk),
+                                       _ptr(xv), _ptr(eta), _ptr(W_chunk), _ptr(b_chunk), _ptr(W),
+                                       _ptr(b), _ptr(ln_gamma), _ptr(ln_beta), _ptr(o),
+                                       _stream(stream)))
+    return o
+
+
 def ttt_ln_l2_bwd(Z, target, ln_gamma, ln_beta, G=None, ln_eps: float = 1e-6, stream=None):
     """Row-wise fused LN + L2 backward. Z, target, G [rows,d] fp32; gamma/beta [d]."""
     rows, d = Z.shape

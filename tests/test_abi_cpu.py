@@ -157,6 +157,28 @@ def _bwd(lib, B=2, H=3, L=40, d=64, mb=16, io=1, eps=1e-6, ws_bytes=None, ptrs=N
                                    p[14], p[15], p[16], ws if ws is not None else p[17], nb, None)
 
 
+def _dmb(lib, T=3, mb=4, pos=0, d=64, Wc=FAKE + 6 * (1 << 20), bc=FAKE + 7 * (1 << 20),
+         W=FAKE + 8 * (1 << 20)):
+    p = [FAKE + i * (1 << 20) for i in range(6)]
+    return lib.ttt_decode_steps_mb(T, 2, 3, d, 1, 1e-6, mb, pos, p[0], p[1], p[2], p[3], Wc, bc, W,
+                                   FAKE + 9 * (1 << 20), p[4], p[5], FAKE + 10 * (1 << 20), None)
+
+
+def test_decode_steps_mb_validation(lib):
+    assert _dmb(lib, mb=0) == _lib.TTT_E_SHAPE
+    assert _dmb(lib, mb=17) == _lib.TTT_E_SHAPE
+    assert _dmb(lib, pos=4) == _lib.TTT_E_SHAPE and "pos" in lib.ttt_last_error().decode()
+    assert _dmb(lib, pos=-1) == _lib.TTT_E_SHAPE
+    assert _dmb(lib, T=-1) == _lib.TTT_E_SHAPE
+    assert _dmb(lib, d=32) == _lib.TTT_E_SHAPE
+    assert _dmb(lib, Wc=0) == _lib.TTT_E_NULL and "W_chunk" in lib.ttt_last_error().decode()
+    assert _dmb(lib, bc=0) == _lib.TTT_E_NULL
+    assert _dmb(lib, Wc=FAKE + 8 * (1 << 20)) == _lib.TTT_E_ALIAS   # W_chunk is W
+    assert _dmb(lib, Wc=FAKE) == _lib.TTT_E_ALIAS                   # W_chunk over xq
+    assert _dmb(lib, mb=1, pos=0, Wc=0, bc=0, T=0) == _lib.TTT_OK  # mb = 1 ignores them
+    assert _dmb(lib, T=0, pos=3) == _lib.TTT_OK
+
+
 def test_linear_backward_workspace_size(lib):
     n = ctypes.c_size_t(0)
     assert lib.ttt_linear_backward_workspace(2, 3, 40, 64, 16, ctypes.byref(n)) == _lib.TTT_OK

@@ -393,3 +393,71 @@ def test_linear_bf16_other_minibatch(mb):
     """Mini-batch sizes other than 16 (VALU path) with bf16 storage."""
     x = gen.make_linear(800 + mb, 2, 3, 16 * 6 + 3, 64, io="bf16", ln_random=True)
     _check_linear(x, f"bf16 mb{mb}", mb=mb)
+
+
+# ---------------------------------------------------------------------------
+# Mini-batch decode (b = mb > 1): prefill + decode calls = one prefill over
+# the whole sequence with chunks aligned at its first token
+# ---------------------------------------------------------------------------
+def _mb_case(seed, io, d, B=2, H=3):
+    return gen.make_linear(seed, B, H, 0, d, io=io, ln_random=True, b_random=True, w_std=0.3)
+
+
+@pytest.mark.parametrize("io,d", [("bf16", 64), ("f32", 64), ("f32", 16), ("bf16", 16)])
+@pytest.mark.parametrize("mb", [4, 16])
+def test_decode_steps_mb_continues_the_prefill(io, d, mb):
+    """Prefill 2 chunks, then decode 2.5 chunks in three calls that end and
+    resume inside a chunk; the outputs and both states against the oracle's
+    prefill over the whole sequence (its chunk-start state at the end)."""
+    B, H, L0 = 2, 3, 2 * mb
+    splits = [mb // 2 + 1, mb + 1, mb - 2]           # 2.5 chunks, ends mid-chunk
+    T = sum(splits)
+    x = gen.make_linear(700 + 3 * d + mb, B, H, L0 + T, d, io=io, ln_random=True, b_random=True,
+                        w_std=0.3)
+    dt = P.io_dtype(io)
+    pre = dict(XQ=x.XQ[:, :, :L0], XK=x.XK[:, :, :L0], XV=x.XV[:, :, :L0], eta=x.eta[:, :, :L0])
+    O0, W, b = ttt.ttt_linear_forward(*(P.dev(pre[k], dt) for k in ("XQ", "XK", "XV")),
+                                      P.dev(pre["eta"]), P.dev(x.W0), P.dev(x.b0), P.dev(x.gamma),
+                                      P.dev(x.beta), mb=mb, ln_eps=x.eps)
+    Wc = torch.full_like(W, float("nan"))  # not read at pos = 0
+    bc = torch.full_like(b, float("nan"))
+    step = lambda a: np.ascontiguousarray(np.moveaxis(a, 2, 0))   # [B,H,T,...] -> [T,B,H,...]
+    outs, t, pos = [], L0, 0
+    for n in splits:
+        sl = slice(t, t + n)
+        o = ttt.ttt_decode_steps_mb(P.dev(step(x.XQ[:, :, sl]), dt), P.dev(step(x.XK[:, :, sl]), dt),
+                                    P.dev(step(x.XV[:, :, sl]), dt), P.dev(step(x.eta[:, :, sl])),
+                                    Wc, bc, W, b, P.dev(x.gamma), P.dev(x.beta), mb=mb, pos=pos,
+                                    ln_eps=x.eps)
+        outs.append(np.moveaxis(P.to_np(o), 0, 2))
+        t, pos = t + n, (pos + n) % mb
+    torch.cuda.synchronize()
+    O_ref, W_ref, b_ref = oracle.linear_forward(x.XQ, x.XK, x.XV, x.eta, x.W0, x.b0, x.gamma,
+                                                x.beta, x.eps, mb=mb)
+    # chunk-start state of the last (partial) chunk: the oracle run up to its start
+    Lc = L0 + T - pos
+    _, Wc_ref, bc_ref = oracle.linear_forward(x.XQ[:, :, :Lc], x.XK[:, :, :Lc], x.XV[:, :, :Lc],
+                                              x.eta[:, :, :Lc], x.W0, x.b0, x.gamma, x.beta,
+                                              x.eps, mb=mb)
+    got = (np.concatenate(outs, 2), P.to_np(W), P.to_np(b), P.to_np(Wc), P.to_np(bc))
+    ref = (O_ref[:, :, L0:], W_ref, b_ref, Wc_ref, bc_ref)
+    err = P.errors(got, ref, B * H, ("o", "W", "b", "W_chunk", "b_chunk"))
+    _report(f"decode mb={mb} {io} d{d}", err)
+    assert max(err.values()) <= P.TOL[io], err
+
+
+def test_decode_steps_mb1_is_decode_steps():
+    """mb = 1 ignores the chunk state and equals ttt_decode_steps bit for bit."""
+    x = gen.make_linear(760, 2, 3, 9, 64, io="bf16", ln_random=True, b_random=True, w_std=0.3)
+    dt = torch.bfloat16
+    step = lambda a: P.dev(np.ascontiguousarray(np.moveaxis(a, 2, 0)), dt)
+    args = (step(x.XQ), step(x.XK), step(x.XV),
+            P.dev(np.ascontiguousarray(np.moveaxis(x.eta, 2, 0))))
+    W0 = np.broadcast_to(x.W0, (2, 3, 64, 64)).copy()
+    b0 = np.broadcast_to(x.b0, (2, 3, 64)).copy()
+    Wa, ba, Wb, bb = P.dev(W0), P.dev(b0), P.dev(W0), P.dev(b0)
+    oa = ttt.ttt_decode_steps(*args, Wa, ba, P.dev(x.gamma), P.dev(x.beta), ln_eps=x.eps)
+    ob = ttt.ttt_decode_steps_mb(*args, torch.empty_like(Wb), torch.empty_like(bb), Wb, bb,
+                                 P.dev(x.gamma), P.dev(x.beta), mb=1, ln_eps=x.eps)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob) and torch.equal(Wa, Wb) and torch.equal(ba, bb)
