@@ -122,6 +122,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="3", choices=["3", "2", "5p", "4", "5d", "5r", "5m", "3b", "3g", "3gb", "3o"])
+    ap.add_argument("--peaks", action="store_true",
+                    help="measure achievable HBM copy bandwidth and bf16 GEMM throughput (context)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -136,6 +138,8 @@ def main():
 
     from test_sequence_layer_ttt_amd import gen, ttt
 
+    if args.peaks:
+        return bench_peaks(args)
     if args.copy_calibration:
         # Reference for the HBM byte counters: each launch reads and writes
         # exactly 256 MiB.
@@ -563,6 +567,31 @@ def bench_gate_backward(args):
     _line("learning-rate gate backward tokens/s (L=8192)", B * L / wall, args, wall, "bf16 in, fp32",
           {"workload": "ttt_eta_gate_backward_bf16_B2_H32_L8192_d64", "B": B, "H": H, "L": L,
            "d": d, "io": "bf16", "grads": "fp32", "parallelism": "none (1 GPU)"}, roof, extra)
+
+
+
+def bench_peaks(args):
+    """Achievable peaks on this GPU, as context for the datasheet figures the
+    roofline fractions use: a 1 GiB device-to-device copy (HBM read + write)
+    and an 8192^3 bf16 matrix product through the vendor GEMM library."""
+    import torch
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    _, kc = _timed(lambda: dst.copy_(src), stream, 3, 20)
+    del src, dst
+    m = 8192
+    a = torch.randn(m, m, device=dev).to(torch.bfloat16)
+    b = torch.randn(m, m, device=dev).to(torch.bfloat16)
+    c = torch.empty(m, m, device=dev, dtype=torch.bfloat16)
+    _, kg = _timed(lambda: torch.mm(a, b, out=c), stream, 3, 20)
+    print(json.dumps({
+        "copy": {"bytes_read_plus_written": 2 * n, "us": kc * 1e6, "GBps": 2 * n / kc / 1e9,
+                 "frac_of_8000": 2 * n / kc / 1e9 / HBM_PEAK_GBS},
+        "bf16_gemm": {"shape": [m, m, m], "us": kg * 1e6, "TFLOPs": 2 * m ** 3 / kg / 1e12,
+                      "frac_of_2500": 2 * m ** 3 / kg / 1e12 / BF16_PEAK_TFLOPS}}), flush=True)
 
 
 if __name__ == "__main__":
