@@ -55,7 +55,9 @@ struct BwdSmem {
     // [16 x d] row tiles (token rows, feature columns)
     float XQ[RW * DP], XK[RW * DP], Z[RW * DP], Zb[RW * DP], E[RW * DP], dZb[RW * DP];
     float dE[RW * DP], dZ[RW * DP], dT[RW * DP], dO[RW * DP];
-    float T[RW * TP], dA[RW * TP];  // [t][s]
+    float T[RW * TP], dA[RW * TP];        // [t][s]
+    float Tp[D / 16][RW * TP], Ap[D / 16][RW * TP];  // per-wave partials of T and dA over
+                                                     // 16-feature slices (summed by the reader)
     float red[RW * D];              // final dgamma / dbeta reduction over rows
 };
 
@@ -116,7 +118,9 @@ __global__ __launch_bounds__(NT) void linear_backward_kernel(
         return f32x4{x, x, x, x};
     };
     // M[d x d] += P^T Q over the m token rows, on tiles (rb, w); P, Q [16 x d]
-    auto state_update = [&](float *M, const float *P, const float *Q, const float *P2, const float *Q2) {
+    // (ck: also store the result to a checkpoint, row-major [d x d])
+    auto state_update = [&](float *M, const float *P, const float *Q, const float *P2, const float *Q2,
+                            float *ck) {
         if (!mw) return;
 #pragma unroll
         for (int rb = 0; rb < NTL; ++rb) {
@@ -126,8 +130,22 @@ __global__ __launch_bounds__(NT) void linear_backward_kernel(
             acc = mma<RW>(colm(P + 16 * rb, DP), rowm(Q + 16 * w, DP), g, c, acc);
             if (P2) acc = mma<RW>(colm(P2 + 16 * rb, DP), rowm(Q2 + 16 * w, DP), g, c, acc);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) M[(16 * rb + 4 * g + i) * DP + 16 * w + c] = acc[i];
+            for (int i = 0; i < 4; ++i) {
+                M[(16 * rb + 4 * g + i) * DP + 16 * w + c] = acc[i];
+                if (ck) ck[(16 * rb + 4 * g + i) * D + 16 * w + c] = acc[i];
+            }
         }
+    };
+    // column sums of [16 x d] row tiles (padding rows are zero): all loads first
+    auto colsum = [&](const float *P, const float *Q) {
+        float v[RW];
+#pragma unroll
+        for (int s2 = 0; s2 < RW; ++s2) v[s2] = P[s2 * DP + tid] + (Q ? Q[s2 * DP + tid] : 0.f);
+#pragma unroll
+        for (int k = RW / 2; k >= 1; k >>= 1)
+#pragma unroll
+            for (int s2 = 0; s2 < k; ++s2) v[s2] += v[s2 + k];
+        return v[0];
     };
 
     float gm[NF], bt[NF];
@@ -173,24 +191,33 @@ __global__ __launch_bounds__(NT) void linear_backward_kernel(
     // ahead of their use so that the global-memory latency hides behind the
     // current chunk.
     constexpr int NWP = D * D / NT;
+    // raw storage values (converted when staged), so that the loads stay in
+    // flight until the next chunk instead of being waited on where they issue
     struct Rows {
-        float xq[NF], xk[NF], xv[NF], go[NF], et;
+        TIO xq[NF], xk[NF], xv[NF];
+        float go[NF], et;
+        bool ok;
     };
     struct State {
         float w[NWP], b;
     };
+    // unconditional loads from a row clamped into the sequence; rows past its
+    // end are zeroed when staged
     auto fetch_rows = [&](int ch, bool rev, Rows &R) {
-        const bool ok = r < min(mb, L - ch * mb);
-        const size_t row = xbase + static_cast<size_t>(ch * mb + (ok ? r : 0)) * D;
+        R.ok = r < min(mb, L - ch * mb);
+        const int rr = R.ok ? r : 0;
+        const size_t row = xbase + static_cast<size_t>(ch * mb + rr) * D;
 #pragma unroll
         for (int u = 0; u < NF; ++u) {
             const int f = q + RW * u;
-            R.xk[u] = ok ? io::load(XK, row + f) : 0.f;
-            R.xv[u] = ok ? io::load(XV, row + f) : 0.f;
-            R.xq[u] = ok && rev ? io::load(XQ, row + f) : 0.f;
-            R.go[u] = ok && rev ? dO[row + f] : 0.f;
+            R.xk[u] = XK[row + f];
+            R.xv[u] = XV[row + f];
+            if (rev) {
+                R.xq[u] = XQ[row + f];
+                R.go[u] = dO[row + f];
+            }
         }
-        R.et = ok ? eta[static_cast<size_t>(seq) * L + ch * mb + r] : 0.f;
+        R.et = eta[static_cast<size_t>(seq) * L + ch * mb + rr];
     };
     auto fetch_state = [&](int ch, State &S) {
         const float *wc = wsq + static_cast<size_t>(ch) * (D * D + D);
@@ -199,18 +226,20 @@ __global__ __launch_bounds__(NT) void linear_backward_kernel(
         S.b = tid < D ? wc[D * D + tid] : 0.f;
     };
     // stage a chunk's rows: XK (and XQ, dO) into LDS; tau and eta into registers
-    auto stage_rows = [&](const Rows &R, bool rev, float (&tau)[NF], float &et) {
+    auto stage_rows = [&](const Rows &R, bool rev, float (&tau)[NF], float &et, float (&go)[NF]) {
 #pragma unroll
         for (int u = 0; u < NF; ++u) {
             const int f = q + RW * u;
-            sm.XK[r * DP + f] = R.xk[u];
-            tau[u] = R.xv[u] - R.xk[u];
+            const float xk = R.ok ? io::load(R.xk, u) : 0.f;
+            sm.XK[r * DP + f] = xk;
+            tau[u] = R.ok ? io::load(R.xv, u) - xk : 0.f;
             if (rev) {
-                sm.XQ[r * DP + f] = R.xq[u];
-                sm.dO[r * DP + f] = R.go[u];
+                sm.XQ[r * DP + f] = R.ok ? io::load(R.xq, u) : 0.f;
+                go[u] = R.ok ? R.go[u] : 0.f;
+                sm.dO[r * DP + f] = go[u];
             }
         }
-        et = R.et;
+        et = R.ok ? R.et : 0.f;
     };
     auto rowz = [&](const float *M, float (&z)[NF]) {
 #pragma unroll
@@ -220,13 +249,14 @@ __global__ __launch_bounds__(NT) void linear_backward_kernel(
     // ===== forward: chunk-start states to the workspace ========================
     Rows R;
     if (nch > 0) fetch_rows(0, false, R);
+    if (nch > 0) {  // chunk 0's start state; the others are written by the updates
+        for (int i = tid; i < D * D; i += NT) wsq[i] = W0[st * D * D + i];
+        if (tid < D) wsq[D * D + tid] = b0[st * D + tid];
+    }
     for (int ch = 0; ch < nch; ++ch) {
-        const int m = min(mb, L - ch * mb);
-        float *wc = wsq + static_cast<size_t>(ch) * (D * D + D);
-        for (int i = tid; i < D * D; i += NT) wc[i] = sm.W[(i / D) * DP + i % D];
-        if (tid < D) wc[D * D + tid] = sm.b[tid];
-        float tau[NF], et;
-        stage_rows(R, false, tau, et);
+        float *wn = ch + 1 < nch ? wsq + static_cast<size_t>(ch + 1) * (D * D + D) : nullptr;
+        float tau[NF], et, go_unused[NF];
+        stage_rows(R, false, tau, et, go_unused);
         if (ch + 1 < nch) fetch_rows(ch + 1, false, R);
         __syncthreads();
         if (mw) put(sm.Z, mma<D>(rowm(sm.XK, DP), rowm(sm.W + 16 * w, DP), g, c, brow(sm.b)));
@@ -238,11 +268,11 @@ __global__ __launch_bounds__(NT) void linear_backward_kernel(
 #pragma unroll
         for (int u = 0; u < NF; ++u) sm.E[r * DP + q + RW * u] = -et * s.G[u];
         __syncthreads();
-        state_update(sm.W, sm.XK, sm.E, nullptr, nullptr);  // W += XK^T E
+        state_update(sm.W, sm.XK, sm.E, nullptr, nullptr, wn);  // W += XK^T E
         if (tid < D) {
-            float acc = sm.b[tid];
-            for (int s2 = 0; s2 < m; ++s2) acc += sm.E[s2 * DP + tid];
-            sm.b[tid] = acc;
+            const float bn = sm.b[tid] + colsum(sm.E, nullptr);
+            sm.b[tid] = bn;
+            if (wn) wn[D * D + tid] = bn;
         }
         __syncthreads();
     }
@@ -272,9 +302,7 @@ __global__ __launch_bounds__(NT) void linear_backward_kernel(
         }
         if (tid < D) sm.b[tid] = S.b;
         float tau[NF], et, go[NF];
-        stage_rows(R, true, tau, et);
-#pragma unroll
-        for (int u = 0; u < NF; ++u) go[u] = R.go[u];
+        stage_rows(R, true, tau, et, go);
         if (ch > 0) {
             fetch_rows(ch - 1, true, R);
             fetch_state(ch - 1, S);
@@ -286,15 +314,19 @@ __global__ __launch_bounds__(NT) void linear_backward_kernel(
             put(sm.Z, mma<D>(rowm(sm.XK, DP), rowm(sm.W + 16 * w, DP), g, c, brow(sm.b)));
             put(sm.Zb, mma<D>(rowm(sm.XQ, DP), rowm(sm.W + 16 * w, DP), g, c, brow(sm.b)));
         }
-        if (w == NT / 64 - 1) {
-            const f32x4 t4 = mma<D>(rowm(sm.XQ, DP), colm(sm.XK, DP), g, c, fz);
+        if (mw) {  // this wave's 16-feature slice of XQ XK^T
+            const f32x4 t4 = mma<RW>(rowm(sm.XQ + 16 * w, DP), colm(sm.XK + 16 * w, DP), g, c, fz);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 4 * g + i;
-                sm.T[t * TP + c] = (c <= t && t < m) ? t4[i] + 1.f : 0.f;
-            }
+            for (int i = 0; i < 4; ++i) sm.Tp[w][(4 * g + i) * TP + c] = t4[i];
         }
         __syncthreads();
+        {  // T = tril(sum of the slices + 1) on the chunk's rows; one entry per thread
+            const int t = tid / RW, s2 = tid % RW;
+            float v = 0.f;
+#pragma unroll
+            for (int k = 0; k < NTL; ++k) v += sm.Tp[k][t * TP + s2];
+            sm.T[t * TP + s2] = (s2 <= t && t < m) ? v + 1.f : 0.f;
+        }
         float z[NF];
         rowz(sm.Z, z);
         Lnl2 s;
@@ -345,20 +377,19 @@ __global__ __launch_bounds__(NT) void linear_backward_kernel(
             gq = mma<D>(rowm(sm.dZb, DP), colm(sm.W + 16 * w * DP, DP), g, c, fz);
             gk = mma<D>(rowm(sm.E, DP), colm(sm.dW + 16 * w * DP, DP), g, c, fz);
         }
-        if (w == NT / 64 - 1) {
-            const f32x4 a4 = mma<D>(rowm(sm.dZb, DP), colm(sm.E, DP), g, c, fz);
+        if (mw) {  // this wave's 16-feature slice of dZb E^T
+            const f32x4 a4 = mma<RW>(rowm(sm.dZb + 16 * w, DP), colm(sm.E + 16 * w, DP), g, c, fz);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 4 * g + i;
-                sm.dA[t * TP + c] = (c <= t && t < m) ? a4[i] : 0.f;
-            }
+            for (int i = 0; i < 4; ++i) sm.Ap[w][(4 * g + i) * TP + c] = a4[i];
         }
         __syncthreads();
 
-        // dXQ tile += dA XK;  dXK tile += dA^T XQ
-        if (mw) {
-            gq = mma<RW>(rowm(sm.dA, TP), rowm(sm.XK + 16 * w, DP), g, c, gq);
-            gk = mma<RW>(colm(sm.dA, TP), rowm(sm.XQ + 16 * w, DP), g, c, gk);
+        {  // dA = the slices summed on the causal triangle of the chunk's rows
+            const int t = tid / RW, s2 = tid % RW;
+            float v = 0.f;
+#pragma unroll
+            for (int k = 0; k < NTL; ++k) v += sm.Ap[k][t * TP + s2];
+            sm.dA[t * TP + s2] = (s2 <= t && t < m) ? v : 0.f;
         }
         // row work: deta = -G . dE, dG = -eta dE, then the reverse of lnl2
         float de[NF];
@@ -403,8 +434,10 @@ __global__ __launch_bounds__(NT) void linear_backward_kernel(
         }
         __syncthreads();
 
-        // dXK tile += dZ W^T - dtau;  dXQ tile += dO;  write the tiles
+        // dXQ tile += dA XK + dO;  dXK tile += dA^T XQ + dZ W^T - dtau;  write the tiles
         if (mw) {
+            gq = mma<RW>(rowm(sm.dA, TP), rowm(sm.XK + 16 * w, DP), g, c, gq);
+            gk = mma<RW>(colm(sm.dA, TP), rowm(sm.XQ + 16 * w, DP), g, c, gk);
             gk = mma<D>(rowm(sm.dZ, DP), colm(sm.W + 16 * w * DP, DP), g, c, gk);
             const f32x4 dt4 = get(sm.dT), do4 = get(sm.dO);
 #pragma unroll
@@ -419,12 +452,8 @@ __global__ __launch_bounds__(NT) void linear_backward_kernel(
             }
         }
         // dW += XQ^T dZb + XK^T dZ;  db += 1^T (dZb + dZ)
-        state_update(sm.dW, sm.XQ, sm.dZb, sm.XK, sm.dZ);
-        if (tid < D) {
-            float acc = sm.db[tid];
-            for (int s2 = 0; s2 < m; ++s2) acc += sm.dZb[s2 * DP + tid] + sm.dZ[s2 * DP + tid];
-            sm.db[tid] = acc;
-        }
+        state_update(sm.dW, sm.XQ, sm.dZb, sm.XK, sm.dZ, nullptr);
+        if (tid < D) sm.db[tid] += colsum(sm.dZb, sm.dZ);
     }
     __syncthreads();
 
