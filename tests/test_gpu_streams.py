@@ -1,0 +1,82 @@
+"""The entry points enqueue on the caller's stream: run each on a side
+stream, with HIP events recorded on that stream around the call (the work
+must fall between them), and compare with the same call on the default
+stream bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+from test_sequence_layer_ttt_amd import gen, ttt
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _on_stream(fn, stream):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        out = fn(stream)
+        e1.record(stream)
+    stream.synchronize()
+    return out, e0.elapsed_time(e1) * 1e3  # us
+
+
+def _check(fn, min_us):
+    ref = fn(None)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    got, us = _on_stream(fn, s)
+    print(f"[stream] {us:.1f} us between the side stream's events", flush=True)
+    assert us > min_us, us
+    ref = ref if isinstance(ref, (tuple, list)) else (ref,)
+    got = got if isinstance(got, (tuple, list)) else (got,)
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+
+
+def test_linear_forward_on_side_stream():
+    x = gen.make_workload(3, L=2048, B=2, H=32)
+    dt = torch.bfloat16
+    args = [P.dev(x.XQ, dt), P.dev(x.XK, dt), P.dev(x.XV, dt), P.dev(x.eta), P.dev(x.W0),
+            P.dev(x.b0), P.dev(x.gamma), P.dev(x.beta)]
+    _check(lambda s: ttt.ttt_linear_forward(*args, stream=s), 20.0)
+
+
+def test_mlp_forward_on_side_stream():
+    x = gen.make_workload(4, L=512, B=2, H=12)
+    dt = torch.bfloat16
+    args = [P.dev(x.XQ, dt), P.dev(x.XK, dt), P.dev(x.XV, dt), P.dev(x.eta), P.dev(x.W1),
+            P.dev(x.b1), P.dev(x.W2), P.dev(x.b2), P.dev(x.gamma), P.dev(x.beta)]
+    _check(lambda s: ttt.ttt_mlp_forward(*args, stream=s), 20.0)
+
+
+def test_decode_steps_on_side_stream():
+    rng = np.random.default_rng(77)
+    dec = gen.make_decode(rng, 256, 8, 32, 64, "bf16")
+    W0 = (0.3 * rng.standard_normal((8, 32, 64, 64))).astype(np.float32)
+    g, be = np.ones((32, 64), np.float32), np.zeros((32, 64), np.float32)
+    dt = torch.bfloat16
+
+    def run(s):
+        W, b = P.dev(W0), torch.zeros((8, 32, 64), device="cuda")
+        o = ttt.ttt_decode_steps(P.dev(dec.XQ, dt), P.dev(dec.XK, dt), P.dev(dec.XV, dt),
+                                 P.dev(dec.eta), W, b, P.dev(g), P.dev(be), stream=s)
+        return o, W, b
+    # the state buffers are made on the current stream before the launch; the
+    # side stream's events bracket the launch itself
+    _check(run, 20.0)
+
+
+def test_backward_on_side_stream():
+    x = gen.make_workload(3, L=512, B=2, H=8)
+    dt = torch.bfloat16
+    dO = P.dev(np.random.default_rng(78).standard_normal((2, 8, 512, 64)).astype(np.float32))
+    args = [P.dev(x.XQ, dt), P.dev(x.XK, dt), P.dev(x.XV, dt), P.dev(x.eta), P.dev(x.W0),
+            P.dev(x.b0), P.dev(x.gamma), P.dev(x.beta), dO]
+
+    def run(s):
+        gr = ttt.ttt_linear_backward(*args, stream=s)
+        return tuple(gr[k] for k in sorted(gr))
+    _check(run, 20.0)
