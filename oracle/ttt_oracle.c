@@ -22,7 +22,7 @@
  *   gradient at the chunk-start state; the updates are then applied in token
  *   order and each token's output uses the state that includes its own update.
  *
- * Readings taken where the pages are silent (each listed in the design doc):
+ * Readings taken where the pages are silent:
  *   loss per token  l = 1/2 * sum_j (LN(z)_j - tau_j)^2, summed over tokens;
  *   LN uses the biased variance over the d features with eps inside the root;
  *   the same gamma/beta serve the loss and the output; row-vector convention
