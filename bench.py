@@ -266,6 +266,17 @@ def main():
                                "kind": "oracle",
                                "sample": f"full workload (B={B}, H={H}, L={L}), fp64 primal "
                                          f"form, {nt} threads over (n,h), {tc:.2f} s"}
+        if wl == 2:  # also one thread, on one sequence of the workload (scaled to tokens/s)
+            one = {k: np.ascontiguousarray(v[:1, :1]) for k, v in xs.items()
+                   if k in ("XQ", "XK", "XV", "eta")}
+            t2 = time.perf_counter()
+            oracle.linear_forward(one["XQ"], one["XK"], one["XV"], one["eta"], xs["W0"][:1],
+                                  xs["b0"][:1], xs["gamma"][:1], xs["beta"][:1], x.eps, mb=16,
+                                  nthreads=1)
+            t1s = time.perf_counter() - t2
+            out["cpu_baseline_single_thread"] = {
+                "value": L / t1s, "unit": "token-heads/s", "cores": 1, "kind": "oracle",
+                "sample": f"one sequence (L={L}), fp64 primal form, 1 thread, {t1s:.3f} s"}
         # parity of the timed launch's outputs against the oracle (S18 metric)
         def rel(g, r):
             g = g.detach().float().cpu().numpy().reshape(B * H, -1).astype(np.float64)
