@@ -169,3 +169,13 @@ def test_gated_training_step(io, L):
         err[k] = P.max_rel(got[k], ref[k], nseq)
     _report(f"training step {io} L{L}", err)
     assert max(err.values()) <= 1e-4, err
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_gated_prefill_empty_sequence(io):
+    """L = 0: no eta is formed and the final state is the initial one."""
+    x = _gated(890, 2, 3, 0, 64, io, b_random=True)
+    O, W, b = P.linear_gpu(x)
+    assert O.shape == (2, 3, 0, 64)
+    assert np.array_equal(W, np.broadcast_to(x.W0, W.shape))
+    assert np.array_equal(b, np.broadcast_to(x.b0, b.shape))

@@ -84,3 +84,12 @@ def test_workload3_shape_sampled_heads():
     print("[parity] opts workload3 shape: " + " ".join(f"{k}={v:.2e}" for k, v in err.items()),
           flush=True)
     assert max(err.values()) <= P.TOL["bf16"], err
+
+
+def test_options_empty_sequence():
+    """L = 0 with both options: the final state is the initial one."""
+    x = gen.make_linear(660, 2, 3, 0, 64, io="bf16", b_random=True)
+    O, W, b = _run(x, "inner_product", 0.5, 16)
+    assert O.shape == (2, 3, 0, 64)
+    assert np.array_equal(W, np.broadcast_to(x.W0, W.shape))
+    assert np.array_equal(b, np.broadcast_to(x.b0, b.shape))

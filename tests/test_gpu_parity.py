@@ -461,3 +461,18 @@ def test_decode_steps_mb1_is_decode_steps():
                                  P.dev(x.gamma), P.dev(x.beta), mb=1, ln_eps=x.eps)
     torch.cuda.synchronize()
     assert torch.equal(oa, ob) and torch.equal(Wa, Wb) and torch.equal(ba, bb)
+
+
+def test_decode_steps_mb_zero_steps_leaves_state():
+    """T = 0 touches neither state."""
+    rng = np.random.default_rng(765)
+    W = P.dev(rng.standard_normal((2, 3, 64, 64)).astype(np.float32))
+    b = P.dev(rng.standard_normal((2, 3, 64)).astype(np.float32))
+    Wc, bc = W.clone() * 2, b.clone() * 2
+    W1, b1, Wc1, bc1 = W.clone(), b.clone(), Wc.clone(), bc.clone()
+    e = torch.empty((0, 2, 3, 64), device="cuda", dtype=torch.bfloat16)
+    ttt.ttt_decode_steps_mb(e, e, e, torch.empty((0, 2, 3), device="cuda"), Wc, bc, W, b,
+                            P.dev(np.ones((3, 64), np.float32)), P.dev(np.zeros((3, 64), np.float32)),
+                            mb=16, pos=5)
+    torch.cuda.synchronize()
+    assert torch.equal(W, W1) and torch.equal(b, b1) and torch.equal(Wc, Wc1) and torch.equal(bc, bc1)
