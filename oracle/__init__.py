@@ -54,6 +54,10 @@ def _load():
         + [_D] * 6 + [ctypes.c_int] + [_D] * 2 + [ctypes.c_int, ctypes.c_double] + [_D] * 3 \
         + [ctypes.c_int]
     lib.oracle_linear_forward_opts.restype = ctypes.c_int
+    lib.oracle_mlp_forward_opts.argtypes = [ctypes.c_int] * 5 + [_I, ctypes.c_double] \
+        + [_D] * 8 + [ctypes.c_int] + [_D] * 2 + [ctypes.c_int, ctypes.c_double] + [_D] * 5 \
+        + [ctypes.c_int]
+    lib.oracle_mlp_forward_opts.restype = ctypes.c_int
     lib.oracle_ln_l2_bwd.argtypes = [ctypes.c_int, ctypes.c_int, _D, _D, _D, _D,
                                      ctypes.c_double, _D]
     lib.oracle_ln_l2_bwd.restype = None
@@ -188,6 +192,37 @@ def mlp_forward(XQ, XK, XV, eta, W1, b1, W2, b2, gamma, beta, eps: float, mb: in
            _p(beta), _p(O), _p(W1o), _p(b1o), _p(W2o), _p(b2o), nthreads or default_threads())
     if st != 0:
         raise RuntimeError(f"oracle mlp returned {st}")
+    return O, W1o, b1o, W2o, b2o
+
+
+def mlp_forward_opts(XQ, XK, XV, eta, W1, b1, W2, b2, gamma, beta, eps: float, mb: int = 16,
+                     loss: str = "mse", weight_decay: float = 0.0,
+                     schedule: Optional[Sequence[int]] = None, w0_batched: bool = False,
+                     nthreads: Optional[int] = None):
+    """TTT-MLP with the Modular-TTT options (primal form): loss "mse" (as
+    mlp_forward) or "inner_product" (-< XK + LN(f_res(XK)), XV > per token),
+    and weight decay lambda/2 (||W1||^2 + ||W2||^2) added to every token's
+    loss (not the biases). Returns (O, W1, b1, W2, b2) in float64."""
+    lib = _load()
+    XQ, XK, XV, eta = _f64(XQ), _f64(XK), _f64(XV), _f64(eta)
+    B, H, L, d = XQ.shape
+    m = 4 * d
+    W1, b1, W2, b2 = _f64(W1), _f64(b1), _f64(W2), _f64(b2)
+    gamma, beta = _f64(gamma), _f64(beta)
+    sched, nch = _sched(L, mb, schedule)
+    O = np.zeros((B, H, L, d))
+    W1o = np.zeros((B, H, d, m))
+    b1o = np.zeros((B, H, m))
+    W2o = np.zeros((B, H, m, d))
+    b2o = np.zeros((B, H, d))
+    code = {"mse": 0, "inner_product": 1}[loss]
+    st = lib.oracle_mlp_forward_opts(B, H, L, d, nch, sched.ctypes.data_as(_I), float(eps),
+                                     _p(XQ), _p(XK), _p(XV), _p(eta), _p(W1), _p(b1), _p(W2),
+                                     _p(b2), int(bool(w0_batched)), _p(gamma), _p(beta), code,
+                                     float(weight_decay), _p(O), _p(W1o), _p(b1o), _p(W2o),
+                                     _p(b2o), nthreads or default_threads())
+    if st != 0:
+        raise RuntimeError(f"oracle mlp (options) returned {st}")
     return O, W1o, b1o, W2o, b2o
 
 

@@ -29,10 +29,11 @@
  *   Z = X W with W[i][j] mapping input i to output j ([D] §4.2 forward line);
  *   chunks are aligned at t = 0 and the last chunk may be partial;
  *   GELU is the exact x * Phi(x);
- *   Modular-TTT options (TTT-Linear only): the inner-product loss scores the
- *   prediction f(xk) = xk + LN(xk W + b) against xv as -<f(xk), xv>; weight
- *   decay adds lambda/2 ||W||^2 to each token's loss (W only, not b), its
- *   gradient taken at the chunk-start state like the rest.
+ *   Modular-TTT options: the inner-product loss scores the prediction
+ *   f(xk) = xk + LN(f_res(xk)) against xv as -<f(xk), xv>; weight decay adds
+ *   lambda/2 ||W||^2 to each token's loss for every weight matrix (W, or W1
+ *   and W2 of the MLP; never a bias), its gradient taken at the chunk-start
+ *   state like the rest.
  *
  * Layouts (row-major, contiguous):
  *   XQ, XK, XV, O : [B,H,L,d]         eta : [B,H,L]
@@ -180,8 +181,8 @@ typedef struct {
     int w0_batched;
     const double *gamma, *beta;
     double *O, *W_out, *b_out, *W2_out, *b2_out;
-    int loss;      /* Linear: 0 = squared error (the default), 1 = inner product */
-    double wd;     /* Linear: weight decay lambda on W (0 = none)               */
+    int loss;      /* 0 = squared error (the default), 1 = inner product        */
+    double wd;     /* weight decay lambda on the weight matrices (0 = none)     */
     int nthreads;
     int tid;
     int status;
@@ -502,6 +503,8 @@ static void mlp_primal_seq(job_t *j, int n, int h, double *scratch)
     double *z2 = a + m;                 /* d                             */
     double *tau = z2 + d;               /* d                             */
     double *y = tau + d;                /* d                             */
+    double *W1c = y + d;                /* d x m: chunk-start W1 (decay) */
+    double *W2c = W1c + (size_t)d * m;  /* m x d: chunk-start W2 (decay) */
 
     const size_t bn = j->w0_batched ? (size_t)n : 0;
     memcpy(W1, j->W0 + (bn * H + h) * (size_t)d * m, sizeof(double) * d * m);
@@ -526,12 +529,21 @@ static void mlp_primal_seq(job_t *j, int n, int h, double *scratch)
                 z2[jj] = acc;
                 tau[jj] = v[jj] - k[jj];
             }
-            ln_l2_grad_row(d, z2, tau, gamma, beta, j->eps, G2 + (size_t)s * d);
+            if (j->loss == 1)
+                ln_ip_grad_row(d, z2, v, gamma, j->eps, G2 + (size_t)s * d);
+            else
+                ln_l2_grad_row(d, z2, tau, gamma, beta, j->eps, G2 + (size_t)s * d);
             for (int q = 0; q < m; ++q) {
                 double acc = 0.0;
                 for (int jj = 0; jj < d; ++jj) acc += G2[(size_t)s * d + jj] * W2[(size_t)q * d + jj];
                 G1[(size_t)s * m + q] = acc * gelu_prime(z1[q]);
             }
+        }
+        /* weight decay: lambda * W1 and lambda * W2 at the chunk-start state
+           join every token's gradient (the biases are not decayed) */
+        if (j->wd != 0.0) {
+            memcpy(W1c, W1, sizeof(double) * d * m);
+            memcpy(W2c, W2, sizeof(double) * m * d);
         }
         for (int s = 0; s < len; ++s) {
             const int t = t0 + s;
@@ -539,10 +551,18 @@ static void mlp_primal_seq(job_t *j, int n, int h, double *scratch)
             const double e = eta[t];
             const double *g1 = G1 + (size_t)s * m, *g2 = G2 + (size_t)s * d, *as = A + (size_t)s * m;
             for (int i = 0; i < d; ++i)
-                for (int q = 0; q < m; ++q) W1[(size_t)i * m + q] -= e * k[i] * g1[q];
+                for (int q = 0; q < m; ++q) {
+                    double gw = k[i] * g1[q];
+                    if (j->wd != 0.0) gw += j->wd * W1c[(size_t)i * m + q];
+                    W1[(size_t)i * m + q] -= e * gw;
+                }
             for (int q = 0; q < m; ++q) b1[q] -= e * g1[q];
             for (int q = 0; q < m; ++q)
-                for (int jj = 0; jj < d; ++jj) W2[(size_t)q * d + jj] -= e * as[q] * g2[jj];
+                for (int jj = 0; jj < d; ++jj) {
+                    double gw = as[q] * g2[jj];
+                    if (j->wd != 0.0) gw += j->wd * W2c[(size_t)q * d + jj];
+                    W2[(size_t)q * d + jj] -= e * gw;
+                }
             for (int jj = 0; jj < d; ++jj) b2[jj] -= e * g2[jj];
             for (int q = 0; q < m; ++q) {
                 double acc = b1[q];
@@ -585,7 +605,39 @@ int oracle_mlp_forward(int B, int H, int L, int d, int nchunks, const int *chunk
     j.W_out = W1_out; j.b_out = b1_out; j.W2_out = W2_out; j.b2_out = b2_out;
     j.nthreads = nthreads;
     const size_t m = 4 * (size_t)d;
-    size_t scratch = 2 * (size_t)d * m + m + d + (size_t)j.max_chunk * (2 * m + d) + 2 * m + 3 * (size_t)d;
+    size_t scratch = 4 * (size_t)d * m + m + d + (size_t)j.max_chunk * (2 * m + d) + 2 * m + 3 * (size_t)d;
+    return run_pool(&j, mlp_primal_seq, scratch);
+}
+
+/*
+ * TTT-MLP with the same Modular-TTT options as TTT-Linear: loss = 1 scores
+ * x + LN(f_res(x)) against v by -< ., v > (ln_ip_grad_row at the second
+ * layer's output); weight_decay = lambda adds lambda/2 (||W1||^2 + ||W2||^2)
+ * to every token's loss (the biases b1, b2 are not decayed). Every gradient,
+ * the decay term included, is taken at the chunk-start state.
+ */
+int oracle_mlp_forward_opts(int B, int H, int L, int d, int nchunks, const int *chunk_len,
+                            double eps, const double *XQ, const double *XK, const double *XV,
+                            const double *eta, const double *W1_0, const double *b1_0,
+                            const double *W2_0, const double *b2_0, int w0_batched,
+                            const double *gamma, const double *beta, int loss,
+                            double weight_decay, double *O, double *W1_out, double *b1_out,
+                            double *W2_out, double *b2_out, int nthreads)
+{
+    if (B < 0 || H < 0 || L < 0 || d <= 0 || (loss != 0 && loss != 1)) return ORACLE_E_ARG;
+    job_t j;
+    memset(&j, 0, sizeof j);
+    int st = check_schedule(L, nchunks, chunk_len, &j.max_chunk);
+    if (st) return st;
+    j.B = B; j.H = H; j.L = L; j.d = d; j.nchunks = nchunks; j.chunk_len = chunk_len;
+    j.eps = eps; j.XQ = XQ; j.XK = XK; j.XV = XV; j.eta = eta;
+    j.W0 = W1_0; j.b0 = b1_0; j.W2_0 = W2_0; j.b2_0 = b2_0; j.w0_batched = w0_batched;
+    j.gamma = gamma; j.beta = beta; j.O = O;
+    j.W_out = W1_out; j.b_out = b1_out; j.W2_out = W2_out; j.b2_out = b2_out;
+    j.nthreads = nthreads;
+    j.loss = loss; j.wd = weight_decay;
+    const size_t m = 4 * (size_t)d;
+    size_t scratch = 4 * (size_t)d * m + m + d + (size_t)j.max_chunk * (2 * m + d) + 2 * m + 3 * (size_t)d;
     return run_pool(&j, mlp_primal_seq, scratch);
 }
 
@@ -642,7 +694,10 @@ static void mlp_dual_seq(job_t *j, int n, int h, double *scratch)
                 z2[jj] = acc;
                 tau[jj] = v[jj] - k[jj];
             }
-            ln_l2_grad_row(d, z2, tau, gamma, beta, j->eps, G2 + (size_t)s * d);
+            if (j->loss == 1)
+                ln_ip_grad_row(d, z2, v, gamma, j->eps, G2 + (size_t)s * d);
+            else
+                ln_l2_grad_row(d, z2, tau, gamma, beta, j->eps, G2 + (size_t)s * d);
             for (int q = 0; q < m; ++q) {
                 double acc = 0.0;
                 for (int jj = 0; jj < d; ++jj) acc += G2[(size_t)s * d + jj] * W2[(size_t)q * d + jj];

@@ -82,3 +82,82 @@ def test_inner_product_gradient_is_linear_in_the_values():
                                            loss="inner_product")
     assert np.abs((W2[0] - W0) - 2 * (W1[0] - W0)).max() <= 1e-13
     assert np.abs((b2[0] - b0) - 2 * (b1[0] - b0)).max() <= 1e-13
+
+
+def _mlp_case(seed, L=11, d=4, H=2):
+    rng = np.random.default_rng(seed)
+    m = 4 * d
+    XQ, XK, XV = (rng.standard_normal((1, H, L, d)) for _ in range(3))
+    eta = 0.05 + 0.1 * rng.random((1, H, L))
+    W1 = rng.standard_normal((H, d, m)) / np.sqrt(d)
+    b1 = 0.1 * rng.standard_normal((H, m))
+    W2 = rng.standard_normal((H, m, d)) / np.sqrt(m)
+    b2 = 0.1 * rng.standard_normal((H, d))
+    gamma = 1 + 0.2 * rng.standard_normal((H, d))
+    beta = 0.2 * rng.standard_normal((H, d))
+    return XQ, XK, XV, eta, W1, b1, W2, b2, gamma, beta
+
+
+@pytest.mark.parametrize("loss", ["mse", "inner_product"])
+@pytest.mark.parametrize("wd", [0.0, 0.4])
+@pytest.mark.parametrize("mb", [1, 4])
+def test_mlp_matches_autograd_of_the_definition(loss, wd, mb):
+    XQ, XK, XV, eta, W1, b1, W2, b2, g, be = _mlp_case(40 + mb)
+    got = oracle.mlp_forward_opts(XQ, XK, XV, eta, W1, b1, W2, b2, g, be, 1e-6, mb=mb, loss=loss,
+                                  weight_decay=wd)
+    for h in range(2):
+        ref = torch_ref.mlp_autograd_opts(XQ[0, h], XK[0, h], XV[0, h], eta[0, h], W1[h], b1[h],
+                                          W2[h], b2[h], g[h], be[h], 1e-6, mb, loss, wd)
+        for x, r in zip(got, ref):
+            assert np.abs(x[0, h] - r).max() <= 1e-12 * max(1.0, np.abs(r).max())
+
+
+def test_mlp_defaults_equal_the_plain_layer():
+    c = _mlp_case(50)
+    a = oracle.mlp_forward(*c, 1e-6, mb=4)
+    b = oracle.mlp_forward_opts(*c, 1e-6, mb=4)
+    for p, q in zip(a, b):
+        assert np.array_equal(p, q)
+
+
+def test_mlp_weight_decay_alone_scales_both_weights():
+    """XV = 0 under the inner-product loss makes the loss gradient vanish, so
+    with decay each chunk scales W1 and W2 by 1 - lambda * (sum of the chunk's
+    eta) and leaves b1, b2 alone."""
+    XQ, XK, XV, eta, W1, b1, W2, b2, g, be = _mlp_case(51, L=13)
+    lam, mb = 0.6, 4
+    _, W1o, b1o, W2o, b2o = oracle.mlp_forward_opts(XQ, XK, np.zeros_like(XV), eta, W1, b1, W2,
+                                                    b2, g, be, 1e-6, mb=mb,
+                                                    loss="inner_product", weight_decay=lam)
+    for h in range(2):
+        f = 1.0
+        for c0 in range(0, eta.shape[2], mb):
+            f *= 1.0 - lam * eta[0, h, c0:c0 + mb].sum()
+        assert np.abs(W1o[0, h] - f * W1[h]).max() <= 1e-13
+        assert np.abs(W2o[0, h] - f * W2[h]).max() <= 1e-13
+        assert np.array_equal(b1o[0, h], b1[h]) and np.array_equal(b2o[0, h], b2[h])
+
+
+def test_mlp_inner_product_second_layer_step_is_closed_form():
+    """One token, b = 1, inner-product loss: the gradient at the second
+    layer's output is g = -(gamma * v) pushed back through the layer norm,
+    i.e. -(gamma v - mean(gamma v) - yhat * mean(gamma v * yhat)) / sigma with
+    yhat the normalised z2, so b2' = b2 - eta g and W2' = W2 - eta a g^T with
+    a = gelu(xk W1 + b1)."""
+    from math import erf, sqrt
+    XQ, XK, XV, eta, W1, b1, W2, b2, g, be = _mlp_case(52, L=1)
+    eps = 1e-6
+    _, _, _, W2o, b2o = oracle.mlp_forward_opts(XQ, XK, XV, eta, W1, b1, W2, b2, g, be, eps,
+                                                mb=1, loss="inner_product")
+    for h in range(2):
+        k, v, e = XK[0, h, 0], XV[0, h, 0], eta[0, h, 0]
+        z1 = k @ W1[h] + b1[h]
+        a = np.array([0.5 * x * (1 + erf(x / sqrt(2))) for x in z1])
+        z2 = a @ W2[h] + b2[h]
+        mu = z2.mean()
+        sig = np.sqrt(((z2 - mu) ** 2).mean() + eps)
+        yh = (z2 - mu) / sig
+        u = g[h] * v
+        grad = -(u - u.mean() - yh * (u * yh).mean()) / sig
+        assert np.abs(b2o[0, h] - (b2[h] - e * grad)).max() <= 1e-13
+        assert np.abs(W2o[0, h] - (W2[h] - e * np.outer(a, grad))).max() <= 1e-13

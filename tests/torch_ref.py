@@ -113,6 +113,40 @@ def mlp_autograd(XQ, XK, XV, eta, W1, b1, W2, b2, gamma, beta, eps, mb):
     return (O.numpy(),) + tuple(p.detach().numpy() for p in P)
 
 
+def mlp_autograd_opts(XQ, XK, XV, eta, W1, b1, W2, b2, gamma, beta, eps, mb, loss="mse",
+                      wd=0.0):
+    """mlp_autograd with the Modular-TTT options: per-token loss "mse" or
+    "inner_product" (-< xk + LN(f_res(xk)), xv >), plus
+    wd/2 (||W1||^2 + ||W2||^2); every gradient by autograd at the chunk-start
+    state."""
+    xq, xk, xv, et = _t(XQ), _t(XK), _t(XV), _t(eta)
+    P = [_t(W1).clone(), _t(b1).clone(), _t(W2).clone(), _t(b2).clone()]
+    g_, be_ = _t(gamma), _t(beta)
+    L, d = xq.shape
+
+    def f_res(x, p):
+        return F.gelu(x @ p[0] + p[1], approximate="none") @ p[2] + p[3]
+
+    O = torch.zeros(L, d, dtype=torch.float64)
+    t0 = 0
+    for n in chunk_schedule(L, mb):
+        Pc = [p.clone().requires_grad_(True) for p in P]
+        grads = []
+        for s in range(t0, t0 + n):
+            y = F.layer_norm(f_res(xk[s], Pc), (d,), g_, be_, eps)
+            if loss == "mse":
+                ls = 0.5 * ((y - (xv[s] - xk[s])) ** 2).sum()
+            else:
+                ls = -((xk[s] + y) * xv[s]).sum()
+            ls = ls + 0.5 * wd * ((Pc[0] ** 2).sum() + (Pc[2] ** 2).sum())
+            grads.append(torch.autograd.grad(ls, Pc))
+        for i, s in enumerate(range(t0, t0 + n)):
+            P = [p - et[s] * g for p, g in zip(P, grads[i])]
+            O[s] = xq[s] + F.layer_norm(f_res(xq[s], P), (d,), g_, be_, eps)
+        t0 += n
+    return (O.numpy(),) + tuple(p.detach().numpy() for p in P)
+
+
 def token_loss_np(z, tau, gamma, beta, eps):
     """l(z) = 1/2 ||LN(z) - tau||^2 written with plain NumPy operations that
     also accept complex arguments (for complex-step differentiation)."""
