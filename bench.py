@@ -121,7 +121,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="3", choices=["3", "2", "5p", "4", "5d", "5r", "5m", "3b", "3g", "3gb", "3o"])
+    ap.add_argument("--workload", default="3", choices=["3", "2", "5p", "4", "4o", "5d", "5r", "5m", "3b", "3g", "3gb",
+                             "3o"])
     ap.add_argument("--peaks", action="store_true",
                     help="measure achievable HBM copy bandwidth and bf16 GEMM throughput (context)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -154,6 +155,8 @@ def main():
 
     if args.workload == "4":
         return bench_mlp(args)
+    if args.workload == "4o":
+        return bench_mlp(args, opts=True)
     if args.workload == "5d":
         return bench_decode(args)
     if args.workload == "5r":
@@ -316,8 +319,9 @@ def _line(metric, value, args, wall_step, dtype, config, roofline, extra=None):
     print(json.dumps(out), flush=True)
 
 
-def bench_mlp(args):
-    """TTT-MLP prefill, workload 4 (B=2, H=12, L=8192, d=64, hidden 256)."""
+def bench_mlp(args, opts=False):
+    """TTT-MLP prefill, workload 4 (B=2, H=12, L=8192, d=64, hidden 256); with
+    opts, the inner-product loss and weight decay 0.5 on W1 and W2."""
     import numpy as np
     import torch
     from test_sequence_layer_ttt_amd import gen, ttt
@@ -333,7 +337,11 @@ def bench_mlp(args):
     outs = (torch.empty((B, H, d, 4 * d), **kw), torch.empty((B, H, 4 * d), **kw),
             torch.empty((B, H, 4 * d, d), **kw), torch.empty((B, H, d), **kw))
     stream = torch.cuda.current_stream()
-    step = lambda: ttt.ttt_mlp_forward(*ins, O=O, outs=outs, ln_eps=x.eps, stream=stream)
+    if opts:
+        step = lambda: ttt.ttt_mlp_forward_opts(*ins, "inner_product", 0.5, O=O, outs=outs,
+                                                ln_eps=x.eps, stream=stream)
+    else:
+        step = lambda: ttt.ttt_mlp_forward(*ins, O=O, outs=outs, ln_eps=x.eps, stream=stream)
     wall, kern = _timed(step, stream, args.warmup, args.steps)
     fl = alg_flops_mlp(B, H, L, d)
     roof = {"bound": "mfma", "achieved": fl / kern / 1e12, "peak": BF16_PEAK_TFLOPS,
@@ -343,18 +351,20 @@ def bench_mlp(args):
     if not args.no_cpu_baseline:
         import oracle
         nt = cpu_threads()
-        Ls = 512  # bounded sample: the first 512 tokens of every sequence
-        sl = slice(0, Ls)
         t1 = time.perf_counter()
-        oracle.mlp_forward(x.XQ[:, :, sl], x.XK[:, :, sl], x.XV[:, :, sl], x.eta[:, :, sl],
-                           x.W1, x.b1, x.W2, x.b2, x.gamma, x.beta, x.eps, mb=16, nthreads=nt)
+        run = (lambda *a, **k: oracle.mlp_forward_opts(*a, loss="inner_product",
+                                                       weight_decay=0.5, **k)) if opts \
+            else oracle.mlp_forward
+        run(x.XQ, x.XK, x.XV, x.eta, x.W1, x.b1, x.W2, x.b2, x.gamma, x.beta, x.eps, mb=16,
+            nthreads=nt)
         tc = time.perf_counter() - t1
-        extra["cpu_baseline"] = {"value": B * Ls / tc, "unit": "tokens/s", "cores": nt,
+        extra["cpu_baseline"] = {"value": B * L / tc, "unit": "tokens/s", "cores": nt,
                                  "kind": "oracle",
-                                 "sample": f"first {Ls} tokens of each of the {B}x{H} sequences, "
-                                           f"fp64 primal form, {nt} threads, {tc:.2f} s"}
-    _line(f"TTT-MLP prefill tokens/s (L={L})", B * L / wall, args, wall, "bf16",
-          {"workload": gen.WORKLOADS[4].name, "B": B, "H": H, "L": L, "d": d, "hidden": 4 * d,
+                                 "sample": f"full workload (B={B}, H={H}, L={L}), fp64 primal "
+                                           f"form, {nt} threads over (n,h), {tc:.2f} s"}
+    tag = ", inner-product loss, weight decay 0.5" if opts else ""
+    _line(f"TTT-MLP prefill tokens/s (L={L}{tag})", B * L / wall, args, wall, "bf16",
+          {"workload": gen.WORKLOADS[4].name + ("+ip_loss+wd" if opts else ""), "B": B, "H": H, "L": L, "d": d, "hidden": 4 * d,
            "mini_batch": 16, "io": "bf16", "state": "fp32", "parallelism": "none (1 GPU)"},
           roof, extra)
 

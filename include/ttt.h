@@ -64,9 +64,9 @@ extern "C" {
 #define TTT_E_ALIAS (-5) /* an output overlaps an input or another output      */
 #define TTT_E_HIP (-6)   /* the kernel launch failed                           */
 
-/* Inner loss of ttt_linear_forward_opts. */
-#define TTT_LOSS_MSE 0           /* 1/2 ||LN(XK W + b) - (XV - XK)||^2 per token  */
-#define TTT_LOSS_INNER_PRODUCT 1 /* -< XK + LN(XK W + b), XV > per token          */
+/* Inner loss of ttt_linear_forward_opts and ttt_mlp_forward_opts. */
+#define TTT_LOSS_MSE 0           /* 1/2 ||LN(f_res(XK)) - (XV - XK)||^2 per token */
+#define TTT_LOSS_INNER_PRODUCT 1 /* -< XK + LN(f_res(XK)), XV > per token        */
 
 /* Storage type of XQ/XK/XV and O. State, eta and LN parameters are fp32. */
 typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
@@ -128,9 +128,10 @@ int ttt_linear_forward_gated(int B, int H, int L, int d, int mb, int io, float l
  *                  gains lambda/2 ||W||^2 (W only, not b), its gradient taken at
  *                  the chunk-start state W_c like the rest, so a chunk maps
  *                  W_c -> (1 - lambda * sum_t eta_t) W_c - (eta * XK)^T G.
- * Every other argument as ttt_linear_forward. The defaults (TTT_LOSS_MSE,
- * 0) run ttt_linear_forward's kernels; other values run the fp32 VALU prefill
- * kernel for every shape.
+ * Every other argument, and the numerics, as ttt_linear_forward: the bf16
+ * path with d = 64 and mb = 16 runs the MFMA prefill for every option value
+ * (the defaults, TTT_LOSS_MSE and 0, are exactly ttt_linear_forward), other
+ * shapes the fp32 VALU prefill.
  */
 int ttt_linear_forward_opts(int B, int H, int L, int d, int mb, int io, float ln_eps,
                             const void *XQ, const void *XK, const void *XV, const float *eta,
@@ -186,6 +187,30 @@ int ttt_mlp_forward(int B, int H, int L, int d, int mb, int io, float ln_eps,
                     const float *b2_0, int w0_batched, const float *ln_gamma,
                     const float *ln_beta, void *O, float *W1_out, float *b1_out,
                     float *W2_out, float *b2_out, hipStream_t stream);
+
+/*
+ * ttt_mlp_forward with the two Modular-TTT options of ttt_linear_forward_opts
+ * ([M]: inner loss and weight decay on the fast weights), read for the MLP:
+ *   inner_loss   : TTT_LOSS_MSE (as ttt_mlp_forward) or TTT_LOSS_INNER_PRODUCT,
+ *                  each token's loss -< XK_t + LN(f_res(XK_t)), XV_t >; any
+ *                  other value is TTT_E_SHAPE.
+ *   weight_decay : lambda >= 0 (finite, else TTT_E_SHAPE); every token's loss
+ *                  gains lambda/2 (||W1||^2 + ||W2||^2) (the weight matrices,
+ *                  not b1, b2), its gradient taken at the chunk-start state, so
+ *                  a chunk scales W1 and W2 by 1 - lambda * sum_t eta_t before
+ *                  the loss updates, and token t inside the chunk sees them
+ *                  scaled by 1 - lambda * sum_{s<=t} eta_s.
+ * Every other argument, and the numerics, as ttt_mlp_forward; the bf16 path
+ * with mb = 16 runs the MFMA kernel for every option value, other shapes the
+ * fp32 VALU kernel.
+ */
+int ttt_mlp_forward_opts(int B, int H, int L, int d, int mb, int io, float ln_eps,
+                         const void *XQ, const void *XK, const void *XV, const float *eta,
+                         const float *W1_0, const float *b1_0, const float *W2_0,
+                         const float *b2_0, int w0_batched, const float *ln_gamma,
+                         const float *ln_beta, int inner_loss, float weight_decay, void *O,
+                         float *W1_out, float *b1_out, float *W2_out, float *b2_out,
+                         hipStream_t stream);
 
 /*
  * Backward of ttt_linear_forward: the gradients of

@@ -205,6 +205,60 @@ int gate_common(int B, int H, int L, int d, int io, float eta_base, size_t *xb, 
     return TTT_OK;
 }
 
+// TTT-MLP prefill with the loss / weight-decay options (shared by the plain
+// and the options entry points).
+int mlp_forward(int B, int H, int L, int d, int mb, int io, float ln_eps, const void *XQ,
+                const void *XK, const void *XV, const float *eta, const float *W1_0,
+                const float *b1_0, const float *W2_0, const float *b2_0, int w0_batched,
+                const float *ln_gamma, const float *ln_beta, void *O, float *W1_out,
+                float *b1_out, float *W2_out, float *b2_out, hipStream_t stream, int loss,
+                float weight_decay) {
+    int st;
+    if ((st = check_common(B, H, L, mb, io)) || (st = check_eps(ln_eps))) return st;
+    if (d != 64) return fail(TTT_E_SHAPE, "d = %d: the MLP supports d = 64 only", d);
+    if (loss != TTT_LOSS_MSE && loss != TTT_LOSS_INNER_PRODUCT)
+        return fail(TTT_E_SHAPE, "inner_loss = %d is not TTT_LOSS_MSE / TTT_LOSS_INNER_PRODUCT", loss);
+    if (!(weight_decay >= 0.f) || !std::isfinite(weight_decay))
+        return fail(TTT_E_SHAPE, "weight_decay = %g is not a finite value >= 0",
+                    static_cast<double>(weight_decay));
+    const int nout = (W1_out != nullptr) + (b1_out != nullptr) + (W2_out != nullptr) + (b2_out != nullptr);
+    if (nout != 0 && nout != 4) return fail(TTT_E_NULL, "state outputs must be all NULL or all non-NULL");
+    const size_t es = io == TTT_BF16 ? 2 : 4, m = 4 * static_cast<size_t>(d);
+    const size_t nb = w0_batched ? static_cast<size_t>(B) : 1;
+    size_t xb, eb, w1b, b1b, w2b, b2b, o1, o2, o3, o4;
+    if (!nbytes(&xb, {size_t(B), size_t(H), size_t(L), size_t(d), es}) ||
+        !nbytes(&eb, {size_t(B), size_t(H), size_t(L), sizeof(float)}) ||
+        !nbytes(&w1b, {nb, size_t(H), size_t(d), m, sizeof(float)}) ||
+        !nbytes(&b1b, {nb, size_t(H), m, sizeof(float)}) ||
+        !nbytes(&w2b, {nb, size_t(H), m, size_t(d), sizeof(float)}) ||
+        !nbytes(&b2b, {nb, size_t(H), size_t(d), sizeof(float)}) ||
+        !nbytes(&o1, {size_t(B), size_t(H), size_t(d), m, sizeof(float)}) ||
+        !nbytes(&o2, {size_t(B), size_t(H), m, sizeof(float)}) ||
+        !nbytes(&o3, {size_t(B), size_t(H), m, size_t(d), sizeof(float)}) ||
+        !nbytes(&o4, {size_t(B), size_t(H), size_t(d), sizeof(float)}))
+        return fail(TTT_E_SHAPE, "sizes overflow");
+    const size_t pb = static_cast<size_t>(H) * d * sizeof(float);
+    const Buf in[] = {{XQ, xb, "XQ", false, 16}, {XK, xb, "XK", false, 16},
+                      {XV, xb, "XV", false, 16}, {eta, eb, "eta", false, 4},
+                      {W1_0, w1b, "W1_0", false, 16}, {b1_0, b1b, "b1_0", false, 16},
+                      {W2_0, w2b, "W2_0", false, 16}, {b2_0, b2b, "b2_0", false, 16},
+                      {ln_gamma, pb, "ln_gamma", false, 4}, {ln_beta, pb, "ln_beta", false, 4}};
+    const Buf out[] = {{O, xb, "O", false, 16}, {W1_out, o1, "W1_out", true, 16},
+                       {b1_out, o2, "b1_out", true, 16}, {W2_out, o3, "W2_out", true, 16},
+                       {b2_out, o4, "b2_out", true, 16}};
+    if ((st = check_bufs(in, 10)) || (st = check_bufs(out, 5))) return st;
+    const int pair[] = {-1, w0_batched ? 4 : -1, w0_batched ? 5 : -1, w0_batched ? 6 : -1,
+                        w0_batched ? 7 : -1};
+    if ((st = check_alias(out, 5, in, 10, pair))) return st;
+    if (B * H == 0) return ok();
+    ttt::MLPArgs a{B, H, L, d, mb, io, ln_eps, XQ, XK, XV, eta, W1_0, b1_0, W2_0, b2_0,
+                   w0_batched ? 1 : 0, ln_gamma, ln_beta, O, W1_out, b1_out, W2_out, b2_out};
+    a.loss = loss;
+    a.wd = weight_decay;
+    if (ttt::mlp_mfma_supported(a)) return launched(ttt::launch_mlp_mfma(a, stream));
+    return launched(ttt::launch_mlp(a, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -333,43 +387,21 @@ int ttt_mlp_forward(int B, int H, int L, int d, int mb, int io, float ln_eps,
                     const float *b2_0, int w0_batched, const float *ln_gamma,
                     const float *ln_beta, void *O, float *W1_out, float *b1_out,
                     float *W2_out, float *b2_out, hipStream_t stream) {
-    int st;
-    if ((st = check_common(B, H, L, mb, io)) || (st = check_eps(ln_eps))) return st;
-    if (d != 64) return fail(TTT_E_SHAPE, "d = %d: the MLP supports d = 64 only", d);
-    const int nout = (W1_out != nullptr) + (b1_out != nullptr) + (W2_out != nullptr) + (b2_out != nullptr);
-    if (nout != 0 && nout != 4) return fail(TTT_E_NULL, "state outputs must be all NULL or all non-NULL");
-    const size_t es = io == TTT_BF16 ? 2 : 4, m = 4 * static_cast<size_t>(d);
-    const size_t nb = w0_batched ? static_cast<size_t>(B) : 1;
-    size_t xb, eb, w1b, b1b, w2b, b2b, o1, o2, o3, o4;
-    if (!nbytes(&xb, {size_t(B), size_t(H), size_t(L), size_t(d), es}) ||
-        !nbytes(&eb, {size_t(B), size_t(H), size_t(L), sizeof(float)}) ||
-        !nbytes(&w1b, {nb, size_t(H), size_t(d), m, sizeof(float)}) ||
-        !nbytes(&b1b, {nb, size_t(H), m, sizeof(float)}) ||
-        !nbytes(&w2b, {nb, size_t(H), m, size_t(d), sizeof(float)}) ||
-        !nbytes(&b2b, {nb, size_t(H), size_t(d), sizeof(float)}) ||
-        !nbytes(&o1, {size_t(B), size_t(H), size_t(d), m, sizeof(float)}) ||
-        !nbytes(&o2, {size_t(B), size_t(H), m, sizeof(float)}) ||
-        !nbytes(&o3, {size_t(B), size_t(H), m, size_t(d), sizeof(float)}) ||
-        !nbytes(&o4, {size_t(B), size_t(H), size_t(d), sizeof(float)}))
-        return fail(TTT_E_SHAPE, "sizes overflow");
-    const size_t pb = static_cast<size_t>(H) * d * sizeof(float);
-    const Buf in[] = {{XQ, xb, "XQ", false, 16}, {XK, xb, "XK", false, 16},
-                      {XV, xb, "XV", false, 16}, {eta, eb, "eta", false, 4},
-                      {W1_0, w1b, "W1_0", false, 16}, {b1_0, b1b, "b1_0", false, 16},
-                      {W2_0, w2b, "W2_0", false, 16}, {b2_0, b2b, "b2_0", false, 16},
-                      {ln_gamma, pb, "ln_gamma", false, 4}, {ln_beta, pb, "ln_beta", false, 4}};
-    const Buf out[] = {{O, xb, "O", false, 16}, {W1_out, o1, "W1_out", true, 16},
-                       {b1_out, o2, "b1_out", true, 16}, {W2_out, o3, "W2_out", true, 16},
-                       {b2_out, o4, "b2_out", true, 16}};
-    if ((st = check_bufs(in, 10)) || (st = check_bufs(out, 5))) return st;
-    const int pair[] = {-1, w0_batched ? 4 : -1, w0_batched ? 5 : -1, w0_batched ? 6 : -1,
-                        w0_batched ? 7 : -1};
-    if ((st = check_alias(out, 5, in, 10, pair))) return st;
-    if (B * H == 0) return ok();
-    ttt::MLPArgs a{B, H, L, d, mb, io, ln_eps, XQ, XK, XV, eta, W1_0, b1_0, W2_0, b2_0,
-                   w0_batched ? 1 : 0, ln_gamma, ln_beta, O, W1_out, b1_out, W2_out, b2_out};
-    if (ttt::mlp_mfma_supported(a)) return launched(ttt::launch_mlp_mfma(a, stream));
-    return launched(ttt::launch_mlp(a, stream));
+    return mlp_forward(B, H, L, d, mb, io, ln_eps, XQ, XK, XV, eta, W1_0, b1_0, W2_0, b2_0,
+                       w0_batched, ln_gamma, ln_beta, O, W1_out, b1_out, W2_out, b2_out, stream,
+                       TTT_LOSS_MSE, 0.f);
+}
+
+int ttt_mlp_forward_opts(int B, int H, int L, int d, int mb, int io, float ln_eps,
+                         const void *XQ, const void *XK, const void *XV, const float *eta,
+                         const float *W1_0, const float *b1_0, const float *W2_0,
+                         const float *b2_0, int w0_batched, const float *ln_gamma,
+                         const float *ln_beta, int inner_loss, float weight_decay, void *O,
+                         float *W1_out, float *b1_out, float *W2_out, float *b2_out,
+                         hipStream_t stream) {
+    return mlp_forward(B, H, L, d, mb, io, ln_eps, XQ, XK, XV, eta, W1_0, b1_0, W2_0, b2_0,
+                       w0_batched, ln_gamma, ln_beta, O, W1_out, b1_out, W2_out, b2_out, stream,
+                       inner_loss, weight_decay);
 }
 
 int ttt_decode_step(int B, int H, int d, int io, float ln_eps, const void *xq,

@@ -42,6 +42,8 @@ struct MLPArgs {
     const float *gamma, *beta;
     void *O;
     float *W1_out, *b1_out, *W2_out, *b2_out;
+    int loss = 0;    // 0 squared error, 1 inner product
+    float wd = 0.f;  // weight decay on W1 and W2
 };
 
 struct DecodeArgs {

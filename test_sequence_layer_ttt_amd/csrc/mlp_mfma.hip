@@ -9,6 +9,13 @@
 //   Zb1 = XQ W1 + b1 + T1 E1,   T1 = tril(XQ XK^T + 1),   Ab = gelu(Zb1)
 //   Zb2 = Ab W2 + b2 + T2 E2,   T2 = tril(Ab A^T + 1),    O = XQ + LN(Zb2)
 //   W1 += XK^T E1, b1 += 1^T E1, W2 += A^T E2, b2 += 1^T E2
+// Modular-TTT options (template): LOSS = 1 takes E2 from the inner-product
+// loss -< XK + LN(Z2), XV > (the staged row holds XV itself); DECAY adds
+// lambda/2 (||W1||^2 + ||W2||^2) at the chunk-start state, which makes the
+// weights after token t equal to d_t W + (loss updates) with
+// d_t = 1 - lambda sum_{s<=t} eta_s: XQ W1 and Ab W2 take the factor d_t of
+// their token and the chunk ends with W1, W2 scaled by d_15 (biases are not
+// decayed).
 //
 // Layout (gfx950, one 512-thread workgroup = 8 waves per (n,h) sequence, two
 // per SIMD):
@@ -77,15 +84,67 @@ __device__ __forceinline__ void normal_cdf_pdf(float x, float &Phi, float &phi) 
     phi = 0.39894228040143268f * e;
 }
 
+// E = -eta * G for one row (row layout) under the selected loss. LOSS = 0 is
+// the squared reconstruction error (tau = XV - XK); LOSS = 1 the inner product
+// -< LN(z), v > with tau = v, whose gradient through the layer norm is
+// G = rstd (ghat - mean(ghat) - xhat mean(ghat xhat)), ghat = -gamma v; with
+// gamma = 1 this is a (z - mu) - rstd (v - mean v), a = rstd^3 mean(v (z - mu)).
+template <bool IDENT, int LOSS>
+__device__ __forceinline__ f32x4 row_grad(f32x4 z, f32x4 tau, float mutau, float eta_r,
+                                          const float (&gam)[4], const float (&bet)[4],
+                                          float eps) {
+    if constexpr (LOSS == 0) {
+        return ln_bwd_row<IDENT>(z, tau, mutau, eta_r, gam, bet, eps);
+    } else {
+        constexpr float inv_d = 1.0f / D;
+        f32x4 ev;
+        if constexpr (IDENT) {
+            const float s1 = row16_sum((z[0] + z[1]) + (z[2] + z[3]));
+            const float s2 = row16_sum(z[0] * z[0] + z[1] * z[1] + z[2] * z[2] + z[3] * z[3]);
+            const float s3 = row16_sum(tau[0] * z[0] + tau[1] * z[1] + tau[2] * z[2] + tau[3] * z[3]);
+            const float mu = s1 * inv_d;
+            const float rstd = rsqrtf(fmaxf(s2 * inv_d - mu * mu, 0.f) + eps);
+            const float a = rstd * rstd * rstd * (s3 * inv_d - mutau * mu);
+            const float cz = -eta_r * a, ct = eta_r * rstd;
+            const float c0 = eta_r * (a * mu - rstd * mutau);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ev[e] = fmaf(cz, z[e], fmaf(ct, tau[e], c0));
+        } else {
+            const float mu = row16_sum((z[0] + z[1]) + (z[2] + z[3])) * inv_d;
+            float cz[4], s2 = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                cz[e] = z[e] - mu;
+                s2 += cz[e] * cz[e];
+            }
+            const float rstd = rsqrtf(row16_sum(s2) * inv_d + eps);
+            float xh[4], gh[4], a1 = 0.f, a2 = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                xh[e] = cz[e] * rstd;
+                gh[e] = -gam[e] * tau[e];
+                a1 += gh[e];
+                a2 += gh[e] * xh[e];
+            }
+            const float m1 = row16_sum(a1) * inv_d, m2 = row16_sum(a2) * inv_d;
+            const float ne = -eta_r * rstd;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ev[e] = ne * (gh[e] - m1 - xh[e] * m2);
+        }
+        return ev;
+    }
+}
+
 }  // namespace
 
+template <int LOSS, bool DECAY>
 __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
     int H, int L, float eps, const bf16_t *__restrict__ XQ, const bf16_t *__restrict__ XK,
     const bf16_t *__restrict__ XV, const float *__restrict__ eta,
     const float *__restrict__ W1_0, const float *__restrict__ b1_0,
     const float *__restrict__ W2_0, const float *__restrict__ b2_0, int w0_batched,
     const float *__restrict__ gamma, const float *__restrict__ beta, bf16_t *__restrict__ O,
-    float *W1_out, float *b1_out, float *W2_out, float *b2_out) {
+    float *W1_out, float *b1_out, float *W2_out, float *b2_out, float wd) {
     __shared__ MlpSmem sm;
 
     const int tid = threadIdx.x;
@@ -172,7 +231,7 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
         S.xkt[(f0 + 2) * KS + r] = static_cast<uint16_t>(kh.y & 0xffffu);
         S.xkt[(f0 + 3) * KS + r] = static_cast<uint16_t>(kh.y >> 16);
         *reinterpret_cast<f32x4 *>(&S.xqf[r * RS + f0]) = qf;
-        const f32x4 tau = unpack4(v) - kf;
+        const f32x4 tau = LOSS == 1 ? unpack4(v) : unpack4(v) - kf;
         *reinterpret_cast<f32x4 *>(&S.tau[r * RS + f0]) = tau;
         const float mt = row16_sum((tau[0] + tau[1]) + (tau[2] + tau[3])) * (1.0f / D);
         if (c == 0) {
@@ -195,6 +254,18 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
         float *P = sm.part[w] + (4 * g) * RS + c;
 
         // ===== A: Z1^T, A = gelu(Z1), Z2 partials, T1, A transposed ============
+        // decay: dc = d_t of this lane's token column c, alpha = d_15
+        float dc = 1.f, alpha = 1.f;
+        if constexpr (DECAY) {
+            float run = 0.f, cum = 0.f;
+#pragma unroll
+            for (int s = 0; s < MB; ++s) {
+                run += S.eta[s];
+                cum = s == c ? run : cum;
+            }
+            dc = fmaf(-wd, cum, 1.f);
+            alpha = fmaf(-wd, run, 1.f);
+        }
         f16x8 xkf[2], xqf[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -207,7 +278,13 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
             const f16x8 wa = w1frag(t, 0), wb = w1frag(t, 1);
             f32x4 z = mfma32h(wa, xkf[0], b1v[t]);
             z = mfma32h(wb, xkf[1], z);
-            zq[t] = mfma32h(wb, xqf[1], mfma32h(wa, xqf[0], b1v[t]));  // (XQ W1 + b1)^T
+            if constexpr (DECAY) {  // (d_t XQ W1 + b1)^T
+                const f32x4 p = mfma32h(wb, xqf[1], mfma32h(wa, xqf[0], fzero));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) zq[t][i] = fmaf(dc, p[i], b1v[t][i]);
+            } else {
+                zq[t] = mfma32h(wb, xqf[1], mfma32h(wa, xqf[0], b1v[t]));  // (XQ W1 + b1)^T
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float Phi, phi;
@@ -242,8 +319,8 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
 #pragma unroll
             for (int q = 1; q < NW; ++q) z2 += *reinterpret_cast<const f32x4 *>(&sm.part[q][r * RS + f0]);
             const f32x4 tau = *reinterpret_cast<const f32x4 *>(&S.tau[r * RS + f0]);
-            const f32x4 ev = ident ? ln_bwd_row<true>(z2, tau, S.mutau[r], S.eta[r], gam, bet, eps)
-                                   : ln_bwd_row<false>(z2, tau, S.mutau[r], S.eta[r], gam, bet, eps);
+            const f32x4 ev = ident ? row_grad<true, LOSS>(z2, tau, S.mutau[r], S.eta[r], gam, bet, eps)
+                                   : row_grad<false, LOSS>(z2, tau, S.mutau[r], S.eta[r], gam, bet, eps);
             const uint32_t p01 = pack2h(ev[0], ev[1]), p23 = pack2h(ev[2], ev[3]);
             *reinterpret_cast<uint2 *>(&sm.e2[r * RS + f0]) = make_uint2(p01, p23);
             sm.e2t[(f0 + 0) * KS + r] = static_cast<uint16_t>(p01 & 0xffffu);
@@ -298,6 +375,8 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
             }
         }
         const f16x8 Abf = pack8h(Ab[0], Ab[1]);
+        // A operand of Ab W2 (token c rows), with the decay factor of the token
+        const f16x8 Abw = DECAY ? pack8h(Ab[0] * dc, Ab[1] * dc) : Abf;
         // This wave's share of T2 E2: the causal mask is linear, so
         // tril(Ab A^T + 1) E2 = sum over waves of tril(Ab_w A_w^T) E2, plus
         // tril(1) E2 added once (wave 0). The partial Gram
@@ -312,7 +391,7 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
         // chunk-start b2 tile u from wave u
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const f32x4 acc = mfma16h(t2h, e2b[u], mfma32h(Abf, W2f[u], w == u ? b2w : fzero));
+            const f32x4 acc = mfma16h(t2h, e2b[u], mfma32h(Abw, W2f[u], w == u ? b2w : fzero));
 #pragma unroll
             for (int i = 0; i < 4; ++i) P[i * RS + 16 * u] = acc[i];
         }
@@ -322,6 +401,16 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb)
                 xkt[rb] = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(&S.xkt[(16 * rb + c) * KS + 4 * g]));
+            if constexpr (DECAY) {  // W <- d_15 W before the loss updates
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int rb = 0; rb < 4; ++rb) W1v[t][rb] = W1v[t][rb] * alpha;
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int rb = 0; rb < 2; ++rb) W2v[u][rb] = W2v[u][rb] * alpha;
+            }
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -385,16 +474,26 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
     }
 }
 
-bool mlp_mfma_supported(const MLPArgs &a) { return a.io == 1 && a.d == 64 && a.mb == 16; }
+bool mlp_mfma_supported(const MLPArgs &a) {
+    return a.io == 1 && a.d == 64 && a.mb == 16 && (a.loss == 0 || a.loss == 1);
+}
 
-hipError_t launch_mlp_mfma(const MLPArgs &a, hipStream_t stream) {
-    if (a.B * a.H == 0) return hipSuccess;
-    hipLaunchKernelGGL(mlp_prefill_mfma, dim3(a.B * a.H), dim3(NT), 0, stream, a.H, a.L, a.eps,
+template <int LOSS, bool DECAY>
+static hipError_t launch_mlp_mfma_t(const MLPArgs &a, hipStream_t stream) {
+    hipLaunchKernelGGL((mlp_prefill_mfma<LOSS, DECAY>), dim3(a.B * a.H), dim3(NT), 0, stream, a.H, a.L, a.eps,
                        static_cast<const bf16_t *>(a.XQ), static_cast<const bf16_t *>(a.XK),
                        static_cast<const bf16_t *>(a.XV), a.eta, a.W1, a.b1, a.W2, a.b2,
                        a.w0_batched, a.gamma, a.beta, static_cast<bf16_t *>(a.O), a.W1_out,
-                       a.b1_out, a.W2_out, a.b2_out);
+                       a.b1_out, a.W2_out, a.b2_out, a.wd);
     return hipGetLastError();
+}
+
+hipError_t launch_mlp_mfma(const MLPArgs &a, hipStream_t stream) {
+    if (a.B * a.H == 0) return hipSuccess;
+    const bool decay = a.wd != 0.f;
+    if (a.loss == 1)
+        return decay ? launch_mlp_mfma_t<1, true>(a, stream) : launch_mlp_mfma_t<1, false>(a, stream);
+    return decay ? launch_mlp_mfma_t<0, true>(a, stream) : launch_mlp_mfma_t<0, false>(a, stream);
 }
 
 }  // namespace ttt

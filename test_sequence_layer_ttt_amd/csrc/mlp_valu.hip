@@ -13,19 +13,25 @@
 //   Zb2 = Ab W2 + b2 - M2 G2,     M2[t,s] = eta_s (Ab_t . A_s + 1)
 //   O = XQ + LN(Zb2)
 //   W1 -= (eta XK)^T G1, b1 -= eta^T G1, W2 -= (eta A)^T G2, b2 -= eta^T G2
+// Modular-TTT options (template): LOSS = 1 takes G2 from the inner-product
+// loss -< XK + LN(Z2), XV > (target XV, no subtraction); DECAY adds
+// lambda/2 (||W1||^2 + ||W2||^2) at the chunk-start state, so after token t
+// the weights are d_t W + (loss updates), d_t = 1 - lambda sum_{s<=t} eta_s:
+// the XQ W1 and Ab W2 products take a row factor d_t and the chunk ends with
+// W scaled by d_last (the biases are not decayed).
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace ttt {
 
-template <typename TIO>
+template <typename TIO, int LOSS, bool DECAY>
 __global__ __launch_bounds__(256) void mlp_prefill_valu(
     int H, int L, int mb, float eps, const TIO *__restrict__ XQ, const TIO *__restrict__ XK,
     const TIO *__restrict__ XV, const float *__restrict__ eta, const float *__restrict__ W1_0,
     const float *__restrict__ b1_0, const float *__restrict__ W2_0,
     const float *__restrict__ b2_0, int w0_batched, const float *__restrict__ gamma,
     const float *__restrict__ beta, TIO *__restrict__ O, float *W1_out, float *b1_out,
-    float *W2_out, float *b2_out) {
+    float *W2_out, float *b2_out, float wd) {
     constexpr int D = 64, M = 256, MB = 16, NT = 256, DP = D + 1, MP = M + 1, E = D / 16;
     using io = io_traits<TIO>;
 
@@ -35,7 +41,7 @@ __global__ __launch_bounds__(256) void mlp_prefill_valu(
     __shared__ float sDA[MB * MP], sG1[MB * MP];  // gelu'(Z1), G1
     __shared__ float sQ[MB * DP], sK[MB * DP];
     __shared__ float sT[MB * D], sG2[MB * D], sZ2[MB * D];
-    __shared__ float sEta[MB], sM[MB * MB];
+    __shared__ float sEta[MB], sM[MB * MB], sDec[MB];
 
     const int tid = threadIdx.x;
     const long seq = blockIdx.x;
@@ -77,11 +83,17 @@ __global__ __launch_bounds__(256) void mlp_prefill_valu(
             }
             sQ[s * DP + j] = q;
             sK[s * DP + j] = kk;
-            sT[s * D + j] = v - kk;
+            sT[s * D + j] = LOSS == 1 ? v : v - kk;
         }
         if (tid < MB) sEta[tid] = tid < len ? eta[ebase + t0 + tid] : 0.f;
         __syncthreads();
 
+        // decay factors d_t (eta is 0 past the end of the sequence)
+        if (DECAY && tid < MB) {
+            float a = 0.f;
+            for (int s = 0; s <= tid; ++s) a += sEta[s];
+            sDec[tid] = 1.f - wd * a;
+        }
         // Z1 column k, A = gelu(Z1), gelu'(Z1)
 #pragma unroll 1
         for (int s = 0; s < MB; ++s) {
@@ -116,7 +128,10 @@ __global__ __launch_bounds__(256) void mlp_prefill_valu(
                 z[e] = sZ2[rrow * D + rl + 16 * e];
                 tau[e] = sT[rrow * D + rl + 16 * e];
             }
-            ln_l2_grad<16, E>(z, tau, gam, bet, 1.0f / D, eps, g);
+            if constexpr (LOSS == 1)
+                ln_ip_grad<16, E>(z, tau, gam, 1.0f / D, eps, g);
+            else
+                ln_l2_grad<16, E>(z, tau, gam, bet, 1.0f / D, eps, g);
 #pragma unroll
             for (int e = 0; e < E; ++e) sG2[rrow * D + rl + 16 * e] = rrow < len ? g[e] : 0.f;
             const int t = tid / MB, s = tid % MB;
@@ -136,9 +151,10 @@ __global__ __launch_bounds__(256) void mlp_prefill_valu(
         }
 #pragma unroll 1
         for (int t = 0; t < MB; ++t) {
-            float acc = b1;
+            float acc = DECAY ? 0.f : b1;
 #pragma unroll
             for (int i = 0; i < D; ++i) acc += sQ[t * DP + i] * w1[i];
+            if constexpr (DECAY) acc = fmaf(sDec[t], acc, b1);
 #pragma unroll 4
             for (int s = 0; s < MB; ++s) acc -= sM[t * MB + s] * sG1[s * MP + k];
             sAb[t * MP + k] = gelu_f(acc);
@@ -158,11 +174,15 @@ __global__ __launch_bounds__(256) void mlp_prefill_valu(
         {
             float acc[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = sb2[cj];
+            for (int r = 0; r < 4; ++r) acc[r] = DECAY ? 0.f : sb2[cj];
             for (int q = 0; q < M; ++q) {
                 const float w = sW2[q * DP + cj];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[r] += sAb[(cs0 + 4 * r) * MP + q] * w;
+            }
+            if constexpr (DECAY) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] = fmaf(sDec[cs0 + 4 * r], acc[r], sb2[cj]);
             }
             for (int s = 0; s < MB; ++s) {
                 const float gs = sG2[s * D + cj];
@@ -187,6 +207,11 @@ __global__ __launch_bounds__(256) void mlp_prefill_valu(
                     io::store(O, xbase + static_cast<size_t>(t0 + rrow) * D + j, sQ[rrow * DP + j] + y[e]);
                 }
             }
+            const float alpha = DECAY ? sDec[MB - 1] : 1.f;
+            if constexpr (DECAY) {
+#pragma unroll
+                for (int i = 0; i < D; ++i) w1[i] *= alpha;
+            }
             float db1 = 0.f;
 #pragma unroll 1
             for (int s = 0; s < MB; ++s) {
@@ -201,7 +226,10 @@ __global__ __launch_bounds__(256) void mlp_prefill_valu(
                 float acc = 0.f;
 #pragma unroll
                 for (int s = 0; s < MB; ++s) acc += sEta[s] * sA[s * MP + q] * sG2[s * D + j];
-                sW2[q * DP + j] -= acc;
+                if constexpr (DECAY)
+                    sW2[q * DP + j] = fmaf(alpha, sW2[q * DP + j], -acc);
+                else
+                    sW2[q * DP + j] -= acc;
             }
             if (tid < D) {
                 float acc = 0.f;
@@ -222,20 +250,28 @@ __global__ __launch_bounds__(256) void mlp_prefill_valu(
     }
 }
 
-template <typename TIO>
+template <typename TIO, int LOSS, bool DECAY>
 static hipError_t launch_mlp_t(const MLPArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL((mlp_prefill_valu<TIO>), dim3(a.B * a.H), dim3(256), 0, stream, a.H, a.L,
+    hipLaunchKernelGGL((mlp_prefill_valu<TIO, LOSS, DECAY>), dim3(a.B * a.H), dim3(256), 0, stream, a.H, a.L,
                        a.mb, a.eps, static_cast<const TIO *>(a.XQ),
                        static_cast<const TIO *>(a.XK), static_cast<const TIO *>(a.XV), a.eta,
                        a.W1, a.b1, a.W2, a.b2, a.w0_batched, a.gamma, a.beta,
-                       static_cast<TIO *>(a.O), a.W1_out, a.b1_out, a.W2_out, a.b2_out);
+                       static_cast<TIO *>(a.O), a.W1_out, a.b1_out, a.W2_out, a.b2_out, a.wd);
     return hipGetLastError();
+}
+
+template <typename TIO>
+static hipError_t launch_mlp_io(const MLPArgs &a, hipStream_t stream) {
+    const bool decay = a.wd != 0.f;
+    if (a.loss == 1)
+        return decay ? launch_mlp_t<TIO, 1, true>(a, stream) : launch_mlp_t<TIO, 1, false>(a, stream);
+    return decay ? launch_mlp_t<TIO, 0, true>(a, stream) : launch_mlp_t<TIO, 0, false>(a, stream);
 }
 
 hipError_t launch_mlp(const MLPArgs &a, hipStream_t stream) {
     if (a.B * a.H == 0) return hipSuccess;
-    if (a.d != 64) return hipErrorInvalidValue;
-    return a.io ? launch_mlp_t<bf16_t>(a, stream) : launch_mlp_t<float>(a, stream);
+    if (a.d != 64 || (a.loss != 0 && a.loss != 1)) return hipErrorInvalidValue;
+    return a.io ? launch_mlp_io<bf16_t>(a, stream) : launch_mlp_io<float>(a, stream);
 }
 
 }  // namespace ttt

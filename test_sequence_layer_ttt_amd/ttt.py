@@ -238,11 +238,32 @@ def ttt_mlp_forward(XQ, XK, XV, eta, W1, b1, W2, b2, ln_gamma, ln_beta, O=None, 
     """TTT-MLP prefill (d = 64, hidden 4d). W1 [.,H,d,4d], b1 [.,H,4d],
     W2 [.,H,4d,d], b2 [.,H,d] with "." = B when per batch. Returns
     (O, W1_out, b1_out, W2_out, b2_out)."""
+    return _mlp(XQ, XK, XV, eta, W1, b1, W2, b2, ln_gamma, ln_beta, O, outs, mb, ln_eps, stream,
+                None, 0.0)
+
+
+def ttt_mlp_forward_opts(XQ, XK, XV, eta, W1, b1, W2, b2, ln_gamma, ln_beta,
+                         inner_loss: str = "mse", weight_decay: float = 0.0, O=None, outs=None,
+                         mb: int = 16, ln_eps: float = 1e-6, stream=None):
+    """TTT-MLP prefill with the inner loss ("mse" or "inner_product") and
+    weight decay on W1, W2 as options; the rest as ttt_mlp_forward."""
+    return _mlp(XQ, XK, XV, eta, W1, b1, W2, b2, ln_gamma, ln_beta, O, outs, mb, ln_eps, stream,
+                inner_loss, weight_decay)
+
+
+def _mlp(XQ, XK, XV, eta, W1, b1, W2, b2, ln_gamma, ln_beta, O, outs, mb, ln_eps, stream,
+         inner_loss, weight_decay):
     B, H, L, d = XQ.shape
     m = 4 * d
     io = _IO.get(XQ.dtype)
     if io is None:
         raise TypeError(f"XQ dtype {XQ.dtype} not supported")
+    loss = None
+    if inner_loss is not None:
+        loss = {"mse": _lib.TTT_LOSS_MSE,
+                "inner_product": _lib.TTT_LOSS_INNER_PRODUCT}.get(inner_loss)
+        if loss is None:
+            raise ValueError(f"inner_loss {inner_loss!r} is not 'mse' or 'inner_product'")
     batched = W1.dim() == 4
     pre = (B,) if batched else ()
     for t, n in ((XQ, "XQ"), (XK, "XK"), (XV, "XV")):
@@ -265,10 +286,13 @@ def ttt_mlp_forward(XQ, XK, XV, eta, W1, b1, W2, b2, ln_gamma, ln_beta, O=None, 
                        ((B, H, d, m), (B, H, m), (B, H, m, d), (B, H, d))):
         _need(t, n, s, torch.float32)
     lib = _lib.load()
-    _lib.check(lib.ttt_mlp_forward(B, H, L, d, mb, io, ln_eps, _ptr(XQ), _ptr(XK), _ptr(XV),
-                                   _ptr(eta), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
-                                   int(batched), _ptr(ln_gamma), _ptr(ln_beta), _ptr(O),
-                                   *(_ptr(t) for t in outs), _stream(stream)))
+    head = (B, H, L, d, mb, io, ln_eps, _ptr(XQ), _ptr(XK), _ptr(XV), _ptr(eta), _ptr(W1),
+            _ptr(b1), _ptr(W2), _ptr(b2), int(batched), _ptr(ln_gamma), _ptr(ln_beta))
+    tail = (_ptr(O),) + tuple(_ptr(t) for t in outs) + (_stream(stream),)
+    if loss is None:
+        _lib.check(lib.ttt_mlp_forward(*head, *tail))
+    else:
+        _lib.check(lib.ttt_mlp_forward_opts(*head, loss, float(weight_decay), *tail))
     return (O,) + tuple(outs)
 
 

@@ -249,6 +249,23 @@ def test_linear_forward_opts_validation(lib):
     assert _opts(lib, loss=1, wd=0.5, B=0) == _lib.TTT_OK
 
 
+def _mlp_opts(lib, loss=0, wd=0.0, B=1, d=64):
+    p = [FAKE + i * (1 << 20) for i in range(15)]
+    return lib.ttt_mlp_forward_opts(B, 1, 16, d, 16, 1, 1e-6, *p[:8], 0, p[8], p[9], loss, wd,
+                                    *p[10:15], None)
+
+
+def test_mlp_forward_opts_validation(lib):
+    assert _mlp_opts(lib, loss=2) == _lib.TTT_E_SHAPE
+    assert "inner_loss" in lib.ttt_last_error().decode()
+    assert _mlp_opts(lib, loss=-1) == _lib.TTT_E_SHAPE
+    for bad in (-0.1, float("inf"), float("nan")):
+        assert _mlp_opts(lib, wd=bad) == _lib.TTT_E_SHAPE
+        assert "weight_decay" in lib.ttt_last_error().decode()
+    assert _mlp_opts(lib, d=32) == _lib.TTT_E_SHAPE
+    assert _mlp_opts(lib, loss=1, wd=0.5, B=0) == _lib.TTT_OK
+
+
 def _gate(lib, B=2, H=3, L=40, d=64, io=1, xk=FAKE, th=FAKE + (1 << 20), eta_base=0.5,
           eta=FAKE + 2 * (1 << 20)):
     return lib.ttt_eta_gate(B, H, L, d, io, xk, th, eta_base, eta, None)
