@@ -38,10 +38,14 @@
 //  * contractions over all 256 hidden units (Z2 and Zb2) are summed across
 //    the eight waves through LDS. T2 E2 needs no sum of its own: masking is
 //    linear, so each wave adds tril(Ab_w A_w^T) E2 over its own hidden units
-//    to its Zb2 partial (and wave 0 the tril(1) E2 term). Waves 0-3 also run the
-//    row-layout work (16 lanes per token, DPP reductions) and load the input
-//    rows of their four tokens one chunk ahead; a chunk is staged into LDS a
-//    full iteration after its loads were issued.
+//    to its Zb2 partial (and wave 0 the tril(1) E2 term).
+//  * row-layout work (16 lanes per token, DPP reductions): waves 0-3 run the
+//    LN backward (Z2 -> E2) and load the input rows of their four tokens one
+//    chunk ahead, staging a chunk into LDS a full iteration after its loads
+//    were issued. Waves 4-7 emit O = XQ + LN(Zb2) of a chunk during the next
+//    chunk's first phase, from Zb2 partials kept in a buffer of their own;
+//    three LDS slots hold the previous chunk (its XQ rows for O), the current
+//    one and the next. Three barriers per chunk.
 //  * GELU: x Phi(x) with erf from Abramowitz & Stegun 7.1.26 (|error| <=
 //    1.5e-7, far below the resolution of the MFMA operands); GELU and its
 //    derivative share one exponential.
@@ -65,8 +69,9 @@ constexpr int NW = 8, NT = 64 * NW;
 constexpr int NRW = 4;       // waves running the row-layout work (16 tokens x 16 lanes)
 
 struct alignas(16) MlpSmem {
-    Slot slot[2];
-    alignas(16) float part[NW][MB * RS];  // per-wave partial sums of Z2 / Zb2
+    Slot slot[3];                          // chunks c - 1 (its XQ rows for O), c, c + 1
+    alignas(16) float part[NW][MB * RS];   // per-wave partial sums of Z2
+    alignas(16) float partb[NW][MB * RS];  // per-wave partial sums of Zb2 (read one chunk later)
     alignas(16) uint16_t e2[MB * RS];         // E2, fp16 rows [token][out]
     alignas(16) uint16_t e2t[D * KS];         // E2 transposed, fp16 [out][token]
 };
@@ -134,6 +139,8 @@ __device__ __forceinline__ f32x4 row_grad(f32x4 z, f32x4 tau, float mutau, float
         return ev;
     }
 }
+
+static_assert(sizeof(MlpSmem) <= 160 * 1024, "MLP prefill LDS exceeds 160 KB");
 
 }  // namespace
 
@@ -218,7 +225,7 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
         R.eta = et[tok];
     };
     auto stage = [&](int ch) {
-        Slot &S = sm.slot[ch & 1];
+        Slot &S = sm.slot[ch % 3];
         const bool ok = ch * MB + r < L;
         const uint2 z2 = make_uint2(0u, 0u);
         const uint2 q = ok ? R.q : z2, k = ok ? R.k : z2, v = ok ? R.v : z2;
@@ -246,14 +253,39 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
     }
     lds_barrier();
 
+    // O = XQ + LN(Zb2) of chunk ch from the Zb2 partials (row layout; waves 4-7)
+    auto emit_out = [&](int ch) {
+        const Slot &Sp = sm.slot[ch % 3];
+        f32x4 zb2 = *reinterpret_cast<const f32x4 *>(&sm.partb[0][r * RS + f0]);
+#pragma unroll
+        for (int q = 1; q < NW; ++q) zb2 += *reinterpret_cast<const f32x4 *>(&sm.partb[q][r * RS + f0]);
+        const f32x4 xqv = *reinterpret_cast<const f32x4 *>(&Sp.xqf[r * RS + f0]);
+        const f32x4 o = ident ? ln_fwd_row<true>(zb2, xqv, gam, bet, eps)
+                              : ln_fwd_row<false>(zb2, xqv, gam, bet, eps);
+        if (ch * MB + r < L)
+            *reinterpret_cast<uint2 *>(O + xbase + static_cast<uint32_t>((ch * MB + r) * D + f0)) =
+                make_uint2(pack2(o[0], o[1]), pack2(o[2], o[3]));
+    };
+
     auto w1frag = [&](int t, int kb) { return pack8h(W1v[t][2 * kb], W1v[t][2 * kb + 1]); };
     auto rowh = [&](const uint16_t *tile, int kb) { return __builtin_bit_cast(f16x8, row_frag(tile, c, g, kb)); };
 
     for (int ch = 0; ch < nch; ++ch) {
-        const Slot &S = sm.slot[ch & 1];
+        const Slot &S = sm.slot[ch % 3];
         float *P = sm.part[w] + (4 * g) * RS + c;
 
         // ===== A: Z1^T, A = gelu(Z1), Z2 partials, T1, A transposed ============
+        // Row work beside it: waves 0-3 stage the next chunk (its slot last
+        // served chunk ch - 2) and load the one after; waves 4-7 emit O of the
+        // previous chunk from the Zb2 partials of phase C.
+        if (roww) {
+            if (ch + 1 < nch) {
+                stage(ch + 1);
+                load(ch + 2);
+            }
+        } else if (ch > 0) {
+            emit_out(ch - 1);
+        }
         // decay: dc = d_t of this lane's token column c, alpha = d_15
         float dc = 1.f, alpha = 1.f;
         if constexpr (DECAY) {
@@ -389,11 +421,12 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
         const s16x4 t2h = pack4h(t2);
         // Zb2 partials: Ab_w W2_w + tril(Ab_w A_w^T (+1)) E2, plus the
         // chunk-start b2 tile u from wave u
+        float *Pb = sm.partb[w] + (4 * g) * RS + c;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const f32x4 acc = mfma16h(t2h, e2b[u], mfma32h(Abw, W2f[u], w == u ? b2w : fzero));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) P[i * RS + 16 * u] = acc[i];
+            for (int i = 0; i < 4; ++i) Pb[i * RS + 16 * u] = acc[i];
         }
         // state update (the forward products above used the chunk-start state)
         {
@@ -427,25 +460,8 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
             }
         }
         lds_barrier();
-
-        // ===== E (row layout): stage the next chunk, O = XQ + LN(Zb2) ========
-        if (roww) {
-            f32x4 zb2 = *reinterpret_cast<const f32x4 *>(&sm.part[0][r * RS + f0]);
-#pragma unroll
-            for (int q = 1; q < NW; ++q) zb2 += *reinterpret_cast<const f32x4 *>(&sm.part[q][r * RS + f0]);
-            const f32x4 xqv = *reinterpret_cast<const f32x4 *>(&S.xqf[r * RS + f0]);
-            if (ch + 1 < nch) {
-                stage(ch + 1);
-                load(ch + 2);
-            }
-            const f32x4 o = ident ? ln_fwd_row<true>(zb2, xqv, gam, bet, eps)
-                                  : ln_fwd_row<false>(zb2, xqv, gam, bet, eps);
-            if (ch * MB + r < L)
-                *reinterpret_cast<uint2 *>(O + xbase + static_cast<uint32_t>((ch * MB + r) * D + f0)) =
-                    make_uint2(pack2(o[0], o[1]), pack2(o[2], o[3]));
-        }
-        lds_barrier();
     }
+    if (!roww && nch > 0) emit_out(nch - 1);  // O of the last chunk
 
     if (W1_out) {
         // Recompute the lane coordinates here (opaque copy) instead of keeping
