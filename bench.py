@@ -121,8 +121,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="3", choices=["3", "2", "5p", "4", "4o", "5d", "5r", "5m", "3b", "3g", "3gb",
-                             "3o"])
+    ap.add_argument("--workload", default="3", choices=["3", "2", "5p", "4", "4o", "4g", "5d", "5r", "5m", "3b", "3g",
+                             "3gb", "3o"])
     ap.add_argument("--peaks", action="store_true",
                     help="measure achievable HBM copy bandwidth and bf16 GEMM throughput (context)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -157,6 +157,8 @@ def main():
         return bench_mlp(args)
     if args.workload == "4o":
         return bench_mlp(args, opts=True)
+    if args.workload == "4g":
+        return bench_mlp(args, gated=True)
     if args.workload == "5d":
         return bench_decode(args)
     if args.workload == "5r":
@@ -319,9 +321,11 @@ def _line(metric, value, args, wall_step, dtype, config, roofline, extra=None):
     print(json.dumps(out), flush=True)
 
 
-def bench_mlp(args, opts=False):
+def bench_mlp(args, opts=False, gated=False):
     """TTT-MLP prefill, workload 4 (B=2, H=12, L=8192, d=64, hidden 256); with
-    opts, the inner-product loss and weight decay 0.5 on W1 and W2."""
+    opts, the inner-product loss and weight decay 0.5 on W1 and W2; with
+    gated, eta from the learning-rate gate inside the kernel (theta_lr drawn
+    N(0, 0.02^2) from seed 1004, eta_base = 1/d)."""
     import numpy as np
     import torch
     from test_sequence_layer_ttt_amd import gen, ttt
@@ -337,7 +341,13 @@ def bench_mlp(args, opts=False):
     outs = (torch.empty((B, H, d, 4 * d), **kw), torch.empty((B, H, 4 * d), **kw),
             torch.empty((B, H, 4 * d, d), **kw), torch.empty((B, H, d), **kw))
     stream = torch.cuda.current_stream()
-    if opts:
+    if gated:
+        theta_np = (0.02 * np.random.default_rng(1004).standard_normal((H, d))).astype(np.float32)
+        theta, eta_base = T(theta_np), 1.0 / d
+        gins = ins[:3] + [theta, eta_base] + ins[4:]
+        step = lambda: ttt.ttt_mlp_forward_gated(*gins, O=O, outs=outs, ln_eps=x.eps,
+                                                 stream=stream)
+    elif opts:
         step = lambda: ttt.ttt_mlp_forward_opts(*ins, "inner_product", 0.5, O=O, outs=outs,
                                                 ln_eps=x.eps, stream=stream)
     else:
@@ -355,16 +365,18 @@ def bench_mlp(args, opts=False):
         run = (lambda *a, **k: oracle.mlp_forward_opts(*a, loss="inner_product",
                                                        weight_decay=0.5, **k)) if opts \
             else oracle.mlp_forward
-        run(x.XQ, x.XK, x.XV, x.eta, x.W1, x.b1, x.W2, x.b2, x.gamma, x.beta, x.eps, mb=16,
+        eta = oracle.eta_gate(x.XK, theta_np, eta_base) if gated else x.eta
+        run(x.XQ, x.XK, x.XV, eta, x.W1, x.b1, x.W2, x.b2, x.gamma, x.beta, x.eps, mb=16,
             nthreads=nt)
         tc = time.perf_counter() - t1
         extra["cpu_baseline"] = {"value": B * L / tc, "unit": "tokens/s", "cores": nt,
                                  "kind": "oracle",
                                  "sample": f"full workload (B={B}, H={H}, L={L}), fp64 primal "
                                            f"form, {nt} threads over (n,h), {tc:.2f} s"}
-    tag = ", inner-product loss, weight decay 0.5" if opts else ""
+    tag = ", inner-product loss, weight decay 0.5" if opts else (", gated eta" if gated else "")
     _line(f"TTT-MLP prefill tokens/s (L={L}{tag})", B * L / wall, args, wall, "bf16",
-          {"workload": gen.WORKLOADS[4].name + ("+ip_loss+wd" if opts else ""), "B": B, "H": H, "L": L, "d": d, "hidden": 4 * d,
+          {"workload": gen.WORKLOADS[4].name + ("+ip_loss+wd" if opts else "")
+           + ("+eta_gate" if gated else ""), "B": B, "H": H, "L": L, "d": d, "hidden": 4 * d,
            "mini_batch": 16, "io": "bf16", "state": "fp32", "parallelism": "none (1 GPU)"},
           roof, extra)
 

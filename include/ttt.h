@@ -142,7 +142,7 @@ int ttt_linear_forward_opts(int B, int H, int L, int d, int mb, int io, float ln
 
 /*
  * The learning-rate gate of [Y] §2.2 on its own, for the paths that take eta
- * as an array (MLP prefill, decode, the backward):
+ * as an array (decode, the backward, the prefills with the loss options):
  *   eta[n,h,t] = eta_base * logistic(theta_lr[h] . XK[n,h,t]).
  *   B, H, L >= 0; d in {16, 32, 64}; io as above.
  *   XK [B,H,L,d] io, 16-byte aligned; theta_lr [H,d] fp32; eta [B,H,L] fp32,
@@ -187,6 +187,24 @@ int ttt_mlp_forward(int B, int H, int L, int d, int mb, int io, float ln_eps,
                     const float *b2_0, int w0_batched, const float *ln_gamma,
                     const float *ln_beta, void *O, float *W1_out, float *b1_out,
                     float *W2_out, float *b2_out, hipStream_t stream);
+
+/*
+ * ttt_mlp_forward with each token's rate taken from the learning-rate gate of
+ * [Y] §2.2 while the kernel stages the token (no eta array is read):
+ *   eta_t = eta_base * logistic(theta_lr[h] . XK_t),  logistic(s) = 1/(1+e^-s),
+ * the gate input x read as the head's key XK_t, as in ttt_linear_forward_gated.
+ *   theta_lr : [H,d] fp32, 16-byte aligned.  eta_base : finite, else TTT_E_SHAPE.
+ * Every other argument, and the numerics, as ttt_mlp_forward; the gate itself
+ * is evaluated in fp32 (on the bf16 mb = 16 path with the hardware exp2 and
+ * reciprocal, about 1 ulp each).
+ */
+int ttt_mlp_forward_gated(int B, int H, int L, int d, int mb, int io, float ln_eps,
+                          const void *XQ, const void *XK, const void *XV,
+                          const float *theta_lr, float eta_base, const float *W1_0,
+                          const float *b1_0, const float *W2_0, const float *b2_0,
+                          int w0_batched, const float *ln_gamma, const float *ln_beta, void *O,
+                          float *W1_out, float *b1_out, float *W2_out, float *b2_out,
+                          hipStream_t stream);
 
 /*
  * ttt_mlp_forward with the two Modular-TTT options of ttt_linear_forward_opts

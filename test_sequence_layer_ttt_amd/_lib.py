@@ -55,6 +55,8 @@ def load():
     lib.ttt_mlp_forward.argtypes = [_i] * 6 + [_f] + [_P] * 8 + [_i] + [_P] * 7 + [_P]
     lib.ttt_mlp_forward_opts.argtypes = ([_i] * 6 + [_f] + [_P] * 8 + [_i] + [_P] * 2
                                          + [_i, _f] + [_P] * 5 + [_P])
+    lib.ttt_mlp_forward_gated.argtypes = ([_i] * 6 + [_f] + [_P] * 4 + [_f] + [_P] * 4 + [_i]
+                                          + [_P] * 2 + [_P] * 5 + [_P])
     lib.ttt_decode_step.argtypes = [_i] * 4 + [_f] + [_P] * 9 + [_P]
     lib.ttt_decode_steps.argtypes = [_i] * 5 + [_f] + [_P] * 9 + [_P]
     lib.ttt_decode_steps_mb.argtypes = [_i] * 5 + [_f] + [_i] * 2 + [_P] * 11 + [_P]
@@ -66,6 +68,7 @@ def load():
                  "ttt_linear_backward", "ttt_linear_backward_workspace", "ttt_ln_l2_bwd",
                  "ttt_linear_forward_gated", "ttt_eta_gate", "ttt_eta_gate_backward",
                  "ttt_linear_forward_opts", "ttt_decode_steps_mb", "ttt_mlp_forward_opts",
+                 "ttt_mlp_forward_gated",
                  "ttt_version"):
         getattr(lib, name).restype = _i
     lib.ttt_last_error.restype = ctypes.c_char_p

@@ -208,11 +208,11 @@ int gate_common(int B, int H, int L, int d, int io, float eta_base, size_t *xb, 
 // TTT-MLP prefill with the loss / weight-decay options (shared by the plain
 // and the options entry points).
 int mlp_forward(int B, int H, int L, int d, int mb, int io, float ln_eps, const void *XQ,
-                const void *XK, const void *XV, const float *eta, const float *W1_0,
-                const float *b1_0, const float *W2_0, const float *b2_0, int w0_batched,
-                const float *ln_gamma, const float *ln_beta, void *O, float *W1_out,
-                float *b1_out, float *W2_out, float *b2_out, hipStream_t stream, int loss,
-                float weight_decay) {
+                const void *XK, const void *XV, const float *eta, const float *theta,
+                float eta_base, const float *W1_0, const float *b1_0, const float *W2_0,
+                const float *b2_0, int w0_batched, const float *ln_gamma,
+                const float *ln_beta, void *O, float *W1_out, float *b1_out, float *W2_out,
+                float *b2_out, hipStream_t stream, bool gated, int loss, float weight_decay) {
     int st;
     if ((st = check_common(B, H, L, mb, io)) || (st = check_eps(ln_eps))) return st;
     if (d != 64) return fail(TTT_E_SHAPE, "d = %d: the MLP supports d = 64 only", d);
@@ -221,6 +221,8 @@ int mlp_forward(int B, int H, int L, int d, int mb, int io, float ln_eps, const 
     if (!(weight_decay >= 0.f) || !std::isfinite(weight_decay))
         return fail(TTT_E_SHAPE, "weight_decay = %g is not a finite value >= 0",
                     static_cast<double>(weight_decay));
+    if (gated && !std::isfinite(eta_base))
+        return fail(TTT_E_SHAPE, "eta_base = %g is not finite", static_cast<double>(eta_base));
     const int nout = (W1_out != nullptr) + (b1_out != nullptr) + (W2_out != nullptr) + (b2_out != nullptr);
     if (nout != 0 && nout != 4) return fail(TTT_E_NULL, "state outputs must be all NULL or all non-NULL");
     const size_t es = io == TTT_BF16 ? 2 : 4, m = 4 * static_cast<size_t>(d);
@@ -239,7 +241,8 @@ int mlp_forward(int B, int H, int L, int d, int mb, int io, float ln_eps, const 
         return fail(TTT_E_SHAPE, "sizes overflow");
     const size_t pb = static_cast<size_t>(H) * d * sizeof(float);
     const Buf in[] = {{XQ, xb, "XQ", false, 16}, {XK, xb, "XK", false, 16},
-                      {XV, xb, "XV", false, 16}, {eta, eb, "eta", false, 4},
+                      {XV, xb, "XV", false, 16},
+                      gated ? Buf{theta, pb, "theta_lr", false, 16} : Buf{eta, eb, "eta", false, 4},
                       {W1_0, w1b, "W1_0", false, 16}, {b1_0, b1b, "b1_0", false, 16},
                       {W2_0, w2b, "W2_0", false, 16}, {b2_0, b2b, "b2_0", false, 16},
                       {ln_gamma, pb, "ln_gamma", false, 4}, {ln_beta, pb, "ln_beta", false, 4}};
@@ -251,10 +254,15 @@ int mlp_forward(int B, int H, int L, int d, int mb, int io, float ln_eps, const 
                         w0_batched ? 7 : -1};
     if ((st = check_alias(out, 5, in, 10, pair))) return st;
     if (B * H == 0) return ok();
-    ttt::MLPArgs a{B, H, L, d, mb, io, ln_eps, XQ, XK, XV, eta, W1_0, b1_0, W2_0, b2_0,
-                   w0_batched ? 1 : 0, ln_gamma, ln_beta, O, W1_out, b1_out, W2_out, b2_out};
+    ttt::MLPArgs a{B, H, L, d, mb, io, ln_eps, XQ, XK, XV, gated ? nullptr : eta, W1_0, b1_0,
+                   W2_0, b2_0, w0_batched ? 1 : 0, ln_gamma, ln_beta, O, W1_out, b1_out,
+                   W2_out, b2_out};
     a.loss = loss;
     a.wd = weight_decay;
+    if (gated) {
+        a.theta = theta;
+        a.eta_base = eta_base;
+    }
     if (ttt::mlp_mfma_supported(a)) return launched(ttt::launch_mlp_mfma(a, stream));
     return launched(ttt::launch_mlp(a, stream));
 }
@@ -387,9 +395,21 @@ int ttt_mlp_forward(int B, int H, int L, int d, int mb, int io, float ln_eps,
                     const float *b2_0, int w0_batched, const float *ln_gamma,
                     const float *ln_beta, void *O, float *W1_out, float *b1_out,
                     float *W2_out, float *b2_out, hipStream_t stream) {
-    return mlp_forward(B, H, L, d, mb, io, ln_eps, XQ, XK, XV, eta, W1_0, b1_0, W2_0, b2_0,
-                       w0_batched, ln_gamma, ln_beta, O, W1_out, b1_out, W2_out, b2_out, stream,
-                       TTT_LOSS_MSE, 0.f);
+    return mlp_forward(B, H, L, d, mb, io, ln_eps, XQ, XK, XV, eta, nullptr, 0.f, W1_0, b1_0,
+                       W2_0, b2_0, w0_batched, ln_gamma, ln_beta, O, W1_out, b1_out, W2_out,
+                       b2_out, stream, false, TTT_LOSS_MSE, 0.f);
+}
+
+int ttt_mlp_forward_gated(int B, int H, int L, int d, int mb, int io, float ln_eps,
+                          const void *XQ, const void *XK, const void *XV,
+                          const float *theta_lr, float eta_base, const float *W1_0,
+                          const float *b1_0, const float *W2_0, const float *b2_0,
+                          int w0_batched, const float *ln_gamma, const float *ln_beta, void *O,
+                          float *W1_out, float *b1_out, float *W2_out, float *b2_out,
+                          hipStream_t stream) {
+    return mlp_forward(B, H, L, d, mb, io, ln_eps, XQ, XK, XV, nullptr, theta_lr, eta_base,
+                       W1_0, b1_0, W2_0, b2_0, w0_batched, ln_gamma, ln_beta, O, W1_out, b1_out,
+                       W2_out, b2_out, stream, true, TTT_LOSS_MSE, 0.f);
 }
 
 int ttt_mlp_forward_opts(int B, int H, int L, int d, int mb, int io, float ln_eps,
@@ -399,9 +419,9 @@ int ttt_mlp_forward_opts(int B, int H, int L, int d, int mb, int io, float ln_ep
                          const float *ln_beta, int inner_loss, float weight_decay, void *O,
                          float *W1_out, float *b1_out, float *W2_out, float *b2_out,
                          hipStream_t stream) {
-    return mlp_forward(B, H, L, d, mb, io, ln_eps, XQ, XK, XV, eta, W1_0, b1_0, W2_0, b2_0,
-                       w0_batched, ln_gamma, ln_beta, O, W1_out, b1_out, W2_out, b2_out, stream,
-                       inner_loss, weight_decay);
+    return mlp_forward(B, H, L, d, mb, io, ln_eps, XQ, XK, XV, eta, nullptr, 0.f, W1_0, b1_0,
+                       W2_0, b2_0, w0_batched, ln_gamma, ln_beta, O, W1_out, b1_out, W2_out,
+                       b2_out, stream, false, inner_loss, weight_decay);
 }
 
 int ttt_decode_step(int B, int H, int d, int io, float ln_eps, const void *xq,

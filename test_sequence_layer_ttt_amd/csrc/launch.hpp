@@ -44,6 +44,8 @@ struct MLPArgs {
     float *W1_out, *b1_out, *W2_out, *b2_out;
     int loss = 0;    // 0 squared error, 1 inner product
     float wd = 0.f;  // weight decay on W1 and W2
+    const float *theta = nullptr;  // learning-rate gate [H,d] (eta unused when set)
+    float eta_base = 0.f;
 };
 
 struct DecodeArgs {

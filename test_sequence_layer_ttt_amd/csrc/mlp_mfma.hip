@@ -16,6 +16,9 @@
 // d_t = 1 - lambda sum_{s<=t} eta_s: XQ W1 and Ab W2 take the factor d_t of
 // their token and the chunk ends with W1, W2 scaled by d_15 (biases are not
 // decayed).
+// GATED (template): each token's rate is formed while its chunk is staged,
+// eta_t = eta_base * logistic(theta_lr[h] . XK_t) (the learning-rate gate of
+// the lryc.cn TTT article §2.2, x read as the key), and no eta array is read.
 //
 // Layout (gfx950, one 512-thread workgroup = 8 waves per (n,h) sequence, two
 // per SIMD):
@@ -144,14 +147,15 @@ static_assert(sizeof(MlpSmem) <= 160 * 1024, "MLP prefill LDS exceeds 160 KB");
 
 }  // namespace
 
-template <int LOSS, bool DECAY>
+template <int LOSS, bool DECAY, bool GATED>
 __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
     int H, int L, float eps, const bf16_t *__restrict__ XQ, const bf16_t *__restrict__ XK,
     const bf16_t *__restrict__ XV, const float *__restrict__ eta,
     const float *__restrict__ W1_0, const float *__restrict__ b1_0,
     const float *__restrict__ W2_0, const float *__restrict__ b2_0, int w0_batched,
     const float *__restrict__ gamma, const float *__restrict__ beta, bf16_t *__restrict__ O,
-    float *W1_out, float *b1_out, float *W2_out, float *b2_out, float wd) {
+    float *W1_out, float *b1_out, float *W2_out, float *b2_out, float wd,
+    const float *__restrict__ theta, float eta_base) {
     __shared__ MlpSmem sm;
 
     const int tid = threadIdx.x;
@@ -222,8 +226,13 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
         R.q = *reinterpret_cast<const uint2 *>(xq + off);
         R.k = *reinterpret_cast<const uint2 *>(xk + off);
         R.v = *reinterpret_cast<const uint2 *>(xv + off);
-        R.eta = et[tok];
+        if constexpr (!GATED) R.eta = et[tok];
     };
+    // learning-rate gate: the dot product theta . XK_t split over the 16 lanes
+    // of the token's row; exp2 and reciprocal are the hardware approximations
+    f32x4 thv = {0.f, 0.f, 0.f, 0.f};  // -theta * log2(e) for features f0 .. f0+3
+    if constexpr (GATED)
+        thv = *reinterpret_cast<const f32x4 *>(theta + static_cast<size_t>(h) * D + f0) * -1.4426950408889634f;
     auto stage = [&](int ch) {
         Slot &S = sm.slot[ch % 3];
         const bool ok = ch * MB + r < L;
@@ -241,9 +250,16 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
         const f32x4 tau = LOSS == 1 ? unpack4(v) : unpack4(v) - kf;
         *reinterpret_cast<f32x4 *>(&S.tau[r * RS + f0]) = tau;
         const float mt = row16_sum((tau[0] + tau[1]) + (tau[2] + tau[3])) * (1.0f / D);
+        float e;
+        if constexpr (GATED) {
+            const float ns = row16_sum(fmaf(thv[0], kf[0], thv[1] * kf[1]) + fmaf(thv[2], kf[2], thv[3] * kf[3]));
+            e = eta_base * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(ns));
+        } else {
+            e = R.eta;
+        }
         if (c == 0) {
             S.mutau[r] = mt;
-            S.eta[r] = ok ? R.eta : 0.f;
+            S.eta[r] = ok ? e : 0.f;
         }
     };
     if (roww && nch > 0) {
@@ -491,25 +507,27 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
 }
 
 bool mlp_mfma_supported(const MLPArgs &a) {
-    return a.io == 1 && a.d == 64 && a.mb == 16 && (a.loss == 0 || a.loss == 1);
+    return a.io == 1 && a.d == 64 && a.mb == 16 && (a.loss == 0 || a.loss == 1) &&
+           (a.theta == nullptr || (a.loss == 0 && a.wd == 0.f));
 }
 
-template <int LOSS, bool DECAY>
+template <int LOSS, bool DECAY, bool GATED>
 static hipError_t launch_mlp_mfma_t(const MLPArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL((mlp_prefill_mfma<LOSS, DECAY>), dim3(a.B * a.H), dim3(NT), 0, stream, a.H, a.L, a.eps,
+    hipLaunchKernelGGL((mlp_prefill_mfma<LOSS, DECAY, GATED>), dim3(a.B * a.H), dim3(NT), 0, stream, a.H, a.L, a.eps,
                        static_cast<const bf16_t *>(a.XQ), static_cast<const bf16_t *>(a.XK),
                        static_cast<const bf16_t *>(a.XV), a.eta, a.W1, a.b1, a.W2, a.b2,
                        a.w0_batched, a.gamma, a.beta, static_cast<bf16_t *>(a.O), a.W1_out,
-                       a.b1_out, a.W2_out, a.b2_out, a.wd);
+                       a.b1_out, a.W2_out, a.b2_out, a.wd, a.theta, a.eta_base);
     return hipGetLastError();
 }
 
 hipError_t launch_mlp_mfma(const MLPArgs &a, hipStream_t stream) {
     if (a.B * a.H == 0) return hipSuccess;
+    if (a.theta) return launch_mlp_mfma_t<0, false, true>(a, stream);  // the gate, default options
     const bool decay = a.wd != 0.f;
     if (a.loss == 1)
-        return decay ? launch_mlp_mfma_t<1, true>(a, stream) : launch_mlp_mfma_t<1, false>(a, stream);
-    return decay ? launch_mlp_mfma_t<0, true>(a, stream) : launch_mlp_mfma_t<0, false>(a, stream);
+        return decay ? launch_mlp_mfma_t<1, true, false>(a, stream) : launch_mlp_mfma_t<1, false, false>(a, stream);
+    return decay ? launch_mlp_mfma_t<0, true, false>(a, stream) : launch_mlp_mfma_t<0, false, false>(a, stream);
 }
 
 }  // namespace ttt

@@ -18,20 +18,22 @@
 // lambda/2 (||W1||^2 + ||W2||^2) at the chunk-start state, so after token t
 // the weights are d_t W + (loss updates), d_t = 1 - lambda sum_{s<=t} eta_s:
 // the XQ W1 and Ab W2 products take a row factor d_t and the chunk ends with
-// W scaled by d_last (the biases are not decayed).
+// W scaled by d_last (the biases are not decayed). GATED forms each token's
+// rate from its staged key, eta_t = eta_base * logistic(theta_lr[h] . XK_t)
+// (the learning-rate gate of the lryc.cn article §2.2), instead of reading eta.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace ttt {
 
-template <typename TIO, int LOSS, bool DECAY>
+template <typename TIO, int LOSS, bool DECAY, bool GATED>
 __global__ __launch_bounds__(256) void mlp_prefill_valu(
     int H, int L, int mb, float eps, const TIO *__restrict__ XQ, const TIO *__restrict__ XK,
     const TIO *__restrict__ XV, const float *__restrict__ eta, const float *__restrict__ W1_0,
     const float *__restrict__ b1_0, const float *__restrict__ W2_0,
     const float *__restrict__ b2_0, int w0_batched, const float *__restrict__ gamma,
     const float *__restrict__ beta, TIO *__restrict__ O, float *W1_out, float *b1_out,
-    float *W2_out, float *b2_out, float wd) {
+    float *W2_out, float *b2_out, float wd, const float *__restrict__ theta, float eta_base) {
     constexpr int D = 64, M = 256, MB = 16, NT = 256, DP = D + 1, MP = M + 1, E = D / 16;
     using io = io_traits<TIO>;
 
@@ -41,7 +43,7 @@ __global__ __launch_bounds__(256) void mlp_prefill_valu(
     __shared__ float sDA[MB * MP], sG1[MB * MP];  // gelu'(Z1), G1
     __shared__ float sQ[MB * DP], sK[MB * DP];
     __shared__ float sT[MB * D], sG2[MB * D], sZ2[MB * D];
-    __shared__ float sEta[MB], sM[MB * MB], sDec[MB];
+    __shared__ float sEta[MB], sM[MB * MB], sDec[MB], sTh[D];
 
     const int tid = threadIdx.x;
     const long seq = blockIdx.x;
@@ -59,6 +61,7 @@ __global__ __launch_bounds__(256) void mlp_prefill_valu(
     float b1 = b1_0[sb_ * M + k];
     for (int e = tid; e < M * D; e += NT) sW2[(e / D) * DP + (e % D)] = W2_0[sb_ * M * D + e];
     if (tid < D) sb2[tid] = b2_0[sb_ * D + tid];
+    if (GATED && tid < D) sTh[tid] = theta[static_cast<size_t>(h) * D + tid];
 
     const int rrow = tid / 16, rl = tid % 16;
     float gam[E], bet[E];
@@ -85,14 +88,13 @@ __global__ __launch_bounds__(256) void mlp_prefill_valu(
             sK[s * DP + j] = kk;
             sT[s * D + j] = LOSS == 1 ? v : v - kk;
         }
-        if (tid < MB) sEta[tid] = tid < len ? eta[ebase + t0 + tid] : 0.f;
+        if (!GATED && tid < MB) sEta[tid] = tid < len ? eta[ebase + t0 + tid] : 0.f;
         __syncthreads();
 
-        // decay factors d_t (eta is 0 past the end of the sequence)
-        if (DECAY && tid < MB) {
+        if (GATED && tid < MB) {  // the gate from the staged key
             float a = 0.f;
-            for (int s = 0; s <= tid; ++s) a += sEta[s];
-            sDec[tid] = 1.f - wd * a;
+            for (int i = 0; i < D; ++i) a += sTh[i] * sK[tid * DP + i];
+            sEta[tid] = tid < len ? eta_base / (1.f + expf(-a)) : 0.f;
         }
         // Z1 column k, A = gelu(Z1), gelu'(Z1)
 #pragma unroll 1
@@ -105,6 +107,12 @@ __global__ __launch_bounds__(256) void mlp_prefill_valu(
         }
         __syncthreads();
 
+        // decay factors d_t (eta is 0 past the end of the sequence)
+        if (DECAY && tid < MB) {
+            float a = 0.f;
+            for (int s = 0; s <= tid; ++s) a += sEta[s];
+            sDec[tid] = 1.f - wd * a;
+        }
         // Z2 = A W2 + b2
         {
             float acc[4];
@@ -250,18 +258,20 @@ __global__ __launch_bounds__(256) void mlp_prefill_valu(
     }
 }
 
-template <typename TIO, int LOSS, bool DECAY>
+template <typename TIO, int LOSS, bool DECAY, bool GATED = false>
 static hipError_t launch_mlp_t(const MLPArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL((mlp_prefill_valu<TIO, LOSS, DECAY>), dim3(a.B * a.H), dim3(256), 0, stream, a.H, a.L,
+    hipLaunchKernelGGL((mlp_prefill_valu<TIO, LOSS, DECAY, GATED>), dim3(a.B * a.H), dim3(256), 0, stream, a.H, a.L,
                        a.mb, a.eps, static_cast<const TIO *>(a.XQ),
                        static_cast<const TIO *>(a.XK), static_cast<const TIO *>(a.XV), a.eta,
                        a.W1, a.b1, a.W2, a.b2, a.w0_batched, a.gamma, a.beta,
-                       static_cast<TIO *>(a.O), a.W1_out, a.b1_out, a.W2_out, a.b2_out, a.wd);
+                       static_cast<TIO *>(a.O), a.W1_out, a.b1_out, a.W2_out, a.b2_out, a.wd,
+                       a.theta, a.eta_base);
     return hipGetLastError();
 }
 
 template <typename TIO>
 static hipError_t launch_mlp_io(const MLPArgs &a, hipStream_t stream) {
+    if (a.theta) return launch_mlp_t<TIO, 0, false, true>(a, stream);  // the gate, default options
     const bool decay = a.wd != 0.f;
     if (a.loss == 1)
         return decay ? launch_mlp_t<TIO, 1, true>(a, stream) : launch_mlp_t<TIO, 1, false>(a, stream);

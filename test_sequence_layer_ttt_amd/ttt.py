@@ -242,6 +242,15 @@ def ttt_mlp_forward(XQ, XK, XV, eta, W1, b1, W2, b2, ln_gamma, ln_beta, O=None, 
                 None, 0.0)
 
 
+def ttt_mlp_forward_gated(XQ, XK, XV, theta_lr, eta_base: float, W1, b1, W2, b2, ln_gamma,
+                          ln_beta, O=None, outs=None, mb: int = 16, ln_eps: float = 1e-6,
+                          stream=None):
+    """TTT-MLP prefill with eta_t = eta_base * logistic(theta_lr[h] . XK_t)
+    formed inside the kernel (theta_lr [H,d] fp32); the rest as ttt_mlp_forward."""
+    return _mlp(XQ, XK, XV, None, W1, b1, W2, b2, ln_gamma, ln_beta, O, outs, mb, ln_eps, stream,
+                None, 0.0, gate=(theta_lr, eta_base))
+
+
 def ttt_mlp_forward_opts(XQ, XK, XV, eta, W1, b1, W2, b2, ln_gamma, ln_beta,
                          inner_loss: str = "mse", weight_decay: float = 0.0, O=None, outs=None,
                          mb: int = 16, ln_eps: float = 1e-6, stream=None):
@@ -252,7 +261,7 @@ def ttt_mlp_forward_opts(XQ, XK, XV, eta, W1, b1, W2, b2, ln_gamma, ln_beta,
 
 
 def _mlp(XQ, XK, XV, eta, W1, b1, W2, b2, ln_gamma, ln_beta, O, outs, mb, ln_eps, stream,
-         inner_loss, weight_decay):
+         inner_loss, weight_decay, gate=None):
     B, H, L, d = XQ.shape
     m = 4 * d
     io = _IO.get(XQ.dtype)
@@ -268,7 +277,10 @@ def _mlp(XQ, XK, XV, eta, W1, b1, W2, b2, ln_gamma, ln_beta, O, outs, mb, ln_eps
     pre = (B,) if batched else ()
     for t, n in ((XQ, "XQ"), (XK, "XK"), (XV, "XV")):
         _need(t, n, (B, H, L, d), XQ.dtype)
-    _need(eta, "eta", (B, H, L), torch.float32)
+    if gate is None:
+        _need(eta, "eta", (B, H, L), torch.float32)
+    else:
+        _need(gate[0], "theta_lr", (H, d), torch.float32)
     _need(W1, "W1", pre + (H, d, m), torch.float32)
     _need(b1, "b1", pre + (H, m), torch.float32)
     _need(W2, "W2", pre + (H, m, d), torch.float32)
@@ -286,9 +298,15 @@ def _mlp(XQ, XK, XV, eta, W1, b1, W2, b2, ln_gamma, ln_beta, O, outs, mb, ln_eps
                        ((B, H, d, m), (B, H, m), (B, H, m, d), (B, H, d))):
         _need(t, n, s, torch.float32)
     lib = _lib.load()
+    tail = (_ptr(O),) + tuple(_ptr(t) for t in outs) + (_stream(stream),)
+    if gate is not None:
+        _lib.check(lib.ttt_mlp_forward_gated(B, H, L, d, mb, io, ln_eps, _ptr(XQ), _ptr(XK),
+                                             _ptr(XV), _ptr(gate[0]), float(gate[1]), _ptr(W1),
+                                             _ptr(b1), _ptr(W2), _ptr(b2), int(batched),
+                                             _ptr(ln_gamma), _ptr(ln_beta), *tail))
+        return (O,) + tuple(outs)
     head = (B, H, L, d, mb, io, ln_eps, _ptr(XQ), _ptr(XK), _ptr(XV), _ptr(eta), _ptr(W1),
             _ptr(b1), _ptr(W2), _ptr(b2), int(batched), _ptr(ln_gamma), _ptr(ln_beta))
-    tail = (_ptr(O),) + tuple(_ptr(t) for t in outs) + (_stream(stream),)
     if loss is None:
         _lib.check(lib.ttt_mlp_forward(*head, *tail))
     else:

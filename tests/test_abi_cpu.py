@@ -266,6 +266,23 @@ def test_mlp_forward_opts_validation(lib):
     assert _mlp_opts(lib, loss=1, wd=0.5, B=0) == _lib.TTT_OK
 
 
+def _mlp_gated(lib, eta_base=0.5, theta=FAKE + 3 * (1 << 20), B=1, O=FAKE + 10 * (1 << 20)):
+    p = [FAKE + i * (1 << 20) for i in range(15)]
+    return lib.ttt_mlp_forward_gated(B, 1, 16, 64, 16, 1, 1e-6, p[0], p[1], p[2], theta, eta_base,
+                                     *p[4:8], 0, p[8], p[9], O, *p[11:15], None)
+
+
+def test_mlp_forward_gated_validation(lib):
+    for bad in (float("nan"), float("inf")):
+        assert _mlp_gated(lib, eta_base=bad) == _lib.TTT_E_SHAPE
+        assert "eta_base" in lib.ttt_last_error().decode()
+    assert _mlp_gated(lib, theta=0) == _lib.TTT_E_NULL
+    assert "theta_lr" in lib.ttt_last_error().decode()
+    assert _mlp_gated(lib, theta=FAKE + 3 * (1 << 20) + 4) == _lib.TTT_E_ALIGN
+    assert _mlp_gated(lib, O=FAKE + 3 * (1 << 20)) == _lib.TTT_E_ALIAS  # O over theta_lr
+    assert _mlp_gated(lib, B=0) == _lib.TTT_OK
+
+
 def _gate(lib, B=2, H=3, L=40, d=64, io=1, xk=FAKE, th=FAKE + (1 << 20), eta_base=0.5,
           eta=FAKE + 2 * (1 << 20)):
     return lib.ttt_eta_gate(B, H, L, d, io, xk, th, eta_base, eta, None)

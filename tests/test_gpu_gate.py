@@ -1,5 +1,6 @@
 """GPU parity of the learning-rate gate (the lryc.cn article §2.2, x := the
-head's key) through the C ABI: the fused gated prefill, the standalone gate,
+head's key) through the C ABI: the fused gated TTT-Linear and TTT-MLP
+prefills, the standalone gate,
 its backward, and the gated training step composed from ttt_eta_gate,
 ttt_linear_backward and ttt_eta_gate_backward, each against the fp64 oracle.
 
@@ -179,3 +180,85 @@ def test_gated_prefill_empty_sequence(io):
     assert O.shape == (2, 3, 0, 64)
     assert np.array_equal(W, np.broadcast_to(x.W0, W.shape))
     assert np.array_equal(b, np.broadcast_to(x.b0, b.shape))
+
+
+# ---------------------------------------------------------------------------
+# The gate inside the TTT-MLP prefill (ttt_mlp_forward_gated) against the
+# oracle's gate followed by its MLP prefill.
+# ---------------------------------------------------------------------------
+MLP_NAMES = ("O", "W1_out", "b1_out", "W2_out", "b2_out")
+
+
+def _mlp_gated(seed, B, H, L, io, theta_std=0.3, **kw):
+    x = gen.make_mlp(seed, B, H, L, 64, io=io, **kw)
+    th = (theta_std * np.random.default_rng(seed + 1000).standard_normal((H, 64))).astype(np.float32)
+    return x, th, 1.0 / 64
+
+
+def _mlp_gated_gpu(x, th, eta_base, mb):
+    dt = P.io_dtype(x.io)
+    out = ttt.ttt_mlp_forward_gated(P.dev(x.XQ, dt), P.dev(x.XK, dt), P.dev(x.XV, dt), P.dev(th),
+                                    eta_base, P.dev(x.W1), P.dev(x.b1), P.dev(x.W2), P.dev(x.b2),
+                                    P.dev(x.gamma), P.dev(x.beta), mb=mb, ln_eps=x.eps)
+    torch.cuda.synchronize()
+    return tuple(P.to_np(t) for t in out)
+
+
+def _mlp_gated_oracle(x, th, eta_base, mb):
+    eta = oracle.eta_gate(x.XK, th, eta_base)
+    return oracle.mlp_forward(x.XQ, x.XK, x.XV, eta, x.W1, x.b1, x.W2, x.b2, x.gamma, x.beta,
+                              x.eps, mb=mb)
+
+
+@pytest.mark.parametrize("io,mb,L", [("bf16", 16, 16 * 6 + 5), ("bf16", 16, 16),
+                                     ("f32", 16, 16 * 3 + 7), ("bf16", 5, 23)])
+def test_gated_mlp_prefill(io, mb, L):
+    x, th, eb = _mlp_gated(900 + mb + L, 2, 3, L, io, ln_random=True, b_random=True)
+    got, ref = _mlp_gated_gpu(x, th, eb, mb), _mlp_gated_oracle(x, th, eb, mb)
+    err = P.errors(got, ref, x.B * x.H, MLP_NAMES)
+    _report(f"mlp prefill {io} mb{mb} L{L}", err)
+    assert max(err.values()) <= P.TOL[io], err
+
+
+def test_gated_mlp_prefill_workload4_shape_sampled_heads():
+    """Workload 4's shape (B=2, H=12, L=8192, bf16) with the gate inside the
+    MFMA kernel; the oracle checks batch 1, heads 4 and 9."""
+    x = gen.make_workload(4)
+    th = (0.3 * np.random.default_rng(44).standard_normal((x.H, x.d))).astype(np.float32)
+    got = _mlp_gated_gpu(x, th, 1.0 / x.d, 16)
+    hs = [4, 9]
+    sl = lambda a: np.ascontiguousarray(a[1:2, hs])
+    hp = lambda a: np.ascontiguousarray(a[hs])
+    eta = oracle.eta_gate(sl(x.XK), hp(th), 1.0 / x.d)
+    ref = oracle.mlp_forward(sl(x.XQ), sl(x.XK), sl(x.XV), eta, hp(x.W1), hp(x.b1), hp(x.W2),
+                             hp(x.b2), hp(x.gamma), hp(x.beta), x.eps, mb=16)
+    err = P.errors(tuple(sl(g) for g in got), ref, 2, MLP_NAMES)
+    _report("mlp prefill workload4 shape heads 4,9", err)
+    assert max(err.values()) <= P.TOL["bf16"], err
+
+
+def test_gated_mlp_prefill_equals_gate_then_prefill():
+    """The fused gate against ttt_eta_gate followed by ttt_mlp_forward on the
+    same inputs: the two differ only in the rounding of eta. The fp32 states
+    agree to 1e-3; O is stored in bf16 (one rounding step is 2^-8 of a value),
+    so an output may round the other way: two steps of the largest, 2^-7."""
+    x, th, eb = _mlp_gated(950, 2, 3, 16 * 9 + 3, "bf16", b_random=True)
+    dt = P.io_dtype(x.io)
+    fused = _mlp_gated_gpu(x, th, eb, 16)
+    eta = ttt.ttt_eta_gate(P.dev(x.XK, dt), P.dev(th), eb)
+    two = ttt.ttt_mlp_forward(P.dev(x.XQ, dt), P.dev(x.XK, dt), P.dev(x.XV, dt), eta, P.dev(x.W1),
+                              P.dev(x.b1), P.dev(x.W2), P.dev(x.b2), P.dev(x.gamma),
+                              P.dev(x.beta), ln_eps=x.eps)
+    torch.cuda.synchronize()
+    err = P.errors(fused, tuple(P.to_np(t) for t in two), x.B * x.H, MLP_NAMES)
+    _report("mlp fused vs two-pass", err)
+    assert err["O"] <= 2.0 ** -7, err
+    assert max(v for k, v in err.items() if k != "O") <= 1e-3, err
+
+
+def test_gated_mlp_empty_sequence():
+    x, th, eb = _mlp_gated(960, 2, 3, 0, "bf16", b_random=True)
+    got = _mlp_gated_gpu(x, th, eb, 16)
+    assert got[0].shape == (2, 3, 0, 64)
+    for g_, r_ in zip(got[1:], (x.W1, x.b1, x.W2, x.b2)):
+        assert np.array_equal(g_, np.broadcast_to(r_, g_.shape))
