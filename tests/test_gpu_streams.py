@@ -80,3 +80,35 @@ def test_backward_on_side_stream():
         gr = ttt.ttt_linear_backward(*args, stream=s)
         return tuple(gr[k] for k in sorted(gr))
     _check(run, 20.0)
+
+
+def _variant_args(kind):
+    dt = torch.bfloat16
+    if kind.startswith("linear"):
+        x = gen.make_workload(3, L=1024, B=2, H=32)
+        ins = [P.dev(x.XQ, dt), P.dev(x.XK, dt), P.dev(x.XV, dt)]
+        st = [P.dev(x.W0), P.dev(x.b0), P.dev(x.gamma), P.dev(x.beta)]
+    else:
+        x = gen.make_workload(4, L=512, B=2, H=12)
+        ins = [P.dev(x.XQ, dt), P.dev(x.XK, dt), P.dev(x.XV, dt)]
+        st = [P.dev(x.W1), P.dev(x.b1), P.dev(x.W2), P.dev(x.b2), P.dev(x.gamma), P.dev(x.beta)]
+    th = P.dev((0.3 * np.random.default_rng(78).standard_normal((x.H, x.d))).astype(np.float32))
+    return x, ins, st, th, P.dev(x.eta)
+
+
+@pytest.mark.parametrize("kind", ["linear_gated", "linear_opts", "mlp_gated", "mlp_opts", "gate"])
+def test_variant_entry_points_on_side_stream(kind):
+    """The gated and option prefills and the standalone gate: side stream
+    against default stream, bit for bit (the kernels are deterministic)."""
+    x, ins, st, th, eta = _variant_args(kind)
+    eb = 1.0 / x.d
+    fn = {
+        "linear_gated": lambda s: ttt.ttt_linear_forward_gated(*ins, th, eb, *st, stream=s),
+        "linear_opts": lambda s: ttt.ttt_linear_forward_opts(*ins, eta, *st, "inner_product", 0.5,
+                                                             stream=s),
+        "mlp_gated": lambda s: ttt.ttt_mlp_forward_gated(*ins, th, eb, *st, stream=s),
+        "mlp_opts": lambda s: ttt.ttt_mlp_forward_opts(*ins, eta, *st, "inner_product", 0.5,
+                                                       stream=s),
+        "gate": lambda s: ttt.ttt_eta_gate(ins[1], th, eb, stream=s),
+    }[kind]
+    _check(fn, 1.0 if kind == "gate" else 20.0)
