@@ -211,6 +211,7 @@ def _mlp_gated_oracle(x, th, eta_base, mb):
 
 
 @pytest.mark.parametrize("io,mb,L", [("bf16", 16, 16 * 6 + 5), ("bf16", 16, 16),
+                                     ("bf16", 16, 1), ("bf16", 16, 17),
                                      ("f32", 16, 16 * 3 + 7), ("bf16", 5, 23)])
 def test_gated_mlp_prefill(io, mb, L):
     x, th, eb = _mlp_gated(900 + mb + L, 2, 3, L, io, ln_random=True, b_random=True)

@@ -178,3 +178,18 @@ def test_mlp_options_empty_sequence():
     assert got[0].shape == (2, 3, 0, 64)
     for g_, r_ in zip(got[1:], (x.W1, x.b1, x.W2, x.b2)):
         assert np.array_equal(g_, np.broadcast_to(r_, g_.shape))
+
+
+@pytest.mark.parametrize("L", [1, 15, 17])
+def test_options_mfma_lengths_around_one_chunk(L):
+    """Both options on the MFMA prefills (bf16, b = 16) with a single partial
+    chunk, one chunk short of a full one, and one token past it."""
+    x = gen.make_linear(670 + L, 2, 3, L, 64, io="bf16", ln_random=True, b_random=True, w_std=0.3)
+    err = P.errors(_run(x, "inner_product", 0.5, 16), _ref(x, "inner_product", 0.5, 16), 6, NAMES)
+    xm = gen.make_mlp(770 + L, 2, 3, L, 64, io="bf16", ln_random=True, b_random=True)
+    err_m = P.errors(_mlp_run(xm, "inner_product", 0.5, 16), _mlp_ref(xm, "inner_product", 0.5, 16),
+                     6, MLP_NAMES)
+    print(f"[parity] opts L{L}: linear " + " ".join(f"{k}={v:.2e}" for k, v in err.items())
+          + " | mlp " + " ".join(f"{k}={v:.2e}" for k, v in err_m.items()), flush=True)
+    assert max(err.values()) <= P.TOL["bf16"], err
+    assert max(err_m.values()) <= P.TOL["bf16"], err_m
