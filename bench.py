@@ -121,8 +121,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="3", choices=["3", "2", "5p", "4", "4o", "4g", "5d", "5r", "5m", "3b", "3g",
-                             "3gb", "3o"])
+    ap.add_argument("--workload", default="3", choices=["3", "2", "5p", "4", "4o", "4g", "5d", "5r", "5m", "5g", "3b",
+                             "3g", "3gb", "3o"])
     ap.add_argument("--peaks", action="store_true",
                     help="measure achievable HBM copy bandwidth and bf16 GEMM throughput (context)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -165,6 +165,8 @@ def main():
         return bench_decode_steps(args)
     if args.workload == "5m":
         return bench_decode_steps(args, mb=16)
+    if args.workload == "5g":
+        return bench_decode_steps(args, gated=True)
     if args.workload == "3b":
         return bench_backward(args)
     if args.workload == "3gb":
@@ -435,13 +437,16 @@ def bench_decode(args):
                    "io": "bf16", "state": "fp32", "parallelism": "none (1 GPU)"}, roof, extra)
 
 
-def bench_decode_steps(args, mb: int = 1):
+def bench_decode_steps(args, mb: int = 1, gated: bool = False):
     """Workload 5's 1024 b=1 decode steps on 64 x 32 states in one
     ttt_decode_steps call (states resident in registers), each state started
     from the B=1, L=32768 prefill's final state. A bench step is one call;
     successive calls continue from the state the previous one left. With
     mb > 1 the same tokens go through ttt_decode_steps_mb (mini-batch rule,
-    chunk-start state as a second resident copy)."""
+    chunk-start state as a second resident copy). With gated, each step's
+    eta comes from the learning-rate gate inside the kernel
+    (ttt_decode_steps_gated, theta_lr ~ N(0, 0.02^2) from seed 1005,
+    eta_base = 1/d) instead of the eta array."""
     import numpy as np
     import torch
     from test_sequence_layer_ttt_amd import gen, ttt
@@ -459,7 +464,12 @@ def bench_decode_steps(args, mb: int = 1):
     g, be = T(pre.gamma), T(pre.beta)
     o = torch.empty((S, B, H, d), device=dev, dtype=bf)
     stream = torch.cuda.current_stream()
-    if mb == 1:
+    if gated:
+        theta_np = (0.02 * np.random.default_rng(1005).standard_normal((H, d))).astype(np.float32)
+        th = T(theta_np)
+        step = lambda: ttt.ttt_decode_steps_gated(xq, xk, xv, th, 1.0 / d, W, b, g, be, o=o,
+                                                  ln_eps=pre.eps, stream=stream)
+    elif mb == 1:
         step = lambda: ttt.ttt_decode_steps(xq, xk, xv, et, W, b, g, be, o=o, ln_eps=pre.eps,
                                             stream=stream)
     else:  # 1024 steps are 64 whole chunks, so every call starts a chunk (pos = 0)
@@ -482,7 +492,10 @@ def bench_decode_steps(args, mb: int = 1):
         ns = 4  # bounded sample: four steps
         t1 = time.perf_counter()
         for s_ in range(ns):
-            oracle.decode_step(dec.XQ[s_], dec.XK[s_], dec.XV[s_], dec.eta[s_], Wn, bn,
+            et_s = dec.eta[s_]
+            if gated:  # the oracle's gate on this step's keys ([B,H,d] -> [B,H,1,d])
+                et_s = oracle.eta_gate(dec.XK[s_][:, :, None], theta_np, 1.0 / d)[:, :, 0]
+            oracle.decode_step(dec.XQ[s_], dec.XK[s_], dec.XV[s_], et_s, Wn, bn,
                                pre.gamma, pre.beta, pre.eps, nthreads=nt)
         tc = time.perf_counter() - t1
         extra["cpu_baseline"] = {"value": B * ns / tc, "unit": "tokens/s", "cores": nt,
@@ -504,9 +517,11 @@ def bench_decode_steps(args, mb: int = 1):
                                  "kind": "oracle",
                                  "sample": f"one chunk of {mb} tokens on all {B}x{H} states "
                                            f"(mini-batch rule), fp64, {nt} threads, {tc:.2f} s"}
-    _line(f"TTT-Linear decode tokens/s (64 sequences x 32 heads, b={mb}, 1024 steps per call)",
+    gtag = ", gated eta" if gated else ""
+    _line(f"TTT-Linear decode tokens/s (64 sequences x 32 heads, b={mb}, 1024 steps per call{gtag})",
           B * S / wall, args, wall, "bf16",
-          {"workload": "ttt_linear_decode_steps_bf16_T1024_B64_H32_d64" + (f"_mb{mb}" if mb > 1 else ""),
+          {"workload": "ttt_linear_decode_steps_bf16_T1024_B64_H32_d64" + (f"_mb{mb}" if mb > 1 else "")
+           + ("+eta_gate" if gated else ""),
            "T": S, "B": B, "H": H, "d": d, "mini_batch": mb, "io": "bf16",
            "state": "fp32, resident in registers", "parallelism": "none (1 GPU)"}, roof, extra)
 

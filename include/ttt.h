@@ -142,7 +142,8 @@ int ttt_linear_forward_opts(int B, int H, int L, int d, int mb, int io, float ln
 
 /*
  * The learning-rate gate of [Y] §2.2 on its own, for the paths that take eta
- * as an array (decode, the backward, the prefills with the loss options):
+ * as an array (the backward, the single-step decode, the prefills with the
+ * loss options):
  *   eta[n,h,t] = eta_base * logistic(theta_lr[h] . XK[n,h,t]).
  *   B, H, L >= 0; d in {16, 32, 64}; io as above.
  *   XK [B,H,L,d] io, 16-byte aligned; theta_lr [H,d] fp32; eta [B,H,L] fp32,
@@ -322,6 +323,24 @@ int ttt_decode_steps_mb(int T, int B, int H, int d, int io, float ln_eps, int mb
                         float *W_chunk, float *b_chunk, float *W, float *b,
                         const float *ln_gamma, const float *ln_beta, void *o,
                         hipStream_t stream);
+
+/*
+ * ttt_decode_steps_mb with each step's rate taken from the learning-rate gate
+ * of [Y] §2.2 (no eta array is read):
+ *   eta_t = eta_base * logistic(theta_lr[h] . xk_t),  logistic(s) = 1/(1+e^-s),
+ * the gate input x read as the head's key, as in the gated prefills, so a
+ * gated prefill followed by these calls equals one gated prefill over the
+ * whole sequence. mb = 1 is plain b = 1 decode (W_chunk, b_chunk ignored).
+ *   theta_lr : [H,d] fp32.  eta_base : finite, else TTT_E_SHAPE.
+ * Every other argument, the layouts and the errors as ttt_decode_steps_mb.
+ * The gate is evaluated in fp32 (d = 64: a wave sum, then the hardware exp2
+ * and reciprocal, about 1 ulp each; d = 16: expf and a divide).
+ */
+int ttt_decode_steps_gated(int T, int B, int H, int d, int io, float ln_eps, int mb, int pos,
+                           const void *xq, const void *xk, const void *xv,
+                           const float *theta_lr, float eta_base, float *W_chunk,
+                           float *b_chunk, float *W, float *b, const float *ln_gamma,
+                           const float *ln_beta, void *o, hipStream_t stream);
 
 /*
  * The fused layer-norm + L2 backward step on its own ([D] §4.2), row-wise:

@@ -60,6 +60,8 @@ def load():
     lib.ttt_decode_step.argtypes = [_i] * 4 + [_f] + [_P] * 9 + [_P]
     lib.ttt_decode_steps.argtypes = [_i] * 5 + [_f] + [_P] * 9 + [_P]
     lib.ttt_decode_steps_mb.argtypes = [_i] * 5 + [_f] + [_i] * 2 + [_P] * 11 + [_P]
+    lib.ttt_decode_steps_gated.argtypes = ([_i] * 5 + [_f] + [_i] * 2 + [_P] * 4 + [_f] + [_P] * 7
+                                           + [_P])
     lib.ttt_linear_backward.argtypes = ([_i] * 6 + [_f] + [_P] * 6 + [_i] + [_P] * 14
                                         + [ctypes.c_size_t, _P])
     lib.ttt_linear_backward_workspace.argtypes = [_i] * 5 + [ctypes.POINTER(ctypes.c_size_t)]
@@ -68,7 +70,7 @@ def load():
                  "ttt_linear_backward", "ttt_linear_backward_workspace", "ttt_ln_l2_bwd",
                  "ttt_linear_forward_gated", "ttt_eta_gate", "ttt_eta_gate_backward",
                  "ttt_linear_forward_opts", "ttt_decode_steps_mb", "ttt_mlp_forward_opts",
-                 "ttt_mlp_forward_gated",
+                 "ttt_mlp_forward_gated", "ttt_decode_steps_gated",
                  "ttt_version"):
         getattr(lib, name).restype = _i
     lib.ttt_last_error.restype = ctypes.c_char_p

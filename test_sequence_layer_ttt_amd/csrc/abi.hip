@@ -461,9 +461,12 @@ namespace {
 int decode_steps(int T, int B, int H, int d, int io, float ln_eps, int mb, int pos,
                  const void *xq, const void *xk, const void *xv, const float *eta, float *Wc,
                  float *bc, float *W, float *b, const float *ln_gamma, const float *ln_beta,
-                 void *o, hipStream_t stream) {
+                 void *o, hipStream_t stream, const float *theta = nullptr, float eta_base = 0.f,
+                 bool gated = false) {
     int st;
     if (T < 0) return fail(TTT_E_SHAPE, "T = %d is negative", T);
+    if (gated && !std::isfinite(eta_base))
+        return fail(TTT_E_SHAPE, "eta_base = %g is not finite", static_cast<double>(eta_base));
     if ((st = check_common(B, H, 1, mb, io)) || (st = check_eps(ln_eps))) return st;
     if (pos < 0 || pos >= mb) return fail(TTT_E_SHAPE, "pos = %d not in [0, mb = %d)", pos, mb);
     if (d != 16 && d != 64) return fail(TTT_E_SHAPE, "d = %d not in {16, 64}", d);
@@ -478,7 +481,8 @@ int decode_steps(int T, int B, int H, int d, int io, float ln_eps, int mb, int p
     const size_t pb = static_cast<size_t>(H) * d * sizeof(float);
     const unsigned ea = static_cast<unsigned>(es);
     const Buf in[] = {{xq, xb, "xq", false, ea}, {xk, xb, "xk", false, ea},
-                      {xv, xb, "xv", false, ea}, {eta, eb, "eta", false, 4},
+                      {xv, xb, "xv", false, ea},
+                      gated ? Buf{theta, pb, "theta_lr", false, 4} : Buf{eta, eb, "eta", false, 4},
                       {ln_gamma, pb, "ln_gamma", false, 4}, {ln_beta, pb, "ln_beta", false, 4}};
     const Buf out[] = {{W, wb, "W", false, 4}, {b, bb, "b", false, 4}, {o, xb, "o", false, ea},
                        {ch ? Wc : nullptr, ch ? wb : 0, "W_chunk", false, 4},
@@ -488,7 +492,12 @@ int decode_steps(int T, int B, int H, int d, int io, float ln_eps, int mb, int p
     if ((st = check_alias(out, nout, in, 6, nullptr))) return st;
     if (B * H == 0 || T == 0) return ok();
     if (ttt::decode_steps_resident(d)) {
-        ttt::DecodeArgs a{B, H, d, io, ln_eps, xq, xk, xv, eta, W, b, ln_gamma, ln_beta, o};
+        ttt::DecodeArgs a{B, H, d, io, ln_eps, xq, xk, xv, gated ? nullptr : eta, W, b, ln_gamma,
+                          ln_beta, o};
+        if (gated) {
+            a.theta = theta;
+            a.eta_base = eta_base;
+        }
         if (ch) {
             a.Wc = Wc;
             a.bc = bc;
@@ -503,8 +512,12 @@ int decode_steps(int T, int B, int H, int d, int io, float ln_eps, int mb, int p
     for (int t = 0; t < T; ++t) {
         ttt::DecodeArgs a{B, H, d, io, ln_eps,
                           static_cast<const char *>(xq) + t * step, static_cast<const char *>(xk) + t * step,
-                          static_cast<const char *>(xv) + t * step, eta + t * estep, W, b, ln_gamma,
-                          ln_beta, static_cast<char *>(o) + t * step};
+                          static_cast<const char *>(xv) + t * step, gated ? nullptr : eta + t * estep,
+                          W, b, ln_gamma, ln_beta, static_cast<char *>(o) + t * step};
+        if (gated) {
+            a.theta = theta;
+            a.eta_base = eta_base;
+        }
         if (ch) {
             a.Wc = Wc;
             a.bc = bc;
@@ -534,6 +547,15 @@ int ttt_decode_steps_mb(int T, int B, int H, int d, int io, float ln_eps, int mb
                         hipStream_t stream) {
     return decode_steps(T, B, H, d, io, ln_eps, mb, pos, xq, xk, xv, eta, W_chunk, b_chunk, W, b,
                         ln_gamma, ln_beta, o, stream);
+}
+
+int ttt_decode_steps_gated(int T, int B, int H, int d, int io, float ln_eps, int mb, int pos,
+                           const void *xq, const void *xk, const void *xv,
+                           const float *theta_lr, float eta_base, float *W_chunk,
+                           float *b_chunk, float *W, float *b, const float *ln_gamma,
+                           const float *ln_beta, void *o, hipStream_t stream) {
+    return decode_steps(T, B, H, d, io, ln_eps, mb, pos, xq, xk, xv, nullptr, W_chunk, b_chunk, W,
+                        b, ln_gamma, ln_beta, o, stream, theta_lr, eta_base, true);
 }
 
 }  // extern "C"

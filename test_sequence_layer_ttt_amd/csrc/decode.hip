@@ -18,6 +18,10 @@
 // current state is copied to Wc, bc first, and z uses it), mode 2 reads Wc,
 // bc. The output identity still uses the current W: xq W' + b' =
 // (xq W + b) - eta (xq . xk + 1) G.
+//
+// With theta set, the step's rate comes from the learning-rate gate of the
+// lryc.cn TTT article (§2.2), eta = eta_base * logistic(theta[h] . xk), x read
+// as the key, instead of the eta array.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -28,7 +32,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     int H, float eps, const TIO *__restrict__ xq, const TIO *__restrict__ xk,
     const TIO *__restrict__ xv, const float *__restrict__ eta, float *__restrict__ W,
     float *__restrict__ b, const float *__restrict__ gamma, const float *__restrict__ beta,
-    TIO *__restrict__ o, float *__restrict__ Wc, float *__restrict__ bc, int mode) {
+    TIO *__restrict__ o, float *__restrict__ Wc, float *__restrict__ bc, int mode,
+    const float *__restrict__ theta, float eta_base) {
     constexpr int NT = 256, P = NT / D, RPT = D / P, E = D / 16;
     using io = io_traits<TIO>;
     __shared__ float sq[D], sk[D], sG[D];
@@ -69,7 +74,15 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     __syncthreads();
 
     if (tid < 16) {
-        const float et = eta[seq];
+        float et;
+        if (theta) {  // uniform: the gate from the staged key
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) s += theta[static_cast<size_t>(h) * D + tid + 16 * e] * sk[tid + 16 * e];
+            et = eta_base / (1.f + expf(-group_sum<16>(s)));
+        } else {
+            et = eta[seq];
+        }
         float z[E], tau[E], g[E], zb[E], y[E], gm[E], bt[E], bb[E], q[E];
         float qk = 0.f;
 #pragma unroll
@@ -119,7 +132,7 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((decode_step_kernel<D, TIO>), dim3(a.B * a.H), dim3(256), 0, stream, a.H,
                        a.eps, static_cast<const TIO *>(a.xq), static_cast<const TIO *>(a.xk),
                        static_cast<const TIO *>(a.xv), a.eta, a.W, a.b, a.gamma, a.beta,
-                       static_cast<TIO *>(a.o), a.Wc, a.bc, a.mode);
+                       static_cast<TIO *>(a.o), a.Wc, a.bc, a.mode, a.theta, a.eta_base);
     return hipGetLastError();
 }
 

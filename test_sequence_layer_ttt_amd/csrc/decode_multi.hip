@@ -21,6 +21,11 @@
 // that is refreshed from (W, b) when a chunk starts; z uses the copy, the
 // output and the update use the current state, so the identity above still
 // holds with W the current state.
+//
+// GATED: each step's rate comes from the learning-rate gate of the lryc.cn TTT
+// article (§2.2), eta = eta_base * logistic(theta[h] . xk), x read as the key;
+// theta . xk is a wave sum taken together with xq . xk, then one exp2 and one
+// reciprocal (hardware approximations); no eta array is read.
 #include "common.hpp"
 #include "launch.hpp"
 #include "tile.hpp"
@@ -119,13 +124,14 @@ __device__ __forceinline__ void axpy_bcast(const float (&x)[4], float e, float (
 }
 using Rows16 = std::make_integer_sequence<int, 16>;
 
-template <typename TIO, bool IDENT, bool CH>
+template <typename TIO, bool IDENT, bool CH, bool GATED>
 __device__ __forceinline__ void run_steps(int T, int BH, float eps, int seq, int j,
                                           const TIO *__restrict__ xq, const TIO *__restrict__ xk,
                                           const TIO *__restrict__ xv, const float *__restrict__ eta,
                                           float *__restrict__ Ws, float *__restrict__ bs, float gm,
                                           float bt, TIO *__restrict__ o, int mb, int pos,
-                                          float *__restrict__ Wcs, float *__restrict__ bcs) {
+                                          float *__restrict__ Wcs, float *__restrict__ bcs,
+                                          float thj, float eta_base) {
     using io = io_traits<TIO>;
     constexpr float inv_d = 1.0f / DM;
     float w[DM];  // W[i][j], i = 0 .. 63
@@ -155,7 +161,7 @@ __device__ __forceinline__ void run_steps(int T, int BH, float eps, int seq, int
     rq.load(xq + base, j);
     rk.load(xk + base, j);
     TIO rv = xv[base + j];
-    float et = eta[seq];
+    float et = GATED ? 0.f : eta[seq];
 
     for (int t = 0; t < T; ++t) {
         const bool more = t + 1 < T;  // uniform
@@ -164,16 +170,23 @@ __device__ __forceinline__ void run_steps(int T, int BH, float eps, int seq, int
         rq.bcast(qb);
         rk.bcast(kb);
         const float xqj = rq.own(), xkj = rk.own(), xvj = io::load(&rv, 0);
-        const float etc = et;
+        float etc = et;
         // the next step's inputs, in flight during this one
         if (more) {
             rq.load(xq + nbase, j);
             rk.load(xk + nbase, j);
             rv = xv[nbase + j];
-            et = eta[static_cast<size_t>(t + 1) * BH + seq];
+            if constexpr (!GATED) et = eta[static_cast<size_t>(t + 1) * BH + seq];
         }
         const float tau = xvj - xkj;
-        const float qk = wave_sum(xqj * xkj);
+        float qk;
+        if constexpr (GATED) {  // xq . xk and theta . xk in one pair of wave sums
+            const f32x4 s = wave_sum2(xqj * xkj, thj * xkj);
+            qk = s[0];
+            etc = eta_base * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * s[2]));
+        } else {
+            qk = wave_sum(xqj * xkj);
+        }
 
         // (xq W)_j and z_j = (xk W + b)_j, W, b at the chunk start for z
         float p0 = 0.f, p1 = 0.f, z0, z1 = 0.f;
@@ -240,12 +253,13 @@ __device__ __forceinline__ void run_steps(int T, int BH, float eps, int seq, int
     }
 }
 
-template <typename TIO, bool CH>
+template <typename TIO, bool CH, bool GATED>
 __global__ __launch_bounds__(64) void decode_steps_kernel(
     int T, int BH, int H, float eps, const TIO *__restrict__ xq, const TIO *__restrict__ xk,
     const TIO *__restrict__ xv, const float *__restrict__ eta, float *__restrict__ W,
     float *__restrict__ b, const float *__restrict__ gamma, const float *__restrict__ beta,
-    TIO *__restrict__ o, int mb, int pos, float *__restrict__ Wc, float *__restrict__ bc) {
+    TIO *__restrict__ o, int mb, int pos, float *__restrict__ Wc, float *__restrict__ bc,
+    const float *__restrict__ theta, float eta_base) {
     const int j = threadIdx.x;
     const int seq = blockIdx.x;
     const int h = seq % H;
@@ -254,20 +268,22 @@ __global__ __launch_bounds__(64) void decode_steps_kernel(
     float *Wcs = CH ? Wc + static_cast<size_t>(seq) * DM * DM : nullptr;
     float *bcs = CH ? bc + static_cast<size_t>(seq) * DM : nullptr;
     const float gm = gamma[h * DM + j], bt = beta[h * DM + j];
+    const float thj = GATED ? theta[h * DM + j] : 0.f;
     if (__all(gm == 1.0f && bt == 0.0f))
-        run_steps<TIO, true, CH>(T, BH, eps, seq, j, xq, xk, xv, eta, Ws, bs, gm, bt, o, mb, pos,
-                                 Wcs, bcs);
+        run_steps<TIO, true, CH, GATED>(T, BH, eps, seq, j, xq, xk, xv, eta, Ws, bs, gm, bt, o, mb,
+                                        pos, Wcs, bcs, thj, eta_base);
     else
-        run_steps<TIO, false, CH>(T, BH, eps, seq, j, xq, xk, xv, eta, Ws, bs, gm, bt, o, mb, pos,
-                                  Wcs, bcs);
+        run_steps<TIO, false, CH, GATED>(T, BH, eps, seq, j, xq, xk, xv, eta, Ws, bs, gm, bt, o, mb,
+                                         pos, Wcs, bcs, thj, eta_base);
 }
 
-template <typename TIO, bool CH>
+template <typename TIO, bool CH, bool GATED>
 hipError_t launch_steps_t(const DecodeArgs &a, int T, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_steps_kernel<TIO, CH>), dim3(a.B * a.H), dim3(64), 0, stream, T,
+    hipLaunchKernelGGL((decode_steps_kernel<TIO, CH, GATED>), dim3(a.B * a.H), dim3(64), 0, stream, T,
                        a.B * a.H, a.H, a.eps, static_cast<const TIO *>(a.xq),
                        static_cast<const TIO *>(a.xk), static_cast<const TIO *>(a.xv), a.eta, a.W,
-                       a.b, a.gamma, a.beta, static_cast<TIO *>(a.o), a.mb, a.pos, a.Wc, a.bc);
+                       a.b, a.gamma, a.beta, static_cast<TIO *>(a.o), a.mb, a.pos, a.Wc, a.bc,
+                       a.theta, a.eta_base);
     return hipGetLastError();
 }
 
@@ -278,8 +294,12 @@ bool decode_steps_resident(int d) { return d == DM; }
 hipError_t launch_decode_steps(const DecodeArgs &a, int T, hipStream_t stream) {
     if (a.B * a.H == 0 || T == 0) return hipSuccess;
     const bool ch = a.Wc != nullptr;  // mini-batch decode
-    if (a.io) return ch ? launch_steps_t<bf16_t, true>(a, T, stream) : launch_steps_t<bf16_t, false>(a, T, stream);
-    return ch ? launch_steps_t<float, true>(a, T, stream) : launch_steps_t<float, false>(a, T, stream);
+    if (a.theta) {
+        if (a.io) return ch ? launch_steps_t<bf16_t, true, true>(a, T, stream) : launch_steps_t<bf16_t, false, true>(a, T, stream);
+        return ch ? launch_steps_t<float, true, true>(a, T, stream) : launch_steps_t<float, false, true>(a, T, stream);
+    }
+    if (a.io) return ch ? launch_steps_t<bf16_t, true, false>(a, T, stream) : launch_steps_t<bf16_t, false, false>(a, T, stream);
+    return ch ? launch_steps_t<float, true, false>(a, T, stream) : launch_steps_t<float, false, false>(a, T, stream);
 }
 
 }  // namespace ttt

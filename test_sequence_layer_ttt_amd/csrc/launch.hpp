@@ -62,6 +62,10 @@ struct DecodeArgs {
     // step kernel: pos = position of the first step within its chunk.
     float *Wc = nullptr, *bc = nullptr;
     int mode = 0, mb = 1, pos = 0;
+    // learning-rate gate: eta_t = eta_base * logistic(theta[h] . xk_t) in the
+    // kernel (eta unused when theta is set)
+    const float *theta = nullptr;
+    float eta_base = 0.f;
 };
 
 hipError_t launch_ln_l2_bwd(int rows, int d, const float *Z, const float *T, const float *gamma,

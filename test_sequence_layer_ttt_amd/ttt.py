@@ -396,6 +396,39 @@ def ttt_decode_steps_mb(xq, xk, xv, eta, W_chunk, b_chunk, W, b, ln_gamma, ln_be
     return o
 
 
+def ttt_decode_steps_gated(xq, xk, xv, theta_lr, eta_base: float, W, b, ln_gamma, ln_beta,
+                           mb: int = 1, pos: int = 0, W_chunk=None, b_chunk=None, o=None,
+                           ln_eps: float = 1e-6, stream=None):
+    """T consecutive decode tokens with eta_t = eta_base * logistic(theta_lr[h]
+    . xk_t) formed in the kernel (theta_lr [H,d] fp32). mb = 1 is b = 1 decode;
+    mb > 1 follows the mini-batch rule of ttt_decode_steps_mb and needs
+    W_chunk, b_chunk. States are updated in place. Returns o."""
+    T, B, H, d = xq.shape
+    io = _IO.get(xq.dtype)
+    if io is None:
+        raise TypeError(f"xq dtype {xq.dtype} not supported")
+    for t, n in ((xq, "xq"), (xk, "xk"), (xv, "xv")):
+        _need(t, n, (T, B, H, d), xq.dtype)
+    _need(theta_lr, "theta_lr", (H, d), torch.float32)
+    _need(W, "W", (B, H, d, d), torch.float32)
+    _need(b, "b", (B, H, d), torch.float32)
+    if mb > 1:
+        _need(W_chunk, "W_chunk", (B, H, d, d), torch.float32)
+        _need(b_chunk, "b_chunk", (B, H, d), torch.float32)
+    _need(ln_gamma, "ln_gamma", (H, d), torch.float32)
+    _need(ln_beta, "ln_beta", (H, d), torch.float32)
+    if o is None:
+        o = torch.empty_like(xq)
+    _need(o, "o", (T, B, H, d), xq.dtype)
+    lib = _lib.load()
+    _lib.check(lib.ttt_decode_steps_gated(T, B, H, d, io, ln_eps, mb, pos, _ptr(xq), _ptr(xk),
+                                          _ptr(xv), _ptr(theta_lr), float(eta_base),
+                                          _ptr(W_chunk), _ptr(b_chunk), _ptr(W), _ptr(b),
+                                          _ptr(ln_gamma), _ptr(ln_beta), _ptr(o),
+                                          _stream(stream)))
+    return o
+
+
 def ttt_ln_l2_bwd(Z, target, ln_gamma, ln_beta, G=None, ln_eps: float = 1e-6, stream=None):
     """Row-wise fused LN + L2 backward. Z, target, G [rows,d] fp32; gamma/beta [d]."""
     rows, d = Z.shape

@@ -283,6 +283,26 @@ def test_mlp_forward_gated_validation(lib):
     assert _mlp_gated(lib, B=0) == _lib.TTT_OK
 
 
+def _dec_gated(lib, eta_base=0.5, theta=FAKE + 3 * (1 << 20), mb=1, T=4, d=64,
+               o=FAKE + 8 * (1 << 20)):
+    p = [FAKE + i * (1 << 20) for i in range(12)]
+    return lib.ttt_decode_steps_gated(T, 2, 3, d, 1, 1e-6, mb, 0, p[0], p[1], p[2], theta, eta_base,
+                                      p[4], p[5], p[6], p[7], p[9], p[10], o, None)
+
+
+def test_decode_steps_gated_validation(lib):
+    for bad in (float("nan"), float("-inf")):
+        assert _dec_gated(lib, eta_base=bad) == _lib.TTT_E_SHAPE
+        assert "eta_base" in lib.ttt_last_error().decode()
+    assert _dec_gated(lib, theta=0) == _lib.TTT_E_NULL
+    assert "theta_lr" in lib.ttt_last_error().decode()
+    assert _dec_gated(lib, theta=FAKE + 3 * (1 << 20) + 2) == _lib.TTT_E_ALIGN
+    assert _dec_gated(lib, o=FAKE + 3 * (1 << 20)) == _lib.TTT_E_ALIAS  # o over theta_lr
+    assert _dec_gated(lib, d=32) == _lib.TTT_E_SHAPE
+    assert _dec_gated(lib, T=-1) == _lib.TTT_E_SHAPE
+    assert _dec_gated(lib, T=0) == _lib.TTT_OK  # returns before any launch
+
+
 def _gate(lib, B=2, H=3, L=40, d=64, io=1, xk=FAKE, th=FAKE + (1 << 20), eta_base=0.5,
           eta=FAKE + 2 * (1 << 20)):
     return lib.ttt_eta_gate(B, H, L, d, io, xk, th, eta_base, eta, None)

@@ -263,3 +263,66 @@ def test_gated_mlp_empty_sequence():
     assert got[0].shape == (2, 3, 0, 64)
     for g_, r_ in zip(got[1:], (x.W1, x.b1, x.W2, x.b2)):
         assert np.array_equal(g_, np.broadcast_to(r_, g_.shape))
+
+
+# ---------------------------------------------------------------------------
+# The gate inside the decode kernels (ttt_decode_steps_gated): a gated prefill
+# followed by gated decode calls equals the oracle's gate and prefill over the
+# whole sequence.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("io,d", [("bf16", 64), ("f32", 64), ("f32", 16)])
+@pytest.mark.parametrize("mb", [1, 4, 16])
+def test_gated_decode_continues_the_gated_prefill(io, d, mb):
+    B, H, L0 = 2, 3, 2 * mb
+    splits = [mb // 2 + 1, mb + 1, max(mb - 2, 1)]
+    T = sum(splits)
+    x = _gated(1000 + 3 * d + mb, B, H, L0 + T, d, io, ln_random=True, b_random=True, w_std=0.3)
+    dt = P.io_dtype(io)
+    th = P.dev(x.theta_lr)
+    O0, W, b = ttt.ttt_linear_forward_gated(*(P.dev(a[:, :, :L0], dt) for a in (x.XQ, x.XK, x.XV)),
+                                            th, x.eta_base, P.dev(x.W0), P.dev(x.b0),
+                                            P.dev(x.gamma), P.dev(x.beta), mb=mb, ln_eps=x.eps)
+    Wc, bc = torch.full_like(W, float("nan")), torch.full_like(b, float("nan"))  # unread at pos 0
+    step = lambda a: np.ascontiguousarray(np.moveaxis(a, 2, 0))   # [B,H,T,...] -> [T,B,H,...]
+    outs, t, pos = [], L0, 0
+    for n in splits:
+        sl = slice(t, t + n)
+        o = ttt.ttt_decode_steps_gated(*(P.dev(step(a[:, :, sl]), dt) for a in (x.XQ, x.XK, x.XV)),
+                                       th, x.eta_base, W, b, P.dev(x.gamma), P.dev(x.beta), mb=mb,
+                                       pos=pos, W_chunk=Wc if mb > 1 else None,
+                                       b_chunk=bc if mb > 1 else None, ln_eps=x.eps)
+        outs.append(np.moveaxis(P.to_np(o), 0, 2))
+        t, pos = t + n, (pos + n) % mb
+    torch.cuda.synchronize()
+    eta = oracle.eta_gate(x.XK, x.theta_lr, x.eta_base)
+    O_ref, W_ref, b_ref = oracle.linear_forward(x.XQ, x.XK, x.XV, eta, x.W0, x.b0, x.gamma, x.beta,
+                                                x.eps, mb=mb)
+    got = (np.concatenate(outs, 2), P.to_np(W), P.to_np(b))
+    err = P.errors(got, (O_ref[:, :, L0:], W_ref, b_ref), B * H, ("o", "W", "b"))
+    _report(f"decode mb={mb} {io} d{d}", err)
+    assert max(err.values()) <= P.TOL[io], err
+
+
+def test_gated_decode_workload5_shape():
+    """Workload 5's decode (1024 steps on 64 x 32 states of d = 64, bf16) with
+    the gate inside the resident kernel, from the same start state per
+    sequence, against the oracle's gate and b = 1 recurrence."""
+    _, dec = gen.make_workload(5)
+    rng = np.random.default_rng(55)
+    th = (0.3 * rng.standard_normal((dec.H, dec.d))).astype(np.float32)
+    W0 = (0.3 * rng.standard_normal((dec.B, dec.H, dec.d, dec.d))).astype(np.float32)
+    b0 = (0.1 * rng.standard_normal((dec.B, dec.H, dec.d))).astype(np.float32)
+    g, be = np.ones((dec.H, dec.d), np.float32), np.zeros((dec.H, dec.d), np.float32)
+    dt = P.io_dtype(dec.io)
+    W, b = P.dev(W0), P.dev(b0)
+    o = ttt.ttt_decode_steps_gated(P.dev(dec.XQ, dt), P.dev(dec.XK, dt), P.dev(dec.XV, dt),
+                                   P.dev(th), 1.0 / dec.d, W, b, P.dev(g), P.dev(be))
+    torch.cuda.synchronize()
+    tr = lambda a: np.ascontiguousarray(np.moveaxis(a, 0, 2))  # step-major -> [B,H,T,...]
+    eta = oracle.eta_gate(tr(dec.XK), th, 1.0 / dec.d)
+    ref = oracle.linear_forward(tr(dec.XQ), tr(dec.XK), tr(dec.XV), eta, W0, b0, g, be, 1e-6,
+                                mb=1, w0_batched=True)
+    got = (tr(P.to_np(o)), P.to_np(W), P.to_np(b))
+    err = P.errors(got, ref, dec.B * dec.H, ("o", "W", "b"))
+    _report("decode workload5 shape 64x32x1024", err)
+    assert max(err.values()) <= P.TOL["bf16"], err

@@ -96,11 +96,23 @@ def _variant_args(kind):
     return x, ins, st, th, P.dev(x.eta)
 
 
-@pytest.mark.parametrize("kind", ["linear_gated", "linear_opts", "mlp_gated", "mlp_opts", "gate"])
+def _decode_gated(ins, th, eb, st, s):
+    """64 gated decode steps on 2 x 32 states (the first 64 tokens of the
+    linear case as step-major inputs), each call from the same start state."""
+    step = lambda a: a[:, :, :64].permute(2, 0, 1, 3).contiguous()   # [B,H,T,d] -> [T,B,H,d]
+    W = st[0].unsqueeze(0).expand(2, -1, -1, -1).contiguous()
+    b = st[1].unsqueeze(0).expand(2, -1, -1).contiguous()
+    o = ttt.ttt_decode_steps_gated(step(ins[0]), step(ins[1]), step(ins[2]), th, eb, W, b, st[2],
+                                   st[3], stream=s)
+    return o, W, b
+
+
+@pytest.mark.parametrize("kind", ["linear_gated", "linear_opts", "mlp_gated", "mlp_opts", "gate",
+                                  "decode_gated"])
 def test_variant_entry_points_on_side_stream(kind):
     """The gated and option prefills and the standalone gate: side stream
     against default stream, bit for bit (the kernels are deterministic)."""
-    x, ins, st, th, eta = _variant_args(kind)
+    x, ins, st, th, eta = _variant_args("linear" if kind == "decode_gated" else kind)
     eb = 1.0 / x.d
     fn = {
         "linear_gated": lambda s: ttt.ttt_linear_forward_gated(*ins, th, eb, *st, stream=s),
@@ -110,5 +122,6 @@ def test_variant_entry_points_on_side_stream(kind):
         "mlp_opts": lambda s: ttt.ttt_mlp_forward_opts(*ins, eta, *st, "inner_product", 0.5,
                                                        stream=s),
         "gate": lambda s: ttt.ttt_eta_gate(ins[1], th, eb, stream=s),
+        "decode_gated": lambda s: _decode_gated(ins, th, eb, st, s),
     }[kind]
-    _check(fn, 1.0 if kind == "gate" else 20.0)
+    _check(fn, 1.0 if kind in ("gate", "decode_gated") else 20.0)
