@@ -10,11 +10,17 @@ Other workloads of the same hot path (--workload):
   2   TTT-Linear prefill, B=4, H=12, L=2048 (RMS-normalised inputs)
   5p  TTT-Linear prefill, B=1, H=32, L=32768
   4   TTT-MLP prefill, B=2, H=12, L=8192 (roofline: bf16 MFMA)
+  4o  the MLP prefill through ttt_mlp_forward_opts (inner-product loss, weight
+      decay 0.5 on W1 and W2)
+  4g  the MLP prefill through ttt_mlp_forward_gated (eta from the gate in the
+      kernel, theta_lr ~ N(0, 0.02^2), eta_base = 1/d)
   5d  TTT-Linear decode: one b=1 step on 64 x 32 states (roofline: state bytes)
   5r  TTT-Linear decode: 1024 b=1 steps on 64 x 32 states in one call, states
       resident in registers (roofline: fp32 vector ALU)
   5m  the same 1024 tokens under the mini-batch rule (b = 16) through
       ttt_decode_steps_mb: both states resident (roofline: fp32 vector ALU)
+  5g  the same 1024 b=1 steps through ttt_decode_steps_gated (eta from the
+      gate in the kernel; roofline: fp32 vector ALU)
   3b  TTT-Linear backward (ttt_linear_backward) on workload 3's shapes
       (roofline: fp32 vector ALU)
   3g  workload 3 through ttt_linear_forward_gated: eta from the learning-rate
