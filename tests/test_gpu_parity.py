@@ -476,3 +476,32 @@ def test_decode_steps_mb_zero_steps_leaves_state():
                             mb=16, pos=5)
     torch.cuda.synchronize()
     assert torch.equal(W, W1) and torch.equal(b, b1) and torch.equal(Wc, Wc1) and torch.equal(bc, bc1)
+
+
+def test_decode_steps_mb16_full_workload5():
+    """Workload 5's 1024 decode tokens on 64 x 32 states under the mini-batch
+    rule with b = 16 in one call (the benchmark's launch), from per-state start
+    states: outputs, final state and the last chunk's start state against the
+    oracle's b = 16 recurrence over the same tokens."""
+    _, dec = gen.make_workload(5)
+    rng = np.random.default_rng(56)
+    W0 = (0.3 * rng.standard_normal((dec.B, dec.H, dec.d, dec.d))).astype(np.float32)
+    b0 = (0.1 * rng.standard_normal((dec.B, dec.H, dec.d))).astype(np.float32)
+    g, be = np.ones((dec.H, dec.d), np.float32), np.zeros((dec.H, dec.d), np.float32)
+    dt = P.io_dtype(dec.io)
+    W, b = P.dev(W0), P.dev(b0)
+    Wc, bc = torch.full_like(W, float("nan")), torch.full_like(b, float("nan"))  # unread at pos 0
+    o = ttt.ttt_decode_steps_mb(P.dev(dec.XQ, dt), P.dev(dec.XK, dt), P.dev(dec.XV, dt),
+                                P.dev(dec.eta), Wc, bc, W, b, P.dev(g), P.dev(be), mb=16, pos=0)
+    torch.cuda.synchronize()
+    tr = lambda a: np.ascontiguousarray(np.moveaxis(a, 0, 2))  # step-major -> [B,H,T,...]
+    xs = [tr(a) for a in (dec.XQ, dec.XK, dec.XV, dec.eta)]
+    O_ref, W_ref, b_ref = oracle.linear_forward(*xs, W0, b0, g, be, 1e-6, mb=16, w0_batched=True)
+    Lc = dec.steps - 16  # start of the last chunk
+    _, Wc_ref, bc_ref = oracle.linear_forward(*(a[:, :, :Lc] for a in xs), W0, b0, g, be, 1e-6,
+                                              mb=16, w0_batched=True)
+    got = (tr(P.to_np(o)), P.to_np(W), P.to_np(b), P.to_np(Wc), P.to_np(bc))
+    err = P.errors(got, (O_ref, W_ref, b_ref, Wc_ref, bc_ref), dec.B * dec.H,
+                   ("o", "W", "b", "W_chunk", "b_chunk"))
+    _report("workload5 decode_steps_mb b=16 64x32x1024", err)
+    assert max(err.values()) <= P.TOL["bf16"], err
