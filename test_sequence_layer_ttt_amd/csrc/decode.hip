@@ -19,7 +19,7 @@
 // bc. The output identity still uses the current W: xq W' + b' =
 // (xq W + b) - eta (xq . xk + 1) G.
 //
-// With theta set, the step's rate comes from the learning-rate gate of the
+// GATED: the step's rate comes from the learning-rate gate of the
 // lryc.cn TTT article (§2.2), eta = eta_base * logistic(theta[h] . xk), x read
 // as the key, instead of the eta array.
 #include "common.hpp"
@@ -27,12 +27,12 @@
 
 namespace ttt {
 
-template <int D, typename TIO>
+template <int D, typename TIO, bool GATED, int MODE>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     int H, float eps, const TIO *__restrict__ xq, const TIO *__restrict__ xk,
     const TIO *__restrict__ xv, const float *__restrict__ eta, float *__restrict__ W,
     float *__restrict__ b, const float *__restrict__ gamma, const float *__restrict__ beta,
-    TIO *__restrict__ o, float *__restrict__ Wc, float *__restrict__ bc, int mode,
+    TIO *__restrict__ o, float *__restrict__ Wc, float *__restrict__ bc,
     const float *__restrict__ theta, float eta_base) {
     constexpr int NT = 256, P = NT / D, RPT = D / P, E = D / 16;
     using io = io_traits<TIO>;
@@ -56,8 +56,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     for (int r = 0; r < RPT; ++r) w[r] = Ws[static_cast<size_t>(p * RPT + r) * D + j];
 #pragma unroll
     for (int r = 0; r < RPT; ++r)
-        wz[r] = mode == 2 ? Wcs[static_cast<size_t>(p * RPT + r) * D + j] : w[r];
-    if (mode == 1) {  // a chunk starts here: its start state is the current one
+        wz[r] = MODE == 2 ? Wcs[static_cast<size_t>(p * RPT + r) * D + j] : w[r];
+    if constexpr (MODE == 1) {  // a chunk starts here: its start state is the current one
 #pragma unroll
         for (int r = 0; r < RPT; ++r) Wcs[static_cast<size_t>(p * RPT + r) * D + j] = w[r];
     }
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 
     if (tid < 16) {
         float et;
-        if (theta) {  // uniform: the gate from the staged key
+        if constexpr (GATED) {  // the gate from the staged key
             float s = 0.f;
 #pragma unroll
             for (int e = 0; e < E; ++e) s += theta[static_cast<size_t>(h) * D + tid + 16 * e] * sk[tid + 16 * e];
@@ -96,8 +96,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
             }
             bb[e] = b[static_cast<size_t>(seq) * D + jj];
             const size_t bi = static_cast<size_t>(seq) * D + jj;
-            z[e] = zs + (mode == 2 ? bc[bi] : bb[e]);
-            if (mode == 1) bc[bi] = bb[e];
+            z[e] = zs + (MODE == 2 ? bc[bi] : bb[e]);
+            if constexpr (MODE == 1) bc[bi] = bb[e];
             q[e] = qs;
             tau[e] = io::load(xv, static_cast<size_t>(seq) * D + jj) - sk[jj];
             gm[e] = gamma[static_cast<size_t>(h) * D + jj];
@@ -127,20 +127,33 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         Ws[static_cast<size_t>(p * RPT + r) * D + j] = w[r] - et * sk[p * RPT + r] * gj;
 }
 
-template <int D, typename TIO>
-static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_step_kernel<D, TIO>), dim3(a.B * a.H), dim3(256), 0, stream, a.H,
+template <int D, typename TIO, bool GATED, int MODE>
+static hipError_t launch_decode_m(const DecodeArgs &a, hipStream_t stream) {
+    hipLaunchKernelGGL((decode_step_kernel<D, TIO, GATED, MODE>), dim3(a.B * a.H), dim3(256), 0, stream, a.H,
                        a.eps, static_cast<const TIO *>(a.xq), static_cast<const TIO *>(a.xk),
                        static_cast<const TIO *>(a.xv), a.eta, a.W, a.b, a.gamma, a.beta,
-                       static_cast<TIO *>(a.o), a.Wc, a.bc, a.mode, a.theta, a.eta_base);
+                       static_cast<TIO *>(a.o), a.Wc, a.bc, a.theta, a.eta_base);
     return hipGetLastError();
+}
+
+// mode (b > 1 decode): 0 plain b = 1 step, 1 starts a chunk, 2 continues one
+template <int D, typename TIO, bool GATED>
+static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
+    if (a.mode == 1) return launch_decode_m<D, TIO, GATED, 1>(a, stream);
+    if (a.mode == 2) return launch_decode_m<D, TIO, GATED, 2>(a, stream);
+    return launch_decode_m<D, TIO, GATED, 0>(a, stream);
+}
+
+template <bool GATED>
+static hipError_t launch_decode_g(const DecodeArgs &a, hipStream_t stream) {
+    if (a.d == 16) return a.io ? launch_decode_t<16, bf16_t, GATED>(a, stream) : launch_decode_t<16, float, GATED>(a, stream);
+    if (a.d == 64) return a.io ? launch_decode_t<64, bf16_t, GATED>(a, stream) : launch_decode_t<64, float, GATED>(a, stream);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     if (a.B * a.H == 0) return hipSuccess;
-    if (a.d == 16) return a.io ? launch_decode_t<16, bf16_t>(a, stream) : launch_decode_t<16, float>(a, stream);
-    if (a.d == 64) return a.io ? launch_decode_t<64, bf16_t>(a, stream) : launch_decode_t<64, float>(a, stream);
-    return hipErrorInvalidValue;
+    return a.theta ? launch_decode_g<true>(a, stream) : launch_decode_g<false>(a, stream);
 }
 
 }  // namespace ttt
