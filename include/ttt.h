@@ -64,6 +64,11 @@ extern "C" {
 #define TTT_E_ALIAS (-5) /* an output overlaps an input or another output      */
 #define TTT_E_HIP (-6)   /* the kernel launch failed                           */
 
+/* Longest sequence any prefill entry point accepts (tokens per (n,h));
+ * longer L is TTT_E_SHAPE. Token and chunk indices inside the kernels are
+ * 32-bit ints; byte offsets are 64-bit. */
+#define TTT_MAX_L (1 << 30)
+
 /* Inner loss of ttt_linear_forward_opts and ttt_mlp_forward_opts. */
 #define TTT_LOSS_MSE 0           /* 1/2 ||LN(f_res(XK)) - (XV - XK)||^2 per token */
 #define TTT_LOSS_INNER_PRODUCT 1 /* -< XK + LN(f_res(XK)), XV > per token        */
@@ -87,7 +92,13 @@ typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
  *              skips the store). With w0_batched == 1 they may be exactly
  *              W0 / b0 (in-place resume); any other overlap is TTT_E_ALIAS.
  *   ln_eps   : a positive normal float (>= FLT_MIN, finite), else TTT_E_SHAPE
- *              (the same for every entry point below).
+ *              (the same for every entry point below). L > TTT_MAX_L is
+ *              TTT_E_SHAPE (also for every prefill and backward entry point).
+ *   W0 and b0 may carry any offset: the layer-norm statistics are sums of
+ *   centred values (the bf16 d = 64 kernel holds the state with its row means
+ *   removed, which shifts z by a per-token constant the layer norm does not
+ *   see; the other kernels centre each row before squaring), so rows whose
+ *   mean is large against their spread keep their accuracy.
  * Numerics: state, accumulation and layer-norm statistics in fp32. On the
  * bf16 path with d = 64 and mb = 16 the products XK W and XQ W take W and
  * the XQ / XK rows as fp16 MFMA operands (the bf16 inputs convert exactly;

@@ -89,6 +89,8 @@ int check_common(int B, int H, int L, int mb, int io) {
     if (B < 0 || H < 0 || L < 0) return fail(TTT_E_SHAPE, "negative size (B=%d H=%d L=%d)", B, H, L);
     if (io != TTT_F32 && io != TTT_BF16) return fail(TTT_E_DTYPE, "io dtype %d is not TTT_F32/TTT_BF16", io);
     if (mb < 1 || mb > 16) return fail(TTT_E_SHAPE, "mini-batch size %d not in [1, 16]", mb);
+    // token and chunk indices inside the kernels are 32-bit ints
+    if (L > TTT_MAX_L) return fail(TTT_E_SHAPE, "L = %d exceeds TTT_MAX_L = %d", L, TTT_MAX_L);
     if (static_cast<long long>(B) * H > INT_MAX) return fail(TTT_E_SHAPE, "B*H = %lld too large", static_cast<long long>(B) * H);
     return TTT_OK;
 }

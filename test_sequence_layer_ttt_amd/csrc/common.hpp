@@ -61,21 +61,33 @@ __device__ __forceinline__ float gelu_prime_f(float x) {
 // Layer-norm helpers over one row of D features spread over a group of
 // GL lanes, each lane holding E = D / GL values (element j = lane + GL * e).
 // ---------------------------------------------------------------------------
+// Centred row cz = z - mean(z) and rstd = 1 / sqrt(var + eps), in three
+// rounds: the mean m1, then the mean of z - m1 (the rounding error of m1,
+// which a large common offset of the row makes comparable to the row's
+// spread), then the variance as the mean of the squared centred values.
+// Nothing subtracts two large sums, so the result keeps its accuracy
+// whatever the row's offset.
 template <int GL, int E>
-__device__ __forceinline__ void row_stats(const float (&z)[E], float inv_d, float eps,
-                                          float &mu, float &rstd) {
+__device__ __forceinline__ void row_centre(const float (&z)[E], float inv_d, float eps,
+                                           float (&cz)[E], float &rstd) {
     float s = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) s += z[e];
-    mu = group_sum<GL>(s) * inv_d;
+    const float m1 = group_sum<GL>(s) * inv_d;
+    float s1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        cz[e] = z[e] - m1;
+        s1 += cz[e];
+    }
+    const float dm = group_sum<GL>(s1) * inv_d;
     float v = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        const float c = z[e] - mu;
-        v += c * c;
+        cz[e] -= dm;
+        v += cz[e] * cz[e];
     }
-    v = group_sum<GL>(v) * inv_d;
-    rstd = rsqrtf(v + eps);
+    rstd = rsqrtf(group_sum<GL>(v) * inv_d + eps);
 }
 
 // G = d/dz 1/2 ||gamma * xhat + beta - tau||^2
@@ -84,13 +96,13 @@ template <int GL, int E>
 __device__ __forceinline__ void ln_l2_grad(const float (&z)[E], const float (&tau)[E],
                                            const float (&gamma)[E], const float (&beta)[E],
                                            float inv_d, float eps, float (&G)[E]) {
-    float mu, rstd;
-    row_stats<GL, E>(z, inv_d, eps, mu, rstd);
+    float cz[E], rstd;
+    row_centre<GL, E>(z, inv_d, eps, cz, rstd);
     float xh[E], gh[E];
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        xh[e] = (z[e] - mu) * rstd;
+        xh[e] = cz[e] * rstd;
         gh[e] = gamma[e] * (gamma[e] * xh[e] + beta[e] - tau[e]);
         s1 += gh[e];
         s2 += gh[e] * xh[e];
@@ -107,13 +119,13 @@ template <int GL, int E>
 __device__ __forceinline__ void ln_ip_grad(const float (&z)[E], const float (&v)[E],
                                            const float (&gamma)[E], float inv_d, float eps,
                                            float (&G)[E]) {
-    float mu, rstd;
-    row_stats<GL, E>(z, inv_d, eps, mu, rstd);
+    float cz[E], rstd;
+    row_centre<GL, E>(z, inv_d, eps, cz, rstd);
     float xh[E], gh[E];
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        xh[e] = (z[e] - mu) * rstd;
+        xh[e] = cz[e] * rstd;
         gh[e] = -gamma[e] * v[e];
         s1 += gh[e];
         s2 += gh[e] * xh[e];
@@ -128,10 +140,10 @@ template <int GL, int E>
 __device__ __forceinline__ void ln_fwd(const float (&z)[E], const float (&gamma)[E],
                                        const float (&beta)[E], float inv_d, float eps,
                                        float (&y)[E]) {
-    float mu, rstd;
-    row_stats<GL, E>(z, inv_d, eps, mu, rstd);
+    float cz[E], rstd;
+    row_centre<GL, E>(z, inv_d, eps, cz, rstd);
 #pragma unroll
-    for (int e = 0; e < E; ++e) y[e] = gamma[e] * ((z[e] - mu) * rstd) + beta[e];
+    for (int e = 0; e < E; ++e) y[e] = gamma[e] * (cz[e] * rstd) + beta[e];
 }
 
 }  // namespace ttt

@@ -30,8 +30,6 @@
 #include "launch.hpp"
 #include "tile.hpp"
 
-#include <utility>
-
 namespace ttt {
 namespace {
 
@@ -48,18 +46,73 @@ __device__ __forceinline__ f32x4 wave_sum2(float a, float b) {
     return rows4_gather(rows4_reduce2(row16_sum(a), row16_sum(b)));
 }
 
-// acc + x[lane n of this lane's DPP row] * w: the broadcast is the DPP
-// source modifier of the FMA itself (row_newbcast), so it costs nothing.
-// A DPP source must be written at least two wait states before it is read;
-// the compiler does not see DPP inside asm, so dpp_guard (an s_nop 1 that
-// takes the sources as operands, hence follows their last write) precedes
-// each run of these FMAs, and both are volatile so they keep that order.
-template <int N>
-__device__ __forceinline__ float fmac_bcast(float acc, float x, float w) {
-    asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
-        : "+v"(acc)
-        : "v"(x), "v"(w), "n"(N));
-    return acc;
+// DPP row-broadcast FMAs. Element i = 4 n + m of a broadcast-layout vector
+// x (see Raw below) is x[m] of lane n of each 16-lane DPP row, so
+// row_newbcast:n as the FMA's own source modifier hands it to every lane at
+// no cost. The compiler does not fold a DPP move into an FMA, so these are
+// written in assembly, sixteen FMAs (rows 4 NB .. 4 NB + 3) to a block. A DPP
+// instruction must not read a VGPR within two wait states of a VALU write to
+// it (five after an EXEC write); each block therefore opens with s_nop 4 and
+// takes every register it reads as an operand, so nothing the compiler
+// schedules can fall between the guard and the FMAs. Inside a block no FMA
+// reads a register written by either of the two instructions before it: the
+// dot product rotates four accumulators (one per m) and the update writes
+// sixteen distinct elements.
+
+// a[m] += sum over n in 4 NB .. 4 NB + 3 of x_{4n+m} w[4n+m]
+template <int NB>
+__device__ __forceinline__ void dot_block(const float (&x)[4], const float (&w)[DM], float (&a)[4]) {
+    asm("s_nop 4\n\t"
+        "v_fmac_f32_dpp %0, %4, %8 row_newbcast:%24 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %9 row_newbcast:%24 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %10 row_newbcast:%24 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %11 row_newbcast:%24 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %12 row_newbcast:%25 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %13 row_newbcast:%25 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %14 row_newbcast:%25 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %15 row_newbcast:%25 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %16 row_newbcast:%26 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %17 row_newbcast:%26 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %18 row_newbcast:%26 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %19 row_newbcast:%26 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %20 row_newbcast:%27 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %21 row_newbcast:%27 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %22 row_newbcast:%27 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %23 row_newbcast:%27 row_mask:0xf bank_mask:0xf\n\t"
+        : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3])
+        : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(w[16 * NB + 0]), "v"(w[16 * NB + 1]),
+          "v"(w[16 * NB + 2]), "v"(w[16 * NB + 3]), "v"(w[16 * NB + 4]), "v"(w[16 * NB + 5]),
+          "v"(w[16 * NB + 6]), "v"(w[16 * NB + 7]), "v"(w[16 * NB + 8]), "v"(w[16 * NB + 9]),
+          "v"(w[16 * NB + 10]), "v"(w[16 * NB + 11]), "v"(w[16 * NB + 12]), "v"(w[16 * NB + 13]),
+          "v"(w[16 * NB + 14]), "v"(w[16 * NB + 15]), "n"(4 * NB), "n"(4 * NB + 1), "n"(4 * NB + 2),
+          "n"(4 * NB + 3));
+}
+// w[4n+m] += x_{4n+m} e for n in 4 NB .. 4 NB + 3
+template <int NB>
+__device__ __forceinline__ void axpy_block(const float (&x)[4], float e, float (&w)[DM]) {
+    asm("s_nop 4\n\t"
+        "v_fmac_f32_dpp %0, %16, %20 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %17, %20 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %18, %20 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %19, %20 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %16, %20 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %17, %20 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %18, %20 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %19, %20 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %8, %16, %20 row_newbcast:%23 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %9, %17, %20 row_newbcast:%23 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %10, %18, %20 row_newbcast:%23 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %11, %19, %20 row_newbcast:%23 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %12, %16, %20 row_newbcast:%24 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %13, %17, %20 row_newbcast:%24 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %14, %18, %20 row_newbcast:%24 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %15, %19, %20 row_newbcast:%24 row_mask:0xf bank_mask:0xf\n\t"
+        : "+v"(w[16 * NB + 0]), "+v"(w[16 * NB + 1]), "+v"(w[16 * NB + 2]), "+v"(w[16 * NB + 3]),
+          "+v"(w[16 * NB + 4]), "+v"(w[16 * NB + 5]), "+v"(w[16 * NB + 6]), "+v"(w[16 * NB + 7]),
+          "+v"(w[16 * NB + 8]), "+v"(w[16 * NB + 9]), "+v"(w[16 * NB + 10]), "+v"(w[16 * NB + 11]),
+          "+v"(w[16 * NB + 12]), "+v"(w[16 * NB + 13]), "+v"(w[16 * NB + 14]), "+v"(w[16 * NB + 15])
+        : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(e), "n"(4 * NB), "n"(4 * NB + 1),
+          "n"(4 * NB + 2), "n"(4 * NB + 3));
 }
 
 // Broadcast layout of a 64-element input vector: lane l holds elements
@@ -99,30 +152,22 @@ template <> struct Raw<float> {
     __device__ __forceinline__ float own() const { return v1; }
 };
 
-__device__ __forceinline__ void dpp_guard(const float (&x)[4]) {
-    asm volatile("s_nop 1" ::"v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]));
+// sum over i of x_i w[i], as four partial sums
+__device__ __forceinline__ float dot64(const float (&x)[4], const float (&w)[DM], float init) {
+    float a[4] = {init, 0.f, 0.f, 0.f};
+    dot_block<0>(x, w, a);
+    dot_block<1>(x, w, a);
+    dot_block<2>(x, w, a);
+    dot_block<3>(x, w, a);
+    return (a[0] + a[1]) + (a[2] + a[3]);
 }
-
-// a0 + a1 = sum over i of x_i w[i] (two accumulators).
-template <int... N>
-__device__ __forceinline__ void dot_bcast(const float (&x)[4], const float (&w)[DM], float &a0,
-                                          float &a1, std::integer_sequence<int, N...>) {
-    dpp_guard(x);
-    ((a0 = fmac_bcast<N>(a0, x[0], w[4 * N]), a1 = fmac_bcast<N>(a1, x[1], w[4 * N + 1]),
-      a0 = fmac_bcast<N>(a0, x[2], w[4 * N + 2]), a1 = fmac_bcast<N>(a1, x[3], w[4 * N + 3])),
-     ...);
+// w[i] += x_i e
+__device__ __forceinline__ void axpy64(const float (&x)[4], float e, float (&w)[DM]) {
+    axpy_block<0>(x, e, w);
+    axpy_block<1>(x, e, w);
+    axpy_block<2>(x, e, w);
+    axpy_block<3>(x, e, w);
 }
-// w[i] += x_i e.
-template <int... N>
-__device__ __forceinline__ void axpy_bcast(const float (&x)[4], float e, float (&w)[DM],
-                                           std::integer_sequence<int, N...>) {
-    dpp_guard(x);
-    ((w[4 * N] = fmac_bcast<N>(w[4 * N], x[0], e), w[4 * N + 1] = fmac_bcast<N>(w[4 * N + 1], x[1], e),
-      w[4 * N + 2] = fmac_bcast<N>(w[4 * N + 2], x[2], e),
-      w[4 * N + 3] = fmac_bcast<N>(w[4 * N + 3], x[3], e)),
-     ...);
-}
-using Rows16 = std::make_integer_sequence<int, 16>;
 
 template <typename TIO, bool IDENT, bool CH, bool GATED>
 __device__ __forceinline__ void run_steps(int T, int BH, float eps, int seq, int j,
@@ -147,13 +192,33 @@ __device__ __forceinline__ void run_steps(int T, int BH, float eps, int seq, int
             bcj = bcs[j];
         }
     }
+    // Centred state for the whole call: W - wbar 1^T and b - bbar (wbar the
+    // row means of W, bbar the mean of b, each wave sum bitwise identical in
+    // every lane). Every z and zbar then moves by a per-token constant that
+    // the layer norm and its backward do not see, and the per-step updates
+    // (rows of E sum to zero, so they keep the centring) accumulate into
+    // small numbers instead of into a large offset, whose fp32 spacing would
+    // swallow them. The chunk-start copy takes the same shift. The caller's
+    // representation is restored before the state is stored.
+    float wb_own = 0.f;  // lane j keeps wbar_j for the way out
+#pragma unroll
+    for (int i = 0; i < DM; ++i) {
+        const float m = wave_sum(w[i]) * inv_d;
+        wb_own = (i == j) ? m : wb_own;
+        w[i] -= m;
+        if constexpr (CH) {
+            if (pos > 0) wc[i] -= m;  // (pos == 0: set when the first step starts its chunk)
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one reduction at a time: no register peak here
+    }
+    asm volatile("" : "+v"(wb_own));  // formed here, not sunk to its use after the loop
+    const float bbar = wave_sum(bj) * inv_d;
+    bj -= bbar;
+    if constexpr (CH) bcj -= bbar;
     int k = pos;  // CH: position of step t within its chunk
     // per-head constants of the general layer-norm backward
-    float Sg2 = static_cast<float>(DM), Sgb = 0.f;
-    if constexpr (!IDENT) {
-        Sg2 = wave_sum(gm * gm);
-        Sgb = wave_sum(gm * bt);
-    }
+    float Sgb = 0.f;
+    if constexpr (!IDENT) Sgb = wave_sum(gm * bt);
     const float g2 = gm * gm;
 
     size_t base = static_cast<size_t>(seq) * DM;  // step 0
@@ -179,77 +244,82 @@ __device__ __forceinline__ void run_steps(int T, int BH, float eps, int seq, int
             if constexpr (!GATED) et = eta[static_cast<size_t>(t + 1) * BH + seq];
         }
         const float tau = xvj - xkj;
-        float qk;
-        if constexpr (GATED) {  // xq . xk and theta . xk in one pair of wave sums
-            const f32x4 s = wave_sum2(xqj * xkj, thj * xkj);
-            qk = s[0];
-            etc = eta_base * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * s[2]));
-        } else {
-            qk = wave_sum(xqj * xkj);
-        }
 
         // (xq W)_j and z_j = (xk W + b)_j, W, b at the chunk start for z
-        float p0 = 0.f, p1 = 0.f, z0, z1 = 0.f;
-        dot_bcast(qb, w, p0, p1, Rows16{});
+        const float p = dot64(qb, w, 0.f);
+        float z;
         if constexpr (CH) {
             if (k == 0) {  // a chunk starts: its start state is the current one
 #pragma unroll
                 for (int i = 0; i < DM; ++i) wc[i] = w[i];
                 bcj = bj;
             }
-            z0 = bcj;
-            dot_bcast(kb, wc, z0, z1, Rows16{});
+            z = dot64(kb, wc, bcj);
             k = (k + 1 == mb) ? 0 : k + 1;
         } else {
-            z0 = bj;
-            dot_bcast(kb, w, z0, z1, Rows16{});
+            z = dot64(kb, w, bj);
         }
-        const float z = z0 + z1, p = p0 + p1;
 
-        // E_j = -eta * d/dz_j [ 1/2 || LN(z) - tau ||^2 ]
-        float e;
+        // E_j = -eta * d/dz_j [ 1/2 || LN(z) - tau ||^2 ]. Layer-norm sums in
+        // two rounds: the means first (with xq . xk and the gate's theta . xk),
+        // then sums of centred products, so a large common offset of z cancels
+        // exactly instead of in E[z^2] - mu^2.
+        const float qkp = xqj * xkj, thp = GATED ? thj * xkj : 0.f;
+        float e, qk;
         if constexpr (IDENT) {
-            const f32x4 s = wave_sum4(z, z * z, tau * z, tau);
-            const float mu = s[0] * inv_d, mut = s[3] * inv_d;
-            const float var = fmaxf(fmaf(s[1], inv_d, -mu * mu), 0.f);
-            const float r = rsq(var + eps);
+            const f32x4 s = wave_sum4(z, tau, qkp, thp);
+            qk = s[2];
+            if constexpr (GATED)
+                etc = eta_base * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * s[3]));
+            const float cz = z - s[0] * inv_d, ct = tau - s[1] * inv_d;
+            const f32x4 q = wave_sum2(cz * cz, ct * cz);
+            const float r = rsq(fmaf(q[0], inv_d, eps));
             const float r2 = r * r;
-            const float a = r2 * fmaf(r, fmaf(s[2], inv_d, -mut * mu), eps * r2);
-            e = -etc * fmaf(a, z - mu, -r * (tau - mut));
+            // a = r^2 (eps r^2 + r mean((tau - mean tau)(z - mu)))
+            const float a = r2 * fmaf(r, q[2] * inv_d, eps * r2);
+            e = -etc * fmaf(a, cz, -r * ct);
         } else {
-            const f32x4 s = wave_sum4(z, z * z, g2 * z, g2 * z * z);
-            const f32x4 s2 = wave_sum4(gm * bt * z, gm * tau * z, gm * tau, 0.f);
-            const float mu = s[0] * inv_d;
-            const float var = fmaxf(fmaf(s[1], inv_d, -mu * mu), 0.f);
-            const float r = rsq(var + eps);
-            // mean(ghat) and mean(ghat xhat), ghat = gamma (gamma xhat + beta - tau)
-            const float m1 = (fmaf(r, fmaf(-mu, Sg2, s[2]), Sgb) - s2[2]) * inv_d;
-            const float q2 = fmaf(mu, fmaf(mu, Sg2, -2.f * s[2]), s[3]);
-            const float q1 = fmaf(-mu, Sgb, s2[0]) - fmaf(-mu, s2[2], s2[1]);
-            const float m2 = fmaf(r * r, q2, r * q1) * inv_d;
-            e = -etc * r * (fmaf(r * (g2 - m2), z - mu, gm * (bt - tau)) - m1);
+            const f32x4 s = wave_sum4(z, gm * tau, qkp, thp);
+            qk = s[2];
+            if constexpr (GATED)
+                etc = eta_base * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * s[3]));
+            const float cz = z - s[0] * inv_d;
+            const float gbt = gm * (bt - tau);
+            const f32x4 q = wave_sum4(cz * cz, g2 * cz, g2 * cz * cz, gbt * cz);
+            const float r = rsq(fmaf(q[0], inv_d, eps));
+            // mean(ghat) and mean(ghat xhat), ghat = gamma (gamma xhat + beta - tau), xhat = r cz
+            const float m1 = (fmaf(r, q[1], Sgb) - s[1]) * inv_d;
+            const float m2 = r * fmaf(r, q[2], q[3]) * inv_d;
+            e = -etc * r * (fmaf(r * (g2 - m2), cz, gbt) - m1);
         }
 
         // W += xk^T E (column j)
-        axpy_bcast(kb, e, w, Rows16{});
+        axpy64(kb, e, w);
 
         // o = xq + LN(xq W' + b'),  xq W' + b' = xq W + b + (xq . xk + 1) E
         const float zb = fmaf(qk + 1.f, e, p + bj);
         bj += e;
-        const f32x4 f = wave_sum2(zb, zb * zb);
-        const float mu = f[0] * inv_d;
-        const float r = rsq(fmaxf(fmaf(f[2], inv_d, -mu * mu), 0.f) + eps);
-        io::store(o, base + j, IDENT ? fmaf(zb - mu, r, xqj) : xqj + fmaf(gm, (zb - mu) * r, bt));
+        const float cb = zb - wave_sum(zb) * inv_d;
+        const float r = rsq(fmaf(wave_sum(cb * cb), inv_d, eps));
+        io::store(o, base + j, IDENT ? fmaf(cb, r, xqj) : xqj + fmaf(gm, cb * r, bt));
 
         base = nbase;
     }
+    // wbar in the broadcast layout (lane l: elements 4 (l mod 16) + m), then
+    // w[i] += 1 * wbar_i with the broadcast FMAs (exact product, one rounding)
+    float wbb[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        wbb[m] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (4 * (j & 15) + m), __float_as_int(wb_own)));
+    axpy64(wbb, 1.0f, w);
+    if constexpr (CH) axpy64(wbb, 1.0f, wc);  // the start state of the last step's chunk
 #pragma unroll
     for (int i = 0; i < DM; ++i) Ws[i * DM + j] = w[i];
-    bs[j] = bj;
-    if constexpr (CH) {  // the start state of the chunk the last step belongs to
+    bs[j] = bj + bbar;
+    if constexpr (CH) {
 #pragma unroll
         for (int i = 0; i < DM; ++i) Wcs[i * DM + j] = wc[i];
-        bcs[j] = bcj;
+        bcs[j] = bcj + bbar;
     }
 }
 

@@ -48,6 +48,12 @@
 //  * two barriers per chunk. Phase 1: chain Z_c and its partial row sums;
 //    state waves apply E_{c-1} and start O_{c-1}. Phase 2: chain E_c; state
 //    waves finish O_{c-1} and prepare the operands of chunks c .. c+2.
+//  * centred state: the state waves hold W - wbar 1^T and b - bbar (wbar the
+//    row means of W_0, bbar the mean of b_0), which shifts every row of Z and
+//    Zbar by a per-token constant that the layer norm and its backward do not
+//    see; the rows of E sum to zero, so the updates keep the centring. The
+//    one-pass row sums of z and z^2 therefore act on rows whose mean is near
+//    zero, whatever offsets the caller's W_0 and b_0 carry.
 //  Precision: W grows along the sequence and its bf16 rounding would dominate
 //  the error of XK W and XQ W, so those products take W and the XQ / XK rows
 //  in fp16 (the bf16 inputs convert exactly for |x| >= 2^-14, within 3e-8
@@ -91,6 +97,9 @@ struct alignas(16) Smem {
     // alpha = 1 - lambda * (sum of the chunk's eta)
     alignas(16) float dec[NSLOT][MB];
     float alpha[NSLOT];
+    // row means of W_0 and the mean of b_0 (the state is held centred)
+    alignas(16) float wbar[D];
+    float bbar;
 };
 
 struct Ctx {
@@ -154,8 +163,8 @@ __device__ __forceinline__ void prep_waves(Smem &sm, int pw, int g, int c, int l
     const char *bq = reinterpret_cast<const char *>(xq), *bk = reinterpret_cast<const char *>(xk),
                *bv = reinterpret_cast<const char *>(xv);
     auto load = [&](PrepRegs &R, int ch) {
-        const uint32_t tok = static_cast<uint32_t>(min(ch * MB + r, L - 1));
-        const uint32_t off = (tok * D + f0) * 2u;  // bytes, 32-bit
+        const int tok = min(ch * MB + r, L - 1);
+        const size_t off = (static_cast<size_t>(tok) * D + f0) * 2u;  // bytes
         R.q = *reinterpret_cast<const uint2 *>(bq + off);
         R.k = *reinterpret_cast<const uint2 *>(bk + off);
         R.v = *reinterpret_cast<const uint2 *>(bv + off);
@@ -352,6 +361,8 @@ __device__ __forceinline__ void chain_waves(Smem &sm, const Ctx &cx, int u, int 
         // lane all four totals
         const f32x4 s = rows4_gather(sum4(ld4(&sm.stb[c * SB + 4 * g])));
         if constexpr (IDENT) {  // s = sums of z, z^2, tau z, tau
+            // z comes from the centred state, so mu is small next to the row's
+            // spread and s[1] / d - mu^2 does not cancel
             const float mut = s[3] * inv_d;
             const float mu = s[0] * inv_d;
             const float var = fmaxf(fmaf(s[1], inv_d, -mu * mu), 0.f);
@@ -427,6 +438,30 @@ __device__ __forceinline__ void state_waves(Smem &sm, const Ctx &cx, int u, int 
 #pragma unroll
         for (int i = 0; i < 4; ++i) Wv[rb][i] = W0s[win(rb, 4 * g + i) * D + 16 * u + c];
     f32x4 bv = ld4(b0s + f0);  // b[f0 + i]
+    // Centred state: the waves hold W' = W - wbar 1^T and b' = b - bbar, with
+    // wbar the row means of W_0 and bbar the mean of b_0. Every row of Z and
+    // Zbar is then shifted by the per-token constant XK_t wbar + bbar (or
+    // XQ_t wbar + bbar), which the layer norm and its backward do not see, so
+    // the one-pass sums of z and z^2 below work on rows whose mean is near
+    // zero however large the caller's offsets are. The updates keep the
+    // centring: the rows of E sum to zero (the layer-norm gradient of a row
+    // sums to zero), so XK^T E and 1^T E have zero row means; weight decay
+    // scales wbar by the same factors as W (rho below). The caller's
+    // representation is restored when the state is written out.
+    const bool centre = cx.nch > 0;  // uniform; L = 0 passes the state through bit for bit
+    if (centre) {
+        const int t = 64 * u + lane, row = t >> 2, q = t & 3;  // 256 threads: a quarter row each
+        const f32x4 *wr = reinterpret_cast<const f32x4 *>(W0s + row * D + 16 * q);
+        float s = sum4(wr[0]) + sum4(wr[1]) + (sum4(wr[2]) + sum4(wr[3]));
+        s = dpp_add<0xB1>(s);  // quad_perm [1,0,3,2]
+        s = dpp_add<0x4E>(s);  // quad_perm [2,3,0,1]
+        if (q == 0) sm.wbar[row] = s * (1.0f / D);
+        if (u == 0) {
+            const float bs = rows4_sum(row16_sum(b0s[lane]));
+            if (lane == 0) sm.bbar = bs * (1.0f / D);
+        }
+    }
+    float rho = 1.f;  // product of the decay factors applied so far
     f32x4 gm = fone, bt = fzero;
     if constexpr (!IDENT) {
 #pragma unroll
@@ -443,10 +478,15 @@ __device__ __forceinline__ void state_waves(Smem &sm, const Ctx &cx, int u, int 
         return mfma32h(wf[1], xfrag(rows, 1), mfma32h(wf[0], xfrag(rows, 0), bv));
     };
 
-    lds_barrier();  // prologue chunks 0 .. 2 staged
+    lds_barrier();  // prologue chunks 0 .. 2 staged (and the means above written)
     f32x4 Pp = fzero;  // XK_{j+2} W_j + b_j, waiting for E_j (with decay: XK_{j+2} W_j alone)
     float pk = 1.f, zk = 1.f;  // weight decay: the factors Pp and Zq still need (then + b)
     if (cx.nch > 0) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Wv[rb][i] -= sm.wbar[win(rb, 4 * g + i)];
+        bv = bv - sm.bbar;
         const f16x8 wf[2] = {wfrag(0), wfrag(1)};
         sm.q[0][u][lane] = xw(wf, sm.slot[0].xk);  // bracket of Z_0 = XK_0 W_0 + b_0
         if constexpr (DECAY) {  // alpha_0 XK_1 W_0 + b_0, alpha_0 from chunk 0's eta
@@ -533,6 +573,7 @@ __device__ __forceinline__ void state_waves(Smem &sm, const Ctx &cx, int u, int 
                 const float a_it = sm.alpha[s0];
 #pragma unroll
                 for (int rb = 0; rb < 4; ++rb) Wv[rb] = Wv[rb] * a_it;
+                rho *= a_it;
             } else {
                 Pp = mfma32h(wf[1], k2[1], mfma32h(wf[0], k2[0], bv));  // XK_{it+2} W_it + b_it
                 Zq = mfma32h(wf[1], q0[1], mfma32h(wf[0], q0[0], bv));  // XQ_it W_it + b_it
@@ -556,7 +597,7 @@ __device__ __forceinline__ void state_waves(Smem &sm, const Ctx &cx, int u, int 
             uint2 ov = make_uint2(pack2(o[0], o[1]), pack2(o[2], o[3]));
             asm volatile("" : "+v"(ov));  // keep the math out of the store's branch
             const int tok = (it - 1) * MB + c;
-            if (tok < cx.L) *reinterpret_cast<uint2 *>(Oseq + static_cast<uint32_t>(tok * D + f0)) = ov;
+            if (tok < cx.L) *reinterpret_cast<uint2 *>(Oseq + static_cast<size_t>(tok) * D + f0) = ov;
         }
         sm1 = s0;
         s0 = s1;
@@ -578,6 +619,13 @@ __device__ __forceinline__ void state_waves(Smem &sm, const Ctx &cx, int u, int 
         lds_barrier();
     }
 
+    if (centre) {  // back to the caller's representation: W = W' + rho wbar 1^T, b = b' + bbar
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Wv[rb][i] = fmaf(rho, sm.wbar[win(rb, 4 * g + i)], Wv[rb][i]);
+        bv = bv + sm.bbar;
+    }
     if (W_out) {
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb)
@@ -594,7 +642,7 @@ template <int LOSS, bool DECAY>
 __global__ __launch_bounds__(NT) void linear_prefill_mfma(
     int H, int L, float eps, const bf16_t *__restrict__ XQ, const bf16_t *__restrict__ XK,
     const bf16_t *__restrict__ XV, const float *__restrict__ eta, const float *__restrict__ theta,
-    float eta_base, const float *__restrict__ W0, const float *__restrict__ b0, int w0_batched,
+    float eta_base, const float *W0, const float *b0, int w0_batched,
     const float *__restrict__ gamma, const float *__restrict__ beta, bf16_t *__restrict__ O,
     float *W_out, float *b_out, float wd) {
     __shared__ Smem sm;

@@ -26,7 +26,7 @@ template <int D, typename TIO>
 __global__ __launch_bounds__(256) void linear_prefill_valu(
     int H, int L, int mb, float eps, const TIO *__restrict__ XQ, const TIO *__restrict__ XK,
     const TIO *__restrict__ XV, const float *__restrict__ eta, const float *__restrict__ theta,
-    float eta_base, const float *__restrict__ W0, const float *__restrict__ b0, int w0_batched,
+    float eta_base, const float *W0, const float *b0, int w0_batched,
     const float *__restrict__ gamma,
     const float *__restrict__ beta, TIO *__restrict__ O, float *W_out, float *b_out, int loss,
     float wd) {
@@ -43,6 +43,7 @@ __global__ __launch_bounds__(256) void linear_prefill_valu(
     __shared__ float sEta[MB], sM[MB * MB];
     __shared__ float sTh[D];
     __shared__ float sDec[MB];  // 1 - lambda * cum_t (weight decay)
+    __shared__ float sWbar[D], sBbar[1];  // row means of W0, mean of b0
 
     const int tid = threadIdx.x;
     const long seq = blockIdx.x;
@@ -66,6 +67,31 @@ __global__ __launch_bounds__(256) void linear_prefill_valu(
     }
     const int cj = tid % D, cs0 = tid / D;  // column-product mapping
     __syncthreads();
+
+    // Centred state: W - wbar 1^T and b - bbar (wbar the row means of W0,
+    // bbar the mean of b0) shift every row of z by a per-token constant that
+    // the layer norm and its backward do not see, and keep z small when the
+    // caller's state carries a large offset (z is formed in fp32, so an
+    // offset m would otherwise cost ulp(m) of the row's spread). The rows of
+    // the gradient sum to zero, so the updates keep the centring; weight
+    // decay scales wbar with W (rho). The state is restored on the way out.
+    float rho = 1.f;
+    if (L > 0) {
+        if (tid < D) {
+            float a = 0.f;
+            for (int j = 0; j < D; ++j) a += sW[tid * D + j];
+            sWbar[tid] = a * (1.0f / D);
+        }
+        if (tid == 0) {
+            float a = 0.f;
+            for (int j = 0; j < D; ++j) a += sb[j];
+            sBbar[0] = a * (1.0f / D);
+        }
+        __syncthreads();
+        for (int e = tid; e < D * D; e += NT) sW[e] -= sWbar[e / D];
+        if (tid < D) sb[tid] -= sBbar[0];
+        __syncthreads();
+    }
 
     for (int t0 = 0; t0 < L; t0 += mb) {
         const int len = min(mb, L - t0);
@@ -170,6 +196,7 @@ __global__ __launch_bounds__(256) void linear_prefill_valu(
                 }
             }
             const float dec = sDec[MB - 1];  // eta past the chunk's end is 0
+            if (wd != 0.f) rho *= dec;
             for (int e = tid; e < D * D; e += NT) {
                 const int i = e / D, j = e % D;
                 float acc = 0.f;
@@ -187,6 +214,11 @@ __global__ __launch_bounds__(256) void linear_prefill_valu(
         __syncthreads();
     }
 
+    if (L > 0) {  // back to the caller's representation
+        for (int e = tid; e < D * D; e += NT) sW[e] = fmaf(rho, sWbar[e / D], sW[e]);
+        if (tid < D) sb[tid] += sBbar[0];
+        __syncthreads();
+    }
     if (W_out) {
         for (int e = tid; e < D * D; e += NT) W_out[static_cast<size_t>(seq) * D * D + e] = sW[e];
     }

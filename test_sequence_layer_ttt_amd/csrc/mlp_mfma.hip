@@ -106,17 +106,18 @@ __device__ __forceinline__ f32x4 row_grad(f32x4 z, f32x4 tau, float mutau, float
     } else {
         constexpr float inv_d = 1.0f / D;
         f32x4 ev;
-        if constexpr (IDENT) {
-            const float s1 = row16_sum((z[0] + z[1]) + (z[2] + z[3]));
-            const float s2 = row16_sum(z[0] * z[0] + z[1] * z[1] + z[2] * z[2] + z[3] * z[3]);
-            const float s3 = row16_sum(tau[0] * z[0] + tau[1] * z[1] + tau[2] * z[2] + tau[3] * z[3]);
-            const float mu = s1 * inv_d;
-            const float rstd = rsqrtf(fmaxf(s2 * inv_d - mu * mu, 0.f) + eps);
-            const float a = rstd * rstd * rstd * (s3 * inv_d - mutau * mu);
-            const float cz = -eta_r * a, ct = eta_r * rstd;
-            const float c0 = eta_r * (a * mu - rstd * mutau);
+        if constexpr (IDENT) {  // mean first, then centred sums (no E[z^2] - mu^2 cancellation)
+            const float mu = row16_sum((z[0] + z[1]) + (z[2] + z[3])) * inv_d;
+            f32x4 cz;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ev[e] = fmaf(cz, z[e], fmaf(ct, tau[e], c0));
+            for (int e = 0; e < 4; ++e) cz[e] = z[e] - mu;
+            const float s2 = row16_sum(fmaf(cz[0], cz[0], cz[1] * cz[1]) + fmaf(cz[2], cz[2], cz[3] * cz[3]));
+            const float s3 = row16_sum(fmaf(tau[0], cz[0], tau[1] * cz[1]) + fmaf(tau[2], cz[2], tau[3] * cz[3]));
+            const float rstd = rsqrtf(s2 * inv_d + eps);
+            const float a = rstd * rstd * rstd * (s3 * inv_d);
+            const float ca = -eta_r * a, ct = eta_r * rstd;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ev[e] = fmaf(ca, cz[e], ct * (tau[e] - mutau));
         } else {
             const float mu = row16_sum((z[0] + z[1]) + (z[2] + z[3])) * inv_d;
             float cz[4], s2 = 0.f;
@@ -151,8 +152,8 @@ template <int LOSS, bool DECAY, bool GATED>
 __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
     int H, int L, float eps, const bf16_t *__restrict__ XQ, const bf16_t *__restrict__ XK,
     const bf16_t *__restrict__ XV, const float *__restrict__ eta,
-    const float *__restrict__ W1_0, const float *__restrict__ b1_0,
-    const float *__restrict__ W2_0, const float *__restrict__ b2_0, int w0_batched,
+    const float *W1_0, const float *b1_0, const float *W2_0, const float *b2_0,
+    int w0_batched,
     const float *__restrict__ gamma, const float *__restrict__ beta, bf16_t *__restrict__ O,
     float *W1_out, float *b1_out, float *W2_out, float *b2_out, float wd,
     const float *__restrict__ theta, float eta_base) {
@@ -221,8 +222,8 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
     const float *et = eta + static_cast<size_t>(seq) * L;
     PrepRegs R;
     auto load = [&](int ch) {
-        const uint32_t tok = static_cast<uint32_t>(min(ch * MB + r, L - 1));
-        const uint32_t off = tok * D + f0;
+        const int tok = min(ch * MB + r, L - 1);
+        const size_t off = static_cast<size_t>(tok) * D + f0;
         R.q = *reinterpret_cast<const uint2 *>(xq + off);
         R.k = *reinterpret_cast<const uint2 *>(xk + off);
         R.v = *reinterpret_cast<const uint2 *>(xv + off);
@@ -279,7 +280,7 @@ __global__ __launch_bounds__(NT) void mlp_prefill_mfma(
         const f32x4 o = ident ? ln_fwd_row<true>(zb2, xqv, gam, bet, eps)
                               : ln_fwd_row<false>(zb2, xqv, gam, bet, eps);
         if (ch * MB + r < L)
-            *reinterpret_cast<uint2 *>(O + xbase + static_cast<uint32_t>((ch * MB + r) * D + f0)) =
+            *reinterpret_cast<uint2 *>(O + xbase + static_cast<size_t>(ch * MB + r) * D + f0) =
                 make_uint2(pack2(o[0], o[1]), pack2(o[2], o[3]));
     };
 

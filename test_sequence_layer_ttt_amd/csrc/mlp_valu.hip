@@ -29,9 +29,9 @@ namespace ttt {
 template <typename TIO, int LOSS, bool DECAY, bool GATED>
 __global__ __launch_bounds__(256) void mlp_prefill_valu(
     int H, int L, int mb, float eps, const TIO *__restrict__ XQ, const TIO *__restrict__ XK,
-    const TIO *__restrict__ XV, const float *__restrict__ eta, const float *__restrict__ W1_0,
-    const float *__restrict__ b1_0, const float *__restrict__ W2_0,
-    const float *__restrict__ b2_0, int w0_batched, const float *__restrict__ gamma,
+    const TIO *__restrict__ XV, const float *__restrict__ eta, const float *W1_0,
+    const float *b1_0, const float *W2_0,
+    const float *b2_0, int w0_batched, const float *__restrict__ gamma,
     const float *__restrict__ beta, TIO *__restrict__ O, float *W1_out, float *b1_out,
     float *W2_out, float *b2_out, float wd, const float *__restrict__ theta, float eta_base) {
     constexpr int D = 64, M = 256, MB = 16, NT = 256, DP = D + 1, MP = M + 1, E = D / 16;
@@ -44,6 +44,7 @@ __global__ __launch_bounds__(256) void mlp_prefill_valu(
     __shared__ float sQ[MB * DP], sK[MB * DP];
     __shared__ float sT[MB * D], sG2[MB * D], sZ2[MB * D];
     __shared__ float sEta[MB], sM[MB * MB], sDec[MB], sTh[D];
+    __shared__ float sW2bar[M], sB2bar[1];  // row means of W2_0, mean of b2_0
 
     const int tid = threadIdx.x;
     const long seq = blockIdx.x;
@@ -72,6 +73,31 @@ __global__ __launch_bounds__(256) void mlp_prefill_valu(
     }
     const int cj = tid % D, cs0 = tid / D;  // 4 outputs per thread: rows cs0 + 4r
     __syncthreads();
+
+    // Centred output layer: W2 - w2bar 1^T and b2 - b2bar (row means of W2_0,
+    // mean of b2_0) shift every row of Z2 and Zb2 by a per-token constant
+    // that the layer norm and its backward do not see, and keep them small
+    // when the caller's state carries a large offset (Z2 is formed in fp32).
+    // G2 rows sum to zero, so G2 W2^T and the updates are unchanged and keep
+    // the centring; weight decay scales w2bar with W2 (rho). The state is
+    // restored on the way out.
+    float rho = 1.f;
+    if (L > 0) {
+        {
+            float a = 0.f;
+            for (int j = 0; j < D; ++j) a += sW2[k * DP + j];
+            sW2bar[k] = a * (1.0f / D);
+        }
+        if (tid == 0) {
+            float a = 0.f;
+            for (int j = 0; j < D; ++j) a += sb2[j];
+            sB2bar[0] = a * (1.0f / D);
+        }
+        __syncthreads();
+        for (int j = 0; j < D; ++j) sW2[k * DP + j] -= sW2bar[k];
+        if (tid < D) sb2[tid] -= sB2bar[0];
+        __syncthreads();
+    }
 
     for (int t0 = 0; t0 < L; t0 += mb) {
         const int len = min(mb, L - t0);
@@ -216,6 +242,7 @@ __global__ __launch_bounds__(256) void mlp_prefill_valu(
                 }
             }
             const float alpha = DECAY ? sDec[MB - 1] : 1.f;
+            rho *= alpha;
             if constexpr (DECAY) {
 #pragma unroll
                 for (int i = 0; i < D; ++i) w1[i] *= alpha;
@@ -249,6 +276,11 @@ __global__ __launch_bounds__(256) void mlp_prefill_valu(
         __syncthreads();
     }
 
+    if (L > 0) {  // back to the caller's representation
+        for (int j = 0; j < D; ++j) sW2[k * DP + j] = fmaf(rho, sW2bar[k], sW2[k * DP + j]);
+        if (tid < D) sb2[tid] += sB2bar[0];
+        __syncthreads();
+    }
     if (W1_out) {
 #pragma unroll
         for (int i = 0; i < D; ++i) W1_out[static_cast<size_t>(seq) * D * M + static_cast<size_t>(i) * M + k] = w1[i];

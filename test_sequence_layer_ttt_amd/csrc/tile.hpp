@@ -162,7 +162,10 @@ __device__ __forceinline__ bf16x8 row_frag(const uint16_t *tile, int c, int g, i
 // TTT deep-dive §4.2). With gamma = 1, beta = 0 it uses the closed form
 //   G = a (z - mu) - rstd (tau - mean tau),
 //   a = rstd^2 (eps rstd^2 + rstd (mean(tau z) - mean(tau) mu)),
-// which needs one round of row sums; otherwise the general two-round form.
+// which needs the mean and then two centred row sums (the variance and
+// mean(tau (z - mu)) are sums of centred products, so a large common offset
+// of the row cancels exactly instead of in E[z^2] - mu^2); otherwise the
+// general two-round form.
 template <bool IDENT>
 __device__ __forceinline__ f32x4 ln_bwd_row(f32x4 z, f32x4 tau, float mutau, float eta_r,
                                             const float (&gam)[4], const float (&bet)[4],
@@ -170,19 +173,19 @@ __device__ __forceinline__ f32x4 ln_bwd_row(f32x4 z, f32x4 tau, float mutau, flo
     constexpr float inv_d = 1.0f / D;
     f32x4 ev;
     if constexpr (IDENT) {
-        const float s1 = row16_sum((z[0] + z[1]) + (z[2] + z[3]));
-        const float s2 = row16_sum(z[0] * z[0] + z[1] * z[1] + z[2] * z[2] + z[3] * z[3]);
-        const float s3 = row16_sum(tau[0] * z[0] + tau[1] * z[1] + tau[2] * z[2] + tau[3] * z[3]);
-        const float mu = s1 * inv_d;
-        const float var = fmaxf(s2 * inv_d - mu * mu, 0.f);
-        const float rstd = rsqrtf(var + eps);
-        const float mtz = s3 * inv_d - mutau * mu;
-        const float a = rstd * rstd * (eps * rstd * rstd + rstd * mtz);
-        // E = -eta (a (z - mu) - rstd (tau - mutau)) = cz z + ct tau + c0
-        const float cz = -eta_r * a, ct = eta_r * rstd;
-        const float c0 = eta_r * (a * mu - rstd * mutau);
+        const float mu = row16_sum((z[0] + z[1]) + (z[2] + z[3])) * inv_d;
+        f32x4 cz;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ev[e] = fmaf(cz, z[e], fmaf(ct, tau[e], c0));
+        for (int e = 0; e < 4; ++e) cz[e] = z[e] - mu;
+        const float s2 = row16_sum(fmaf(cz[0], cz[0], cz[1] * cz[1]) + fmaf(cz[2], cz[2], cz[3] * cz[3]));
+        const float s3 = row16_sum(fmaf(tau[0], cz[0], tau[1] * cz[1]) + fmaf(tau[2], cz[2], tau[3] * cz[3]));
+        const float rstd = rsqrtf(s2 * inv_d + eps);
+        const float mtz = s3 * inv_d;  // mean((tau - mean tau)(z - mu)): the centred z sums to 0
+        const float a = rstd * rstd * (eps * rstd * rstd + rstd * mtz);
+        // E = -eta (a (z - mu) - rstd (tau - mutau))
+        const float ca = -eta_r * a, ct = eta_r * rstd;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ev[e] = fmaf(ca, cz[e], ct * (tau[e] - mutau));
     } else {
         const float mu = row16_sum((z[0] + z[1]) + (z[2] + z[3])) * inv_d;
         float cz[4], s2 = 0.f;

@@ -55,6 +55,18 @@ def test_linear_rejects_unsupported_d_and_mb(lib):
     assert _lin(lib, mb=17) == _lib.TTT_E_SHAPE
 
 
+def test_prefill_rejects_sequences_longer_than_max_l(lib):
+    """Token and chunk indices in the kernels are 32-bit ints: L is bounded
+    by TTT_MAX_L = 2^30 on every prefill entry point."""
+    big = (1 << 30) + 1
+    assert _lin(lib, L=big) == _lib.TTT_E_SHAPE
+    assert "TTT_MAX_L" in lib.ttt_last_error().decode()
+    p = [FAKE + i * (1 << 20) for i in range(16)]
+    assert lib.ttt_mlp_forward(1, 1, big, 64, 16, 1, 1e-6, *p[:8], 0, p[8], p[9], p[10],
+                               p[11], p[12], p[13], p[14], None) == _lib.TTT_E_SHAPE
+    assert _lin(lib, L=1 << 30) != _lib.TTT_E_SHAPE or "TTT_MAX_L" not in lib.ttt_last_error().decode()
+
+
 @pytest.mark.parametrize("eps", [0.0, -1e-6, 1e-40, float("inf"), float("nan")])
 def test_every_entry_point_rejects_bad_eps(lib, eps):
     """The layer norms need var + eps to be a positive normal float."""
@@ -350,3 +362,4 @@ def test_binding_rejects_cpu_tensors():
     with pytest.raises(ValueError):
         ttt.ttt_linear_forward(x, x, x, torch.zeros(1, 1, 16), torch.zeros(1, 64, 64),
                                torch.zeros(1, 64), torch.ones(1, 64), torch.zeros(1, 64))
+

@@ -30,6 +30,8 @@ def test_bench_prints_one_line_with_the_contract_fields():
     roof = j["roofline"]
     assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-12
-    assert roof["traffic"] is not None and roof["traffic"] > 0
+    # counter bytes are reported only while the kernel's sources match the
+    # ones the stored FETCH_SIZE / WRITE_SIZE runs measured (else null)
+    assert roof["traffic"] is None or roof["traffic"] > 0
     cb = j["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0 and cb["sample"]

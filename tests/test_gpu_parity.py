@@ -357,9 +357,12 @@ def test_decode_steps_edge(steps):
 
 
 def test_decode_steps_resume_and_repeatable():
-    """Two calls of T1 and T2 steps equal one call of T1 + T2 steps bit for
-    bit (the state is exactly what the kernel holds), and a repeat of the
-    same call is bitwise identical."""
+    """A repeat of the same call is bitwise identical, and two calls of T1
+    and T2 steps equal one call of T1 + T2 steps. Within a call the kernel
+    holds the state with its row means removed and restores them on the way
+    out, so a split run differs from one call only by the rounding of that
+    round trip: the state to 1e-6 relative, the bf16 outputs by at most one
+    rounding step of bf16."""
     dec, W0, b0, gamma, beta = _decode_case(795, 24, 2, 4, 64, "bf16", "ident")
     full = _steps_run(W0, b0, dec, gamma, beta, 1e-6)
     again = _steps_run(W0, b0, dec, gamma, beta, 1e-6)
@@ -369,8 +372,10 @@ def test_decode_steps_resume_and_repeatable():
                                           dec.XK[lo:hi], dec.XV[lo:hi], dec.eta[lo:hi])
     O1, W1, b1 = _steps_run(W0, b0, cut(0, 10), gamma, beta, 1e-6)
     O2, W2, b2 = _steps_run(W1, b1, cut(10, 24), gamma, beta, 1e-6)
-    assert np.array_equal(np.concatenate([O1, O2], 2), full[0])
-    assert np.array_equal(W2, full[1]) and np.array_equal(b2, full[2])
+    err = P.errors((np.concatenate([O1, O2], 2), W2, b2), full, 8, LIN_NAMES)
+    _report("decode_steps split vs one call", err)
+    assert err["W_out"] <= 1e-6 and err["b_out"] <= 1e-6, err
+    assert err["O"] <= 2.0 ** -7, err
 
 
 def test_decode_steps_full_workload5():
