@@ -275,6 +275,35 @@ int ttt_linear_backward(int B, int H, int L, int d, int mb, int io, float ln_eps
 int ttt_linear_backward_workspace(int B, int H, int L, int d, int mb, size_t *bytes);
 
 /*
+ * ttt_linear_backward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving or training loops, harnesses that
+ * forbid hipMalloc. Same arguments, results and kernel as
+ * ttt_linear_backward, minus the workspace: the chunk-start checkpoints go to
+ * a fixed device array inside the library, TTT_BACKWARD_SCRATCH_BYTES
+ * (64 MiB) on every GPU the library runs on, held until the process ends.
+ *   - B*H*ceil(L/mb)*(d*d+d)*4 (ttt_linear_backward_workspace) must not
+ *     exceed TTT_BACKWARD_SCRATCH_BYTES, else TTT_E_SHAPE before any HIP
+ *     call (d = 64: at most 4032 chunk states B*H*ceil(L/mb), e.g. B*H = 8 at L = 8064 with mb = 16).
+ *   - Calls no hipMalloc, hipFree or allocating library routine. The first
+ *     call on a device looks up the array's device address once
+ *     (hipGetSymbolAddress with that device current).
+ *   - `stream` must belong to the current device (else TTT_E_HIP).
+ *   - Every call on one GPU shares that GPU's array and it keeps the last
+ *     call's contents; a call reads only checkpoints it wrote itself, so
+ *     nothing needs clearing. Calls that overlap in time on one GPU (other
+ *     streams, other host threads) race on the array and give wrong
+ *     gradients: order them, e.g. on one stream.
+ */
+#define TTT_BACKWARD_SCRATCH_BYTES ((size_t)64 << 20)
+int ttt_linear_backward_noalloc(int B, int H, int L, int d, int mb, int io, float ln_eps,
+                                const void *XQ, const void *XK, const void *XV,
+                                const float *eta, const float *W0, const float *b0,
+                                int w0_batched, const float *ln_gamma, const float *ln_beta,
+                                const float *dO, const float *dW_out, const float *db_out,
+                                float *dXQ, float *dXK, float *dXV, float *deta, float *dW0,
+                                float *db0, float *dgamma, float *dbeta, hipStream_t stream);
+
+/*
  * One single-token TTT-Linear step (b = 1, primal form) for B x H independent
  * states held in place -- the fast-weight cache of [D] §5.2:
  *   G = lnbwd(xk W + b, xv - xk);  W <- W - eta xk^T G;  b <- b - eta G;

@@ -80,6 +80,10 @@ hipError_t launch_eta_gate_backward(int B, int H, int L, int d, int io, const vo
                                     float *dXK, float *dtheta, hipStream_t stream);
 
 size_t linear_backward_workspace_floats(int B, int H, int L, int d, int mb);
+// the fixed device scratch of ttt_linear_backward_noalloc: its size, and its
+// address on the current device
+size_t linear_backward_scratch_bytes();
+hipError_t linear_backward_scratch(float **ptr);
 hipError_t launch_linear_backward(const LinearBwdArgs &a, hipStream_t stream);
 hipError_t launch_mlp(const MLPArgs &a, hipStream_t stream);
 bool mlp_mfma_supported(const MLPArgs &a);

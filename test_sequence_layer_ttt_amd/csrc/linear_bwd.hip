@@ -37,7 +37,10 @@
 // result, and tiles (rb, u) of each [d x d] state update, reading its
 // operands from LDS tiles whose rows are padded to d + 1 floats.
 #include "common.hpp"
+#include <mutex>
+
 #include "launch.hpp"
+#include "ttt.h"
 #include "tile.hpp"
 
 namespace ttt {
@@ -490,6 +493,38 @@ hipError_t launch_bwd_t(const LinearBwdArgs &a, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Fixed scratch of ttt_linear_backward_noalloc: the chunk-start checkpoints
+// live here instead of in a caller workspace (64 MiB, held by every GPU the
+// library runs on until the process ends). Host code must never pass the
+// array's name to a kernel: on the host it is only a stand-in for the symbol;
+// linear_backward_scratch below returns the device address.
+constexpr size_t kScratchBytes = TTT_BACKWARD_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+size_t linear_backward_scratch_bytes() { return kScratchBytes; }
+
+// Device address of `scratch` on the current device, looked up once per
+// device (hipGetSymbolAddress with that device current) and kept.
+hipError_t linear_backward_scratch(float **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static float *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = static_cast<float *>(p);
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 size_t linear_backward_workspace_floats(int B, int H, int L, int d, int mb) {
     const size_t nch = L > 0 ? static_cast<size_t>((L + mb - 1) / mb) : 0;

@@ -233,6 +233,47 @@ def ttt_linear_backward(XQ, XK, XV, eta, W0, b0, ln_gamma, ln_beta, dO, dW_out=N
     return g
 
 
+def ttt_linear_backward_noalloc(XQ, XK, XV, eta, W0, b0, ln_gamma, ln_beta, dO, dW_out=None,
+                                db_out=None, mb: int = 16, ln_eps: float = 1e-6,
+                                grads=None, stream=None) -> dict:
+    """ttt_linear_backward without a workspace: the checkpoints go to the
+    library's fixed device scratch (TTT_BACKWARD_SCRATCH_BYTES per GPU), and
+    the library allocates nothing. `grads` may hold preallocated outputs
+    (a dict like the one returned), so the call itself allocates nothing on
+    the Python side either; calls that overlap on one GPU race."""
+    B, H, L, d = XQ.shape
+    io = _IO.get(XQ.dtype)
+    if io is None:
+        raise TypeError(f"XQ dtype {XQ.dtype} not supported")
+    batched = W0.dim() == 4
+    for t, n in ((XQ, "XQ"), (XK, "XK"), (XV, "XV")):
+        _need(t, n, (B, H, L, d), XQ.dtype)
+    _need(eta, "eta", (B, H, L), torch.float32)
+    _need(W0, "W0", ((B,) if batched else ()) + (H, d, d), torch.float32)
+    _need(b0, "b0", ((B,) if batched else ()) + (H, d), torch.float32)
+    _need(ln_gamma, "ln_gamma", (H, d), torch.float32)
+    _need(ln_beta, "ln_beta", (H, d), torch.float32)
+    _need(dO, "dO", (B, H, L, d), torch.float32)
+    if dW_out is not None:
+        _need(dW_out, "dW_out", (B, H, d, d), torch.float32)
+    if db_out is not None:
+        _need(db_out, "db_out", (B, H, d), torch.float32)
+    shapes = {"dXQ": (B, H, L, d), "dXK": (B, H, L, d), "dXV": (B, H, L, d), "deta": (B, H, L),
+              "dW0": (B, H, d, d), "db0": (B, H, d), "dgamma": (B, H, d), "dbeta": (B, H, d)}
+    if grads is None:
+        grads = {k: torch.empty(v, device=XQ.device, dtype=torch.float32) for k, v in shapes.items()}
+    for k, v in shapes.items():
+        _need(grads[k], k, v, torch.float32)
+    g = grads
+    lib = _lib.load()
+    _lib.check(lib.ttt_linear_backward_noalloc(
+        B, H, L, d, mb, io, ln_eps, _ptr(XQ), _ptr(XK), _ptr(XV), _ptr(eta), _ptr(W0), _ptr(b0),
+        int(batched), _ptr(ln_gamma), _ptr(ln_beta), _ptr(dO), _ptr(dW_out), _ptr(db_out),
+        _ptr(g["dXQ"]), _ptr(g["dXK"]), _ptr(g["dXV"]), _ptr(g["deta"]), _ptr(g["dW0"]),
+        _ptr(g["db0"]), _ptr(g["dgamma"]), _ptr(g["dbeta"]), _stream(stream)))
+    return g
+
+
 def ttt_mlp_forward(XQ, XK, XV, eta, W1, b1, W2, b2, ln_gamma, ln_beta, O=None, outs=None,
                     mb: int = 16, ln_eps: float = 1e-6, stream=None):
     """TTT-MLP prefill (d = 64, hidden 4d). W1 [.,H,d,4d], b1 [.,H,4d],

@@ -22,7 +22,7 @@ def test_exports_every_declared_symbol(lib):
                           "ttt_decode_steps", "ttt_linear_backward",
                           "ttt_linear_backward_workspace", "ttt_ln_l2_bwd", "ttt_last_error",
                           "ttt_version", "ttt_linear_forward_gated", "ttt_eta_gate",
-                          "ttt_eta_gate_backward"}
+                          "ttt_eta_gate_backward", "ttt_linear_backward_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
@@ -363,3 +363,15 @@ def test_binding_rejects_cpu_tensors():
         ttt.ttt_linear_forward(x, x, x, torch.zeros(1, 1, 16), torch.zeros(1, 64, 64),
                                torch.zeros(1, 64), torch.ones(1, 64), torch.zeros(1, 64))
 
+
+def test_backward_noalloc_rejects_inputs_beyond_its_scratch(lib):
+    """The no-allocation backward refuses, before any HIP call, inputs whose
+    checkpoints exceed its fixed 64 MiB scratch (4032 d = 64 chunk states)."""
+    p = [FAKE + i * (1 << 24) for i in range(24)]
+
+    def call(B, H, L):
+        return lib.ttt_linear_backward_noalloc(B, H, L, 64, 16, 1, 1e-6, *p[:6], 0, *p[6:19], None)
+    assert call(8, 1, 16 * 4033) == _lib.TTT_E_SHAPE
+    msg = lib.ttt_last_error().decode()
+    assert "scratch" in msg and str(64 << 20) in msg
+    assert call(1, 1, -1) == _lib.TTT_E_SHAPE
