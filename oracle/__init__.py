@@ -62,6 +62,8 @@ def _load():
                                      ctypes.c_double, _D]
     lib.oracle_ln_l2_bwd.restype = None
     lib.oracle_ln_fwd.argtypes = [ctypes.c_int, ctypes.c_int, _D, _D, _D, ctypes.c_double, _D]
+    lib.oracle_qkv_project.argtypes = [ctypes.c_int] * 5 + [_D] * 5
+    lib.oracle_qkv_project_at.argtypes = [ctypes.c_int] * 5 + [_D, _D, ctypes.c_int, _I, _D]
     lib.oracle_ln_fwd.restype = None
     lib.oracle_version.restype = ctypes.c_int
     _lib = lib
@@ -262,3 +264,36 @@ def linear_forward_gated(XQ, XK, XV, theta_lr, eta_base: float, W0, b0, gamma, b
     """TTT-Linear with eta from the gate (eta_gate), then linear_forward."""
     return linear_forward(XQ, XK, XV, eta_gate(XK, theta_lr, eta_base), W0, b0, gamma,
                           beta, eps, mb=mb, **kw)
+
+
+def qkv_project(X, theta, H: int):
+    """Key, value and query views of the layer input ([Y] §2.2 projections
+    theta_Q, theta_K, theta_V; [D] §4.2 inputs XQ, XK, XV): with theta
+    [3, H*d, d_model] stored output-major, XQ[b,h,t,j] = sum_k X[b,t,k]
+    theta[0][h*d+j][k] (XK: theta[1], XV: theta[2]). X [B,L,d_model].
+    Returns (XQ, XK, XV), each [B,H,L,d] in float64."""
+    X, th = _f64(X), _f64(theta)
+    B, L, dm = X.shape
+    if th.shape[0] != 3 or th.shape[2] != dm or th.shape[1] % H:
+        raise ValueError("theta must be [3, H*d, d_model]")
+    d = th.shape[1] // H
+    outs = [np.empty((B, H, L, d)) for _ in range(3)]
+    st = _load().oracle_qkv_project(B, L, dm, H, d, _p(X), _p(th), *(_p(o) for o in outs))
+    if st:
+        raise ValueError(f"oracle_qkv_project: error {st}")
+    return tuple(outs)
+
+
+def qkv_project_at(X, theta, H: int, idx) -> np.ndarray:
+    """qkv_project at chosen outputs only: idx [n,5] rows (view, b, h, t, j)
+    with view 0 = XQ, 1 = XK, 2 = XV. Returns the n values in float64."""
+    X, th = _f64(X), _f64(theta)
+    B, L, dm = X.shape
+    d = th.shape[1] // H
+    idx = np.ascontiguousarray(np.asarray(idx, dtype=np.int32).reshape(-1, 5))
+    out = np.empty(idx.shape[0])
+    st = _load().oracle_qkv_project_at(B, L, dm, H, d, _p(X), _p(th), idx.shape[0],
+                                       idx.ctypes.data_as(_I), _p(out))
+    if st:
+        raise ValueError(f"oracle_qkv_project_at: error {st}")
+    return out

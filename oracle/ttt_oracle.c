@@ -788,3 +788,57 @@ int oracle_mlp_dual(int B, int H, int L, int d, int nchunks, const int *chunk_le
     size_t scratch = 2 * (size_t)d * m + m + d + (size_t)j.max_chunk * (3 * m + d) + m + 3 * (size_t)d;
     return run_pool(&j, mlp_dual_seq, scratch);
 }
+
+/*
+ * Input projections of the layer ([Y] §2.2: the outer loop learns the
+ * projections theta_K, theta_V, theta_Q that make the key, value and query
+ * views of each token; [D] §4.2 feeds those views, XK, XV, XQ, to the inner
+ * loop). Reading taken where the pages are silent: each view is a linear map
+ * of the layer input x_t (width d_model) to H heads of width d, with the
+ * weight stored output-major like a linear layer's, so that
+ *     XQ[b,h,t,j] = sum_k X[b,t,k] * theta[0][h*d + j][k]
+ *     XK[b,h,t,j] = sum_k X[b,t,k] * theta[1][h*d + j][k]
+ *     XV[b,h,t,j] = sum_k X[b,t,k] * theta[2][h*d + j][k]
+ * X : [B,L,d_model]   theta : [3, H*d, d_model]   XQ, XK, XV : [B,H,L,d]
+ * The sum runs over k in increasing order, in fp64.
+ */
+int oracle_qkv_project(int B, int L, int dm, int H, int d, const double *X,
+                       const double *theta, double *XQ, double *XK, double *XV)
+{
+    if (B < 0 || L < 0 || dm <= 0 || H < 0 || d <= 0) return ORACLE_E_ARG;
+    double *outs[3] = {XQ, XK, XV};
+    const size_t hd = (size_t)H * d;
+    for (int v = 0; v < 3; ++v)
+        for (int b = 0; b < B; ++b)
+            for (int h = 0; h < H; ++h)
+                for (int t = 0; t < L; ++t)
+                    for (int j = 0; j < d; ++j) {
+                        const double *x = X + ((size_t)b * L + t) * dm;
+                        const double *w = theta + ((size_t)v * hd + (size_t)h * d + j) * dm;
+                        double s = 0.0;
+                        for (int k = 0; k < dm; ++k) s += x[k] * w[k];
+                        outs[v][(((size_t)b * H + h) * L + t) * d + j] = s;
+                    }
+    return ORACLE_OK;
+}
+
+/* The same sums at n chosen outputs: idx[5*i .. 5*i+4] = (view, b, h, t, j),
+ * view 0 = XQ, 1 = XK, 2 = XV; out[i] receives that output. */
+int oracle_qkv_project_at(int B, int L, int dm, int H, int d, const double *X,
+                          const double *theta, int n, const int *idx, double *out)
+{
+    if (B < 0 || L < 0 || dm <= 0 || H < 0 || d <= 0 || n < 0) return ORACLE_E_ARG;
+    const size_t hd = (size_t)H * d;
+    for (int i = 0; i < n; ++i) {
+        const int v = idx[5 * i], b = idx[5 * i + 1], h = idx[5 * i + 2], t = idx[5 * i + 3],
+                  j = idx[5 * i + 4];
+        if (v < 0 || v > 2 || b < 0 || b >= B || h < 0 || h >= H || t < 0 || t >= L || j < 0 || j >= d)
+            return ORACLE_E_ARG;
+        const double *x = X + ((size_t)b * L + t) * dm;
+        const double *w = theta + ((size_t)v * hd + (size_t)h * d + j) * dm;
+        double s = 0.0;
+        for (int k = 0; k < dm; ++k) s += x[k] * w[k];
+        out[i] = s;
+    }
+    return ORACLE_OK;
+}

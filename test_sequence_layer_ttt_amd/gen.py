@@ -305,3 +305,35 @@ def make_workload(num: int, L: Optional[int] = None, B: Optional[int] = None,
 def head_tokens(num: int) -> int:
     w = WORKLOADS[num]
     return w.B * w.H * w.L
+
+
+# ----------------------------------------------------------------------------
+# Layer input and projections (the views XQ, XK, XV are made from X)
+# ----------------------------------------------------------------------------
+@dataclass
+class ProjInputs:
+    B: int
+    L: int
+    dm: int                      # model width d_model
+    H: int
+    d: int
+    X: np.ndarray                # [B, L, dm], bf16 values widened to float32
+    theta: np.ndarray            # [3, H*d, dm]: theta_Q, theta_K, theta_V (output-major)
+
+
+def make_proj(seed: int, B: int, L: int, dm: int, H: int, d: int) -> ProjInputs:
+    """Layer input X ~ N(0, 1) and the three projections theta ~ N(0, 0.02^2)
+    (the initialisation scale of the damodev deep-dive, section 4.3, stands in
+    for trained outer-loop weights), both rounded to bfloat16. Draw order: X,
+    then theta_Q, theta_K, theta_V."""
+    rng = np.random.default_rng(seed)
+    X = round_bf16(_normal_f32(rng, (B, L, dm)))
+    theta = round_bf16(_normal_f32(rng, (3, H * d, dm), 0.02))
+    return ProjInputs(B, L, dm, H, d, X, theta)
+
+
+def make_proj_workload(num: int, L: Optional[int] = None, B: Optional[int] = None) -> ProjInputs:
+    """Projection inputs at a Linear workload's shape: model width H*d (the
+    configs name it: 768 for workload 2, 2048 for workload 3). Seed 100 + num."""
+    w = WORKLOADS[num]
+    return make_proj(100 + num, w.B if B is None else B, w.L if L is None else L, w.H * w.d, w.H, w.d)
