@@ -179,6 +179,25 @@ int ttt_eta_gate_backward(int B, int H, int L, int d, int io, const void *XK,
                           float *dtheta, hipStream_t stream);
 
 /*
+ * Input projections of the layer: the query, key and value views of the
+ * layer input ([Y] §2.2: the outer loop learns theta_Q, theta_K, theta_V;
+ * [D] §4.2 feeds the views XQ, XK, XV to the inner loop). With the weights
+ * stored output-major, like a linear layer's,
+ *   XQ[b,h,t,j] = sum_k X[b,t,k] theta[0][h*d + j][k]   (XK: theta[1], XV: theta[2]),
+ * written in the [B,H,L,d] layout every prefill entry point reads.
+ *   B, L, H >= 0; d = 64; d_model a positive multiple of 64; B*L and 3*H*d
+ *   at most INT_MAX, else TTT_E_SHAPE.
+ *   X [B,L,d_model] bf16 and theta [3,H*d,d_model] bf16, 16-byte aligned,
+ *   read only. XQ, XK, XV [B,H,L,d] bf16, 16-byte aligned, written; none may
+ *   overlap another argument (TTT_E_ALIAS).
+ *   Arithmetic: bf16 products, fp32 accumulation, outputs rounded to bf16
+ *   (nearest even). Empty outputs (B, L or H = 0): nothing is read or launched.
+ * The per-token rates then come from ttt_eta_gate on XK.
+ */
+int ttt_qkv_project(int B, int L, int d_model, int H, int d, const void *X, const void *theta, void *XQ,
+                    void *XK, void *XV, hipStream_t stream);
+
+/*
  * TTT-MLP prefill ([Y] §2.1: f_res(x) = GELU(x W1 + b1) W2 + b2, hidden m = 4d,
  * exact GELU x * Phi(x)), mini-batch form as above.
  *   d = 64 (m = 256); 1 <= mb <= 16.

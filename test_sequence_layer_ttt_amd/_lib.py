@@ -51,6 +51,7 @@ def load():
     lib.ttt_linear_forward_opts.argtypes = ([_i] * 6 + [_f] + [_P] * 6 + [_i] + [_P] * 2
                                             + [_i, _f] + [_P] * 3 + [_P])
     lib.ttt_eta_gate.argtypes = [_i] * 5 + [_P, _P, _f, _P, _P]
+    lib.ttt_qkv_project.argtypes = [_i] * 5 + [_P] * 5 + [_P]
     lib.ttt_eta_gate_backward.argtypes = [_i] * 5 + [_P, _P, _f, _P, _P, _P, _P]
     lib.ttt_mlp_forward.argtypes = [_i] * 6 + [_f] + [_P] * 8 + [_i] + [_P] * 7 + [_P]
     lib.ttt_mlp_forward_opts.argtypes = ([_i] * 6 + [_f] + [_P] * 8 + [_i] + [_P] * 2
@@ -71,7 +72,7 @@ def load():
     for name in ("ttt_linear_forward", "ttt_mlp_forward", "ttt_decode_step", "ttt_decode_steps",
                  "ttt_linear_backward", "ttt_linear_backward_workspace", "ttt_ln_l2_bwd",
                  "ttt_linear_backward_noalloc",
-                 "ttt_linear_forward_gated", "ttt_eta_gate", "ttt_eta_gate_backward",
+                 "ttt_linear_forward_gated", "ttt_eta_gate", "ttt_eta_gate_backward", "ttt_qkv_project",
                  "ttt_linear_forward_opts", "ttt_decode_steps_mb", "ttt_mlp_forward_opts",
                  "ttt_mlp_forward_gated", "ttt_decode_steps_gated",
                  "ttt_version"):

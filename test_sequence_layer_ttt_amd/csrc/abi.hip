@@ -406,6 +406,32 @@ int ttt_eta_gate_backward(int B, int H, int L, int d, int io, const void *XK,
                                                   dXK, dtheta, stream));
 }
 
+int ttt_qkv_project(int B, int L, int d_model, int H, int d, const void *X, const void *theta, void *XQ,
+                    void *XK, void *XV, hipStream_t stream) {
+    if (B < 0 || L < 0 || H < 0) return fail(TTT_E_SHAPE, "negative size (B=%d L=%d H=%d)", B, L, H);
+    if (d != 64) return fail(TTT_E_SHAPE, "d = %d: the projection kernel serves d = 64", d);
+    if (d_model <= 0 || d_model % 64)
+        return fail(TTT_E_SHAPE, "d_model = %d is not a positive multiple of 64", d_model);
+    if (L > TTT_MAX_L) return fail(TTT_E_SHAPE, "L = %d exceeds TTT_MAX_L", L);
+    if (static_cast<long long>(B) * L > INT_MAX || 3LL * H * d > INT_MAX)
+        return fail(TTT_E_SHAPE, "B*L or 3*H*d exceeds INT_MAX");
+    size_t xb, tb, ob;
+    if (!nbytes(&xb, {size_t(B), size_t(L), size_t(d_model), 2}) ||
+        !nbytes(&tb, {3, size_t(H), size_t(d), size_t(d_model), 2}) ||
+        !nbytes(&ob, {size_t(B), size_t(H), size_t(L), size_t(d), 2}))
+        return fail(TTT_E_SHAPE, "sizes overflow");
+    const bool work = ob > 0;  // nothing to write: no input is read
+    const Buf in[] = {{X, work ? xb : 0, "X", false, 16}, {theta, work ? tb : 0, "theta", false, 16}};
+    const Buf out[] = {{XQ, ob, "XQ", false, 16}, {XK, ob, "XK", false, 16}, {XV, ob, "XV", false, 16}};
+    int st;
+    if ((st = check_bufs(in, 2)) || (st = check_bufs(out, 3))) return st;
+    if ((st = check_alias(out, 3, in, 2, nullptr)) || (st = check_alias(out, 1, out + 1, 2, nullptr)) ||
+        (st = check_alias(out + 1, 1, out + 2, 1, nullptr)))
+        return st;
+    if (!work) return TTT_OK;
+    return launched(ttt::launch_qkv_project(B, L, d_model, H, X, theta, XQ, XK, XV, stream));
+}
+
 int ttt_linear_backward_workspace(int B, int H, int L, int d, int mb, size_t *bytes) {
     int st;
     if ((st = check_common(B, H, L, mb, TTT_F32))) return st;

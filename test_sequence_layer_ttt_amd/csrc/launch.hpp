@@ -73,6 +73,8 @@ hipError_t launch_ln_l2_bwd(int rows, int d, const float *Z, const float *T, con
 hipError_t launch_linear_valu(const LinearArgs &a, hipStream_t stream);
 bool linear_mfma_supported(const LinearArgs &a);
 hipError_t launch_linear_mfma(const LinearArgs &a, hipStream_t stream);
+hipError_t launch_qkv_project(int B, int L, int dm, int H, const void *X, const void *theta, void *XQ,
+                              void *XK, void *XV, hipStream_t stream);
 hipError_t launch_eta_gate(int B, int H, int L, int d, int io, const void *XK, const float *theta,
                            float eta_base, float *eta, hipStream_t stream);
 hipError_t launch_eta_gate_backward(int B, int H, int L, int d, int io, const void *XK,

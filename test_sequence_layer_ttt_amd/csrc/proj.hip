@@ -1,0 +1,150 @@
+// Input projections of the layer: the query, key and value views XQ, XK, XV
+// of the layer input X, made by the outer-loop weights theta_Q, theta_K,
+// theta_V (lryc.cn TTT article §2.2; the damodev.csdn.net deep-dive §4.2
+// feeds the three views to the inner loop):
+//     out_v[b,h,t,j] = sum_k X[b,t,k] theta[v][h d + j][k],   v = Q, K, V.
+//
+// One bf16 GEMM with fp32 accumulation, computed transposed, C^T = Theta X^T:
+// rows = the 3 H d output features, columns = the B L tokens, contraction
+// over d_model. With Theta as the A operand of the 16x16x32 MFMA, a lane's
+// four accumulator values are four consecutive features of one token, which
+// go straight to the [B,H,L,d] layout the prefill kernels read as one 8-byte
+// store.
+//  * block tile 256 features x 256 tokens, contraction steps of 64; 8 waves
+//    (2 along the features x 4 along the tokens), 128 x 64 per wave = 8 x 4
+//    MFMA tiles, 32 fp32 accumulator quads;
+//  * operands staged in LDS, two stages: each step's global loads are issued
+//    before the MFMAs of the previous step and written to the other stage
+//    after them, one barrier per step. LDS rows are padded to 144 bytes, so
+//    the 16 rows one fragment read touches start on different banks;
+//  * XCD-aware order: workgroups go to the 8 XCDs round robin, so XCD x is
+//    given the feature blocks x, x + 8, ... (its slice of Theta stays in its
+//    L2) and runs them over every token block.
+#include "launch.hpp"
+#include "tile.hpp"
+
+namespace ttt {
+namespace {
+
+using namespace tile;
+
+constexpr int PF = 256;           // output features per block
+constexpr int PT = 256;           // tokens per block
+constexpr int PK = 64;            // contraction step
+constexpr int PSTR = PK + 8;      // LDS row stride (bf16)
+constexpr int PNT = 512;          // threads (8 waves)
+constexpr int WF = 128, WT = 64;  // per-wave tile
+constexpr int NXCD = 8;
+
+struct ProjSmem {
+    uint16_t a[2][PF * PSTR];  // Theta rows [feature][k]
+    uint16_t b[2][PT * PSTR];  // X rows [token][k]
+};
+
+__global__ __launch_bounds__(PNT) void qkv_project_kernel(int NF, int M, int K, int HD, int H, int L,
+                                                          const bf16_t *X, const bf16_t *theta,
+                                                          bf16_t *XQ, bf16_t *XK, bf16_t *XV) {
+    __shared__ ProjSmem sm;
+    const int nfb = (NF + PF - 1) / PF, nfx = (nfb + NXCD - 1) / NXCD;
+    const int i = blockIdx.x, r = i / NXCD;
+    const int fb = i % NXCD + NXCD * (r % nfx), tb = r / nfx;
+    if (fb >= nfb) return;  // the grid rounds the feature blocks up to a multiple of 8
+    const int f0 = fb * PF, t0 = tb * PT;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c = lane & 15;
+    const int wf0 = (w & 1) * WF, wt0 = (w >> 1) * WT;
+
+    // global -> registers: 4 chunks of 16 bytes of each operand per thread;
+    // rows past the end read row 0 and are zeroed
+    uint4 ra[4], rb[4];
+    auto load = [&](int kt) {
+        const int k0 = kt * PK;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int ch = tid + PNT * q, row = ch >> 3, col = (ch & 7) * 8;
+            const int fr = f0 + row, tr = t0 + row;
+            const uint4 va = *reinterpret_cast<const uint4 *>(theta + static_cast<size_t>(fr < NF ? fr : 0) * K + k0 + col);
+            const uint4 vb = *reinterpret_cast<const uint4 *>(X + static_cast<size_t>(tr < M ? tr : 0) * K + k0 + col);
+            const bool fa_ok = fr < NF, tb_ok = tr < M;  // selects per component (not of the struct)
+            ra[q] = make_uint4(fa_ok ? va.x : 0u, fa_ok ? va.y : 0u, fa_ok ? va.z : 0u, fa_ok ? va.w : 0u);
+            rb[q] = make_uint4(tb_ok ? vb.x : 0u, tb_ok ? vb.y : 0u, tb_ok ? vb.z : 0u, tb_ok ? vb.w : 0u);
+        }
+    };
+    auto store = [&](int st) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int ch = tid + PNT * q, row = ch >> 3, col = (ch & 7) * 8;
+            *reinterpret_cast<uint4 *>(&sm.a[st][row * PSTR + col]) = ra[q];
+            *reinterpret_cast<uint4 *>(&sm.b[st][row * PSTR + col]) = rb[q];
+        }
+    };
+
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc[t][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = K / PK;
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int st = kt & 1;
+        if (kt + 1 < nk) load(kt + 1);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            // fragments: lane (g, c) holds row c of a 16-row tile, k = 32 kk + 8 g .. +7
+            bf16x8 fa[8], fx[4];
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                fa[t] = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const uint4 *>(&sm.a[st][(wf0 + 16 * t + c) * PSTR + 32 * kk + 8 * g]));
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                fx[s] = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const uint4 *>(&sm.b[st][(wt0 + 16 * s + c) * PSTR + 32 * kk + 8 * g]));
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc[t][s] = mfma32(fa[t], fx[s], acc[t][s]);
+        }
+        if (kt + 1 < nk) store(st ^ 1);
+        __syncthreads();
+    }
+
+    // lane (g, c) of tile (t, s): features f0 + wf0 + 16 t + 4 g .. +3 of token t0 + wt0 + 16 s + c
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int m = t0 + wt0 + 16 * s + c;
+        if (m >= M) continue;
+        const int bi = m / L, tp = m - bi * L;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int n = f0 + wf0 + 16 * t + 4 * g;
+            if (n >= NF) continue;
+            const int v = n / HD, hj = n - v * HD, h = hj / D, j = hj - h * D;
+            bf16_t *out = v == 0 ? XQ : (v == 1 ? XK : XV);
+            bf16_t *dst = out + ((static_cast<size_t>(bi) * H + h) * L + tp) * D + j;
+            *reinterpret_cast<uint2 *>(dst) = make_uint2(pack2(acc[t][s][0], acc[t][s][1]),
+                                                        pack2(acc[t][s][2], acc[t][s][3]));
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_qkv_project(int B, int L, int dm, int H, const void *X, const void *theta, void *XQ,
+                              void *XK, void *XV, hipStream_t stream) {
+    const int HD = H * D, NF = 3 * HD;
+    const long Ml = static_cast<long>(B) * L;
+    const int M = static_cast<int>(Ml);
+    const int nfb = (NF + PF - 1) / PF, nfx = (nfb + NXCD - 1) / NXCD, ntb = (M + PT - 1) / PT;
+    const long blocks = static_cast<long>(NXCD) * nfx * ntb;
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(qkv_project_kernel, dim3(static_cast<unsigned>(blocks)), dim3(PNT), 0, stream, NF, M, dm,
+                       HD, H, L, static_cast<const bf16_t *>(X), static_cast<const bf16_t *>(theta),
+                       static_cast<bf16_t *>(XQ), static_cast<bf16_t *>(XK), static_cast<bf16_t *>(XV));
+    return hipGetLastError();
+}
+
+}  // namespace ttt

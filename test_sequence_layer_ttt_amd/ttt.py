@@ -162,6 +162,24 @@ def ttt_eta_gate(XK, theta_lr, eta_base: float, eta=None, stream=None):
     return eta
 
 
+def ttt_qkv_project(X, theta, H: int, out=None, stream=None):
+    """XQ, XK, XV [B,H,L,64] bf16 from X [B,L,d_model] bf16 and theta
+    [3,H*64,d_model] bf16 (output-major): XQ[b,h,t,j] = sum_k X[b,t,k]
+    theta[0][h*64+j][k], likewise XK (theta[1]) and XV (theta[2])."""
+    B, L, dm = X.shape
+    d = 64
+    _need(X, "X", (B, L, dm), torch.bfloat16)
+    _need(theta, "theta", (3, H * d, dm), torch.bfloat16)
+    if out is None:
+        out = tuple(torch.empty((B, H, L, d), device=X.device, dtype=torch.bfloat16) for _ in range(3))
+    for o, n in zip(out, ("XQ", "XK", "XV")):
+        _need(o, n, (B, H, L, d), torch.bfloat16)
+    lib = _lib.load()
+    _lib.check(lib.ttt_qkv_project(B, L, dm, H, d, _ptr(X), _ptr(theta), _ptr(out[0]), _ptr(out[1]),
+                                   _ptr(out[2]), _stream(stream)))
+    return out
+
+
 def ttt_eta_gate_backward(XK, theta_lr, eta_base: float, deta, dXK, dtheta=None, stream=None):
     """Adds the gate's share to dXK [B,H,L,d] fp32 in place; returns dtheta
     [B,H,d] per sequence (sum over B for the parameter's gradient)."""

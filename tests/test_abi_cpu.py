@@ -22,7 +22,7 @@ def test_exports_every_declared_symbol(lib):
                           "ttt_decode_steps", "ttt_linear_backward",
                           "ttt_linear_backward_workspace", "ttt_ln_l2_bwd", "ttt_last_error",
                           "ttt_version", "ttt_linear_forward_gated", "ttt_eta_gate",
-                          "ttt_eta_gate_backward", "ttt_linear_backward_noalloc"}
+                          "ttt_eta_gate_backward", "ttt_linear_backward_noalloc", "ttt_qkv_project"}
     for n in names:
         assert hasattr(lib, n), n
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
@@ -375,3 +375,25 @@ def test_backward_noalloc_rejects_inputs_beyond_its_scratch(lib):
     msg = lib.ttt_last_error().decode()
     assert "scratch" in msg and str(64 << 20) in msg
     assert call(1, 1, -1) == _lib.TTT_E_SHAPE
+
+
+def _proj(lib, B=1, L=16, dm=64, H=1, d=64, ptrs=None):
+    p = ptrs or [FAKE + i * (1 << 24) for i in range(5)]
+    return lib.ttt_qkv_project(B, L, dm, H, d, *[ctypes.c_void_p(x) for x in p], None)
+
+
+def test_qkv_project_rejects_bad_arguments(lib):
+    TTT_E_NULL, TTT_E_SHAPE, TTT_E_ALIGN, TTT_E_ALIAS = -1, -2, -4, -5
+    assert _proj(lib, d=32) == TTT_E_SHAPE
+    assert _proj(lib, dm=96) == TTT_E_SHAPE
+    assert _proj(lib, dm=0) == TTT_E_SHAPE
+    assert _proj(lib, B=-1) == TTT_E_SHAPE
+    assert _proj(lib, B=1 << 16, L=1 << 16) == TTT_E_SHAPE          # B*L > INT_MAX
+    p = [FAKE + i * (1 << 24) for i in range(5)]
+    assert _proj(lib, ptrs=[0] + p[1:]) == TTT_E_NULL
+    assert _proj(lib, ptrs=p[:2] + [p[2] + 8] + p[3:]) == TTT_E_ALIGN
+    assert _proj(lib, ptrs=p[:2] + [p[0]] + p[3:]) == TTT_E_ALIAS   # XQ over X
+    assert _proj(lib, ptrs=p[:3] + [p[2]] + p[4:]) == TTT_E_ALIAS   # XK over XQ
+    assert _proj(lib, ptrs=p[:4] + [p[3]]) == TTT_E_ALIAS           # XV over XK
+    # nothing to write: no pointer is needed and nothing is launched
+    assert _proj(lib, L=0, ptrs=[0, 0, 0, 0, 0]) == 0
