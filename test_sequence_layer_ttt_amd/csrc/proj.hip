@@ -36,6 +36,8 @@ constexpr int PNT = 512;          // threads (8 waves)
 constexpr int WF = 128, WT = 64;  // per-wave tile
 constexpr int NXCD = 8;
 
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;  // 16 bytes, kept in registers
+
 struct ProjSmem {
     uint16_t a[2][PF * PSTR];  // Theta rows [feature][k]
     uint16_t b[2][PT * PSTR];  // X rows [token][k]
@@ -53,28 +55,27 @@ __global__ __launch_bounds__(PNT) void qkv_project_kernel(int NF, int M, int K, 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c = lane & 15;
     const int wf0 = (w & 1) * WF, wt0 = (w >> 1) * WT;
 
-    // global -> registers: 4 chunks of 16 bytes of each operand per thread;
-    // rows past the end read row 0 and are zeroed
-    uint4 ra[4], rb[4];
+    // global -> registers: 4 chunks of 16 bytes of each operand per thread.
+    // Rows past the end read row 0: a feature row only reaches the outputs of
+    // that feature and a token row those of that token, which are not stored,
+    // so the values need no masking.
+    u32x4 ra[4], rb[4];
     auto load = [&](int kt) {
         const int k0 = kt * PK;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int ch = tid + PNT * q, row = ch >> 3, col = (ch & 7) * 8;
             const int fr = f0 + row, tr = t0 + row;
-            const uint4 va = *reinterpret_cast<const uint4 *>(theta + static_cast<size_t>(fr < NF ? fr : 0) * K + k0 + col);
-            const uint4 vb = *reinterpret_cast<const uint4 *>(X + static_cast<size_t>(tr < M ? tr : 0) * K + k0 + col);
-            const bool fa_ok = fr < NF, tb_ok = tr < M;  // selects per component (not of the struct)
-            ra[q] = make_uint4(fa_ok ? va.x : 0u, fa_ok ? va.y : 0u, fa_ok ? va.z : 0u, fa_ok ? va.w : 0u);
-            rb[q] = make_uint4(tb_ok ? vb.x : 0u, tb_ok ? vb.y : 0u, tb_ok ? vb.z : 0u, tb_ok ? vb.w : 0u);
+            ra[q] = *reinterpret_cast<const u32x4 *>(theta + static_cast<size_t>(fr < NF ? fr : 0) * K + k0 + col);
+            rb[q] = *reinterpret_cast<const u32x4 *>(X + static_cast<size_t>(tr < M ? tr : 0) * K + k0 + col);
         }
     };
     auto store = [&](int st) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int ch = tid + PNT * q, row = ch >> 3, col = (ch & 7) * 8;
-            *reinterpret_cast<uint4 *>(&sm.a[st][row * PSTR + col]) = ra[q];
-            *reinterpret_cast<uint4 *>(&sm.b[st][row * PSTR + col]) = rb[q];
+            *reinterpret_cast<u32x4 *>(&sm.a[st][row * PSTR + col]) = ra[q];
+            *reinterpret_cast<u32x4 *>(&sm.b[st][row * PSTR + col]) = rb[q];
         }
     };
 
@@ -91,6 +92,9 @@ __global__ __launch_bounds__(PNT) void qkv_project_kernel(int NF, int M, int K, 
     for (int kt = 0; kt < nk; ++kt) {
         const int st = kt & 1;
         if (kt + 1 < nk) load(kt + 1);
+        // the stores of the next stage stay behind the MFMAs of this one (so
+        // the global loads above have the whole step to arrive)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             // fragments: lane (g, c) holds row c of a 16-row tile, k = 32 kk + 8 g .. +7
@@ -98,16 +102,19 @@ __global__ __launch_bounds__(PNT) void qkv_project_kernel(int NF, int M, int K, 
 #pragma unroll
             for (int t = 0; t < 8; ++t)
                 fa[t] = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const uint4 *>(&sm.a[st][(wf0 + 16 * t + c) * PSTR + 32 * kk + 8 * g]));
+                    bf16x8, *reinterpret_cast<const u32x4 *>(&sm.a[st][(wf0 + 16 * t + c) * PSTR + 32 * kk + 8 * g]));
 #pragma unroll
             for (int s = 0; s < 4; ++s)
                 fx[s] = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const uint4 *>(&sm.b[st][(wt0 + 16 * s + c) * PSTR + 32 * kk + 8 * g]));
+                    bf16x8, *reinterpret_cast<const u32x4 *>(&sm.b[st][(wt0 + 16 * s + c) * PSTR + 32 * kk + 8 * g]));
+            // all twelve reads in flight together, then the 32 products
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int t = 0; t < 8; ++t)
 #pragma unroll
                 for (int s = 0; s < 4; ++s) acc[t][s] = mfma32(fa[t], fx[s], acc[t][s]);
         }
+        __builtin_amdgcn_sched_barrier(0);
         if (kt + 1 < nk) store(st ^ 1);
         __syncthreads();
     }
