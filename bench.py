@@ -113,12 +113,48 @@ def measured_traffic(alg_bytes):
     return t.get("bytes_per_launch")
 
 
-def cpu_threads():
+# host cores a one-GPU machine gives its job (whatever the host's own count is)
+BOX_CPU_SHARE = 16
+
+
+def cpu_threads(nseq: int) -> int:
+    """Oracle threads: min(cores available, the box's share, sequences) -- the
+    oracle parallelises over independent (n, h) sequences only."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
         n = os.cpu_count() or 1
-    return max(1, min(16, n))
+    return max(1, min(BOX_CPU_SHARE, n, int(nseq)))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_single_thread_small():
+    """The oracle on one thread at the two small configs: workload 1 (B1 H1
+    L64 d16, fp32, gated eta) and workload 2 (B4 H12 L2048 d64), in full."""
+    import oracle
+    from test_sequence_layer_ttt_amd import gen
+    out = {}
+    for num in (1, 2):
+        x = gen.make_workload(num)
+        t = time.perf_counter()
+        eta = x.eta if x.eta is not None else oracle.eta_gate(x.XK, x.theta_lr, x.eta_base)
+        oracle.linear_forward(x.XQ, x.XK, x.XV, eta, x.W0, x.b0, x.gamma, x.beta, x.eps, mb=16,
+                              nthreads=1)
+        dt = time.perf_counter() - t
+        out[f"workload{num}"] = {"value": x.B * x.L / dt, "unit": "tokens/s", "seconds": dt,
+                                 "cores": 1, "shape": f"B{x.B} H{x.H} L{x.L} d{x.d}"}
+    return out
 
 
 def main():
@@ -227,6 +263,7 @@ def main():
     wall = time.perf_counter() - t0
     kern_ms = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(K)]
     kern_avg_s = float(np.mean(kern_ms)) / 1e3
+    kern_med_s = float(np.median(kern_ms)) / 1e3
     ms_per_step = wall * 1e3 / K
     tokens = B * L
     value = tokens / (wall / K)
@@ -257,12 +294,14 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "linear_prefill_mfma",
                      "kernel_avg_us": kern_avg_s * 1e6,
+                     "kernel_median_us": kern_med_s * 1e6,
+                     "frac_at_median": ab / kern_med_s / 1e9 / HBM_PEAK_GBS,
                      "alg_bytes_per_launch": ab},
     }
 
     if not args.no_cpu_baseline:
         import oracle
-        nt = cpu_threads()
+        nt = cpu_threads(B * H)
         xs = {k: np.ascontiguousarray(getattr(x, k), np.float64)
               for k in ("XQ", "XK", "XV", "eta", "W0", "b0", "gamma", "beta")}
         t1 = time.perf_counter()
@@ -276,9 +315,13 @@ def main():
                                            nthreads=nt)
         tc = time.perf_counter() - t1
         out["cpu_baseline"] = {"value": tokens / tc, "unit": "tokens/s", "cores": nt,
-                               "kind": "oracle",
+                               "kind": "oracle", "cpu_model": cpu_model(),
+                               "threads_rule": f"min(cores available, box share {BOX_CPU_SHARE}, "
+                                               f"B*H = {B * H})",
                                "sample": f"full workload (B={B}, H={H}, L={L}), fp64 primal "
                                          f"form, {nt} threads over (n,h), {tc:.2f} s"}
+        if wl == WORKLOAD and plain:
+            out["cpu_baseline"]["single_thread"] = cpu_single_thread_small()
         if wl == 2:  # also one thread, on one sequence of the workload (scaled to tokens/s)
             one = {k: np.ascontiguousarray(v[:1, :1]) for k, v in xs.items()
                    if k in ("XQ", "XK", "XV", "eta")}
@@ -368,7 +411,7 @@ def bench_mlp(args, opts=False, gated=False):
     extra = {}
     if not args.no_cpu_baseline:
         import oracle
-        nt = cpu_threads()
+        nt = cpu_threads(B * H)
         t1 = time.perf_counter()
         run = (lambda *a, **k: oracle.mlp_forward_opts(*a, loss="inner_product",
                                                        weight_decay=0.5, **k)) if opts \
@@ -425,7 +468,7 @@ def bench_decode(args):
     extra = {}
     if not args.no_cpu_baseline:
         import oracle
-        nt = cpu_threads()
+        nt = cpu_threads(B * H)
         Wn = np.broadcast_to(Wp[0].cpu().numpy(), (B, H, d, d)).astype(np.float64)
         bn = np.broadcast_to(bp[0].cpu().numpy(), (B, H, d)).astype(np.float64)
         ns = 4  # bounded sample: four steps
@@ -492,7 +535,7 @@ def bench_decode_steps(args, mb: int = 1, gated: bool = False):
     extra = {}
     if mb == 1 and not args.no_cpu_baseline:
         import oracle
-        nt = cpu_threads()
+        nt = cpu_threads(B * H)
         Wn = np.broadcast_to(Wp[0].cpu().numpy(), (B, H, d, d)).astype(np.float64)
         bn = np.broadcast_to(bp[0].cpu().numpy(), (B, H, d)).astype(np.float64)
         ns = 4  # bounded sample: four steps
@@ -511,7 +554,7 @@ def bench_decode_steps(args, mb: int = 1, gated: bool = False):
     if mb > 1 and not args.no_cpu_baseline:
         # the oracle's mini-batch rule over one chunk of mb tokens on all states
         import oracle
-        nt = cpu_threads()
+        nt = cpu_threads(B * H)
         Wn = np.broadcast_to(Wp[0].cpu().numpy(), (B, H, d, d)).astype(np.float64)
         bn = np.broadcast_to(bp[0].cpu().numpy(), (B, H, d)).astype(np.float64)
         tok = lambda a: np.ascontiguousarray(np.moveaxis(a[:mb], 0, 2))  # [T,B,H,..] -> [B,H,T,..]

@@ -28,6 +28,22 @@ def max_rel(got, ref, nseq: int) -> float:
     return float((num / den).max())
 
 
+def elem_rel(got, ref, nseq: int) -> float:
+    """Secondary log of the per-output metric: the largest elementwise ratio
+    |got - ref| / max(|ref|, 1e-3 max|ref|), the floor taken per (n,h) slice
+    (elementwise ratios are undefined near zero without one)."""
+    g = np.asarray(got, np.float64).reshape(nseq, -1)
+    r = np.asarray(ref, np.float64).reshape(nseq, -1)
+    if g.size == 0:
+        return 0.0
+    floor = np.maximum(1e-3 * np.abs(r).max(1, keepdims=True), 1e-30)
+    return float((np.abs(g - r) / np.maximum(np.abs(r), floor)).max())
+
+
+def elem_errors(got, ref, nseq, names):
+    return {n: elem_rel(g, r, nseq) for n, g, r in zip(names, got, ref)}
+
+
 def dev(a, dtype=torch.float32, device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device).to(dtype)
 

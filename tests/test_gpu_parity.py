@@ -24,6 +24,7 @@ def _check_linear(x, tag, mb=None, tol=None):
     ref = P.linear_oracle(x, mb=mb)
     err = P.errors(got, ref, x.B * x.H, LIN_NAMES)
     _report(tag, err)
+    _report(tag + " elementwise (floor 1e-3 max|ref|)", P.elem_errors(got, ref, x.B * x.H, LIN_NAMES))
     tol = tol or P.TOL[x.io]
     assert max(err.values()) <= tol, err
     return got
@@ -144,6 +145,7 @@ def test_mlp_full_workload4():
     got = P.mlp_gpu(x)
     ref = P.mlp_oracle(x)
     err = P.errors(got, ref, x.B * x.H, MLP_NAMES)
+    _report("workload 4 elementwise (floor 1e-3 max|ref|)", P.elem_errors(got, ref, x.B * x.H, MLP_NAMES))
     _report("workload4 full", err)
     assert max(err.values()) <= P.TOL["bf16"], err
 
