@@ -164,7 +164,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="3", choices=["3", "2", "5p", "4", "4o", "4g", "5d", "5r", "5m", "5g", "3b",
-                             "3g", "3gb", "3o"])
+                             "3g", "3gb", "3o", "3p", "2p"])
     ap.add_argument("--peaks", action="store_true",
                     help="measure achievable HBM copy bandwidth and bf16 GEMM throughput (context)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -213,6 +213,8 @@ def main():
         return bench_backward(args)
     if args.workload == "3gb":
         return bench_gate_backward(args)
+    if args.workload in ("3p", "2p"):
+        return bench_proj(args, int(args.workload[0]))
     wl = {"3": 3, "3g": 3, "3o": 3, "2": 2, "5p": 5}[args.workload]
     gated = args.workload == "3g"
     opts = args.workload == "3o"  # inner-product loss, weight decay 0.5
@@ -665,6 +667,46 @@ def bench_gate_backward(args):
           {"workload": "ttt_eta_gate_backward_bf16_B2_H32_L8192_d64", "B": B, "H": H, "L": L,
            "d": d, "io": "bf16", "grads": "fp32", "parallelism": "none (1 GPU)"}, roof, extra)
 
+
+
+def bench_proj(args, num: int):
+    """The layer's Q/K/V input projections (ttt_qkv_project) at a Linear
+    workload's shape (model width H*d), an MFMA-bound bf16 GEMM: the
+    algorithmic flops are 2 * B*L * d_model * 3*H*d per launch."""
+    import numpy as np
+    import torch
+    from test_sequence_layer_ttt_amd import gen, ttt
+    x = gen.make_proj_workload(num)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    X = torch.from_numpy(x.X).to(dev).to(torch.bfloat16)
+    th = torch.from_numpy(x.theta).to(dev).to(torch.bfloat16)
+    out = tuple(torch.empty((x.B, x.H, x.L, x.d), device=dev, dtype=torch.bfloat16) for _ in range(3))
+    stream = torch.cuda.current_stream()
+    wall, kern = _timed(lambda: ttt.ttt_qkv_project(X, th, x.H, out=out, stream=stream), stream,
+                        args.warmup, args.steps)
+    fl = 2.0 * x.B * x.L * x.dm * 3 * x.H * x.d
+    ach = fl / kern / 1e12
+    extra = {}
+    if not args.no_cpu_baseline:  # the oracle's sums at a bounded sample of outputs
+        import oracle
+        rng = np.random.default_rng(num)
+        n = 20000
+        idx = np.stack([rng.integers(0, 3, n), rng.integers(0, x.B, n), rng.integers(0, x.H, n),
+                        rng.integers(0, x.L, n), rng.integers(0, x.d, n)], axis=1).astype(np.int32)
+        t = time.perf_counter()
+        oracle.qkv_project_at(x.X, x.theta, x.H, idx)
+        tc = time.perf_counter() - t
+        extra["cpu_baseline"] = {"value": n / tc / (3 * x.H * x.d) , "unit": "tokens/s", "cores": 1,
+                                 "kind": "oracle", "cpu_model": cpu_model(),
+                                 "sample": f"{n} outputs one by one (fp64 sums over d_model = {x.dm}), "
+                                           f"1 thread, {tc:.2f} s, scaled to tokens of 3 H d outputs"}
+    _line(f"Q/K/V projection tokens/s (d_model={x.dm})", x.B * x.L / wall, args, wall, "bf16",
+          {"workload": f"qkv_project_B{x.B}_L{x.L}_dmodel{x.dm}_H{x.H}_d{x.d}", "B": x.B, "L": x.L,
+           "d_model": x.dm, "H": x.H, "d": x.d, "parallelism": "none (1 GPU)"},
+          {"bound": "mfma", "achieved": ach, "peak": 2500.0, "unit": "TFLOP/s", "frac": ach / 2500.0,
+           "traffic": None, "kernel": "qkv_project_kernel", "kernel_avg_us": kern * 1e6,
+           "alg_flops_per_launch": fl}, extra)
 
 
 def bench_peaks(args):
