@@ -1,4 +1,4 @@
-"""fp64 gradients of the TTT-Linear inner loop -- TEST INFRASTRUCTURE ONLY.
+"""fp64 gradients of the TTT-Linear and TTT-MLP inner loops -- TEST INFRASTRUCTURE ONLY.
 
 Only the tests and the benchmark's CPU baseline may import this module; the
 GPU path never does, and it shares nothing with the GPU path.
@@ -151,4 +151,85 @@ def linear_backward_gated(XQ, XK, XV, theta_lr, eta_base: float, W0, b0, gamma, 
     out["W"] = W.detach().numpy()
     out["b"] = b.detach().numpy()
     out["eta"] = eta.detach().numpy()
+    return out
+
+
+# ----------------------------------------------------------------------------
+# TTT-MLP (the lryc.cn TTT article §2.1: d -> 4d -> d with exact GELU, the
+# same LN-residual output; the same mini-batch rule as TTT-Linear)
+# ----------------------------------------------------------------------------
+
+_SQRT2 = 2.0 ** 0.5
+_INV_SQRT_2PI = (2.0 * np.pi) ** -0.5
+
+
+def gelu(z: torch.Tensor) -> torch.Tensor:
+    """Exact GELU z Phi(z), Phi the standard normal CDF."""
+    return 0.5 * z * (1.0 + torch.erf(z / _SQRT2))
+
+
+def gelu_prime(z: torch.Tensor) -> torch.Tensor:
+    """d/dz gelu(z) = Phi(z) + z phi(z), written out so that autograd can take
+    its own derivative (the inner gradient G1 contains it)."""
+    return 0.5 * (1.0 + torch.erf(z / _SQRT2)) + z * _INV_SQRT_2PI * torch.exp(-0.5 * z * z)
+
+
+def mlp_primal(XQ, XK, XV, eta, W1, b1, W2, b2, gamma, beta, eps: float, mb: int):
+    """Primal forward of TTT-MLP on torch tensors. XQ, XK, XV [B,H,L,d];
+    eta [B,H,L]; W1 [B,H,d,4d]; b1 [B,H,4d]; W2 [B,H,4d,d]; b2 [B,H,d];
+    gamma, beta [H,d]. Every token of a chunk takes its gradient of
+    1/2 ||LN(gelu(k W1 + b1) W2 + b2) - (v - k)||^2 at the chunk-start state;
+    the updates then apply one token at a time, and token t's output is
+    q_t + LN(gelu(q_t W1_t + b1_t) W2_t + b2_t). Returns O, W1, b1, W2, b2."""
+    B, H, L, d = XQ.shape
+    g = gamma[None, :, :]
+    bt = beta[None, :, :]
+    outs = []
+    for c0 in range(0, L, mb):
+        sl = slice(c0, min(L, c0 + mb))
+        xq, xk, xv, et = XQ[:, :, sl], XK[:, :, sl], XV[:, :, sl], eta[:, :, sl]
+        Z1 = xk @ W1 + b1[:, :, None, :]
+        A = gelu(Z1)
+        Z2 = A @ W2 + b2[:, :, None, :]
+        G2 = ln_l2_grad(Z2, xv - xk, g[:, :, None, :], bt[:, :, None, :], eps)
+        G1 = (G2 @ W2.transpose(-1, -2)) * gelu_prime(Z1)
+        for t in range(xq.shape[2]):
+            e = et[:, :, t]
+            W1 = W1 - e[..., None, None] * xk[:, :, t, :, None] * G1[:, :, t, None, :]
+            b1 = b1 - e[..., None] * G1[:, :, t, :]
+            W2 = W2 - e[..., None, None] * A[:, :, t, :, None] * G2[:, :, t, None, :]
+            b2 = b2 - e[..., None] * G2[:, :, t, :]
+            a = gelu((xq[:, :, t, None, :] @ W1)[:, :, 0, :] + b1)
+            zb = (a[:, :, None, :] @ W2)[:, :, 0, :] + b2
+            outs.append(xq[:, :, t, :] + ln(zb, g, bt, eps))
+    O = torch.stack(outs, 2) if outs else XQ * 0.0
+    return O, W1, b1, W2, b2
+
+
+def mlp_backward(XQ, XK, XV, eta, W1, b1, W2, b2, gamma, beta, eps: float, mb: int, dO,
+                 dW1_out=None, db1_out=None, dW2_out=None, db2_out=None) -> dict:
+    """Gradients of <dO, O> + <dW1_out, W1_L> + <db1_out, b1_L>
+    + <dW2_out, W2_L> + <db2_out, b2_L> (float64 NumPy) with respect to XQ,
+    XK, XV, eta, the initial state W1, b1, W2, b2 (per sequence) and gamma,
+    beta (per head, summed over the batch). Also returns the forward."""
+    B, H, L, d = np.shape(XQ)
+    m = 4 * d
+    W1 = np.broadcast_to(W1, (B, H, d, m))
+    b1 = np.broadcast_to(b1, (B, H, m))
+    W2 = np.broadcast_to(W2, (B, H, m, d))
+    b2 = np.broadcast_to(b2, (B, H, d))
+    names = ("XQ", "XK", "XV", "eta", "W1", "b1", "W2", "b2", "gamma", "beta")
+    ts = [_t(a, True) for a in (XQ, XK, XV, eta, W1, b1, W2, b2, gamma, beta)]
+    O, W1L, b1L, W2L, b2L = mlp_primal(*ts, eps, mb)
+    loss = (O * _t(dO)).sum()
+    for fin, adj in ((W1L, dW1_out), (b1L, db1_out), (W2L, dW2_out), (b2L, db2_out)):
+        if adj is not None:
+            loss = loss + (fin * _t(adj)).sum()
+    grads = torch.autograd.grad(loss, ts, allow_unused=True)
+    out = {}
+    for n, t, gr in zip(names, ts, grads):
+        out["d" + n] = np.zeros(t.shape) if gr is None else gr.detach().numpy()
+    out["O"] = O.detach().numpy()
+    out["W1"], out["b1"] = W1L.detach().numpy(), b1L.detach().numpy()
+    out["W2"], out["b2"] = W2L.detach().numpy(), b2L.detach().numpy()
     return out
