@@ -323,6 +323,42 @@ int ttt_linear_backward_noalloc(int B, int H, int L, int d, int mb, int io, floa
                                 float *db0, float *dgamma, float *dbeta, hipStream_t stream);
 
 /*
+ * Backward of ttt_mlp_forward: the gradients of
+ *   loss = <dO, O> + <dW1_out, W1_L> + <db1_out, b1_L> + <dW2_out, W2_L> + <db2_out, b2_L>
+ * with respect to XQ, XK, XV, eta, the initial state W1, b1, W2, b2, gamma
+ * and beta -- the TTT-MLP of [Y] §2.1 (d -> 4d exact-GELU -> d, LN residual)
+ * under the mini-batch rule of [D] §4.1-4.2, trained through the inner loop
+ * as in [D] §6, §7.1. Arguments as ttt_mlp_forward for the forward inputs
+ * (d = 64 only, any 1 <= mb <= 16, any L >= 0, io, ln_eps, w0_batched), plus:
+ *   dO [B,H,L,d] fp32; dW1_out [B,H,d,4d], db1_out [B,H,4d], dW2_out [B,H,4d,d],
+ *   db2_out [B,H,d] fp32, each NULL for zero.
+ *   Outputs, fp32 and per sequence: dXQ, dXK, dXV [B,H,L,d]; deta [B,H,L];
+ *   dW1 [B,H,d,4d]; db1 [B,H,4d]; dW2 [B,H,4d,d]; db2, dgamma, dbeta [B,H,d].
+ *   Parameters shared over the batch (the initial state when w0_batched == 0,
+ *   gamma, beta) need the caller's sum over B.
+ *   workspace: device memory of at least ttt_mlp_backward_workspace bytes
+ *   (the state at every chunk start and two adjoint states), caller-owned,
+ *   overwritten.
+ * No output may overlap an input, another output or the workspace.
+ * Numerics: fp32 throughout (bf16 inputs widened); the forward is recomputed
+ * chunk by chunk from the stored states in the dual form ([D] §4.2).
+ * Errors as ttt_mlp_forward; TTT_E_SHAPE also for a short workspace.
+ */
+int ttt_mlp_backward(int B, int H, int L, int d, int mb, int io, float ln_eps, const void *XQ,
+                     const void *XK, const void *XV, const float *eta, const float *W1_0,
+                     const float *b1_0, const float *W2_0, const float *b2_0, int w0_batched,
+                     const float *ln_gamma, const float *ln_beta, const float *dO,
+                     const float *dW1_out, const float *db1_out, const float *dW2_out,
+                     const float *db2_out, float *dXQ, float *dXK, float *dXV, float *deta,
+                     float *dW1, float *db1, float *dW2, float *db2, float *dgamma, float *dbeta,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes ttt_mlp_backward needs: B*H*(ceil(L/mb)+2)*(8d*d+5d)*4
+ * (d = 64: 132,352 bytes per chunk and sequence). Validates B, H, L, d, mb
+ * as ttt_mlp_backward does. */
+int ttt_mlp_backward_workspace(int B, int H, int L, int d, int mb, size_t *bytes);
+
+/*
  * One single-token TTT-Linear step (b = 1, primal form) for B x H independent
  * states held in place -- the fast-weight cache of [D] §5.2:
  *   G = lnbwd(xk W + b, xv - xk);  W <- W - eta xk^T G;  b <- b - eta G;

@@ -68,10 +68,13 @@ def load():
     lib.ttt_linear_backward_noalloc.argtypes = ([_i] * 6 + [_f] + [_P] * 6 + [_i] + [_P] * 13
                                                 + [_P])
     lib.ttt_linear_backward_workspace.argtypes = [_i] * 5 + [ctypes.POINTER(ctypes.c_size_t)]
+    lib.ttt_mlp_backward.argtypes = ([_i] * 6 + [_f] + [_P] * 8 + [_i] + [_P] * 18
+                                     + [ctypes.c_size_t, _P])
+    lib.ttt_mlp_backward_workspace.argtypes = [_i] * 5 + [ctypes.POINTER(ctypes.c_size_t)]
     lib.ttt_ln_l2_bwd.argtypes = [_i, _i, _P, _P, _P, _P, _f, _P, _P]
     for name in ("ttt_linear_forward", "ttt_mlp_forward", "ttt_decode_step", "ttt_decode_steps",
                  "ttt_linear_backward", "ttt_linear_backward_workspace", "ttt_ln_l2_bwd",
-                 "ttt_linear_backward_noalloc",
+                 "ttt_linear_backward_noalloc", "ttt_mlp_backward", "ttt_mlp_backward_workspace",
                  "ttt_linear_forward_gated", "ttt_eta_gate", "ttt_eta_gate_backward", "ttt_qkv_project",
                  "ttt_linear_forward_opts", "ttt_decode_steps_mb", "ttt_mlp_forward_opts",
                  "ttt_mlp_forward_gated", "ttt_decode_steps_gated",

@@ -342,6 +342,61 @@ int mlp_forward(int B, int H, int L, int d, int mb, int io, float ln_eps, const 
     return launched(ttt::launch_mlp(a, stream));
 }
 
+int mlp_backward(int B, int H, int L, int d, int mb, int io, float ln_eps, const void *XQ,
+                 const void *XK, const void *XV, const float *eta, const float *W1_0,
+                 const float *b1_0, const float *W2_0, const float *b2_0, int w0_batched,
+                 const float *ln_gamma, const float *ln_beta, const float *dO,
+                 const float *dW1_out, const float *db1_out, const float *dW2_out,
+                 const float *db2_out, float *dXQ, float *dXK, float *dXV, float *deta,
+                 float *dW1, float *db1, float *dW2, float *db2, float *dgamma, float *dbeta,
+                 void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    int st;
+    if ((st = check_common(B, H, L, mb, io)) || (st = check_eps(ln_eps))) return st;
+    if (d != 64) return fail(TTT_E_SHAPE, "d = %d: the MLP supports d = 64 only", d);
+    const size_t es = io == TTT_BF16 ? 2 : 4, m = 4 * static_cast<size_t>(d);
+    const size_t nb = w0_batched ? static_cast<size_t>(B) : 1;
+    size_t xb, fb, eb, w1b, b1b, w2b, b2b, o1, o2, o3, o4, need;
+    if (!nbytes(&xb, {size_t(B), size_t(H), size_t(L), size_t(d), es}) ||
+        !nbytes(&fb, {size_t(B), size_t(H), size_t(L), size_t(d), sizeof(float)}) ||
+        !nbytes(&eb, {size_t(B), size_t(H), size_t(L), sizeof(float)}) ||
+        !nbytes(&w1b, {nb, size_t(H), size_t(d), m, sizeof(float)}) ||
+        !nbytes(&b1b, {nb, size_t(H), m, sizeof(float)}) ||
+        !nbytes(&w2b, {nb, size_t(H), m, size_t(d), sizeof(float)}) ||
+        !nbytes(&b2b, {nb, size_t(H), size_t(d), sizeof(float)}) ||
+        !nbytes(&o1, {size_t(B), size_t(H), size_t(d), m, sizeof(float)}) ||
+        !nbytes(&o2, {size_t(B), size_t(H), m, sizeof(float)}) ||
+        !nbytes(&o3, {size_t(B), size_t(H), m, size_t(d), sizeof(float)}) ||
+        !nbytes(&o4, {size_t(B), size_t(H), size_t(d), sizeof(float)}))
+        return fail(TTT_E_SHAPE, "sizes overflow");
+    if ((st = ttt_mlp_backward_workspace(B, H, L, d, mb, &need))) return st;
+    const size_t pb = static_cast<size_t>(H) * d * sizeof(float);
+    const Buf in[] = {{XQ, xb, "XQ", false, 16},       {XK, xb, "XK", false, 16},
+                      {XV, xb, "XV", false, 16},       {eta, eb, "eta", false, 4},
+                      {W1_0, w1b, "W1_0", false, 4},   {b1_0, b1b, "b1_0", false, 4},
+                      {W2_0, w2b, "W2_0", false, 4},   {b2_0, b2b, "b2_0", false, 4},
+                      {ln_gamma, pb, "ln_gamma", false, 4}, {ln_beta, pb, "ln_beta", false, 4},
+                      {dO, fb, "dO", false, 4},        {dW1_out, o1, "dW1_out", true, 4},
+                      {db1_out, o2, "db1_out", true, 4}, {dW2_out, o3, "dW2_out", true, 4},
+                      {db2_out, o4, "db2_out", true, 4}};
+    const Buf out[] = {{dXQ, fb, "dXQ", false, 4},  {dXK, fb, "dXK", false, 4},
+                       {dXV, fb, "dXV", false, 4},  {deta, eb, "deta", false, 4},
+                       {dW1, o1, "dW1", false, 4},  {db1, o2, "db1", false, 4},
+                       {dW2, o3, "dW2", false, 4},  {db2, o4, "db2", false, 4},
+                       {dgamma, o4, "dgamma", false, 4}, {dbeta, o4, "dbeta", false, 4},
+                       {workspace, need, "workspace", false, 4}};
+    if ((st = check_bufs(in, 15)) || (st = check_bufs(out, 11))) return st;
+    if (workspace_bytes < need)
+        return fail(TTT_E_SHAPE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    if ((st = check_alias(out, 11, in, 15, nullptr))) return st;
+    if (B * H == 0) return ok();
+    ttt::MLPBwdArgs a{{B, H, L, d, mb, io, ln_eps, XQ, XK, XV, eta, W1_0, b1_0, W2_0, b2_0,
+                       w0_batched ? 1 : 0, ln_gamma, ln_beta, nullptr, nullptr, nullptr, nullptr,
+                       nullptr},
+                      dO, dW1_out, db1_out, dW2_out, db2_out, dXQ, dXK, dXV, deta, dW1, db1, dW2,
+                      db2, dgamma, dbeta, static_cast<float *>(workspace)};
+    return launched(ttt::launch_mlp_backward(a, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -466,6 +521,32 @@ int ttt_linear_backward_noalloc(int B, int H, int L, int d, int mb, int io, floa
     return linear_backward(B, H, L, d, mb, io, ln_eps, XQ, XK, XV, eta, W0, b0, w0_batched,
                            ln_gamma, ln_beta, dO, dW_out, db_out, dXQ, dXK, dXV, deta, dW0, db0,
                            dgamma, dbeta, nullptr, 0, true, stream);
+}
+
+int ttt_mlp_backward_workspace(int B, int H, int L, int d, int mb, size_t *bytes) {
+    int st;
+    if ((st = check_common(B, H, L, mb, TTT_F32))) return st;
+    if (d != 64) return fail(TTT_E_SHAPE, "d = %d: the MLP supports d = 64 only", d);
+    if (!bytes) return fail(TTT_E_NULL, "bytes is NULL");
+    const size_t nch = L > 0 ? static_cast<size_t>((L + mb - 1) / mb) : 0;
+    const size_t m = 4 * static_cast<size_t>(d);
+    if (!nbytes(bytes, {size_t(B), size_t(H), nch + 2, 2 * size_t(d) * m + m + size_t(d), sizeof(float)}))
+        return fail(TTT_E_SHAPE, "sizes overflow");
+    return ok();
+}
+
+int ttt_mlp_backward(int B, int H, int L, int d, int mb, int io, float ln_eps, const void *XQ,
+                     const void *XK, const void *XV, const float *eta, const float *W1_0,
+                     const float *b1_0, const float *W2_0, const float *b2_0, int w0_batched,
+                     const float *ln_gamma, const float *ln_beta, const float *dO,
+                     const float *dW1_out, const float *db1_out, const float *dW2_out,
+                     const float *db2_out, float *dXQ, float *dXK, float *dXV, float *deta,
+                     float *dW1, float *db1, float *dW2, float *db2, float *dgamma, float *dbeta,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return mlp_backward(B, H, L, d, mb, io, ln_eps, XQ, XK, XV, eta, W1_0, b1_0, W2_0, b2_0,
+                        w0_batched, ln_gamma, ln_beta, dO, dW1_out, db1_out, dW2_out, db2_out, dXQ,
+                        dXK, dXV, deta, dW1, db1, dW2, db2, dgamma, dbeta, workspace,
+                        workspace_bytes, stream);
 }
 
 int ttt_mlp_forward(int B, int H, int L, int d, int mb, int io, float ln_eps,

@@ -48,6 +48,13 @@ struct MLPArgs {
     float eta_base = 0.f;
 };
 
+struct MLPBwdArgs {
+    MLPArgs f;  // forward arguments (O and the state outputs unused)
+    const float *dO, *dW1_out, *db1_out, *dW2_out, *db2_out;
+    float *dXQ, *dXK, *dXV, *deta, *dW1, *db1, *dW2, *db2, *dgamma, *dbeta;
+    float *ws;  // chunk-start states and two adjoint states, mlp_backward_workspace_floats floats
+};
+
 struct DecodeArgs {
     int B, H, d, io;
     float eps;
@@ -87,6 +94,8 @@ size_t linear_backward_workspace_floats(int B, int H, int L, int d, int mb);
 size_t linear_backward_scratch_bytes();
 hipError_t linear_backward_scratch(float **ptr);
 hipError_t launch_linear_backward(const LinearBwdArgs &a, hipStream_t stream);
+size_t mlp_backward_workspace_floats(int B, int H, int L, int d, int mb);
+hipError_t launch_mlp_backward(const MLPBwdArgs &a, hipStream_t stream);
 hipError_t launch_mlp(const MLPArgs &a, hipStream_t stream);
 bool mlp_mfma_supported(const MLPArgs &a);
 hipError_t launch_mlp_mfma(const MLPArgs &a, hipStream_t stream);

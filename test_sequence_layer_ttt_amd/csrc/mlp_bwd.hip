@@ -1,0 +1,751 @@
+// Backward of the TTT-MLP inner loop (d = 64, hidden m = 4d = 256, exact
+// GELU; the lryc.cn TTT article §2.1 model, the mini-batch rule and dual form
+// of the damodev.csdn.net deep-dive §4.1-4.2, trained through the inner loop as
+// in its §6 and §7.1): gradients of
+//   loss = <dO, O> + <dW1', W1_L> + <db1', b1_L> + <dW2', W2_L> + <db2', b2_L>
+// with respect to XQ, XK, XV, eta, the initial state W1, b1, W2, b2, gamma and
+// beta.
+//
+// Per chunk (state W1, b1, W2, b2 at the chunk start, rows = tokens, P = GELU'):
+//   Z1 = XK W1 + b1,  A = gelu(Z1),  Z2 = A W2 + b2,  G2 = lnl2(Z2, XV - XK),
+//   E2 = -eta * G2,  Q = E2 W2^T,  E1 = Q * P(Z1)         (the chunk-start gradients)
+//   T1 = tril(XQ XK^T + 1),  Zb1 = XQ W1 + b1 + T1 E1,  Ab = gelu(Zb1),
+//   T2 = tril(Ab A^T + 1),   Zb2 = Ab W2 + b2 + T2 E2,  O = XQ + LN(Zb2),
+//   W1' = W1 + XK^T E1,  b1' = b1 + 1^T E1,  W2' = W2 + A^T E2,  b2' = b2 + 1^T E2.
+// Reverse, given dO and the adjoints dW1', db1', dW2', db2' of the next state:
+//   dZb2 = LN backward of dO;  dT2 = tril(dZb2 E2^T);
+//   dAb = dZb2 W2^T + dT2 A;  dZb1 = dAb * P(Zb1);  dT1 = tril(dZb1 E1^T);
+//   dE2 = T2^T dZb2 + A dW2' + 1 db2'^T + dQ W2,   with
+//   dE1 = T1^T dZb1 + XK dW1' + 1 db1'^T,  dQ = dE1 * P(Z1);
+//   deta = -rowsum(G2 * dE2);  (dZ2, dtau) = reverse of lnl2 for dG2 = -eta dE2;
+//   dA = dT2^T Ab + E2 dW2'^T + dZ2 W2^T;
+//   dZ1 = dA * P(Z1) + dE1 * Q * GELU''(Z1),  GELU''(x) = phi(x) (2 - x^2);
+//   dXQ = dO + dZb1 W1^T + dT1 XK;  dXK = dT1^T XQ + E1 dW1'^T + dZ1 W1^T - dtau;
+//   dXV = dtau;
+//   dW1 = dW1' + XQ^T dZb1 + XK^T dZ1;       db1 = db1' + 1^T (dZb1 + dZ1);
+//   dW2 = dW2' + Ab^T dZb2 + dQ^T E2 + A^T dZ2;  db2 = db2' + 1^T (dZb2 + dZ2).
+// lnl2 and its reverse are the closed forms of the TTT-Linear backward.
+//
+// One 512-thread workgroup (8 waves) per sequence, fp32 throughout: every
+// product on 16x16x4 fp32 MFMAs (lane (g, c) of a wave supplies row c of the
+// left operand and column c of the right one at contraction index g of each
+// step; the result tile's rows 4g..4g+3 of column c come back). Wave w owns
+// the hidden units 32w..32w+31: it computes their [16 x 32] slices of every
+// hidden-width tile and keeps them in registers, where a tile in the result
+// layout is directly an operand of a product that contracts over the tokens
+// (the contraction order permuted identically on both sides). Products that
+// contract over the hidden units split them in two halves: wave w computes the
+// half w / 4 of 16-feature tile w % 4 and the two partial tiles are summed by
+// their reader. Hidden tiles read across waves or transposed go through LDS.
+//
+// A forward sweep stores the state at every chunk start in the workspace;
+// the reverse sweep reads each chunk's state from there and keeps the running
+// adjoint state in two workspace buffers used alternately (read the one,
+// write the other), so no state matrix occupies LDS.
+#include "common.hpp"
+
+#include "launch.hpp"
+#include "tile.hpp"
+
+namespace ttt {
+namespace {
+
+constexpr int D = 64, M = 4 * D, NT = 512, RW = 16, NF = D / RW;
+constexpr int DP = D + 1, MP = M + 1, TP = RW + 1;
+constexpr int CK = 2 * D * M + M + D;  // floats of one state: W1 [D][M], b1 [M], W2 [M][D], b2 [D]
+constexpr int OB1 = D * M, OW2 = D * M + M, OB2 = 2 * D * M + M;
+#ifndef UNR
+#define UNR 4  // unroll of the loops with global operands (bounds the loads in flight)
+#endif
+
+using tile::f32x4;
+
+struct MlpBwdSmem {
+    // [16 x D] token-row tiles
+    float XQ[RW * DP], XK[RW * DP], dO[RW * DP], E2[RW * DP], dZb2[RW * DP], dZ2[RW * DP], dtau[RW * DP];
+    float part[2][RW * DP], partE[2][RW * DP], partK[2][RW * DP];  // two hidden halves
+    // [16 x M] hidden tiles
+    float HA[RW * MP], HB[RW * MP], HE[RW * MP], HX[RW * MP], HY[RW * MP];
+    // [16 x 16] token-token tiles and per-wave partials
+    float T1[RW * TP], T2[RW * TP], dT1[RW * TP];
+    float gp[NT / 64][RW * TP];
+};
+
+__device__ __forceinline__ f32x4 mf(float a, float b, f32x4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+}
+
+// Global access as a uniform base plus a 32-bit byte offset per lane, the
+// form the scalar-base addressing of global loads and stores takes (one VGPR
+// per address instead of a 64-bit pair).
+__device__ __forceinline__ float gld(const float *base, unsigned idx) {
+    return *reinterpret_cast<const float *>(reinterpret_cast<const char *>(base) + (idx << 2));
+}
+__device__ __forceinline__ void gst(float *base, unsigned idx, float v) {
+    *reinterpret_cast<float *>(reinterpret_cast<char *>(base) + (idx << 2)) = v;
+}
+
+__device__ __forceinline__ float gelu2_f(float x) {  // GELU''(x) = phi(x) (2 - x^2)
+    return 0.39894228040143268f * __expf(-0.5f * x * x) * (2.0f - x * x);
+}
+
+template <typename TIO>
+__global__ __launch_bounds__(NT) void mlp_backward_kernel(
+    int H, int L, int mb, float eps, const TIO *__restrict__ XQ, const TIO *__restrict__ XK,
+    const TIO *__restrict__ XV, const float *__restrict__ eta, const float *__restrict__ W1_0,
+    const float *__restrict__ b1_0, const float *__restrict__ W2_0, const float *__restrict__ b2_0,
+    int w0_batched, const float *__restrict__ gamma, const float *__restrict__ beta,
+    const float *__restrict__ dO, const float *__restrict__ dW1_out, const float *__restrict__ db1_out,
+    const float *__restrict__ dW2_out, const float *__restrict__ db2_out, float *__restrict__ dXQ,
+    float *__restrict__ dXK, float *__restrict__ dXV, float *__restrict__ deta, float *__restrict__ dW1,
+    float *__restrict__ db1, float *__restrict__ dW2, float *__restrict__ db2,
+    float *__restrict__ dgamma, float *__restrict__ dbeta, float *__restrict__ ws) {
+    constexpr float inv_d = 1.0f / D;
+    using io = io_traits<TIO>;
+    __shared__ MlpBwdSmem sm;
+
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
+    const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index as a uniform value
+    const int u = wu & 3, hh = wu >> 2;        // feature tile and hidden half of split products
+    const bool rowt = tid < RW * RW;           // row work: 16 lanes per token row
+    const int r = (tid >> 4) & (RW - 1), q = tid & (RW - 1);
+    const long seq = blockIdx.x;
+    const int h = static_cast<int>(seq % H);
+    const long n = seq / H;
+    const int nch = (L + mb - 1) / mb;
+    const size_t sq = static_cast<size_t>(seq);
+    const size_t xbase = sq * L * D;
+    const size_t st = (w0_batched ? static_cast<size_t>(n) * H : 0) + static_cast<size_t>(h);
+    float *wsq = ws + sq * (static_cast<size_t>(nch) + 2) * CK;
+    float *const adj0 = wsq + static_cast<size_t>(nch) * CK, *const adj1 = adj0 + CK;
+    auto adj = [&](int k) { return (k & 1) ? adj1 : adj0; };
+    const f32x4 fz = {0.f, 0.f, 0.f, 0.f};
+    const int hc0 = 32 * wu + c;  // this lane's hidden column in own tile j: hc0 + 16 j
+    // Global addresses are a uniform pointer plus one of a few per-lane offsets
+    // (elements), so that the per-lane part stays one register per pattern.
+    const unsigned la = g * M + c, lb = c * D + g, lc = g * D + c, ld = c * M + g;
+    const unsigned le = 4 * g * M + c, lf = 4 * g * D + c;
+
+    float gm[NF], bt[NF];
+#pragma unroll
+    for (int k = 0; k < NF; ++k) {
+        gm[k] = gamma[h * D + q + RW * k];
+        bt[k] = beta[h * D + q + RW * k];
+    }
+
+    // ---------------------------------------------------------------- products
+    // own hidden tile j of X [16 x D] (LDS) times W [D x M] (global, row-major)
+    auto x_w = [&](const float *X, const float *W, int j, f32x4 acc) {
+#pragma unroll UNR
+        for (int kb = 0; kb < D / 4; ++kb)
+            acc = mf(X[c * DP + 4 * kb + g], gld(W + 4 * kb * M + 32 * wu + 16 * j, la), acc);
+        return acc;
+    };
+    // own hidden tile j of X [16 x D] (LDS) times V^T, V [M x D] (global, row-major)
+    auto x_vt = [&](const float *X, const float *V, int j, f32x4 acc) {
+#pragma unroll UNR
+        for (int kb = 0; kb < D / 4; ++kb)
+            acc = mf(X[c * DP + 4 * kb + g], gld(V + (32 * wu + 16 * j) * D + 4 * kb, lb), acc);
+        return acc;
+    };
+    // feature tile u over hidden half hh of Y [16 x M] (LDS) times V [M x D] (global)
+    auto y_v = [&](const float *Y, const float *V, f32x4 acc) {
+#pragma unroll UNR
+        for (int kb = 0; kb < M / 8; ++kb) {
+            const int k0 = M / 2 * hh + 4 * kb;
+            acc = mf(Y[c * MP + k0 + g], gld(V + k0 * D + 16 * u, lc), acc);
+        }
+        return acc;
+    };
+    // the same with a token-token tile: [16 x 16] (LDS, transposed if tr) times X [16 x D]
+    auto t_x = [&](const float *T, bool tr, const float *X, f32x4 acc) {
+#pragma unroll
+        for (int kb = 0; kb < RW / 4; ++kb) {
+            const int k = 4 * kb + g;
+            acc = mf(tr ? T[k * TP + c] : T[c * TP + k], X[k * DP + 16 * u + c], acc);
+        }
+        return acc;
+    };
+    // own hidden tile of T^T Hj: rows of T (LDS) contracted with the register tile Hj
+    auto tt_h = [&](const float *T, f32x4 Hj, f32x4 acc) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = mf(T[(4 * g + i) * TP + c], Hj[i], acc);
+        return acc;
+    };
+    // [D x M] update tile (rb, j) += X^T Hj over the tokens (X [16 x D] in LDS)
+    auto xt_h = [&](const float *X, int rb, f32x4 Hj, f32x4 acc) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = mf(X[(4 * g + i) * DP + 16 * rb + c], Hj[i], acc);
+        return acc;
+    };
+    // [M x D] update tile (j, uu) += Hj^T Y over the tokens (Y [16 x D] in LDS)
+    auto ht_y = [&](f32x4 Hj, const float *Y, int uu, f32x4 acc) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = mf(Hj[i], Y[(4 * g + i) * DP + 16 * uu + c], acc);
+        return acc;
+    };
+    auto put_h = [&](float *Hs, int j, f32x4 v) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Hs[(4 * g + i) * MP + hc0 + 16 * j] = v[i];
+    };
+    auto put_d = [&](float *P, f32x4 v) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) P[(4 * g + i) * DP + 16 * u + c] = v[i];
+    };
+    auto get_d = [&](const float *P) {
+        f32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = P[(4 * g + i) * DP + 16 * u + c];
+        return v;
+    };
+    auto bcast = [](float x) { return f32x4{x, x, x, x}; };
+    // token-token tile from per-wave partials: T[t][s] = sum + add on s <= t < m, else 0
+    auto tri_sum = [&](float *T, int nparts, float add, int m) {
+        if (tid < RW * RW) {
+            const int t = tid >> 4, s = tid & 15;
+            float v = 0.f;
+            for (int k = 0; k < nparts; ++k) v += sm.gp[k][t * TP + s];
+            T[t * TP + s] = (s <= t && t < m) ? v + add : 0.f;
+        }
+    };
+    auto rowz2 = [&](const float *P0, const float *P1, float (&z)[NF]) {
+#pragma unroll
+        for (int k = 0; k < NF; ++k) z[k] = P0[r * DP + q + RW * k] + P1[r * DP + q + RW * k];
+    };
+
+    // layer-norm L2 gradient of one row (16 lanes) and what its reverse needs
+    struct Lnl2 {
+        float xh[NF], gh[NF], G[NF];
+        float sigma, c;
+    };
+    auto lnl2 = [&](const float (&z)[NF], const float (&tau)[NF], Lnl2 &s) {
+        float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+        for (int k = 0; k < NF; ++k) s1 += z[k];
+        const float mu = tile::row16_sum(s1) * inv_d;
+#pragma unroll
+        for (int k = 0; k < NF; ++k) s2 += (z[k] - mu) * (z[k] - mu);
+        s.sigma = sqrtf(tile::row16_sum(s2) * inv_d + eps);
+        const float rs = 1.0f / s.sigma;
+        float sa = 0.f, sc = 0.f;
+#pragma unroll
+        for (int k = 0; k < NF; ++k) {
+            s.xh[k] = (z[k] - mu) * rs;
+            s.gh[k] = gm[k] * fmaf(gm[k], s.xh[k], bt[k] - tau[k]);
+            sa += s.gh[k];
+            sc += s.gh[k] * s.xh[k];
+        }
+        const float a = tile::row16_sum(sa) * inv_d;
+        s.c = tile::row16_sum(sc) * inv_d;
+#pragma unroll
+        for (int k = 0; k < NF; ++k) s.G[k] = (s.gh[k] - a - s.xh[k] * s.c) * rs;
+    };
+
+    // Inputs of one chunk for this row thread, fetched a chunk ahead of use;
+    // unconditional loads from a row clamped into the sequence, rows past its
+    // end zeroed when staged.
+    struct Rows {
+        TIO xq[NF], xk[NF], xv[NF];
+        float go[NF], et;
+        bool ok;
+    };
+    auto fetch_rows = [&](int ch, bool rev, Rows &R) {
+        R.ok = r < min(mb, L - ch * mb);
+        const int rr = R.ok ? r : 0;
+        const size_t row = xbase + static_cast<size_t>(ch * mb + rr) * D;
+#pragma unroll
+        for (int k = 0; k < NF; ++k) {
+            const int f = q + RW * k;
+            R.xk[k] = XK[row + f];
+            R.xv[k] = XV[row + f];
+            if (rev) {
+                R.xq[k] = XQ[row + f];
+                R.go[k] = dO[row + f];
+            }
+        }
+        R.et = eta[sq * L + ch * mb + rr];
+    };
+    auto stage_rows = [&](const Rows &R, bool rev, float (&tau)[NF], float &et, float (&go)[NF]) {
+#pragma unroll
+        for (int k = 0; k < NF; ++k) {
+            const int f = q + RW * k;
+            const float xk = R.ok ? io::load(R.xk, k) : 0.f;
+            sm.XK[r * DP + f] = xk;
+            tau[k] = R.ok ? io::load(R.xv, k) - xk : 0.f;
+            if (rev) {
+                sm.XQ[r * DP + f] = R.ok ? io::load(R.xq, k) : 0.f;
+                go[k] = R.ok ? R.go[k] : 0.f;
+                sm.dO[r * DP + f] = go[k];
+            }
+        }
+        et = R.ok ? R.et : 0.f;
+    };
+
+    // ======================= forward sweep: chunk-start states ===================
+    {
+        const float *s1 = W1_0 + st * D * M, *s2 = b1_0 + st * M, *s3 = W2_0 + st * M * D, *s4 = b2_0 + st * D;
+        for (int i = tid; i < D * M; i += NT) {
+            wsq[i] = s1[i];
+            wsq[OW2 + i] = s3[i];
+        }
+        if (tid < M) wsq[OB1 + tid] = s2[tid];
+        if (tid < D) wsq[OB2 + tid] = s4[tid];
+    }
+    Rows R;
+    if (rowt && nch > 1) fetch_rows(0, false, R);
+    __syncthreads();
+    for (int ch = 0; ch + 1 < nch; ++ch) {
+        const float *S = wsq + static_cast<size_t>(ch) * CK;
+        float *Sn = wsq + static_cast<size_t>(ch + 1) * CK;
+        float tau[NF], et = 0.f, go_unused[NF];
+        if (rowt) {
+            stage_rows(R, false, tau, et, go_unused);
+            if (ch + 2 < nch) fetch_rows(ch + 1, false, R);
+        }
+        __syncthreads();
+        // Z1 = XK W1 + b1 on the own hidden tiles; A = gelu(Z1), P = gelu'(Z1)
+        f32x4 Ar[2], Pr[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const f32x4 z = x_w(sm.XK, S, j, bcast(gld(S + OB1 + 32 * wu + 16 * j, c)));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                Ar[j][i] = gelu_f(z[i]);
+                Pr[j][i] = gelu_prime_f(z[i]);
+            }
+            put_h(sm.HA, j, Ar[j]);
+        }
+        __syncthreads();
+        // Z2 = A W2 + b2, the two hidden halves
+        put_d(sm.part[hh], y_v(sm.HA, S + OW2, hh == 0 ? bcast(gld(S + OB2 + 16 * u, c)) : fz));
+        __syncthreads();
+        if (rowt) {  // E2 = -eta lnl2(Z2, XV - XK)
+            float z[NF];
+            rowz2(sm.part[0], sm.part[1], z);
+            Lnl2 s;
+            lnl2(z, tau, s);
+#pragma unroll
+            for (int k = 0; k < NF; ++k) sm.E2[r * DP + q + RW * k] = -et * s.G[k];
+        }
+        __syncthreads();
+        // E1 = (E2 W2^T) * P;  W1 += XK^T E1, b1 += 1^T E1;  W2 += A^T E2, b2 += 1^T E2
+        f32x4 E1r[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const f32x4 qv = x_vt(sm.E2, S + OW2, j, fz);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) E1r[j][i] = qv[i] * Pr[j][i];
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                f32x4 acc;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = gld(S + (16 * rb + i) * M + 32 * wu + 16 * j, le);
+                acc = xt_h(sm.XK, rb, E1r[j], acc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) gst(Sn + (16 * rb + i) * M + 32 * wu + 16 * j, le, acc[i]);
+            }
+            const float cs = tile::rows4_sum((E1r[j][0] + E1r[j][1]) + (E1r[j][2] + E1r[j][3]));
+            if (g == 0) gst(Sn + OB1 + 32 * wu + 16 * j, c, gld(S + OB1 + 32 * wu + 16 * j, c) + cs);
+#pragma unroll
+            for (int uu = 0; uu < 4; ++uu) {
+                f32x4 acc;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = gld(S + OW2 + (32 * wu + 16 * j + i) * D + 16 * uu, lf);
+                acc = ht_y(Ar[j], sm.E2, uu, acc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) gst(Sn + OW2 + (32 * wu + 16 * j + i) * D + 16 * uu, lf, acc[i]);
+            }
+        }
+        if (tid < D) {
+            float cs = 0.f;
+            for (int t = 0; t < RW; ++t) cs += sm.E2[t * DP + tid];
+            Sn[OB2 + tid] = S[OB2 + tid] + cs;
+        }
+        __syncthreads();  // the new state is complete before the next chunk reads it
+    }
+
+    // ============================== reverse sweep ==================================
+    // the adjoint of the final state: the caller's dW1', db1', dW2', db2' (zero if absent)
+    float *a0 = adj(nch - 1);
+    if (nch > 0) {
+        for (int i = tid; i < D * M; i += NT) {
+            a0[i] = dW1_out ? dW1_out[sq * D * M + i] : 0.f;
+            a0[OW2 + i] = dW2_out ? dW2_out[sq * M * D + i] : 0.f;
+        }
+        if (tid < M) a0[OB1 + tid] = db1_out ? db1_out[sq * M + tid] : 0.f;
+        if (tid < D) a0[OB2 + tid] = db2_out ? db2_out[sq * D + tid] : 0.f;
+    } else {  // no tokens: the state passes through unchanged
+        for (int i = tid; i < D * M; i += NT) {
+            dW1[sq * D * M + i] = dW1_out ? dW1_out[sq * D * M + i] : 0.f;
+            dW2[sq * M * D + i] = dW2_out ? dW2_out[sq * M * D + i] : 0.f;
+        }
+        if (tid < M) db1[sq * M + tid] = db1_out ? db1_out[sq * M + tid] : 0.f;
+        if (tid < D) db2[sq * D + tid] = db2_out ? db2_out[sq * D + tid] : 0.f;
+    }
+    float dg_acc[NF], db_acc[NF];
+#pragma unroll
+    for (int k = 0; k < NF; ++k) dg_acc[k] = db_acc[k] = 0.f;
+
+    if (rowt && nch > 0) fetch_rows(nch - 1, true, R);
+    for (int ch = nch - 1; ch >= 0; --ch) {
+        const int m = min(mb, L - ch * mb);
+        const bool ok = r < m;
+        const float *S = wsq + static_cast<size_t>(ch) * CK;
+        const float *Ad = adj(ch);  // adjoint of this chunk's end state
+        float *dst1 = ch > 0 ? adj(ch + 1) : dW1 + sq * D * M;
+        float *dstb1 = ch > 0 ? adj(ch + 1) + OB1 : db1 + sq * M;
+        float *dst2 = ch > 0 ? adj(ch + 1) + OW2 : dW2 + sq * M * D;
+        float *dstb2 = ch > 0 ? adj(ch + 1) + OB2 : db2 + sq * D;
+        __syncthreads();  // the previous chunk is done with every tile and its adjoint writes
+        float tau[NF], et = 0.f, go[NF];
+        if (rowt) {
+            stage_rows(R, true, tau, et, go);
+            if (ch > 0) fetch_rows(ch - 1, true, R);
+        }
+        __syncthreads();
+
+        // Z1 = XK W1 + b1 and XQ W1 + b1 on the own hidden tiles; T1 slices
+        f32x4 Ar[2], Pr[2], Rr[2], ZQ[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const float b = gld(S + OB1 + 32 * wu + 16 * j, c);
+            f32x4 z = bcast(b), zq = bcast(b);
+#pragma unroll UNR
+            for (int kb = 0; kb < D / 4; ++kb) {
+                const float wv = gld(S + 4 * kb * M + 32 * wu + 16 * j, la);
+                z = mf(sm.XK[c * DP + 4 * kb + g], wv, z);
+                zq = mf(sm.XQ[c * DP + 4 * kb + g], wv, zq);
+            }
+            ZQ[j] = zq;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                Ar[j][i] = gelu_f(z[i]);
+                Pr[j][i] = gelu_prime_f(z[i]);
+                Rr[j][i] = gelu2_f(z[i]);
+            }
+            put_h(sm.HA, j, Ar[j]);
+        }
+        if (w < 4) {  // T1 slice over features 16w..16w+15
+            f32x4 t4 = fz;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                t4 = mf(sm.XQ[c * DP + 16 * w + 4 * kb + g], sm.XK[c * DP + 16 * w + 4 * kb + g], t4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm.gp[w][(4 * g + i) * TP + c] = t4[i];
+        }
+        __syncthreads();
+
+        // Z2 = A W2 + b2 (two halves);  T1 = tril(XQ XK^T + 1)
+        put_d(sm.part[hh], y_v(sm.HA, S + OW2, hh == 0 ? bcast(gld(S + OB2 + 16 * u, c)) : fz));
+        tri_sum(sm.T1, 4, 1.f, m);
+        __syncthreads();
+
+        Lnl2 s;
+        if (rowt) {  // E2 = -eta lnl2(Z2, XV - XK)
+            float z[NF];
+            rowz2(sm.part[0], sm.part[1], z);
+            lnl2(z, tau, s);
+#pragma unroll
+            for (int k = 0; k < NF; ++k) sm.E2[r * DP + q + RW * k] = -et * s.G[k];
+        }
+        __syncthreads();
+
+        // Q = E2 W2^T, E1 = Q * P;  Zb1 = XQ W1 + b1 + T1 E1, Ab = gelu(Zb1), Pb = gelu'(Zb1)
+        f32x4 E1r[2], Abr[2], Pbr[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const f32x4 qv = x_vt(sm.E2, S + OW2, j, fz);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                E1r[j][i] = qv[i] * Pr[j][i];
+                Rr[j][i] *= qv[i];  // Q * GELU''(Z1), the factor of dE1 in dZ1
+            }
+            put_h(sm.HE, j, E1r[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            f32x4 zb = ZQ[j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) zb = mf(sm.T1[c * TP + 4 * g + i], E1r[j][i], zb);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                Abr[j][i] = gelu_f(zb[i]);
+                Pbr[j][i] = gelu_prime_f(zb[i]);
+            }
+            put_h(sm.HB, j, Abr[j]);
+        }
+        __syncthreads();
+
+        // Ab W2 + b2 (two halves); slices of the Gram Ab A^T over the own hidden units
+        put_d(sm.part[hh], y_v(sm.HB, S + OW2, hh == 0 ? bcast(gld(S + OB2 + 16 * u, c)) : fz));
+        {
+            f32x4 t4 = fz;
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb)
+                t4 = mf(sm.HB[c * MP + 32 * w + 4 * kb + g], sm.HA[c * MP + 32 * w + 4 * kb + g], t4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm.gp[w][(4 * g + i) * TP + c] = t4[i];
+        }
+        __syncthreads();
+        tri_sum(sm.T2, NT / 64, 1.f, m);  // T2 = tril(Ab A^T + 1)
+        __syncthreads();
+
+        if (rowt) {  // Zb2 = Ab W2 + b2 + T2 E2;  dZb2 = LN backward of dO
+            float zb[NF];
+            rowz2(sm.part[0], sm.part[1], zb);
+#pragma unroll
+            for (int s2 = 0; s2 < RW; ++s2) {
+                const float tv = sm.T2[r * TP + s2];
+#pragma unroll
+                for (int k = 0; k < NF; ++k) zb[k] = fmaf(tv, sm.E2[s2 * DP + q + RW * k], zb[k]);
+            }
+            float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+            for (int k = 0; k < NF; ++k) s1 += zb[k];
+            const float mu = tile::row16_sum(s1) * inv_d;
+#pragma unroll
+            for (int k = 0; k < NF; ++k) s2 += (zb[k] - mu) * (zb[k] - mu);
+            const float rs = 1.0f / sqrtf(tile::row16_sum(s2) * inv_d + eps);
+            float xb[NF], dx[NF], m1 = 0.f, m2 = 0.f;
+#pragma unroll
+            for (int k = 0; k < NF; ++k) {
+                xb[k] = (zb[k] - mu) * rs;
+                dx[k] = gm[k] * go[k];
+                dg_acc[k] = fmaf(go[k], xb[k], dg_acc[k]);
+                db_acc[k] += go[k];
+                m1 += dx[k];
+                m2 += dx[k] * xb[k];
+            }
+            m1 = tile::row16_sum(m1) * inv_d;
+            m2 = tile::row16_sum(m2) * inv_d;
+#pragma unroll
+            for (int k = 0; k < NF; ++k) sm.dZb2[r * DP + q + RW * k] = (dx[k] - m1 - xb[k] * m2) * rs;
+        }
+        __syncthreads();
+
+        // dT2 = tril(dZb2 E2^T) (every wave its own copy, result layout: row t = 4g+i, column s = c)
+        f32x4 dt2 = fz;
+#pragma unroll
+        for (int kb = 0; kb < D / 4; ++kb) dt2 = mf(sm.dZb2[c * DP + 4 * kb + g], sm.E2[c * DP + 4 * kb + g], dt2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (c > 4 * g + i) dt2[i] = 0.f;
+            sm.gp[w][(4 * g + i) * TP + c] = dt2[i];
+        }
+        // dAb = dZb2 W2^T + dT2 A, dZb1 = dAb * Pb;  dA (first part) = dT2^T Ab
+        f32x4 dZb1r[2], dAr[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            f32x4 v = x_vt(sm.dZb2, S + OW2, j, fz);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v = mf(sm.gp[w][c * TP + 4 * g + i], Ar[j][i], v);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dZb1r[j][i] = v[i] * Pbr[j][i];
+            put_h(sm.HX, j, dZb1r[j]);
+            f32x4 a = fz;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a = mf(dt2[i], Abr[j][i], a);
+            dAr[j] = a;
+        }
+        // dE2 (first parts) = A dW2' + T2^T dZb2 + db2' (two halves)
+        {
+            f32x4 e = y_v(sm.HA, Ad + OW2, hh == 0 ? bcast(gld(Ad + OB2 + 16 * u, c)) : fz);
+            if (hh == 0) e = t_x(sm.T2, true, sm.dZb2, e);
+            put_d(sm.partE[hh], e);
+        }
+        __syncthreads();
+
+        // slices of dT1 = dZb1 E1^T over the own hidden units;
+        // dE1 = T1^T dZb1 + XK dW1' + db1' (zero on rows past the chunk), dQ = dE1 * P
+        {
+            f32x4 t4 = fz;
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb)
+                t4 = mf(sm.HX[c * MP + 32 * w + 4 * kb + g], sm.HE[c * MP + 32 * w + 4 * kb + g], t4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm.gp[w][(4 * g + i) * TP + c] = t4[i];
+        }
+        f32x4 dQr[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            f32x4 de = x_w(sm.XK, Ad, j, bcast(gld(Ad + OB1 + 32 * wu + 16 * j, c)));
+            de = tt_h(sm.T1, dZb1r[j], de);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float v = 4 * g + i < m ? de[i] : 0.f;
+                dQr[j][i] = v * Pr[j][i];
+                Rr[j][i] *= v;  // dE1 * Q * GELU''(Z1)
+            }
+            put_h(sm.HY, j, dQr[j]);
+        }
+        __syncthreads();
+
+        // dT1 = tril(sum of the slices);  dE2 += dQ W2 (two halves)
+        tri_sum(sm.dT1, NT / 64, 0.f, m);
+        put_d(sm.partE[hh], y_v(sm.HY, S + OW2, get_d(sm.partE[hh])));
+        __syncthreads();
+
+        if (rowt) {  // deta = -G2 . dE2;  dG2 = -eta dE2;  reverse of lnl2 -> dZ2, dtau
+            float de[NF];
+            rowz2(sm.partE[0], sm.partE[1], de);
+            float pe = 0.f;
+#pragma unroll
+            for (int k = 0; k < NF; ++k) pe = fmaf(s.G[k], de[k], pe);
+            const float d_eta = -tile::row16_sum(pe);
+            float dG[NF], mdg = 0.f, mdgx = 0.f, sgG = 0.f;
+#pragma unroll
+            for (int k = 0; k < NF; ++k) {
+                dG[k] = -et * de[k];
+                mdg += dG[k];
+                mdgx += dG[k] * s.xh[k];
+                sgG += dG[k] * s.G[k];
+            }
+            mdg = tile::row16_sum(mdg) * inv_d;
+            mdgx = tile::row16_sum(mdgx) * inv_d;
+            const float rs = 1.0f / s.sigma;
+            const float dsig = -tile::row16_sum(sgG) * rs;
+            float dxh[NF], mdx = 0.f, mdxx = 0.f;
+#pragma unroll
+            for (int k = 0; k < NF; ++k) {
+                const float dgh = (dG[k] - mdg - s.xh[k] * mdgx) * rs;
+                dxh[k] = gm[k] * gm[k] * dgh - (s.c * dG[k] + s.gh[k] * mdgx) * rs;
+                sm.dtau[r * DP + q + RW * k] = ok ? -gm[k] * dgh : 0.f;
+                dg_acc[k] = fmaf(dgh, fmaf(2.f * gm[k], s.xh[k], bt[k] - tau[k]), dg_acc[k]);
+                db_acc[k] = fmaf(gm[k], dgh, db_acc[k]);
+                mdx += dxh[k];
+                mdxx += dxh[k] * s.xh[k];
+            }
+            mdx = tile::row16_sum(mdx) * inv_d;
+            mdxx = tile::row16_sum(mdxx) * inv_d;
+#pragma unroll
+            for (int k = 0; k < NF; ++k) {
+                const float dz = fmaf(dsig * inv_d, s.xh[k], (dxh[k] - mdx - s.xh[k] * mdxx) * rs);
+                sm.dZ2[r * DP + q + RW * k] = ok ? dz : 0.f;
+            }
+            if (ok && q == 0) deta[sq * L + ch * mb + r] = d_eta;
+        }
+        __syncthreads();
+
+        // dA += E2 dW2'^T + dZ2 W2^T;  dZ1 = dA * P + dE1 * Q * GELU'';
+        // the adjoint state of the chunk start: dW2, dW1, db1, db2
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            f32x4 a = x_vt(sm.E2, Ad + OW2, j, dAr[j]);
+            a = x_vt(sm.dZ2, S + OW2, j, a);
+            f32x4 dz1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dz1[i] = fmaf(a[i], Pr[j][i], Rr[j][i]);
+            put_h(sm.HY, j, dz1);
+#pragma unroll
+            for (int uu = 0; uu < 4; ++uu) {  // dW2 = dW2' + Ab^T dZb2 + dQ^T E2 + A^T dZ2
+                f32x4 acc;
+                const int o = (32 * wu + 16 * j) * D + 16 * uu;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = gld(Ad + OW2 + o + i * D, lf);
+                acc = ht_y(Abr[j], sm.dZb2, uu, acc);
+                acc = ht_y(dQr[j], sm.E2, uu, acc);
+                acc = ht_y(Ar[j], sm.dZ2, uu, acc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) gst(dst2 + o + i * D, lf, acc[i]);
+            }
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {  // dW1 = dW1' + XQ^T dZb1 + XK^T dZ1
+                f32x4 acc;
+                const int o = 16 * rb * M + 32 * wu + 16 * j;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = gld(Ad + o + i * M, le);
+                acc = xt_h(sm.XQ, rb, dZb1r[j], acc);
+                acc = xt_h(sm.XK, rb, dz1, acc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) gst(dst1 + o + i * M, le, acc[i]);
+            }
+            const float cs = tile::rows4_sum((dZb1r[j][0] + dz1[0]) + (dZb1r[j][1] + dz1[1]) +
+                                             ((dZb1r[j][2] + dz1[2]) + (dZb1r[j][3] + dz1[3])));
+            if (g == 0) gst(dstb1 + 32 * wu + 16 * j, c, gld(Ad + OB1 + 32 * wu + 16 * j, c) + cs);
+        }
+        if (tid < D) {
+            float cs = 0.f;
+            for (int t = 0; t < RW; ++t) cs += sm.dZb2[t * DP + tid] + sm.dZ2[t * DP + tid];
+            gst(dstb2, tid, gld(Ad, OB2 + tid) + cs);
+        }
+        __syncthreads();
+
+        // dXQ = dO + dZb1 W1^T + dT1 XK;  dXK = dT1^T XQ + E1 dW1'^T + dZ1 W1^T - dtau (halves)
+        {
+            f32x4 aq = hh == 0 ? t_x(sm.dT1, false, sm.XK, fz) : fz;
+            f32x4 ak = hh == 0 ? t_x(sm.dT1, true, sm.XQ, fz) : fz;
+#pragma unroll UNR
+            for (int kb = 0; kb < M / 8; ++kb) {
+                const int k0 = M / 2 * hh + 4 * kb, k = k0 + g;
+                const float w1t = gld(S + 16 * u * M + k0, ld), a1t = gld(Ad + 16 * u * M + k0, ld);
+                aq = mf(sm.HX[c * MP + k], w1t, aq);
+                ak = mf(sm.HY[c * MP + k], w1t, ak);
+                ak = mf(sm.HE[c * MP + k], a1t, ak);
+            }
+            put_d(sm.part[hh], aq);
+            put_d(sm.partK[hh], ak);
+        }
+        __syncthreads();
+        for (int e = tid; e < RW * D; e += NT) {
+            const int t = e / D, f = e % D;
+            if (t < m) {
+                const size_t at = xbase + static_cast<size_t>(ch * mb + t) * D + f;
+                const float dt = sm.dtau[t * DP + f];
+                dXQ[at] = sm.part[0][t * DP + f] + sm.part[1][t * DP + f] + sm.dO[t * DP + f];
+                dXK[at] = sm.partK[0][t * DP + f] + sm.partK[1][t * DP + f] - dt;
+                dXV[at] = dt;
+            }
+        }
+    }
+    __syncthreads();
+
+    // per-sequence dgamma, dbeta: sum the 16 row groups
+    float *red = sm.HA;
+    if (rowt) {
+#pragma unroll
+        for (int k = 0; k < NF; ++k) {
+            red[r * D + q + RW * k] = dg_acc[k];
+            red[RW * D + r * D + q + RW * k] = db_acc[k];
+        }
+    }
+    __syncthreads();
+    if (tid < D) {
+        float a = 0.f, b = 0.f;
+        for (int rr = 0; rr < RW; ++rr) {
+            a += red[rr * D + tid];
+            b += red[RW * D + rr * D + tid];
+        }
+        dgamma[sq * D + tid] = a;
+        dbeta[sq * D + tid] = b;
+    }
+}
+
+template <typename TIO>
+hipError_t launch_t(const MLPBwdArgs &a, hipStream_t stream) {
+    hipLaunchKernelGGL((mlp_backward_kernel<TIO>), dim3(a.f.B * a.f.H), dim3(NT), 0, stream, a.f.H, a.f.L,
+                       a.f.mb, a.f.eps, static_cast<const TIO *>(a.f.XQ), static_cast<const TIO *>(a.f.XK),
+                       static_cast<const TIO *>(a.f.XV), a.f.eta, a.f.W1, a.f.b1, a.f.W2, a.f.b2,
+                       a.f.w0_batched, a.f.gamma, a.f.beta, a.dO, a.dW1_out, a.db1_out, a.dW2_out,
+                       a.db2_out, a.dXQ, a.dXK, a.dXV, a.deta, a.dW1, a.db1, a.dW2, a.db2, a.dgamma,
+                       a.dbeta, a.ws);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t mlp_backward_workspace_floats(int B, int H, int L, int d, int mb) {
+    const size_t nch = L > 0 ? static_cast<size_t>((L + mb - 1) / mb) : 0;
+    const size_t ck = 2 * static_cast<size_t>(d) * 4 * d + 4 * static_cast<size_t>(d) + d;
+    return static_cast<size_t>(B) * H * (nch + 2) * ck;
+}
+
+hipError_t launch_mlp_backward(const MLPBwdArgs &a, hipStream_t stream) {
+    if (a.f.B * a.f.H == 0) return hipSuccess;
+    if (a.f.d != D) return hipErrorInvalidValue;
+    return a.f.io ? launch_t<bf16_t>(a, stream) : launch_t<float>(a, stream);
+}
+
+}  // namespace ttt

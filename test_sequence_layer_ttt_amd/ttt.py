@@ -251,6 +251,67 @@ def ttt_linear_backward(XQ, XK, XV, eta, W0, b0, ln_gamma, ln_beta, dO, dW_out=N
     return g
 
 
+def ttt_mlp_backward_workspace(B: int, H: int, L: int, d: int, mb: int = 16) -> int:
+    """Bytes of device workspace ttt_mlp_backward needs."""
+    n = ctypes.c_size_t(0)
+    lib = _lib.load()
+    _lib.check(lib.ttt_mlp_backward_workspace(B, H, L, d, mb, ctypes.byref(n)))
+    return n.value
+
+
+def ttt_mlp_backward(XQ, XK, XV, eta, W1, b1, W2, b2, ln_gamma, ln_beta, dO, dW1_out=None,
+                     db1_out=None, dW2_out=None, db2_out=None, mb: int = 16, ln_eps: float = 1e-6,
+                     workspace=None, stream=None) -> dict:
+    """Gradients of <dO,O> + <dW1_out,W1_L> + <db1_out,b1_L> + <dW2_out,W2_L> +
+    <db2_out,b2_L> through ttt_mlp_forward. Inputs as ttt_mlp_forward plus dO
+    [B,H,L,d] fp32 and the optional state adjoints. Returns per-sequence fp32
+    gradients dXQ, dXK, dXV [B,H,L,d], deta [B,H,L], dW1 [B,H,d,4d], db1
+    [B,H,4d], dW2 [B,H,4d,d], db2, dgamma, dbeta [B,H,d]."""
+    B, H, L, d = XQ.shape
+    m = 4 * d
+    io = _IO.get(XQ.dtype)
+    if io is None:
+        raise TypeError(f"XQ dtype {XQ.dtype} not supported")
+    batched = W1.dim() == 4
+    pre = (B,) if batched else ()
+    for t, n in ((XQ, "XQ"), (XK, "XK"), (XV, "XV")):
+        _need(t, n, (B, H, L, d), XQ.dtype)
+    _need(eta, "eta", (B, H, L), torch.float32)
+    _need(W1, "W1", pre + (H, d, m), torch.float32)
+    _need(b1, "b1", pre + (H, m), torch.float32)
+    _need(W2, "W2", pre + (H, m, d), torch.float32)
+    _need(b2, "b2", pre + (H, d), torch.float32)
+    _need(ln_gamma, "ln_gamma", (H, d), torch.float32)
+    _need(ln_beta, "ln_beta", (H, d), torch.float32)
+    _need(dO, "dO", (B, H, L, d), torch.float32)
+    for t, n, shp in ((dW1_out, "dW1_out", (B, H, d, m)), (db1_out, "db1_out", (B, H, m)),
+                      (dW2_out, "dW2_out", (B, H, m, d)), (db2_out, "db2_out", (B, H, d))):
+        if t is not None:
+            _need(t, n, shp, torch.float32)
+    kw = dict(device=XQ.device, dtype=torch.float32)
+    g = {"dXQ": torch.empty((B, H, L, d), **kw), "dXK": torch.empty((B, H, L, d), **kw),
+         "dXV": torch.empty((B, H, L, d), **kw), "deta": torch.empty((B, H, L), **kw),
+         "dW1": torch.empty((B, H, d, m), **kw), "db1": torch.empty((B, H, m), **kw),
+         "dW2": torch.empty((B, H, m, d), **kw), "db2": torch.empty((B, H, d), **kw),
+         "dgamma": torch.empty((B, H, d), **kw), "dbeta": torch.empty((B, H, d), **kw)}
+    need = ttt_mlp_backward_workspace(B, H, L, d, mb)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), device=XQ.device, dtype=torch.uint8)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    lib = _lib.load()
+    _lib.check(lib.ttt_mlp_backward(B, H, L, d, mb, io, ln_eps, _ptr(XQ), _ptr(XK), _ptr(XV),
+                                    _ptr(eta), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2), int(batched),
+                                    _ptr(ln_gamma), _ptr(ln_beta), _ptr(dO), _ptr(dW1_out),
+                                    _ptr(db1_out), _ptr(dW2_out), _ptr(db2_out), _ptr(g["dXQ"]),
+                                    _ptr(g["dXK"]), _ptr(g["dXV"]), _ptr(g["deta"]), _ptr(g["dW1"]),
+                                    _ptr(g["db1"]), _ptr(g["dW2"]), _ptr(g["db2"]),
+                                    _ptr(g["dgamma"]), _ptr(g["dbeta"]), _ptr(workspace), nbytes,
+                                    _stream(stream)))
+    return g
+
+
 def ttt_linear_backward_noalloc(XQ, XK, XV, eta, W0, b0, ln_gamma, ln_beta, dO, dW_out=None,
                                 db_out=None, mb: int = 16, ln_eps: float = 1e-6,
                                 grads=None, stream=None) -> dict:

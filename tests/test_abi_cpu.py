@@ -397,3 +397,49 @@ def test_qkv_project_rejects_bad_arguments(lib):
     assert _proj(lib, ptrs=p[:4] + [p[3]]) == TTT_E_ALIAS           # XV over XK
     # nothing to write: no pointer is needed and nothing is launched
     assert _proj(lib, L=0, ptrs=[0, 0, 0, 0, 0]) == 0
+
+
+def _mbwd(lib, B=2, H=3, L=40, d=64, mb=16, io=1, eps=1e-6, ws_bytes=None, ptrs=None, ws=None,
+          adj=(None, None, None, None)):
+    p = ptrs or [FAKE + i * (1 << 24) for i in range(24)]
+    need = ctypes.c_size_t(0)
+    lib.ttt_mlp_backward_workspace(max(B, 0), max(H, 0), max(L, 0), 64, 16, ctypes.byref(need))
+    nb = need.value if ws_bytes is None else ws_bytes
+    return lib.ttt_mlp_backward(B, H, L, d, mb, io, eps, *p[:8], 0, p[8], p[9], p[10], *adj,
+                                *p[11:21], ws if ws is not None else p[21], nb, None)
+
+
+def test_mlp_backward_workspace_size(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.ttt_mlp_backward_workspace(2, 3, 40, 64, 16, ctypes.byref(n)) == _lib.TTT_OK
+    # ceil(40 / 16) = 3 chunk-start states plus two adjoint states, each W1, b1, W2, b2
+    assert n.value == 2 * 3 * (3 + 2) * (2 * 64 * 256 + 256 + 64) * 4
+    assert lib.ttt_mlp_backward_workspace(1, 1, 0, 64, 16, ctypes.byref(n)) == _lib.TTT_OK
+    assert n.value == 2 * 132352
+    assert lib.ttt_mlp_backward_workspace(2, 3, 40, 16, 16, ctypes.byref(n)) == _lib.TTT_E_SHAPE
+    assert lib.ttt_mlp_backward_workspace(2, 3, 40, 64, 17, ctypes.byref(n)) == _lib.TTT_E_SHAPE
+    assert lib.ttt_mlp_backward_workspace(2, 3, 40, 64, 16, None) == _lib.TTT_E_NULL
+
+
+def test_mlp_backward_validation(lib):
+    assert _mbwd(lib, ws_bytes=4096) == _lib.TTT_E_SHAPE
+    assert "workspace" in lib.ttt_last_error().decode()
+    assert _mbwd(lib, d=16) == _lib.TTT_E_SHAPE
+    assert _mbwd(lib, mb=0) == _lib.TTT_E_SHAPE
+    assert _mbwd(lib, io=3) == _lib.TTT_E_DTYPE
+    assert _mbwd(lib, eps=0.0) == _lib.TTT_E_SHAPE
+    assert _mbwd(lib, L=-1) == _lib.TTT_E_SHAPE
+    p = [FAKE + i * (1 << 24) for i in range(24)]
+    q = list(p); q[11] = p[0]  # dXQ on XQ
+    assert _mbwd(lib, ptrs=q) == _lib.TTT_E_ALIAS
+    q = list(p); q[15] = p[17]  # dW1 on dW2
+    assert _mbwd(lib, ptrs=q) == _lib.TTT_E_ALIAS
+    assert _mbwd(lib, ws=p[13]) == _lib.TTT_E_ALIAS  # workspace on dXV
+    assert _mbwd(lib, adj=(p[15], None, None, None)) == _lib.TTT_E_ALIAS  # dW1_out is dW1
+    q = list(p); q[10] = 0  # dO
+    assert _mbwd(lib, ptrs=q) == _lib.TTT_E_NULL
+    q = list(p); q[20] = 0  # dbeta
+    assert _mbwd(lib, ptrs=q) == _lib.TTT_E_NULL
+    q = list(p); q[4] = p[4] + 2  # W1_0 misaligned
+    assert _mbwd(lib, ptrs=q) == _lib.TTT_E_ALIGN
+    assert _mbwd(lib, B=0) == _lib.TTT_OK  # nothing to do, no HIP call
