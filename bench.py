@@ -23,6 +23,8 @@ Other workloads of the same hot path (--workload):
       gate in the kernel; roofline: fp32 vector ALU)
   3b  TTT-Linear backward (ttt_linear_backward) on workload 3's shapes
       (roofline: fp32 vector ALU)
+  4b  TTT-MLP backward (ttt_mlp_backward) on workload 4's shapes (roofline:
+      fp32 MFMA)
   3g  workload 3 through ttt_linear_forward_gated: eta from the learning-rate
       gate evaluated in the kernel (theta_lr ~ N(0, 0.02^2), eta_base = 1/d)
   3gb ttt_eta_gate_backward on workload 3's keys (dXK += the path through
@@ -48,6 +50,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, datasheet
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, datasheet
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (packed FMA), datasheet
+FP32_MFMA_PEAK_TFLOPS = 157.3    # MI355X dense fp32 MFMA, datasheet
 WORKLOAD = 3
 METRIC = "TTT layer tokens/s (dual-form prefill, L=8192) + % of roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_linear_prefill_workload3.json")
@@ -87,6 +90,22 @@ def alg_flops_linear_backward(B, H, L, d, b=16):
     and the reverse products (dZb W^T, XK dW', E dW'^T, dZ W^T, XQ^T dZb,
     XK^T dZ: 12 d^2; dA, T^T dZb, dA XK, dA^T XQ: 8 b d; T: 2 b d)."""
     return B * H * L * (20 * d * d + 12 * b * d)
+
+
+def alg_flops_mlp_backward(B, H, L, d, b=16):
+    """Algorithmic flops of one ttt_mlp_backward launch per token-head (hidden
+    m = 4d, every product 2 flops per multiply-add):
+      forward pass storing the chunk-start states: Z1, Z2, E2 W2^T and the two
+      state updates, 5 x 2 d m = 40 d^2;
+      recomputed chunk: Z1, XQ W1, Z2, E2 W2^T, Ab W2 (40 d^2), T1 and T2 E2
+      (4 b d), T1 E1 and the Gram Ab A^T (16 b d);
+      reverse products: dZb2 W2^T, A dW2', XK dW1', dQ W2, E2 dW2'^T, dZ2 W2^T,
+      dZb1 W1^T, E1 dW1'^T, dZ1 W1^T and the five adjoint-state updates
+      (Ab^T dZb2, dQ^T E2, A^T dZ2, XQ^T dZb1, XK^T dZ1): 14 x 8 d^2 = 112 d^2;
+      dT2 A, dT2^T Ab, dZb1 E1^T, T1^T dZb1 (32 b d); dZb2 E2^T, T2^T dZb2,
+      dT1 XK, dT1^T XQ (8 b d).
+    Total 192 d^2 + 60 b d."""
+    return B * H * L * (192 * d * d + 60 * b * d)
 
 
 def kernel_sources_hash():
@@ -163,7 +182,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="3", choices=["3", "2", "5p", "4", "4o", "4g", "5d", "5r", "5m", "5g", "3b",
+    ap.add_argument("--workload", default="3", choices=["3", "2", "5p", "4", "4o", "4g", "5d", "5r", "5m", "5g", "3b", "4b",
                              "3g", "3gb", "3o", "3p", "2p"])
     ap.add_argument("--peaks", action="store_true",
                     help="measure achievable HBM copy bandwidth and bf16 GEMM throughput (context)")
@@ -211,6 +230,8 @@ def main():
         return bench_decode_steps(args, gated=True)
     if args.workload == "3b":
         return bench_backward(args)
+    if args.workload == "4b":
+        return bench_mlp_backward(args)
     if args.workload == "3gb":
         return bench_gate_backward(args)
     if args.workload in ("3p", "2p"):
@@ -621,6 +642,52 @@ def bench_backward(args):
            "d": d, "mini_batch": 16, "io": "bf16", "grads": "fp32", "parallelism": "none (1 GPU)"},
           roof, extra)
 
+
+
+def bench_mlp_backward(args):
+    """ttt_mlp_backward on workload 4's shapes (B=2, H=12, L=8192, d=64,
+    hidden 256, b=16, bf16 inputs), with a seeded dO and the state adjoints
+    dW1_out ... db2_out = 0."""
+    import numpy as np
+    import torch
+    from test_sequence_layer_ttt_amd import gen, ttt
+    x = gen.make_workload(4)
+    B, H, L, d = x.B, x.H, x.L, x.d
+    dev = torch.device("cuda:0")
+    T = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev).to(dt)
+    bf = torch.bfloat16
+    ins = [T(x.XQ, bf), T(x.XK, bf), T(x.XV, bf), T(x.eta), T(x.W1), T(x.b1), T(x.W2), T(x.b2),
+           T(x.gamma), T(x.beta)]
+    dO = torch.randn((B, H, L, d), generator=torch.Generator(device="cpu").manual_seed(4),
+                     dtype=torch.float32).to(dev)
+    ws = torch.empty(ttt.ttt_mlp_backward_workspace(B, H, L, d, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    step = lambda: ttt.ttt_mlp_backward(*ins, dO, mb=16, ln_eps=x.eps, workspace=ws, stream=stream)
+    wall, kern = _timed(step, stream, args.warmup, args.steps)
+    fl = alg_flops_mlp_backward(B, H, L, d)
+    roof = {"bound": "mfma", "achieved": fl / kern / 1e12, "peak": FP32_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": fl / kern / 1e12 / FP32_MFMA_PEAK_TFLOPS,
+            "traffic": None, "kernel": "mlp_backward_kernel", "kernel_avg_us": kern * 1e6,
+            "alg_flops_per_launch": fl,
+            "frac_of_busy_cus": fl / kern / 1e12 / (FP32_MFMA_PEAK_TFLOPS * min(B * H, 256) / 256)}
+    extra = {}
+    if not args.no_cpu_baseline:
+        from oracle import grad as OG
+        # bounded sample: one sequence, the first 2048 tokens
+        ns = 2048
+        sl = lambda a: np.ascontiguousarray(a[:1, :1, :ns])
+        t1 = time.perf_counter()
+        OG.mlp_backward(sl(x.XQ), sl(x.XK), sl(x.XV), sl(x.eta), x.W1[:1], x.b1[:1], x.W2[:1],
+                        x.b2[:1], x.gamma[:1], x.beta[:1], x.eps, 16, dO[:1, :1, :ns].cpu().numpy())
+        tc = time.perf_counter() - t1
+        extra["cpu_baseline"] = {"value": ns / tc, "unit": "token-heads/s (one head)",
+                                 "cores": torch.get_num_threads(), "kind": "oracle",
+                                 "sample": f"autograd of the fp64 TTT-MLP primal recurrence, one head, "
+                                           f"{ns} tokens, {tc:.2f} s"}
+    _line("TTT-MLP backward tokens/s (L=8192)", B * L / wall, args, wall, "bf16 in, fp32",
+          {"workload": "ttt_mlp_backward_bf16_B2_H12_L8192_d64", "B": B, "H": H, "L": L, "d": d,
+           "hidden": 4 * d, "mini_batch": 16, "io": "bf16", "grads": "fp32",
+           "parallelism": "none (1 GPU)"}, roof, extra)
 
 
 def bench_gate_backward(args):
