@@ -71,6 +71,19 @@ struct MlpBwdSmem {
     float gp[NT / 64][RW * TP];
 };
 
+// The forward sweep's tiles (the same LDS, reused): XK, A, the two Z2 halves,
+// E2, and a copy of W2 (rows padded to 68 floats: the 16 rows one operand
+// read touches start on distinct banks) for E2 W2^T and A W2.
+constexpr int W2P = D + 4;
+struct MlpFwdSmem {
+    float XK[RW * DP], HA[RW * MP], part[2][RW * DP], E2[RW * DP];
+    float W2[M * W2P], b2[D];
+};
+union MlpSmem {
+    MlpBwdSmem r;
+    MlpFwdSmem f;
+};
+
 __device__ __forceinline__ f32x4 mf(float a, float b, f32x4 acc) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
 }
@@ -102,7 +115,9 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
     float *__restrict__ dgamma, float *__restrict__ dbeta, float *__restrict__ ws) {
     constexpr float inv_d = 1.0f / D;
     using io = io_traits<TIO>;
-    __shared__ MlpBwdSmem sm;
+    __shared__ MlpSmem smu;
+    MlpBwdSmem &sm = smu.r;
+    MlpFwdSmem &sf = smu.f;
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
     const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index as a uniform value
@@ -265,12 +280,12 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
         }
         R.et = eta[sq * L + ch * mb + rr];
     };
-    auto stage_rows = [&](const Rows &R, bool rev, float (&tau)[NF], float &et, float (&go)[NF]) {
+    auto stage_rows = [&](const Rows &R, bool rev, float *xkt, float (&tau)[NF], float &et, float (&go)[NF]) {
 #pragma unroll
         for (int k = 0; k < NF; ++k) {
             const int f = q + RW * k;
             const float xk = R.ok ? io::load(R.xk, k) : 0.f;
-            sm.XK[r * DP + f] = xk;
+            xkt[r * DP + f] = xk;
             tau[k] = R.ok ? io::load(R.xv, k) - xk : 0.f;
             if (rev) {
                 sm.XQ[r * DP + f] = R.ok ? io::load(R.xq, k) : 0.f;
@@ -282,90 +297,124 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
     };
 
     // ======================= forward sweep: chunk-start states ===================
+    // The state stays in registers in the result layout of its updates: wave w
+    // holds W1[16 rb + 4 g + i][32 w + 16 j + c] and W2[32 w + 16 j + 4 g + i][16 uu + c],
+    // which with the contraction order permuted identically is also the right
+    // operand of XK W1. W2 is mirrored in LDS for A W2 and E2 W2^T. Every chunk
+    // start is stored to the workspace (write-only).
+    f32x4 W1r[4][2], W2r[2][4];
+    float b1r[2], b2r = 0.f;
     {
         const float *s1 = W1_0 + st * D * M, *s2 = b1_0 + st * M, *s3 = W2_0 + st * M * D, *s4 = b2_0 + st * D;
-        for (int i = tid; i < D * M; i += NT) {
-            wsq[i] = s1[i];
-            wsq[OW2 + i] = s3[i];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) W1r[rb][j][i] = gld(s1 + (16 * rb + i) * M + 32 * wu + 16 * j, le);
+#pragma unroll
+            for (int uu = 0; uu < 4; ++uu)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) W2r[j][uu][i] = gld(s3 + (32 * wu + 16 * j + i) * D + 16 * uu, lf);
+            b1r[j] = gld(s2 + 32 * wu + 16 * j, c);
         }
-        if (tid < M) wsq[OB1 + tid] = s2[tid];
-        if (tid < D) wsq[OB2 + tid] = s4[tid];
+        if (tid < D) b2r = s4[tid];
     }
+    // the current state to the workspace checkpoint S and to the LDS mirror of W2
+    auto put_state = [&](float *Sn) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) gst(Sn + (16 * rb + i) * M + 32 * wu + 16 * j, le, W1r[rb][j][i]);
+#pragma unroll
+            for (int uu = 0; uu < 4; ++uu)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    gst(Sn + OW2 + (32 * wu + 16 * j + i) * D + 16 * uu, lf, W2r[j][uu][i]);
+                    sf.W2[(32 * wu + 16 * j + 4 * g + i) * W2P + 16 * uu + c] = W2r[j][uu][i];
+                }
+            if (g == 0) gst(Sn + OB1 + 32 * wu + 16 * j, c, b1r[j]);
+        }
+        if (tid < D) {
+            gst(Sn + OB2, tid, b2r);
+            sf.b2[tid] = b2r;
+        }
+    };
     Rows R;
+    if (nch > 0) put_state(wsq);
     if (rowt && nch > 1) fetch_rows(0, false, R);
-    __syncthreads();
     for (int ch = 0; ch + 1 < nch; ++ch) {
-        const float *S = wsq + static_cast<size_t>(ch) * CK;
-        float *Sn = wsq + static_cast<size_t>(ch + 1) * CK;
         float tau[NF], et = 0.f, go_unused[NF];
         if (rowt) {
-            stage_rows(R, false, tau, et, go_unused);
+            stage_rows(R, false, sf.XK, tau, et, go_unused);
             if (ch + 2 < nch) fetch_rows(ch + 1, false, R);
         }
         __syncthreads();
-        // Z1 = XK W1 + b1 on the own hidden tiles; A = gelu(Z1), P = gelu'(Z1)
+        // Z1 = XK W1 + b1 on the own hidden tiles (W1 from registers); A = gelu(Z1), P = gelu'(Z1)
         f32x4 Ar[2], Pr[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const f32x4 z = x_w(sm.XK, S, j, bcast(gld(S + OB1 + 32 * wu + 16 * j, c)));
+            f32x4 z = bcast(b1r[j]);
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) z = mf(sf.XK[c * DP + 16 * rb + 4 * g + i], W1r[rb][j][i], z);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 Ar[j][i] = gelu_f(z[i]);
                 Pr[j][i] = gelu_prime_f(z[i]);
             }
-            put_h(sm.HA, j, Ar[j]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sf.HA[(4 * g + i) * MP + hc0 + 16 * j] = Ar[j][i];
         }
         __syncthreads();
-        // Z2 = A W2 + b2, the two hidden halves
-        put_d(sm.part[hh], y_v(sm.HA, S + OW2, hh == 0 ? bcast(gld(S + OB2 + 16 * u, c)) : fz));
+        {  // Z2 = A W2 + b2, the two hidden halves (W2 from LDS)
+            f32x4 acc = hh == 0 ? bcast(sf.b2[16 * u + c]) : fz;
+#pragma unroll
+            for (int kb = 0; kb < M / 8; ++kb) {
+                const int k = M / 2 * hh + 4 * kb + g;
+                acc = mf(sf.HA[c * MP + k], sf.W2[k * W2P + 16 * u + c], acc);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sf.part[hh][(4 * g + i) * DP + 16 * u + c] = acc[i];
+        }
         __syncthreads();
         if (rowt) {  // E2 = -eta lnl2(Z2, XV - XK)
             float z[NF];
-            rowz2(sm.part[0], sm.part[1], z);
+            rowz2(sf.part[0], sf.part[1], z);
             Lnl2 s;
             lnl2(z, tau, s);
 #pragma unroll
-            for (int k = 0; k < NF; ++k) sm.E2[r * DP + q + RW * k] = -et * s.G[k];
+            for (int k = 0; k < NF; ++k) sf.E2[r * DP + q + RW * k] = -et * s.G[k];
         }
         __syncthreads();
         // E1 = (E2 W2^T) * P;  W1 += XK^T E1, b1 += 1^T E1;  W2 += A^T E2, b2 += 1^T E2
-        f32x4 E1r[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const f32x4 qv = x_vt(sm.E2, S + OW2, j, fz);
+            f32x4 qv = fz;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) E1r[j][i] = qv[i] * Pr[j][i];
-        }
+            for (int kb = 0; kb < D / 4; ++kb)
+                qv = mf(sf.E2[c * DP + 4 * kb + g], sf.W2[(hc0 + 16 * j) * W2P + 4 * kb + g], qv);
+            f32x4 e1;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+            for (int i = 0; i < 4; ++i) e1[i] = qv[i] * Pr[j][i];
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                f32x4 acc;
+            for (int rb = 0; rb < 4; ++rb) W1r[rb][j] = xt_h(sf.XK, rb, e1, W1r[rb][j]);
+            b1r[j] += tile::rows4_sum((e1[0] + e1[1]) + (e1[2] + e1[3]));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = gld(S + (16 * rb + i) * M + 32 * wu + 16 * j, le);
-                acc = xt_h(sm.XK, rb, E1r[j], acc);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) gst(Sn + (16 * rb + i) * M + 32 * wu + 16 * j, le, acc[i]);
-            }
-            const float cs = tile::rows4_sum((E1r[j][0] + E1r[j][1]) + (E1r[j][2] + E1r[j][3]));
-            if (g == 0) gst(Sn + OB1 + 32 * wu + 16 * j, c, gld(S + OB1 + 32 * wu + 16 * j, c) + cs);
-#pragma unroll
-            for (int uu = 0; uu < 4; ++uu) {
-                f32x4 acc;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = gld(S + OW2 + (32 * wu + 16 * j + i) * D + 16 * uu, lf);
-                acc = ht_y(Ar[j], sm.E2, uu, acc);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) gst(Sn + OW2 + (32 * wu + 16 * j + i) * D + 16 * uu, lf, acc[i]);
-            }
+            for (int uu = 0; uu < 4; ++uu) W2r[j][uu] = ht_y(Ar[j], sf.E2, uu, W2r[j][uu]);
         }
         if (tid < D) {
             float cs = 0.f;
-            for (int t = 0; t < RW; ++t) cs += sm.E2[t * DP + tid];
-            Sn[OB2 + tid] = S[OB2 + tid] + cs;
+            for (int t = 0; t < RW; ++t) cs += sf.E2[t * DP + tid];
+            b2r += cs;
         }
-        __syncthreads();  // the new state is complete before the next chunk reads it
+        __syncthreads();  // every read of the W2 mirror is done
+        put_state(wsq + static_cast<size_t>(ch + 1) * CK);
     }
+    __syncthreads();
 
     // ============================== reverse sweep ==================================
     // the adjoint of the final state: the caller's dW1', db1', dW2', db2' (zero if absent)
@@ -402,7 +451,7 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
         __syncthreads();  // the previous chunk is done with every tile and its adjoint writes
         float tau[NF], et = 0.f, go[NF];
         if (rowt) {
-            stage_rows(R, true, tau, et, go);
+            stage_rows(R, true, sm.XK, tau, et, go);
             if (ch > 0) fetch_rows(ch - 1, true, R);
         }
         __syncthreads();
