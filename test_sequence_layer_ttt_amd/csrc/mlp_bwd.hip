@@ -54,21 +54,24 @@ constexpr int D = 64, M = 4 * D, NT = 512, RW = 16, NF = D / RW;
 constexpr int DP = D + 1, MP = M + 1, TP = RW + 1;
 constexpr int CK = 2 * D * M + M + D;  // floats of one state: W1 [D][M], b1 [M], W2 [M][D], b2 [D]
 constexpr int OB1 = D * M, OW2 = D * M + M, OB2 = 2 * D * M + M;
-#ifndef UNR
-#define UNR 4  // unroll of the loops with global operands (bounds the loads in flight)
-#endif
 
 using tile::f32x4;
 
 struct MlpBwdSmem {
     // [16 x D] token-row tiles
     float XQ[RW * DP], XK[RW * DP], dO[RW * DP], E2[RW * DP], dZb2[RW * DP], dZ2[RW * DP], dtau[RW * DP];
-    float part[2][RW * DP], partE[2][RW * DP], partK[2][RW * DP];  // two hidden halves
-    // [16 x M] hidden tiles
-    float HA[RW * MP], HB[RW * MP], HE[RW * MP], HX[RW * MP], HY[RW * MP];
+    float tau[RW * DP];
+    // partials of the two hidden halves; partE holds dE2 and later the dXK partials
+    float part[2][RW * DP], partE[2][RW * DP];
+    // [16 x M] hidden tiles; HY holds Ab, later dQ, later dZ1
+    float HA[RW * MP], HE[RW * MP], HX[RW * MP], HY[RW * MP];
+    // row-work values: gamma, beta, eta of the chunk's rows, dgamma and dbeta per row
+    float gam[D], bet[D], eta[RW], accg[RW * DP], accb[RW * DP];
     // [16 x 16] token-token tiles and per-wave partials
     float T1[RW * TP], T2[RW * TP], dT1[RW * TP];
     float gp[NT / 64][RW * TP];
+    // what the reverse of lnl2 needs from the forward: xhat, ghat and G per row
+    float lxh[RW * DP], lgh[RW * DP], lG[RW * DP];
 };
 
 // The forward sweep's tiles (the same LDS, reused): XK, A, the two Z2 halves,
@@ -96,6 +99,13 @@ __device__ __forceinline__ float gld(const float *base, unsigned idx) {
 }
 __device__ __forceinline__ void gst(float *base, unsigned idx, float v) {
     *reinterpret_cast<float *>(reinterpret_cast<char *>(base) + (idx << 2)) = v;
+}
+// 16-byte forms (base + idx 16-byte aligned)
+__device__ __forceinline__ tile::f32x4 gld4(const float *base, unsigned idx) {
+    return *reinterpret_cast<const tile::f32x4 *>(reinterpret_cast<const char *>(base) + (idx << 2));
+}
+__device__ __forceinline__ void gst4(float *base, unsigned idx, tile::f32x4 v) {
+    *reinterpret_cast<tile::f32x4 *>(reinterpret_cast<char *>(base) + (idx << 2)) = v;
 }
 
 __device__ __forceinline__ float gelu2_f(float x) {  // GELU''(x) = phi(x) (2 - x^2)
@@ -140,6 +150,8 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
     // (elements), so that the per-lane part stays one register per pattern.
     const unsigned la = g * M + c, lb = c * D + g, lc = g * D + c, ld = c * M + g;
     const unsigned le = 4 * g * M + c, lf = 4 * g * D + c;
+    // 16-byte per-lane runs: W2^T fragments and the transposed adjoint tiles
+    const unsigned lbv = c * D + 16 * g, lg = c * D + 4 * g, lh = c * M + 4 * g;
 
     float gm[NF], bt[NF];
 #pragma unroll
@@ -149,29 +161,6 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
     }
 
     // ---------------------------------------------------------------- products
-    // own hidden tile j of X [16 x D] (LDS) times W [D x M] (global, row-major)
-    auto x_w = [&](const float *X, const float *W, int j, f32x4 acc) {
-#pragma unroll UNR
-        for (int kb = 0; kb < D / 4; ++kb)
-            acc = mf(X[c * DP + 4 * kb + g], gld(W + 4 * kb * M + 32 * wu + 16 * j, la), acc);
-        return acc;
-    };
-    // own hidden tile j of X [16 x D] (LDS) times V^T, V [M x D] (global, row-major)
-    auto x_vt = [&](const float *X, const float *V, int j, f32x4 acc) {
-#pragma unroll UNR
-        for (int kb = 0; kb < D / 4; ++kb)
-            acc = mf(X[c * DP + 4 * kb + g], gld(V + (32 * wu + 16 * j) * D + 4 * kb, lb), acc);
-        return acc;
-    };
-    // feature tile u over hidden half hh of Y [16 x M] (LDS) times V [M x D] (global)
-    auto y_v = [&](const float *Y, const float *V, f32x4 acc) {
-#pragma unroll UNR
-        for (int kb = 0; kb < M / 8; ++kb) {
-            const int k0 = M / 2 * hh + 4 * kb;
-            acc = mf(Y[c * MP + k0 + g], gld(V + k0 * D + 16 * u, lc), acc);
-        }
-        return acc;
-    };
     // the same with a token-token tile: [16 x 16] (LDS, transposed if tr) times X [16 x D]
     auto t_x = [&](const float *T, bool tr, const float *X, f32x4 acc) {
 #pragma unroll
@@ -214,6 +203,55 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
         return v;
     };
     auto bcast = [](float x) { return f32x4{x, x, x, x}; };
+    // Operand fragments: the right operands that one product reads from global
+    // memory, loaded into registers as one block a phase ahead of the product,
+    // so that their latency overlaps earlier work instead of stalling it.
+    typedef float Frag[32];
+    auto ld_w = [&](const float *W, Frag &v) {  // W [D x M]: own hidden tiles, contraction over D
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int kb = 0; kb < D / 4; ++kb) v[16 * j + kb] = gld(W + 4 * kb * M + 32 * wu + 16 * j, la);
+    };
+    // V [M x D] transposed: own hidden tiles, contraction over D in the order
+    // where lane group g takes the features 16 g .. 16 g + 15 (four 16-byte loads)
+    auto ld_vt = [&](const float *V, Frag &v) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const f32x4 t = gld4(V + (32 * wu + 16 * j) * D + 4 * qq, lbv);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[16 * j + 4 * qq + e] = t[e];
+            }
+    };
+    auto ld_v = [&](const float *V, Frag &v) {  // V [M x D]: feature tile u over hidden half hh
+#pragma unroll
+        for (int kb = 0; kb < M / 8; ++kb) v[kb] = gld(V + (M / 2 * hh + 4 * kb) * D + 16 * u, lc);
+    };
+    auto ld_wt = [&](const float *W, Frag &v) {  // W [D x M] transposed: feature tile u over half hh
+#pragma unroll
+        for (int kb = 0; kb < M / 8; ++kb) v[kb] = gld(W + 16 * u * M + M / 2 * hh + 4 * kb, ld);
+    };
+    // own hidden tile j of X [16 x D] (LDS) times a fragment of ld_w / ld_vt
+    auto mm_x = [&](const float *X, const Frag &v, int j, f32x4 acc) {
+#pragma unroll
+        for (int kb = 0; kb < D / 4; ++kb) acc = mf(X[c * DP + 4 * kb + g], v[16 * j + kb], acc);
+        return acc;
+    };
+    // feature tile u over hidden half hh of Y [16 x M] (LDS) times a fragment of ld_v / ld_wt
+    auto mm_y = [&](const float *Y, const Frag &v, f32x4 acc) {
+#pragma unroll
+        for (int kb = 0; kb < M / 8; ++kb) acc = mf(Y[c * MP + M / 2 * hh + 4 * kb + g], v[kb], acc);
+        return acc;
+    };
+    // the same for ld_vt fragments (contraction order 16 g + step)
+    auto mm_xt = [&](const float *X, const Frag &v, int j, f32x4 acc) {
+#pragma unroll
+        for (int st = 0; st < D / 4; ++st) acc = mf(X[c * DP + 16 * g + st], v[16 * j + st], acc);
+        return acc;
+    };
+    auto issue = [] { __builtin_amdgcn_sched_barrier(0); };  // keeps the loads above where they are
     // token-token tile from per-wave partials: T[t][s] = sum + add on s <= t < m, else 0
     auto tri_sum = [&](float *T, int nparts, float add, int m) {
         if (tid < RW * RW) {
@@ -233,7 +271,8 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
         float xh[NF], gh[NF], G[NF];
         float sigma, c;
     };
-    auto lnl2 = [&](const float (&z)[NF], const float (&tau)[NF], Lnl2 &s) {
+    auto lnl2 = [&](const float (&z)[NF], const float (&tau)[NF], const float (&gm)[NF], const float (&bt)[NF],
+                    Lnl2 &s) {
         float s1 = 0.f, s2 = 0.f;
 #pragma unroll
         for (int k = 0; k < NF; ++k) s1 += z[k];
@@ -296,6 +335,25 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
         et = R.ok ? R.et : 0.f;
     };
 
+    // a reverse chunk's rows into LDS: XQ, XK, XV - XK, dO and eta (zero past the end)
+    auto stage_rev = [&](const Rows &R) {
+#pragma unroll
+        for (int k = 0; k < NF; ++k) {
+            const int f = q + RW * k;
+            const float xk = R.ok ? io::load(R.xk, k) : 0.f;
+            sm.XK[r * DP + f] = xk;
+            sm.tau[r * DP + f] = R.ok ? io::load(R.xv, k) - xk : 0.f;
+            sm.XQ[r * DP + f] = R.ok ? io::load(R.xq, k) : 0.f;
+            sm.dO[r * DP + f] = R.ok ? R.go[k] : 0.f;
+        }
+        if (q == 0) sm.eta[r] = R.ok ? R.et : 0.f;
+    };
+    // one row of a [16 x D] tile (ld = 0: a [D] vector) for this row thread
+    auto rowld = [&](const float *P, int ld, float (&z)[NF]) {
+#pragma unroll
+        for (int k = 0; k < NF; ++k) z[k] = P[r * ld + q + RW * k];
+    };
+
     // ======================= forward sweep: chunk-start states ===================
     // The state stays in registers in the result layout of its updates: wave w
     // holds W1[16 rb + 4 g + i][32 w + 16 j + c] and W2[32 w + 16 j + 4 g + i][16 uu + c],
@@ -351,7 +409,7 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
             stage_rows(R, false, sf.XK, tau, et, go_unused);
             if (ch + 2 < nch) fetch_rows(ch + 1, false, R);
         }
-        __syncthreads();
+        tile::lds_barrier();
         // Z1 = XK W1 + b1 on the own hidden tiles (W1 from registers); A = gelu(Z1), P = gelu'(Z1)
         f32x4 Ar[2], Pr[2];
 #pragma unroll
@@ -369,7 +427,7 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) sf.HA[(4 * g + i) * MP + hc0 + 16 * j] = Ar[j][i];
         }
-        __syncthreads();
+        tile::lds_barrier();
         {  // Z2 = A W2 + b2, the two hidden halves (W2 from LDS)
             f32x4 acc = hh == 0 ? bcast(sf.b2[16 * u + c]) : fz;
 #pragma unroll
@@ -380,16 +438,16 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) sf.part[hh][(4 * g + i) * DP + 16 * u + c] = acc[i];
         }
-        __syncthreads();
+        tile::lds_barrier();
         if (rowt) {  // E2 = -eta lnl2(Z2, XV - XK)
             float z[NF];
             rowz2(sf.part[0], sf.part[1], z);
             Lnl2 s;
-            lnl2(z, tau, s);
+            lnl2(z, tau, gm, bt, s);
 #pragma unroll
             for (int k = 0; k < NF; ++k) sf.E2[r * DP + q + RW * k] = -et * s.G[k];
         }
-        __syncthreads();
+        tile::lds_barrier();
         // E1 = (E2 W2^T) * P;  W1 += XK^T E1, b1 += 1^T E1;  W2 += A^T E2, b2 += 1^T E2
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -411,7 +469,7 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
             for (int t = 0; t < RW; ++t) cs += sf.E2[t * DP + tid];
             b2r += cs;
         }
-        __syncthreads();  // every read of the W2 mirror is done
+        tile::lds_barrier();  // every read of the W2 mirror is done
         put_state(wsq + static_cast<size_t>(ch + 1) * CK);
     }
     __syncthreads();
@@ -434,39 +492,38 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
         if (tid < M) db1[sq * M + tid] = db1_out ? db1_out[sq * M + tid] : 0.f;
         if (tid < D) db2[sq * D + tid] = db2_out ? db2_out[sq * D + tid] : 0.f;
     }
-    float dg_acc[NF], db_acc[NF];
-#pragma unroll
-    for (int k = 0; k < NF; ++k) dg_acc[k] = db_acc[k] = 0.f;
-
-    if (rowt && nch > 0) fetch_rows(nch - 1, true, R);
+    for (int i = tid; i < RW * DP; i += NT) sm.accg[i] = sm.accb[i] = 0.f;
+    if (tid < D) {
+        sm.gam[tid] = gamma[h * D + tid];
+        sm.bet[tid] = beta[h * D + tid];
+    }
+    Frag fA, fB;
     for (int ch = nch - 1; ch >= 0; --ch) {
         const int m = min(mb, L - ch * mb);
         const bool ok = r < m;
         const float *S = wsq + static_cast<size_t>(ch) * CK;
         const float *Ad = adj(ch);  // adjoint of this chunk's end state
-        float *dst1 = ch > 0 ? adj(ch + 1) : dW1 + sq * D * M;
-        float *dstb1 = ch > 0 ? adj(ch + 1) + OB1 : db1 + sq * M;
-        float *dst2 = ch > 0 ? adj(ch + 1) + OW2 : dW2 + sq * M * D;
-        float *dstb2 = ch > 0 ? adj(ch + 1) + OB2 : db2 + sq * D;
+        float *dst1 = adj(ch + 1);  // adjoint of this chunk's start state
+        float *dstb1 = dst1 + OB1, *dst2 = dst1 + OW2, *dstb2 = dst1 + OB2;
         __syncthreads();  // the previous chunk is done with every tile and its adjoint writes
-        float tau[NF], et = 0.f, go[NF];
         if (rowt) {
-            stage_rows(R, true, sm.XK, tau, et, go);
-            if (ch > 0) fetch_rows(ch - 1, true, R);
+            fetch_rows(ch, true, R);
+            stage_rev(R);
         }
-        __syncthreads();
+        tile::lds_barrier();
 
         // Z1 = XK W1 + b1 and XQ W1 + b1 on the own hidden tiles; T1 slices
+        ld_w(S, fA);
+        issue();
         f32x4 Ar[2], Pr[2], Rr[2], ZQ[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const float b = gld(S + OB1 + 32 * wu + 16 * j, c);
             f32x4 z = bcast(b), zq = bcast(b);
-#pragma unroll UNR
+#pragma unroll
             for (int kb = 0; kb < D / 4; ++kb) {
-                const float wv = gld(S + 4 * kb * M + 32 * wu + 16 * j, la);
-                z = mf(sm.XK[c * DP + 4 * kb + g], wv, z);
-                zq = mf(sm.XQ[c * DP + 4 * kb + g], wv, zq);
+                z = mf(sm.XK[c * DP + 4 * kb + g], fA[16 * j + kb], z);
+                zq = mf(sm.XQ[c * DP + 4 * kb + g], fA[16 * j + kb], zq);
             }
             ZQ[j] = zq;
 #pragma unroll
@@ -485,28 +542,45 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) sm.gp[w][(4 * g + i) * TP + c] = t4[i];
         }
-        __syncthreads();
+        tile::lds_barrier();
 
         // Z2 = A W2 + b2 (two halves);  T1 = tril(XQ XK^T + 1)
-        put_d(sm.part[hh], y_v(sm.HA, S + OW2, hh == 0 ? bcast(gld(S + OB2 + 16 * u, c)) : fz));
+        ld_v(S + OW2, fB);
+        issue();
+        put_d(sm.part[hh], mm_y(sm.HA, fB, hh == 0 ? bcast(gld(S + OB2 + 16 * u, c)) : fz));
         tri_sum(sm.T1, 4, 1.f, m);
-        __syncthreads();
+        tile::lds_barrier();
 
-        Lnl2 s;
+        float l_sigma = 1.f, l_c = 0.f;
         if (rowt) {  // E2 = -eta lnl2(Z2, XV - XK)
-            float z[NF];
+            float z[NF], tau[NF], gm[NF], bt[NF];
             rowz2(sm.part[0], sm.part[1], z);
-            lnl2(z, tau, s);
+            rowld(sm.tau, DP, tau);
+            rowld(sm.gam, 0, gm);
+            rowld(sm.bet, 0, bt);
+            const float et = sm.eta[r];
+            Lnl2 s;
+            lnl2(z, tau, gm, bt, s);
 #pragma unroll
-            for (int k = 0; k < NF; ++k) sm.E2[r * DP + q + RW * k] = -et * s.G[k];
+            for (int k = 0; k < NF; ++k) {
+                const int o = r * DP + q + RW * k;
+                sm.E2[r * DP + q + RW * k] = -et * s.G[k];
+                sm.lxh[o] = s.xh[k];
+                sm.lgh[o] = s.gh[k];
+                sm.lG[o] = s.G[k];
+            }
+            l_sigma = s.sigma;
+            l_c = s.c;
         }
-        __syncthreads();
+        tile::lds_barrier();
 
         // Q = E2 W2^T, E1 = Q * P;  Zb1 = XQ W1 + b1 + T1 E1, Ab = gelu(Zb1), Pb = gelu'(Zb1)
         f32x4 E1r[2], Abr[2], Pbr[2];
+        ld_vt(S + OW2, fA);
+        issue();
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const f32x4 qv = x_vt(sm.E2, S + OW2, j, fz);
+            const f32x4 qv = mm_xt(sm.E2, fA, j, fz);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 E1r[j][i] = qv[i] * Pr[j][i];
@@ -524,23 +598,25 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
                 Abr[j][i] = gelu_f(zb[i]);
                 Pbr[j][i] = gelu_prime_f(zb[i]);
             }
-            put_h(sm.HB, j, Abr[j]);
+            put_h(sm.HY, j, Abr[j]);
         }
-        __syncthreads();
+        tile::lds_barrier();
 
         // Ab W2 + b2 (two halves); slices of the Gram Ab A^T over the own hidden units
-        put_d(sm.part[hh], y_v(sm.HB, S + OW2, hh == 0 ? bcast(gld(S + OB2 + 16 * u, c)) : fz));
+        ld_v(S + OW2, fB);
+        issue();
+        put_d(sm.part[hh], mm_y(sm.HY, fB, hh == 0 ? bcast(gld(S + OB2 + 16 * u, c)) : fz));
         {
             f32x4 t4 = fz;
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb)
-                t4 = mf(sm.HB[c * MP + 32 * w + 4 * kb + g], sm.HA[c * MP + 32 * w + 4 * kb + g], t4);
+                t4 = mf(sm.HY[c * MP + 32 * w + 4 * kb + g], sm.HA[c * MP + 32 * w + 4 * kb + g], t4);
 #pragma unroll
             for (int i = 0; i < 4; ++i) sm.gp[w][(4 * g + i) * TP + c] = t4[i];
         }
-        __syncthreads();
+        tile::lds_barrier();
         tri_sum(sm.T2, NT / 64, 1.f, m);  // T2 = tril(Ab A^T + 1)
-        __syncthreads();
+        tile::lds_barrier();
 
         if (rowt) {  // Zb2 = Ab W2 + b2 + T2 E2;  dZb2 = LN backward of dO
             float zb[NF];
@@ -558,13 +634,16 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
 #pragma unroll
             for (int k = 0; k < NF; ++k) s2 += (zb[k] - mu) * (zb[k] - mu);
             const float rs = 1.0f / sqrtf(tile::row16_sum(s2) * inv_d + eps);
-            float xb[NF], dx[NF], m1 = 0.f, m2 = 0.f;
+            float xb[NF], dx[NF], go[NF], gm[NF], m1 = 0.f, m2 = 0.f;
+            rowld(sm.dO, DP, go);
+            rowld(sm.gam, 0, gm);
 #pragma unroll
             for (int k = 0; k < NF; ++k) {
+                const int o = r * DP + q + RW * k;
                 xb[k] = (zb[k] - mu) * rs;
                 dx[k] = gm[k] * go[k];
-                dg_acc[k] = fmaf(go[k], xb[k], dg_acc[k]);
-                db_acc[k] += go[k];
+                sm.accg[o] = fmaf(go[k], xb[k], sm.accg[o]);
+                sm.accb[o] += go[k];
                 m1 += dx[k];
                 m2 += dx[k] * xb[k];
             }
@@ -573,7 +652,7 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
 #pragma unroll
             for (int k = 0; k < NF; ++k) sm.dZb2[r * DP + q + RW * k] = (dx[k] - m1 - xb[k] * m2) * rs;
         }
-        __syncthreads();
+        tile::lds_barrier();
 
         // dT2 = tril(dZb2 E2^T) (every wave its own copy, result layout: row t = 4g+i, column s = c)
         f32x4 dt2 = fz;
@@ -584,11 +663,21 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
             if (c > 4 * g + i) dt2[i] = 0.f;
             sm.gp[w][(4 * g + i) * TP + c] = dt2[i];
         }
+        // dE2 (first parts) = A dW2' + T2^T dZb2 + db2' (two halves)
+        {
+            ld_v(Ad + OW2, fB);
+            issue();
+            f32x4 e = mm_y(sm.HA, fB, hh == 0 ? bcast(gld(Ad + OB2 + 16 * u, c)) : fz);
+            if (hh == 0) e = t_x(sm.T2, true, sm.dZb2, e);
+            put_d(sm.partE[hh], e);
+        }
         // dAb = dZb2 W2^T + dT2 A, dZb1 = dAb * Pb;  dA (first part) = dT2^T Ab
         f32x4 dZb1r[2], dAr[2];
+        ld_vt(S + OW2, fA);
+        issue();
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            f32x4 v = x_vt(sm.dZb2, S + OW2, j, fz);
+            f32x4 v = mm_xt(sm.dZb2, fA, j, fz);
 #pragma unroll
             for (int i = 0; i < 4; ++i) v = mf(sm.gp[w][c * TP + 4 * g + i], Ar[j][i], v);
 #pragma unroll
@@ -599,13 +688,7 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
             for (int i = 0; i < 4; ++i) a = mf(dt2[i], Abr[j][i], a);
             dAr[j] = a;
         }
-        // dE2 (first parts) = A dW2' + T2^T dZb2 + db2' (two halves)
-        {
-            f32x4 e = y_v(sm.HA, Ad + OW2, hh == 0 ? bcast(gld(Ad + OB2 + 16 * u, c)) : fz);
-            if (hh == 0) e = t_x(sm.T2, true, sm.dZb2, e);
-            put_d(sm.partE[hh], e);
-        }
-        __syncthreads();
+        tile::lds_barrier();
 
         // slices of dT1 = dZb1 E1^T over the own hidden units;
         // dE1 = T1^T dZb1 + XK dW1' + db1' (zero on rows past the chunk), dQ = dE1 * P
@@ -618,9 +701,11 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
             for (int i = 0; i < 4; ++i) sm.gp[w][(4 * g + i) * TP + c] = t4[i];
         }
         f32x4 dQr[2];
+        ld_w(Ad, fA);
+        issue();
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            f32x4 de = x_w(sm.XK, Ad, j, bcast(gld(Ad + OB1 + 32 * wu + 16 * j, c)));
+            f32x4 de = mm_x(sm.XK, fA, j, bcast(gld(Ad + OB1 + 32 * wu + 16 * j, c)));
             de = tt_h(sm.T1, dZb1r[j], de);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -630,16 +715,32 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
             }
             put_h(sm.HY, j, dQr[j]);
         }
-        __syncthreads();
+        tile::lds_barrier();
 
         // dT1 = tril(sum of the slices);  dE2 += dQ W2 (two halves)
         tri_sum(sm.dT1, NT / 64, 0.f, m);
-        put_d(sm.partE[hh], y_v(sm.HY, S + OW2, get_d(sm.partE[hh])));
-        __syncthreads();
+        ld_v(S + OW2, fB);
+        issue();
+        put_d(sm.partE[hh], mm_y(sm.HY, fB, get_d(sm.partE[hh])));
+        tile::lds_barrier();
 
         if (rowt) {  // deta = -G2 . dE2;  dG2 = -eta dE2;  reverse of lnl2 -> dZ2, dtau
-            float de[NF];
+            Lnl2 s;
+#pragma unroll
+            for (int k = 0; k < NF; ++k) {
+                const int o = r * DP + q + RW * k;
+                s.xh[k] = sm.lxh[o];
+                s.gh[k] = sm.lgh[o];
+                s.G[k] = sm.lG[o];
+            }
+            s.sigma = l_sigma;
+            s.c = l_c;
+            float de[NF], tau[NF], gm[NF], bt[NF];
             rowz2(sm.partE[0], sm.partE[1], de);
+            rowld(sm.tau, DP, tau);
+            rowld(sm.gam, 0, gm);
+            rowld(sm.bet, 0, bt);
+            const float et = sm.eta[r];
             float pe = 0.f;
 #pragma unroll
             for (int k = 0; k < NF; ++k) pe = fmaf(s.G[k], de[k], pe);
@@ -662,8 +763,9 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
                 const float dgh = (dG[k] - mdg - s.xh[k] * mdgx) * rs;
                 dxh[k] = gm[k] * gm[k] * dgh - (s.c * dG[k] + s.gh[k] * mdgx) * rs;
                 sm.dtau[r * DP + q + RW * k] = ok ? -gm[k] * dgh : 0.f;
-                dg_acc[k] = fmaf(dgh, fmaf(2.f * gm[k], s.xh[k], bt[k] - tau[k]), dg_acc[k]);
-                db_acc[k] = fmaf(gm[k], dgh, db_acc[k]);
+                const int o = r * DP + q + RW * k;
+                sm.accg[o] = fmaf(dgh, fmaf(2.f * gm[k], s.xh[k], bt[k] - tau[k]), sm.accg[o]);
+                sm.accb[o] = fmaf(gm[k], dgh, sm.accb[o]);
                 mdx += dxh[k];
                 mdxx += dxh[k] * s.xh[k];
             }
@@ -676,43 +778,46 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
             }
             if (ok && q == 0) deta[sq * L + ch * mb + r] = d_eta;
         }
-        __syncthreads();
+        tile::lds_barrier();
 
         // dA += E2 dW2'^T + dZ2 W2^T;  dZ1 = dA * P + dE1 * Q * GELU'';
         // the adjoint state of the chunk start: dW2, dW1, db1, db2
+        f32x4 dZ1r[2];
+        ld_vt(Ad + OW2, fA);
+        ld_vt(S + OW2, fB);
+        issue();
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            f32x4 a = x_vt(sm.E2, Ad + OW2, j, dAr[j]);
-            a = x_vt(sm.dZ2, S + OW2, j, a);
-            f32x4 dz1;
+            f32x4 a = mm_xt(sm.E2, fA, j, dAr[j]);
+            a = mm_xt(sm.dZ2, fB, j, a);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dz1[i] = fmaf(a[i], Pr[j][i], Rr[j][i]);
-            put_h(sm.HY, j, dz1);
+            for (int i = 0; i < 4; ++i) dZ1r[j][i] = fmaf(a[i], Pr[j][i], Rr[j][i]);
+            put_h(sm.HY, j, dZ1r[j]);
+        }
 #pragma unroll
-            for (int uu = 0; uu < 4; ++uu) {  // dW2 = dW2' + Ab^T dZb2 + dQ^T E2 + A^T dZ2
-                f32x4 acc;
-                const int o = (32 * wu + 16 * j) * D + 16 * uu;
+        for (int j = 0; j < 2; ++j) {
+            // dW2 = dW2' + Ab^T dZb2 + dQ^T E2 + A^T dZ2, accumulated transposed: a lane
+            // holds four consecutive features of one hidden unit's row of dW2
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = gld(Ad + OW2 + o + i * D, lf);
-                acc = ht_y(Abr[j], sm.dZb2, uu, acc);
-                acc = ht_y(dQr[j], sm.E2, uu, acc);
-                acc = ht_y(Ar[j], sm.dZ2, uu, acc);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) gst(dst2 + o + i * D, lf, acc[i]);
+            for (int rb = 0; rb < 4; ++rb) {
+                const float *src = Ad + OW2 + (32 * wu + 16 * j) * D + 16 * rb;
+                f32x4 acc = gld4(src, lg);
+                acc = xt_h(sm.dZb2, rb, Abr[j], acc);
+                acc = xt_h(sm.E2, rb, dQr[j], acc);
+                acc = xt_h(sm.dZ2, rb, Ar[j], acc);
+                gst4(dst2 + (32 * wu + 16 * j) * D + 16 * rb, lg, acc);
             }
+            // dW1 = dW1' + XQ^T dZb1 + XK^T dZ1, transposed: four consecutive hidden
+            // units of one feature's row of dW1
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {  // dW1 = dW1' + XQ^T dZb1 + XK^T dZ1
-                f32x4 acc;
-                const int o = 16 * rb * M + 32 * wu + 16 * j;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = gld(Ad + o + i * M, le);
-                acc = xt_h(sm.XQ, rb, dZb1r[j], acc);
-                acc = xt_h(sm.XK, rb, dz1, acc);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) gst(dst1 + o + i * M, le, acc[i]);
+            for (int uu = 0; uu < 4; ++uu) {
+                f32x4 acc = gld4(Ad + 16 * uu * M + 32 * wu + 16 * j, lh);
+                acc = ht_y(dZb1r[j], sm.XQ, uu, acc);
+                acc = ht_y(dZ1r[j], sm.XK, uu, acc);
+                gst4(dst1 + 16 * uu * M + 32 * wu + 16 * j, lh, acc);
             }
-            const float cs = tile::rows4_sum((dZb1r[j][0] + dz1[0]) + (dZb1r[j][1] + dz1[1]) +
-                                             ((dZb1r[j][2] + dz1[2]) + (dZb1r[j][3] + dz1[3])));
+            const float cs = tile::rows4_sum((dZb1r[j][0] + dZ1r[j][0]) + (dZb1r[j][1] + dZ1r[j][1]) +
+                                             ((dZb1r[j][2] + dZ1r[j][2]) + (dZb1r[j][3] + dZ1r[j][3])));
             if (g == 0) gst(dstb1 + 32 * wu + 16 * j, c, gld(Ad + OB1 + 32 * wu + 16 * j, c) + cs);
         }
         if (tid < D) {
@@ -720,52 +825,50 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
             for (int t = 0; t < RW; ++t) cs += sm.dZb2[t * DP + tid] + sm.dZ2[t * DP + tid];
             gst(dstb2, tid, gld(Ad, OB2 + tid) + cs);
         }
-        __syncthreads();
+        tile::lds_barrier();
 
         // dXQ = dO + dZb1 W1^T + dT1 XK;  dXK = dT1^T XQ + E1 dW1'^T + dZ1 W1^T - dtau (halves)
         {
+            ld_wt(S, fA);
+            ld_wt(Ad, fB);
+            issue();
             f32x4 aq = hh == 0 ? t_x(sm.dT1, false, sm.XK, fz) : fz;
             f32x4 ak = hh == 0 ? t_x(sm.dT1, true, sm.XQ, fz) : fz;
-#pragma unroll UNR
-            for (int kb = 0; kb < M / 8; ++kb) {
-                const int k0 = M / 2 * hh + 4 * kb, k = k0 + g;
-                const float w1t = gld(S + 16 * u * M + k0, ld), a1t = gld(Ad + 16 * u * M + k0, ld);
-                aq = mf(sm.HX[c * MP + k], w1t, aq);
-                ak = mf(sm.HY[c * MP + k], w1t, ak);
-                ak = mf(sm.HE[c * MP + k], a1t, ak);
-            }
+            aq = mm_y(sm.HX, fA, aq);
+            ak = mm_y(sm.HY, fA, ak);
+            ak = mm_y(sm.HE, fB, ak);
             put_d(sm.part[hh], aq);
-            put_d(sm.partK[hh], ak);
+            put_d(sm.partE[hh], ak);
         }
-        __syncthreads();
+        tile::lds_barrier();
         for (int e = tid; e < RW * D; e += NT) {
             const int t = e / D, f = e % D;
             if (t < m) {
                 const size_t at = xbase + static_cast<size_t>(ch * mb + t) * D + f;
                 const float dt = sm.dtau[t * DP + f];
                 dXQ[at] = sm.part[0][t * DP + f] + sm.part[1][t * DP + f] + sm.dO[t * DP + f];
-                dXK[at] = sm.partK[0][t * DP + f] + sm.partK[1][t * DP + f] - dt;
+                dXK[at] = sm.partE[0][t * DP + f] + sm.partE[1][t * DP + f] - dt;
                 dXV[at] = dt;
             }
         }
     }
     __syncthreads();
+    if (nch > 0) {  // the adjoint of the initial state, from the workspace to the outputs
+        const float *a = adj(1);
+        for (int i = tid; i < D * M; i += NT) {
+            dW1[sq * D * M + i] = a[i];
+            dW2[sq * M * D + i] = a[OW2 + i];
+        }
+        if (tid < M) db1[sq * M + tid] = a[OB1 + tid];
+        if (tid < D) db2[sq * D + tid] = a[OB2 + tid];
+    }
 
     // per-sequence dgamma, dbeta: sum the 16 row groups
-    float *red = sm.HA;
-    if (rowt) {
-#pragma unroll
-        for (int k = 0; k < NF; ++k) {
-            red[r * D + q + RW * k] = dg_acc[k];
-            red[RW * D + r * D + q + RW * k] = db_acc[k];
-        }
-    }
-    __syncthreads();
     if (tid < D) {
         float a = 0.f, b = 0.f;
         for (int rr = 0; rr < RW; ++rr) {
-            a += red[rr * D + tid];
-            b += red[RW * D + rr * D + tid];
+            a += sm.accg[rr * DP + tid];
+            b += sm.accb[rr * DP + tid];
         }
         dgamma[sq * D + tid] = a;
         dbeta[sq * D + tid] = b;
