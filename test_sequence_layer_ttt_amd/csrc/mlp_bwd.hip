@@ -52,7 +52,9 @@ namespace {
 
 constexpr int D = 64, M = 4 * D, NT = 512, RW = 16, NF = D / RW;
 constexpr int DP = D + 1, MP = M + 1, TP = RW + 1;
-constexpr int CK = 2 * D * M + M + D;  // floats of one state: W1 [D][M], b1 [M], W2 [M][D], b2 [D]
+// floats of one stored state: W1 transposed [M][D], b1 [M], W2 [M][D], b2 [D] (both weight
+// matrices hidden-unit-major, as are the adjoint states)
+constexpr int CK = 2 * D * M + M + D;
 constexpr int OB1 = D * M, OW2 = D * M + M, OB2 = 2 * D * M + M;
 
 using tile::f32x4;
@@ -148,10 +150,9 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
     const int hc0 = 32 * wu + c;  // this lane's hidden column in own tile j: hc0 + 16 j
     // Global addresses are a uniform pointer plus one of a few per-lane offsets
     // (elements), so that the per-lane part stays one register per pattern.
-    const unsigned la = g * M + c, lb = c * D + g, lc = g * D + c, ld = c * M + g;
-    const unsigned le = 4 * g * M + c, lf = 4 * g * D + c;
+    const unsigned lc = g * D + c, le = 4 * g * M + c, lf = 4 * g * D + c;
     // 16-byte per-lane runs: W2^T fragments and the transposed adjoint tiles
-    const unsigned lbv = c * D + 16 * g, lg = c * D + 4 * g, lh = c * M + 4 * g;
+    const unsigned lbv = c * D + 4 * g, lg = c * D + 4 * g;
 
     float gm[NF], bt[NF];
 #pragma unroll
@@ -207,20 +208,15 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
     // memory, loaded into registers as one block a phase ahead of the product,
     // so that their latency overlaps earlier work instead of stalling it.
     typedef float Frag[32];
-    auto ld_w = [&](const float *W, Frag &v) {  // W [D x M]: own hidden tiles, contraction over D
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int kb = 0; kb < D / 4; ++kb) v[16 * j + kb] = gld(W + 4 * kb * M + 32 * wu + 16 * j, la);
-    };
     // V [M x D] transposed: own hidden tiles, contraction over D in the order
-    // where lane group g takes the features 16 g .. 16 g + 15 (four 16-byte loads)
+    // where load q of lane group g takes the features 16 q + 4 g .. + 3 (the four
+    // groups of a row read 64 contiguous bytes per load)
     auto ld_vt = [&](const float *V, Frag &v) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
-                const f32x4 t = gld4(V + (32 * wu + 16 * j) * D + 4 * qq, lbv);
+                const f32x4 t = gld4(V + (32 * wu + 16 * j) * D + 16 * qq, lbv);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[16 * j + 4 * qq + e] = t[e];
             }
@@ -229,26 +225,18 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
 #pragma unroll
         for (int kb = 0; kb < M / 8; ++kb) v[kb] = gld(V + (M / 2 * hh + 4 * kb) * D + 16 * u, lc);
     };
-    auto ld_wt = [&](const float *W, Frag &v) {  // W [D x M] transposed: feature tile u over half hh
-#pragma unroll
-        for (int kb = 0; kb < M / 8; ++kb) v[kb] = gld(W + 16 * u * M + M / 2 * hh + 4 * kb, ld);
-    };
-    // own hidden tile j of X [16 x D] (LDS) times a fragment of ld_w / ld_vt
-    auto mm_x = [&](const float *X, const Frag &v, int j, f32x4 acc) {
-#pragma unroll
-        for (int kb = 0; kb < D / 4; ++kb) acc = mf(X[c * DP + 4 * kb + g], v[16 * j + kb], acc);
-        return acc;
-    };
-    // feature tile u over hidden half hh of Y [16 x M] (LDS) times a fragment of ld_v / ld_wt
+    // feature tile u over hidden half hh of Y [16 x M] (LDS) times a fragment of ld_v
     auto mm_y = [&](const float *Y, const Frag &v, f32x4 acc) {
 #pragma unroll
         for (int kb = 0; kb < M / 8; ++kb) acc = mf(Y[c * MP + M / 2 * hh + 4 * kb + g], v[kb], acc);
         return acc;
     };
-    // the same for ld_vt fragments (contraction order 16 g + step)
+    // own hidden tile j of X [16 x D] (LDS) times a fragment of ld_vt (step 4 q + e:
+    // feature 16 q + 4 g + e)
     auto mm_xt = [&](const float *X, const Frag &v, int j, f32x4 acc) {
 #pragma unroll
-        for (int st = 0; st < D / 4; ++st) acc = mf(X[c * DP + 16 * g + st], v[16 * j + st], acc);
+        for (int st = 0; st < D / 4; ++st)
+            acc = mf(X[c * DP + 16 * (st >> 2) + 4 * g + (st & 3)], v[16 * j + st], acc);
         return acc;
     };
     auto issue = [] { __builtin_amdgcn_sched_barrier(0); };  // keeps the loads above where they are
@@ -383,9 +371,7 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) gst(Sn + (16 * rb + i) * M + 32 * wu + 16 * j, le, W1r[rb][j][i]);
+            for (int rb = 0; rb < 4; ++rb) gst4(Sn + (32 * wu + 16 * j) * D + 16 * rb, lg, W1r[rb][j]);
 #pragma unroll
             for (int uu = 0; uu < 4; ++uu)
 #pragma unroll
@@ -479,7 +465,7 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
     float *a0 = adj(nch - 1);
     if (nch > 0) {
         for (int i = tid; i < D * M; i += NT) {
-            a0[i] = dW1_out ? dW1_out[sq * D * M + i] : 0.f;
+            a0[(i % M) * D + i / M] = dW1_out ? dW1_out[sq * D * M + i] : 0.f;
             a0[OW2 + i] = dW2_out ? dW2_out[sq * M * D + i] : 0.f;
         }
         if (tid < M) a0[OB1 + tid] = db1_out ? db1_out[sq * M + tid] : 0.f;
@@ -513,7 +499,7 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
         tile::lds_barrier();
 
         // Z1 = XK W1 + b1 and XQ W1 + b1 on the own hidden tiles; T1 slices
-        ld_w(S, fA);
+        ld_vt(S, fA);  // W1 (stored transposed)
         issue();
         f32x4 Ar[2], Pr[2], Rr[2], ZQ[2];
 #pragma unroll
@@ -521,9 +507,10 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
             const float b = gld(S + OB1 + 32 * wu + 16 * j, c);
             f32x4 z = bcast(b), zq = bcast(b);
 #pragma unroll
-            for (int kb = 0; kb < D / 4; ++kb) {
-                z = mf(sm.XK[c * DP + 4 * kb + g], fA[16 * j + kb], z);
-                zq = mf(sm.XQ[c * DP + 4 * kb + g], fA[16 * j + kb], zq);
+            for (int st = 0; st < D / 4; ++st) {
+                const int k = 16 * (st >> 2) + 4 * g + (st & 3);
+                z = mf(sm.XK[c * DP + k], fA[16 * j + st], z);
+                zq = mf(sm.XQ[c * DP + k], fA[16 * j + st], zq);
             }
             ZQ[j] = zq;
 #pragma unroll
@@ -701,11 +688,11 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
             for (int i = 0; i < 4; ++i) sm.gp[w][(4 * g + i) * TP + c] = t4[i];
         }
         f32x4 dQr[2];
-        ld_w(Ad, fA);
+        ld_vt(Ad, fA);  // dW1' (transposed)
         issue();
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            f32x4 de = mm_x(sm.XK, fA, j, bcast(gld(Ad + OB1 + 32 * wu + 16 * j, c)));
+            f32x4 de = mm_xt(sm.XK, fA, j, bcast(gld(Ad + OB1 + 32 * wu + 16 * j, c)));
             de = tt_h(sm.T1, dZb1r[j], de);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -807,14 +794,14 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
                 acc = xt_h(sm.dZ2, rb, Ar[j], acc);
                 gst4(dst2 + (32 * wu + 16 * j) * D + 16 * rb, lg, acc);
             }
-            // dW1 = dW1' + XQ^T dZb1 + XK^T dZ1, transposed: four consecutive hidden
-            // units of one feature's row of dW1
+            // dW1 = dW1' + XQ^T dZb1 + XK^T dZ1: four consecutive features of one hidden
+            // unit's row of the transposed dW1
 #pragma unroll
-            for (int uu = 0; uu < 4; ++uu) {
-                f32x4 acc = gld4(Ad + 16 * uu * M + 32 * wu + 16 * j, lh);
-                acc = ht_y(dZb1r[j], sm.XQ, uu, acc);
-                acc = ht_y(dZ1r[j], sm.XK, uu, acc);
-                gst4(dst1 + 16 * uu * M + 32 * wu + 16 * j, lh, acc);
+            for (int rb = 0; rb < 4; ++rb) {
+                f32x4 acc = gld4(Ad + (32 * wu + 16 * j) * D + 16 * rb, lg);
+                acc = xt_h(sm.XQ, rb, dZb1r[j], acc);
+                acc = xt_h(sm.XK, rb, dZ1r[j], acc);
+                gst4(dst1 + (32 * wu + 16 * j) * D + 16 * rb, lg, acc);
             }
             const float cs = tile::rows4_sum((dZb1r[j][0] + dZ1r[j][0]) + (dZb1r[j][1] + dZ1r[j][1]) +
                                              ((dZb1r[j][2] + dZ1r[j][2]) + (dZb1r[j][3] + dZ1r[j][3])));
@@ -829,8 +816,8 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
 
         // dXQ = dO + dZb1 W1^T + dT1 XK;  dXK = dT1^T XQ + E1 dW1'^T + dZ1 W1^T - dtau (halves)
         {
-            ld_wt(S, fA);
-            ld_wt(Ad, fB);
+            ld_v(S, fA);   // W1 (stored transposed), for dZb1 W1^T and dZ1 W1^T
+            ld_v(Ad, fB);  // dW1' (transposed), for E1 dW1'^T
             issue();
             f32x4 aq = hh == 0 ? t_x(sm.dT1, false, sm.XK, fz) : fz;
             f32x4 ak = hh == 0 ? t_x(sm.dT1, true, sm.XQ, fz) : fz;
@@ -856,7 +843,7 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
     if (nch > 0) {  // the adjoint of the initial state, from the workspace to the outputs
         const float *a = adj(1);
         for (int i = tid; i < D * M; i += NT) {
-            dW1[sq * D * M + i] = a[i];
+            dW1[sq * D * M + i] = a[(i % M) * D + i / M];
             dW2[sq * M * D + i] = a[OW2 + i];
         }
         if (tid < M) db1[sq * M + tid] = a[OB1 + tid];
