@@ -532,9 +532,10 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
         tile::lds_barrier();
 
         // Z2 = A W2 + b2 (two halves);  T1 = tril(XQ XK^T + 1)
-        ld_v(S + OW2, fB);
+        Frag fW;  // W2 rows of this wave's hidden half, held for A W2, Ab W2 and dQ W2
+        ld_v(S + OW2, fW);
         issue();
-        put_d(sm.part[hh], mm_y(sm.HA, fB, hh == 0 ? bcast(gld(S + OB2 + 16 * u, c)) : fz));
+        put_d(sm.part[hh], mm_y(sm.HA, fW, hh == 0 ? bcast(gld(S + OB2 + 16 * u, c)) : fz));
         tri_sum(sm.T1, 4, 1.f, m);
         tile::lds_barrier();
 
@@ -563,11 +564,12 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
 
         // Q = E2 W2^T, E1 = Q * P;  Zb1 = XQ W1 + b1 + T1 E1, Ab = gelu(Zb1), Pb = gelu'(Zb1)
         f32x4 E1r[2], Abr[2], Pbr[2];
-        ld_vt(S + OW2, fA);
+        Frag fT;  // W2^T of this wave's hidden units, held for E2 W2^T, dZb2 W2^T and dZ2 W2^T
+        ld_vt(S + OW2, fT);
         issue();
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const f32x4 qv = mm_xt(sm.E2, fA, j, fz);
+            const f32x4 qv = mm_xt(sm.E2, fT, j, fz);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 E1r[j][i] = qv[i] * Pr[j][i];
@@ -590,9 +592,7 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
         tile::lds_barrier();
 
         // Ab W2 + b2 (two halves); slices of the Gram Ab A^T over the own hidden units
-        ld_v(S + OW2, fB);
-        issue();
-        put_d(sm.part[hh], mm_y(sm.HY, fB, hh == 0 ? bcast(gld(S + OB2 + 16 * u, c)) : fz));
+        put_d(sm.part[hh], mm_y(sm.HY, fW, hh == 0 ? bcast(gld(S + OB2 + 16 * u, c)) : fz));
         {
             f32x4 t4 = fz;
 #pragma unroll
@@ -660,11 +660,9 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
         }
         // dAb = dZb2 W2^T + dT2 A, dZb1 = dAb * Pb;  dA (first part) = dT2^T Ab
         f32x4 dZb1r[2], dAr[2];
-        ld_vt(S + OW2, fA);
-        issue();
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            f32x4 v = mm_xt(sm.dZb2, fA, j, fz);
+            f32x4 v = mm_xt(sm.dZb2, fT, j, fz);
 #pragma unroll
             for (int i = 0; i < 4; ++i) v = mf(sm.gp[w][c * TP + 4 * g + i], Ar[j][i], v);
 #pragma unroll
@@ -706,9 +704,7 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
 
         // dT1 = tril(sum of the slices);  dE2 += dQ W2 (two halves)
         tri_sum(sm.dT1, NT / 64, 0.f, m);
-        ld_v(S + OW2, fB);
-        issue();
-        put_d(sm.partE[hh], mm_y(sm.HY, fB, get_d(sm.partE[hh])));
+        put_d(sm.partE[hh], mm_y(sm.HY, fW, get_d(sm.partE[hh])));
         tile::lds_barrier();
 
         if (rowt) {  // deta = -G2 . dE2;  dG2 = -eta dE2;  reverse of lnl2 -> dZ2, dtau
@@ -771,12 +767,11 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
         // the adjoint state of the chunk start: dW2, dW1, db1, db2
         f32x4 dZ1r[2];
         ld_vt(Ad + OW2, fA);
-        ld_vt(S + OW2, fB);
         issue();
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             f32x4 a = mm_xt(sm.E2, fA, j, dAr[j]);
-            a = mm_xt(sm.dZ2, fB, j, a);
+            a = mm_xt(sm.dZ2, fT, j, a);
 #pragma unroll
             for (int i = 0; i < 4; ++i) dZ1r[j][i] = fmaf(a[i], Pr[j][i], Rr[j][i]);
             put_h(sm.HY, j, dZ1r[j]);
