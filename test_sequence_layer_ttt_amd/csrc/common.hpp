@@ -47,6 +47,19 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// Phi(x) and phi(x) (standard normal cdf / pdf) with erf from Abramowitz &
+// Stegun 7.1.26: erf(y) = 1 - (a1 t + ... + a5 t^5) exp(-y^2), t = 1/(1 + p y).
+__device__ __forceinline__ void normal_cdf_pdf(float x, float &Phi, float &phi) {
+    const float y = fabsf(x) * 0.70710678118654752f;  // |x| / sqrt(2)
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, y, 1.0f));
+    const float p = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 1.061405429f, -1.453152027f), 1.421413741f),
+                                     -0.284496736f), 0.254829592f);
+    const float e = __expf(-y * y);                   // exp(-x^2 / 2)
+    const float half_erfc = 0.5f * p * e;             // erfc(|x| / sqrt(2)) / 2
+    Phi = x >= 0.f ? 1.0f - half_erfc : half_erfc;
+    phi = 0.39894228040143268f * e;
+}
+
 // Exact GELU x * Phi(x) and its derivative.
 __device__ __forceinline__ float gelu_f(float x) {
     return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));

@@ -79,19 +79,6 @@ struct alignas(16) MlpSmem {
     alignas(16) uint16_t e2t[D * KS];         // E2 transposed, fp16 [out][token]
 };
 
-// Phi(x) and phi(x) (standard normal cdf / pdf) with erf from Abramowitz &
-// Stegun 7.1.26: erf(y) = 1 - (a1 t + ... + a5 t^5) exp(-y^2), t = 1/(1 + p y).
-__device__ __forceinline__ void normal_cdf_pdf(float x, float &Phi, float &phi) {
-    const float y = fabsf(x) * 0.70710678118654752f;  // |x| / sqrt(2)
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, y, 1.0f));
-    const float p = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 1.061405429f, -1.453152027f), 1.421413741f),
-                                     -0.284496736f), 0.254829592f);
-    const float e = __expf(-y * y);                   // exp(-x^2 / 2)
-    const float half_erfc = 0.5f * p * e;             // erfc(|x| / sqrt(2)) / 2
-    Phi = x >= 0.f ? 1.0f - half_erfc : half_erfc;
-    phi = 0.39894228040143268f * e;
-}
-
 // E = -eta * G for one row (row layout) under the selected loss. LOSS = 0 is
 // the squared reconstruction error (tau = XV - XK); LOSS = 1 the inner product
 // -< LN(z), v > with tau = v, whose gradient through the layer norm is
