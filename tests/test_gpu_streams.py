@@ -82,6 +82,26 @@ def test_backward_on_side_stream():
     _check(run, 20.0)
 
 
+def test_mlp_backward_on_side_stream():
+    x = gen.make_workload(4, L=256, B=2, H=4)
+    dt = torch.bfloat16
+    dO = P.dev(np.random.default_rng(79).standard_normal((2, 4, 256, 64)).astype(np.float32))
+    args = [P.dev(x.XQ, dt), P.dev(x.XK, dt), P.dev(x.XV, dt), P.dev(x.eta), P.dev(x.W1),
+            P.dev(x.b1), P.dev(x.W2), P.dev(x.b2), P.dev(x.gamma), P.dev(x.beta), dO]
+
+    def run(s):
+        gr = ttt.ttt_mlp_backward(*args, stream=s)
+        return tuple(gr[k] for k in sorted(gr))
+    _check(run, 20.0)
+
+
+def test_qkv_project_on_side_stream():
+    x = gen.make_proj_workload(2, L=1024)
+    X = P.dev(x.X, torch.bfloat16)
+    th = P.dev(x.theta, torch.bfloat16)
+    _check(lambda s: ttt.ttt_qkv_project(X, th, x.H, stream=s), 5.0)
+
+
 def _variant_args(kind):
     dt = torch.bfloat16
     if kind.startswith("linear"):
