@@ -337,8 +337,10 @@ int ttt_linear_backward_noalloc(int B, int H, int L, int d, int mb, int io, floa
  *   Parameters shared over the batch (the initial state when w0_batched == 0,
  *   gamma, beta) need the caller's sum over B.
  *   workspace: device memory of at least ttt_mlp_backward_workspace bytes
- *   (the state at every chunk start and two adjoint states), caller-owned,
- *   overwritten.
+ *   (the state at every chunk start, two adjoint states and, per chunk, the
+ *   reverse's values that do not depend on the adjoint state), caller-owned,
+ *   overwritten. The call is three launches on `stream`: the forward sweep,
+ *   a pre-pass over all chunks at once, the reverse sweep.
  * No output may overlap an input, another output or the workspace.
  * Numerics: fp32 throughout (bf16 inputs widened); the forward is recomputed
  * chunk by chunk from the stored states in the dual form ([D] §4.2).
@@ -353,9 +355,10 @@ int ttt_mlp_backward(int B, int H, int L, int d, int mb, int io, float ln_eps, c
                      float *dW1, float *db1, float *dW2, float *db2, float *dgamma, float *dbeta,
                      void *workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes ttt_mlp_backward needs: B*H*(ceil(L/mb)+2)*(8d*d+5d)*4
- * (d = 64: 132,352 bytes per chunk and sequence). Validates B, H, L, d, mb
- * as ttt_mlp_backward does. */
+/* Workspace bytes ttt_mlp_backward needs, with n = ceil(L/mb):
+ * B*H*((n+2)*(8d*d+5d) + n*(594d+32))*4 (d = 64: 284,544 bytes per chunk and
+ * sequence plus 264,704 per sequence). Validates B, H, L, d, mb as
+ * ttt_mlp_backward does; TTT_E_SHAPE also when B*H*n exceeds 2^31 - 1. */
 int ttt_mlp_backward_workspace(int B, int H, int L, int d, int mb, size_t *bytes);
 
 /*

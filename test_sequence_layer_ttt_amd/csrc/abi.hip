@@ -529,8 +529,9 @@ int ttt_mlp_backward_workspace(int B, int H, int L, int d, int mb, size_t *bytes
     if (d != 64) return fail(TTT_E_SHAPE, "d = %d: the MLP supports d = 64 only", d);
     if (!bytes) return fail(TTT_E_NULL, "bytes is NULL");
     const size_t nch = L > 0 ? static_cast<size_t>((L + mb - 1) / mb) : 0;
-    const size_t m = 4 * static_cast<size_t>(d);
-    if (!nbytes(bytes, {size_t(B), size_t(H), nch + 2, 2 * size_t(d) * m + m + size_t(d), sizeof(float)}))
+    if (static_cast<size_t>(B) * H * nch > 0x7fffffffu)
+        return fail(TTT_E_SHAPE, "B*H*ceil(L/mb) = %zu chunks exceeds 2^31 - 1", static_cast<size_t>(B) * H * nch);
+    if (!nbytes(bytes, {size_t(B), size_t(H), ttt::mlp_backward_seq_floats(L, d, mb), sizeof(float)}))
         return fail(TTT_E_SHAPE, "sizes overflow");
     return ok();
 }

@@ -52,7 +52,7 @@ struct MLPBwdArgs {
     MLPArgs f;  // forward arguments (O and the state outputs unused)
     const float *dO, *dW1_out, *db1_out, *dW2_out, *db2_out;
     float *dXQ, *dXK, *dXV, *deta, *dW1, *db1, *dW2, *db2, *dgamma, *dbeta;
-    float *ws;  // chunk-start states and two adjoint states, mlp_backward_workspace_floats floats
+    float *ws;  // chunk-start states, two adjoint states and chunk records: B*H*mlp_backward_seq_floats
 };
 
 struct DecodeArgs {
@@ -94,7 +94,7 @@ size_t linear_backward_workspace_floats(int B, int H, int L, int d, int mb);
 size_t linear_backward_scratch_bytes();
 hipError_t linear_backward_scratch(float **ptr);
 hipError_t launch_linear_backward(const LinearBwdArgs &a, hipStream_t stream);
-size_t mlp_backward_workspace_floats(int B, int H, int L, int d, int mb);
+size_t mlp_backward_seq_floats(int L, int d, int mb);  // workspace floats per sequence
 hipError_t launch_mlp_backward(const MLPBwdArgs &a, hipStream_t stream);
 hipError_t launch_mlp(const MLPArgs &a, hipStream_t stream);
 bool mlp_mfma_supported(const MLPArgs &a);

@@ -38,10 +38,15 @@
 // half w / 4 of 16-feature tile w % 4 and the two partial tiles are summed by
 // their reader. Hidden tiles read across waves or transposed go through LDS.
 //
-// A forward sweep stores the state at every chunk start in the workspace;
-// the reverse sweep reads each chunk's state from there and keeps the running
-// adjoint state in two workspace buffers used alternately (read the one,
-// write the other), so no state matrix occupies LDS.
+// Three launches. A forward sweep stores the state at every chunk start in the
+// workspace. A pre-pass, one workgroup per chunk and all chunks at once,
+// recomputes each chunk from its stored state and does every part of the
+// chunk's reverse that does not involve the adjoint state of the chunk end
+// (dZb2, dT2, dZb1, dT1, T2^T dZb2, dT2^T Ab, T1^T dZb1, dXQ in full, the dT1^T XQ
+// part of dXK); it stores what the rest needs in a per-chunk record. The
+// reverse sweep then runs the adjoint-dependent rest chunk by chunk from the
+// last, keeping the running adjoint state in two workspace buffers used
+// alternately (read the one, write the other), so no state matrix occupies LDS.
 #include "common.hpp"
 
 #include "launch.hpp"
@@ -73,7 +78,7 @@ struct MlpBwdSmem {
     float T1[RW * TP], T2[RW * TP], dT1[RW * TP];
     float gp[NT / 64][RW * TP];
     // what the reverse of lnl2 needs from the forward: xhat, ghat and G per row
-    float lxh[RW * DP], lgh[RW * DP], lG[RW * DP];
+    float lxh[RW * DP], lgh[RW * DP], lG[RW * DP], lsig[RW], lcc[RW];
 };
 
 // The forward sweep's tiles (the same LDS, reused): XK, A, the two Z2 halves,
@@ -110,6 +115,26 @@ __device__ __forceinline__ void gst4(float *base, unsigned idx, tile::f32x4 v) {
     *reinterpret_cast<tile::f32x4 *>(reinterpret_cast<char *>(base) + (idx << 2)) = v;
 }
 
+__device__ __forceinline__ tile::f32x2 gld2(const float *base, unsigned idx) {  // 8-byte form
+    return *reinterpret_cast<const tile::f32x2 *>(reinterpret_cast<const char *>(base) + (idx << 2));
+}
+// two consecutive input elements in one load: raw bits and the two values as fp32
+template <typename T> struct pair_io;
+template <> struct pair_io<float> {
+    typedef tile::f32x2 raw;
+    static __device__ __forceinline__ raw ld(const float *base, unsigned idx) { return gld2(base, idx); }
+    static __device__ __forceinline__ float lo(raw v) { return v[0]; }
+    static __device__ __forceinline__ float hi(raw v) { return v[1]; }
+};
+template <> struct pair_io<bf16_t> {
+    typedef uint32_t raw;
+    static __device__ __forceinline__ raw ld(const bf16_t *base, unsigned idx) {
+        return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(base) + (idx << 1));
+    }
+    static __device__ __forceinline__ float lo(raw v) { return __uint_as_float(v << 16); }
+    static __device__ __forceinline__ float hi(raw v) { return __uint_as_float(v & 0xffff0000u); }
+};
+
 // GELU(x) = x Phi(x), GELU'(x) = Phi(x) + x phi(x), GELU''(x) = phi(x) (2 - x^2), from one
 // evaluation of Phi and phi (erf to |error| <= 1.5e-7, far below the fp32 products' bar)
 __device__ __forceinline__ void gelu3(float x, float &g0, float &g1, float &g2) {
@@ -126,9 +151,27 @@ __device__ __forceinline__ void gelu2(float x, float &g0, float &g1) {
     g1 = fmaf(x, phi, Phi);
 }
 
-template <typename TIO>
+// Record of one chunk, written by the pre-pass and read once by the reverse
+// sweep: eight hidden tensors [16 x M] in the register layout of the waves that
+// own them (tensor t, wave w, tile j, lane: four consecutive floats), five
+// [16 x D] row tensors, sigma and c of the chunk's layer-norm gradient rows, and
+// the chunk's share of dgamma and dbeta from the output layer norm.
+constexpr int RH = RW * M;
+enum { HT_A, HT_P, HT_RQ, HT_AB, HT_DZB1, HT_DAT, HT_TZ, HT_E1, NHT };
+enum { RT_XH, RT_GH, RT_G, RT_DZB2, RT_T2Z, NRT };
+constexpr int OR = NHT * RH, OS = OR + NRT * RW * D, OGB = OS + 2 * RW, REC = OGB + 2 * D;
+static_assert(CK % 4 == 0 && REC % 4 == 0, "16-byte aligned records");
+
+// The three launches: the forward sweep stores every chunk-start state (one
+// workgroup per sequence); the pre-pass recomputes each chunk from its state
+// and does all of the chunk's reverse that does not depend on the adjoint state
+// (one workgroup per chunk, all chunks at once); the reverse sweep runs the
+// adjoint-dependent rest, chunk by chunk from the last (one per sequence).
+enum { FWD = 0, PRE = 1, REV = 2 };
+
+template <typename TIO, int MODE>
 __global__ __launch_bounds__(NT) void mlp_backward_kernel(
-    int H, int L, int mb, float eps, const TIO *__restrict__ XQ, const TIO *__restrict__ XK,
+    int nseq, int H, int L, int mb, float eps, const TIO *__restrict__ XQ, const TIO *__restrict__ XK,
     const TIO *__restrict__ XV, const float *__restrict__ eta, const float *__restrict__ W1_0,
     const float *__restrict__ b1_0, const float *__restrict__ W2_0, const float *__restrict__ b2_0,
     int w0_batched, const float *__restrict__ gamma, const float *__restrict__ beta,
@@ -148,16 +191,18 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
     const int u = wu & 3, hh = wu >> 2;        // feature tile and hidden half of split products
     const bool rowt = tid < RW * RW;           // row work: 16 lanes per token row
     const int r = (tid >> 4) & (RW - 1), q = tid & (RW - 1);
-    const long seq = blockIdx.x;
+    const int nch = (L + mb - 1) / mb;
+    // the pre-pass takes one chunk: workgroup index = sequence * chunks + chunk
+    const long seq = MODE == PRE ? static_cast<long>(blockIdx.x) / nch : static_cast<long>(blockIdx.x);
     const int h = static_cast<int>(seq % H);
     const long n = seq / H;
-    const int nch = (L + mb - 1) / mb;
     const size_t sq = static_cast<size_t>(seq);
     const size_t xbase = sq * L * D;
     const size_t st = (w0_batched ? static_cast<size_t>(n) * H : 0) + static_cast<size_t>(h);
     float *wsq = ws + sq * (static_cast<size_t>(nch) + 2) * CK;
     float *const adj0 = wsq + static_cast<size_t>(nch) * CK, *const adj1 = adj0 + CK;
     auto adj = [&](int k) { return (k & 1) ? adj1 : adj0; };
+    float *const recq = ws + static_cast<size_t>(nseq) * (nch + 2) * CK + sq * nch * REC;
     const f32x4 fz = {0.f, 0.f, 0.f, 0.f};
     const int hc0 = 32 * wu + c;  // this lane's hidden column in own tile j: hc0 + 16 j
     // Global addresses are a uniform pointer plus one of a few per-lane offsets
@@ -165,13 +210,8 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
     const unsigned lc = g * D + c, le = 4 * g * M + c, lf = 4 * g * D + c;
     // 16-byte per-lane runs: W2^T fragments and the transposed adjoint tiles
     const unsigned lbv = c * D + 4 * g, lg = c * D + 4 * g;
-
-    float gm[NF], bt[NF];
-#pragma unroll
-    for (int k = 0; k < NF; ++k) {
-        gm[k] = gamma[h * D + q + RW * k];
-        bt[k] = beta[h * D + q + RW * k];
-    }
+    // record: a lane's four floats of a hidden tile; a row thread's features of a row tensor
+    const unsigned lh = 4 * lane, lrq = r * D + q;
 
     // ---------------------------------------------------------------- products
     // the same with a token-token tile: [16 x 16] (LDS, transposed if tr) times X [16 x D]
@@ -208,12 +248,6 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
     auto put_d = [&](float *P, f32x4 v) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) P[(4 * g + i) * DP + 16 * u + c] = v[i];
-    };
-    auto get_d = [&](const float *P) {
-        f32x4 v;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = P[(4 * g + i) * DP + 16 * u + c];
-        return v;
     };
     auto bcast = [](float x) { return f32x4{x, x, x, x}; };
     // Operand fragments: the right operands that one product reads from global
@@ -265,6 +299,10 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
 #pragma unroll
         for (int k = 0; k < NF; ++k) z[k] = P0[r * DP + q + RW * k] + P1[r * DP + q + RW * k];
     };
+    // a hidden tile of the record (tensor t, own tile j)
+    auto put_rec = [&](float *rc, int t, int j, f32x4 v) { gst4(rc + t * RH + (2 * wu + j) * 256, lh, v); };
+    auto get_rec = [&](const float *rc, int t, int j) { return gld4(rc + t * RH + (2 * wu + j) * 256, lh); };
+    auto rrow = [&](int t) { return OR + t * RW * D; };  // offset of row tensor t in a record
 
     // layer-norm L2 gradient of one row (16 lanes) and what its reverse needs
     struct Lnl2 {
@@ -295,15 +333,14 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
         for (int k = 0; k < NF; ++k) s.G[k] = (s.gh[k] - a - s.xh[k] * s.c) * rs;
     };
 
-    // Inputs of one chunk for this row thread, fetched a chunk ahead of use;
-    // unconditional loads from a row clamped into the sequence, rows past its
-    // end zeroed when staged.
+    // Inputs of one chunk for this row thread; unconditional loads from a row
+    // clamped into the sequence, rows past its end zeroed when staged.
     struct Rows {
         TIO xq[NF], xk[NF], xv[NF];
         float go[NF], et;
         bool ok;
     };
-    auto fetch_rows = [&](int ch, bool rev, Rows &R) {
+    auto fetch_rows = [&](int ch, bool xq, bool go, Rows &R) {
         R.ok = r < min(mb, L - ch * mb);
         const int rr = R.ok ? r : 0;
         const size_t row = xbase + static_cast<size_t>(ch * mb + rr) * D;
@@ -312,41 +349,10 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
             const int f = q + RW * k;
             R.xk[k] = XK[row + f];
             R.xv[k] = XV[row + f];
-            if (rev) {
-                R.xq[k] = XQ[row + f];
-                R.go[k] = dO[row + f];
-            }
+            if (xq) R.xq[k] = XQ[row + f];
+            if (go) R.go[k] = dO[row + f];
         }
         R.et = eta[sq * L + ch * mb + rr];
-    };
-    auto stage_rows = [&](const Rows &R, bool rev, float *xkt, float (&tau)[NF], float &et, float (&go)[NF]) {
-#pragma unroll
-        for (int k = 0; k < NF; ++k) {
-            const int f = q + RW * k;
-            const float xk = R.ok ? io::load(R.xk, k) : 0.f;
-            xkt[r * DP + f] = xk;
-            tau[k] = R.ok ? io::load(R.xv, k) - xk : 0.f;
-            if (rev) {
-                sm.XQ[r * DP + f] = R.ok ? io::load(R.xq, k) : 0.f;
-                go[k] = R.ok ? R.go[k] : 0.f;
-                sm.dO[r * DP + f] = go[k];
-            }
-        }
-        et = R.ok ? R.et : 0.f;
-    };
-
-    // a reverse chunk's rows into LDS: XQ, XK, XV - XK, dO and eta (zero past the end)
-    auto stage_rev = [&](const Rows &R) {
-#pragma unroll
-        for (int k = 0; k < NF; ++k) {
-            const int f = q + RW * k;
-            const float xk = R.ok ? io::load(R.xk, k) : 0.f;
-            sm.XK[r * DP + f] = xk;
-            sm.tau[r * DP + f] = R.ok ? io::load(R.xv, k) - xk : 0.f;
-            sm.XQ[r * DP + f] = R.ok ? io::load(R.xq, k) : 0.f;
-            sm.dO[r * DP + f] = R.ok ? R.go[k] : 0.f;
-        }
-        if (q == 0) sm.eta[r] = R.ok ? R.et : 0.f;
     };
     // one row of a [16 x D] tile (ld = 0: a [D] vector) for this row thread
     auto rowld = [&](const float *P, int ld, float (&z)[NF]) {
@@ -354,165 +360,168 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
         for (int k = 0; k < NF; ++k) z[k] = P[r * ld + q + RW * k];
     };
 
-    // ======================= forward sweep: chunk-start states ===================
-    // The state stays in registers in the result layout of its updates: wave w
-    // holds W1[16 rb + 4 g + i][32 w + 16 j + c] and W2[32 w + 16 j + 4 g + i][16 uu + c],
-    // which with the contraction order permuted identically is also the right
-    // operand of XK W1. W2 is mirrored in LDS for A W2 and E2 W2^T. Every chunk
-    // start is stored to the workspace (write-only).
-    f32x4 W1r[4][2], W2r[2][4];
-    float b1r[2], b2r = 0.f;
-    {
-        const float *s1 = W1_0 + st * D * M, *s2 = b1_0 + st * M, *s3 = W2_0 + st * M * D, *s4 = b2_0 + st * D;
+    if constexpr (MODE == FWD) {
+        // ======================= forward sweep: chunk-start states ===================
+        // The state stays in registers in the result layout of its updates: wave w
+        // holds W1[16 rb + 4 g + i][32 w + 16 j + c] and W2[32 w + 16 j + 4 g + i][16 uu + c],
+        // which with the contraction order permuted identically is also the right
+        // operand of XK W1. W2 is mirrored in LDS for A W2 and E2 W2^T. Every chunk
+        // start is stored to the workspace (write-only).
+        float gm[NF], bt[NF];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) W1r[rb][j][i] = gld(s1 + (16 * rb + i) * M + 32 * wu + 16 * j, le);
-#pragma unroll
-            for (int uu = 0; uu < 4; ++uu)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) W2r[j][uu][i] = gld(s3 + (32 * wu + 16 * j + i) * D + 16 * uu, lf);
-            b1r[j] = gld(s2 + 32 * wu + 16 * j, c);
+        for (int k = 0; k < NF; ++k) {
+            gm[k] = gamma[h * D + q + RW * k];
+            bt[k] = beta[h * D + q + RW * k];
         }
-        if (tid < D) b2r = s4[tid];
-    }
-    // the current state to the workspace checkpoint S and to the LDS mirror of W2
-    auto put_state = [&](float *Sn) {
+        f32x4 W1r[4][2], W2r[2][4];
+        float b1r[2], b2r = 0.f;
+        {
+            const float *s1 = W1_0 + st * D * M, *s2 = b1_0 + st * M, *s3 = W2_0 + st * M * D, *s4 = b2_0 + st * D;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < 2; ++j) {
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) gst4(Sn + (32 * wu + 16 * j) * D + 16 * rb, lg, W1r[rb][j]);
+                for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-            for (int uu = 0; uu < 4; ++uu)
+                    for (int i = 0; i < 4; ++i) W1r[rb][j][i] = gld(s1 + (16 * rb + i) * M + 32 * wu + 16 * j, le);
+#pragma unroll
+                for (int uu = 0; uu < 4; ++uu)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) W2r[j][uu][i] = gld(s3 + (32 * wu + 16 * j + i) * D + 16 * uu, lf);
+                b1r[j] = gld(s2 + 32 * wu + 16 * j, c);
+            }
+            if (tid < D) b2r = s4[tid];
+        }
+        // the current state to the workspace checkpoint S and to the LDS mirror of W2
+        auto put_state = [&](float *Sn) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) gst4(Sn + (32 * wu + 16 * j) * D + 16 * rb, lg, W1r[rb][j]);
+#pragma unroll
+                for (int uu = 0; uu < 4; ++uu)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        gst(Sn + OW2 + (32 * wu + 16 * j + i) * D + 16 * uu, lf, W2r[j][uu][i]);
+                        sf.W2[(32 * wu + 16 * j + 4 * g + i) * W2P + 16 * uu + c] = W2r[j][uu][i];
+                    }
+                if (g == 0) gst(Sn + OB1 + 32 * wu + 16 * j, c, b1r[j]);
+            }
+            if (tid < D) {
+                gst(Sn + OB2, tid, b2r);
+                sf.b2[tid] = b2r;
+            }
+        };
+        Rows R;
+        if (nch > 0) put_state(wsq);
+        if (rowt && nch > 1) fetch_rows(0, false, false, R);
+        for (int ch = 0; ch + 1 < nch; ++ch) {
+            float tau[NF], et = 0.f;
+            if (rowt) {
+#pragma unroll
+                for (int k = 0; k < NF; ++k) {
+                    const float xk = R.ok ? io::load(R.xk, k) : 0.f;
+                    sf.XK[r * DP + q + RW * k] = xk;
+                    tau[k] = R.ok ? io::load(R.xv, k) - xk : 0.f;
+                }
+                et = R.ok ? R.et : 0.f;
+                if (ch + 2 < nch) fetch_rows(ch + 1, false, false, R);
+            }
+            tile::lds_barrier();
+            // Z1 = XK W1 + b1 on the own hidden tiles (W1 from registers); A = gelu(Z1), P = gelu'(Z1)
+            f32x4 Ar[2], Pr[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                f32x4 z = bcast(b1r[j]);
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) z = mf(sf.XK[c * DP + 16 * rb + 4 * g + i], W1r[rb][j][i], z);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    gst(Sn + OW2 + (32 * wu + 16 * j + i) * D + 16 * uu, lf, W2r[j][uu][i]);
-                    sf.W2[(32 * wu + 16 * j + 4 * g + i) * W2P + 16 * uu + c] = W2r[j][uu][i];
+                    float g0, g1;
+                    gelu2(z[i], g0, g1);
+                    Ar[j][i] = g0;
+                    Pr[j][i] = g1;
                 }
-            if (g == 0) gst(Sn + OB1 + 32 * wu + 16 * j, c, b1r[j]);
-        }
-        if (tid < D) {
-            gst(Sn + OB2, tid, b2r);
-            sf.b2[tid] = b2r;
-        }
-    };
-    Rows R;
-    if (nch > 0) put_state(wsq);
-    if (rowt && nch > 1) fetch_rows(0, false, R);
-    for (int ch = 0; ch + 1 < nch; ++ch) {
-        float tau[NF], et = 0.f, go_unused[NF];
-        if (rowt) {
-            stage_rows(R, false, sf.XK, tau, et, go_unused);
-            if (ch + 2 < nch) fetch_rows(ch + 1, false, R);
-        }
-        tile::lds_barrier();
-        // Z1 = XK W1 + b1 on the own hidden tiles (W1 from registers); A = gelu(Z1), P = gelu'(Z1)
-        f32x4 Ar[2], Pr[2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            f32x4 z = bcast(b1r[j]);
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) z = mf(sf.XK[c * DP + 16 * rb + 4 * g + i], W1r[rb][j][i], z);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float g0, g1;
-                gelu2(z[i], g0, g1);
-                Ar[j][i] = g0;
-                Pr[j][i] = g1;
+                for (int i = 0; i < 4; ++i) sf.HA[(4 * g + i) * MP + hc0 + 16 * j] = Ar[j][i];
             }
+            tile::lds_barrier();
+            {  // Z2 = A W2 + b2, the two hidden halves (W2 from LDS)
+                f32x4 acc = hh == 0 ? bcast(sf.b2[16 * u + c]) : fz;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sf.HA[(4 * g + i) * MP + hc0 + 16 * j] = Ar[j][i];
-        }
-        tile::lds_barrier();
-        {  // Z2 = A W2 + b2, the two hidden halves (W2 from LDS)
-            f32x4 acc = hh == 0 ? bcast(sf.b2[16 * u + c]) : fz;
+                for (int kb = 0; kb < M / 8; ++kb) {
+                    const int k = M / 2 * hh + 4 * kb + g;
+                    acc = mf(sf.HA[c * MP + k], sf.W2[k * W2P + 16 * u + c], acc);
+                }
 #pragma unroll
-            for (int kb = 0; kb < M / 8; ++kb) {
-                const int k = M / 2 * hh + 4 * kb + g;
-                acc = mf(sf.HA[c * MP + k], sf.W2[k * W2P + 16 * u + c], acc);
+                for (int i = 0; i < 4; ++i) sf.part[hh][(4 * g + i) * DP + 16 * u + c] = acc[i];
             }
+            tile::lds_barrier();
+            if (rowt) {  // E2 = -eta lnl2(Z2, XV - XK)
+                float z[NF];
+                rowz2(sf.part[0], sf.part[1], z);
+                Lnl2 s;
+                lnl2(z, tau, gm, bt, s);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sf.part[hh][(4 * g + i) * DP + 16 * u + c] = acc[i];
+                for (int k = 0; k < NF; ++k) sf.E2[r * DP + q + RW * k] = -et * s.G[k];
+            }
+            tile::lds_barrier();
+            // E1 = (E2 W2^T) * P;  W1 += XK^T E1, b1 += 1^T E1;  W2 += A^T E2, b2 += 1^T E2
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                f32x4 qv = fz;
+#pragma unroll
+                for (int kb = 0; kb < D / 4; ++kb)
+                    qv = mf(sf.E2[c * DP + 4 * kb + g], sf.W2[(hc0 + 16 * j) * W2P + 4 * kb + g], qv);
+                f32x4 e1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) e1[i] = qv[i] * Pr[j][i];
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) W1r[rb][j] = xt_h(sf.XK, rb, e1, W1r[rb][j]);
+                b1r[j] += tile::rows4_sum((e1[0] + e1[1]) + (e1[2] + e1[3]));
+#pragma unroll
+                for (int uu = 0; uu < 4; ++uu) W2r[j][uu] = ht_y(Ar[j], sf.E2, uu, W2r[j][uu]);
+            }
+            if (tid < D) {
+                float cs = 0.f;
+                for (int t = 0; t < RW; ++t) cs += sf.E2[t * DP + tid];
+                b2r += cs;
+            }
+            tile::lds_barrier();  // every read of the W2 mirror is done
+            put_state(wsq + static_cast<size_t>(ch + 1) * CK);
         }
-        tile::lds_barrier();
-        if (rowt) {  // E2 = -eta lnl2(Z2, XV - XK)
-            float z[NF];
-            rowz2(sf.part[0], sf.part[1], z);
-            Lnl2 s;
-            lnl2(z, tau, gm, bt, s);
-#pragma unroll
-            for (int k = 0; k < NF; ++k) sf.E2[r * DP + q + RW * k] = -et * s.G[k];
-        }
-        tile::lds_barrier();
-        // E1 = (E2 W2^T) * P;  W1 += XK^T E1, b1 += 1^T E1;  W2 += A^T E2, b2 += 1^T E2
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            f32x4 qv = fz;
-#pragma unroll
-            for (int kb = 0; kb < D / 4; ++kb)
-                qv = mf(sf.E2[c * DP + 4 * kb + g], sf.W2[(hc0 + 16 * j) * W2P + 4 * kb + g], qv);
-            f32x4 e1;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) e1[i] = qv[i] * Pr[j][i];
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) W1r[rb][j] = xt_h(sf.XK, rb, e1, W1r[rb][j]);
-            b1r[j] += tile::rows4_sum((e1[0] + e1[1]) + (e1[2] + e1[3]));
-#pragma unroll
-            for (int uu = 0; uu < 4; ++uu) W2r[j][uu] = ht_y(Ar[j], sf.E2, uu, W2r[j][uu]);
-        }
-        if (tid < D) {
-            float cs = 0.f;
-            for (int t = 0; t < RW; ++t) cs += sf.E2[t * DP + tid];
-            b2r += cs;
-        }
-        tile::lds_barrier();  // every read of the W2 mirror is done
-        put_state(wsq + static_cast<size_t>(ch + 1) * CK);
     }
-    __syncthreads();
 
-    // ============================== reverse sweep ==================================
-    // the adjoint of the final state: the caller's dW1', db1', dW2', db2' (zero if absent)
-    float *a0 = adj(nch - 1);
-    if (nch > 0) {
-        for (int i = tid; i < D * M; i += NT) {
-            a0[(i % M) * D + i / M] = dW1_out ? dW1_out[sq * D * M + i] : 0.f;
-            a0[OW2 + i] = dW2_out ? dW2_out[sq * M * D + i] : 0.f;
-        }
-        if (tid < M) a0[OB1 + tid] = db1_out ? db1_out[sq * M + tid] : 0.f;
-        if (tid < D) a0[OB2 + tid] = db2_out ? db2_out[sq * D + tid] : 0.f;
-    } else {  // no tokens: the state passes through unchanged
-        for (int i = tid; i < D * M; i += NT) {
-            dW1[sq * D * M + i] = dW1_out ? dW1_out[sq * D * M + i] : 0.f;
-            dW2[sq * M * D + i] = dW2_out ? dW2_out[sq * M * D + i] : 0.f;
-        }
-        if (tid < M) db1[sq * M + tid] = db1_out ? db1_out[sq * M + tid] : 0.f;
-        if (tid < D) db2[sq * D + tid] = db2_out ? db2_out[sq * D + tid] : 0.f;
-    }
-    for (int i = tid; i < RW * DP; i += NT) sm.accg[i] = sm.accb[i] = 0.f;
-    if (tid < D) {
-        sm.gam[tid] = gamma[h * D + tid];
-        sm.bet[tid] = beta[h * D + tid];
-    }
-    Frag fA, fB;
-    for (int ch = nch - 1; ch >= 0; --ch) {
+    if constexpr (MODE == PRE) {
+        // ============ pre-pass: one chunk, everything independent of the adjoint ============
+        const int ch = static_cast<int>(blockIdx.x % nch);
         const int m = min(mb, L - ch * mb);
-        const bool ok = r < m;
         const float *S = wsq + static_cast<size_t>(ch) * CK;
-        const float *Ad = adj(ch);  // adjoint of this chunk's end state
-        float *dst1 = adj(ch + 1);  // adjoint of this chunk's start state
-        float *dstb1 = dst1 + OB1, *dst2 = dst1 + OW2, *dstb2 = dst1 + OB2;
-        __syncthreads();  // the previous chunk is done with every tile and its adjoint writes
-        if (rowt) {
-            fetch_rows(ch, true, R);
-            stage_rev(R);
+        float *rc = recq + static_cast<size_t>(ch) * REC;
+        for (int i = tid; i < RW * DP; i += NT) sm.accg[i] = sm.accb[i] = 0.f;
+        if (tid < D) {
+            sm.gam[tid] = gamma[h * D + tid];
+            sm.bet[tid] = beta[h * D + tid];
+        }
+        if (rowt) {  // the chunk's rows into LDS: XQ, XK, XV - XK, dO and eta (zero past the end)
+            Rows R;
+            fetch_rows(ch, true, true, R);
+#pragma unroll
+            for (int k = 0; k < NF; ++k) {
+                const int f = q + RW * k;
+                const float xk = R.ok ? io::load(R.xk, k) : 0.f;
+                sm.XK[r * DP + f] = xk;
+                sm.tau[r * DP + f] = R.ok ? io::load(R.xv, k) - xk : 0.f;
+                sm.XQ[r * DP + f] = R.ok ? io::load(R.xq, k) : 0.f;
+                sm.dO[r * DP + f] = R.ok ? R.go[k] : 0.f;
+            }
+            if (q == 0) sm.eta[r] = R.ok ? R.et : 0.f;
         }
         tile::lds_barrier();
 
         // Z1 = XK W1 + b1 and XQ W1 + b1 on the own hidden tiles; T1 slices
+        Frag fA;
         ld_vt(S, fA);  // W1 (stored transposed)
         issue();
         f32x4 Ar[2], Pr[2], Rr[2], ZQ[2];
@@ -536,6 +545,8 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
                 Rr[j][i] = g2;
             }
             put_h(sm.HA, j, Ar[j]);
+            put_rec(rc, HT_A, j, Ar[j]);
+            put_rec(rc, HT_P, j, Pr[j]);
         }
         if (w < 4) {  // T1 slice over features 16w..16w+15
             f32x4 t4 = fz;
@@ -548,15 +559,14 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
         tile::lds_barrier();
 
         // Z2 = A W2 + b2 (two halves);  T1 = tril(XQ XK^T + 1)
-        Frag fW;  // W2 rows of this wave's hidden half, held for A W2, Ab W2 and dQ W2
+        Frag fW;  // W2 rows of this wave's hidden half, held for A W2 and Ab W2
         ld_v(S + OW2, fW);
         issue();
         put_d(sm.part[hh], mm_y(sm.HA, fW, hh == 0 ? bcast(gld(S + OB2 + 16 * u, c)) : fz));
         tri_sum(sm.T1, 4, 1.f, m);
         tile::lds_barrier();
 
-        float l_sigma = 1.f, l_c = 0.f;
-        if (rowt) {  // E2 = -eta lnl2(Z2, XV - XK)
+        if (rowt) {  // E2 = -eta lnl2(Z2, XV - XK); the lnl2 values its reverse needs go to the record
             float z[NF], tau[NF], gm[NF], bt[NF];
             rowz2(sm.part[0], sm.part[1], z);
             rowld(sm.tau, DP, tau);
@@ -567,20 +577,21 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
             lnl2(z, tau, gm, bt, s);
 #pragma unroll
             for (int k = 0; k < NF; ++k) {
-                const int o = r * DP + q + RW * k;
                 sm.E2[r * DP + q + RW * k] = -et * s.G[k];
-                sm.lxh[o] = s.xh[k];
-                sm.lgh[o] = s.gh[k];
-                sm.lG[o] = s.G[k];
+                gst(rc + rrow(RT_XH) + RW * k, lrq, s.xh[k]);
+                gst(rc + rrow(RT_GH) + RW * k, lrq, s.gh[k]);
+                gst(rc + rrow(RT_G) + RW * k, lrq, s.G[k]);
             }
-            l_sigma = s.sigma;
-            l_c = s.c;
+            if (q == 0) {
+                gst(rc + OS, r, s.sigma);
+                gst(rc + OS + RW, r, s.c);
+            }
         }
         tile::lds_barrier();
 
         // Q = E2 W2^T, E1 = Q * P;  Zb1 = XQ W1 + b1 + T1 E1, Ab = gelu(Zb1), Pb = gelu'(Zb1)
         f32x4 E1r[2], Abr[2], Pbr[2];
-        Frag fT;  // W2^T of this wave's hidden units, held for E2 W2^T, dZb2 W2^T and dZ2 W2^T
+        Frag fT;  // W2^T of this wave's hidden units, held for E2 W2^T and dZb2 W2^T
         ld_vt(S + OW2, fT);
         issue();
 #pragma unroll
@@ -592,6 +603,8 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
                 Rr[j][i] *= qv[i];  // Q * GELU''(Z1), the factor of dE1 in dZ1
             }
             put_h(sm.HE, j, E1r[j]);
+            put_rec(rc, HT_E1, j, E1r[j]);
+            put_rec(rc, HT_RQ, j, Rr[j]);
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -606,6 +619,7 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
                 Pbr[j][i] = g1;
             }
             put_h(sm.HY, j, Abr[j]);
+            put_rec(rc, HT_AB, j, Abr[j]);
         }
         tile::lds_barrier();
 
@@ -647,18 +661,32 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
                 const int o = r * DP + q + RW * k;
                 xb[k] = (zb[k] - mu) * rs;
                 dx[k] = gm[k] * go[k];
-                sm.accg[o] = fmaf(go[k], xb[k], sm.accg[o]);
-                sm.accb[o] += go[k];
+                sm.accg[o] = go[k] * xb[k];
+                sm.accb[o] = go[k];
                 m1 += dx[k];
                 m2 += dx[k] * xb[k];
             }
             m1 = tile::row16_sum(m1) * inv_d;
             m2 = tile::row16_sum(m2) * inv_d;
 #pragma unroll
-            for (int k = 0; k < NF; ++k) sm.dZb2[r * DP + q + RW * k] = (dx[k] - m1 - xb[k] * m2) * rs;
+            for (int k = 0; k < NF; ++k) {
+                const float v = (dx[k] - m1 - xb[k] * m2) * rs;
+                sm.dZb2[r * DP + q + RW * k] = v;
+                gst(rc + rrow(RT_DZB2) + RW * k, lrq, v);
+            }
         }
         tile::lds_barrier();
 
+        // the chunk's share of dgamma, dbeta: the output layer norm's sums over its rows
+        if (tid < D) {
+            float a = 0.f, b = 0.f;
+            for (int rr = 0; rr < RW; ++rr) {
+                a += sm.accg[rr * DP + tid];
+                b += sm.accb[rr * DP + tid];
+            }
+            gst(rc + OGB, tid, a);
+            gst(rc + OGB + D, tid, b);
+        }
         // dT2 = tril(dZb2 E2^T) (every wave its own copy, result layout: row t = 4g+i, column s = c)
         f32x4 dt2 = fz;
 #pragma unroll
@@ -668,16 +696,13 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
             if (c > 4 * g + i) dt2[i] = 0.f;
             sm.gp[w][(4 * g + i) * TP + c] = dt2[i];
         }
-        // dE2 (first parts) = A dW2' + T2^T dZb2 + db2' (two halves)
-        {
-            ld_v(Ad + OW2, fB);
-            issue();
-            f32x4 e = mm_y(sm.HA, fB, hh == 0 ? bcast(gld(Ad + OB2 + 16 * u, c)) : fz);
-            if (hh == 0) e = t_x(sm.T2, true, sm.dZb2, e);
-            put_d(sm.partE[hh], e);
+        if (hh == 0) {  // T2^T dZb2, the adjoint-free part of dE2
+            const f32x4 e = t_x(sm.T2, true, sm.dZb2, fz);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gst(rc + rrow(RT_T2Z) + i * D + 16 * u, lf, e[i]);
         }
-        // dAb = dZb2 W2^T + dT2 A, dZb1 = dAb * Pb;  dA (first part) = dT2^T Ab
-        f32x4 dZb1r[2], dAr[2];
+        // dAb = dZb2 W2^T + dT2 A, dZb1 = dAb * Pb;  dT2^T Ab, the adjoint-free part of dA
+        f32x4 dZb1r[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             f32x4 v = mm_xt(sm.dZb2, fT, j, fz);
@@ -686,15 +711,15 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) dZb1r[j][i] = v[i] * Pbr[j][i];
             put_h(sm.HX, j, dZb1r[j]);
+            put_rec(rc, HT_DZB1, j, dZb1r[j]);
             f32x4 a = fz;
 #pragma unroll
             for (int i = 0; i < 4; ++i) a = mf(dt2[i], Abr[j][i], a);
-            dAr[j] = a;
+            put_rec(rc, HT_DAT, j, a);
         }
         tile::lds_barrier();
 
-        // slices of dT1 = dZb1 E1^T over the own hidden units;
-        // dE1 = T1^T dZb1 + XK dW1' + db1' (zero on rows past the chunk), dQ = dE1 * P
+        // slices of dT1 = dZb1 E1^T over the own hidden units;  T1^T dZb1, the adjoint-free part of dE1
         {
             f32x4 t4 = fz;
 #pragma unroll
@@ -703,182 +728,344 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) sm.gp[w][(4 * g + i) * TP + c] = t4[i];
         }
-        f32x4 dQr[2];
-        ld_vt(Ad, fA);  // dW1' (transposed)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) put_rec(rc, HT_TZ, j, tt_h(sm.T1, dZb1r[j], fz));
+        ld_v(S, fA);  // W1 (stored transposed), for dZb1 W1^T
         issue();
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            f32x4 de = mm_xt(sm.XK, fA, j, bcast(gld(Ad + OB1 + 32 * wu + 16 * j, c)));
-            de = tt_h(sm.T1, dZb1r[j], de);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float v = 4 * g + i < m ? de[i] : 0.f;
-                dQr[j][i] = v * Pr[j][i];
-                Rr[j][i] *= v;  // dE1 * Q * GELU''(Z1)
-            }
-            put_h(sm.HY, j, dQr[j]);
-        }
         tile::lds_barrier();
-
-        // dT1 = tril(sum of the slices);  dE2 += dQ W2 (two halves)
         tri_sum(sm.dT1, NT / 64, 0.f, m);
-        put_d(sm.partE[hh], mm_y(sm.HY, fW, get_d(sm.partE[hh])));
         tile::lds_barrier();
 
-        if (rowt) {  // deta = -G2 . dE2;  dG2 = -eta dE2;  reverse of lnl2 -> dZ2, dtau
-            Lnl2 s;
-#pragma unroll
-            for (int k = 0; k < NF; ++k) {
-                const int o = r * DP + q + RW * k;
-                s.xh[k] = sm.lxh[o];
-                s.gh[k] = sm.lgh[o];
-                s.G[k] = sm.lG[o];
-            }
-            s.sigma = l_sigma;
-            s.c = l_c;
-            float de[NF], tau[NF], gm[NF], bt[NF];
-            rowz2(sm.partE[0], sm.partE[1], de);
-            rowld(sm.tau, DP, tau);
-            rowld(sm.gam, 0, gm);
-            rowld(sm.bet, 0, bt);
-            const float et = sm.eta[r];
-            float pe = 0.f;
-#pragma unroll
-            for (int k = 0; k < NF; ++k) pe = fmaf(s.G[k], de[k], pe);
-            const float d_eta = -tile::row16_sum(pe);
-            float dG[NF], mdg = 0.f, mdgx = 0.f, sgG = 0.f;
-#pragma unroll
-            for (int k = 0; k < NF; ++k) {
-                dG[k] = -et * de[k];
-                mdg += dG[k];
-                mdgx += dG[k] * s.xh[k];
-                sgG += dG[k] * s.G[k];
-            }
-            mdg = tile::row16_sum(mdg) * inv_d;
-            mdgx = tile::row16_sum(mdgx) * inv_d;
-            const float rs = 1.0f / s.sigma;
-            const float dsig = -tile::row16_sum(sgG) * rs;
-            float dxh[NF], mdx = 0.f, mdxx = 0.f;
-#pragma unroll
-            for (int k = 0; k < NF; ++k) {
-                const float dgh = (dG[k] - mdg - s.xh[k] * mdgx) * rs;
-                dxh[k] = gm[k] * gm[k] * dgh - (s.c * dG[k] + s.gh[k] * mdgx) * rs;
-                sm.dtau[r * DP + q + RW * k] = ok ? -gm[k] * dgh : 0.f;
-                const int o = r * DP + q + RW * k;
-                sm.accg[o] = fmaf(dgh, fmaf(2.f * gm[k], s.xh[k], bt[k] - tau[k]), sm.accg[o]);
-                sm.accb[o] = fmaf(gm[k], dgh, sm.accb[o]);
-                mdx += dxh[k];
-                mdxx += dxh[k] * s.xh[k];
-            }
-            mdx = tile::row16_sum(mdx) * inv_d;
-            mdxx = tile::row16_sum(mdxx) * inv_d;
-#pragma unroll
-            for (int k = 0; k < NF; ++k) {
-                const float dz = fmaf(dsig * inv_d, s.xh[k], (dxh[k] - mdx - s.xh[k] * mdxx) * rs);
-                sm.dZ2[r * DP + q + RW * k] = ok ? dz : 0.f;
-            }
-            if (ok && q == 0) deta[sq * L + ch * mb + r] = d_eta;
-        }
-        tile::lds_barrier();
-
-        // dA += E2 dW2'^T + dZ2 W2^T;  dZ1 = dA * P + dE1 * Q * GELU'';
-        // the adjoint state of the chunk start: dW2, dW1, db1, db2
-        f32x4 dZ1r[2];
-        ld_vt(Ad + OW2, fA);
-        issue();
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            f32x4 a = mm_xt(sm.E2, fA, j, dAr[j]);
-            a = mm_xt(sm.dZ2, fT, j, a);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dZ1r[j][i] = fmaf(a[i], Pr[j][i], Rr[j][i]);
-            put_h(sm.HY, j, dZ1r[j]);
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            // dW2 = dW2' + Ab^T dZb2 + dQ^T E2 + A^T dZ2, accumulated transposed: a lane
-            // holds four consecutive features of one hidden unit's row of dW2
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                const float *src = Ad + OW2 + (32 * wu + 16 * j) * D + 16 * rb;
-                f32x4 acc = gld4(src, lg);
-                acc = xt_h(sm.dZb2, rb, Abr[j], acc);
-                acc = xt_h(sm.E2, rb, dQr[j], acc);
-                acc = xt_h(sm.dZ2, rb, Ar[j], acc);
-                gst4(dst2 + (32 * wu + 16 * j) * D + 16 * rb, lg, acc);
-            }
-            // dW1 = dW1' + XQ^T dZb1 + XK^T dZ1: four consecutive features of one hidden
-            // unit's row of the transposed dW1
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                f32x4 acc = gld4(Ad + (32 * wu + 16 * j) * D + 16 * rb, lg);
-                acc = xt_h(sm.XQ, rb, dZb1r[j], acc);
-                acc = xt_h(sm.XK, rb, dZ1r[j], acc);
-                gst4(dst1 + (32 * wu + 16 * j) * D + 16 * rb, lg, acc);
-            }
-            const float cs = tile::rows4_sum((dZb1r[j][0] + dZ1r[j][0]) + (dZb1r[j][1] + dZ1r[j][1]) +
-                                             ((dZb1r[j][2] + dZ1r[j][2]) + (dZb1r[j][3] + dZ1r[j][3])));
-            if (g == 0) gst(dstb1 + 32 * wu + 16 * j, c, gld(Ad + OB1 + 32 * wu + 16 * j, c) + cs);
-        }
-        if (tid < D) {
-            float cs = 0.f;
-            for (int t = 0; t < RW; ++t) cs += sm.dZb2[t * DP + tid] + sm.dZ2[t * DP + tid];
-            gst(dstb2, tid, gld(Ad, OB2 + tid) + cs);
-        }
-        tile::lds_barrier();
-
-        // dXQ = dO + dZb1 W1^T + dT1 XK;  dXK = dT1^T XQ + E1 dW1'^T + dZ1 W1^T - dtau (halves)
+        // dXQ = dO + dZb1 W1^T + dT1 XK (halves);  dT1^T XQ, the adjoint-free part of dXK
         {
-            ld_v(S, fA);   // W1 (stored transposed), for dZb1 W1^T and dZ1 W1^T
-            ld_v(Ad, fB);  // dW1' (transposed), for E1 dW1'^T
-            issue();
             f32x4 aq = hh == 0 ? t_x(sm.dT1, false, sm.XK, fz) : fz;
-            f32x4 ak = hh == 0 ? t_x(sm.dT1, true, sm.XQ, fz) : fz;
             aq = mm_y(sm.HX, fA, aq);
-            ak = mm_y(sm.HY, fA, ak);
-            ak = mm_y(sm.HE, fB, ak);
             put_d(sm.part[hh], aq);
-            put_d(sm.partE[hh], ak);
+            if (hh == 0) put_d(sm.partE[0], t_x(sm.dT1, true, sm.XQ, fz));
         }
         tile::lds_barrier();
         for (int e = tid; e < RW * D; e += NT) {
             const int t = e / D, f = e % D;
             if (t < m) {
                 const size_t at = xbase + static_cast<size_t>(ch * mb + t) * D + f;
-                const float dt = sm.dtau[t * DP + f];
                 dXQ[at] = sm.part[0][t * DP + f] + sm.part[1][t * DP + f] + sm.dO[t * DP + f];
-                dXK[at] = sm.partE[0][t * DP + f] + sm.partE[1][t * DP + f] - dt;
-                dXV[at] = dt;
+                dXK[at] = sm.partE[0][t * DP + f];
             }
         }
     }
-    __syncthreads();
-    if (nch > 0) {  // the adjoint of the initial state, from the workspace to the outputs
-        const float *a = adj(1);
-        for (int i = tid; i < D * M; i += NT) {
-            dW1[sq * D * M + i] = a[(i % M) * D + i / M];
-            dW2[sq * M * D + i] = a[OW2 + i];
-        }
-        if (tid < M) db1[sq * M + tid] = a[OB1 + tid];
-        if (tid < D) db2[sq * D + tid] = a[OB2 + tid];
-    }
 
-    // per-sequence dgamma, dbeta: sum the 16 row groups
-    if (tid < D) {
-        float a = 0.f, b = 0.f;
-        for (int rr = 0; rr < RW; ++rr) {
-            a += sm.accg[rr * DP + tid];
-            b += sm.accb[rr * DP + tid];
+    if constexpr (MODE == REV) {
+        // ================= reverse sweep: the adjoint-dependent rest ==================
+        // the adjoint of the final state: the caller's dW1', db1', dW2', db2' (zero if absent)
+        float *a0 = adj(nch - 1);
+        if (nch > 0) {
+            for (int i = tid; i < D * M; i += NT) {
+                a0[(i % M) * D + i / M] = dW1_out ? dW1_out[sq * D * M + i] : 0.f;
+                a0[OW2 + i] = dW2_out ? dW2_out[sq * M * D + i] : 0.f;
+            }
+            if (tid < M) a0[OB1 + tid] = db1_out ? db1_out[sq * M + tid] : 0.f;
+            if (tid < D) a0[OB2 + tid] = db2_out ? db2_out[sq * D + tid] : 0.f;
+        } else {  // no tokens: the state passes through unchanged
+            for (int i = tid; i < D * M; i += NT) {
+                dW1[sq * D * M + i] = dW1_out ? dW1_out[sq * D * M + i] : 0.f;
+                dW2[sq * M * D + i] = dW2_out ? dW2_out[sq * M * D + i] : 0.f;
+            }
+            if (tid < M) db1[sq * M + tid] = db1_out ? db1_out[sq * M + tid] : 0.f;
+            if (tid < D) db2[sq * D + tid] = db2_out ? db2_out[sq * D + tid] : 0.f;
         }
-        dgamma[sq * D + tid] = a;
-        dbeta[sq * D + tid] = b;
+        for (int i = tid; i < RW * DP; i += NT) sm.accg[i] = sm.accb[i] = 0.f;
+        if (tid < D) {
+            sm.gam[tid] = gamma[h * D + tid];
+            sm.bet[tid] = beta[h * D + tid];
+        }
+        float accG = 0.f, accB = 0.f;  // the output layer norm's dgamma, dbeta from the records
+        // A chunk's staged values, loaded during the previous chunk: two consecutive
+        // features (f, f + 1) of token row t of the inputs, of the record's row tensors
+        // and of the pre-pass's part of dXK, the row's eta, and sigma, c of row tid % 16.
+        using pio = pair_io<TIO>;
+        const int at_t = tid >> 5, at_f = 2 * (tid & 31);
+        struct Ahead {
+            typename pio::raw xq, xk, xv;
+            tile::f32x2 xh, gh, G, dzb2, dxk;
+            float et, sig, cc;
+            bool ok;
+        };
+        auto load_ahead = [&](int ch, Ahead &N) {
+            const int mc = min(mb, L - ch * mb);
+            N.ok = at_t < mc;
+            const unsigned o = (N.ok ? at_t : 0) * D + at_f, orec = at_t * D + at_f;
+            const size_t r0 = xbase + static_cast<size_t>(ch) * mb * D;
+            const float *rc = recq + static_cast<size_t>(ch) * REC;
+            N.xq = pio::ld(XQ + r0, o);
+            N.xk = pio::ld(XK + r0, o);
+            N.xv = pio::ld(XV + r0, o);
+            N.xh = gld2(rc + rrow(RT_XH), orec);
+            N.gh = gld2(rc + rrow(RT_GH), orec);
+            N.G = gld2(rc + rrow(RT_G), orec);
+            N.dzb2 = gld2(rc + rrow(RT_DZB2), orec);
+            N.dxk = gld2(dXK + r0, o);
+            N.et = gld(eta + sq * L + static_cast<size_t>(ch) * mb, N.ok ? at_t : 0);
+            N.sig = gld(rc + OS, tid & (RW - 1));
+            N.cc = gld(rc + OS + RW, tid & (RW - 1));
+        };
+        // into LDS: XQ, XK, XV - XK, E2 = -eta G2, dZb2, the lnl2 rows, eta, sigma, c, the dXK part
+        // (inputs and eta zero on rows past the chunk)
+        auto stage_ahead = [&](const Ahead &N) {
+            const int o = at_t * DP + at_f;
+            const float et = N.ok ? N.et : 0.f;
+            const float q0 = N.ok ? pio::lo(N.xq) : 0.f, q1 = N.ok ? pio::hi(N.xq) : 0.f;
+            const float k0 = N.ok ? pio::lo(N.xk) : 0.f, k1 = N.ok ? pio::hi(N.xk) : 0.f;
+            const float v0 = N.ok ? pio::lo(N.xv) : 0.f, v1 = N.ok ? pio::hi(N.xv) : 0.f;
+            sm.XQ[o] = q0;
+            sm.XQ[o + 1] = q1;
+            sm.XK[o] = k0;
+            sm.XK[o + 1] = k1;
+            sm.tau[o] = v0 - k0;
+            sm.tau[o + 1] = v1 - k1;
+            sm.lxh[o] = N.xh[0];
+            sm.lxh[o + 1] = N.xh[1];
+            sm.lgh[o] = N.gh[0];
+            sm.lgh[o + 1] = N.gh[1];
+            sm.lG[o] = N.G[0];
+            sm.lG[o + 1] = N.G[1];
+            sm.E2[o] = -et * N.G[0];
+            sm.E2[o + 1] = -et * N.G[1];
+            sm.dZb2[o] = N.dzb2[0];
+            sm.dZb2[o + 1] = N.dzb2[1];
+            sm.part[0][o] = N.dxk[0];
+            sm.part[0][o + 1] = N.dxk[1];
+            if ((tid & 31) == 0) sm.eta[at_t] = et;
+            if (tid < RW) {
+                sm.lsig[tid] = N.sig;
+                sm.lcc[tid] = N.cc;
+            }
+        };
+        Frag fA, fB, fW;
+        Ahead N;
+        if (nch > 0) load_ahead(nch - 1, N);
+        for (int ch = nch - 1; ch >= 0; --ch) {
+            const int m = min(mb, L - ch * mb);
+            const bool ok = r < m;
+            const float *S = wsq + static_cast<size_t>(ch) * CK;
+            const float *rc = recq + static_cast<size_t>(ch) * REC;
+            const float *Ad = adj(ch);  // adjoint of this chunk's end state
+            float *dst1 = adj(ch + 1);  // adjoint of this chunk's start state
+            float *dstb1 = dst1 + OB1, *dst2 = dst1 + OW2, *dstb2 = dst1 + OB2;
+            __syncthreads();  // the previous chunk is done with every tile and its adjoint writes
+            stage_ahead(N);
+            // the record's hidden tiles of the first phases (own tiles of this wave)
+            f32x4 Ar[2], Pr[2], Rr[2], TZr[2], E1r[2], Abr[2], dZb1r[2], dAr[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                TZr[j] = get_rec(rc, HT_TZ, j);
+                Pr[j] = get_rec(rc, HT_P, j);
+                Rr[j] = get_rec(rc, HT_RQ, j);
+                Ar[j] = get_rec(rc, HT_A, j);
+                E1r[j] = get_rec(rc, HT_E1, j);
+            }
+            f32x4 t2z = fz;
+            if (hh == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) t2z[i] = gld(rc + rrow(RT_T2Z) + i * D + 16 * u, lf);
+            }
+            if (tid < D) {
+                accG += gld(rc + OGB, tid);
+                accB += gld(rc + OGB + D, tid);
+            }
+            ld_vt(Ad, fA);  // dW1' (transposed)
+            const float db1v[2] = {gld(Ad + OB1 + 32 * wu, c), gld(Ad + OB1 + 32 * wu + 16, c)};
+            const float db2v = tid < D ? gld(Ad, OB2 + tid) : 0.f;
+            issue();
+            tile::lds_barrier();
+
+            // dE1 = T1^T dZb1 + XK dW1' + db1' (zero on rows past the chunk), dQ = dE1 * P;
+            // A and E1 into LDS for the products over the hidden units
+            f32x4 dQr[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                f32x4 de = mm_xt(sm.XK, fA, j, bcast(db1v[j]));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float v = 4 * g + i < m ? de[i] + TZr[j][i] : 0.f;
+                    dQr[j][i] = v * Pr[j][i];
+                    Rr[j][i] *= v;  // dE1 * Q * GELU''(Z1)
+                }
+                put_h(sm.HY, j, dQr[j]);
+                put_h(sm.HA, j, Ar[j]);
+                put_h(sm.HE, j, E1r[j]);
+            }
+            ld_v(Ad + OW2, fB);  // dW2'
+            ld_v(S + OW2, fW);   // W2
+            issue();
+            tile::lds_barrier();
+
+            // dE2 = T2^T dZb2 + db2' + A dW2' + dQ W2 (two halves)
+            {
+                f32x4 e = hh == 0 ? t2z + bcast(gld(Ad + OB2 + 16 * u, c)) : fz;
+                e = mm_y(sm.HA, fB, e);
+                e = mm_y(sm.HY, fW, e);
+                put_d(sm.partE[hh], e);
+            }
+            ld_vt(Ad + OW2, fA);  // dW2' (transposed)
+            ld_vt(S + OW2, fB);   // W2^T
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {  // the record's tiles for dA and the adjoint-state update
+                dAr[j] = get_rec(rc, HT_DAT, j);
+                Abr[j] = get_rec(rc, HT_AB, j);
+                dZb1r[j] = get_rec(rc, HT_DZB1, j);
+            }
+            issue();
+            tile::lds_barrier();
+
+            if (rowt) {  // deta = -G2 . dE2;  dG2 = -eta dE2;  reverse of lnl2 -> dZ2, dtau
+                float de[NF], gm[NF], bt[NF], lxh[NF], lgh[NF], lG[NF], tau[NF];
+                rowz2(sm.partE[0], sm.partE[1], de);
+                rowld(sm.gam, 0, gm);
+                rowld(sm.bet, 0, bt);
+                rowld(sm.lxh, DP, lxh);
+                rowld(sm.lgh, DP, lgh);
+                rowld(sm.lG, DP, lG);
+                rowld(sm.tau, DP, tau);
+                const float et = sm.eta[r], l_sigma = sm.lsig[r], l_c = sm.lcc[r];
+                float pe = 0.f;
+#pragma unroll
+                for (int k = 0; k < NF; ++k) pe = fmaf(lG[k], de[k], pe);
+                const float d_eta = -tile::row16_sum(pe);
+                float dG[NF], mdg = 0.f, mdgx = 0.f, sgG = 0.f;
+#pragma unroll
+                for (int k = 0; k < NF; ++k) {
+                    dG[k] = -et * de[k];
+                    mdg += dG[k];
+                    mdgx += dG[k] * lxh[k];
+                    sgG += dG[k] * lG[k];
+                }
+                mdg = tile::row16_sum(mdg) * inv_d;
+                mdgx = tile::row16_sum(mdgx) * inv_d;
+                const float rs = 1.0f / l_sigma;
+                const float dsig = -tile::row16_sum(sgG) * rs;
+                float dxh[NF], mdx = 0.f, mdxx = 0.f;
+#pragma unroll
+                for (int k = 0; k < NF; ++k) {
+                    const int o = r * DP + q + RW * k;
+                    const float dgh = (dG[k] - mdg - lxh[k] * mdgx) * rs;
+                    dxh[k] = gm[k] * gm[k] * dgh - (l_c * dG[k] + lgh[k] * mdgx) * rs;
+                    sm.dtau[o] = ok ? -gm[k] * dgh : 0.f;
+                    sm.accg[o] = fmaf(dgh, fmaf(2.f * gm[k], lxh[k], bt[k] - tau[k]), sm.accg[o]);
+                    sm.accb[o] = fmaf(gm[k], dgh, sm.accb[o]);
+                    mdx += dxh[k];
+                    mdxx += dxh[k] * lxh[k];
+                }
+                mdx = tile::row16_sum(mdx) * inv_d;
+                mdxx = tile::row16_sum(mdxx) * inv_d;
+#pragma unroll
+                for (int k = 0; k < NF; ++k) {
+                    const float dz = fmaf(dsig * inv_d, lxh[k], (dxh[k] - mdx - lxh[k] * mdxx) * rs);
+                    sm.dZ2[r * DP + q + RW * k] = ok ? dz : 0.f;
+                }
+                if (ok && q == 0) gst(deta + sq * L + static_cast<size_t>(ch) * mb, r, d_eta);
+            }
+            tile::lds_barrier();
+
+            // dA = dT2^T Ab + E2 dW2'^T + dZ2 W2^T;  dZ1 = dA * P + dE1 * Q * GELU'';
+            // the adjoint state of the chunk start: dW2, dW1, db1, db2
+            f32x4 dZ1r[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                f32x4 a = mm_xt(sm.E2, fA, j, dAr[j]);
+                a = mm_xt(sm.dZ2, fB, j, a);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dZ1r[j][i] = fmaf(a[i], Pr[j][i], Rr[j][i]);
+                put_h(sm.HY, j, dZ1r[j]);
+            }
+            // the dW1' tiles, read while the dW2 tiles are formed (layout of ld_vt)
+            ld_vt(Ad, fB);
+            issue();
+            // dW2 = dW2' + Ab^T dZb2 + dQ^T E2 + A^T dZ2, accumulated transposed: a lane holds
+            // four consecutive features of one hidden unit's row of dW2 -- the layout of the
+            // dW2'^T fragment, which therefore starts each accumulator
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) {
+                    f32x4 acc = {fA[16 * j + 4 * rb], fA[16 * j + 4 * rb + 1], fA[16 * j + 4 * rb + 2],
+                                 fA[16 * j + 4 * rb + 3]};
+                    acc = xt_h(sm.dZb2, rb, Abr[j], acc);
+                    acc = xt_h(sm.E2, rb, dQr[j], acc);
+                    acc = xt_h(sm.dZ2, rb, Ar[j], acc);
+                    gst4(dst2 + (32 * wu + 16 * j) * D + 16 * rb, lg, acc);
+                }
+            ld_v(S, fA);  // W1 (stored transposed), for dZ1 W1^T
+            issue();
+            // dW1 = dW1' + XQ^T dZb1 + XK^T dZ1: four consecutive features of one hidden unit's
+            // row of the transposed dW1
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) {
+                    f32x4 acc = {fB[16 * j + 4 * rb], fB[16 * j + 4 * rb + 1], fB[16 * j + 4 * rb + 2],
+                                 fB[16 * j + 4 * rb + 3]};
+                    acc = xt_h(sm.XQ, rb, dZb1r[j], acc);
+                    acc = xt_h(sm.XK, rb, dZ1r[j], acc);
+                    gst4(dst1 + (32 * wu + 16 * j) * D + 16 * rb, lg, acc);
+                }
+                const float cs = tile::rows4_sum((dZb1r[j][0] + dZ1r[j][0]) + (dZb1r[j][1] + dZ1r[j][1]) +
+                                                 ((dZb1r[j][2] + dZ1r[j][2]) + (dZb1r[j][3] + dZ1r[j][3])));
+                if (g == 0) gst(dstb1 + 32 * wu + 16 * j, c, db1v[j] + cs);
+            }
+            if (tid < D) {
+                float cs = 0.f;
+                for (int t = 0; t < RW; ++t) cs += sm.dZb2[t * DP + tid] + sm.dZ2[t * DP + tid];
+                gst(dstb2, tid, db2v + cs);
+            }
+            ld_v(Ad, fB);  // dW1' (transposed), for E1 dW1'^T
+            load_ahead(max(ch - 1, 0), N);  // unconditional: the last chunk reloads chunk 0
+            issue();
+            tile::lds_barrier();
+
+            // dXK = dT1^T XQ + E1 dW1'^T + dZ1 W1^T - dtau (halves);  dXV = dtau
+            put_d(sm.partE[hh], mm_y(sm.HE, fB, mm_y(sm.HY, fA, fz)));
+            tile::lds_barrier();
+            {
+                float *const oK = dXK + xbase + static_cast<size_t>(ch) * mb * D;
+                float *const oV = dXV + xbase + static_cast<size_t>(ch) * mb * D;
+                for (int e = tid; e < RW * D; e += NT) {
+                    const int t = e / D, f = e % D;
+                    if (t < m) {
+                        const float dt = sm.dtau[t * DP + f];
+                        gst(oK, e, sm.part[0][t * DP + f] + sm.partE[0][t * DP + f] + sm.partE[1][t * DP + f] - dt);
+                        gst(oV, e, dt);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        if (nch > 0) {  // the adjoint of the initial state, from the workspace to the outputs
+            const float *a = adj(1);
+            for (int i = tid; i < D * M; i += NT) {
+                dW1[sq * D * M + i] = a[(i % M) * D + i / M];
+                dW2[sq * M * D + i] = a[OW2 + i];
+            }
+            if (tid < M) db1[sq * M + tid] = a[OB1 + tid];
+            if (tid < D) db2[sq * D + tid] = a[OB2 + tid];
+        }
+
+        // per-sequence dgamma, dbeta: the 16 row groups of the lnl2 reverse plus the output norm's share
+        if (tid < D) {
+            float a = accG, b = accB;
+            for (int rr = 0; rr < RW; ++rr) {
+                a += sm.accg[rr * DP + tid];
+                b += sm.accb[rr * DP + tid];
+            }
+            dgamma[sq * D + tid] = a;
+            dbeta[sq * D + tid] = b;
+        }
     }
 }
 
-template <typename TIO>
-hipError_t launch_t(const MLPBwdArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL((mlp_backward_kernel<TIO>), dim3(a.f.B * a.f.H), dim3(NT), 0, stream, a.f.H, a.f.L,
-                       a.f.mb, a.f.eps, static_cast<const TIO *>(a.f.XQ), static_cast<const TIO *>(a.f.XK),
+template <typename TIO, int MODE>
+hipError_t launch_mode(const MLPBwdArgs &a, unsigned grid, hipStream_t stream) {
+    hipLaunchKernelGGL((mlp_backward_kernel<TIO, MODE>), dim3(grid), dim3(NT), 0, stream, a.f.B * a.f.H, a.f.H,
+                       a.f.L, a.f.mb, a.f.eps, static_cast<const TIO *>(a.f.XQ), static_cast<const TIO *>(a.f.XK),
                        static_cast<const TIO *>(a.f.XV), a.f.eta, a.f.W1, a.f.b1, a.f.W2, a.f.b2,
                        a.f.w0_batched, a.f.gamma, a.f.beta, a.dO, a.dW1_out, a.db1_out, a.dW2_out,
                        a.db2_out, a.dXQ, a.dXK, a.dXV, a.deta, a.dW1, a.db1, a.dW2, a.db2, a.dgamma,
@@ -886,12 +1073,25 @@ hipError_t launch_t(const MLPBwdArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <typename TIO>
+hipError_t launch_t(const MLPBwdArgs &a, hipStream_t stream) {
+    const size_t nseq = static_cast<size_t>(a.f.B) * a.f.H;
+    const size_t nch = a.f.L > 0 ? static_cast<size_t>((a.f.L + a.f.mb - 1) / a.f.mb) : 0;
+    if (nseq * nch > 0x7fffffffu) return hipErrorInvalidValue;
+    hipError_t e;
+    if (nch > 0) {
+        if ((e = launch_mode<TIO, FWD>(a, static_cast<unsigned>(nseq), stream)) != hipSuccess) return e;
+        if ((e = launch_mode<TIO, PRE>(a, static_cast<unsigned>(nseq * nch), stream)) != hipSuccess) return e;
+    }
+    return launch_mode<TIO, REV>(a, static_cast<unsigned>(nseq), stream);
+}
+
 }  // namespace
 
-size_t mlp_backward_workspace_floats(int B, int H, int L, int d, int mb) {
+size_t mlp_backward_seq_floats(int L, int d, int mb) {
+    if (d != D) return 0;
     const size_t nch = L > 0 ? static_cast<size_t>((L + mb - 1) / mb) : 0;
-    const size_t ck = 2 * static_cast<size_t>(d) * 4 * d + 4 * static_cast<size_t>(d) + d;
-    return static_cast<size_t>(B) * H * (nch + 2) * ck;
+    return (nch + 2) * CK + nch * REC;
 }
 
 hipError_t launch_mlp_backward(const MLPBwdArgs &a, hipStream_t stream) {

@@ -412,13 +412,19 @@ def _mbwd(lib, B=2, H=3, L=40, d=64, mb=16, io=1, eps=1e-6, ws_bytes=None, ptrs=
 def test_mlp_backward_workspace_size(lib):
     n = ctypes.c_size_t(0)
     assert lib.ttt_mlp_backward_workspace(2, 3, 40, 64, 16, ctypes.byref(n)) == _lib.TTT_OK
-    # ceil(40 / 16) = 3 chunk-start states plus two adjoint states, each W1, b1, W2, b2
-    assert n.value == 2 * 3 * (3 + 2) * (2 * 64 * 256 + 256 + 64) * 4
+    # ceil(40 / 16) = 3 chunk-start states plus two adjoint states, each W1, b1, W2, b2,
+    # and 3 chunk records: eight [16 x 256] hidden tensors, five [16 x 64] row tensors,
+    # two values per row and two per feature
+    state = 2 * 64 * 256 + 256 + 64
+    record = 8 * 16 * 256 + 5 * 16 * 64 + 2 * 16 + 2 * 64
+    assert n.value == 2 * 3 * ((3 + 2) * state + 3 * record) * 4
     assert lib.ttt_mlp_backward_workspace(1, 1, 0, 64, 16, ctypes.byref(n)) == _lib.TTT_OK
     assert n.value == 2 * 132352
     assert lib.ttt_mlp_backward_workspace(2, 3, 40, 16, 16, ctypes.byref(n)) == _lib.TTT_E_SHAPE
     assert lib.ttt_mlp_backward_workspace(2, 3, 40, 64, 17, ctypes.byref(n)) == _lib.TTT_E_SHAPE
     assert lib.ttt_mlp_backward_workspace(2, 3, 40, 64, 16, None) == _lib.TTT_E_NULL
+    # one pre-pass workgroup per chunk: B*H*ceil(L/mb) must fit a launch grid
+    assert lib.ttt_mlp_backward_workspace(64, 64, 1 << 20, 64, 1, ctypes.byref(n)) == _lib.TTT_E_SHAPE
 
 
 def test_mlp_backward_validation(lib):
