@@ -162,13 +162,18 @@ __device__ __forceinline__ void prep_waves(Smem &sm, int pw, int g, int c, int l
     }
     const char *bq = reinterpret_cast<const char *>(xq), *bk = reinterpret_cast<const char *>(xk),
                *bv = reinterpret_cast<const char *>(xv);
+    const int last = (L - 1) / MB;  // the last chunk
+    // Chunk ch's row r (both clamped into the sequence): a uniform 64-bit chunk base and a
+    // 32-bit offset within the chunk, so the per-lane address arithmetic stays 32-bit.
     auto load = [&](PrepRegs &R, int ch) {
-        const int tok = min(ch * MB + r, L - 1);
-        const size_t off = (static_cast<size_t>(tok) * D + f0) * 2u;  // bytes
-        R.q = *reinterpret_cast<const uint2 *>(bq + off);
-        R.k = *reinterpret_cast<const uint2 *>(bk + off);
-        R.v = *reinterpret_cast<const uint2 *>(bv + off);
-        if constexpr (!GATED) R.eta = et[tok];
+        const int cc = min(ch, last);
+        const uint32_t rr = static_cast<uint32_t>(min(r, L - 1 - cc * MB));
+        const size_t cb = static_cast<size_t>(cc) * (MB * D * 2);  // bytes
+        const uint32_t off = (rr * D + f0) * 2u;
+        R.q = *reinterpret_cast<const uint2 *>(bq + cb + off);
+        R.k = *reinterpret_cast<const uint2 *>(bk + cb + off);
+        R.v = *reinterpret_cast<const uint2 *>(bv + cb + off);
+        if constexpr (!GATED) R.eta = (et + static_cast<size_t>(cc) * MB)[rr];
     };
     // learning-rate gate (GATED): eta = eta_base * logistic(theta . XK_t), the
     // dot product split over the 16 lanes of the token's DPP row; exp2 and
@@ -597,7 +602,8 @@ __device__ __forceinline__ void state_waves(Smem &sm, const Ctx &cx, int u, int 
             uint2 ov = make_uint2(pack2(o[0], o[1]), pack2(o[2], o[3]));
             asm volatile("" : "+v"(ov));  // keep the math out of the store's branch
             const int tok = (it - 1) * MB + c;
-            if (tok < cx.L) *reinterpret_cast<uint2 *>(Oseq + static_cast<size_t>(tok) * D + f0) = ov;
+            if (tok < cx.L)
+                *reinterpret_cast<uint2 *>(Oseq + static_cast<size_t>(it - 1) * (MB * D) + (c * D + f0)) = ov;
         }
         sm1 = s0;
         s0 = s1;
