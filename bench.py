@@ -84,7 +84,7 @@ def alg_flops_decode_step(B, H, d):
 
 
 def alg_flops_linear_backward(B, H, L, d, b=16):
-    """Algorithmic flops of one ttt_linear_backward launch per token-head:
+    """Algorithmic flops of one ttt_linear_backward call per token-head:
     the forward pass that stores the chunk-start states (XK W and the state
     update, 4 d^2), the recomputed chunk (XK W, XQ W, T E: 4 d^2 + 2 b d),
     and the reverse products (dZb W^T, XK dW', E dW'^T, dZ W^T, XQ^T dZb,
@@ -619,10 +619,12 @@ def bench_backward(args):
                                            stream=stream)
     wall, kern = _timed(step, stream, args.warmup, args.steps)
     fl = alg_flops_linear_backward(B, H, L, d)
+    # one call is three launches of linear_backward_kernel (forward sweep, pre-pass, reverse
+    # sweep); the events bracket the call, so kernel_avg_us is their sum
     roof = {"bound": "alu", "achieved": fl / kern / 1e12, "peak": FP32_VECTOR_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": fl / kern / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
-            "traffic": None, "kernel": "linear_backward_kernel", "kernel_avg_us": kern * 1e6,
-            "alg_flops_per_launch": fl}
+            "traffic": None, "kernel": "linear_backward_kernel (forward sweep + pre-pass + reverse sweep)",
+            "kernel_avg_us": kern * 1e6, "alg_flops_per_launch": fl, "launches_per_call": 3}
     extra = {}
     if not args.no_cpu_baseline:
         from oracle import grad as OG

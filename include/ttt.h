@@ -274,7 +274,10 @@ int ttt_mlp_forward_opts(int B, int H, int L, int d, int mb, int io, float ln_ep
  *   batch (W0 and b0 when w0_batched == 0, gamma, beta) need the caller's
  *   sum over B.
  *   workspace: device memory of at least the size ttt_linear_backward_workspace
- *   reports (the state at every chunk start), caller-owned, overwritten.
+ *   reports (the state at every chunk start and, per chunk, the reverse's
+ *   values that do not depend on dW', db'), caller-owned, overwritten. The
+ *   call is three launches on `stream`: the forward sweep, a pre-pass over all
+ *   chunks at once, the reverse sweep.
  * No output may overlap an input, another output or the workspace.
  * Numerics: fp32 throughout (bf16 inputs widened); the forward is recomputed
  * chunk by chunk from the stored states in the dual form ([D] §4.2).
@@ -289,27 +292,32 @@ int ttt_linear_backward(int B, int H, int L, int d, int mb, int io, float ln_eps
                         float *dbeta, void *workspace, size_t workspace_bytes,
                         hipStream_t stream);
 
-/* Workspace bytes ttt_linear_backward needs: B*H*ceil(L/mb)*(d*d+d)*4.
- * Validates B, H, L, d, mb as ttt_linear_backward does. */
+/* Workspace bytes ttt_linear_backward needs:
+ * B*H*ceil(L/mb)*(d*d + d + 80d + 2d + 32)*4 (a chunk-start state and a
+ * chunk record per chunk; d = 64: 37,760 bytes per chunk and sequence).
+ * Validates B, H, L, d, mb as ttt_linear_backward does; TTT_E_SHAPE also
+ * when B*H*ceil(L/mb) exceeds 2^31 - 1. */
 int ttt_linear_backward_workspace(int B, int H, int L, int d, int mb, size_t *bytes);
 
 /*
  * ttt_linear_backward for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving or training loops, harnesses that
  * forbid hipMalloc. Same arguments, results and kernel as
- * ttt_linear_backward, minus the workspace: the chunk-start checkpoints go to
- * a fixed device array inside the library, TTT_BACKWARD_SCRATCH_BYTES
- * (64 MiB) on every GPU the library runs on, held until the process ends.
- *   - B*H*ceil(L/mb)*(d*d+d)*4 (ttt_linear_backward_workspace) must not
- *     exceed TTT_BACKWARD_SCRATCH_BYTES, else TTT_E_SHAPE before any HIP
- *     call (d = 64: at most 4032 chunk states B*H*ceil(L/mb), e.g. B*H = 8 at L = 8064 with mb = 16).
+ * ttt_linear_backward, minus the workspace: the chunk-start checkpoints and
+ * chunk records go to a fixed device array inside the library,
+ * TTT_BACKWARD_SCRATCH_BYTES (64 MiB) on every GPU the library runs on, held
+ * until the process ends.
+ *   - ttt_linear_backward_workspace's size must not exceed
+ *     TTT_BACKWARD_SCRATCH_BYTES, else TTT_E_SHAPE before any HIP call
+ *     (d = 64: at most 1777 chunks B*H*ceil(L/mb), e.g. B*H = 3 at L = 9472
+ *     with mb = 16).
  *   - Calls no hipMalloc, hipFree or allocating library routine. The first
  *     call on a device looks up the array's device address once
  *     (hipGetSymbolAddress with that device current).
  *   - `stream` must belong to the current device (else TTT_E_HIP).
  *   - Every call on one GPU shares that GPU's array and it keeps the last
- *     call's contents; a call reads only checkpoints it wrote itself, so
- *     nothing needs clearing. Calls that overlap in time on one GPU (other
+ *     call's contents; a call reads only values it wrote itself, so nothing
+ *     needs clearing. Calls that overlap in time on one GPU (other
  *     streams, other host threads) race on the array and give wrong
  *     gradients: order them, e.g. on one stream.
  */

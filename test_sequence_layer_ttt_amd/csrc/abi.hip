@@ -149,8 +149,8 @@ int linear_backward(int B, int H, int L, int d, int mb, int io, float ln_eps, co
     if (fixed_scratch) {
         if (need > ttt::linear_backward_scratch_bytes())
             return fail(TTT_E_SHAPE,
-                        "the checkpoints need %zu bytes; the no-allocation entry point's scratch "
-                        "holds %zu (B*H*ceil(L/mb)*(d*d+d)*4 must not exceed it)",
+                        "the checkpoints and chunk records need %zu bytes; the no-allocation entry "
+                        "point's scratch holds %zu (ttt_linear_backward_workspace must not exceed it)",
                         need, ttt::linear_backward_scratch_bytes());
     } else if (workspace_bytes < need) {
         return fail(TTT_E_SHAPE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
@@ -493,7 +493,9 @@ int ttt_linear_backward_workspace(int B, int H, int L, int d, int mb, size_t *by
     if (d != 16 && d != 64) return fail(TTT_E_SHAPE, "d = %d not in {16, 64}", d);
     if (!bytes) return fail(TTT_E_NULL, "bytes is NULL");
     const size_t nch = L > 0 ? static_cast<size_t>((L + mb - 1) / mb) : 0;
-    if (!nbytes(bytes, {size_t(B), size_t(H), nch, size_t(d) * d + d, sizeof(float)}))
+    if (static_cast<size_t>(B) * H * nch > 0x7fffffffu)
+        return fail(TTT_E_SHAPE, "B*H*ceil(L/mb) = %zu chunks exceeds 2^31 - 1", static_cast<size_t>(B) * H * nch);
+    if (!nbytes(bytes, {size_t(B), size_t(H), nch, ttt::linear_backward_chunk_floats(d), sizeof(float)}))
         return fail(TTT_E_SHAPE, "sizes overflow");
     return ok();
 }

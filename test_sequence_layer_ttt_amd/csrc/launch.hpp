@@ -30,7 +30,7 @@ struct LinearBwdArgs {
     LinearArgs f;  // forward arguments (O, W_out, b_out unused)
     const float *dO, *dW_out, *db_out;
     float *dXQ, *dXK, *dXV, *deta, *dW0, *db0, *dgamma, *dbeta;
-    float *ws;  // chunk-start states, linear_backward_workspace_floats floats
+    float *ws;  // chunk-start states and chunk records: B*H*ceil(L/mb)*linear_backward_chunk_floats
 };
 
 struct MLPArgs {
@@ -88,7 +88,7 @@ hipError_t launch_eta_gate_backward(int B, int H, int L, int d, int io, const vo
                                     const float *theta, float eta_base, const float *deta,
                                     float *dXK, float *dtheta, hipStream_t stream);
 
-size_t linear_backward_workspace_floats(int B, int H, int L, int d, int mb);
+size_t linear_backward_chunk_floats(int d);  // workspace floats per sequence and chunk
 // the fixed device scratch of ttt_linear_backward_noalloc: its size, and its
 // address on the current device
 size_t linear_backward_scratch_bytes();

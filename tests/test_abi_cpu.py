@@ -194,7 +194,11 @@ def test_decode_steps_mb_validation(lib):
 def test_linear_backward_workspace_size(lib):
     n = ctypes.c_size_t(0)
     assert lib.ttt_linear_backward_workspace(2, 3, 40, 64, 16, ctypes.byref(n)) == _lib.TTT_OK
-    assert n.value == 2 * 3 * 3 * (64 * 64 + 64) * 4  # ceil(40 / 16) = 3 chunk-start states
+    # ceil(40 / 16) = 3 chunks, each a start state (W, b) and a record (five [16 x d] row
+    # tensors, two values per row, two per feature)
+    assert n.value == 2 * 3 * 3 * (64 * 64 + 64 + 5 * 16 * 64 + 2 * 16 + 2 * 64) * 4
+    assert lib.ttt_linear_backward_workspace(1, 1, 16, 16, 16, ctypes.byref(n)) == _lib.TTT_OK
+    assert n.value == (16 * 16 + 16 + 5 * 16 * 16 + 2 * 16 + 2 * 16) * 4
     assert lib.ttt_linear_backward_workspace(2, 3, 0, 16, 4, ctypes.byref(n)) == _lib.TTT_OK
     assert n.value == 0
     assert lib.ttt_linear_backward_workspace(2, 3, 40, 48, 16, ctypes.byref(n)) == _lib.TTT_E_SHAPE
@@ -366,12 +370,12 @@ def test_binding_rejects_cpu_tensors():
 
 def test_backward_noalloc_rejects_inputs_beyond_its_scratch(lib):
     """The no-allocation backward refuses, before any HIP call, inputs whose
-    checkpoints exceed its fixed 64 MiB scratch (4032 d = 64 chunk states)."""
+    checkpoints and chunk records exceed its fixed 64 MiB scratch (1777 d = 64 chunks)."""
     p = [FAKE + i * (1 << 24) for i in range(24)]
 
     def call(B, H, L):
         return lib.ttt_linear_backward_noalloc(B, H, L, 64, 16, 1, 1e-6, *p[:6], 0, *p[6:19], None)
-    assert call(8, 1, 16 * 4033) == _lib.TTT_E_SHAPE
+    assert call(1, 1, 16 * 1778) == _lib.TTT_E_SHAPE
     msg = lib.ttt_last_error().decode()
     assert "scratch" in msg and str(64 << 20) in msg
     assert call(1, 1, -1) == _lib.TTT_E_SHAPE
