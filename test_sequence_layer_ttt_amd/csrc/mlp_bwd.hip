@@ -58,7 +58,7 @@ namespace {
 constexpr int D = 64, M = 4 * D, NT = 512, RW = 16, NF = D / RW;
 constexpr int DP = D + 1, MP = M + 1, TP = RW + 1;
 // floats of one stored state: W1 transposed [M][D], b1 [M], W2 [M][D], b2 [D] (both weight
-// matrices hidden-unit-major, as are the adjoint states)
+// matrices hidden-unit-major, as are the adjoint states, and stored as 16 x 16 tiles: see tix)
 constexpr int CK = 2 * D * M + M + D;
 constexpr int OB1 = D * M, OW2 = D * M + M, OB2 = 2 * D * M + M;
 
@@ -93,6 +93,12 @@ union MlpSmem {
     MlpBwdSmem r;
     MlpFwdSmem f;
 };
+
+// Offset of element (n, f) (hidden unit n, feature f) of a stored [M x D] state matrix: 16 x 16
+// tiles, each 1 KB contiguous and row-major, tile (n / 16, f / 16) at (4 (n / 16) + f / 16) KB.
+__device__ __forceinline__ int tix(int n, int f) {
+    return ((n >> 4) * (D / 16) + (f >> 4)) * 256 + (n & 15) * 16 + (f & 15);
+}
 
 __device__ __forceinline__ f32x4 mf(float a, float b, f32x4 acc) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
@@ -207,9 +213,9 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
     const int hc0 = 32 * wu + c;  // this lane's hidden column in own tile j: hc0 + 16 j
     // Global addresses are a uniform pointer plus one of a few per-lane offsets
     // (elements), so that the per-lane part stays one register per pattern.
-    const unsigned lc = g * D + c, le = 4 * g * M + c, lf = 4 * g * D + c;
+    const unsigned lc = g * 16 + c, le = 4 * g * M + c, lf = 4 * g * D + c;
     // 16-byte per-lane runs: W2^T fragments and the transposed adjoint tiles
-    const unsigned lbv = c * D + 4 * g, lg = c * D + 4 * g;
+    const unsigned lbv = c * 16 + 4 * g, lg = c * 16 + 4 * g, lw = 64 * g + c;
     // record: a lane's four floats of a hidden tile; a row thread's features of a row tensor
     const unsigned lh = 4 * lane, lrq = r * D + q;
 
@@ -262,14 +268,14 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
-                const f32x4 t = gld4(V + (32 * wu + 16 * j) * D + 16 * qq, lbv);
+                const f32x4 t = gld4(V + (2 * wu + j) * 1024 + 256 * qq, lbv);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[16 * j + 4 * qq + e] = t[e];
             }
     };
     auto ld_v = [&](const float *V, Frag &v) {  // V [M x D]: feature tile u over hidden half hh
 #pragma unroll
-        for (int kb = 0; kb < M / 8; ++kb) v[kb] = gld(V + (M / 2 * hh + 4 * kb) * D + 16 * u, lc);
+        for (int kb = 0; kb < M / 8; ++kb) v[kb] = gld(V + ((8 * hh + (kb >> 2)) * 4 + u) * 256 + 64 * (kb & 3), lc);
     };
     // feature tile u over hidden half hh of Y [16 x M] (LDS) times a fragment of ld_v
     auto mm_y = [&](const float *Y, const Frag &v, f32x4 acc) {
@@ -396,12 +402,12 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
 #pragma unroll
-                for (int rb = 0; rb < 4; ++rb) gst4(Sn + (32 * wu + 16 * j) * D + 16 * rb, lg, W1r[rb][j]);
+                for (int rb = 0; rb < 4; ++rb) gst4(Sn + (2 * wu + j) * 1024 + 256 * rb, lg, W1r[rb][j]);
 #pragma unroll
                 for (int uu = 0; uu < 4; ++uu)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        gst(Sn + OW2 + (32 * wu + 16 * j + i) * D + 16 * uu, lf, W2r[j][uu][i]);
+                        gst(Sn + OW2 + ((2 * wu + j) * 4 + uu) * 256 + 16 * i, lw, W2r[j][uu][i]);
                         sf.W2[(32 * wu + 16 * j + 4 * g + i) * W2P + 16 * uu + c] = W2r[j][uu][i];
                     }
                 if (g == 0) gst(Sn + OB1 + 32 * wu + 16 * j, c, b1r[j]);
@@ -760,8 +766,8 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
         float *a0 = adj(nch - 1);
         if (nch > 0) {
             for (int i = tid; i < D * M; i += NT) {
-                a0[(i % M) * D + i / M] = dW1_out ? dW1_out[sq * D * M + i] : 0.f;
-                a0[OW2 + i] = dW2_out ? dW2_out[sq * M * D + i] : 0.f;
+                a0[tix(i % M, i / M)] = dW1_out ? dW1_out[sq * D * M + i] : 0.f;
+                a0[OW2 + tix(i / D, i % D)] = dW2_out ? dW2_out[sq * M * D + i] : 0.f;
             }
             if (tid < M) a0[OB1 + tid] = db1_out ? db1_out[sq * M + tid] : 0.f;
             if (tid < D) a0[OB2 + tid] = db2_out ? db2_out[sq * D + tid] : 0.f;
@@ -992,7 +998,7 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
                     acc = xt_h(sm.dZb2, rb, Abr[j], acc);
                     acc = xt_h(sm.E2, rb, dQr[j], acc);
                     acc = xt_h(sm.dZ2, rb, Ar[j], acc);
-                    gst4(dst2 + (32 * wu + 16 * j) * D + 16 * rb, lg, acc);
+                    gst4(dst2 + (2 * wu + j) * 1024 + 256 * rb, lg, acc);
                 }
             ld_v(S, fA);  // W1 (stored transposed), for dZ1 W1^T
             issue();
@@ -1006,7 +1012,7 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
                                  fB[16 * j + 4 * rb + 3]};
                     acc = xt_h(sm.XQ, rb, dZb1r[j], acc);
                     acc = xt_h(sm.XK, rb, dZ1r[j], acc);
-                    gst4(dst1 + (32 * wu + 16 * j) * D + 16 * rb, lg, acc);
+                    gst4(dst1 + (2 * wu + j) * 1024 + 256 * rb, lg, acc);
                 }
                 const float cs = tile::rows4_sum((dZb1r[j][0] + dZ1r[j][0]) + (dZb1r[j][1] + dZ1r[j][1]) +
                                                  ((dZb1r[j][2] + dZ1r[j][2]) + (dZb1r[j][3] + dZ1r[j][3])));
@@ -1042,8 +1048,8 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
         if (nch > 0) {  // the adjoint of the initial state, from the workspace to the outputs
             const float *a = adj(1);
             for (int i = tid; i < D * M; i += NT) {
-                dW1[sq * D * M + i] = a[(i % M) * D + i / M];
-                dW2[sq * M * D + i] = a[OW2 + i];
+                dW1[sq * D * M + i] = a[tix(i % M, i / M)];
+                dW2[sq * M * D + i] = a[OW2 + tix(i / D, i % D)];
             }
             if (tid < M) db1[sq * M + tid] = a[OB1 + tid];
             if (tid < D) db2[sq * D + tid] = a[OB2 + tid];
