@@ -248,8 +248,11 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
         return acc;
     };
     auto put_h = [&](float *Hs, int j, f32x4 v) {
+        int lo = 4 * g * MP + c;
+        asm volatile("" : "+v"(lo));  // recomputed per use: no per-tile address held across the loop
+        float *p = Hs + lo + 32 * wu + 16 * j;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Hs[(4 * g + i) * MP + hc0 + 16 * j] = v[i];
+        for (int i = 0; i < 4; ++i) p[i * MP] = v[i];
     };
     auto put_d = [&](float *P, f32x4 v) {
 #pragma unroll
