@@ -796,7 +796,8 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
         struct Ahead {
             typename pio::raw xq, xk, xv;
             tile::f32x2 xh, gh, G, dzb2, dxk;
-            float et, sig, cc;
+            float et, sig, cc, pg, pb;
+            f32x4 t2z;
             bool ok;
         };
         auto load_ahead = [&](int ch, Ahead &N) {
@@ -816,6 +817,11 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
             N.et = gld(eta + sq * L + static_cast<size_t>(ch) * mb, N.ok ? at_t : 0);
             N.sig = gld(rc + OS, tid & (RW - 1));
             N.cc = gld(rc + OS + RW, tid & (RW - 1));
+            // T2^T dZb2 in the tile layout of the dE2 partial (hidden half 0), the chunk's dgamma, dbeta share
+#pragma unroll
+            for (int i = 0; i < 4; ++i) N.t2z[i] = gld(rc + rrow(RT_T2Z) + i * D + 16 * u, lf);
+            N.pg = gld(rc + OGB, tid & (D - 1));
+            N.pb = gld(rc + OGB + D, tid & (D - 1));
         };
         // into LDS: XQ, XK, XV - XK, E2 = -eta G2, dZb2, the lnl2 rows, eta, sigma, c, the dXK part
         // (inputs and eta zero on rows past the chunk)
@@ -872,18 +878,15 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
                 Ar[j] = get_rec(rc, HT_A, j);
                 E1r[j] = get_rec(rc, HT_E1, j);
             }
-            f32x4 t2z = fz;
-            if (hh == 0) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) t2z[i] = gld(rc + rrow(RT_T2Z) + i * D + 16 * u, lf);
-            }
+            const f32x4 t2z = N.t2z;
             if (tid < D) {
-                accG += gld(rc + OGB, tid);
-                accB += gld(rc + OGB + D, tid);
+                accG += N.pg;
+                accB += N.pb;
             }
             ld_vt(Ad, fA);  // dW1' (transposed)
             const float db1v[2] = {gld(Ad + OB1 + 32 * wu, c), gld(Ad + OB1 + 32 * wu + 16, c)};
             const float db2v = tid < D ? gld(Ad, OB2 + tid) : 0.f;
+            const float db2u = gld(Ad + OB2 + 16 * u, c);  // db2' of this wave's feature tile
             issue();
             tile::lds_barrier();
 
@@ -910,7 +913,7 @@ __global__ __launch_bounds__(NT) void mlp_backward_kernel(
 
             // dE2 = T2^T dZb2 + db2' + A dW2' + dQ W2 (two halves)
             {
-                f32x4 e = hh == 0 ? t2z + bcast(gld(Ad + OB2 + 16 * u, c)) : fz;
+                f32x4 e = hh == 0 ? t2z + bcast(db2u) : fz;
                 e = mm_y(sm.HA, fB, e);
                 e = mm_y(sm.HY, fW, e);
                 put_d(sm.partE[hh], e);
