@@ -16,7 +16,8 @@
 //  * operands staged in LDS, two stages: each step's global loads are issued
 //    before the MFMAs of the previous step and written to the other stage
 //    after them, one barrier per step. LDS rows are padded to 144 bytes, so
-//    the 16 rows one fragment read touches start on different banks;
+//    the 16 rows one fragment read touches start on different banks; within
+//    a step each A fragment is read three groups ahead of its four products;
 //  * XCD-aware order: workgroups go to the 8 XCDs round robin, so XCD x is
 //    given the feature blocks x, x + 8, ... (its slice of Theta stays in its
 //    L2) and runs them over every token block.
@@ -95,24 +96,37 @@ __global__ __launch_bounds__(PNT) void qkv_project_kernel(int NF, int M, int K, 
         // the stores of the next stage stay behind the MFMAs of this one (so
         // the global loads above have the whole step to arrive)
         __builtin_amdgcn_sched_barrier(0);
+        // fragments: lane (g, c) holds row c of a 16-row tile, k = 32 kk + 8 g .. +7.
+        // The step's 16 A fragments (kk, t) are read PD groups ahead of the four
+        // products that use each, so the LDS reads of one group overlap the
+        // MFMAs of the groups before it (scheduling barriers keep the order).
+        auto rd_a = [&](int idx) {
+            const int kk = idx >> 3, t = idx & 7;
+            return __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4 *>(&sm.a[st][(wf0 + 16 * t + c) * PSTR + 32 * kk + 8 * g]));
+        };
+        auto rd_x = [&](int kk, int s) {
+            return __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4 *>(&sm.b[st][(wt0 + 16 * s + c) * PSTR + 32 * kk + 8 * g]));
+        };
+        constexpr int PD = 3;
+        bf16x8 fa[16], fx[2][4];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            // fragments: lane (g, c) holds row c of a 16-row tile, k = 32 kk + 8 g .. +7
-            bf16x8 fa[8], fx[4];
+        for (int s = 0; s < 4; ++s) fx[0][s] = rd_x(0, s);
 #pragma unroll
-            for (int t = 0; t < 8; ++t)
-                fa[t] = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const u32x4 *>(&sm.a[st][(wf0 + 16 * t + c) * PSTR + 32 * kk + 8 * g]));
+        for (int i = 0; i < PD; ++i) fa[i] = rd_a(i);
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                fx[s] = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const u32x4 *>(&sm.b[st][(wt0 + 16 * s + c) * PSTR + 32 * kk + 8 * g]));
-            // all twelve reads in flight together, then the 32 products
+        for (int idx = 0; idx < 16; ++idx) {
+            if (idx + PD < 16) fa[idx + PD] = rd_a(idx + PD);
+            if (idx == 2) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) fx[1][s] = rd_x(1, s);
+            }
             __builtin_amdgcn_sched_barrier(0);
+            const int kk = idx >> 3, t = idx & 7;
 #pragma unroll
-            for (int t = 0; t < 8; ++t)
-#pragma unroll
-                for (int s = 0; s < 4; ++s) acc[t][s] = mfma32(fa[t], fx[s], acc[t][s]);
+            for (int s = 0; s < 4; ++s) acc[t][s] = mfma32(fa[idx], fx[kk][s], acc[t][s]);
+            __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_sched_barrier(0);
         if (kt + 1 < nk) store(st ^ 1);
