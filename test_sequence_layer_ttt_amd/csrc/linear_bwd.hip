@@ -296,7 +296,17 @@ __global__ __launch_bounds__(NT) void linear_backward_kernel(
 
     if constexpr (MODE == FWD) {
         // ===== forward: chunk-start states to the workspace ========================
-        for (int i = tid; i < D * D; i += NT) sm.W[(i / D) * DP + i % D] = W0[st * D * D + i];
+        // W stays in registers for the whole sweep: wave w holds the tiles (rb, w),
+        // lane (g, c) rows 16 rb + 4g .. +3 of column 16 w + c (the output layout of
+        // the update). Z = XK W + b takes them as its B operand directly, with the
+        // contraction order k <-> 16 rb + 4g + i of the accumulator rows.
+        f32x4 Wr[NTL];
+        if (mw) {
+#pragma unroll
+            for (int rb = 0; rb < NTL; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Wr[rb][i] = W0[st * D * D + (16 * rb + 4 * g + i) * D + 16 * w + c];
+        }
         if (tid < D) sm.b[tid] = b0[st * D + tid];
         __syncthreads();
         Rows R;
@@ -311,7 +321,16 @@ __global__ __launch_bounds__(NT) void linear_backward_kernel(
             stage_rows(R, false, false, tau, et, go_unused);
             if (ch + 2 < nch) fetch_rows(ch + 1, false, false, R);
             __syncthreads();
-            if (mw) put(sm.Z, mma<D>(rowm(sm.XK, DP), rowm(sm.W + 16 * w, DP), g, c, brow(sm.b)));
+            if (mw) {
+                f32x4 zt = brow(sm.b);
+#pragma unroll
+                for (int rb = 0; rb < NTL; ++rb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        zt = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.XK[c * DP + 16 * rb + 4 * g + i], Wr[rb][i], zt,
+                                                                  0, 0, 0);
+                put(sm.Z, zt);
+            }
             __syncthreads();
             float z[NF];
             rowz(sm.Z, z);
@@ -320,7 +339,14 @@ __global__ __launch_bounds__(NT) void linear_backward_kernel(
 #pragma unroll
             for (int u = 0; u < NF; ++u) sm.E[r * DP + q + RW * u] = -et * s.G[u];
             __syncthreads();
-            state_update(sm.W, sm.XK, sm.E, nullptr, nullptr, wn);  // W += XK^T E
+            if (mw) {  // W += XK^T E on the register tiles, and the checkpoint
+#pragma unroll
+                for (int rb = 0; rb < NTL; ++rb) {
+                    Wr[rb] = mma<RW>(colm(sm.XK + 16 * rb, DP), rowm(sm.E + 16 * w, DP), g, c, Wr[rb]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) wn[(16 * rb + 4 * g + i) * D + 16 * w + c] = Wr[rb][i];
+                }
+            }
             if (tid < D) {
                 const float bn = sm.b[tid] + colsum(sm.E, nullptr);
                 sm.b[tid] = bn;
