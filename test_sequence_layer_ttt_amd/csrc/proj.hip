@@ -13,10 +13,13 @@
 //  * block tile 256 features x 256 tokens, contraction steps of 64; 8 waves
 //    (2 along the features x 4 along the tokens), 128 x 64 per wave = 8 x 4
 //    MFMA tiles, 32 fp32 accumulator quads;
-//  * operands staged in LDS, two stages: each step's global loads are issued
-//    before the MFMAs of the previous step and written to the other stage
-//    after them, one barrier per step. LDS rows are padded to 144 bytes, so
-//    the 16 rows one fragment read touches start on different banks; within
+//  * operands staged in LDS, two stages, by direct global-to-LDS loads: each
+//    step's loads into the other stage are issued before its MFMAs and land
+//    while they run (no register staging, no LDS store instructions), one
+//    barrier per step after a wait for this wave's loads. A load instruction
+//    puts lane i at 16 i bytes, so rows are unpadded 128 bytes with their
+//    16-byte chunks XOR-swizzled by row & 7: the 8 rows that one fragment
+//    read's lanes c = 0 .. 7 touch then use distinct chunk positions. Within
 //    a step each A fragment is read three groups ahead of its four products;
 //  * XCD-aware order: workgroups go to the 8 XCDs round robin, so XCD x is
 //    given the feature blocks x, x + 8, ... (its slice of Theta stays in its
@@ -32,17 +35,18 @@ using namespace tile;
 constexpr int PF = 256;           // output features per block
 constexpr int PT = 256;           // tokens per block
 constexpr int PK = 64;            // contraction step
-constexpr int PSTR = PK + 8;      // LDS row stride (bf16)
 constexpr int PNT = 512;          // threads (8 waves)
 constexpr int WF = 128, WT = 64;  // per-wave tile
 constexpr int NXCD = 8;
 
-typedef __attribute__((ext_vector_type(4))) unsigned u32x4;  // 16 bytes, kept in registers
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;  // 16 bytes
 
 struct ProjSmem {
-    uint16_t a[2][PF * PSTR];  // Theta rows [feature][k]
-    uint16_t b[2][PT * PSTR];  // X rows [token][k]
+    uint16_t a[2][PF * PK];  // Theta rows [feature][k], 16-byte chunks XOR-swizzled by row & 7
+    uint16_t b[2][PT * PK];  // X rows [token][k], same swizzle
 };
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void glb_void;
 
 __global__ __launch_bounds__(PNT) void qkv_project_kernel(int NF, int M, int K, int HD, int H, int L,
                                                           const bf16_t *X, const bf16_t *theta,
@@ -56,27 +60,23 @@ __global__ __launch_bounds__(PNT) void qkv_project_kernel(int NF, int M, int K, 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c = lane & 15;
     const int wf0 = (w & 1) * WF, wt0 = (w >> 1) * WT;
 
-    // global -> registers: 4 chunks of 16 bytes of each operand per thread.
+    // global -> LDS directly: wave w, instruction q fills rows 8 (4w + q) .. +7
+    // (1 KB); lane i lands at 16 i bytes, i.e. row 8 (4w + q) + i / 8, physical
+    // chunk i % 8, which holds logical chunk (i % 8) ^ (i / 8) of that row.
     // Rows past the end read row 0: a feature row only reaches the outputs of
     // that feature and a token row those of that token, which are not stored,
     // so the values need no masking.
-    u32x4 ra[4], rb[4];
-    auto load = [&](int kt) {
+    auto dma = [&](int kt, int stg) {
         const int k0 = kt * PK;
+        const int rl = lane >> 3, lc = (lane & 7) ^ rl;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int ch = tid + PNT * q, row = ch >> 3, col = (ch & 7) * 8;
+            const int blk = 4 * w + q, row = 8 * blk + rl;
             const int fr = f0 + row, tr = t0 + row;
-            ra[q] = *reinterpret_cast<const u32x4 *>(theta + static_cast<size_t>(fr < NF ? fr : 0) * K + k0 + col);
-            rb[q] = *reinterpret_cast<const u32x4 *>(X + static_cast<size_t>(tr < M ? tr : 0) * K + k0 + col);
-        }
-    };
-    auto store = [&](int st) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int ch = tid + PNT * q, row = ch >> 3, col = (ch & 7) * 8;
-            *reinterpret_cast<u32x4 *>(&sm.a[st][row * PSTR + col]) = ra[q];
-            *reinterpret_cast<u32x4 *>(&sm.b[st][row * PSTR + col]) = rb[q];
+            const bf16_t *sa = theta + static_cast<size_t>(fr < NF ? fr : 0) * K + k0 + lc * 8;
+            const bf16_t *sb = X + static_cast<size_t>(tr < M ? tr : 0) * K + k0 + lc * 8;
+            __builtin_amdgcn_global_load_lds((glb_void *)sa, (lds_void *)&sm.a[stg][8 * blk * PK], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void *)sb, (lds_void *)&sm.b[stg][8 * blk * PK], 16, 0, 0);
         }
     };
 
@@ -87,27 +87,23 @@ __global__ __launch_bounds__(PNT) void qkv_project_kernel(int NF, int M, int K, 
         for (int s = 0; s < 4; ++s) acc[t][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nk = K / PK;
-    load(0);
-    store(0);
+    dma(0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const int st = kt & 1;
-        if (kt + 1 < nk) load(kt + 1);
-        // the stores of the next stage stay behind the MFMAs of this one (so
-        // the global loads above have the whole step to arrive)
+        if (kt + 1 < nk) dma(kt + 1, st ^ 1);
         __builtin_amdgcn_sched_barrier(0);
-        // fragments: lane (g, c) holds row c of a 16-row tile, k = 32 kk + 8 g .. +7.
-        // The step's 16 A fragments (kk, t) are read PD groups ahead of the four
-        // products that use each, so the LDS reads of one group overlap the
-        // MFMAs of the groups before it (scheduling barriers keep the order).
         auto rd_a = [&](int idx) {
             const int kk = idx >> 3, t = idx & 7;
+            const int j = (4 * kk + g) ^ (c & 7);
             return __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4 *>(&sm.a[st][(wf0 + 16 * t + c) * PSTR + 32 * kk + 8 * g]));
+                bf16x8, *reinterpret_cast<const u32x4 *>(&sm.a[st][(wf0 + 16 * t + c) * PK + 8 * j]));
         };
         auto rd_x = [&](int kk, int s) {
+            const int j = (4 * kk + g) ^ (c & 7);
             return __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4 *>(&sm.b[st][(wt0 + 16 * s + c) * PSTR + 32 * kk + 8 * g]));
+                bf16x8, *reinterpret_cast<const u32x4 *>(&sm.b[st][(wt0 + 16 * s + c) * PK + 8 * j]));
         };
         constexpr int PD = 3;
         bf16x8 fa[16], fx[2][4];
@@ -128,8 +124,7 @@ __global__ __launch_bounds__(PNT) void qkv_project_kernel(int NF, int M, int K, 
             for (int s = 0; s < 4; ++s) acc[t][s] = mfma32(fa[idx], fx[kk][s], acc[t][s]);
             __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        if (kt + 1 < nk) store(st ^ 1);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads into the other stage have landed
         __syncthreads();
     }
 
