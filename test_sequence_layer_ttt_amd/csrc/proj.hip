@@ -21,9 +21,11 @@
 //    16-byte chunks XOR-swizzled by row & 7: the 8 rows that one fragment
 //    read's lanes c = 0 .. 7 touch then use distinct chunk positions. Within
 //    a step each A fragment is read three groups ahead of its four products;
-//  * XCD-aware order: workgroups go to the 8 XCDs round robin, so XCD x is
-//    given the feature blocks x, x + 8, ... (its slice of Theta stays in its
-//    L2) and runs them over every token block.
+//  * XCD-aware order: workgroups go to the 8 XCDs round robin and workgroup
+//    i takes feature block i % nfb of token block i / nfb. When the number of
+//    feature blocks nfb is a multiple of 8, XCD x is given the feature blocks
+//    x, x + 8, ... (its slice of Theta stays in its L2) over every token
+//    block; otherwise the blocks still spread evenly over the XCDs.
 #include "launch.hpp"
 #include "tile.hpp"
 
@@ -37,7 +39,6 @@ constexpr int PT = 256;           // tokens per block
 constexpr int PK = 64;            // contraction step
 constexpr int PNT = 512;          // threads (8 waves)
 constexpr int WF = 128, WT = 64;  // per-wave tile
-constexpr int NXCD = 8;
 
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;  // 16 bytes
 
@@ -52,10 +53,8 @@ __global__ __launch_bounds__(PNT) void qkv_project_kernel(int NF, int M, int K, 
                                                           const bf16_t *X, const bf16_t *theta,
                                                           bf16_t *XQ, bf16_t *XK, bf16_t *XV) {
     __shared__ ProjSmem sm;
-    const int nfb = (NF + PF - 1) / PF, nfx = (nfb + NXCD - 1) / NXCD;
-    const int i = blockIdx.x, r = i / NXCD;
-    const int fb = i % NXCD + NXCD * (r % nfx), tb = r / nfx;
-    if (fb >= nfb) return;  // the grid rounds the feature blocks up to a multiple of 8
+    const int nfb = (NF + PF - 1) / PF;
+    const int i = blockIdx.x, fb = i % nfb, tb = i / nfb;
     const int f0 = fb * PF, t0 = tb * PT;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c = lane & 15;
     const int wf0 = (w & 1) * WF, wt0 = (w >> 1) * WT;
@@ -154,8 +153,8 @@ hipError_t launch_qkv_project(int B, int L, int dm, int H, const void *X, const 
     const int HD = H * D, NF = 3 * HD;
     const long Ml = static_cast<long>(B) * L;
     const int M = static_cast<int>(Ml);
-    const int nfb = (NF + PF - 1) / PF, nfx = (nfb + NXCD - 1) / NXCD, ntb = (M + PT - 1) / PT;
-    const long blocks = static_cast<long>(NXCD) * nfx * ntb;
+    const int nfb = (NF + PF - 1) / PF, ntb = (M + PT - 1) / PT;
+    const long blocks = static_cast<long>(nfb) * ntb;
     if (blocks <= 0) return hipSuccess;
     hipLaunchKernelGGL(qkv_project_kernel, dim3(static_cast<unsigned>(blocks)), dim3(PNT), 0, stream, NF, M, dm,
                        HD, H, L, static_cast<const bf16_t *>(X), static_cast<const bf16_t *>(theta),
