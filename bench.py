@@ -31,6 +31,11 @@ Other workloads of the same hot path (--workload):
       eta, dtheta per sequence; roofline: HBM)
   3o  workload 3 through ttt_linear_forward_opts with the inner-product loss
       and weight decay 0.5 (the MFMA prefill's option instantiation; roofline: HBM)
+  3p  the layer's Q/K/V input projections (ttt_qkv_project) at workload 3's
+      shape, model width 2048 (roofline: bf16 MFMA); 2p at workload 2's (768)
+  3L  the layer's inner path from its input at workload 3's shape: the Q/K/V
+      projections, then the gated prefill, on one stream as one step
+      (roofline: bf16 MFMA over the flops of both)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
                        [--no-cpu-baseline]
@@ -69,6 +74,14 @@ def alg_flops_mlp(B, H, L, d, b=16):
     """Algorithmic flops of one TTT-MLP prefill launch (dual form, hidden 4d):
     56 d^2 + 20 b d per token-head."""
     return B * H * L * (56 * d * d + 20 * b * d)
+
+
+def alg_flops_layer(B, L, dm, H, d, b=16):
+    """Algorithmic flops of the layer's inner path from its input: the Q/K/V
+    projections (2 B L d_model 3 H d) and the TTT-Linear dual-form prefill,
+    6 d^2 + 4 b d per token-head (XK W, XQ W, the state update, the two
+    token x token Grams and their products with E)."""
+    return 2 * B * L * dm * 3 * H * d + B * H * L * (6 * d * d + 4 * b * d)
 
 
 def alg_bytes_decode(B, H, d, s_in=2, s_out=2):
@@ -183,7 +196,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="3", choices=["3", "2", "5p", "4", "4o", "4g", "5d", "5r", "5m", "5g", "3b", "4b",
-                             "3g", "3gb", "3o", "3p", "2p"])
+                             "3g", "3gb", "3o", "3p", "2p", "3L"])
     ap.add_argument("--peaks", action="store_true",
                     help="measure achievable HBM copy bandwidth and bf16 GEMM throughput (context)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -236,6 +249,8 @@ def main():
         return bench_gate_backward(args)
     if args.workload in ("3p", "2p"):
         return bench_proj(args, int(args.workload[0]))
+    if args.workload == "3L":
+        return bench_layer(args)
     wl = {"3": 3, "3g": 3, "3o": 3, "2": 2, "5p": 5}[args.workload]
     gated = args.workload == "3g"
     opts = args.workload == "3o"  # inner-product loss, weight decay 0.5
@@ -779,6 +794,50 @@ def bench_proj(args, num: int):
           {"bound": "mfma", "achieved": ach, "peak": 2500.0, "unit": "TFLOP/s", "frac": ach / 2500.0,
            "traffic": None, "kernel": "qkv_project_kernel", "kernel_avg_us": kern * 1e6,
            "alg_flops_per_launch": fl}, extra)
+
+
+def bench_layer(args):
+    """The TTT-Linear layer's inner path from its input at workload 3's shape
+    (B=2, L=8192, model width 2048, H=32, d=64): the Q/K/V projections of X
+    (ttt_qkv_project) and the prefill with the learning-rate gate inside the
+    kernel (ttt_linear_forward_gated), launched back to back on one stream and
+    timed as one step. X ~ N(0, 1) and theta ~ N(0, 0.02^2) as in the
+    projection workload (seed 103); W0 ~ N(0, 0.02^2), b0 = 0, gamma = 1,
+    beta = 0, theta_lr ~ N(0, 0.02^2), eta_base = 1/d (seed 1003)."""
+    import numpy as np
+    import torch
+    from test_sequence_layer_ttt_amd import gen, ttt
+    x = gen.make_proj_workload(3)
+    B, L, dm, H, d = x.B, x.L, x.dm, x.H, x.d
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    X = torch.from_numpy(x.X).to(dev).to(torch.bfloat16)
+    th = torch.from_numpy(x.theta).to(dev).to(torch.bfloat16)
+    XQ, XK, XV, O = (torch.empty((B, H, L, d), device=dev, dtype=torch.bfloat16) for _ in range(4))
+    rng = np.random.default_rng(1003)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+    W0 = f32(0.02 * rng.standard_normal((H, d, d)))
+    theta_lr = f32(0.02 * rng.standard_normal((H, d)))
+    b0, gam, bet = f32(np.zeros((H, d))), f32(np.ones((H, d))), f32(np.zeros((H, d)))
+    Wo = torch.empty((B, H, d, d), device=dev)
+    bo = torch.empty((B, H, d), device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ttt.ttt_qkv_project(X, th, H, out=(XQ, XK, XV), stream=stream)
+        ttt.ttt_linear_forward_gated(XQ, XK, XV, theta_lr, 1.0 / d, W0, b0, gam, bet, O=O, W_out=Wo,
+                                     b_out=bo, mb=16, ln_eps=gen.LN_EPS, stream=stream)
+
+    wall, kern = _timed(step, stream, args.warmup, args.steps)
+    fl = alg_flops_layer(B, L, dm, H, d)
+    ach = fl / kern / 1e12
+    _line("TTT-Linear layer tokens/s from its input (Q/K/V projections + gated dual-form prefill)",
+          B * L / wall, args, wall, "bf16",
+          {"workload": f"ttt_linear_layer_B{B}_L{L}_dmodel{dm}_H{H}_d{d}", "B": B, "L": L, "d_model": dm,
+           "H": H, "d": d, "mini_batch": 16, "parallelism": "none (1 GPU)"},
+          {"bound": "mfma", "achieved": ach, "peak": 2500.0, "unit": "TFLOP/s", "frac": ach / 2500.0,
+           "traffic": None, "kernel": "qkv_project_kernel + linear_prefill_mfma (gated)",
+           "kernel_avg_us": kern * 1e6, "alg_flops_per_launch": fl})
 
 
 def bench_peaks(args):

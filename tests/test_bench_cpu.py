@@ -37,3 +37,9 @@ def test_decode_algorithmic_work():
     # one b = 1 step: 6 d^2 flops per state; state bytes 2 x (d^2 + d) x 4 each way
     assert bench.alg_flops_decode_step(64, 32, 64) == 64 * 32 * 6 * 4096
     assert bench.alg_bytes_decode(64, 32, 64) == 64 * 32 * (2 * 4160 * 4 + 3 * 128 + 4 + 128)
+
+
+def test_layer_algorithmic_flops():
+    # projections: 2 x (B L = 16,384) x d_model 2,048 x (3 H d = 6,144) = 412.3 GFLOP;
+    # prefill: 6 d^2 + 4 b d = 28,672 flop per token-head over B H L = 524,288
+    assert bench.alg_flops_layer(2, 8192, 2048, 32, 64) == 412_316_860_416 + 524_288 * 28_672
