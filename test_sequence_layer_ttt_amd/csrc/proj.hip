@@ -54,7 +54,7 @@ __global__ __launch_bounds__(PNT) void qkv_project_kernel(int NF, int M, int K, 
                                                           bf16_t *XQ, bf16_t *XK, bf16_t *XV) {
     __shared__ ProjSmem sm;
     const int nfb = (NF + PF - 1) / PF;
-    const int i = blockIdx.x, fb = i % nfb, tb = i / nfb;
+    const int blk_id = blockIdx.x, fb = blk_id % nfb, tb = blk_id / nfb;
     const int f0 = fb * PF, t0 = tb * PT;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c = lane & 15;
     const int wf0 = (w & 1) * WF, wt0 = (w >> 1) * WT;
