@@ -28,7 +28,7 @@
 //
 // Three launches of 256-thread workgroups. A forward sweep (one workgroup per
 // (n, h) sequence) stores the state at every chunk start in the caller's
-// workspace. A pre-pass (one workgroup per chunk, all chunks at once)
+// workspace. A pre-pass (persistent workgroups taking the chunks in turn)
 // recomputes each chunk from its stored state and applies every rule above
 // that does not involve dW', db': Z, G, E, T, Zb, dZb, dA, dXQ in full, the
 // dA^T XQ part of dXK and T^T dZb, storing what the rest needs in a per-chunk
@@ -106,7 +106,7 @@ struct Rec {
 // The three launches: the forward sweep stores every chunk-start state (one
 // workgroup per sequence); the pre-pass recomputes each chunk from its state
 // and does all of the chunk's reverse that does not depend on the adjoint
-// state (one workgroup per chunk, all chunks at once); the reverse sweep runs
+// state (as many workgroups as run at once, each taking chunks in turn); the reverse sweep runs
 // the adjoint-dependent rest, chunk by chunk from the last (one per sequence).
 enum { FWD = 0, PRE = 1, REV = 2 };
 
@@ -126,12 +126,13 @@ __global__ __launch_bounds__(NT) void linear_backward_kernel(
     using io = io_traits<TIO>;
     __shared__ std::conditional_t<MODE == PRE, PreSmem<D>, BwdSmem<D>> sm;
 
-    const int tid = threadIdx.x, r = tid / RW, q = tid % RW;
-    const int w = tid / 64, lane = tid % 64, g = lane / 16, c = lane % 16;  // MFMA coordinates
+    // (not const: the pre-pass's chunk loop makes them opaque per chunk)
+    int tid = threadIdx.x, r = tid / RW, q = tid % RW;
+    int w = tid / 64, lane = tid % 64, g = lane / 16, c = lane % 16;  // MFMA coordinates
     const bool mw = w < NTL;  // this wave owns column tile w
     const int nch = (L + mb - 1) / mb;
-    // the pre-pass takes one chunk: workgroup index = sequence * chunks + chunk
-    const long seq = MODE == PRE ? static_cast<long>(blockIdx.x) / nch : static_cast<long>(blockIdx.x);
+    // one sequence per workgroup in the sweeps; the pre-pass sets its sequence per chunk
+    const long seq = MODE == PRE ? 0 : static_cast<long>(blockIdx.x);
     const int h = static_cast<int>(seq % H);
     const long n = seq / H;
     const size_t sq = static_cast<size_t>(seq);
@@ -253,10 +254,11 @@ __global__ __launch_bounds__(NT) void linear_backward_kernel(
     };
     // unconditional loads from a row clamped into the sequence; rows past its
     // end are zeroed when staged
-    auto fetch_rows = [&](int ch, bool xq, bool go, Rows &R) {
+    // (xb: the sequence's first element in the [.., L, d] arrays; sqi: its index)
+    auto fetch_rows_at = [&](size_t xb, size_t sqi, int ch, bool xq, bool go, Rows &R) {
         R.ok = r < min(mb, L - ch * mb);
         const int rr = R.ok ? r : 0;
-        const size_t row = xbase + static_cast<size_t>(ch * mb + rr) * D;
+        const size_t row = xb + static_cast<size_t>(ch * mb + rr) * D;
 #pragma unroll
         for (int u = 0; u < NF; ++u) {
             const int f = q + RW * u;
@@ -265,14 +267,15 @@ __global__ __launch_bounds__(NT) void linear_backward_kernel(
             if (xq) R.xq[u] = XQ[row + f];
             if (go) R.go[u] = dO[row + f];
         }
-        R.et = eta[sq * L + ch * mb + rr];
+        R.et = eta[sqi * L + ch * mb + rr];
     };
-    auto fetch_state = [&](int ch, State &S) {
-        const float *wc = wsq + static_cast<size_t>(ch) * (D * D + D);
+    auto fetch_rows = [&](int ch, bool xq, bool go, Rows &R) { fetch_rows_at(xbase, sq, ch, xq, go, R); };
+    auto fetch_state_at = [&](const float *wc, State &S) {
 #pragma unroll
         for (int k = 0; k < NWP; ++k) S.w[k] = wc[tid + NT * k];
         S.b = tid < D ? wc[D * D + tid] : 0.f;
     };
+    auto fetch_state = [&](int ch, State &S) { fetch_state_at(wsq + static_cast<size_t>(ch) * (D * D + D), S); };
     // stage a chunk's rows: XK (and XQ, dO) into LDS; tau and eta into registers
     auto stage_rows = [&](const Rows &R, bool xq, bool go, float (&tau)[NF], float &et, float (&gov)[NF]) {
 #pragma unroll
@@ -357,136 +360,163 @@ __global__ __launch_bounds__(NT) void linear_backward_kernel(
     }
 
     if constexpr (MODE == PRE) {
-        // ========== pre-pass: one chunk, everything independent of the adjoint ==========
-        const int ch = static_cast<int>(blockIdx.x % nch);
-        const int m = min(mb, L - ch * mb);
-        const float *S = wsq + static_cast<size_t>(ch) * (D * D + D);
-        float *rc = recq + static_cast<size_t>(ch) * REC;
-        for (int i = tid; i < D * D; i += NT) sm.W[(i / D) * DP + i % D] = S[i];
-        if (tid < D) sm.b[tid] = S[D * D + tid];
-        float tau[NF], et, go[NF];
-        {
-            Rows R;
-            fetch_rows(ch, true, true, R);
+        // ========== pre-pass: every chunk, everything independent of the adjoint ==========
+        // Persistent workgroups: workgroup i takes the chunks i, i + grid, i + 2 grid, ...
+        // of the sequence-major chunk list. Once a chunk is staged, the next one's
+        // rows and checkpoint are fetched into the same registers, so the
+        // global-memory latency hides behind a chunk's work.
+        const long total = static_cast<long>(nseq) * nch;
+        auto fetch = [&](long gi, Rows &R, State &S) {
+            const long sqi = gi / nch;
+            fetch_rows_at(static_cast<size_t>(sqi) * L * D, static_cast<size_t>(sqi), static_cast<int>(gi - sqi * nch),
+                          true, true, R);
+            fetch_state_at(ws + static_cast<size_t>(gi) * (D * D + D), S);
+        };
+        Rows R;
+        State S;
+        fetch(min(static_cast<long>(blockIdx.x), total - 1), R, S);
+        for (long gi = blockIdx.x; gi < total; gi += gridDim.x) {
+            // lane coordinates opaque per chunk: the per-lane LDS and record addresses are
+            // formed where they are used instead of being hoisted out of the loop and held
+            asm volatile("" : "+v"(tid), "+v"(r), "+v"(q), "+v"(g), "+v"(c));
+            const long sqi = gi / nch;
+            const int ch = static_cast<int>(gi - sqi * nch), hh = static_cast<int>(sqi % H);
+            const size_t xb = static_cast<size_t>(sqi) * L * D;
+            const int m = min(mb, L - ch * mb);
+            float *rc = ws + static_cast<size_t>(total) * (D * D + D) + static_cast<size_t>(gi) * REC;
+#pragma unroll
+            for (int u = 0; u < NF; ++u) {
+                gm[u] = gamma[hh * D + q + RW * u];
+                bt[u] = beta[hh * D + q + RW * u];
+            }
+#pragma unroll
+            for (int k = 0; k < NWP; ++k) {
+                const int i = tid + NT * k;
+                sm.W[(i / D) * DP + i % D] = S.w[k];
+            }
+            if (tid < D) sm.b[tid] = S.b;
+            float tau[NF], et, go[NF];
             stage_rows(R, true, true, tau, et, go);
-        }
-        __syncthreads();
+            fetch(min(gi + static_cast<long>(gridDim.x), total - 1), R, S);  // a valid chunk even past the end
+            __syncthreads();
 
-        // Z = XK W + b, Zq = XQ W + b (tile w); T = XQ XK^T + 1 on the causal triangle
-        if (mw) {
-            put(sm.Z, mma<D>(rowm(sm.XK, DP), rowm(sm.W + 16 * w, DP), g, c, brow(sm.b)));
-            put(sm.Zb, mma<D>(rowm(sm.XQ, DP), rowm(sm.W + 16 * w, DP), g, c, brow(sm.b)));
-            const f32x4 t4 = mma<RW>(rowm(sm.XQ + 16 * w, DP), colm(sm.XK + 16 * w, DP), g, c, fz);
+            // Z = XK W + b, Zq = XQ W + b (tile w); T = XQ XK^T + 1 on the causal triangle
+            if (mw) {
+                put(sm.Z, mma<D>(rowm(sm.XK, DP), rowm(sm.W + 16 * w, DP), g, c, brow(sm.b)));
+                put(sm.Zb, mma<D>(rowm(sm.XQ, DP), rowm(sm.W + 16 * w, DP), g, c, brow(sm.b)));
+                const f32x4 t4 = mma<RW>(rowm(sm.XQ + 16 * w, DP), colm(sm.XK + 16 * w, DP), g, c, fz);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sm.TA[w][(4 * g + i) * TP + c] = t4[i];
-        }
-        __syncthreads();
-        {  // T = tril(sum of the slices + 1) on the chunk's rows; one entry per thread
-            const int t = tid / RW, s2 = tid % RW;
-            float v = 0.f;
-#pragma unroll
-            for (int k = 0; k < NTL; ++k) v += sm.TA[k][t * TP + s2];
-            sm.T[t * TP + s2] = (s2 <= t && t < m) ? v + 1.f : 0.f;
-        }
-        {  // G = lnl2(Z, XV - XK), E = -eta G; the values the reverse of lnl2 needs to the record
-            float z[NF];
-            rowz(sm.Z, z);
-            Lnl2 s;
-            lnl2(z, tau, s);
-#pragma unroll
-            for (int u = 0; u < NF; ++u) {
-                const int f = q + RW * u;
-                sm.E[r * DP + f] = -et * s.G[u];
-                rc[RT_XH * RW * D + r * D + f] = s.xh[u];
-                rc[RT_GH * RW * D + r * D + f] = s.gh[u];
-                rc[RT_G * RW * D + r * D + f] = s.G[u];
+                for (int i = 0; i < 4; ++i) sm.TA[w][(4 * g + i) * TP + c] = t4[i];
             }
-            if (q == 0) {
-                rc[OS + r] = s.sigma;
-                rc[OS + RW + r] = s.c;
+            __syncthreads();
+            {  // T = tril(sum of the slices + 1) on the chunk's rows; one entry per thread
+                const int t = tid / RW, s2 = tid % RW;
+                float v = 0.f;
+#pragma unroll
+                for (int k = 0; k < NTL; ++k) v += sm.TA[k][t * TP + s2];
+                sm.T[t * TP + s2] = (s2 <= t && t < m) ? v + 1.f : 0.f;
             }
-        }
-        __syncthreads();
-
-        // Zb = XQ W + b + T E
-        if (mw) put(sm.Zb, mma<RW>(rowm(sm.T, TP), rowm(sm.E + 16 * w, DP), g, c, get(sm.Zb)));
-        __syncthreads();
-
-        // the reverse of O = XQ + LN(Zb): dZb, and the chunk's share of dgamma, dbeta
-        float dgp[NF], dbp[NF];
-        {
-            float zb[NF];
-            rowz(sm.Zb, zb);
-            float s1 = 0.f, s2 = 0.f;
+            {  // G = lnl2(Z, XV - XK), E = -eta G; the values the reverse of lnl2 needs to the record
+                float z[NF];
+                rowz(sm.Z, z);
+                Lnl2 s;
+                lnl2(z, tau, s);
 #pragma unroll
-            for (int u = 0; u < NF; ++u) s1 += zb[u];
-            const float mu = tile::row16_sum(s1) * inv_d;
-#pragma unroll
-            for (int u = 0; u < NF; ++u) s2 += (zb[u] - mu) * (zb[u] - mu);
-            const float rs = 1.0f / sqrtf(tile::row16_sum(s2) * inv_d + eps);
-            float xb[NF], dx[NF], m1 = 0.f, m2 = 0.f;
-#pragma unroll
-            for (int u = 0; u < NF; ++u) {
-                xb[u] = (zb[u] - mu) * rs;
-                dx[u] = gm[u] * go[u];
-                dgp[u] = go[u] * xb[u];
-                dbp[u] = go[u];
-                m1 += dx[u];
-                m2 += dx[u] * xb[u];
-            }
-            m1 = tile::row16_sum(m1) * inv_d;
-            m2 = tile::row16_sum(m2) * inv_d;
-#pragma unroll
-            for (int u = 0; u < NF; ++u) {
-                const float v = (dx[u] - m1 - xb[u] * m2) * rs;
-                sm.Z[r * DP + q + RW * u] = v;
-                rc[RT_DZB * RW * D + r * D + q + RW * u] = v;
-            }
-        }
-        __syncthreads();  // every row of Zb read: its tile becomes the row-sum buffer
-        {
-            const float a = rowsum(sm.Zb, dgp), b = rowsum(sm.Zb, dbp);  // (two barriers each)
-            if (tid < D) {
-                rc[OGB + tid] = a;
-                rc[OGB + D + tid] = b;
-            }
-        }
-
-        // dXQ tile = dZb W^T; slices of dA = dZb E^T; T^T dZb, the adjoint-free part of dE
-        f32x4 gq = fz;
-        if (mw) {
-            gq = mma<D>(rowm(sm.Z, DP), colm(sm.W + 16 * w * DP, DP), g, c, fz);
-            const f32x4 a4 = mma<RW>(rowm(sm.Z + 16 * w, DP), colm(sm.E + 16 * w, DP), g, c, fz);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sm.TA[w][(4 * g + i) * TP + c] = a4[i];
-            const f32x4 td = mma<RW>(colm(sm.T, TP), rowm(sm.Z + 16 * w, DP), g, c, fz);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) rc[RT_TDZ * RW * D + (4 * g + i) * D + 16 * w + c] = td[i];
-        }
-        __syncthreads();
-        {  // dA = the slices summed on the causal triangle of the chunk's rows
-            const int t = tid / RW, s2 = tid % RW;
-            float v = 0.f;
-#pragma unroll
-            for (int k = 0; k < NTL; ++k) v += sm.TA[k][t * TP + s2];
-            sm.dA[t * TP + s2] = (s2 <= t && t < m) ? v : 0.f;
-        }
-        __syncthreads();
-
-        // dXQ = dO + dZb W^T + dA XK;  dA^T XQ, the adjoint-free part of dXK
-        if (mw) {
-            gq = mma<RW>(rowm(sm.dA, TP), rowm(sm.XK + 16 * w, DP), g, c, gq);
-            const f32x4 gk = mma<RW>(colm(sm.dA, TP), rowm(sm.XQ + 16 * w, DP), g, c, fz);
-            const f32x4 do4 = get(sm.dO);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 4 * g + i;
-                if (t < m) {
-                    const size_t at = xbase + static_cast<size_t>(ch * mb + t) * D + 16 * w + c;
-                    dXQ[at] = gq[i] + do4[i];
-                    dXK[at] = gk[i];
+                for (int u = 0; u < NF; ++u) {
+                    const int f = q + RW * u;
+                    sm.E[r * DP + f] = -et * s.G[u];
+                    rc[RT_XH * RW * D + r * D + f] = s.xh[u];
+                    rc[RT_GH * RW * D + r * D + f] = s.gh[u];
+                    rc[RT_G * RW * D + r * D + f] = s.G[u];
+                }
+                if (q == 0) {
+                    rc[OS + r] = s.sigma;
+                    rc[OS + RW + r] = s.c;
                 }
             }
+            __syncthreads();
+
+            // Zb = XQ W + b + T E
+            if (mw) put(sm.Zb, mma<RW>(rowm(sm.T, TP), rowm(sm.E + 16 * w, DP), g, c, get(sm.Zb)));
+            __syncthreads();
+
+            // the reverse of O = XQ + LN(Zb): dZb, and the chunk's share of dgamma, dbeta
+            float dgp[NF], dbp[NF];
+            {
+                float zb[NF];
+                rowz(sm.Zb, zb);
+                float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+                for (int u = 0; u < NF; ++u) s1 += zb[u];
+                const float mu = tile::row16_sum(s1) * inv_d;
+#pragma unroll
+                for (int u = 0; u < NF; ++u) s2 += (zb[u] - mu) * (zb[u] - mu);
+                const float rs = 1.0f / sqrtf(tile::row16_sum(s2) * inv_d + eps);
+                float xb[NF], dx[NF], m1 = 0.f, m2 = 0.f;
+#pragma unroll
+                for (int u = 0; u < NF; ++u) {
+                    xb[u] = (zb[u] - mu) * rs;
+                    dx[u] = gm[u] * go[u];
+                    dgp[u] = go[u] * xb[u];
+                    dbp[u] = go[u];
+                    m1 += dx[u];
+                    m2 += dx[u] * xb[u];
+                }
+                m1 = tile::row16_sum(m1) * inv_d;
+                m2 = tile::row16_sum(m2) * inv_d;
+#pragma unroll
+                for (int u = 0; u < NF; ++u) {
+                    const float v = (dx[u] - m1 - xb[u] * m2) * rs;
+                    sm.Z[r * DP + q + RW * u] = v;
+                    rc[RT_DZB * RW * D + r * D + q + RW * u] = v;
+                }
+            }
+            __syncthreads();  // every row of Zb read: its tile becomes the row-sum buffer
+            {
+                const float a = rowsum(sm.Zb, dgp), b = rowsum(sm.Zb, dbp);  // (two barriers each)
+                if (tid < D) {
+                    rc[OGB + tid] = a;
+                    rc[OGB + D + tid] = b;
+                }
+            }
+
+            // dXQ tile = dZb W^T; slices of dA = dZb E^T; T^T dZb, the adjoint-free part of dE
+            f32x4 gq = fz;
+            if (mw) {
+                gq = mma<D>(rowm(sm.Z, DP), colm(sm.W + 16 * w * DP, DP), g, c, fz);
+                const f32x4 a4 = mma<RW>(rowm(sm.Z + 16 * w, DP), colm(sm.E + 16 * w, DP), g, c, fz);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm.TA[w][(4 * g + i) * TP + c] = a4[i];
+                const f32x4 td = mma<RW>(colm(sm.T, TP), rowm(sm.Z + 16 * w, DP), g, c, fz);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) rc[RT_TDZ * RW * D + (4 * g + i) * D + 16 * w + c] = td[i];
+            }
+            __syncthreads();
+            {  // dA = the slices summed on the causal triangle of the chunk's rows
+                const int t = tid / RW, s2 = tid % RW;
+                float v = 0.f;
+#pragma unroll
+                for (int k = 0; k < NTL; ++k) v += sm.TA[k][t * TP + s2];
+                sm.dA[t * TP + s2] = (s2 <= t && t < m) ? v : 0.f;
+            }
+            __syncthreads();
+
+            // dXQ = dO + dZb W^T + dA XK;  dA^T XQ, the adjoint-free part of dXK
+            if (mw) {
+                gq = mma<RW>(rowm(sm.dA, TP), rowm(sm.XK + 16 * w, DP), g, c, gq);
+                const f32x4 gk = mma<RW>(colm(sm.dA, TP), rowm(sm.XQ + 16 * w, DP), g, c, fz);
+                const f32x4 do4 = get(sm.dO);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 4 * g + i;
+                    if (t < m) {
+                        const size_t at = xb + static_cast<size_t>(ch * mb + t) * D + 16 * w + c;
+                        dXQ[at] = gq[i] + do4[i];
+                        dXK[at] = gk[i];
+                    }
+                }
+            }
+            __syncthreads();  // the next chunk's staging overwrites every tile
         }
     }
 
@@ -663,7 +693,15 @@ hipError_t launch_bwd_t(const LinearBwdArgs &a, hipStream_t stream) {
     hipError_t e;
     if (nch > 0) {
         if ((e = launch_mode<D, TIO, FWD>(a, static_cast<unsigned>(nseq), stream)) != hipSuccess) return e;
-        if ((e = launch_mode<D, TIO, PRE>(a, static_cast<unsigned>(nseq * nch), stream)) != hipSuccess) return e;
+        // the pre-pass's persistent workgroups: as many as run at once, at most one per chunk
+        int dev = 0, ncu = 0, per = 0;
+        if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+        if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+        if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, linear_backward_kernel<D, TIO, PRE>, NT, 0)) !=
+            hipSuccess)
+            return e;
+        const size_t pre = std::min(nseq * nch, static_cast<size_t>(std::max(1, ncu * per)));
+        if ((e = launch_mode<D, TIO, PRE>(a, static_cast<unsigned>(pre), stream)) != hipSuccess) return e;
     }
     return launch_mode<D, TIO, REV>(a, static_cast<unsigned>(nseq), stream);
 }
