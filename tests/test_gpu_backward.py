@@ -95,7 +95,9 @@ def test_backward_repeatable():
 def test_backward_workload3_sampled_heads():
     """Workload 3's full length (L = 8192, 512 chunks) on two of its heads
     (batch 0, heads 0 and 17): the oracle's autograd runs on those two
-    sequences only."""
+    sequences only. Its 1,024 chunks exceed the pre-pass's resident
+    workgroups (three per compute unit), so workgroups take a second chunk,
+    of the other sequence, through the pre-pass's chunk loop."""
     full = gen.make_workload(3)
     hs = [0, 17]
     sl = lambda a: np.ascontiguousarray(a[:1, hs])
