@@ -119,6 +119,43 @@ def test_linear_in_place_resume():
     assert max(err.values()) <= P.TOL["bf16"]
 
 
+def test_linear_prefill_rows_past_4gib():
+    """One head at L = 2^25 + 32: the bf16 rows of the last two chunks start
+    4 GiB into XQ, XK, XV and O, where 32-bit byte offsets would wrap. The
+    single call's last two chunks of O and its final state are compared with
+    the oracle run over those two chunks from the state the kernel returns
+    for the first 2^25 tokens (a chain of 2^21 chunks is out of the oracle's
+    reach). Inputs follow the bf16 recipe (rows N(0, 1), eta = logistic(N(0, 1))
+    / d), drawn on the GPU from a seeded torch generator, W0, b0, gamma, beta
+    from the generator module; O starts as NaN, so an unwritten row fails."""
+    L0, tail, d = 1 << 25, 32, 64
+    L = L0 + tail
+    print(f"[parity] prefill past 4 GiB: B=1 H=1 L={L}", flush=True)
+    rng = torch.Generator(device="cuda")
+    rng.manual_seed(2525)
+    shp = (1, 1, L, d)
+    XQ, XK, XV = (torch.randn(shp, generator=rng, device="cuda", dtype=torch.bfloat16) for _ in range(3))
+    eta = torch.sigmoid(torch.randn((1, 1, L), generator=rng, device="cuda")) / d
+    x0 = gen.make_linear(2525, 1, 1, 16, d)
+    W0, b0, g, be = (P.dev(a) for a in (x0.W0, x0.b0, x0.gamma, x0.beta))
+    O = torch.full(shp, float("nan"), device="cuda", dtype=torch.bfloat16)
+    _, W_full, b_full = ttt.ttt_linear_forward(XQ, XK, XV, eta, W0, b0, g, be, O=O)
+    h = slice(0, L0)
+    _, W_mid, b_mid = ttt.ttt_linear_forward(XQ[:, :, h], XK[:, :, h], XV[:, :, h], eta[:, :, h], W0, b0, g, be)
+    torch.cuda.synchronize()
+    t = slice(L0, L)
+    f32 = lambda a: P.to_np(a).astype(np.float32)
+    two = gen.LinearInputs(1, 1, tail, d, "bf16", f32(XQ[:, :, t]), f32(XK[:, :, t]), f32(XV[:, :, t]),
+                           f32(eta[:, :, t]), f32(W_mid)[0], f32(b_mid)[0], x0.gamma, x0.beta)
+    got = (P.to_np(O[:, :, t]), P.to_np(W_full), P.to_np(b_full))
+    del XQ, XK, XV, eta, O
+    torch.cuda.empty_cache()
+    ref = P.linear_oracle(two)
+    err = P.errors(got, ref, 1, LIN_NAMES)
+    _report("prefill L = 2^25 + 32, last two chunks", err)
+    assert max(err.values()) <= P.TOL["bf16"], err
+
+
 def test_linear_bitwise_repeatable():
     x = gen.make_workload(3, L=16 * 40, B=2, H=4)
     a = P.linear_gpu(x)
