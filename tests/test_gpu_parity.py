@@ -156,6 +156,39 @@ def test_linear_prefill_rows_past_4gib():
     assert max(err.values()) <= P.TOL["bf16"], err
 
 
+def test_mlp_prefill_rows_past_4gib():
+    """TTT-MLP at L = 2^25 + 32, checked as the TTT-Linear case above: the
+    single call's last two chunks of O and its final W1, b1, W2, b2 against the
+    oracle run over those two chunks from the state the kernel returns for
+    the first 2^25 tokens."""
+    L0, tail, d = 1 << 25, 32, 64
+    L = L0 + tail
+    print(f"[parity] MLP prefill past 4 GiB: B=1 H=1 L={L}", flush=True)
+    rng = torch.Generator(device="cuda")
+    rng.manual_seed(2526)
+    shp = (1, 1, L, d)
+    XQ, XK, XV = (torch.randn(shp, generator=rng, device="cuda", dtype=torch.bfloat16) for _ in range(3))
+    eta = torch.sigmoid(torch.randn((1, 1, L), generator=rng, device="cuda")) / d
+    x0 = gen.make_mlp(2526, 1, 1, 16, d)
+    st = [P.dev(a) for a in (x0.W1, x0.b1, x0.W2, x0.b2, x0.gamma, x0.beta)]
+    O = torch.full(shp, float("nan"), device="cuda", dtype=torch.bfloat16)
+    full = ttt.ttt_mlp_forward(XQ, XK, XV, eta, *st, O=O)
+    h = slice(0, L0)
+    mid = ttt.ttt_mlp_forward(XQ[:, :, h], XK[:, :, h], XV[:, :, h], eta[:, :, h], *st)
+    torch.cuda.synchronize()
+    t = slice(L0, L)
+    f32 = lambda a: P.to_np(a).astype(np.float32)
+    two = gen.MLPInputs(1, 1, tail, d, "bf16", f32(XQ[:, :, t]), f32(XK[:, :, t]), f32(XV[:, :, t]),
+                        f32(eta[:, :, t]), *(f32(a)[0] for a in mid[1:]), x0.gamma, x0.beta)
+    got = (P.to_np(O[:, :, t]), *(P.to_np(a) for a in full[1:]))
+    del XQ, XK, XV, eta, O, full, mid
+    torch.cuda.empty_cache()
+    ref = P.mlp_oracle(two)
+    err = P.errors(got, ref, 1, MLP_NAMES)
+    _report("MLP prefill L = 2^25 + 32, last two chunks", err)
+    assert max(err.values()) <= P.TOL["bf16"], err
+
+
 def test_linear_bitwise_repeatable():
     x = gen.make_workload(3, L=16 * 40, B=2, H=4)
     a = P.linear_gpu(x)
