@@ -34,14 +34,16 @@ namespace {
 
 using namespace tile;
 
-constexpr int PF = 256;           // output features per block
-constexpr int PT = 256;           // tokens per block
-constexpr int PK = 64;            // contraction step
-constexpr int PNT = 512;          // threads (8 waves)
-constexpr int WF = 128, WT = 64;  // per-wave tile
+constexpr int PT = 256;  // tokens per block
+constexpr int PK = 64;   // contraction step
+constexpr int PNT = 512; // threads (8 waves)
+constexpr int WT = 64;   // tokens per wave tile
 
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;  // 16 bytes
 
+// PF output features per block (256, or 128 when the 256-feature tiles would
+// leave most compute units idle in a last round); a wave tile is PF / 2 x 64
+template <int PF>
 struct ProjSmem {
     uint16_t a[2][PF * PK];  // Theta rows [feature][k], 16-byte chunks XOR-swizzled by row & 7
     uint16_t b[2][PT * PK];  // X rows [token][k], same swizzle
@@ -49,10 +51,12 @@ struct ProjSmem {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void glb_void;
 
+template <int PF>
 __global__ __launch_bounds__(PNT) void qkv_project_kernel(int NF, int M, int K, int HD, int H, int L,
                                                           const bf16_t *X, const bf16_t *theta,
                                                           bf16_t *XQ, bf16_t *XK, bf16_t *XV) {
-    __shared__ ProjSmem sm;
+    constexpr int WF = PF / 2, NTA = WF / 16;  // features per wave tile, its MFMA row tiles
+    __shared__ ProjSmem<PF> sm;
     const int nfb = (NF + PF - 1) / PF;
     const int blk_id = blockIdx.x, fb = blk_id % nfb, tb = blk_id / nfb;
     const int f0 = fb * PF, t0 = tb * PT;
@@ -60,7 +64,8 @@ __global__ __launch_bounds__(PNT) void qkv_project_kernel(int NF, int M, int K, 
     const int wf0 = (w & 1) * WF, wt0 = (w >> 1) * WT;
 
     // global -> LDS directly: wave w, instruction q fills rows 8 (4w + q) .. +7
-    // (1 KB); lane i lands at 16 i bytes, i.e. row 8 (4w + q) + i / 8, physical
+    // (1 KB) of X, and for q < PF / 64 rows 8 ((PF / 64) w + q) .. +7 of Theta; lane i lands
+    // at 16 i bytes, i.e. row 8 blk + i / 8, physical
     // chunk i % 8, which holds logical chunk (i % 8) ^ (i / 8) of that row.
     // Rows past the end read row 0: a feature row only reaches the outputs of
     // that feature and a token row those of that token, which are not stored,
@@ -70,18 +75,20 @@ __global__ __launch_bounds__(PNT) void qkv_project_kernel(int NF, int M, int K, 
         const int rl = lane >> 3, lc = (lane & 7) ^ rl;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int blk = 4 * w + q, row = 8 * blk + rl;
-            const int fr = f0 + row, tr = t0 + row;
-            const bf16_t *sa = theta + static_cast<size_t>(fr < NF ? fr : 0) * K + k0 + lc * 8;
+            const int blk = 4 * w + q, tr = t0 + 8 * blk + rl;
             const bf16_t *sb = X + static_cast<size_t>(tr < M ? tr : 0) * K + k0 + lc * 8;
-            __builtin_amdgcn_global_load_lds((glb_void *)sa, (lds_void *)&sm.a[stg][8 * blk * PK], 16, 0, 0);
+            if (q < PF / 64) {  // compile-time after unrolling; Theta rows 8 ((PF / 64) w + q) .. +7
+                const int blka = (PF / 64) * w + q, fr = f0 + 8 * blka + rl;
+                const bf16_t *sa = theta + static_cast<size_t>(fr < NF ? fr : 0) * K + k0 + lc * 8;
+                __builtin_amdgcn_global_load_lds((glb_void *)sa, (lds_void *)&sm.a[stg][8 * blka * PK], 16, 0, 0);
+            }
             __builtin_amdgcn_global_load_lds((glb_void *)sb, (lds_void *)&sm.b[stg][8 * blk * PK], 16, 0, 0);
         }
     };
 
-    f32x4 acc[8][4];
+    f32x4 acc[NTA][4];
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int t = 0; t < NTA; ++t)
 #pragma unroll
         for (int s = 0; s < 4; ++s) acc[t][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -94,7 +101,7 @@ __global__ __launch_bounds__(PNT) void qkv_project_kernel(int NF, int M, int K, 
         if (kt + 1 < nk) dma(kt + 1, st ^ 1);
         __builtin_amdgcn_sched_barrier(0);
         auto rd_a = [&](int idx) {
-            const int kk = idx >> 3, t = idx & 7;
+            const int kk = idx / NTA, t = idx % NTA;
             const int j = (4 * kk + g) ^ (c & 7);
             return __builtin_bit_cast(
                 bf16x8, *reinterpret_cast<const u32x4 *>(&sm.a[st][(wf0 + 16 * t + c) * PK + 8 * j]));
@@ -104,21 +111,21 @@ __global__ __launch_bounds__(PNT) void qkv_project_kernel(int NF, int M, int K, 
             return __builtin_bit_cast(
                 bf16x8, *reinterpret_cast<const u32x4 *>(&sm.b[st][(wt0 + 16 * s + c) * PK + 8 * j]));
         };
-        constexpr int PD = 3;
-        bf16x8 fa[16], fx[2][4];
+        constexpr int PD = 3, NG = 2 * NTA;  // read-ahead depth; groups of four products per step
+        bf16x8 fa[NG], fx[2][4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) fx[0][s] = rd_x(0, s);
 #pragma unroll
         for (int i = 0; i < PD; ++i) fa[i] = rd_a(i);
 #pragma unroll
-        for (int idx = 0; idx < 16; ++idx) {
-            if (idx + PD < 16) fa[idx + PD] = rd_a(idx + PD);
+        for (int idx = 0; idx < NG; ++idx) {
+            if (idx + PD < NG) fa[idx + PD] = rd_a(idx + PD);
             if (idx == 2) {
 #pragma unroll
                 for (int s = 0; s < 4; ++s) fx[1][s] = rd_x(1, s);
             }
             __builtin_amdgcn_sched_barrier(0);
-            const int kk = idx >> 3, t = idx & 7;
+            const int kk = idx / NTA, t = idx % NTA;
 #pragma unroll
             for (int s = 0; s < 4; ++s) acc[t][s] = mfma32(fa[idx], fx[kk][s], acc[t][s]);
             __builtin_amdgcn_sched_barrier(0);
@@ -134,7 +141,7 @@ __global__ __launch_bounds__(PNT) void qkv_project_kernel(int NF, int M, int K, 
         if (m >= M) continue;
         const int bi = m / L, tp = m - bi * L;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
+        for (int t = 0; t < NTA; ++t) {
             const int n = f0 + wf0 + 16 * t + 4 * g;
             if (n >= NF) continue;
             const int v = n / HD, hj = n - v * HD, h = hj / D, j = hj - h * D;
@@ -148,18 +155,35 @@ __global__ __launch_bounds__(PNT) void qkv_project_kernel(int NF, int M, int K, 
 
 }  // namespace
 
+template <int PF>
+hipError_t launch_pf(int NF, int M, int dm, int HD, int H, int L, const void *X, const void *theta, void *XQ,
+                     void *XK, void *XV, hipStream_t stream) {
+    const long blocks = static_cast<long>((NF + PF - 1) / PF) * ((M + PT - 1) / PT);
+    hipLaunchKernelGGL(qkv_project_kernel<PF>, dim3(static_cast<unsigned>(blocks)), dim3(PNT), 0, stream, NF, M,
+                       dm, HD, H, L, static_cast<const bf16_t *>(X), static_cast<const bf16_t *>(theta),
+                       static_cast<bf16_t *>(XQ), static_cast<bf16_t *>(XK), static_cast<bf16_t *>(XV));
+    return hipGetLastError();
+}
+
 hipError_t launch_qkv_project(int B, int L, int dm, int H, const void *X, const void *theta, void *XQ,
                               void *XK, void *XV, hipStream_t stream) {
     const int HD = H * D, NF = 3 * HD;
     const long Ml = static_cast<long>(B) * L;
     const int M = static_cast<int>(Ml);
-    const int nfb = (NF + PF - 1) / PF, ntb = (M + PT - 1) / PT;
-    const long blocks = static_cast<long>(nfb) * ntb;
-    if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(qkv_project_kernel, dim3(static_cast<unsigned>(blocks)), dim3(PNT), 0, stream, NF, M, dm,
-                       HD, H, L, static_cast<const bf16_t *>(X), static_cast<const bf16_t *>(theta),
-                       static_cast<bf16_t *>(XQ), static_cast<bf16_t *>(XK), static_cast<bf16_t *>(XV));
-    return hipGetLastError();
+    const long ntb = (M + PT - 1) / PT, t256 = ntb * ((NF + 255) / 256), t128 = ntb * ((NF + 127) / 128);
+    if (t256 <= 0) return hipSuccess;
+    // One 256 x 256 tile per compute unit at a time (128 KB of LDS). Rounds of the grid over the
+    // chip, a 128-feature tile costing about 0.6 of a 256-feature one: take the 128-feature tiles
+    // when they finish in fewer tile-times.
+    int dev = 0, ncu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    ncu = ncu > 0 ? ncu : 1;
+    const long r256 = (t256 + ncu - 1) / ncu, r128 = (t128 + ncu - 1) / ncu;
+    if (3 * r128 < 5 * r256)
+        return launch_pf<128>(NF, M, dm, HD, H, L, X, theta, XQ, XK, XV, stream);
+    return launch_pf<256>(NF, M, dm, HD, H, L, X, theta, XQ, XK, XV, stream);
 }
 
 }  // namespace ttt
